@@ -1,0 +1,200 @@
+/*
+ * dyra.h -- C-ABI of libdyra.so: the DyRA layer forward on AMD MI355X (gfx950).
+ *
+ * DyRA (arXiv 2610.02882, "DyRA: Dynamic Residual Approximation for Efficient
+ * Matrix Multiplication in DNNs") splits a dense weight W (c1 x c2) into a
+ * structured approximation W_hat (low-rank, Monarch or BLAST) and a dense
+ * residual, W = W_hat + W_res, and corrects the residual product X W_res of
+ * each input with one alternating-least-squares step at inference time:
+ *
+ *   L = X P                     P = W_res R0^T, R0 = top-r right singular
+ *                               vectors of W_res (prepared offline)
+ *   R = (L^T L + lambda I)^-1 (L^T X) W_res
+ *   Y = X W_hat + L R + bias    (the n x c2 product X W_res is never formed)
+ *
+ * Sources (page title + section; see the design notes for the full list):
+ *   nanless.github.io DyRA digest post: the split equations W = W_hat + W_res
+ *   and XW = X W_hat + X W_res; the residual-product objective
+ *   min ||X W_res - L R||_F^2 and the cheap ALS ordering; the one-iteration
+ *   form XW ~ X W_hat + L1 R1 with L1 = X times a precomputable thin matrix;
+ *   the offline/online split; the structured-matrix definitions.
+ *   paperlayer.ai summary: 2.2 (ALS, ridge), 2.4 (fused merge, Cholesky for
+ *   small r, Newton-Schulz for large r), App. A (offline + online stages),
+ *   App. B (structured matrices).
+ *
+ * Conventions (every entry point):
+ *   - Returns int: DYRA_OK (0) or a negative DYRA_E* code.  No C++ exception
+ *     crosses the ABI.  dyra_status_string() names a code.
+ *   - Arguments are validated on the host before any HIP call; an invalid
+ *     call touches no device state.
+ *   - The caller owns every buffer (host and device).  The library allocates
+ *     no device memory and keeps no global state: calls on distinct streams
+ *     with distinct workspaces are independent.
+ *   - Matrices are row-major and contiguous.  Device pointers must be 16-byte
+ *     aligned.  "stream" is a hipStream_t passed as void* (NULL = default).
+ *   - dtype: DYRA_F32 (fp32 storage, fp32 arithmetic) or DYRA_BF16 (bf16
+ *     storage, fp32 accumulation, fp32 solver).
+ *   - Size constraints: c1, c2, k, r multiples of 8; 1 <= r <= min(c1, c2);
+ *     r <= 128.  Low-rank: k + r <= min(c1, c2).  Monarch: c1 == c2 ==
+ *     mblk^2 with mblk == 32 (bf16 only).  BLAST: nb divides c1 and c2,
+ *     rb <= min(c1, c2) / nb, rb multiple of 32 (bf16 only).
+ */
+#ifndef DYRA_H
+#define DYRA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define DYRA_OK          0
+#define DYRA_EINVAL     -1   /* null pointer, negative ridge, unknown enum   */
+#define DYRA_ESHAPE     -2   /* sizes violate the constraints above         */
+#define DYRA_EWORKSPACE -3   /* workspace smaller than dyra_workspace_size  */
+#define DYRA_EHIP       -4   /* a HIP launch or copy reported an error      */
+#define DYRA_ENOCONV    -5   /* host eigensolver did not converge           */
+#define DYRA_EDTYPE     -6   /* dtype not supported for this structure      */
+
+/* static structure */
+#define DYRA_LOWRANK 0
+#define DYRA_MONARCH 1
+#define DYRA_BLAST   2
+
+/* storage / arithmetic type */
+#define DYRA_F32  0
+#define DYRA_BF16 1
+
+/* r x r solver choice for dyra_forward */
+#define DYRA_SOLVER_AUTO 0   /* Cholesky for r < 128, Newton-Schulz for r >= 128 */
+#define DYRA_SOLVER_CHOL 1
+#define DYRA_SOLVER_NS   2
+
+/* per-segment solver status words (dyra_solver_status) */
+#define DYRA_SOLVE_OK        0
+#define DYRA_SOLVE_NOT_SPD   1   /* Cholesky met a pivot <= 0: R_b := 0, Y_b = X_b W_hat + bias */
+#define DYRA_SOLVE_NOCONV    2   /* Newton-Schulz stopped at its iteration cap           */
+#define DYRA_SOLVE_ZERO      3   /* trace(G_b) == 0 (X_b P == 0): R_b := 0               */
+
+typedef struct {
+  int32_t kind;   /* DYRA_LOWRANK / DYRA_MONARCH / DYRA_BLAST                  */
+  int32_t k;      /* low-rank: static rank                                     */
+  int32_t mblk;   /* Monarch: block count == block size m, c1 == c2 == m*m     */
+  int32_t nb;     /* BLAST: nb x nb block grid                                 */
+  int32_t rb;     /* BLAST: rank of the shared row / column bases              */
+  int32_t r;      /* residual (dynamic) rank                                   */
+  int64_t c1;     /* input features                                            */
+  int64_t c2;     /* output features                                           */
+} dyra_spec;
+
+/* Element counts of each host factor array (0 = unused by this structure). */
+typedef struct {
+  int64_t U, V;        /* low-rank                                      */
+  int64_t B1, B2;      /* Monarch                                       */
+  int64_t Ub, S, Vb;   /* BLAST                                         */
+  int64_t P, R0, Wres, res_sv;
+} dyra_sizes;
+
+/*
+ * Host float64 factors written by dyra_prepare (caller-allocated, sizes from
+ * dyra_prepare_sizes; pointers of unused arrays may be NULL):
+ *   U  [c1][k], V [k][c2]                      W_hat = U V, sqrt(sigma) on each side
+ *   B1 [m][m][m] (block a, row i, col j), B2 [m][m][m] (block j, row a, col l):
+ *        W_hat[a*m+i][j*m+l] = B1[a][i][j] * B2[j][a][l]
+ *        (= blockdiag(B1) . Pi . blockdiag(B2), Pi the reshape-transpose)
+ *   Ub [nb][c1/nb][rb], S [nb][nb][rb][rb], Vb [nb][c2/nb][rb]:
+ *        block (i, j) of W_hat = Ub[i] S[i][j] Vb[j]^T
+ *   P [c1][r] = W_res R0^T,  R0 [r][c2] (orthonormal rows),  Wres [c1][c2],
+ *   res_sv [r] = top singular values of W_res (descending).
+ */
+typedef struct {
+  double* U;  double* V;
+  double* B1; double* B2;
+  double* Ub; double* S; double* Vb;
+  double* P;  double* R0; double* Wres; double* res_sv;
+} dyra_host_factors;
+
+/* Element counts of the factor arrays for a spec.  Errors: EINVAL, ESHAPE. */
+int dyra_prepare_sizes(const dyra_spec* spec, dyra_sizes* out);
+
+/*
+ * Offline preparation on the host (float64, not part of the timed forward).
+ * Fits W_hat by structure (low-rank: truncated SVD; Monarch: rank-1 SVD of
+ * each m x m block; BLAST: shared bases from block-row / block-column SVDs
+ * and least-squares couplings), forms W_res = W - W_hat, takes R0 = top-r
+ * right singular vectors of W_res and P = W_res R0^T.
+ *   W: host [c1][c2] float64 (read only).  out: caller-allocated arrays.
+ *   nthreads: host worker threads (<= 0: hardware concurrency).
+ * Errors: EINVAL, ESHAPE, ENOCONV.
+ * Source: nanless.github.io DyRA digest, "overall DyRA flow" and "offline
+ * preparation and online computation" sections; paperlayer.ai App. A, App. B.
+ */
+int dyra_prepare(const dyra_spec* spec, const double* W, dyra_host_factors* out,
+                 int32_t nthreads);
+
+/* Bytes of the packed device plan for (spec, dtype).  Errors: EINVAL, ESHAPE, EDTYPE. */
+int dyra_plan_size(const dyra_spec* spec, int32_t dtype, size_t* bytes);
+
+/*
+ * Packs host float64 factors into the device plan layout (a host buffer of
+ * dyra_plan_size bytes that the caller copies to device memory once).
+ * Values are rounded fp64 -> fp32 (RNE), then to bf16 (RNE) for DYRA_BF16.
+ * The layout is internal to the library (weights stored output-major so
+ * every GEMM operand is contiguous along its reduction axis).
+ * Errors: EINVAL, ESHAPE, EDTYPE.
+ */
+int dyra_plan_pack(const dyra_spec* spec, const dyra_host_factors* f, int32_t dtype,
+                   void* host_plan);
+
+/* Bytes of device workspace dyra_forward needs for B segments of s rows. */
+int dyra_workspace_size(const dyra_spec* spec, int64_t B, int64_t s, int32_t dtype,
+                        size_t* bytes);
+
+/*
+ * The DyRA layer forward (asynchronous on `stream`; no host synchronisation).
+ *   plan:      device, packed by dyra_plan_pack for the same spec and dtype.
+ *   X:         device [B*s][c1], dtype.   Segment b = rows [b*s, (b+1)*s):
+ *              each segment gets its own ALS solve (L_b, G_b, M_b, R_b).
+ *   bias:      device [c2], dtype, or NULL.
+ *   Y:         device [B*s][c2], dtype (written; must not alias X).
+ *   ridge_eps: lambda_b = ridge_eps * trace(G_b) / r (>= 0; 1e-6 typical).
+ *   solver:    DYRA_SOLVER_*.
+ *   workspace: device, >= dyra_workspace_size bytes; holds the per-segment
+ *              solver status words read by dyra_solver_status.
+ * Errors (before any HIP call): EINVAL, ESHAPE, EDTYPE, EWORKSPACE; EHIP if
+ * a launch fails.  Per-segment numerical trouble is not an error: see the
+ * DYRA_SOLVE_* status words.
+ * Source: nanless.github.io DyRA digest, equations XW = X W_hat + X W_res,
+ * min_{L,R} ||X W_res - L R||_F^2 and XW ~ X W_hat + L1 R1; paperlayer.ai
+ * 2.2 and 2.4.
+ */
+int dyra_forward(const dyra_spec* spec, const void* plan, const void* X, const void* bias,
+                 void* Y, int64_t B, int64_t s, int32_t dtype, float ridge_eps,
+                 int32_t solver, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Copies the B per-segment solver status words of the last dyra_forward on
+ * this workspace to host_out[B] (synchronises `stream`).  Errors: EINVAL, EHIP.
+ */
+int dyra_solver_status(const dyra_spec* spec, const void* workspace, int64_t B, int64_t s,
+                       int32_t dtype, int32_t* host_out, void* stream);
+
+/*
+ * Dense comparator Y = X W + bias on the same GEMM core (asynchronous).
+ *   X: device [n][c1]; Wt: device [c2][c1] (W transposed, i.e. the weight in
+ *   output-major order as a linear layer stores it); bias: device [c2] or
+ *   NULL; Y: device [n][c2].  Errors: EINVAL, ESHAPE, EDTYPE, EHIP.
+ */
+int dyra_dense_ref(const void* X, const void* Wt, const void* bias, void* Y, int64_t n,
+                   int64_t c1, int64_t c2, int32_t dtype, void* stream);
+
+/* Static string naming a status code. */
+const char* dyra_status_string(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DYRA_H */

@@ -1,0 +1,67 @@
+// Device-side building blocks for the gfx950 DyRA kernels: bf16 conversion,
+// MFMA wrappers, the swizzled LDS tile layout, and the XCD-aware tile order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef uint16_t bf16_t;
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf2f(bf16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// fp32 -> bf16, round to nearest even (gfx950 v_cvt_pk_bf16_f32).
+__device__ __forceinline__ bf16_t f2bf(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
+
+// Element traits.  A 16-byte chunk holds KPC elements; one "k-substep" of the
+// MMA covers two chunks (lanes 0-31 read chunk 2s, lanes 32-63 chunk 2s+1).
+template <typename T> struct TT;
+
+template <> struct TT<bf16_t> {
+  static constexpr int KPC = 8;
+  static constexpr int ESZ = 2;
+  // 32x32 block += (lane rows of a) x (lane rows of b)^T over 16 k values.
+  __device__ static __forceinline__ void mma(f32x16& acc, const uint4& a, const uint4& b) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                  __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
+  }
+  __device__ static __forceinline__ float to_f(bf16_t v) { return bf2f(v); }
+  __device__ static __forceinline__ bf16_t from_f(float v) { return f2bf(v); }
+};
+
+template <> struct TT<float> {
+  static constexpr int KPC = 4;
+  static constexpr int ESZ = 4;
+  // four 32x32x2 fp32 MFMAs, element e of each lane's chunk in the e-th one.
+  __device__ static __forceinline__ void mma(f32x16& acc, const uint4& a, const uint4& b) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
+  }
+  __device__ static __forceinline__ float to_f(float v) { return v; }
+  __device__ static __forceinline__ float from_f(float v) { return v; }
+};
+
+// Operand tiles in LDS: one row = 128 bytes = 8 chunks of 16 bytes; the chunk
+// index is XOR-swizzled with the row so that 8 consecutive rows reading the
+// same logical chunk hit 8 different bank groups.
+__device__ __forceinline__ int lds_off(int row, int chunk) { return row * 128 + (((chunk ^ row) & 7) << 4); }
+
+// Output staging tiles: rows of CPR chunks (CPR a multiple of 8); the low
+// three bits of the chunk index are XOR-swizzled with the row.
+__device__ __forceinline__ int stage_chunk(int row, int chunk) { return (chunk & ~7) | ((chunk ^ row) & 7); }
+
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own
+// L2).  Renumber so that consecutive tile ids run on the same XCD and share
+// operand rows in its L2.
+__device__ __forceinline__ int xcd_tile_id(int bid, int nwg) {
+  const int full = nwg & ~7;
+  if (bid >= full) return bid;
+  const int per = full >> 3;
+  return (bid & 7) * per + (bid >> 3);
+}
+
+__device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }

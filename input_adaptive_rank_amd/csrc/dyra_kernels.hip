@@ -1,0 +1,701 @@
+// DyRA layer forward on gfx950: kernels and the C-ABI entry points that
+// launch them.
+//
+// Per segment b (rows [b s, (b+1) s) of X), following the one-step ALS
+// correction of the DyRA pages (nanless.github.io digest: residual-product
+// objective, its cheap ordering, and the one-iteration form
+// XW ~ X W_hat + L1 R1; paperlayer.ai 2.2 and 2.4):
+//   S1  [T | L] = X [U | P]           one MFMA pass over X (T = X U_f, L = X P)
+//   S3  M_b = L_b^T X_b, G_b = L_b^T L_b   split-N MFMA reductions over tokens
+//   S4  Ginv_b = (G_b + lambda_b I)^-1     symmetric sweep (r < 128) or
+//                                          Newton-Schulz (r >= 128)
+//       M'_b = Ginv_b M_b
+//   S5  R_b = M'_b W_res               one GEMM over all segments (R^T stored)
+//   S6  Y_b = T_b V + L_b R_b + bias    one fused GEMM, K = k + r, with a
+//                                       per-segment second operand; L R is
+//                                       never written to memory
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "../../include/dyra.h"
+#include "device_common.h"
+#include "gemm_engine.h"
+#include "spec.h"
+
+using namespace dyra_spec_util;
+
+namespace {
+
+__host__ __device__ __forceinline__ int64_t imin64(int64_t a, int64_t b) { return a < b ? a : b; }
+__host__ __device__ __forceinline__ int64_t imax64(int64_t a, int64_t b) { return a > b ? a : b; }
+
+// ===========================================================================
+// generic single-phase GEMM: C[M x N] = A[M x K] B[N x K]^T (+ bias[N])
+// ===========================================================================
+
+template <class C>
+__global__ __launch_bounds__(C::NT) void gemm_tn_kernel(const char* A, int64_t lda, const char* B,
+                                                        int64_t ldb, char* Cg, int64_t ldc, int64_t M,
+                                                        int64_t N, int64_t K,
+                                                        const typename C::elem* bias, int tiles_n) {
+  typedef typename C::elem T;
+  __shared__ __attribute__((aligned(16))) char lds[C::LDS];
+  const int t = xcd_tile_id(blockIdx.x, gridDim.x);
+  const int64_t m0 = (int64_t)(t / tiles_n) * C::BM, n0 = (int64_t)(t % tiles_n) * C::BN;
+  const int64_t kb = K * TT<T>::ESZ;
+  auto prov = [=](int p, Phase& ph) -> bool {
+    if (p != 0) return false;
+    ph.a = OpK{A, lda, m0, 0, M, kb};
+    ph.b = OpK{B, ldb, n0, 0, N, kb};
+    return true;
+  };
+  f32x16 acc[C::FM][C::FN];
+  gemm_mainloop<C>(prov, lds, acc);
+  stage_out<C>(lds, acc, bias ? bias + n0 : nullptr, (int)(N - n0));
+  copy_out<C>(lds, Cg + m0 * ldc + n0 * TT<T>::ESZ, ldc, (int)imin64(C::BM, M - m0),
+              (N - n0) * TT<T>::ESZ);
+}
+
+// ===========================================================================
+// S1 (low-rank): [T | L] = X [U_f | P], plus L^T (token-contiguous) for S3
+// ===========================================================================
+
+template <class C>
+__global__ __launch_bounds__(C::NT) void s1_lowrank_kernel(const typename C::elem* X,
+                                                           const typename C::elem* UPt,
+                                                           typename C::elem* TL, typename C::elem* Lt,
+                                                           int64_t n, int64_t c1, int k, int r,
+                                                           int64_t ldt, int tiles_n) {
+  typedef typename C::elem T;
+  constexpr int E = TT<T>::ESZ, KPC = TT<T>::KPC;
+  __shared__ __attribute__((aligned(16))) char lds[C::LDS];
+  const int t = xcd_tile_id(blockIdx.x, gridDim.x);
+  const int64_t m0 = (int64_t)(t / tiles_n) * C::BM, n0 = (int64_t)(t % tiles_n) * C::BN;
+  const int64_t N = k + r;
+  auto prov = [=](int p, Phase& ph) -> bool {
+    if (p != 0) return false;
+    ph.a = OpK{reinterpret_cast<const char*>(X), c1 * E, m0, 0, n, c1 * E};
+    ph.b = OpK{reinterpret_cast<const char*>(UPt), c1 * E, n0, 0, N, c1 * E};
+    return true;
+  };
+  f32x16 acc[C::FM][C::FN];
+  gemm_mainloop<C>(prov, lds, acc);
+  stage_out<C>(lds, acc, nullptr, 0);
+  copy_out<C>(lds, reinterpret_cast<char*>(TL) + (m0 * N + n0) * E, N * E,
+              (int)imin64(C::BM, n - m0), (N - n0) * E);
+  // L columns of this tile, written transposed: Lt[j - k][m0 + rows]
+  const int64_t j0 = imax64(n0, k), j1 = imin64(n0 + C::BN, N);
+  if (j0 < j1) {
+    const int ncol = (int)(j1 - j0);
+    const int groups = C::BM / KPC;
+    for (int c = threadIdx.x; c < ncol * groups; c += C::NT) {
+      const int jl = (int)(j0 - n0) + c / groups, rg = c % groups;
+      const int64_t row = m0 + (int64_t)rg * KPC;
+      if (row >= ldt) continue;
+      T v[KPC];
+#pragma unroll
+      for (int e = 0; e < KPC; ++e) v[e] = staged_elem<C>(lds, rg * KPC + e, jl);
+      *reinterpret_cast<uint4*>(Lt + (n0 + jl - k) * ldt + row) = *reinterpret_cast<const uint4*>(v);
+    }
+  }
+}
+
+// ===========================================================================
+// S6 (low-rank): Y = T V + L R_b + bias, segments handled by row masks
+// ===========================================================================
+
+template <class C>
+__global__ __launch_bounds__(C::NT) void s6_lowrank_kernel(const typename C::elem* TL,
+                                                           const typename C::elem* Vt,
+                                                           const typename C::elem* Rt,
+                                                           const typename C::elem* bias,
+                                                           typename C::elem* Y, int64_t n, int64_t c2,
+                                                           int k, int r, int64_t seg, int64_t B,
+                                                           int tiles_n) {
+  typedef typename C::elem T;
+  constexpr int E = TT<T>::ESZ;
+  __shared__ __attribute__((aligned(16))) char lds[C::LDS];
+  const int t = xcd_tile_id(blockIdx.x, gridDim.x);
+  const int64_t m0 = (int64_t)(t / tiles_n) * C::BM, n0 = (int64_t)(t % tiles_n) * C::BN;
+  const int64_t lda = (int64_t)(k + r) * E;
+  const int64_t bfirst = m0 / seg;
+  const int64_t blast = imin64(B - 1, (imin64(m0 + C::BM, n) - 1) / seg);
+  const char* TLc = reinterpret_cast<const char*>(TL);
+  auto prov = [=](int p, Phase& ph) -> bool {
+    if (p == 0) {
+      ph.a = OpK{TLc, lda, m0, 0, n, (int64_t)k * E};
+      ph.b = OpK{reinterpret_cast<const char*>(Vt), (int64_t)k * E, n0, 0, c2, (int64_t)k * E};
+      return true;
+    }
+    const int64_t b = bfirst + p - 1;
+    if (b > blast) return false;
+    ph.a = OpK{TLc + (int64_t)k * E, lda, m0, b * seg, imin64((b + 1) * seg, n), (int64_t)r * E};
+    ph.b = OpK{reinterpret_cast<const char*>(Rt + b * r), B * r * E, n0, 0, c2, (int64_t)r * E};
+    return true;
+  };
+  f32x16 acc[C::FM][C::FN];
+  gemm_mainloop<C>(prov, lds, acc);
+  stage_out<C>(lds, acc, bias ? bias + n0 : nullptr, (int)(c2 - n0));
+  copy_out<C>(lds, reinterpret_cast<char*>(Y) + (m0 * c2 + n0) * E, c2 * E,
+              (int)imin64(C::BM, n - m0), (c2 - n0) * E);
+}
+
+// ===========================================================================
+// S3: M_b = L_b^T X_b (r x c1) and G_b = L_b^T L_b (r x r), fp32 outputs.
+// The reduction runs over the tokens of one segment inside one workgroup
+// (no atomics, fixed order), double-buffered through LDS.  X arrives
+// token-major, so its tiles are transposed on the way into LDS.
+// ===========================================================================
+
+template <typename T>
+__device__ __forceinline__ uint4 mask_tokens(uint4 v, int64_t t0, int64_t lo, int64_t hi) {
+  constexpr int KPC = TT<T>::KPC;
+  if (t0 >= lo && t0 + KPC <= hi) return v;
+  if (t0 + KPC <= lo || t0 >= hi) return zero4();
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int e = 0; e < KPC; ++e) {
+    const int64_t tt = t0 + e;
+    if (tt < lo || tt >= hi) {
+      if constexpr (KPC == 8) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+      else w[e] = 0u;
+    }
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+template <class C>
+__global__ __launch_bounds__(C::NT) void s3_gram_kernel(const typename C::elem* Lt, int64_t ldt,
+                                                        const typename C::elem* X, int64_t c1, int r,
+                                                        int64_t seg, int64_t n, float* M, float* G,
+                                                        int tiles_r, int tiles_cm, int tiles_cg) {
+  typedef typename C::elem T;
+  constexpr int E = TT<T>::ESZ, KPC = TT<T>::KPC, BKE = 8 * KPC;
+  constexpr int XCH = C::BN / KPC;   // chunks per token row of an X tile
+  static_assert(C::BCH * C::NT == BKE * XCH, "X tile chunks");
+  __shared__ __attribute__((aligned(16))) char lds[C::LDS];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wm = w / C::NWN, wn = w % C::NWN;
+  const int per_seg = tiles_r * (tiles_cm + tiles_cg);
+  const int t = blockIdx.x;
+  const int64_t b = t / per_seg;
+  const int rem = t % per_seg;
+  const int tr = rem / (tiles_cm + tiles_cg), tc = rem % (tiles_cm + tiles_cg);
+  const bool is_g = tc >= tiles_cm;
+  const int p0 = tr * C::BM;
+  const int64_t c0 = (int64_t)(is_g ? tc - tiles_cm : tc) * C::BN;
+  const int64_t lo = b * seg, hi = imin64((b + 1) * seg, n);
+  const int64_t kt0 = lo / BKE, kt1 = (hi + BKE - 1) / BKE;
+
+  f32x16 acc[C::FM][C::FN];
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[fm][fn][v] = 0.f;
+
+  uint4 ra[C::ACH], rb[C::BCH];
+  auto load = [&](int64_t kt) {
+    const int64_t tb = kt * BKE;
+#pragma unroll
+    for (int i = 0; i < C::ACH; ++i) {
+      const int c = tid + i * C::NT;
+      const int row = c >> 3, ch = c & 7;
+      const int64_t t0 = tb + ch * KPC;
+      uint4 v = zero4();
+      if (p0 + row < r && t0 < ldt) v = *reinterpret_cast<const uint4*>(Lt + (p0 + row) * ldt + t0);
+      ra[i] = mask_tokens<T>(v, t0, lo, hi);
+    }
+#pragma unroll
+    for (int i = 0; i < C::BCH; ++i) {
+      const int c = tid + i * C::NT;
+      uint4 v = zero4();
+      if (is_g) {
+        const int row = c >> 3, ch = c & 7;
+        const int64_t t0 = tb + ch * KPC;
+        if (c0 + row < r && t0 < ldt) v = *reinterpret_cast<const uint4*>(Lt + (c0 + row) * ldt + t0);
+        v = mask_tokens<T>(v, t0, lo, hi);
+      } else {
+        const int tok = c / XCH, cc = c % XCH;
+        const int64_t tt = tb + tok, col = c0 + (int64_t)cc * KPC;
+        if (tt >= lo && tt < hi && col < c1) v = *reinterpret_cast<const uint4*>(X + tt * c1 + col);
+      }
+      rb[i] = v;
+    }
+  };
+  auto store = [&](char* stage) {
+#pragma unroll
+    for (int i = 0; i < C::ACH; ++i) {
+      const int c = tid + i * C::NT;
+      *reinterpret_cast<uint4*>(stage + lds_off(c >> 3, c & 7)) = ra[i];
+    }
+    char* bs = stage + C::BM * 128;
+#pragma unroll
+    for (int i = 0; i < C::BCH; ++i) {
+      const int c = tid + i * C::NT;
+      if (is_g) {
+        *reinterpret_cast<uint4*>(bs + lds_off(c >> 3, c & 7)) = rb[i];
+      } else {
+        // token tok, channels cc*KPC .. +KPC-1  ->  rows (channels), column tok
+        const int tok = c / XCH, cc = c % XCH;
+        const T* v = reinterpret_cast<const T*>(&rb[i]);
+#pragma unroll
+        for (int e = 0; e < KPC; ++e) {
+          const int nrow = cc * KPC + e;
+          *reinterpret_cast<T*>(bs + lds_off(nrow, tok / KPC) + (tok % KPC) * E) = v[e];
+        }
+      }
+    }
+  };
+
+  if (kt0 < kt1) {
+    load(kt0);
+    store(lds);
+    __syncthreads();
+    int it = 0;
+    for (int64_t kt = kt0; kt < kt1; ++kt, ++it) {
+      const bool more = kt + 1 < kt1;
+      if (more) load(kt + 1);
+      compute_tile<C>(lds + (it & 1) * C::STAGE, acc, lane, wm, wn);
+      if (!more) break;
+      store(lds + ((it + 1) & 1) * C::STAGE);
+      __syncthreads();
+    }
+  }
+  // write fp32 results (lane: one output row, 4 consecutive columns per q)
+  const int l = lane & 31, g = lane >> 5;
+  const int64_t ncols = is_g ? r : c1;
+  float* out = is_g ? G + b * r * r : M + b * r * c1;
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm) {
+    const int p = p0 + wm * C::WM + fm * 32 + l;
+    if (p >= r) continue;
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t col = c0 + wn * C::WN + fn * 32 + 8 * q + 4 * g;
+        if (col < ncols)
+          *reinterpret_cast<float4*>(out + p * ncols + col) =
+              make_float4(acc[fm][fn][4 * q], acc[fm][fn][4 * q + 1], acc[fm][fn][4 * q + 2],
+                          acc[fm][fn][4 * q + 3]);
+      }
+  }
+}
+
+// ===========================================================================
+// block reductions
+// ===========================================================================
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+template <int NT>
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __syncthreads();
+  if (lane == 0) red[w] = v;
+  __syncthreads();
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) s += red[i];
+  return s;
+}
+
+// ===========================================================================
+// S4a: (G + lambda I)^-1 by the symmetric sweep (Gauss-Jordan) operator.
+// One workgroup per segment; the r x r matrix lives in registers (up to 16
+// elements per thread), the pivot column is broadcast through LDS.
+// Sweeping pivot k maps A to A' with A'_ij = A_ij - A_ik A_kj / A_kk,
+// A'_ik = A_ik / A_kk, A'_kk = -1 / A_kk; after all pivots A = -(A_0)^-1.
+// A pivot <= 0 means the matrix is not positive definite.
+// ===========================================================================
+
+constexpr int SW_NT = 1024;
+constexpr int SW_EPT = 16;   // 128 * 128 / 1024
+
+__global__ __launch_bounds__(SW_NT) void sweep_inverse_kernel(const float* G, float* Ginv, int32_t* status,
+                                                              int r, float eps) {
+  __shared__ float cv[2][128];
+  __shared__ float red[SW_NT / 64];
+  const int64_t b = blockIdx.x;
+  const float* Gb = G + b * r * r;
+  float* Ob = Ginv + b * r * r;
+  const int tid = threadIdx.x;
+  const int rr = r * r;
+  float a[SW_EPT];
+  int ii[SW_EPT], jj[SW_EPT];
+  float tr = 0.f;
+#pragma unroll
+  for (int q = 0; q < SW_EPT; ++q) {
+    const int e = tid + q * SW_NT;
+    ii[q] = e < rr ? e / r : -1;
+    jj[q] = e < rr ? e % r : -1;
+    a[q] = e < rr ? Gb[e] : 0.f;
+    if (e < rr && ii[q] == jj[q]) tr += a[q];
+  }
+  tr = block_sum<SW_NT>(tr, red);
+  int st = DYRA_SOLVE_OK;
+  if (tr == 0.f) st = DYRA_SOLVE_ZERO;
+  else if (!(tr > 0.f) || !isfinite(tr)) st = DYRA_SOLVE_NOT_SPD;
+  if (st == DYRA_SOLVE_OK) {
+    const float lam = eps * tr / (float)r;
+#pragma unroll
+    for (int q = 0; q < SW_EPT; ++q) {
+      if (ii[q] >= 0 && ii[q] == jj[q]) a[q] += lam;
+      if (jj[q] == 0) cv[0][ii[q]] = a[q];
+    }
+    __syncthreads();
+    for (int k = 0; k < r; ++k) {
+      const float* buf = cv[k & 1];
+      const float D = buf[k];
+      if (!(D > 0.f) || !isfinite(D)) {
+        st = DYRA_SOLVE_NOT_SPD;
+        break;
+      }
+      const float invD = 1.f / D;
+      float* nxt = cv[(k + 1) & 1];
+#pragma unroll
+      for (int q = 0; q < SW_EPT; ++q) {
+        const int i = ii[q], j = jj[q];
+        if (i < 0) continue;
+        if (i != k && j != k) a[q] = fmaf(-buf[i] * invD, buf[j], a[q]);
+        else if (i == k && j == k) a[q] = -invD;
+        else a[q] = (i == k ? buf[j] : buf[i]) * invD;
+        if (j == k + 1) nxt[i] = a[q];
+      }
+      __syncthreads();
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < SW_EPT; ++q) {
+    const int e = tid + q * SW_NT;
+    if (e < rr) Ob[e] = st == DYRA_SOLVE_OK ? -a[q] : 0.f;
+  }
+  if (tid == 0) status[b] = st;
+}
+
+// ===========================================================================
+// S4a': Newton-Schulz inverse on fp32 MFMA (one workgroup per segment,
+// 16 waves, each owning one 32x32 block of the 128 x 128 iterate).
+// Jacobi-scaled A' = D^-1/2 (G + lambda I) D^-1/2 (unit diagonal, padded
+// with the identity up to 128); X_0 = I / ||A'||_F;
+// X_{k+1} = X_k (2 I - A' X_k) until ||I - A' X_k||_F <= tol or the error
+// stalls at the fp32 floor; Ginv = D^-1/2 X D^-1/2.
+// ===========================================================================
+
+constexpr int NS_N = 128;
+constexpr int NS_P = 129;   // padded LDS pitch (odd: row-strided reads spread over banks)
+
+__global__ __launch_bounds__(1024) void ns_inverse_kernel(const float* G, float* Ginv, int32_t* status,
+                                                          int r, float eps, int maxit, float tol) {
+  __shared__ float Xs[NS_N * NS_P];
+  __shared__ float Ts[NS_N * NS_P];
+  __shared__ float dsc[NS_N];
+  __shared__ float red[16];
+  const int64_t b = blockIdx.x;
+  const float* Gb = G + b * r * r;
+  float* Ob = Ginv + b * r * r;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l = lane & 31, g = lane >> 5;
+  const int bi = w >> 2, bj = w & 3;
+
+  // trace, ridge and Jacobi scaling
+  const float dv = tid < r ? Gb[tid * r + tid] : 0.f;
+  const float tr = block_sum<1024>(dv, red);
+  const float lam = eps * tr / (float)r;
+  float badf = 0.f;
+  if (tid < NS_N) {
+    const float d = tid < r ? dv + lam : 1.f;
+    dsc[tid] = d > 0.f ? rsqrtf(d) : 0.f;
+    if (!(d > 0.f) || !isfinite(d)) badf = 1.f;
+  }
+  badf = block_sum<1024>(badf, red);   // barrier: dsc complete afterwards
+  int st = DYRA_SOLVE_OK;
+  if (tr == 0.f) st = DYRA_SOLVE_ZERO;
+  else if (!(tr > 0.f) || !isfinite(tr) || badf > 0.f) st = DYRA_SOLVE_NOT_SPD;
+  // A' fragments in registers: Af[s] = A'[bi*32 + l][2s + g]
+  float Af[64];
+  float fro2 = 0.f;
+#pragma unroll
+  for (int s = 0; s < 64; ++s) {
+    const int row = bi * 32 + l, col = 2 * s + g;
+    float v;
+    if (row < r && col < r) v = (Gb[row * r + col] + (row == col ? lam : 0.f)) * dsc[row] * dsc[col];
+    else v = row == col ? 1.f : 0.f;
+    Af[s] = v;
+    if (bj == 0) fro2 += v * v;   // waves with bj == 0 cover every row band once
+  }
+  fro2 = block_sum<1024>(fro2, red);
+  const float x0 = 1.f / sqrtf(fro2);
+  for (int e = tid; e < NS_N * NS_N; e += 1024) {
+    const int i = e / NS_N, j = e % NS_N;
+    Xs[i * NS_P + j] = i == j ? x0 : 0.f;
+  }
+  __syncthreads();
+  float prev = 1e30f;
+  int it = 0;
+  bool ok = st == DYRA_SOLVE_OK;
+  bool converged = false;
+  while (ok && it < maxit) {
+    // T = A' X  (this wave's block)
+    f32x16 acc;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+#pragma unroll
+    for (int s = 0; s < 64; ++s) {
+      const float bx = Xs[(2 * s + g) * NS_P + bj * 32 + l];
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(Af[s], bx, acc, 0, 0, 0);
+    }
+    float e2 = 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int rr = bi * 32 + (v >> 2) * 8 + g * 4 + (v & 3), cc = bj * 32 + l;
+      Ts[rr * NS_P + cc] = acc[v];
+      const float d = (rr == cc ? 1.f : 0.f) - acc[v];
+      e2 += d * d;
+    }
+    e2 = block_sum<1024>(e2, red);   // contains barriers: Ts complete afterwards
+    const float err = sqrtf(e2);
+    if (!isfinite(err)) {
+      ok = false;
+      break;
+    }
+    if (err <= tol) {
+      converged = true;
+      break;
+    }
+    if (err > 0.5f * prev && prev < 1e-2f) {   // stalled at the fp32 floor
+      converged = err < 1e-2f;
+      break;
+    }
+    prev = err;
+    // X <- 2 X - X T
+    f32x16 acc2;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc2[v] = 0.f;
+#pragma unroll
+    for (int s = 0; s < 64; ++s) {
+      const float ax = Xs[(bi * 32 + l) * NS_P + 2 * s + g];
+      const float bt = Ts[(2 * s + g) * NS_P + bj * 32 + l];
+      acc2 = __builtin_amdgcn_mfma_f32_32x32x2f32(ax, bt, acc2, 0, 0, 0);
+    }
+    float xo[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int rr = bi * 32 + (v >> 2) * 8 + g * 4 + (v & 3), cc = bj * 32 + l;
+      xo[v] = Xs[rr * NS_P + cc];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int rr = bi * 32 + (v >> 2) * 8 + g * 4 + (v & 3), cc = bj * 32 + l;
+      Xs[rr * NS_P + cc] = 2.f * xo[v] - acc2[v];
+    }
+    __syncthreads();
+    ++it;
+  }
+  if (ok && !converged && st == DYRA_SOLVE_OK) st = DYRA_SOLVE_NOCONV;
+  if (!ok && st == DYRA_SOLVE_OK) st = DYRA_SOLVE_NOT_SPD;
+  const bool good = st == DYRA_SOLVE_OK || st == DYRA_SOLVE_NOCONV;
+  for (int e = tid; e < r * r; e += 1024) {
+    const int i = e / r, j = e % r;
+    Ob[e] = good ? dsc[i] * Xs[i * NS_P + j] * dsc[j] : 0.f;
+  }
+  if (tid == 0) status[b] = st;
+}
+
+// ===========================================================================
+// S4b: M'_b = Ginv_b M_b  (fp32 arithmetic, stored as T for the S5 GEMM)
+// ===========================================================================
+
+template <typename T>
+__global__ __launch_bounds__(256) void apply_inverse_kernel(const float* Ginv, const float* M, T* Mp, int r,
+                                                            int64_t c1) {
+  __shared__ float Gs[128 * 128];
+  __shared__ float Ms[128 * 64];
+  const int64_t tiles = (c1 + 63) / 64;
+  const int64_t b = blockIdx.x / tiles;
+  const int64_t c0 = (blockIdx.x % tiles) * 64;
+  const int tid = threadIdx.x;
+  const float* Gb = Ginv + b * r * r;
+  const float* Mb = M + b * r * c1;
+  for (int e = tid; e < r * r; e += 256) Gs[e] = Gb[e];
+  for (int e = tid; e < r * 64; e += 256) {
+    const int q = e / 64, c = e % 64;
+    Ms[e] = c0 + c < c1 ? Mb[q * c1 + c0 + c] : 0.f;
+  }
+  __syncthreads();
+  const int c = tid & 63;
+  if (c0 + c >= c1) return;
+  for (int p = tid >> 6; p < r; p += 4) {
+    float s = 0.f;
+    for (int q = 0; q < r; ++q) s = fmaf(Gs[p * r + q], Ms[q * 64 + c], s);
+    Mp[(b * r + p) * c1 + c0 + c] = TT<T>::from_f(s);
+  }
+}
+
+// ===========================================================================
+// host-side launch helpers
+// ===========================================================================
+
+typedef GemmCfg<bf16_t, 128, 128, 2, 2> CfgB;   // bf16 GEMMs
+typedef GemmCfg<float, 64, 64, 2, 2> CfgF;      // fp32 GEMMs
+typedef GemmCfg<bf16_t, 64, 128, 2, 2> CfgB3;   // S3, bf16
+typedef GemmCfg<float, 64, 64, 2, 2> CfgF3;     // S3, fp32
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+template <class C>
+void launch_gemm_tn(const void* A, int64_t lda_el, const void* B, int64_t ldb_el, void* Cm, int64_t ldc_el,
+                    int64_t M, int64_t N, int64_t K, const void* bias, hipStream_t st) {
+  typedef typename C::elem T;
+  const int tiles_n = (int)cdiv(N, C::BN);
+  const int64_t tiles = cdiv(M, C::BM) * tiles_n;
+  if (tiles <= 0) return;
+  hipLaunchKernelGGL(gemm_tn_kernel<C>, dim3((unsigned)tiles), dim3(C::NT), 0, st,
+                     reinterpret_cast<const char*>(A), lda_el * TT<T>::ESZ, reinterpret_cast<const char*>(B),
+                     ldb_el * TT<T>::ESZ, reinterpret_cast<char*>(Cm), ldc_el * TT<T>::ESZ, M, N, K,
+                     reinterpret_cast<const T*>(bias), tiles_n);
+}
+
+inline int64_t lt_pitch(int64_t n) { return cdiv(n, 256) * 256; }
+
+template <class C, class C3>
+int forward_lowrank(const dyra_spec& s, const char* plan, const void* X, const void* bias, void* Y,
+                    int64_t B, int64_t seg, float eps, int solver, char* ws, hipStream_t st) {
+  typedef typename C::elem T;
+  const int dtype = TT<T>::ESZ == 2 ? DYRA_BF16 : DYRA_F32;
+  const PlanLayout PL = plan_layout(s, dtype);
+  const WsLayout WL = ws_layout(s, B, seg, dtype);
+  const int64_t n = B * seg, c1 = s.c1, c2 = s.c2;
+  const int k = s.k, r = s.r;
+  const T* UPt = reinterpret_cast<const T*>(plan + PL.UPt);
+  const T* Vt = reinterpret_cast<const T*>(plan + PL.Vt);
+  const T* Wrt = reinterpret_cast<const T*>(plan + PL.Wrt);
+  T* TL = reinterpret_cast<T*>(ws + WL.A);
+  T* Lt = reinterpret_cast<T*>(ws + WL.Lt);
+  float* G = reinterpret_cast<float*>(ws + WL.G);
+  float* M = reinterpret_cast<float*>(ws + WL.M);
+  float* Gi = reinterpret_cast<float*>(ws + WL.Ginv);
+  T* Mp = reinterpret_cast<T*>(ws + WL.Mp);
+  T* Rt = reinterpret_cast<T*>(ws + WL.Rt);
+  int32_t* stat = reinterpret_cast<int32_t*>(ws + WL.status);
+  const int64_t ldt = lt_pitch(n);
+
+  {  // S1
+    const int tiles_n = (int)cdiv(k + r, C::BN);
+    const int64_t tiles = cdiv(n, C::BM) * tiles_n;
+    hipLaunchKernelGGL(s1_lowrank_kernel<C>, dim3((unsigned)tiles), dim3(C::NT), 0, st,
+                       reinterpret_cast<const T*>(X), UPt, TL, Lt, n, c1, k, r, ldt, tiles_n);
+  }
+  {  // S3
+    const int tr = (int)cdiv(r, C3::BM), tcm = (int)cdiv(c1, C3::BN), tcg = (int)cdiv(r, C3::BN);
+    const int64_t grid = B * tr * (tcm + tcg);
+    hipLaunchKernelGGL(s3_gram_kernel<C3>, dim3((unsigned)grid), dim3(C3::NT), 0, st, Lt, ldt,
+                       reinterpret_cast<const T*>(X), c1, r, seg, n, M, G, tr, tcm, tcg);
+  }
+  {  // S4
+    const bool ns = solver == DYRA_SOLVER_NS || (solver == DYRA_SOLVER_AUTO && r >= 128);
+    if (ns)
+      hipLaunchKernelGGL(ns_inverse_kernel, dim3((unsigned)B), dim3(1024), 0, st, G, Gi, stat, r, eps, 60,
+                         2e-6f);
+    else
+      hipLaunchKernelGGL(sweep_inverse_kernel, dim3((unsigned)B), dim3(SW_NT), 0, st, G, Gi, stat, r, eps);
+    hipLaunchKernelGGL(apply_inverse_kernel<T>, dim3((unsigned)(cdiv(c1, 64) * B)), dim3(256), 0, st,
+                       Gi, M, Mp, r, c1);
+  }
+  // S5: Rt (c2 x B r) = Wrt (c2 x c1) . Mp (B r x c1)^T
+  launch_gemm_tn<C>(Wrt, c1, Mp, c1, Rt, B * r, c2, B * r, c1, nullptr, st);
+  {  // S6
+    const int tiles_n = (int)cdiv(c2, C::BN);
+    const int64_t tiles = cdiv(n, C::BM) * tiles_n;
+    hipLaunchKernelGGL(s6_lowrank_kernel<C>, dim3((unsigned)tiles), dim3(C::NT), 0, st, TL, Vt, Rt,
+                       reinterpret_cast<const T*>(bias), reinterpret_cast<T*>(Y), n, c2, k, r, seg, B,
+                       tiles_n);
+  }
+  return hipGetLastError() == hipSuccess ? DYRA_OK : DYRA_EHIP;
+}
+
+int check_forward_args(const dyra_spec* spec, const void* plan, const void* X, void* Y, int64_t B, int64_t s,
+                       int32_t dtype, float eps, int32_t solver, void* ws, size_t ws_bytes) {
+  if (!spec || !plan || !X || !Y || !ws) return DYRA_EINVAL;
+  int rc = validate_spec(spec);
+  if (rc) return rc;
+  rc = validate_dtype(*spec, dtype);
+  if (rc) return rc;
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return DYRA_EINVAL;
+  if (solver < DYRA_SOLVER_AUTO || solver > DYRA_SOLVER_NS) return DYRA_EINVAL;
+  if (B <= 0 || s <= 0 || B >= ((int64_t)1 << 31) || s >= ((int64_t)1 << 31)) return DYRA_ESHAPE;
+  if (B * s >= ((int64_t)1 << 31)) return DYRA_ESHAPE;
+  if ((reinterpret_cast<uintptr_t>(plan) | reinterpret_cast<uintptr_t>(X) | reinterpret_cast<uintptr_t>(Y) |
+       reinterpret_cast<uintptr_t>(ws)) & 15)
+    return DYRA_EINVAL;
+  if (ws_bytes < ws_layout(*spec, B, s, dtype).total) return DYRA_EWORKSPACE;
+  if (spec->kind != DYRA_LOWRANK) return DYRA_EDTYPE;
+  return DYRA_OK;
+}
+
+}  // namespace
+
+extern "C" int dyra_workspace_size(const dyra_spec* spec, int64_t B, int64_t s, int32_t dtype, size_t* bytes) {
+  if (!spec || !bytes) return DYRA_EINVAL;
+  int rc = validate_spec(spec);
+  if (rc) return rc;
+  rc = validate_dtype(*spec, dtype);
+  if (rc) return rc;
+  if (B <= 0 || s <= 0 || B * s >= ((int64_t)1 << 31)) return DYRA_ESHAPE;
+  *bytes = ws_layout(*spec, B, s, dtype).total;
+  return DYRA_OK;
+}
+
+extern "C" int dyra_forward(const dyra_spec* spec, const void* plan, const void* X, const void* bias, void* Y,
+                            int64_t B, int64_t s, int32_t dtype, float ridge_eps, int32_t solver,
+                            void* workspace, size_t ws_bytes, void* stream) {
+  int rc = check_forward_args(spec, plan, X, Y, B, s, dtype, ridge_eps, solver, workspace, ws_bytes);
+  if (rc) return rc;
+  if (bias && (reinterpret_cast<uintptr_t>(bias) & 15)) return DYRA_EINVAL;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const char* plan_c = reinterpret_cast<const char*>(plan);
+  char* ws = reinterpret_cast<char*>(workspace);
+  if (dtype == DYRA_BF16)
+    return forward_lowrank<CfgB, CfgB3>(*spec, plan_c, X, bias, Y, B, s, ridge_eps, solver, ws, st);
+  return forward_lowrank<CfgF, CfgF3>(*spec, plan_c, X, bias, Y, B, s, ridge_eps, solver, ws, st);
+}
+
+extern "C" int dyra_solver_status(const dyra_spec* spec, const void* workspace, int64_t B, int64_t s,
+                                  int32_t dtype, int32_t* host_out, void* stream) {
+  if (!spec || !workspace || !host_out) return DYRA_EINVAL;
+  int rc = validate_spec(spec);
+  if (rc) return rc;
+  rc = validate_dtype(*spec, dtype);
+  if (rc) return rc;
+  if (B <= 0 || s <= 0) return DYRA_ESHAPE;
+  const WsLayout WL = ws_layout(*spec, B, s, dtype);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(host_out, reinterpret_cast<const char*>(workspace) + WL.status, (size_t)B * 4,
+                     hipMemcpyDeviceToHost, st) != hipSuccess)
+    return DYRA_EHIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return DYRA_EHIP;
+  return DYRA_OK;
+}
+
+extern "C" int dyra_dense_ref(const void* X, const void* Wt, const void* bias, void* Y, int64_t n, int64_t c1,
+                              int64_t c2, int32_t dtype, void* stream) {
+  if (!X || !Wt || !Y) return DYRA_EINVAL;
+  if (dtype != DYRA_F32 && dtype != DYRA_BF16) return DYRA_EINVAL;
+  if (n <= 0 || c1 <= 0 || c2 <= 0 || c1 % 8 || c2 % 8 || n >= ((int64_t)1 << 31)) return DYRA_ESHAPE;
+  if ((reinterpret_cast<uintptr_t>(X) | reinterpret_cast<uintptr_t>(Wt) | reinterpret_cast<uintptr_t>(Y) |
+       reinterpret_cast<uintptr_t>(bias)) & 15)
+    return DYRA_EINVAL;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (dtype == DYRA_BF16) launch_gemm_tn<CfgB>(X, c1, Wt, c1, Y, c2, n, c2, c1, bias, st);
+  else launch_gemm_tn<CfgF>(X, c1, Wt, c1, Y, c2, n, c2, c1, bias, st);
+  return hipGetLastError() == hipSuccess ? DYRA_OK : DYRA_EHIP;
+}

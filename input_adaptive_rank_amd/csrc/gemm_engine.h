@@ -1,0 +1,243 @@
+// MFMA GEMM engine for gfx950: C[BM x BN] tile += sum over phases of
+// A_phase[BM x K_phase] * B_phase[BN x K_phase]^T, every operand contiguous
+// along its reduction axis ("TN" layout).  A phase sequence lets one tile
+// accumulate products with different operands (e.g. T V + L R_b for several
+// segments b) through one software pipeline:
+//   global -> registers (tile t+1)  ||  LDS -> MFMA (tile t)  -> LDS (t+1)
+// with double-buffered, XOR-swizzled LDS stages and one barrier per k-tile.
+// The MFMA is issued with the operands swapped so each lane ends up holding
+// four consecutive output columns of one output row; the epilogue stages the
+// tile through LDS and writes 16-byte coalesced rows.
+#pragma once
+
+#include "device_common.h"
+
+// One K-contiguous operand of a phase: tile rows [row0, row0 + tile) of a
+// row-major matrix; rows outside [row_lo, row_hi) and bytes at or beyond
+// kbytes along k read as zero.  kbytes is a multiple of 16.
+struct OpK {
+  const char* ptr;   // byte address of (row 0, k 0)
+  int64_t ld;        // bytes between rows
+  int64_t row0, row_lo, row_hi;
+  int64_t kbytes;
+};
+
+struct Phase {
+  OpK a, b;
+};
+
+template <typename T, int BM_, int BN_, int NWM_, int NWN_>
+struct GemmCfg {
+  typedef T elem;
+  static constexpr int BM = BM_, BN = BN_, NWM = NWM_, NWN = NWN_;
+  static constexpr int NT = NWM * NWN * 64;
+  static constexpr int WM = BM / NWM, WN = BN / NWN;
+  static constexpr int FM = WM / 32, FN = WN / 32;
+  static constexpr int ACH = BM * 8 / NT, BCH = BN * 8 / NT;
+  static constexpr int STAGE = (BM + BN) * 128;
+  static constexpr int LDS_OPS = 2 * STAGE;
+  static constexpr int CPR = BN * TT<T>::ESZ / 16;
+  static constexpr int LDS_OUT = BM * CPR * 16;
+  static constexpr int LDS = LDS_OPS > LDS_OUT ? LDS_OPS : LDS_OUT;
+  static_assert(ACH * NT == BM * 8, "A tile chunks must divide over the threads");
+  static_assert(BCH * NT == BN * 8, "B tile chunks must divide over the threads");
+  static_assert(FM * 32 == WM && FN * 32 == WN, "wave tile must be a multiple of 32x32");
+  static_assert(CPR % 8 == 0, "output row must be a multiple of 128 bytes");
+};
+
+template <class C>
+struct TileRegs {
+  uint4 a[C::ACH];
+  uint4 b[C::BCH];
+};
+
+__device__ __forceinline__ uint4 load_opk(const OpK& o, int row, int64_t kb) {
+  const int64_t grow = o.row0 + row;
+  const bool ok = grow >= o.row_lo && grow < o.row_hi && kb < o.kbytes;
+  return ok ? *reinterpret_cast<const uint4*>(o.ptr + grow * o.ld + kb) : zero4();
+}
+
+template <class C>
+__device__ __forceinline__ void load_tile(const Phase& ph, int kt, TileRegs<C>& r, int tid) {
+  const int64_t kb = (int64_t)kt * 128;
+#pragma unroll
+  for (int i = 0; i < C::ACH; ++i) {
+    const int c = tid + i * C::NT;
+    r.a[i] = load_opk(ph.a, c >> 3, kb + (c & 7) * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < C::BCH; ++i) {
+    const int c = tid + i * C::NT;
+    r.b[i] = load_opk(ph.b, c >> 3, kb + (c & 7) * 16);
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void store_tile(char* stage, const TileRegs<C>& r, int tid) {
+#pragma unroll
+  for (int i = 0; i < C::ACH; ++i) {
+    const int c = tid + i * C::NT;
+    *reinterpret_cast<uint4*>(stage + lds_off(c >> 3, c & 7)) = r.a[i];
+  }
+  char* bs = stage + C::BM * 128;
+#pragma unroll
+  for (int i = 0; i < C::BCH; ++i) {
+    const int c = tid + i * C::NT;
+    *reinterpret_cast<uint4*>(bs + lds_off(c >> 3, c & 7)) = r.b[i];
+  }
+}
+
+// acc[fm][fn] (a 32x32 block, transposed in the lanes) += A_blk * B_blk^T over
+// one 128-byte k-tile held in `stage`.
+template <class C>
+__device__ __forceinline__ void compute_tile(const char* stage, f32x16 (&acc)[C::FM][C::FN], int lane,
+                                             int wm, int wn) {
+  typedef typename C::elem T;
+  const char* as = stage;
+  const char* bs = stage + C::BM * 128;
+  const int l = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    uint4 af[C::FM], bfr[C::FN];
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm) {
+      const int row = wm * C::WM + fm * 32 + l;
+      af[fm] = *reinterpret_cast<const uint4*>(as + lds_off(row, 2 * ks + g));
+    }
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn) {
+      const int row = wn * C::WN + fn * 32 + l;
+      bfr[fn] = *reinterpret_cast<const uint4*>(bs + lds_off(row, 2 * ks + g));
+    }
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn) TT<T>::mma(acc[fm][fn], bfr[fn], af[fm]);
+  }
+}
+
+// Walks the phases of a tile, k-tile by k-tile.  Prov is a functor
+// bool(int p, Phase&) that fills phase p or returns false when there is none.
+template <class Prov>
+struct Cursor {
+  Phase ph;
+  int p, kt, nkt;
+  bool valid;
+  __device__ __forceinline__ void settle(const Prov& prov) {
+    while (valid) {
+      nkt = (int)((ph.a.kbytes + 127) >> 7);
+      if (kt < nkt) break;
+      ++p;
+      kt = 0;
+      valid = prov(p, ph);
+    }
+  }
+  __device__ __forceinline__ void init(const Prov& prov) {
+    p = 0;
+    kt = 0;
+    nkt = 0;
+    valid = prov(0, ph);
+    settle(prov);
+  }
+  __device__ __forceinline__ void advance(const Prov& prov) {
+    ++kt;
+    settle(prov);
+  }
+};
+
+template <class C, class Prov>
+__device__ __forceinline__ void gemm_mainloop(const Prov& prov, char* lds, f32x16 (&acc)[C::FM][C::FN]) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wm = w / C::NWN, wn = w % C::NWN;
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[fm][fn][v] = 0.f;
+  Cursor<Prov> cur;
+  cur.init(prov);
+  if (!cur.valid) return;
+  TileRegs<C> r;
+  load_tile<C>(cur.ph, cur.kt, r, tid);
+  store_tile<C>(lds, r, tid);
+  __syncthreads();
+  int it = 0;
+  for (;;) {
+    Cursor<Prov> nxt = cur;
+    nxt.advance(prov);
+    if (nxt.valid) load_tile<C>(nxt.ph, nxt.kt, r, tid);
+    compute_tile<C>(lds + (it & 1) * C::STAGE, acc, lane, wm, wn);
+    if (!nxt.valid) break;
+    store_tile<C>(lds + ((it + 1) & 1) * C::STAGE, r, tid);
+    __syncthreads();
+    cur = nxt;
+    ++it;
+  }
+}
+
+// Writes acc (+ bias[col] when bias != nullptr; bias points at the tile's
+// first column and holds bias_n valid entries) into the LDS staging tile as T.
+template <class C>
+__device__ __forceinline__ void stage_out(char* lds, const f32x16 (&acc)[C::FM][C::FN],
+                                          const typename C::elem* bias, int bias_n) {
+  typedef typename C::elem T;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wm = w / C::NWN, wn = w % C::NWN;
+  const int l = lane & 31, g = lane >> 5;
+  __syncthreads();
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm) {
+    const int row = wm * C::WM + fm * 32 + l;
+    char* rowp = lds + row * (C::CPR * 16);
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int col = wn * C::WN + fn * 32 + 8 * q + 4 * g;
+        float v0 = acc[fm][fn][4 * q + 0], v1 = acc[fm][fn][4 * q + 1];
+        float v2 = acc[fm][fn][4 * q + 2], v3 = acc[fm][fn][4 * q + 3];
+        if (bias != nullptr && col < bias_n) {
+          v0 += TT<T>::to_f(bias[col + 0]);
+          v1 += TT<T>::to_f(bias[col + 1]);
+          v2 += TT<T>::to_f(bias[col + 2]);
+          v3 += TT<T>::to_f(bias[col + 3]);
+        }
+        if constexpr (TT<T>::ESZ == 2) {
+          uint2 pk;
+          pk.x = (uint32_t)f2bf(v0) | ((uint32_t)f2bf(v1) << 16);
+          pk.y = (uint32_t)f2bf(v2) | ((uint32_t)f2bf(v3) << 16);
+          const int chunk = col >> 3;
+          *reinterpret_cast<uint2*>(rowp + stage_chunk(row, chunk) * 16 + (col & 4) * 2) = pk;
+        } else {
+          const int chunk = col >> 2;
+          *reinterpret_cast<float4*>(rowp + stage_chunk(row, chunk) * 16) = make_float4(v0, v1, v2, v3);
+        }
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// Copies the staged tile to global rows: dst = byte address of the tile's
+// (0, 0) element, ldb = bytes between rows; rows >= rows_valid and bytes >=
+// colbytes_valid are not written.
+template <class C>
+__device__ __forceinline__ void copy_out(const char* lds, char* dst, int64_t ldb, int rows_valid,
+                                         int64_t colbytes_valid) {
+  for (int c = threadIdx.x; c < C::BM * C::CPR; c += C::NT) {
+    const int row = c / C::CPR, ch = c % C::CPR;
+    if (row < rows_valid && (int64_t)ch * 16 < colbytes_valid) {
+      *reinterpret_cast<uint4*>(dst + row * ldb + ch * 16) =
+          *reinterpret_cast<const uint4*>(lds + row * (C::CPR * 16) + stage_chunk(row, ch) * 16);
+    }
+  }
+}
+
+// Reads element (row, col) of the staged tile.
+template <class C>
+__device__ __forceinline__ typename C::elem staged_elem(const char* lds, int row, int col) {
+  typedef typename C::elem T;
+  const int byte = col * TT<T>::ESZ;
+  return *reinterpret_cast<const T*>(lds + row * (C::CPR * 16) + stage_chunk(row, byte >> 4) * 16 + (byte & 15));
+}

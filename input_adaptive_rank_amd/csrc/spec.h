@@ -1,0 +1,140 @@
+// Shared host-side helpers: spec validation and the byte layouts of the
+// packed device plan and of the forward workspace.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/dyra.h"
+
+namespace dyra_spec_util {
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+inline size_t elem_bytes(int dtype) { return dtype == DYRA_BF16 ? 2 : 4; }
+
+// Validates a spec (and optionally a dtype).  Returns DYRA_OK or an error.
+inline int validate_spec(const dyra_spec* sp) {
+  if (!sp) return DYRA_EINVAL;
+  const dyra_spec& s = *sp;
+  if (s.c1 <= 0 || s.c2 <= 0 || s.r <= 0) return DYRA_ESHAPE;
+  if (s.c1 % 8 || s.c2 % 8 || s.r % 8) return DYRA_ESHAPE;
+  if (s.r > 128) return DYRA_ESHAPE;
+  const int64_t mn = s.c1 < s.c2 ? s.c1 : s.c2;
+  if (s.r > mn) return DYRA_ESHAPE;
+  if (s.c1 > (int64_t)1 << 24 || s.c2 > (int64_t)1 << 24) return DYRA_ESHAPE;
+  switch (s.kind) {
+    case DYRA_LOWRANK:
+      if (s.k <= 0 || s.k % 8 || s.k + s.r > mn) return DYRA_ESHAPE;
+      break;
+    case DYRA_MONARCH:
+      if (s.mblk <= 0 || s.c1 != s.c2 || s.c1 != (int64_t)s.mblk * s.mblk) return DYRA_ESHAPE;
+      break;
+    case DYRA_BLAST:
+      if (s.nb <= 0 || s.rb <= 0 || s.c1 % s.nb || s.c2 % s.nb) return DYRA_ESHAPE;
+      if (s.rb > s.c1 / s.nb || s.rb > s.c2 / s.nb) return DYRA_ESHAPE;
+      break;
+    default:
+      return DYRA_EINVAL;
+  }
+  return DYRA_OK;
+}
+
+// Structures / dtypes the device path implements.
+inline int validate_dtype(const dyra_spec& s, int dtype) {
+  if (dtype != DYRA_F32 && dtype != DYRA_BF16) return DYRA_EINVAL;
+  if (s.kind == DYRA_MONARCH) {
+    if (dtype != DYRA_BF16 || s.mblk != 32) return DYRA_EDTYPE;
+  }
+  if (s.kind == DYRA_BLAST) {
+    if (dtype != DYRA_BF16 || s.rb % 32 || (s.c1 / s.nb) % 32 || (s.c2 / s.nb) % 32) return DYRA_EDTYPE;
+  }
+  return DYRA_OK;
+}
+
+// ---- packed device plan --------------------------------------------------
+// low-rank : UPt [(k+r) x c1] ([U | P]^T), Vt [c2 x k] (V^T), Wrt [c2 x c1] (W_res^T)
+// Monarch  : B1t [m][m][m] (B1t[a][j][i] = B1[a][i][j]), Pt [r x c],
+//            B2t [m][m][m] (B2t[j][l][a] = B2[j][a][l]), Wrt [c x c]
+// BLAST    : Ubt [nb][rb][c1/nb] (U_i^T), Pt [r x c1],
+//            St [(nb rb) x (nb rb)] (St[j rb + q][i rb + p] = S[i][j][p][q]),
+//            Vb [nb][c2/nb][rb] (as prepared), Wrt [c2 x c1]
+struct PlanLayout {
+  size_t UPt = 0, Vt = 0, B1t = 0, B2t = 0, Pt = 0, Ubt = 0, St = 0, Vb = 0, Wrt = 0;
+  size_t total = 0;
+};
+
+inline PlanLayout plan_layout(const dyra_spec& s, int dtype) {
+  PlanLayout L;
+  const size_t e = elem_bytes(dtype);
+  size_t off = 0;
+  auto take = [&](size_t elems) {
+    size_t o = off;
+    off = align256(off + elems * e);
+    return o;
+  };
+  const size_t c1 = (size_t)s.c1, c2 = (size_t)s.c2, r = (size_t)s.r;
+  if (s.kind == DYRA_LOWRANK) {
+    L.UPt = take(((size_t)s.k + r) * c1);
+    L.Vt = take(c2 * (size_t)s.k);
+  } else if (s.kind == DYRA_MONARCH) {
+    const size_t m = (size_t)s.mblk;
+    L.B1t = take(m * m * m);
+    L.Pt = take(r * c1);
+    L.B2t = take(m * m * m);
+  } else {
+    const size_t nb = (size_t)s.nb, rb = (size_t)s.rb;
+    L.Ubt = take(nb * rb * (c1 / nb));
+    L.Pt = take(r * c1);
+    L.St = take(nb * rb * nb * rb);
+    L.Vb = take(nb * (c2 / nb) * rb);
+  }
+  L.Wrt = take(c2 * c1);
+  L.total = off;
+  return L;
+}
+
+// ---- forward workspace -----------------------------------------------------
+// A    [n x wa]   stage-1 output: low-rank [T | L] (wa = k + r); Monarch
+//                 [V | L] (wa = c + r, V the permuted stage-1 output);
+//                 BLAST [Z | L] (wa = nb rb + r)
+// Wp   [n x nb rb] BLAST coupled output Z S (BLAST only)
+// Lt   [r x n256] L transposed (token-contiguous, pitch n rounded up to 256)
+// G    [B x r x r] fp32, M [B x r x c1] fp32, Ginv [B x r x r] fp32
+// Mp   [B x r x c1] dtype: (G + lambda I)^-1 M
+// Rt   [c2 x B r] dtype: R_b^T for every segment, R_b = Mp_b W_res
+// status [B] int32
+struct WsLayout {
+  int64_t wa = 0;
+  size_t A = 0, Wp = 0, Lt = 0, G = 0, M = 0, Ginv = 0, Mp = 0, Rt = 0, status = 0;
+  size_t total = 0;
+};
+
+inline WsLayout ws_layout(const dyra_spec& s, int64_t B, int64_t seg, int dtype) {
+  WsLayout W;
+  const size_t e = elem_bytes(dtype);
+  const size_t n = (size_t)(B * seg), r = (size_t)s.r, c1 = (size_t)s.c1, c2 = (size_t)s.c2;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  int64_t stat = 0;
+  if (s.kind == DYRA_LOWRANK) stat = s.k;
+  else if (s.kind == DYRA_MONARCH) stat = s.c2;
+  else stat = (int64_t)s.nb * s.rb;
+  W.wa = stat + s.r;
+  W.A = take(n * (size_t)W.wa * e);
+  if (s.kind == DYRA_BLAST) W.Wp = take(n * (size_t)stat * e);
+  W.Lt = take(r * ((n + 255) / 256 * 256) * e);   // token pitch padded to 256
+  W.G = take((size_t)B * r * r * 4);
+  W.M = take((size_t)B * r * c1 * 4);
+  W.Ginv = take((size_t)B * r * r * 4);
+  W.Mp = take((size_t)B * r * c1 * e);
+  W.Rt = take(c2 * (size_t)B * r * e);
+  W.status = take((size_t)B * 4);
+  W.total = off;
+  return W;
+}
+
+}  // namespace dyra_spec_util

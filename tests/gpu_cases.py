@@ -1,0 +1,79 @@
+"""Shared helpers for the GPU parity tests: build a case from the seeded
+generator, prepare it with the oracle, run the library on the GPU through the
+C-ABI and compare with the oracle forward on the same storage-rounded inputs
+and factors."""
+from __future__ import annotations
+
+import sys
+import time
+
+import numpy as np
+
+from input_adaptive_rank_amd import dyra as D
+from input_adaptive_rank_amd import synth
+from oracle import dyra_oracle as O
+
+TOL = {synth.DT_F32: 1e-4, synth.DT_BF16: 2e-2}
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def oracle_prepare(w, W):
+    return O.prepare(W, w.kind, w.r, k=w.k, mblk=w.mblk, nb=w.nb, rb=w.rb)
+
+
+def host_factors_from_oracle(prep) -> dict:
+    st = prep["static"]
+    f = {"P": prep["P"], "R0": prep["R0"], "Wres": prep["W_res"], "res_sv": prep["res_sv"]}
+    if prep["kind"] == O.KIND_LOWRANK:
+        f.update(U=st["U"], V=st["V"])
+    elif prep["kind"] == O.KIND_MONARCH:
+        f.update(B1=st["B1"], B2=st["B2"])
+    else:
+        f.update(Ub=st["U"], Vb=st["V"], S=st["S"])
+    return f
+
+
+def rounded_prep(prep, dtype):
+    """The oracle's prepared factors rounded to storage precision, i.e. the
+    exact values the device plan holds."""
+    rnd = lambda a: synth.round_storage(a, dtype)
+    st = {k: rnd(v) for k, v in prep["static"].items() if k != "sv"}
+    return dict(prep, static=st, P=rnd(prep["P"]), W_res=rnd(prep["W_res"]))
+
+
+def gpu_forward(w, factors, X, bias, eps=1e-6, solver="auto", repeat=1):
+    import torch
+    layer = D.DyraLayer(D.spec_of(w), factors, w.dtype, bias=bias, eps=eps, solver=D.SOLVERS[solver])
+    Xd = D.to_device(X, w.dtype)
+    outs = []
+    for _ in range(repeat):
+        Y = layer.forward(Xd, w.B, w.s)
+        torch.cuda.synchronize()
+        outs.append(Y.float().cpu().numpy().astype(np.float64))
+    status = layer.status(w.B, w.s)
+    return outs, status
+
+
+def run_same_factor_case(w, eps=1e-6, solver="auto", tol=None, inputs=None, prep=None):
+    """Same-factor parity: GPU forward vs oracle forward on identical inputs
+    and identical (rounded) factors.  Returns (err, status, Y_gpu, Y_oracle)."""
+    t0 = time.time()
+    inp = inputs if inputs is not None else synth.make_inputs(w)
+    if prep is None:
+        prep = oracle_prepare(w, inp.W)
+    rp = rounded_prep(prep, w.dtype)
+    Y_or = O.forward(inp.X, rp, inp.bias, w.B, w.s, eps=eps)
+    t1 = time.time()
+    (Yg,), status = gpu_forward(w, host_factors_from_oracle(prep), inp.X, inp.bias, eps=eps, solver=solver)
+    err = O.rel_fro(Yg, Y_or)
+    log(f"  case {w.name} B={w.B} s={w.s} c1={w.c1} c2={w.c2} r={w.r} k={w.k} dtype={w.dtype} "
+        f"solver={solver}: rel_fro={err:.3e} status={np.unique(status).tolist()} "
+        f"(oracle {t1 - t0:.1f}s, gpu {time.time() - t1:.1f}s)")
+    tol = TOL[w.dtype] if tol is None else tol
+    assert np.all(np.isfinite(Yg)), "non-finite output"
+    assert err <= tol, f"rel_fro {err} > {tol}"
+    return err, status, Yg, Y_or

@@ -1,0 +1,122 @@
+"""GPU parity of the low-rank DyRA forward against the float64 oracle, through
+the C-ABI.  Bars: relative Frobenius error <= 1e-4 (fp32) / 2e-2 (bf16 with
+fp32 accumulation) on the same seeded inputs and the same storage-rounded
+factors.  Run on an MI355X: pytest -m gpu."""
+import numpy as np
+import pytest
+
+from input_adaptive_rank_amd import dyra as D
+from input_adaptive_rank_amd import synth
+from oracle import dyra_oracle as O
+
+from gpu_cases import TOL, gpu_forward, log, oracle_prepare, rounded_prep, run_same_factor_case
+
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS
+sc = synth.scaled
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    D.lib()
+
+
+SMALL = [
+    W["tiny_fp32"],
+    sc(W["vitb_fc1"], name="ragged_bf16", B=3, s=77, c1=192, c2=200, k=24, r=16),
+    sc(W["vitb_fc1"], name="ragged_fp32", B=3, s=77, c1=192, c2=200, k=24, r=16, dtype=synth.DT_F32),
+    sc(W["vitb_fc1"], name="one_small_tile", B=1, s=20, c1=64, c2=64, k=8, r=8),
+    sc(W["vitb_fc1"], name="many_short_segments", B=37, s=13, c1=128, c2=136, k=16, r=8),
+    sc(W["vitb_fc1"], name="wide_k", B=2, s=300, c1=512, c2=256, k=200, r=56),
+    sc(W["vitl_fc1"], name="r128_ns", B=2, s=300, c1=256, c2=384, k=64, r=128, solver="ns"),
+]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
+def test_small_cases(w):
+    run_same_factor_case(w, solver=w.solver)
+
+
+@pytest.mark.parametrize("solver", ["chol", "ns"])
+def test_solver_choice_r64(solver):
+    w = sc(W["vitl_fc1"], name=f"r64_{solver}", B=4, s=257, c1=256, c2=512, k=64, r=64)
+    err, status, _, _ = run_same_factor_case(w, solver=solver)
+    assert np.all(status == D.SOLVE_OK)
+
+
+def test_segment_shorter_than_rank():
+    """s < r: L_b is rank deficient, G_b singular; the ridge keeps it SPD."""
+    w = sc(W["vitb_fc1"], name="s_lt_r", B=6, s=5, c1=128, c2=128, k=16, r=16)
+    run_same_factor_case(w, eps=1e-3)
+
+
+@pytest.mark.parametrize("name", ["vitb_fc1", "vitl_fc1"])
+def test_full_size(name):
+    w = W[name]
+    err, status, _, _ = run_same_factor_case(w)
+    assert np.all(status == D.SOLVE_OK)
+
+
+def test_zero_residual_gives_static_output_and_zero_status():
+    """W of exact rank k: P = W_res = 0, so G_b = 0, status ZERO and
+    Y = X W_hat + bias."""
+    rng = np.random.default_rng(11)
+    w = sc(W["vitb_fc1"], name="zero_res", B=2, s=64, c1=128, c2=128, k=16, r=8)
+    inp = synth.make_inputs(w)
+    U = synth.haar_columns(rng.standard_normal((128, 16)))
+    V = synth.haar_columns(rng.standard_normal((128, 16)))
+    Wk = synth.round_bf16((U * np.linspace(1, 0.5, 16)) @ V.T)
+    prep = oracle_prepare(w, Wk)
+    prep["W_res"] = np.zeros_like(prep["W_res"])
+    prep["P"] = np.zeros_like(prep["P"])
+    inp2 = synth.Inputs(X=inp.X, W=Wk, bias=inp.bias, W_exact=Wk, spectrum=None)
+    err, status, Yg, Y_or = run_same_factor_case(w, inputs=inp2, prep=prep)
+    assert np.all(status == D.SOLVE_ZERO)
+    rp = rounded_prep(prep, w.dtype)
+    static = O.static_apply(w.kind, inp.X, rp["static"]) + inp.bias
+    assert O.rel_fro(Yg, static) <= TOL[w.dtype]
+
+
+def test_bitwise_deterministic():
+    w = sc(W["vitb_fc1"], name="det", B=3, s=100, c1=256, c2=256, k=32, r=16)
+    inp = synth.make_inputs(w)
+    prep = oracle_prepare(w, inp.W)
+    from gpu_cases import host_factors_from_oracle
+    outs, _ = gpu_forward(w, host_factors_from_oracle(prep), inp.X, inp.bias, repeat=3)
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "vitl_fc1"])
+def test_end_to_end_library_prepare(name):
+    """End-to-end: the library's own host prepare + GPU forward vs the oracle's
+    prepare + forward (both from the same W)."""
+    w = W[name]
+    inp = synth.make_inputs(w)
+    f = D.prepare(inp.W, D.spec_of(w))
+    (Yg,), status = gpu_forward(w, f, inp.X, inp.bias)
+    prep = oracle_prepare(w, inp.W)
+    Y_or = O.forward(inp.X, prep, inp.bias, w.B, w.s, eps=1e-6)
+    err = O.rel_fro(Yg, Y_or)
+    log(f"  end-to-end {name}: rel_fro={err:.3e}")
+    assert err <= TOL[w.dtype]
+
+
+@pytest.mark.parametrize("dtype", [synth.DT_F32, synth.DT_BF16])
+def test_dense_ref(dtype):
+    import torch
+    rng = np.random.default_rng(5)
+    n, c1, c2 = 300, 264, 200
+    X = synth.round_storage(rng.standard_normal((n, c1)), dtype)
+    Wm = synth.round_storage(rng.standard_normal((c1, c2)) / np.sqrt(c1), dtype)
+    b = synth.round_storage(rng.standard_normal(c2), dtype)
+    Xd, Wt, bd = D.to_device(X, dtype), D.to_device(Wm.T.copy(), dtype), D.to_device(b, dtype)
+    Y = torch.empty((n, c2), dtype=D.torch_dtype(dtype), device="cuda")
+    D.dense_ref(Xd, Wt, bd, Y, dtype)
+    torch.cuda.synchronize()
+    ref = X @ Wm + b
+    err = O.rel_fro(Y.float().cpu().numpy().astype(float), ref)
+    # fp32: accumulation rounding only; bf16: plus the output rounding (2^-9)
+    assert err <= (1e-5 if dtype == synth.DT_F32 else 4e-3), err
