@@ -1,0 +1,253 @@
+#!/usr/bin/env python
+"""DyRA layer-forward benchmark on one MI355X.  Prints ONE JSON line.
+
+A step is one full DyRA forward (stage-1 pass, token reductions, r x r solve,
+right-factor GEMM, fused output GEMM) over one batch of synthetic input of the
+ViT-L/16 (DINOv3-like, 1029 tokens per image) MLP fc1 shape: B = 32 images,
+X (32*1029) x 1024 -> Y (32*1029) x 4096, low-rank static rank 256, residual
+rank 64, bf16 storage with fp32 accumulation.  Inputs and the prepared plan
+are resident in HBM before the timed region starts.
+
+Extra legs (excluded from `value`): per-stage HIP-event timing of the same
+launches (the roofline of the dominant kernel), the dense X W comparators
+(the library's own MFMA GEMM and torch.matmul / hipBLASLt), and the float64
+oracle timed on the host cores (cpu_baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+STAGES = ["stage1_X_UP", "token_reductions_M_G", "solve_apply", "right_factor_R", "fused_output_Y"]
+
+
+def stage_work(w):
+    """Algorithmic flops and HBM bytes of each stage for one launch (one
+    batch of B segments); bf16 = 2 bytes, fp32 = 4 bytes.  Low-rank."""
+    e = 2 if w.dtype == 1 else 4
+    n, c1, c2, k, r, B = w.n, w.c1, w.c2, w.k, w.r, w.B
+    N = k + r
+    return {
+        "stage1_X_UP": (2 * n * c1 * N, e * (n * c1 + N * c1 + n * N + r * n)),
+        "token_reductions_M_G": (2 * n * r * c1 + 2 * n * r * r,
+                                 e * (n * c1 + r * n) + 4 * (B * r * c1 + B * r * r)),
+        "solve_apply": (B * (2 * r ** 3 + 2 * r * r * c1), 4 * (2 * B * r * r + B * r * c1) + e * B * r * c1),
+        "right_factor_R": (2 * c2 * B * r * c1, e * (c2 * c1 + B * r * c1 + c2 * B * r)),
+        "fused_output_Y": (2 * n * N * c2, e * (n * N + c2 * k + c2 * B * r + c2 + n * c2)),
+    }
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "input_adaptive_rank_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")) and f not in ("host_linalg.h",):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def counters_traffic(workload, kernel_hash):
+    """HBM bytes per launch of the fused output GEMM from committed rocprofv3
+    counter runs (profiles/), or None if absent or taken on other kernel code."""
+    path = os.path.join(ROOT, "profiles", f"counters_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m = re.search(r"```json\n(.*?)\n```", txt, re.S)
+    if not m:
+        return None
+    d = json.loads(m.group(1))
+    if d.get("kernel_source_hash") != kernel_hash:
+        return None
+    return d.get("fused_output_traffic_bytes")
+
+
+def cpu_baseline(w, budget_s=12.0):
+    """The float64 oracle forward on the host cores, on the same workload."""
+    from input_adaptive_rank_amd import synth
+    from oracle import dyra_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:   # noqa: BLE001
+        threads = os.cpu_count()
+    inp = synth.make_inputs(w)
+    prep = O.prepare(inp.W, w.kind, w.r, k=w.k)
+    t0 = time.perf_counter()
+    runs = 0
+    while True:
+        O.forward(inp.X, prep, inp.bias, w.B, w.s, eps=1e-6)
+        runs += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or runs >= 3:
+            break
+    return {"value": round(w.n * runs / el, 1), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"full {w.name} batch ({w.B} x {w.s} tokens), float64 numpy oracle forward, "
+                      f"{runs} run(s) in {el:.2f} s (prepare excluded)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="vitl_fc1")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run a plain device copy of this size (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
+              "the DyRA forward shards by segments with no communication, see the design notes.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from input_adaptive_rank_amd import dyra as D
+    from input_adaptive_rank_amd import synth
+
+    w = synth.WORKLOADS[args.workload]
+    assert w.kind == synth.KIND_LOWRANK, "bench workload must be a low-rank layer"
+    dev = torch.device("cuda:0")
+    inp = synth.make_inputs(w)
+    t0 = time.perf_counter()
+    factors = D.prepare(inp.W, D.spec_of(w))
+    prep_s = time.perf_counter() - t0
+    layer = D.DyraLayer(D.spec_of(w), factors, w.dtype, bias=inp.bias, device=dev)
+    tdt = D.torch_dtype(w.dtype)
+    # 4 input/output buffer sets so X is not cache-resident from the previous step
+    NB = 4
+    X0 = D.to_device(inp.X, w.dtype, dev)
+    Xs = [X0] + [X0.clone() for _ in range(NB - 1)]
+    Ys = [torch.empty((w.n, w.c2), dtype=tdt, device=dev) for _ in range(NB)]
+    layer.workspace(w.B, w.s)
+    stream = torch.cuda.current_stream()
+
+    for i in range(args.warmup):
+        layer.forward(Xs[i % NB], w.B, w.s, out=Ys[i % NB])
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
+    for row in ev:           # create the HIP events
+        for e in row:
+            e.record(stream)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(K):
+        layer.forward_events(Xs[i % NB], w.B, w.s, Ys[i % NB], ev[i], stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / K
+    stage_ms = {STAGES[j]: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(K)]))
+                for j in range(5)}
+    status = layer.status(w.B, w.s)
+
+    work = stage_work(w)
+    stages = {}
+    for name, (fl, by) in work.items():
+        t = stage_ms[name] * 1e-3
+        stages[name] = {"ms": round(stage_ms[name], 5), "TFLOP/s": round(fl / t / 1e12, 1),
+                        "GB/s": round(by / t / 1e9, 1), "gflop": round(fl / 1e9, 3), "mb": round(by / 1e6, 2)}
+    total_flops = sum(v[0] for v in work.values())
+
+    # roofline of the dominant kernel: the fused output GEMM (Y = [T|L][V;R_b] + bias)
+    fl, by = work["fused_output_Y"]
+    t6 = stage_ms["fused_output_Y"] * 1e-3
+    t_mfma, t_hbm = fl / (PEAK_BF16_TFLOPS * 1e12), by / (PEAK_HBM_GBS * 1e9)
+    khash = kernel_source_hash()
+    traffic = counters_traffic(w.name, khash)
+    if t_hbm >= t_mfma:
+        roof = {"bound": "hbm", "achieved": round(by / t6 / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": round(fl / t6 / 1e12, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = traffic
+    roof["kernel"] = "s6_lowrank_kernel (fused T V + L R_b + bias)"
+    roof["mfma_frac"] = round(fl / t6 / 1e12 / PEAK_BF16_TFLOPS, 4)
+
+    # dense comparators on the same shape: library MFMA GEMM and torch.matmul (hipBLASLt)
+    dense = None
+    if not args.no_dense:
+        Wt = D.to_device(np.ascontiguousarray(inp.W.T), w.dtype, dev)
+        bias_d = layer.bias
+        Yd = torch.empty((w.n, w.c2), dtype=tdt, device=dev)
+
+        def timeit(fn, iters):
+            for i in range(3):
+                fn(i)
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for i in range(iters):
+                fn(i)
+            b.record(stream)
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) / iters
+
+        it = max(10, K // 2)
+        ms_ref = timeit(lambda i: D.dense_ref(Xs[i % NB], Wt, bias_d, Ys[i % NB], w.dtype), it)
+        ms_torch = timeit(lambda i: torch.addmm(bias_d, Xs[i % NB], Wt.t(), out=Yd), it)
+        best = min(ms_ref, ms_torch)
+        dense = {"dyra_dense_ref_ms": round(ms_ref, 5), "torch_matmul_ms": round(ms_torch, 5),
+                 "dense_gflop": round(2 * w.n * w.c1 * w.c2 / 1e9, 1),
+                 "speedup_vs_dense": round(best / ms, 3)}
+
+    if args.copy_probe_mib:
+        nbytes = args.copy_probe_mib << 20
+        a = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w)
+
+    out = {
+        "metric": "DyRA layer tokens/s + % bf16 MFMA peak at ViT-L shape; speedup vs dense XW",
+        "value": round(w.n / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: ViT-L/16 MLP fc1, B={w.B} x {w.s} tokens, {w.c1}->{w.c2}, "
+                               f"low-rank k={w.k}, r={w.r}, bf16, fp32 accumulate",
+                   "global_batch": w.B, "seq_len": w.s, "tokens": w.n},
+        "tflops": round(total_flops / (ms * 1e-3) / 1e12, 1),
+        "pct_bf16_peak": round(100 * total_flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "dense": dense,
+        "speedup_vs_dense": dense["speedup_vs_dense"] if dense else None,
+        "stages": stages,
+        "solver_status_ok": bool(np.all(status == 0)),
+        "kernel_source_hash": khash,
+        "prepare_s": round(prep_s, 2),
+        "gpu": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

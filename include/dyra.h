@@ -153,6 +153,26 @@ int dyra_workspace_size(const dyra_spec* spec, int64_t B, int64_t s, int32_t dty
                         size_t* bytes);
 
 /*
+ * Byte offsets of the forward's intermediates inside the workspace, for
+ * inspection and per-stage testing (the layout is otherwise internal):
+ *   A      [n][wa]      stage-1 output: low-rank [T | L] (wa = k + r)
+ *   Lt     [r][lt_pitch] L transposed (token-contiguous), dtype
+ *   G      [B][r][r]    fp32  L_b^T L_b
+ *   M      [B][r][c1]   fp32  L_b^T X_b
+ *   Ginv   [B][r][r]    fp32  (G_b + lambda_b I)^-1
+ *   Mp     [B][r][c1]   dtype Ginv_b M_b
+ *   Rt     [c2][B r]    dtype R_b^T, R_b = Mp_b W_res
+ *   status [B]          int32 solver status words
+ * Errors: EINVAL, ESHAPE, EDTYPE.
+ */
+typedef struct {
+  int64_t A, Wp, Lt, G, M, Ginv, Mp, Rt, status, total, wa, lt_pitch;
+} dyra_ws_offsets;
+
+int dyra_workspace_offsets(const dyra_spec* spec, int64_t B, int64_t s, int32_t dtype,
+                           dyra_ws_offsets* out);
+
+/*
  * The DyRA layer forward (asynchronous on `stream`; no host synchronisation).
  *   plan:      device, packed by dyra_plan_pack for the same spec and dtype.
  *   X:         device [B*s][c1], dtype.   Segment b = rows [b*s, (b+1)*s):
@@ -173,6 +193,22 @@ int dyra_workspace_size(const dyra_spec* spec, int64_t B, int64_t s, int32_t dty
 int dyra_forward(const dyra_spec* spec, const void* plan, const void* X, const void* bias,
                  void* Y, int64_t B, int64_t s, int32_t dtype, float ridge_eps,
                  int32_t solver, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * dyra_forward with stage-boundary events, a profiling aid.  events[i] are
+ * caller-created hipEvent_t handles (passed as void*; NULL entries skipped;
+ * nevents <= 6 used): events[0] is recorded on `stream` before the first
+ * kernel, events[i] after stage i -- 1: the stage-1 pass over X ([T | L] or
+ * the structured first stage and L), 2: the token reductions M_b, G_b,
+ * 3: the r x r solve and M'_b, 4: the right-factor GEMM R (and the BLAST
+ * coupling GEMM), 5: the fused output GEMM.  Same arguments, results and
+ * errors as dyra_forward (EINVAL also for nevents < 0 or events == NULL with
+ * nevents > 0).
+ */
+int dyra_forward_events(const dyra_spec* spec, const void* plan, const void* X, const void* bias,
+                        void* Y, int64_t B, int64_t s, int32_t dtype, float ridge_eps,
+                        int32_t solver, void* workspace, size_t ws_bytes, void* stream,
+                        void* const* events, int32_t nevents);
 
 /*
  * Copies the B per-segment solver status words of the last dyra_forward on

@@ -65,3 +65,34 @@ __device__ __forceinline__ int xcd_tile_id(int bid, int nwg) {
 }
 
 __device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
+
+// 16x16 block += A(16 x 32) * B(32 x 16): lane (i, g) holds A[i][8g .. 8g+7],
+// lane (j, g) holds B[8g .. 8g+7][j]; D[i][j] at lane j + 16 (i / 4), reg i % 4.
+__device__ __forceinline__ void mma16(f32x4& acc, const uint4& a, const uint4& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                acc, 0, 0, 0);
+}
+
+// 8 x 8 transpose of 16-bit elements held in registers: in[e] holds row e
+// (8 elements), out[c] receives column c (element e = in[e][c]).
+__device__ __forceinline__ void transpose8x8_b16(const uint4 (&in)[8], uint4 (&out)[8]) {
+  uint32_t w[8][4];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    w[e][0] = in[e].x;
+    w[e][1] = in[e].y;
+    w[e][2] = in[e].z;
+    w[e][3] = in[e].w;
+  }
+  uint32_t o[8][4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      // low halves of rows 2m, 2m+1 -> column 2p; high halves -> column 2p+1
+      o[2 * p][m] = __builtin_amdgcn_perm(w[2 * m + 1][p], w[2 * m][p], 0x05040100u);
+      o[2 * p + 1][m] = __builtin_amdgcn_perm(w[2 * m + 1][p], w[2 * m][p], 0x07060302u);
+    }
+#pragma unroll
+  for (int c = 0; c < 8; ++c) out[c] = make_uint4(o[c][0], o[c][1], o[c][2], o[c][3]);
+}

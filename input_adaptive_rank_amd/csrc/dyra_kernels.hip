@@ -44,14 +44,13 @@ __global__ __launch_bounds__(C::NT) void gemm_tn_kernel(const char* A, int64_t l
   const int t = xcd_tile_id(blockIdx.x, gridDim.x);
   const int64_t m0 = (int64_t)(t / tiles_n) * C::BM, n0 = (int64_t)(t % tiles_n) * C::BN;
   const int64_t kb = K * TT<T>::ESZ;
-  auto prov = [=](int p, Phase& ph) -> bool {
-    if (p != 0) return false;
+  auto src = [=](int t, Phase& ph, int& kt) {
     ph.a = OpK{A, lda, m0, 0, M, kb};
     ph.b = OpK{B, ldb, n0, 0, N, kb};
-    return true;
+    kt = t;
   };
   f32x16 acc[C::FM][C::FN];
-  gemm_mainloop<C>(prov, lds, acc);
+  gemm_mainloop<C>(src, ktiles(kb), lds, acc);
   stage_out<C>(lds, acc, bias ? bias + n0 : nullptr, (int)(N - n0));
   copy_out<C>(lds, Cg + m0 * ldc + n0 * TT<T>::ESZ, ldc, (int)imin64(C::BM, M - m0),
               (N - n0) * TT<T>::ESZ);
@@ -73,14 +72,13 @@ __global__ __launch_bounds__(C::NT) void s1_lowrank_kernel(const typename C::ele
   const int t = xcd_tile_id(blockIdx.x, gridDim.x);
   const int64_t m0 = (int64_t)(t / tiles_n) * C::BM, n0 = (int64_t)(t % tiles_n) * C::BN;
   const int64_t N = k + r;
-  auto prov = [=](int p, Phase& ph) -> bool {
-    if (p != 0) return false;
+  auto src = [=](int t, Phase& ph, int& kt) {
     ph.a = OpK{reinterpret_cast<const char*>(X), c1 * E, m0, 0, n, c1 * E};
     ph.b = OpK{reinterpret_cast<const char*>(UPt), c1 * E, n0, 0, N, c1 * E};
-    return true;
+    kt = t;
   };
   f32x16 acc[C::FM][C::FN];
-  gemm_mainloop<C>(prov, lds, acc);
+  gemm_mainloop<C>(src, ktiles(c1 * E), lds, acc);
   stage_out<C>(lds, acc, nullptr, 0);
   copy_out<C>(lds, reinterpret_cast<char*>(TL) + (m0 * N + n0) * E, N * E,
               (int)imin64(C::BM, n - m0), (N - n0) * E);
@@ -122,20 +120,23 @@ __global__ __launch_bounds__(C::NT) void s6_lowrank_kernel(const typename C::ele
   const int64_t bfirst = m0 / seg;
   const int64_t blast = imin64(B - 1, (imin64(m0 + C::BM, n) - 1) / seg);
   const char* TLc = reinterpret_cast<const char*>(TL);
-  auto prov = [=](int p, Phase& ph) -> bool {
-    if (p == 0) {
+  const int nk0 = ktiles((int64_t)k * E), nkr = ktiles((int64_t)r * E);
+  const int total = nk0 + (int)(blast - bfirst + 1) * nkr;
+  auto src = [=](int t, Phase& ph, int& kt) {
+    if (t < nk0) {
       ph.a = OpK{TLc, lda, m0, 0, n, (int64_t)k * E};
       ph.b = OpK{reinterpret_cast<const char*>(Vt), (int64_t)k * E, n0, 0, c2, (int64_t)k * E};
-      return true;
+      kt = t;
+      return;
     }
-    const int64_t b = bfirst + p - 1;
-    if (b > blast) return false;
+    const int u = t - nk0;
+    const int64_t b = bfirst + u / nkr;
+    kt = u % nkr;
     ph.a = OpK{TLc + (int64_t)k * E, lda, m0, b * seg, imin64((b + 1) * seg, n), (int64_t)r * E};
     ph.b = OpK{reinterpret_cast<const char*>(Rt + b * r), B * r * E, n0, 0, c2, (int64_t)r * E};
-    return true;
   };
   f32x16 acc[C::FM][C::FN];
-  gemm_mainloop<C>(prov, lds, acc);
+  gemm_mainloop<C>(src, total, lds, acc);
   stage_out<C>(lds, acc, bias ? bias + n0 : nullptr, (int)(c2 - n0));
   copy_out<C>(lds, reinterpret_cast<char*>(Y) + (m0 * c2 + n0) * E, c2 * E,
               (int)imin64(C::BM, n - m0), (c2 - n0) * E);
@@ -309,6 +310,314 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 }
 
 // ===========================================================================
+// S3 (bf16): token reductions without an LDS transpose.
+// Workgroups [0, B): G_b = L_b^T L_b and its inverse (the r x r solve runs
+// here, concurrently with the M strips).  Workgroups [B, ...): one
+// 128-channel strip of M_b = L_b^T X_b each.  Each wave streams a quarter of
+// the segment's tokens: a lane loads 8 token rows x 8 channels of X (16 B per
+// row, coalesced along channels), transposes the 8 x 8 bf16 block in
+// registers (v_perm) and feeds it as the B operand of 16x16x32 MFMAs whose A
+// operand is L^T (token-contiguous).  Output block q then holds channels
+// 8j + q.  Partial sums of the 4 waves are reduced through LDS in a fixed
+// order (deterministic, no atomics).
+// ===========================================================================
+
+constexpr int S3_NT = 256;
+constexpr int S3_STRIP = 128;
+// LDS: M strips use 64 KB of partials; the G/solve role uses 16 KB of
+// partials + r*r fp32 G + the 2 x 128 pivot-column buffer + reduction slots.
+template <int NB>
+struct S3Lds {
+  static constexpr int G_OFF = 16 * 1024;
+  static constexpr int CV_OFF = G_OFF + NB * 32 * NB * 32 * 4;
+  static constexpr int RED_OFF = CV_OFF + 256 * 4;
+  static constexpr int G_END = RED_OFF + 64;
+  static constexpr int BYTES = G_END > 64 * 1024 ? G_END : 64 * 1024;
+};
+
+template <int NRB>
+__device__ __forceinline__ void s3_m_strip(const bf16_t* __restrict__ Lt, int64_t ldt,
+                                           const bf16_t* __restrict__ X, int64_t c1, int r, int64_t lo,
+                                           int64_t hi, int64_t c0, float* __restrict__ Mb, char* lds) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int j = lane & 15, g = lane >> 4;
+  f32x4 acc[NRB][8];
+#pragma unroll
+  for (int ib = 0; ib < NRB; ++ib)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[ib][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int64_t a0 = lo & ~(int64_t)7;
+  const int nsteps = (int)((hi - a0 + 31) / 32);
+  const int s0 = w * nsteps / 4, s1 = (w + 1) * nsteps / 4;
+  const int64_t col = c0 + 8 * j;
+  const bool colok = col < c1;
+  auto load = [&](int st, uint4 (&xv)[8], uint4 (&av)[NRB]) {
+    const int64_t t0 = a0 + 32 * (int64_t)st + 8 * g;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int64_t tt = t0 + e;
+      xv[e] = (colok && tt >= lo && tt < hi) ? *reinterpret_cast<const uint4*>(X + tt * c1 + col) : zero4();
+    }
+#pragma unroll
+    for (int ib = 0; ib < NRB; ++ib) {
+      const int row = ib * 16 + j;
+      uint4 v = (row < r && t0 < ldt) ? *reinterpret_cast<const uint4*>(Lt + row * ldt + t0) : zero4();
+      av[ib] = mask_tokens<bf16_t>(v, t0, lo, hi);
+    }
+  };
+  if constexpr (NRB <= 2) {
+    // registers allow a one-step software prefetch
+    if (s0 < s1) {
+      uint4 xv[8], av[NRB];
+      load(s0, xv, av);
+      for (int st = s0; st < s1; ++st) {
+        uint4 bv[8];
+        transpose8x8_b16(xv, bv);
+        uint4 ac[NRB];
+#pragma unroll
+        for (int ib = 0; ib < NRB; ++ib) ac[ib] = av[ib];
+        if (st + 1 < s1) load(st + 1, xv, av);
+#pragma unroll
+        for (int ib = 0; ib < NRB; ++ib)
+#pragma unroll
+          for (int q = 0; q < 8; ++q) mma16(acc[ib][q], ac[ib], bv[q]);
+      }
+    }
+  } else {
+    // latency hidden by the second resident workgroup instead
+    for (int st = s0; st < s1; ++st) {
+      uint4 xv[8], av[NRB], bv[8];
+      load(st, xv, av);
+      transpose8x8_b16(xv, bv);
+#pragma unroll
+      for (int ib = 0; ib < NRB; ++ib)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) mma16(acc[ib][q], av[ib], bv[q]);
+    }
+  }
+  // Reduce the 4 wave partials pairwise through LDS (fixed order: ((w0 + w2)
+  // + (w1 + w3))), 4 row blocks (16 KB per wave) per round, then wave 0
+  // writes the strip: lane (j, g) holds rows 4g + v of each 16-row block and
+  // channels 8j .. 8j + 7 -> two 16-byte fp32 stores per (block, v).
+  float* part = reinterpret_cast<float*>(lds);
+  constexpr int RB = NRB < 4 ? NRB : 4;
+  constexpr int PW = RB * 8 * 4;   // floats per lane per round
+#pragma unroll
+  for (int rb0 = 0; rb0 < NRB; rb0 += RB) {
+    auto slot = [&](int sl, int ib, int q, int v) -> float& {
+      return part[((sl * RB + ib) * 32 + q * 4 + v) * 64 + lane];
+    };
+    __syncthreads();
+    if (w >= 2) {
+#pragma unroll
+      for (int ib = 0; ib < RB; ++ib)
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) slot(w - 2, ib, q, v) = acc[rb0 + ib][q][v];
+    }
+    __syncthreads();
+    if (w < 2) {
+#pragma unroll
+      for (int ib = 0; ib < RB; ++ib)
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[rb0 + ib][q][v] += slot(w, ib, q, v);
+    }
+    __syncthreads();
+    if (w == 1) {
+#pragma unroll
+      for (int ib = 0; ib < RB; ++ib)
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) slot(0, ib, q, v) = acc[rb0 + ib][q][v];
+    }
+    __syncthreads();
+    if (w == 0 && colok) {
+#pragma unroll
+      for (int ib = 0; ib < RB; ++ib)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int row = (rb0 + ib) * 16 + 4 * g + v;
+          if (row >= r) continue;
+          float sum[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) sum[q] = acc[rb0 + ib][q][v] + slot(0, ib, q, v);
+          float4* dst = reinterpret_cast<float4*>(Mb + (int64_t)row * c1 + col);
+          dst[0] = make_float4(sum[0], sum[1], sum[2], sum[3]);
+          dst[1] = make_float4(sum[4], sum[5], sum[6], sum[7]);
+        }
+    }
+    (void)PW;
+  }
+}
+
+// G_b = L_b^T L_b (fp32, into LDS as a dense r x r matrix at `Gs`), from
+// L^T rows with 32x32x16 MFMAs; the 4 waves split the tokens.
+template <int NB>
+__device__ __forceinline__ void s3_gram(const bf16_t* __restrict__ Lt, int64_t ldt, int r, int64_t lo, int64_t hi,
+                                        float* Gs, char* lds) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l = lane & 31, g = lane >> 5;
+  f32x16 acc[NB][NB];
+#pragma unroll
+  for (int a = 0; a < NB; ++a)
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
+  const int64_t a0 = lo & ~(int64_t)7;
+  const int nsteps = (int)((hi - a0 + 15) / 16);
+  const int s0 = w * nsteps / 4, s1 = (w + 1) * nsteps / 4;
+  for (int st = s0; st < s1; ++st) {
+    const int64_t t0 = a0 + 16 * (int64_t)st + 8 * g;
+    uint4 f[NB];
+#pragma unroll
+    for (int rb = 0; rb < NB; ++rb) {
+      const int row = rb * 32 + l;
+      uint4 v = (row < r && t0 < ldt) ? *reinterpret_cast<const uint4*>(Lt + row * ldt + t0) : zero4();
+      f[rb] = mask_tokens<bf16_t>(v, t0, lo, hi);
+    }
+#pragma unroll
+    for (int a = 0; a < NB; ++a)
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, f[a]),
+                                                            __builtin_bit_cast(bf16x8_t, f[b]), acc[a][b], 0, 0, 0);
+  }
+  // reduce: wave partials through LDS, one 32x32 block pair at a time
+  float* part = reinterpret_cast<float*>(lds);   // [4 waves][16 regs][64 lanes]
+#pragma unroll
+  for (int a = 0; a < NB; ++a)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      __syncthreads();
+#pragma unroll
+      for (int v = 0; v < 16; ++v) part[(w * 16 + v) * 64 + lane] = acc[a][b][v];
+      __syncthreads();
+      for (int u = tid; u < 16 * 64; u += S3_NT) {
+        const int ln = u & 63, v = u >> 6;
+        const float sum = part[(0 * 16 + v) * 64 + ln] + part[(1 * 16 + v) * 64 + ln] +
+                          part[(2 * 16 + v) * 64 + ln] + part[(3 * 16 + v) * 64 + ln];
+        const int i = a * 32 + (v >> 2) * 8 + (ln >> 5) * 4 + (v & 3), jj = b * 32 + (ln & 31);
+        if (i < r && jj < r) Gs[i * r + jj] = sum;
+      }
+    }
+  __syncthreads();
+}
+
+// Inverse of Gs + lambda I (Gs: r x r fp32 in LDS) by the symmetric sweep
+// (Gauss-Jordan) operator, 256 threads.  Thread t owns JW consecutive
+// entries of one row (row i = t / (r / JW), columns j0 .. j0 + JW - 1), kept
+// in registers; the pivot column is broadcast through LDS (double-buffered,
+// one barrier per pivot).  With c_k = -1 the pivot-row/column rules fold into
+//   a_ij <- [i != k][j != k] a_ij - c_i c_j / a_kk,
+// which after all r pivots leaves -(G + lambda I)^-1.  A pivot <= 0 marks the
+// matrix as not positive definite.  Writes Ginv (fp32) and the status word.
+template <int JW>
+__device__ __forceinline__ void sweep_inverse_256(const float* Gs, int r, float eps, float* Gf, int32_t* status,
+                                                  float* cv /* 2 x 128 */, float* red) {
+  const int tid = threadIdx.x;
+  const int per_row = (r + JW - 1) / JW;   // threads per row (r * per_row <= 256)
+  const int i = tid / per_row, j0 = (tid % per_row) * JW;
+  const bool own = i < r;
+  float a[JW];
+  float tr = 0.f;
+#pragma unroll
+  for (int q = 0; q < JW; ++q) {
+    const bool v = own && j0 + q < r;
+    a[q] = v ? Gs[i * r + j0 + q] : 0.f;
+    if (v && j0 + q == i) tr += a[q];
+  }
+  tr = block_sum<S3_NT>(tr, red);
+  int st = DYRA_SOLVE_OK;
+  if (tr == 0.f) st = DYRA_SOLVE_ZERO;
+  else if (!(tr > 0.f) || !isfinite(tr)) st = DYRA_SOLVE_NOT_SPD;
+  if (st == DYRA_SOLVE_OK) {
+    const float lam = eps * tr / (float)r;
+#pragma unroll
+    for (int q = 0; q < JW; ++q)
+      if (own && j0 + q == i) a[q] += lam;
+    if (own && j0 == 0) cv[i] = a[0];
+    __syncthreads();
+    for (int k = 0; k < r; ++k) {
+      const float* buf = cv + (k & 1) * 128;
+      float* nxt = cv + ((k + 1) & 1) * 128;
+      const float D = buf[k];
+      if (!(D > 0.f) || !isfinite(D)) {
+        st = DYRA_SOLVE_NOT_SPD;
+        break;
+      }
+      const float invD = 1.f / D;
+      float cj[JW];
+#pragma unroll
+      for (int q = 0; q < JW; q += 4) {
+        const float4 v4 = *reinterpret_cast<const float4*>(buf + j0 + q);
+        cj[q] = v4.x;
+        cj[q + 1] = v4.y;
+        cj[q + 2] = v4.z;
+        cj[q + 3] = v4.w;
+      }
+      const bool rowk = i == k;
+      const float ci = rowk ? -1.f : buf[own ? i : 0];
+      const float f = -ci * invD;
+#pragma unroll
+      for (int q = 0; q < JW; ++q) {
+        const bool colk = j0 + q == k;
+        const float c = colk ? -1.f : cj[q];
+        const float base = (rowk || colk) ? 0.f : a[q];
+        a[q] = fmaf(f, c, base);
+      }
+      // publish column k + 1 for the next pivot
+      if (own && k + 1 < r && (k + 1) >= j0 && (k + 1) < j0 + JW) {
+#pragma unroll
+        for (int q = 0; q < JW; ++q)
+          if (j0 + q == k + 1) nxt[i] = a[q];
+      }
+      __syncthreads();
+    }
+  }
+  if (own) {
+#pragma unroll
+    for (int q = 0; q < JW; ++q)
+      if (j0 + q < r) Gf[i * r + j0 + q] = st == DYRA_SOLVE_OK ? -a[q] : 0.f;
+  }
+  if (tid == 0) *status = st;
+}
+
+template <int NRB, int NB>
+__global__ __launch_bounds__(S3_NT, NRB <= 4 ? 2 : 1) void s3_reduce_solve_kernel(
+    const bf16_t* __restrict__ Lt, int64_t ldt, const bf16_t* __restrict__ X, int64_t c1, int r, int64_t seg,
+    int64_t n, int64_t B, float* __restrict__ M, float* __restrict__ G, float* __restrict__ Gi,
+    int32_t* __restrict__ status, float eps, int do_sweep, int strips) {
+  __shared__ __attribute__((aligned(16))) char lds[S3Lds<NB>::BYTES];
+  float* cv = reinterpret_cast<float*>(lds + S3Lds<NB>::CV_OFF);
+  float* red = reinterpret_cast<float*>(lds + S3Lds<NB>::RED_OFF);
+  const int64_t bid = blockIdx.x;
+  if (bid < B) {
+    const int64_t b = bid;
+    const int64_t lo = b * seg, hi = imin64((b + 1) * seg, n);
+    float* Gs = reinterpret_cast<float*>(lds + S3Lds<NB>::G_OFF);
+    s3_gram<NB>(Lt, ldt, r, lo, hi, Gs, lds);
+    // publish G (the Newton-Schulz path and diagnostics read it)
+    for (int e = threadIdx.x; e < r * r; e += S3_NT) G[b * r * r + e] = Gs[e];
+    if (do_sweep) {
+      // JW entries per thread: r * ceil(r / JW) <= 256 threads for r <= 32 NB
+      constexpr int JW = NB == 1 ? 4 : (NB == 2 ? 16 : 64);
+      sweep_inverse_256<JW>(Gs, r, eps, Gi + b * r * r, status + b, cv, red);
+    }
+    return;
+  }
+  const int64_t u = bid - B;
+  const int64_t b = u / strips;
+  const int64_t c0 = (u % strips) * S3_STRIP;
+  const int64_t lo = b * seg, hi = imin64((b + 1) * seg, n);
+  s3_m_strip<NRB>(Lt, ldt, X, c1, r, lo, hi, c0, M + b * r * c1, lds);
+}
+
+// ===========================================================================
 // S4a: (G + lambda I)^-1 by the symmetric sweep (Gauss-Jordan) operator.
 // One workgroup per segment; the r x r matrix lives in registers (up to 16
 // elements per thread), the pivot column is broadcast through LDS.
@@ -393,15 +702,15 @@ __global__ __launch_bounds__(SW_NT) void sweep_inverse_kernel(const float* G, fl
 constexpr int NS_N = 128;
 constexpr int NS_P = 129;   // padded LDS pitch (odd: row-strided reads spread over banks)
 
-__global__ __launch_bounds__(1024) void ns_inverse_kernel(const float* G, float* Ginv, int32_t* status,
-                                                          int r, float eps, int maxit, float tol) {
+__global__ __launch_bounds__(1024) void ns_inverse_kernel(const float* G, float* Ginv, bf16_t* Ghi, bf16_t* Glo,
+                                                          int32_t* status, int r, float eps, int maxit,
+                                                          float tol) {
   __shared__ float Xs[NS_N * NS_P];
   __shared__ float Ts[NS_N * NS_P];
   __shared__ float dsc[NS_N];
   __shared__ float red[16];
   const int64_t b = blockIdx.x;
   const float* Gb = G + b * r * r;
-  float* Ob = Ginv + b * r * r;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l = lane & 31, g = lane >> 5;
   const int bi = w >> 2, bj = w & 3;
@@ -506,38 +815,74 @@ __global__ __launch_bounds__(1024) void ns_inverse_kernel(const float* G, float*
   const bool good = st == DYRA_SOLVE_OK || st == DYRA_SOLVE_NOCONV;
   for (int e = tid; e < r * r; e += 1024) {
     const int i = e / r, j = e % r;
-    Ob[e] = good ? dsc[i] * Xs[i * NS_P + j] * dsc[j] : 0.f;
+    const float v = good ? dsc[i] * Xs[i * NS_P + j] * dsc[j] : 0.f;
+    if (Ginv) Ginv[b * r * r + e] = v;
+    if (Ghi) {
+      const bf16_t h = f2bf(v);
+      Ghi[b * r * r + e] = h;
+      Glo[b * r * r + e] = f2bf(v - bf2f(h));
+    }
   }
   if (tid == 0) status[b] = st;
 }
 
 // ===========================================================================
-// S4b: M'_b = Ginv_b M_b  (fp32 arithmetic, stored as T for the S5 GEMM)
+// S4b: M'_b = Ginv_b M_b in fp32, stored as T (the S5 GEMM operand).
+// Applying the inverse before rounding keeps the rounding error relative to
+// the least-squares coefficients themselves, which stays well-behaved when
+// L_b is ill-conditioned.
 // ===========================================================================
 
 template <typename T>
-__global__ __launch_bounds__(256) void apply_inverse_kernel(const float* Ginv, const float* M, T* Mp, int r,
-                                                            int64_t c1) {
-  __shared__ float Gs[128 * 128];
-  __shared__ float Ms[128 * 64];
+__global__ __launch_bounds__(256) void apply_inverse_kernel(const float* __restrict__ Ginv,
+                                                            const float* __restrict__ M, T* __restrict__ Mp,
+                                                            int r, int64_t c1) {
+  // tile: all r rows x 64 columns; thread = 4 rows x 4 columns per pass
+  extern __shared__ __attribute__((aligned(16))) float sh[];
+  float* Gs = sh;               // [q][p] = Ginv[p][q]
+  float* Ms = sh + r * r;       // [q][c]
   const int64_t tiles = (c1 + 63) / 64;
   const int64_t b = blockIdx.x / tiles;
   const int64_t c0 = (blockIdx.x % tiles) * 64;
   const int tid = threadIdx.x;
   const float* Gb = Ginv + b * r * r;
   const float* Mb = M + b * r * c1;
-  for (int e = tid; e < r * r; e += 256) Gs[e] = Gb[e];
-  for (int e = tid; e < r * 64; e += 256) {
-    const int q = e / 64, c = e % 64;
-    Ms[e] = c0 + c < c1 ? Mb[q * c1 + c0 + c] : 0.f;
+  for (int e = tid; e < r * r; e += 256) {
+    const int p = e / r, q = e % r;
+    Gs[q * r + p] = Gb[e];
+  }
+  for (int e = tid; e < r * 16; e += 256) {
+    const int q = e >> 4, c4 = (e & 15) * 4;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (c0 + c4 < c1) v = *reinterpret_cast<const float4*>(Mb + q * c1 + c0 + c4);
+    *reinterpret_cast<float4*>(Ms + q * 64 + c4) = v;
   }
   __syncthreads();
-  const int c = tid & 63;
-  if (c0 + c >= c1) return;
-  for (int p = tid >> 6; p < r; p += 4) {
-    float s = 0.f;
-    for (int q = 0; q < r; ++q) s = fmaf(Gs[p * r + q], Ms[q * 64 + c], s);
-    Mp[(b * r + p) * c1 + c0 + c] = TT<T>::from_f(s);
+  const int cq = tid & 15;                      // column quad
+  for (int pq = tid >> 4; pq * 4 < r; pq += 16) {   // row quad
+    float acc[4][4] = {};
+    for (int q = 0; q < r; ++q) {
+      const float4 g4 = *reinterpret_cast<const float4*>(Gs + q * r + pq * 4);
+      const float4 m4 = *reinterpret_cast<const float4*>(Ms + q * 64 + cq * 4);
+      const float gv[4] = {g4.x, g4.y, g4.z, g4.w}, mv[4] = {m4.x, m4.y, m4.z, m4.w};
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[a][c] = fmaf(gv[a], mv[c], acc[a][c]);
+    }
+    if (c0 + cq * 4 >= c1) continue;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      T* dst = Mp + (b * r + pq * 4 + a) * c1 + c0 + cq * 4;
+      if constexpr (TT<T>::ESZ == 2) {
+        uint2 pk;
+        pk.x = (uint32_t)f2bf(acc[a][0]) | ((uint32_t)f2bf(acc[a][1]) << 16);
+        pk.y = (uint32_t)f2bf(acc[a][2]) | ((uint32_t)f2bf(acc[a][3]) << 16);
+        *reinterpret_cast<uint2*>(dst) = pk;
+      } else {
+        *reinterpret_cast<float4*>(dst) = make_float4(acc[a][0], acc[a][1], acc[a][2], acc[a][3]);
+      }
+    }
   }
 }
 
@@ -546,6 +891,7 @@ __global__ __launch_bounds__(256) void apply_inverse_kernel(const float* Ginv, c
 // ===========================================================================
 
 typedef GemmCfg<bf16_t, 128, 128, 2, 2> CfgB;   // bf16 GEMMs
+typedef GemmCfg<bf16_t, 256, 256, 2, 4> CfgB6;  // bf16 fused output GEMM (short K, wide output)
 typedef GemmCfg<float, 64, 64, 2, 2> CfgF;      // fp32 GEMMs
 typedef GemmCfg<bf16_t, 64, 128, 2, 2> CfgB3;   // S3, bf16
 typedef GemmCfg<float, 64, 64, 2, 2> CfgF3;     // S3, fp32
@@ -567,11 +913,33 @@ void launch_gemm_tn(const void* A, int64_t lda_el, const void* B, int64_t ldb_el
 
 inline int64_t lt_pitch(int64_t n) { return cdiv(n, 256) * 256; }
 
-template <class C, class C3>
+// Stage-boundary events (profiling aid): ev[0] before the first kernel,
+// ev[i] after stage i (1 stage-1 pass, 2 token reductions, 3 solve + apply,
+// 4 right-factor GEMM, 5 fused output GEMM).
+struct StageEvents {
+  void* const* ev;
+  int n;
+  void mark(int i, hipStream_t st) const {
+    if (ev && i < n && ev[i]) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(ev[i]), st);
+  }
+};
+
+template <int NRB, int NB>
+void launch_s3_bf16(const bf16_t* Lt, int64_t ldt, const bf16_t* X, int64_t c1, int r, int64_t seg, int64_t n,
+                    int64_t B, float* M, float* G, float* Gi, int32_t* stat, float eps, bool sweep,
+                    hipStream_t st) {
+  const int strips = (int)cdiv(c1, S3_STRIP);
+  hipLaunchKernelGGL((s3_reduce_solve_kernel<NRB, NB>), dim3((unsigned)(B + B * strips)), dim3(S3_NT), 0, st, Lt,
+                     ldt, X, c1, r, seg, n, B, M, G, Gi, stat, eps, sweep ? 1 : 0, strips);
+}
+
+template <class C, class C3, class C6>
 int forward_lowrank(const dyra_spec& s, const char* plan, const void* X, const void* bias, void* Y,
-                    int64_t B, int64_t seg, float eps, int solver, char* ws, hipStream_t st) {
+                    int64_t B, int64_t seg, float eps, int solver, char* ws, hipStream_t st,
+                    const StageEvents& E) {
   typedef typename C::elem T;
-  const int dtype = TT<T>::ESZ == 2 ? DYRA_BF16 : DYRA_F32;
+  constexpr bool BF = TT<T>::ESZ == 2;
+  const int dtype = BF ? DYRA_BF16 : DYRA_F32;
   const PlanLayout PL = plan_layout(s, dtype);
   const WsLayout WL = ws_layout(s, B, seg, dtype);
   const int64_t n = B * seg, c1 = s.c1, c2 = s.c2;
@@ -588,38 +956,54 @@ int forward_lowrank(const dyra_spec& s, const char* plan, const void* X, const v
   T* Rt = reinterpret_cast<T*>(ws + WL.Rt);
   int32_t* stat = reinterpret_cast<int32_t*>(ws + WL.status);
   const int64_t ldt = lt_pitch(n);
+  const bool ns = solver == DYRA_SOLVER_NS || (solver == DYRA_SOLVER_AUTO && r >= 128);
 
-  {  // S1
+  E.mark(0, st);
+  {  // S1: [T | L] = X [U | P], L^T
     const int tiles_n = (int)cdiv(k + r, C::BN);
     const int64_t tiles = cdiv(n, C::BM) * tiles_n;
     hipLaunchKernelGGL(s1_lowrank_kernel<C>, dim3((unsigned)tiles), dim3(C::NT), 0, st,
                        reinterpret_cast<const T*>(X), UPt, TL, Lt, n, c1, k, r, ldt, tiles_n);
   }
-  {  // S3
+  E.mark(1, st);
+  // S3: M_b, G_b (bf16: with the sweep solve in the same launch)
+  bool solved = false;
+  if constexpr (BF) {
+    const bf16_t* Xb = reinterpret_cast<const bf16_t*>(X);
+    if (r <= 16) launch_s3_bf16<1, 1>(Lt, ldt, Xb, c1, r, seg, n, B, M, G, Gi, stat, eps, !ns, st);
+    else if (r <= 32) launch_s3_bf16<2, 1>(Lt, ldt, Xb, c1, r, seg, n, B, M, G, Gi, stat, eps, !ns, st);
+    else if (r <= 64) launch_s3_bf16<4, 2>(Lt, ldt, Xb, c1, r, seg, n, B, M, G, Gi, stat, eps, !ns, st);
+    else launch_s3_bf16<8, 4>(Lt, ldt, Xb, c1, r, seg, n, B, M, G, Gi, stat, eps, !ns, st);
+    solved = !ns;
+  } else {
     const int tr = (int)cdiv(r, C3::BM), tcm = (int)cdiv(c1, C3::BN), tcg = (int)cdiv(r, C3::BN);
     const int64_t grid = B * tr * (tcm + tcg);
     hipLaunchKernelGGL(s3_gram_kernel<C3>, dim3((unsigned)grid), dim3(C3::NT), 0, st, Lt, ldt,
                        reinterpret_cast<const T*>(X), c1, r, seg, n, M, G, tr, tcm, tcg);
   }
-  {  // S4
-    const bool ns = solver == DYRA_SOLVER_NS || (solver == DYRA_SOLVER_AUTO && r >= 128);
+  E.mark(2, st);
+  // S4: Ginv_b (unless solved above), M'_b = Ginv_b M_b
+  if (!solved) {
     if (ns)
-      hipLaunchKernelGGL(ns_inverse_kernel, dim3((unsigned)B), dim3(1024), 0, st, G, Gi, stat, r, eps, 60,
-                         2e-6f);
+      hipLaunchKernelGGL(ns_inverse_kernel, dim3((unsigned)B), dim3(1024), 0, st, G, Gi, nullptr, nullptr, stat,
+                         r, eps, 60, 2e-6f);
     else
       hipLaunchKernelGGL(sweep_inverse_kernel, dim3((unsigned)B), dim3(SW_NT), 0, st, G, Gi, stat, r, eps);
-    hipLaunchKernelGGL(apply_inverse_kernel<T>, dim3((unsigned)(cdiv(c1, 64) * B)), dim3(256), 0, st,
-                       Gi, M, Mp, r, c1);
   }
-  // S5: Rt (c2 x B r) = Wrt (c2 x c1) . Mp (B r x c1)^T
+  hipLaunchKernelGGL(apply_inverse_kernel<T>, dim3((unsigned)(cdiv(c1, 64) * B)), dim3(256),
+                     (size_t)(r * r + r * 64) * 4, st, Gi, M, Mp, r, c1);
+  E.mark(3, st);
+  // S5: R^T (c2 x B r) = W_res^T (c2 x c1) . M' (B r x c1)^T
   launch_gemm_tn<C>(Wrt, c1, Mp, c1, Rt, B * r, c2, B * r, c1, nullptr, st);
-  {  // S6
-    const int tiles_n = (int)cdiv(c2, C::BN);
-    const int64_t tiles = cdiv(n, C::BM) * tiles_n;
-    hipLaunchKernelGGL(s6_lowrank_kernel<C>, dim3((unsigned)tiles), dim3(C::NT), 0, st, TL, Vt, Rt,
+  E.mark(4, st);
+  {  // S6: Y = T V + L R_b + bias
+    const int tiles_n = (int)cdiv(c2, C6::BN);
+    const int64_t tiles = cdiv(n, C6::BM) * tiles_n;
+    hipLaunchKernelGGL(s6_lowrank_kernel<C6>, dim3((unsigned)tiles), dim3(C6::NT), 0, st, TL, Vt, Rt,
                        reinterpret_cast<const T*>(bias), reinterpret_cast<T*>(Y), n, c2, k, r, seg, B,
                        tiles_n);
   }
+  E.mark(5, st);
   return hipGetLastError() == hipSuccess ? DYRA_OK : DYRA_EHIP;
 }
 
@@ -655,9 +1039,10 @@ extern "C" int dyra_workspace_size(const dyra_spec* spec, int64_t B, int64_t s, 
   return DYRA_OK;
 }
 
-extern "C" int dyra_forward(const dyra_spec* spec, const void* plan, const void* X, const void* bias, void* Y,
-                            int64_t B, int64_t s, int32_t dtype, float ridge_eps, int32_t solver,
-                            void* workspace, size_t ws_bytes, void* stream) {
+namespace {
+int forward_impl(const dyra_spec* spec, const void* plan, const void* X, const void* bias, void* Y, int64_t B,
+                 int64_t s, int32_t dtype, float ridge_eps, int32_t solver, void* workspace, size_t ws_bytes,
+                 void* stream, const StageEvents& E) {
   int rc = check_forward_args(spec, plan, X, Y, B, s, dtype, ridge_eps, solver, workspace, ws_bytes);
   if (rc) return rc;
   if (bias && (reinterpret_cast<uintptr_t>(bias) & 15)) return DYRA_EINVAL;
@@ -665,8 +1050,25 @@ extern "C" int dyra_forward(const dyra_spec* spec, const void* plan, const void*
   const char* plan_c = reinterpret_cast<const char*>(plan);
   char* ws = reinterpret_cast<char*>(workspace);
   if (dtype == DYRA_BF16)
-    return forward_lowrank<CfgB, CfgB3>(*spec, plan_c, X, bias, Y, B, s, ridge_eps, solver, ws, st);
-  return forward_lowrank<CfgF, CfgF3>(*spec, plan_c, X, bias, Y, B, s, ridge_eps, solver, ws, st);
+    return forward_lowrank<CfgB, CfgB3, CfgB6>(*spec, plan_c, X, bias, Y, B, s, ridge_eps, solver, ws, st, E);
+  return forward_lowrank<CfgF, CfgF3, CfgF>(*spec, plan_c, X, bias, Y, B, s, ridge_eps, solver, ws, st, E);
+}
+}  // namespace
+
+extern "C" int dyra_forward(const dyra_spec* spec, const void* plan, const void* X, const void* bias, void* Y,
+                            int64_t B, int64_t s, int32_t dtype, float ridge_eps, int32_t solver,
+                            void* workspace, size_t ws_bytes, void* stream) {
+  return forward_impl(spec, plan, X, bias, Y, B, s, dtype, ridge_eps, solver, workspace, ws_bytes, stream,
+                      StageEvents{nullptr, 0});
+}
+
+extern "C" int dyra_forward_events(const dyra_spec* spec, const void* plan, const void* X, const void* bias,
+                                   void* Y, int64_t B, int64_t s, int32_t dtype, float ridge_eps,
+                                   int32_t solver, void* workspace, size_t ws_bytes, void* stream,
+                                   void* const* events, int32_t nevents) {
+  if (nevents < 0 || (nevents > 0 && !events)) return DYRA_EINVAL;
+  return forward_impl(spec, plan, X, bias, Y, B, s, dtype, ridge_eps, solver, workspace, ws_bytes, stream,
+                      StageEvents{events, nevents});
 }
 
 extern "C" int dyra_solver_status(const dyra_spec* spec, const void* workspace, int64_t B, int64_t s,

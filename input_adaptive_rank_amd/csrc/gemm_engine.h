@@ -116,37 +116,12 @@ __device__ __forceinline__ void compute_tile(const char* stage, f32x16 (&acc)[C:
   }
 }
 
-// Walks the phases of a tile, k-tile by k-tile.  Prov is a functor
-// bool(int p, Phase&) that fills phase p or returns false when there is none.
-template <class Prov>
-struct Cursor {
-  Phase ph;
-  int p, kt, nkt;
-  bool valid;
-  __device__ __forceinline__ void settle(const Prov& prov) {
-    while (valid) {
-      nkt = (int)((ph.a.kbytes + 127) >> 7);
-      if (kt < nkt) break;
-      ++p;
-      kt = 0;
-      valid = prov(p, ph);
-    }
-  }
-  __device__ __forceinline__ void init(const Prov& prov) {
-    p = 0;
-    kt = 0;
-    nkt = 0;
-    valid = prov(0, ph);
-    settle(prov);
-  }
-  __device__ __forceinline__ void advance(const Prov& prov) {
-    ++kt;
-    settle(prov);
-  }
-};
-
-template <class C, class Prov>
-__device__ __forceinline__ void gemm_mainloop(const Prov& prov, char* lds, f32x16 (&acc)[C::FM][C::FN]) {
+// Runs the software pipeline over `total` k-tiles.  src(t, ph, kt) resolves
+// flat k-tile t to its phase operands and the k-tile index inside the phase
+// (uniform scalar arithmetic, no state carried between iterations).
+template <class C, class Src>
+__device__ __forceinline__ void gemm_mainloop(const Src& src, int total, char* lds,
+                                              f32x16 (&acc)[C::FM][C::FN]) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wm = w / C::NWN, wn = w % C::NWN;
 #pragma unroll
@@ -155,26 +130,33 @@ __device__ __forceinline__ void gemm_mainloop(const Prov& prov, char* lds, f32x1
     for (int fn = 0; fn < C::FN; ++fn)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[fm][fn][v] = 0.f;
-  Cursor<Prov> cur;
-  cur.init(prov);
-  if (!cur.valid) return;
+  if (total <= 0) return;
   TileRegs<C> r;
-  load_tile<C>(cur.ph, cur.kt, r, tid);
+  {
+    Phase ph;
+    int kt;
+    src(0, ph, kt);
+    load_tile<C>(ph, kt, r, tid);
+  }
   store_tile<C>(lds, r, tid);
   __syncthreads();
-  int it = 0;
-  for (;;) {
-    Cursor<Prov> nxt = cur;
-    nxt.advance(prov);
-    if (nxt.valid) load_tile<C>(nxt.ph, nxt.kt, r, tid);
-    compute_tile<C>(lds + (it & 1) * C::STAGE, acc, lane, wm, wn);
-    if (!nxt.valid) break;
-    store_tile<C>(lds + ((it + 1) & 1) * C::STAGE, r, tid);
-    __syncthreads();
-    cur = nxt;
-    ++it;
+  for (int t = 0; t < total; ++t) {
+    const bool more = t + 1 < total;
+    if (more) {
+      Phase ph;
+      int kt;
+      src(t + 1, ph, kt);
+      load_tile<C>(ph, kt, r, tid);
+    }
+    compute_tile<C>(lds + (t & 1) * C::STAGE, acc, lane, wm, wn);
+    if (more) {
+      store_tile<C>(lds + ((t + 1) & 1) * C::STAGE, r, tid);
+      __syncthreads();
+    }
   }
 }
+
+__device__ __forceinline__ int ktiles(int64_t kbytes) { return (int)((kbytes + 127) >> 7); }
 
 // Writes acc (+ bias[col] when bias != nullptr; bias points at the tile's
 // first column and holds bias_n valid entries) into the LDS staging tile as T.

@@ -291,3 +291,27 @@ extern "C" int dyra_plan_pack(const dyra_spec* spec, const dyra_host_factors* f,
     for (int64_t j = 0; j < c2; ++j) put(host_plan, L.Wrt, (size_t)(j * c1 + i), f->Wres[i * c2 + j], dtype);
   return DYRA_OK;
 }
+
+extern "C" int dyra_workspace_offsets(const dyra_spec* spec, int64_t B, int64_t s, int32_t dtype,
+                                      dyra_ws_offsets* out) {
+  if (!spec || !out) return DYRA_EINVAL;
+  int rc = validate_spec(spec);
+  if (rc) return rc;
+  rc = validate_dtype(*spec, dtype);
+  if (rc) return rc;
+  if (B <= 0 || s <= 0 || B * s >= ((int64_t)1 << 31)) return DYRA_ESHAPE;
+  const WsLayout W = ws_layout(*spec, B, s, dtype);
+  out->A = (int64_t)W.A;
+  out->Wp = (int64_t)W.Wp;
+  out->Lt = (int64_t)W.Lt;
+  out->G = (int64_t)W.G;
+  out->M = (int64_t)W.M;
+  out->Ginv = (int64_t)W.Ginv;
+  out->Mp = (int64_t)W.Mp;
+  out->Rt = (int64_t)W.Rt;
+  out->status = (int64_t)W.status;
+  out->total = (int64_t)W.total;
+  out->wa = W.wa;
+  out->lt_pitch = (B * s + 255) / 256 * 256;
+  return DYRA_OK;
+}

@@ -99,9 +99,11 @@ inline PlanLayout plan_layout(const dyra_spec& s, int dtype) {
 //                 BLAST [Z | L] (wa = nb rb + r)
 // Wp   [n x nb rb] BLAST coupled output Z S (BLAST only)
 // Lt   [r x n256] L transposed (token-contiguous, pitch n rounded up to 256)
-// G    [B x r x r] fp32, M [B x r x c1] fp32, Ginv [B x r x r] fp32
-// Mp   [B x r x c1] dtype: (G + lambda I)^-1 M
-// Rt   [c2 x B r] dtype: R_b^T for every segment, R_b = Mp_b W_res
+// G    [B x r x r] fp32        Gram matrices L_b^T L_b
+// M    [B x r x c1] fp32       L_b^T X_b
+// Ginv [B x r x r] fp32        (G_b + lambda_b I)^-1
+// Mp   [B x r x c1] dtype      M'_b = Ginv_b M_b
+// Rt   [c2 x B r] dtype        R_b^T for every segment, R_b = M'_b W_res
 // status [B] int32
 struct WsLayout {
   int64_t wa = 0;

@@ -48,6 +48,11 @@ class Spec(ctypes.Structure):
 _FACTORS = ("U", "V", "B1", "B2", "Ub", "S", "Vb", "P", "R0", "Wres", "res_sv")
 
 
+class WsOffsets(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_int64) for f in ("A", "Wp", "Lt", "G", "M", "Ginv", "Mp", "Rt", "status", "total",
+                                                "wa", "lt_pitch")]
+
+
 class Sizes(ctypes.Structure):
     _fields_ = [(f, ctypes.c_int64) for f in _FACTORS]
 
@@ -75,8 +80,11 @@ def lib():
             "dyra_plan_pack": [SP, ctypes.POINTER(HostFactors), I32, P],
             "dyra_workspace_size": [SP, I64, I64, I32, ctypes.POINTER(SZ)],
             "dyra_forward": [SP, P, P, P, P, I64, I64, I32, ctypes.c_float, I32, P, SZ, P],
+            "dyra_forward_events": [SP, P, P, P, P, I64, I64, I32, ctypes.c_float, I32, P, SZ, P,
+                                    ctypes.POINTER(ctypes.c_void_p), I32],
             "dyra_solver_status": [SP, P, I64, I64, I32, ctypes.POINTER(I32), P],
             "dyra_dense_ref": [P, P, P, P, I64, I64, I64, I32, P],
+            "dyra_workspace_offsets": [SP, I64, I64, I32, ctypes.POINTER(WsOffsets)],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -170,6 +178,12 @@ def workspace_size(spec: Spec, B: int, s: int, dtype: int) -> int:
     return n.value
 
 
+def workspace_offsets(spec: Spec, B: int, s: int, dtype: int) -> dict:
+    o = WsOffsets()
+    _check("dyra_workspace_offsets", lib().dyra_workspace_offsets(ctypes.byref(spec), B, s, dtype, ctypes.byref(o)))
+    return {f: getattr(o, f) for f, _ in WsOffsets._fields_}
+
+
 # ---------------------------------------------------------------------------
 # device calls (torch tensors as plain device buffers)
 # ---------------------------------------------------------------------------
@@ -208,6 +222,18 @@ def forward(spec: Spec, plan, X, bias, Y, B: int, s: int, dtype: int, eps: float
                             _dev(Y, "Y"), B, s, dtype, eps, solver, _dev(workspace, "workspace"),
                             workspace.numel() * workspace.element_size(), _stream(stream))
     _check("dyra_forward", rc)
+
+
+def forward_events(spec: Spec, plan, X, bias, Y, B: int, s: int, dtype: int, eps: float, solver: int,
+                   workspace, events, stream=None):
+    """dyra_forward recording stage-boundary events (torch.cuda.Event objects
+    that have been recorded once, so their HIP handles exist)."""
+    arr = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
+    rc = lib().dyra_forward_events(ctypes.byref(spec), _dev(plan, "plan"), _dev(X, "X"), _dev(bias, "bias"),
+                                   _dev(Y, "Y"), B, s, dtype, eps, solver, _dev(workspace, "workspace"),
+                                   workspace.numel() * workspace.element_size(), _stream(stream), arr,
+                                   len(events))
+    _check("dyra_forward_events", rc)
 
 
 def solver_status(spec: Spec, workspace, B: int, s: int, dtype: int, stream=None) -> np.ndarray:
@@ -265,6 +291,12 @@ class DyraLayer:
         ws = self.workspace(B, s)
         forward(self.spec, self.plan, X, self.bias, Y, B, s, self.dtype, self.eps, self.solver, ws, stream)
         return Y
+
+    def forward_events(self, X, B: int, s: int, out, events, stream=None):
+        ws = self.workspace(B, s)
+        forward_events(self.spec, self.plan, X, self.bias, out, B, s, self.dtype, self.eps, self.solver, ws,
+                       events, stream)
+        return out
 
     def status(self, B: int, s: int, stream=None) -> np.ndarray:
         return solver_status(self.spec, self.workspace(B, s), B, s, self.dtype, stream)
