@@ -75,8 +75,10 @@ extern "C" {
 /* per-segment solver status words (dyra_solver_status) */
 #define DYRA_SOLVE_OK        0
 #define DYRA_SOLVE_NOT_SPD   1   /* Cholesky met a pivot <= 0: R_b := 0, Y_b = X_b W_hat + bias */
-#define DYRA_SOLVE_NOCONV    2   /* Newton-Schulz stopped at its iteration cap           */
+#define DYRA_SOLVE_NOCONV    2   /* reserved: an iterative solve without a usable result */
 #define DYRA_SOLVE_ZERO      3   /* trace(G_b) == 0 (X_b P == 0): R_b := 0               */
+#define DYRA_SOLVE_FALLBACK  4   /* Newton-Schulz did not reach its tolerance in fp32;    */
+                                 /* R_b solved by the sweep instead (result valid)        */
 
 typedef struct {
   int32_t kind;   /* DYRA_LOWRANK / DYRA_MONARCH / DYRA_BLAST                  */

@@ -38,16 +38,22 @@ template <class C>
 __global__ __launch_bounds__(C::NT) void gemm_tn_kernel(const char* A, int64_t lda, const char* B,
                                                         int64_t ldb, char* Cg, int64_t ldc, int64_t M,
                                                         int64_t N, int64_t K,
-                                                        const typename C::elem* bias, int tiles_n) {
+                                                        const typename C::elem* bias, int tiles_n,
+                                                        int64_t sA, int64_t sB, int64_t sC, int tiles_per_batch) {
   typedef typename C::elem T;
   __shared__ __attribute__((aligned(16))) char lds[C::LDS];
-  const int t = xcd_tile_id(blockIdx.x, gridDim.x);
+  // batch z: A += z sA, B += z sB, C += z sC (byte strides)
+  const int z = blockIdx.x / tiles_per_batch;
+  const int t = xcd_tile_id(blockIdx.x % tiles_per_batch, tiles_per_batch);
+  A += z * sA;
+  B += z * sB;
+  Cg += z * sC;
   const int64_t m0 = (int64_t)(t / tiles_n) * C::BM, n0 = (int64_t)(t % tiles_n) * C::BN;
   const int64_t kb = K * TT<T>::ESZ;
-  auto src = [=](int t, Phase& ph, int& kt) {
+  auto src = [=](int tt, Phase& ph, int& kt) {
     ph.a = OpK{A, lda, m0, 0, M, kb};
     ph.b = OpK{B, ldb, n0, 0, N, kb};
-    kt = t;
+    kt = tt;
   };
   f32x16 acc[C::FM][C::FN];
   gemm_mainloop<C>(src, ktiles(kb), lds, acc);
@@ -60,12 +66,13 @@ __global__ __launch_bounds__(C::NT) void gemm_tn_kernel(const char* A, int64_t l
 // S1 (low-rank): [T | L] = X [U_f | P], plus L^T (token-contiguous) for S3
 // ===========================================================================
 
+// TL: output rows of pitch ldo elements (columns [0, k) = T, [k, k + r) = L).
 template <class C>
 __global__ __launch_bounds__(C::NT) void s1_lowrank_kernel(const typename C::elem* X,
                                                            const typename C::elem* UPt,
                                                            typename C::elem* TL, typename C::elem* Lt,
                                                            int64_t n, int64_t c1, int k, int r,
-                                                           int64_t ldt, int tiles_n) {
+                                                           int64_t ldt, int tiles_n, int64_t ldo) {
   typedef typename C::elem T;
   constexpr int E = TT<T>::ESZ, KPC = TT<T>::KPC;
   __shared__ __attribute__((aligned(16))) char lds[C::LDS];
@@ -80,7 +87,7 @@ __global__ __launch_bounds__(C::NT) void s1_lowrank_kernel(const typename C::ele
   f32x16 acc[C::FM][C::FN];
   gemm_mainloop<C>(src, ktiles(c1 * E), lds, acc);
   stage_out<C>(lds, acc, nullptr, 0);
-  copy_out<C>(lds, reinterpret_cast<char*>(TL) + (m0 * N + n0) * E, N * E,
+  copy_out<C>(lds, reinterpret_cast<char*>(TL) + (m0 * ldo + n0) * E, ldo * E,
               (int)imin64(C::BM, n - m0), (N - n0) * E);
   // L columns of this tile, written transposed: Lt[j - k][m0 + rows]
   const int64_t j0 = imax64(n0, k), j1 = imin64(n0 + C::BN, N);
@@ -140,6 +147,202 @@ __global__ __launch_bounds__(C::NT) void s6_lowrank_kernel(const typename C::ele
   stage_out<C>(lds, acc, bias ? bias + n0 : nullptr, (int)(c2 - n0));
   copy_out<C>(lds, reinterpret_cast<char*>(Y) + (m0 * c2 + n0) * E, c2 * E,
               (int)imin64(C::BM, n - m0), (c2 - n0) * E);
+}
+
+// ===========================================================================
+// Monarch static branch (m = 32 blocks of 32 x 32, c = 1024), bf16.
+// W_hat = blockdiag(B1_a) . Pi . blockdiag(B2_j), Pi the reshape(32, 32)
+// transpose: u_a = x_a B1_a, v[j*32 + a] = u[a*32 + j], y_j = v_j B2_j.
+// Both kernels feed the MFMA straight from global memory (each 32 x 32
+// operand block is one 16-byte load per lane per k-step) -- the work is
+// bound by streaming X, V and Y, not by the tiny block products.
+// ===========================================================================
+
+constexpr int MO = 32;
+
+// Stage 1 + L: one pass over X.  A wave owns 32 rows; for each group of 8
+// blocks a it accumulates U_a (32 x 32 each) and then writes the permuted
+// V[row][j*32 + a0 .. a0 + 7] as one 16-byte store per (row, j).  L = X P is
+// accumulated across all 32 blocks (K slice a*32 .. a*32 + 31 per block).
+template <int RB>
+__global__ __launch_bounds__(256) void s1_monarch_kernel(const bf16_t* __restrict__ X,
+                                                         const bf16_t* __restrict__ B1t,
+                                                         const bf16_t* __restrict__ Pt,
+                                                         bf16_t* __restrict__ A, bf16_t* __restrict__ Lt,
+                                                         int64_t n, int r, int64_t ldt) {
+  constexpr int C = MO * MO;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int l = lane & 31, g = lane >> 5;
+  const int64_t row = (int64_t)blockIdx.x * 128 + w * 32 + l;
+  const bool rok = row < n;
+  const int64_t lda = C + r;
+  f32x16 lacc[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) lacc[rb][v] = 0.f;
+  for (int ag = 0; ag < MO / 8; ++ag) {
+    f32x16 uacc[8];
+#pragma unroll
+    for (int ai = 0; ai < 8; ++ai) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) uacc[ai][v] = 0.f;
+      const int a = ag * 8 + ai;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int kk = a * MO + 16 * s + 8 * g;
+        const uint4 xa = rok ? *reinterpret_cast<const uint4*>(X + row * C + kk) : zero4();
+        const uint4 b1 = *reinterpret_cast<const uint4*>(B1t + ((int64_t)a * MO + l) * MO + 16 * s + 8 * g);
+        TT<bf16_t>::mma(uacc[ai], b1, xa);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const int p = rb * 32 + l;
+          const uint4 pb = p < r ? *reinterpret_cast<const uint4*>(Pt + (int64_t)p * C + kk) : zero4();
+          TT<bf16_t>::mma(lacc[rb], pb, xa);
+        }
+      }
+    }
+    if (rok) {
+      // lane holds U[row][a*32 + j] for j = 8q + 4g + e (reg 4q + e), a = ag*8 + ai
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = 8 * q + 4 * g + e;
+          uint32_t pk[4];
+#pragma unroll
+          for (int h = 0; h < 4; ++h)
+            pk[h] = (uint32_t)f2bf(uacc[2 * h][4 * q + e]) | ((uint32_t)f2bf(uacc[2 * h + 1][4 * q + e]) << 16);
+          *reinterpret_cast<uint4*>(A + row * lda + j * MO + ag * 8) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+        }
+    }
+  }
+  if (!rok) return;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int p0 = rb * 32 + 8 * q + 4 * g;
+      if (p0 >= r) continue;
+      const float v[4] = {lacc[rb][4 * q], lacc[rb][4 * q + 1], lacc[rb][4 * q + 2], lacc[rb][4 * q + 3]};
+      uint2 pk;
+      pk.x = (uint32_t)f2bf(lacc[rb][4 * q]) | ((uint32_t)f2bf(lacc[rb][4 * q + 1]) << 16);
+      pk.y = (uint32_t)f2bf(lacc[rb][4 * q + 2]) | ((uint32_t)f2bf(lacc[rb][4 * q + 3]) << 16);
+      *reinterpret_cast<uint2*>(A + row * lda + C + p0) = pk;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Lt[(int64_t)(p0 + e) * ldt + row] = f2bf(v[e]);
+    }
+}
+
+// Stage 2 fused with the residual correction and bias: a wave computes 32
+// rows x 128 output columns (4 blocks j): y_j = V_j B2_j + L R_b[:, j] + bias.
+template <int RB>
+__global__ __launch_bounds__(256) void s6_monarch_kernel(const bf16_t* __restrict__ A,
+                                                         const bf16_t* __restrict__ B2t,
+                                                         const bf16_t* __restrict__ Rt,
+                                                         const bf16_t* __restrict__ bias, bf16_t* __restrict__ Y,
+                                                         int64_t n, int r, int64_t seg, int64_t B) {
+  constexpr int C = MO * MO;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int l = lane & 31, g = lane >> 5;
+  const int tiles_n = C / 128;
+  const int64_t m0 = (int64_t)(blockIdx.x / tiles_n) * 128 + w * 32;
+  const int j0 = (blockIdx.x % tiles_n) * 4;
+  const int64_t row = m0 + l;
+  const bool rok = row < n;
+  const int64_t lda = C + r;
+  f32x16 acc[4];
+#pragma unroll
+  for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[jb][v] = 0.f;
+  // V_j B2_j (K = 32: two 16-wide k steps)
+#pragma unroll
+  for (int jb = 0; jb < 4; ++jb) {
+    const int j = j0 + jb;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const uint4 va = rok ? *reinterpret_cast<const uint4*>(A + row * lda + j * MO + 16 * s + 8 * g) : zero4();
+      const uint4 b2 = *reinterpret_cast<const uint4*>(B2t + ((int64_t)j * MO + l) * MO + 16 * s + 8 * g);
+      TT<bf16_t>::mma(acc[jb], b2, va);
+    }
+  }
+  // L R_b for every segment overlapping this wave's 32 rows
+  if (m0 < n) {
+    const int64_t bf = m0 / seg, bl = imin64(B - 1, (imin64(m0 + 32, n) - 1) / seg);
+    for (int64_t b = bf; b <= bl; ++b) {
+      const bool in = rok && row >= b * seg && row < (b + 1) * seg;
+      for (int k0 = 0; k0 < r; k0 += 16) {
+        const int kk = k0 + 8 * g;
+        const uint4 la = (in && kk < r) ? *reinterpret_cast<const uint4*>(A + row * lda + C + kk) : zero4();
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) {
+          const int64_t col = (int64_t)(j0 + jb) * MO + l;
+          const uint4 rt = kk < r ? *reinterpret_cast<const uint4*>(Rt + col * (B * r) + b * r + kk) : zero4();
+          TT<bf16_t>::mma(acc[jb], rt, la);
+        }
+      }
+    }
+  }
+  if (!rok) return;
+#pragma unroll
+  for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int col = (j0 + jb) * MO + 8 * q + 4 * g;
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = acc[jb][4 * q + e] + (bias ? bf2f(bias[col + e]) : 0.f);
+      uint2 pk;
+      pk.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+      pk.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+      *reinterpret_cast<uint2*>(Y + row * C + col) = pk;
+    }
+}
+
+// ===========================================================================
+// BLAST fused output: for output block column j (width b2 = c2 / nb), the
+// static part is W'_j V_j^T with W' = Z S (the coupled block-row outputs),
+// then the residual correction L R_b and the bias, as one phased GEMM.
+// The tile width divides b2, so every tile lies inside one block column.
+// ===========================================================================
+
+template <class C>
+__global__ __launch_bounds__(C::NT) void s6_blast_kernel(const bf16_t* Wp, int64_t ldw, const bf16_t* ZL,
+                                                         int64_t ldzl, int64_t loff, const bf16_t* Vb,
+                                                         const bf16_t* Rt, const bf16_t* bias, bf16_t* Y,
+                                                         int64_t n, int64_t c2, int64_t b2, int rb, int r,
+                                                         int64_t seg, int64_t B, int tiles_n) {
+  constexpr int E = 2;
+  __shared__ __attribute__((aligned(16))) char lds[C::LDS];
+  const int t = xcd_tile_id(blockIdx.x, gridDim.x);
+  const int64_t m0 = (int64_t)(t / tiles_n) * C::BM, n0 = (int64_t)(t % tiles_n) * C::BN;
+  const int64_t j = n0 / b2;
+  const int64_t bfirst = m0 / seg;
+  const int64_t blast = imin64(B - 1, (imin64(m0 + C::BM, n) - 1) / seg);
+  const int nk0 = ktiles((int64_t)rb * E), nkr = ktiles((int64_t)r * E);
+  const int total = nk0 + (int)(blast - bfirst + 1) * nkr;
+  const char* Wpc = reinterpret_cast<const char*>(Wp + j * rb);
+  const char* Vbc = reinterpret_cast<const char*>(Vb + j * b2 * rb);
+  const char* Lc = reinterpret_cast<const char*>(ZL + loff);
+  auto src = [=](int tt, Phase& ph, int& kt) {
+    if (tt < nk0) {
+      ph.a = OpK{Wpc, ldw * E, m0, 0, n, (int64_t)rb * E};
+      ph.b = OpK{Vbc, (int64_t)rb * E, n0 - j * b2, 0, b2, (int64_t)rb * E};
+      kt = tt;
+      return;
+    }
+    const int u = tt - nk0;
+    const int64_t b = bfirst + u / nkr;
+    kt = u % nkr;
+    ph.a = OpK{Lc, ldzl * E, m0, b * seg, imin64((b + 1) * seg, n), (int64_t)r * E};
+    ph.b = OpK{reinterpret_cast<const char*>(Rt + b * r), B * r * E, n0, 0, c2, (int64_t)r * E};
+  };
+  f32x16 acc[C::FM][C::FN];
+  gemm_mainloop<C>(src, total, lds, acc);
+  stage_out<C>(lds, acc, bias ? bias + n0 : nullptr, (int)(c2 - n0));
+  copy_out<C>(lds, reinterpret_cast<char*>(Y) + (m0 * c2 + n0) * E, c2 * E, (int)imin64(C::BM, n - m0),
+              (c2 - n0) * E);
 }
 
 // ===========================================================================
@@ -629,13 +832,10 @@ __global__ __launch_bounds__(S3_NT, NRB <= 4 ? 2 : 1) void s3_reduce_solve_kerne
 constexpr int SW_NT = 1024;
 constexpr int SW_EPT = 16;   // 128 * 128 / 1024
 
-__global__ __launch_bounds__(SW_NT) void sweep_inverse_kernel(const float* G, float* Ginv, int32_t* status,
-                                                              int r, float eps) {
-  __shared__ float cv[2][128];
-  __shared__ float red[SW_NT / 64];
-  const int64_t b = blockIdx.x;
-  const float* Gb = G + b * r * r;
-  float* Ob = Ginv + b * r * r;
+// Body of the 1024-thread sweep: reads G_b from global, writes Ginv_b and
+// returns the status (identical in every thread).  cv: 2 x 128 floats of
+// LDS, red: SW_NT / 64 floats of LDS.
+__device__ int sweep_inverse_1024(const float* Gb, float* Ob, int r, float eps, float (*cv)[128], float* red) {
   const int tid = threadIdx.x;
   const int rr = r * r;
   float a[SW_EPT];
@@ -687,7 +887,16 @@ __global__ __launch_bounds__(SW_NT) void sweep_inverse_kernel(const float* G, fl
     const int e = tid + q * SW_NT;
     if (e < rr) Ob[e] = st == DYRA_SOLVE_OK ? -a[q] : 0.f;
   }
-  if (tid == 0) status[b] = st;
+  return st;
+}
+
+__global__ __launch_bounds__(SW_NT) void sweep_inverse_kernel(const float* G, float* Ginv, int32_t* status,
+                                                              int r, float eps) {
+  __shared__ float cv[2][128];
+  __shared__ float red[SW_NT / 64];
+  const int64_t b = blockIdx.x;
+  const int st = sweep_inverse_1024(G + b * r * r, Ginv + b * r * r, r, eps, cv, red);
+  if (threadIdx.x == 0) status[b] = st;
 }
 
 // ===========================================================================
@@ -810,9 +1019,15 @@ __global__ __launch_bounds__(1024) void ns_inverse_kernel(const float* G, float*
     __syncthreads();
     ++it;
   }
-  if (ok && !converged && st == DYRA_SOLVE_OK) st = DYRA_SOLVE_NOCONV;
-  if (!ok && st == DYRA_SOLVE_OK) st = DYRA_SOLVE_NOT_SPD;
-  const bool good = st == DYRA_SOLVE_OK || st == DYRA_SOLVE_NOCONV;
+  if (st == DYRA_SOLVE_OK && !(ok && converged)) {
+    // Newton-Schulz stalled above tolerance (fp32 with a very ill-conditioned
+    // G) or broke down: solve by the sweep instead, flagged in the status.
+    __syncthreads();
+    const int sst = sweep_inverse_1024(Gb, Ginv + b * r * r, r, eps, reinterpret_cast<float(*)[128]>(Ts), red);
+    if (tid == 0) status[b] = sst == DYRA_SOLVE_OK ? DYRA_SOLVE_FALLBACK : sst;
+    return;
+  }
+  const bool good = st == DYRA_SOLVE_OK;
   for (int e = tid; e < r * r; e += 1024) {
     const int i = e / r, j = e % r;
     const float v = good ? dsc[i] * Xs[i * NS_P + j] * dsc[j] : 0.f;
@@ -898,17 +1113,21 @@ typedef GemmCfg<float, 64, 64, 2, 2> CfgF3;     // S3, fp32
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// C[M x N] (+)= A[M x K] B[N x K]^T (+ bias) for `batch` problems whose
+// operands are `sA/sB/sC` elements apart.
 template <class C>
 void launch_gemm_tn(const void* A, int64_t lda_el, const void* B, int64_t ldb_el, void* Cm, int64_t ldc_el,
-                    int64_t M, int64_t N, int64_t K, const void* bias, hipStream_t st) {
+                    int64_t M, int64_t N, int64_t K, const void* bias, hipStream_t st, int batch = 1,
+                    int64_t sA = 0, int64_t sB = 0, int64_t sC = 0) {
   typedef typename C::elem T;
+  constexpr int E = TT<T>::ESZ;
   const int tiles_n = (int)cdiv(N, C::BN);
   const int64_t tiles = cdiv(M, C::BM) * tiles_n;
-  if (tiles <= 0) return;
-  hipLaunchKernelGGL(gemm_tn_kernel<C>, dim3((unsigned)tiles), dim3(C::NT), 0, st,
-                     reinterpret_cast<const char*>(A), lda_el * TT<T>::ESZ, reinterpret_cast<const char*>(B),
-                     ldb_el * TT<T>::ESZ, reinterpret_cast<char*>(Cm), ldc_el * TT<T>::ESZ, M, N, K,
-                     reinterpret_cast<const T*>(bias), tiles_n);
+  if (tiles <= 0 || batch <= 0) return;
+  hipLaunchKernelGGL(gemm_tn_kernel<C>, dim3((unsigned)(tiles * batch)), dim3(C::NT), 0, st,
+                     reinterpret_cast<const char*>(A), lda_el * E, reinterpret_cast<const char*>(B), ldb_el * E,
+                     reinterpret_cast<char*>(Cm), ldc_el * E, M, N, K, reinterpret_cast<const T*>(bias), tiles_n,
+                     sA * E, sB * E, sC * E, (int)tiles);
 }
 
 inline int64_t lt_pitch(int64_t n) { return cdiv(n, 256) * 256; }
@@ -933,21 +1152,19 @@ void launch_s3_bf16(const bf16_t* Lt, int64_t ldt, const bf16_t* X, int64_t c1, 
                      ldt, X, c1, r, seg, n, B, M, G, Gi, stat, eps, sweep ? 1 : 0, strips);
 }
 
-template <class C, class C3, class C6>
-int forward_lowrank(const dyra_spec& s, const char* plan, const void* X, const void* bias, void* Y,
-                    int64_t B, int64_t seg, float eps, int solver, char* ws, hipStream_t st,
-                    const StageEvents& E) {
+// S3, S4 and S5, shared by every structure: M_b, G_b, Ginv_b, M'_b and
+// R^T = W_res^T M'^T.  Needs L^T (Lt, pitch ldt) and X.
+template <class C, class C3>
+void forward_residual(const dyra_spec& s, const char* plan, const void* X, int64_t B, int64_t seg, float eps,
+                      int solver, char* ws, hipStream_t st, const StageEvents& E) {
   typedef typename C::elem T;
   constexpr bool BF = TT<T>::ESZ == 2;
   const int dtype = BF ? DYRA_BF16 : DYRA_F32;
   const PlanLayout PL = plan_layout(s, dtype);
   const WsLayout WL = ws_layout(s, B, seg, dtype);
   const int64_t n = B * seg, c1 = s.c1, c2 = s.c2;
-  const int k = s.k, r = s.r;
-  const T* UPt = reinterpret_cast<const T*>(plan + PL.UPt);
-  const T* Vt = reinterpret_cast<const T*>(plan + PL.Vt);
+  const int r = s.r;
   const T* Wrt = reinterpret_cast<const T*>(plan + PL.Wrt);
-  T* TL = reinterpret_cast<T*>(ws + WL.A);
   T* Lt = reinterpret_cast<T*>(ws + WL.Lt);
   float* G = reinterpret_cast<float*>(ws + WL.G);
   float* M = reinterpret_cast<float*>(ws + WL.M);
@@ -957,15 +1174,6 @@ int forward_lowrank(const dyra_spec& s, const char* plan, const void* X, const v
   int32_t* stat = reinterpret_cast<int32_t*>(ws + WL.status);
   const int64_t ldt = lt_pitch(n);
   const bool ns = solver == DYRA_SOLVER_NS || (solver == DYRA_SOLVER_AUTO && r >= 128);
-
-  E.mark(0, st);
-  {  // S1: [T | L] = X [U | P], L^T
-    const int tiles_n = (int)cdiv(k + r, C::BN);
-    const int64_t tiles = cdiv(n, C::BM) * tiles_n;
-    hipLaunchKernelGGL(s1_lowrank_kernel<C>, dim3((unsigned)tiles), dim3(C::NT), 0, st,
-                       reinterpret_cast<const T*>(X), UPt, TL, Lt, n, c1, k, r, ldt, tiles_n);
-  }
-  E.mark(1, st);
   // S3: M_b, G_b (bf16: with the sweep solve in the same launch)
   bool solved = false;
   if constexpr (BF) {
@@ -995,13 +1203,127 @@ int forward_lowrank(const dyra_spec& s, const char* plan, const void* X, const v
   E.mark(3, st);
   // S5: R^T (c2 x B r) = W_res^T (c2 x c1) . M' (B r x c1)^T
   launch_gemm_tn<C>(Wrt, c1, Mp, c1, Rt, B * r, c2, B * r, c1, nullptr, st);
+}
+
+template <class C, class C3, class C6>
+int forward_lowrank(const dyra_spec& s, const char* plan, const void* X, const void* bias, void* Y,
+                    int64_t B, int64_t seg, float eps, int solver, char* ws, hipStream_t st,
+                    const StageEvents& E) {
+  typedef typename C::elem T;
+  const int dtype = TT<T>::ESZ == 2 ? DYRA_BF16 : DYRA_F32;
+  const PlanLayout PL = plan_layout(s, dtype);
+  const WsLayout WL = ws_layout(s, B, seg, dtype);
+  const int64_t n = B * seg, c1 = s.c1, c2 = s.c2;
+  const int k = s.k, r = s.r;
+  T* TL = reinterpret_cast<T*>(ws + WL.A);
+  T* Lt = reinterpret_cast<T*>(ws + WL.Lt);
+  T* Rt = reinterpret_cast<T*>(ws + WL.Rt);
+  E.mark(0, st);
+  {  // S1: [T | L] = X [U | P], L^T
+    const int tiles_n = (int)cdiv(k + r, C::BN);
+    const int64_t tiles = cdiv(n, C::BM) * tiles_n;
+    hipLaunchKernelGGL(s1_lowrank_kernel<C>, dim3((unsigned)tiles), dim3(C::NT), 0, st,
+                       reinterpret_cast<const T*>(X), reinterpret_cast<const T*>(plan + PL.UPt), TL, Lt, n, c1, k,
+                       r, lt_pitch(n), tiles_n, (int64_t)(k + r));
+  }
+  E.mark(1, st);
+  forward_residual<C, C3>(s, plan, X, B, seg, eps, solver, ws, st, E);
   E.mark(4, st);
   {  // S6: Y = T V + L R_b + bias
     const int tiles_n = (int)cdiv(c2, C6::BN);
     const int64_t tiles = cdiv(n, C6::BM) * tiles_n;
-    hipLaunchKernelGGL(s6_lowrank_kernel<C6>, dim3((unsigned)tiles), dim3(C6::NT), 0, st, TL, Vt, Rt,
-                       reinterpret_cast<const T*>(bias), reinterpret_cast<T*>(Y), n, c2, k, r, seg, B,
-                       tiles_n);
+    hipLaunchKernelGGL(s6_lowrank_kernel<C6>, dim3((unsigned)tiles), dim3(C6::NT), 0, st, TL,
+                       reinterpret_cast<const T*>(plan + PL.Vt), Rt, reinterpret_cast<const T*>(bias),
+                       reinterpret_cast<T*>(Y), n, c2, k, r, seg, B, tiles_n);
+  }
+  E.mark(5, st);
+  return hipGetLastError() == hipSuccess ? DYRA_OK : DYRA_EHIP;
+}
+
+template <int RB>
+void launch_monarch(const bf16_t* X, const char* plan, const PlanLayout& PL, bf16_t* A, bf16_t* Lt, int64_t n,
+                    int r, int64_t ldt, hipStream_t st) {
+  hipLaunchKernelGGL((s1_monarch_kernel<RB>), dim3((unsigned)cdiv(n, 128)), dim3(256), 0, st, X,
+                     reinterpret_cast<const bf16_t*>(plan + PL.B1t), reinterpret_cast<const bf16_t*>(plan + PL.Pt),
+                     A, Lt, n, r, ldt);
+}
+
+template <int RB>
+void launch_monarch6(const bf16_t* A, const char* plan, const PlanLayout& PL, const bf16_t* Rt, const bf16_t* bias,
+                     bf16_t* Y, int64_t n, int r, int64_t seg, int64_t B, hipStream_t st) {
+  hipLaunchKernelGGL((s6_monarch_kernel<RB>), dim3((unsigned)(cdiv(n, 128) * (MO * MO / 128))), dim3(256), 0, st,
+                     A, reinterpret_cast<const bf16_t*>(plan + PL.B2t), Rt, bias, Y, n, r, seg, B);
+}
+
+int forward_monarch(const dyra_spec& s, const char* plan, const void* X, const void* bias, void* Y, int64_t B,
+                    int64_t seg, float eps, int solver, char* ws, hipStream_t st, const StageEvents& E) {
+  const PlanLayout PL = plan_layout(s, DYRA_BF16);
+  const WsLayout WL = ws_layout(s, B, seg, DYRA_BF16);
+  const int64_t n = B * seg;
+  const int r = s.r;
+  bf16_t* A = reinterpret_cast<bf16_t*>(ws + WL.A);
+  bf16_t* Lt = reinterpret_cast<bf16_t*>(ws + WL.Lt);
+  const bf16_t* Xb = reinterpret_cast<const bf16_t*>(X);
+  const int64_t ldt = lt_pitch(n);
+  E.mark(0, st);
+  if (r <= 32) launch_monarch<1>(Xb, plan, PL, A, Lt, n, r, ldt, st);
+  else if (r <= 64) launch_monarch<2>(Xb, plan, PL, A, Lt, n, r, ldt, st);
+  else launch_monarch<4>(Xb, plan, PL, A, Lt, n, r, ldt, st);
+  E.mark(1, st);
+  forward_residual<CfgB, CfgB3>(s, plan, X, B, seg, eps, solver, ws, st, E);
+  E.mark(4, st);
+  const bf16_t* Rt = reinterpret_cast<const bf16_t*>(ws + WL.Rt);
+  const bf16_t* bb = reinterpret_cast<const bf16_t*>(bias);
+  bf16_t* Yb = reinterpret_cast<bf16_t*>(Y);
+  if (r <= 32) launch_monarch6<1>(A, plan, PL, Rt, bb, Yb, n, r, seg, B, st);
+  else if (r <= 64) launch_monarch6<2>(A, plan, PL, Rt, bb, Yb, n, r, seg, B, st);
+  else launch_monarch6<4>(A, plan, PL, Rt, bb, Yb, n, r, seg, B, st);
+  E.mark(5, st);
+  return hipGetLastError() == hipSuccess ? DYRA_OK : DYRA_EHIP;
+}
+
+int forward_blast(const dyra_spec& s, const char* plan, const void* X, const void* bias, void* Y, int64_t B,
+                  int64_t seg, float eps, int solver, char* ws, hipStream_t st, const StageEvents& E) {
+  const PlanLayout PL = plan_layout(s, DYRA_BF16);
+  const WsLayout WL = ws_layout(s, B, seg, DYRA_BF16);
+  const int64_t n = B * seg, c1 = s.c1, c2 = s.c2;
+  const int r = s.r, nb = s.nb, rb = s.rb;
+  const int64_t b1 = c1 / nb, b2 = c2 / nb, NR = (int64_t)nb * rb, ldzl = NR + r;
+  bf16_t* ZL = reinterpret_cast<bf16_t*>(ws + WL.A);
+  bf16_t* Wp = reinterpret_cast<bf16_t*>(ws + WL.Wp);
+  bf16_t* Lt = reinterpret_cast<bf16_t*>(ws + WL.Lt);
+  const bf16_t* Xb = reinterpret_cast<const bf16_t*>(X);
+  E.mark(0, st);
+  // S1: Z_i = X_i U_i for every block row i (batched), and L = X P with L^T
+  launch_gemm_tn<CfgB>(Xb, c1, plan + PL.Ubt, b1, ZL, ldzl, n, rb, b1, nullptr, st, nb, b1, (int64_t)rb * b1, rb);
+  {
+    const int tiles_n = (int)cdiv(r, CfgB::BN);
+    const int64_t tiles = cdiv(n, CfgB::BM) * tiles_n;
+    hipLaunchKernelGGL(s1_lowrank_kernel<CfgB>, dim3((unsigned)tiles), dim3(CfgB::NT), 0, st, Xb,
+                       reinterpret_cast<const bf16_t*>(plan + PL.Pt), ZL + NR, Lt, n, c1, 0, r, lt_pitch(n), tiles_n,
+                       ldzl);
+  }
+  E.mark(1, st);
+  forward_residual<CfgB, CfgB3>(s, plan, X, B, seg, eps, solver, ws, st, E);
+  // coupling W' = Z S (dense over the nb x nb grid of rb x rb blocks)
+  launch_gemm_tn<CfgB>(ZL, ldzl, plan + PL.St, NR, Wp, NR, n, NR, NR, nullptr, st);
+  E.mark(4, st);
+  {
+    typedef CfgB6 C6;
+    const bf16_t* Rt = reinterpret_cast<const bf16_t*>(ws + WL.Rt);
+    if (b2 % C6::BN == 0) {
+      const int tiles_n = (int)(c2 / C6::BN);
+      const int64_t tiles = cdiv(n, C6::BM) * tiles_n;
+      hipLaunchKernelGGL(s6_blast_kernel<C6>, dim3((unsigned)tiles), dim3(C6::NT), 0, st, Wp, NR, ZL, ldzl, NR,
+                         reinterpret_cast<const bf16_t*>(plan + PL.Vb), Rt, reinterpret_cast<const bf16_t*>(bias),
+                         reinterpret_cast<bf16_t*>(Y), n, c2, b2, rb, r, seg, B, tiles_n);
+    } else {
+      const int tiles_n = (int)(c2 / CfgB::BN);
+      const int64_t tiles = cdiv(n, CfgB::BM) * tiles_n;
+      hipLaunchKernelGGL(s6_blast_kernel<CfgB>, dim3((unsigned)tiles), dim3(CfgB::NT), 0, st, Wp, NR, ZL, ldzl, NR,
+                         reinterpret_cast<const bf16_t*>(plan + PL.Vb), Rt, reinterpret_cast<const bf16_t*>(bias),
+                         reinterpret_cast<bf16_t*>(Y), n, c2, b2, rb, r, seg, B, tiles_n);
+    }
   }
   E.mark(5, st);
   return hipGetLastError() == hipSuccess ? DYRA_OK : DYRA_EHIP;
@@ -1022,7 +1344,6 @@ int check_forward_args(const dyra_spec* spec, const void* plan, const void* X, v
        reinterpret_cast<uintptr_t>(ws)) & 15)
     return DYRA_EINVAL;
   if (ws_bytes < ws_layout(*spec, B, s, dtype).total) return DYRA_EWORKSPACE;
-  if (spec->kind != DYRA_LOWRANK) return DYRA_EDTYPE;
   return DYRA_OK;
 }
 
@@ -1049,6 +1370,9 @@ int forward_impl(const dyra_spec* spec, const void* plan, const void* X, const v
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const char* plan_c = reinterpret_cast<const char*>(plan);
   char* ws = reinterpret_cast<char*>(workspace);
+  if (spec->kind == DYRA_MONARCH)
+    return forward_monarch(*spec, plan_c, X, bias, Y, B, s, ridge_eps, solver, ws, st, E);
+  if (spec->kind == DYRA_BLAST) return forward_blast(*spec, plan_c, X, bias, Y, B, s, ridge_eps, solver, ws, st, E);
   if (dtype == DYRA_BF16)
     return forward_lowrank<CfgB, CfgB3, CfgB6>(*spec, plan_c, X, bias, Y, B, s, ridge_eps, solver, ws, st, E);
   return forward_lowrank<CfgF, CfgF3, CfgF>(*spec, plan_c, X, bias, Y, B, s, ridge_eps, solver, ws, st, E);

@@ -46,7 +46,7 @@ inline int validate_dtype(const dyra_spec& s, int dtype) {
     if (dtype != DYRA_BF16 || s.mblk != 32) return DYRA_EDTYPE;
   }
   if (s.kind == DYRA_BLAST) {
-    if (dtype != DYRA_BF16 || s.rb % 32 || (s.c1 / s.nb) % 32 || (s.c2 / s.nb) % 32) return DYRA_EDTYPE;
+    if (dtype != DYRA_BF16 || s.rb % 8 || (s.c1 / s.nb) % 8 || (s.c2 / s.nb) % 128) return DYRA_EDTYPE;
   }
   return DYRA_OK;
 }

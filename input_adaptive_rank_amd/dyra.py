@@ -27,7 +27,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 
 SOLVER_AUTO, SOLVER_CHOL, SOLVER_NS = 0, 1, 2
 SOLVERS = {"auto": SOLVER_AUTO, "chol": SOLVER_CHOL, "ns": SOLVER_NS}
-SOLVE_OK, SOLVE_NOT_SPD, SOLVE_NOCONV, SOLVE_ZERO = 0, 1, 2, 3
+SOLVE_OK, SOLVE_NOT_SPD, SOLVE_NOCONV, SOLVE_ZERO, SOLVE_FALLBACK = 0, 1, 2, 3, 4
 
 ERRORS = {0: "DYRA_OK", -1: "DYRA_EINVAL", -2: "DYRA_ESHAPE", -3: "DYRA_EWORKSPACE",
           -4: "DYRA_EHIP", -5: "DYRA_ENOCONV", -6: "DYRA_EDTYPE"}

@@ -53,7 +53,7 @@ def test_segment_shorter_than_rank():
     run_same_factor_case(w, eps=1e-3)
 
 
-@pytest.mark.parametrize("name", ["vitb_fc1", "vitl_fc1"])
+@pytest.mark.parametrize("name", ["vitb_fc1", "vitl_fc1", "vitl_fc2"])
 def test_full_size(name):
     w = W[name]
     err, status, _, _ = run_same_factor_case(w)

@@ -1,0 +1,70 @@
+"""GPU parity of the Monarch and BLAST DyRA forwards against the float64
+oracle (same seeded inputs, same storage-rounded factors).  Bar: relative
+Frobenius error <= 2e-2 (bf16 storage, fp32 accumulation)."""
+import numpy as np
+import pytest
+
+from input_adaptive_rank_amd import dyra as D
+from input_adaptive_rank_amd import synth
+
+from gpu_cases import run_same_factor_case
+
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS
+sc = synth.scaled
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    D.lib()
+
+
+MONARCH = [
+    sc(W["monarch"], name="monarch_ragged_r64", B=3, s=77),
+    sc(W["monarch"], name="monarch_r32", B=2, s=130, r=32),
+    sc(W["monarch"], name="monarch_r8_short_segments", B=9, s=11, r=8),
+    sc(W["monarch"], name="monarch_r128_chol", B=2, s=300, r=128, solver="chol"),
+]
+
+BLAST = [
+    sc(W["lm_blast"], name="blast_small_chol", B=2, s=200, c1=512, c2=1536, nb=4, rb=32, r=32, solver="auto",
+       n_out=4),
+    sc(W["lm_blast"], name="blast_small_ns", B=1, s=300, c1=512, c2=1536, nb=4, rb=32, r=64, solver="ns",
+       n_out=4),
+    sc(W["lm_blast"], name="blast_b2_128", B=3, s=100, c1=256, c2=1024, nb=8, rb=16, r=16, solver="auto",
+       n_out=2),
+]
+
+
+@pytest.mark.parametrize("w", MONARCH, ids=lambda w: w.name)
+def test_monarch_small(w):
+    err, status, _, _ = run_same_factor_case(w, solver=w.solver)
+    assert np.all(status == D.SOLVE_OK)
+
+
+@pytest.mark.parametrize("w", BLAST, ids=lambda w: w.name)
+def test_blast_small(w):
+    err, status, _, _ = run_same_factor_case(w, solver=w.solver)
+    assert np.all(status == D.SOLVE_OK)
+
+
+def test_ns_falls_back_to_sweep_on_ill_conditioned_gram():
+    """cond(G) ~ 3e6 (short segments, r = 128): fp32 Newton-Schulz stalls, the
+    kernel re-solves by the sweep and reports DYRA_SOLVE_FALLBACK."""
+    w = sc(W["monarch"], name="monarch_r128_ns_fallback", B=2, s=300, r=128, solver="ns")
+    err, status, _, _ = run_same_factor_case(w, solver="ns")
+    assert np.all(status == D.SOLVE_FALLBACK)
+
+
+def test_monarch_full_size():
+    err, status, _, _ = run_same_factor_case(W["monarch"])
+    assert np.all(status == D.SOLVE_OK)
+
+
+def test_blast_full_size():
+    w = W["lm_blast"]
+    err, status, _, _ = run_same_factor_case(w, solver=w.solver)
+    assert np.all(status == D.SOLVE_OK)
