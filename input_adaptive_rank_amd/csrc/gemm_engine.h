@@ -51,24 +51,35 @@ struct TileRegs {
   uint4 b[C::BCH];
 };
 
-__device__ __forceinline__ uint4 load_opk(const OpK& o, int row, int64_t kb) {
+// Operand loads are raw buffer loads relative to the tile's first row: a
+// chunk outside the operand (row mask or k extent) gets an out-of-range
+// offset and reads as zero, so the loads are branch-free and the compiler can
+// keep several k-tiles in flight.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const OpK& o) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(o.ptr + o.row0 * o.ld), (short)0, 0x7fffffff,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ uint4 load_opk(const OpK& o, __amdgpu_buffer_rsrc_t rs, int row, int kb) {
   const int64_t grow = o.row0 + row;
   const bool ok = grow >= o.row_lo && grow < o.row_hi && kb < o.kbytes;
-  return ok ? *reinterpret_cast<const uint4*>(o.ptr + grow * o.ld + kb) : zero4();
+  const int off = ok ? (int)(row * o.ld) + kb : (int)0x80000000u;
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
 }
 
 template <class C>
 __device__ __forceinline__ void load_tile(const Phase& ph, int kt, TileRegs<C>& r, int tid) {
-  const int64_t kb = (int64_t)kt * 128;
+  const int kb = kt * 128;
+  const __amdgpu_buffer_rsrc_t ra = tile_rsrc(ph.a), rb = tile_rsrc(ph.b);
 #pragma unroll
   for (int i = 0; i < C::ACH; ++i) {
     const int c = tid + i * C::NT;
-    r.a[i] = load_opk(ph.a, c >> 3, kb + (c & 7) * 16);
+    r.a[i] = load_opk(ph.a, ra, c >> 3, kb + (c & 7) * 16);
   }
 #pragma unroll
   for (int i = 0; i < C::BCH; ++i) {
     const int c = tid + i * C::NT;
-    r.b[i] = load_opk(ph.b, c >> 3, kb + (c & 7) * 16);
+    r.b[i] = load_opk(ph.b, rb, c >> 3, kb + (c & 7) * 16);
   }
 }
 
@@ -180,10 +191,13 @@ __device__ __forceinline__ void stage_out(char* lds, const f32x16 (&acc)[C::FM][
         float v0 = acc[fm][fn][4 * q + 0], v1 = acc[fm][fn][4 * q + 1];
         float v2 = acc[fm][fn][4 * q + 2], v3 = acc[fm][fn][4 * q + 3];
         if (bias != nullptr && col < bias_n) {
-          v0 += TT<T>::to_f(bias[col + 0]);
-          v1 += TT<T>::to_f(bias[col + 1]);
-          v2 += TT<T>::to_f(bias[col + 2]);
-          v3 += TT<T>::to_f(bias[col + 3]);
+          T b4[4];
+          if constexpr (TT<T>::ESZ == 2) *reinterpret_cast<uint2*>(b4) = *reinterpret_cast<const uint2*>(bias + col);
+          else *reinterpret_cast<float4*>(b4) = *reinterpret_cast<const float4*>(bias + col);
+          v0 += TT<T>::to_f(b4[0]);
+          v1 += TT<T>::to_f(b4[1]);
+          v2 += TT<T>::to_f(b4[2]);
+          v3 += TT<T>::to_f(b4[3]);
         }
         if constexpr (TT<T>::ESZ == 2) {
           uint2 pk;
