@@ -513,6 +513,176 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 }
 
 // ===========================================================================
+// S4a: (G + lambda I)^-1 by the symmetric sweep operator, SW_BK pivots at a
+// time.  Sweeping an index block K of a symmetric A gives
+//   A'_KK = -A_KK^-1,  A'_KJ = A_KK^-1 A_KJ,  A'_JJ = A_JJ - A_JK A_KK^-1 A_KJ
+// (J: the other indices), i.e. a'_ij = [i, j not in K] a_ij - (C A_KK^-1 C^T)_ij
+// with C = A_{:,K} whose rows in K are replaced by -I.  Sweeping every block
+// in turn leaves -(G + lambda I)^-1, the same operator as one pivot at a time
+// (the sweep is order independent) with one barrier per block instead of per
+// pivot.  Thread t owns a TB x TB tile of A.  The pivot rows of a block (its
+// columns, by symmetry) are broadcast through LDS, double-buffered; every
+// thread inverts the SW_BK x SW_BK pivot block itself by sweeping its pivots
+// one by one.  A pivot <= 0 (or not finite) marks the matrix as not positive
+// definite.
+// ===========================================================================
+
+constexpr int SW_BK = 4;
+struct SweepLds {
+  double pv[2][SW_BK][128];
+  float red[16];
+};
+
+// 1 / D for D > 0: hardware reciprocal estimate refined by two Newton steps
+// (x <- x + x (1 - D x)), which reach full double precision.
+__device__ __forceinline__ double recip_pos(double D) {
+  double x = __builtin_amdgcn_rcp(D);
+  double e = fma(-D, x, 1.0);
+  x = fma(x, e, x);
+  e = fma(-D, x, 1.0);
+  return fma(x, e, x);
+}
+
+// Gb: r x r row-major fp32 (global or LDS); Ob: r x r row-major fp32,
+// receives the inverse (zeros unless the status is OK).  The arithmetic is
+// fp64: the ridge bounds cond(G + lambda I) only by about r / eps (~1e8 for
+// eps = 1e-6), past what fp32 elimination survives.  Needs r % SW_BK == 0,
+// r <= 128 and ceil(r / TB)^2 <= NT.  Returns the status (same in every
+// thread).
+template <int NT, int TB>
+__device__ __forceinline__ int sweep_inverse(const float* Gb, float* Ob, int r, float eps, SweepLds& sh) {
+  static_assert(TB % SW_BK == 0 && TB % 2 == 0, "tile");
+  const int tid = threadIdx.x;
+  const int tpr = (r + TB - 1) / TB;
+  const int i0 = (tid / tpr) * TB, j0 = (tid % tpr) * TB;
+  const bool own = i0 < r;
+  double a[TB][TB];
+  float trf = 0.f;
+#pragma unroll
+  for (int x = 0; x < TB; ++x)
+#pragma unroll
+    for (int y = 0; y < TB; ++y) {
+      const bool v = own && i0 + x < r && j0 + y < r;
+      const float g = v ? Gb[(i0 + x) * r + j0 + y] : 0.f;
+      a[x][y] = g;
+      if (v && x + i0 == y + j0) trf += g;
+    }
+  const float tr = block_sum<NT>(trf, sh.red);
+  int st = DYRA_SOLVE_OK;
+  if (tr == 0.f) st = DYRA_SOLVE_ZERO;
+  else if (!(tr > 0.f) || !isfinite(tr)) st = DYRA_SOLVE_NOT_SPD;
+  // rows k0 .. k0 + SW_BK - 1 of this tile (if it holds them) -> pv[buf]
+  auto publish_row = [&](int x, int k0, int buf) {
+    const int i = i0 + x;
+    if (own && i >= k0 && i < k0 + SW_BK) {
+#pragma unroll
+      for (int y = 0; y < TB; y += 2)
+        if (j0 + y < r)
+          *reinterpret_cast<double2*>(&sh.pv[buf][i - k0][j0 + y]) = make_double2(a[x][y], a[x][y + 1]);
+    }
+  };
+  if (st == DYRA_SOLVE_OK) {
+    const double lam = (double)(eps * tr / (float)r);
+#pragma unroll
+    for (int x = 0; x < TB; ++x)
+#pragma unroll
+      for (int y = 0; y < TB; ++y)
+        if (own && x + i0 == y + j0) a[x][y] += lam;
+#pragma unroll
+    for (int x = 0; x < TB; ++x) publish_row(x, 0, 0);
+    __syncthreads();
+    for (int kb = 0, blk = 0; kb < r; kb += SW_BK, ++blk) {
+      const double(*buf)[128] = sh.pv[blk & 1];
+      // Q <- -A_KK^-1 by sweeping the pivot block's own pivots
+      double Q[SW_BK][SW_BK];
+#pragma unroll
+      for (int x = 0; x < SW_BK; ++x)
+#pragma unroll
+        for (int y = 0; y < SW_BK; y += 2) {
+          const double2 v = *reinterpret_cast<const double2*>(&buf[x][kb + y]);
+          Q[x][y] = v.x;
+          Q[x][y + 1] = v.y;
+        }
+      bool bad = false;
+#pragma unroll
+      for (int p = 0; p < SW_BK; ++p) {
+        const double D = Q[p][p];
+        if (!(D > 0.0) || !isfinite(D)) bad = true;
+        const double invD = recip_pos(D);
+        double c[SW_BK];
+#pragma unroll
+        for (int x = 0; x < SW_BK; ++x) c[x] = x == p ? -1.0 : Q[x][p];
+#pragma unroll
+        for (int x = 0; x < SW_BK; ++x) {
+          const double f = -c[x] * invD;
+#pragma unroll
+          for (int y = 0; y < SW_BK; ++y) Q[x][y] = fma(f, c[y], (x == p || y == p) ? 0.0 : Q[x][y]);
+        }
+      }
+      if (bad) {   // uniform: every thread read the same pivot block
+        st = DYRA_SOLVE_NOT_SPD;
+        break;
+      }
+      // the block's rows/columns sit at tile offset kb - i0 / kb - j0
+      // (a multiple of SW_BK) when this tile holds them
+      const int oi = kb - i0, oj = kb - j0;
+      // C_j = pivot rows at this tile's columns
+      double cj[SW_BK][TB];
+#pragma unroll
+      for (int p = 0; p < SW_BK; ++p)
+#pragma unroll
+        for (int y = 0; y < TB; y += 2) {
+          const double2 v = *reinterpret_cast<const double2*>(&buf[p][j0 + y]);
+          cj[p][y] = v.x;
+          cj[p][y + 1] = v.y;
+        }
+#pragma unroll
+      for (int x = 0; x < TB; x += 2) {
+        // C_i for rows x, x + 1: pivot rows at column i (symmetry)
+        double ci[2][SW_BK];
+#pragma unroll
+        for (int q = 0; q < SW_BK; ++q) {
+          const double2 v = own ? *reinterpret_cast<const double2*>(&buf[q][i0 + x]) : make_double2(0.0, 0.0);
+          ci[0][q] = v.x;
+          ci[1][q] = v.y;
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int xx = x + h;
+          const bool iK = oi == (xx & ~(SW_BK - 1));
+          // d = C_i A_KK^-1 = -C_i Q; a row inside the block has C_i = -e_i
+          double d[SW_BK];
+#pragma unroll
+          for (int p = 0; p < SW_BK; ++p) {
+            double v = 0.0;
+#pragma unroll
+            for (int q = 0; q < SW_BK; ++q) v = fma(ci[h][q], Q[q][p], v);
+            d[p] = iK ? Q[xx & (SW_BK - 1)][p] : -v;
+          }
+#pragma unroll
+          for (int y = 0; y < TB; ++y) {
+            const bool jK = oj == (y & ~(SW_BK - 1));
+            double v = iK ? 0.0 : a[xx][y];
+#pragma unroll
+            for (int p = 0; p < SW_BK; ++p) v = fma(-d[p], cj[p][y], v);
+            // a column inside the block has C_j = -e_j: a_ij <- d_j
+            a[xx][y] = jK ? d[y & (SW_BK - 1)] : v;
+          }
+          publish_row(xx, kb + SW_BK, (blk + 1) & 1);
+        }
+      }
+      __syncthreads();
+    }
+  }
+#pragma unroll
+  for (int x = 0; x < TB; ++x)
+#pragma unroll
+    for (int y = 0; y < TB; ++y)
+      if (own && i0 + x < r && j0 + y < r) Ob[(i0 + x) * r + j0 + y] = st == DYRA_SOLVE_OK ? (float)-a[x][y] : 0.f;
+  return st;
+}
+
+// ===========================================================================
 // S3 (bf16): token reductions without an LDS transpose.
 // Workgroups [0, B): G_b = L_b^T L_b and its inverse (the r x r solve runs
 // here, concurrently with the M strips).  Workgroups [B, ...): one
@@ -528,13 +698,12 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 constexpr int S3_NT = 256;
 constexpr int S3_STRIP = 128;
 // LDS: M strips use 64 KB of partials; the G/solve role uses 16 KB of
-// partials + r*r fp32 G + the 2 x 128 pivot-column buffer + reduction slots.
+// partials + r*r fp32 G + the sweep's pivot-row buffers.
 template <int NB>
 struct S3Lds {
   static constexpr int G_OFF = 16 * 1024;
-  static constexpr int CV_OFF = G_OFF + NB * 32 * NB * 32 * 4;
-  static constexpr int RED_OFF = CV_OFF + 256 * 4;
-  static constexpr int G_END = RED_OFF + 64;
+  static constexpr int SW_OFF = G_OFF + NB * 32 * NB * 32 * 4;
+  static constexpr int G_END = SW_OFF + (int)sizeof(SweepLds);
   static constexpr int BYTES = G_END > 64 * 1024 ? G_END : 64 * 1024;
 };
 
@@ -674,21 +843,30 @@ __device__ __forceinline__ void s3_gram(const bf16_t* __restrict__ Lt, int64_t l
   const int64_t a0 = lo & ~(int64_t)7;
   const int nsteps = (int)((hi - a0 + 15) / 16);
   const int s0 = w * nsteps / 4, s1 = (w + 1) * nsteps / 4;
-  for (int st = s0; st < s1; ++st) {
-    const int64_t t0 = a0 + 16 * (int64_t)st + 8 * g;
-    uint4 f[NB];
+  // PF token steps per round: their loads are all issued before the MFMAs
+  constexpr int PF = NB <= 2 ? 4 : 2;
+  for (int st0 = s0; st0 < s1; st0 += PF) {
+    uint4 f[PF][NB];
 #pragma unroll
-    for (int rb = 0; rb < NB; ++rb) {
-      const int row = rb * 32 + l;
-      uint4 v = (row < r && t0 < ldt) ? *reinterpret_cast<const uint4*>(Lt + row * ldt + t0) : zero4();
-      f[rb] = mask_tokens<bf16_t>(v, t0, lo, hi);
+    for (int u = 0; u < PF; ++u) {
+      const int64_t t0 = a0 + 16 * (int64_t)(st0 + u) + 8 * g;
+      const bool in = st0 + u < s1;
+#pragma unroll
+      for (int rb = 0; rb < NB; ++rb) {
+        const int row = rb * 32 + l;
+        uint4 v = (in && row < r && t0 < ldt) ? *reinterpret_cast<const uint4*>(Lt + row * ldt + t0) : zero4();
+        f[u][rb] = mask_tokens<bf16_t>(v, t0, lo, hi);
+      }
     }
 #pragma unroll
-    for (int a = 0; a < NB; ++a)
+    for (int u = 0; u < PF; ++u)
 #pragma unroll
-      for (int b = 0; b < NB; ++b)
-        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, f[a]),
-                                                            __builtin_bit_cast(bf16x8_t, f[b]), acc[a][b], 0, 0, 0);
+      for (int a = 0; a < NB; ++a)
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, f[u][a]),
+                                                              __builtin_bit_cast(bf16x8_t, f[u][b]), acc[a][b], 0, 0,
+                                                              0);
   }
   // reduce: wave partials through LDS, one 32x32 block pair at a time
   float* part = reinterpret_cast<float*>(lds);   // [4 waves][16 regs][64 lanes]
@@ -711,93 +889,13 @@ __device__ __forceinline__ void s3_gram(const bf16_t* __restrict__ Lt, int64_t l
   __syncthreads();
 }
 
-// Inverse of Gs + lambda I (Gs: r x r fp32 in LDS) by the symmetric sweep
-// (Gauss-Jordan) operator, 256 threads.  Thread t owns JW consecutive
-// entries of one row (row i = t / (r / JW), columns j0 .. j0 + JW - 1), kept
-// in registers; the pivot column is broadcast through LDS (double-buffered,
-// one barrier per pivot).  With c_k = -1 the pivot-row/column rules fold into
-//   a_ij <- [i != k][j != k] a_ij - c_i c_j / a_kk,
-// which after all r pivots leaves -(G + lambda I)^-1.  A pivot <= 0 marks the
-// matrix as not positive definite.  Writes Ginv (fp32) and the status word.
-template <int JW>
-__device__ __forceinline__ void sweep_inverse_256(const float* Gs, int r, float eps, float* Gf, int32_t* status,
-                                                  float* cv /* 2 x 128 */, float* red) {
-  const int tid = threadIdx.x;
-  const int per_row = (r + JW - 1) / JW;   // threads per row (r * per_row <= 256)
-  const int i = tid / per_row, j0 = (tid % per_row) * JW;
-  const bool own = i < r;
-  float a[JW];
-  float tr = 0.f;
-#pragma unroll
-  for (int q = 0; q < JW; ++q) {
-    const bool v = own && j0 + q < r;
-    a[q] = v ? Gs[i * r + j0 + q] : 0.f;
-    if (v && j0 + q == i) tr += a[q];
-  }
-  tr = block_sum<S3_NT>(tr, red);
-  int st = DYRA_SOLVE_OK;
-  if (tr == 0.f) st = DYRA_SOLVE_ZERO;
-  else if (!(tr > 0.f) || !isfinite(tr)) st = DYRA_SOLVE_NOT_SPD;
-  if (st == DYRA_SOLVE_OK) {
-    const float lam = eps * tr / (float)r;
-#pragma unroll
-    for (int q = 0; q < JW; ++q)
-      if (own && j0 + q == i) a[q] += lam;
-    if (own && j0 == 0) cv[i] = a[0];
-    __syncthreads();
-    for (int k = 0; k < r; ++k) {
-      const float* buf = cv + (k & 1) * 128;
-      float* nxt = cv + ((k + 1) & 1) * 128;
-      const float D = buf[k];
-      if (!(D > 0.f) || !isfinite(D)) {
-        st = DYRA_SOLVE_NOT_SPD;
-        break;
-      }
-      const float invD = 1.f / D;
-      float cj[JW];
-#pragma unroll
-      for (int q = 0; q < JW; q += 4) {
-        const float4 v4 = *reinterpret_cast<const float4*>(buf + j0 + q);
-        cj[q] = v4.x;
-        cj[q + 1] = v4.y;
-        cj[q + 2] = v4.z;
-        cj[q + 3] = v4.w;
-      }
-      const bool rowk = i == k;
-      const float ci = rowk ? -1.f : buf[own ? i : 0];
-      const float f = -ci * invD;
-#pragma unroll
-      for (int q = 0; q < JW; ++q) {
-        const bool colk = j0 + q == k;
-        const float c = colk ? -1.f : cj[q];
-        const float base = (rowk || colk) ? 0.f : a[q];
-        a[q] = fmaf(f, c, base);
-      }
-      // publish column k + 1 for the next pivot
-      if (own && k + 1 < r && (k + 1) >= j0 && (k + 1) < j0 + JW) {
-#pragma unroll
-        for (int q = 0; q < JW; ++q)
-          if (j0 + q == k + 1) nxt[i] = a[q];
-      }
-      __syncthreads();
-    }
-  }
-  if (own) {
-#pragma unroll
-    for (int q = 0; q < JW; ++q)
-      if (j0 + q < r) Gf[i * r + j0 + q] = st == DYRA_SOLVE_OK ? -a[q] : 0.f;
-  }
-  if (tid == 0) *status = st;
-}
-
 template <int NRB, int NB>
 __global__ __launch_bounds__(S3_NT, NRB <= 4 ? 2 : 1) void s3_reduce_solve_kernel(
     const bf16_t* __restrict__ Lt, int64_t ldt, const bf16_t* __restrict__ X, int64_t c1, int r, int64_t seg,
     int64_t n, int64_t B, float* __restrict__ M, float* __restrict__ G, float* __restrict__ Gi,
     int32_t* __restrict__ status, float eps, int do_sweep, int strips) {
   __shared__ __attribute__((aligned(16))) char lds[S3Lds<NB>::BYTES];
-  float* cv = reinterpret_cast<float*>(lds + S3Lds<NB>::CV_OFF);
-  float* red = reinterpret_cast<float*>(lds + S3Lds<NB>::RED_OFF);
+  SweepLds* sl = reinterpret_cast<SweepLds*>(lds + S3Lds<NB>::SW_OFF);
   const int64_t bid = blockIdx.x;
   if (bid < B) {
     const int64_t b = bid;
@@ -807,9 +905,10 @@ __global__ __launch_bounds__(S3_NT, NRB <= 4 ? 2 : 1) void s3_reduce_solve_kerne
     // publish G (the Newton-Schulz path and diagnostics read it)
     for (int e = threadIdx.x; e < r * r; e += S3_NT) G[b * r * r + e] = Gs[e];
     if (do_sweep) {
-      // JW entries per thread: r * ceil(r / JW) <= 256 threads for r <= 32 NB
-      constexpr int JW = NB == 1 ? 4 : (NB == 2 ? 16 : 64);
-      sweep_inverse_256<JW>(Gs, r, eps, Gi + b * r * r, status + b, cv, red);
+      // TB x TB tiles: ceil(r / TB)^2 <= 256 threads for r <= 32 NB
+      constexpr int TB = NB <= 2 ? 4 : 8;
+      const int st = sweep_inverse<S3_NT, TB>(Gs, Gi + b * r * r, r, eps, *sl);
+      if (threadIdx.x == 0) status[b] = st;
     }
     return;
   }
@@ -820,83 +919,29 @@ __global__ __launch_bounds__(S3_NT, NRB <= 4 ? 2 : 1) void s3_reduce_solve_kerne
   s3_m_strip<NRB>(Lt, ldt, X, c1, r, lo, hi, c0, M + b * r * c1, lds);
 }
 
-// ===========================================================================
-// S4a: (G + lambda I)^-1 by the symmetric sweep (Gauss-Jordan) operator.
-// One workgroup per segment; the r x r matrix lives in registers (up to 16
-// elements per thread), the pivot column is broadcast through LDS.
-// Sweeping pivot k maps A to A' with A'_ij = A_ij - A_ik A_kj / A_kk,
-// A'_ik = A_ik / A_kk, A'_kk = -1 / A_kk; after all pivots A = -(A_0)^-1.
-// A pivot <= 0 means the matrix is not positive definite.
-// ===========================================================================
-
-constexpr int SW_NT = 1024;
-constexpr int SW_EPT = 16;   // 128 * 128 / 1024
-
-// Body of the 1024-thread sweep: reads G_b from global, writes Ginv_b and
-// returns the status (identical in every thread).  cv: 2 x 128 floats of
-// LDS, red: SW_NT / 64 floats of LDS.
-__device__ int sweep_inverse_1024(const float* Gb, float* Ob, int r, float eps, float (*cv)[128], float* red) {
-  const int tid = threadIdx.x;
-  const int rr = r * r;
-  float a[SW_EPT];
-  int ii[SW_EPT], jj[SW_EPT];
-  float tr = 0.f;
-#pragma unroll
-  for (int q = 0; q < SW_EPT; ++q) {
-    const int e = tid + q * SW_NT;
-    ii[q] = e < rr ? e / r : -1;
-    jj[q] = e < rr ? e % r : -1;
-    a[q] = e < rr ? Gb[e] : 0.f;
-    if (e < rr && ii[q] == jj[q]) tr += a[q];
-  }
-  tr = block_sum<SW_NT>(tr, red);
-  int st = DYRA_SOLVE_OK;
-  if (tr == 0.f) st = DYRA_SOLVE_ZERO;
-  else if (!(tr > 0.f) || !isfinite(tr)) st = DYRA_SOLVE_NOT_SPD;
-  if (st == DYRA_SOLVE_OK) {
-    const float lam = eps * tr / (float)r;
-#pragma unroll
-    for (int q = 0; q < SW_EPT; ++q) {
-      if (ii[q] >= 0 && ii[q] == jj[q]) a[q] += lam;
-      if (jj[q] == 0) cv[0][ii[q]] = a[q];
-    }
-    __syncthreads();
-    for (int k = 0; k < r; ++k) {
-      const float* buf = cv[k & 1];
-      const float D = buf[k];
-      if (!(D > 0.f) || !isfinite(D)) {
-        st = DYRA_SOLVE_NOT_SPD;
-        break;
-      }
-      const float invD = 1.f / D;
-      float* nxt = cv[(k + 1) & 1];
-#pragma unroll
-      for (int q = 0; q < SW_EPT; ++q) {
-        const int i = ii[q], j = jj[q];
-        if (i < 0) continue;
-        if (i != k && j != k) a[q] = fmaf(-buf[i] * invD, buf[j], a[q]);
-        else if (i == k && j == k) a[q] = -invD;
-        else a[q] = (i == k ? buf[j] : buf[i]) * invD;
-        if (j == k + 1) nxt[i] = a[q];
-      }
-      __syncthreads();
-    }
-  }
-#pragma unroll
-  for (int q = 0; q < SW_EPT; ++q) {
-    const int e = tid + q * SW_NT;
-    if (e < rr) Ob[e] = st == DYRA_SOLVE_OK ? -a[q] : 0.f;
-  }
-  return st;
+// S4a as its own launch: one 256-thread workgroup per segment.  With
+// only_flagged, segments whose status is not DYRA_SOLVE_FALLBACK are left
+// alone: the Newton-Schulz kernel flags the segments it could not solve, and
+// those keep the FALLBACK status when the sweep succeeds.
+template <int TB>
+__global__ __launch_bounds__(256) void sweep_inverse_kernel(const float* G, float* Ginv, int32_t* status, int r,
+                                                            float eps, int only_flagged) {
+  __shared__ SweepLds sl;
+  const int64_t b = blockIdx.x;
+  // every thread reads the flag before the sweep's first barrier; thread 0
+  // rewrites it only after the sweep
+  if (only_flagged && status[b] != DYRA_SOLVE_FALLBACK) return;
+  const int st = sweep_inverse<256, TB>(G + b * r * r, Ginv + b * r * r, r, eps, sl);
+  if (threadIdx.x == 0) status[b] = (only_flagged && st == DYRA_SOLVE_OK) ? DYRA_SOLVE_FALLBACK : st;
 }
 
-__global__ __launch_bounds__(SW_NT) void sweep_inverse_kernel(const float* G, float* Ginv, int32_t* status,
-                                                              int r, float eps) {
-  __shared__ float cv[2][128];
-  __shared__ float red[SW_NT / 64];
-  const int64_t b = blockIdx.x;
-  const int st = sweep_inverse_1024(G + b * r * r, Ginv + b * r * r, r, eps, cv, red);
-  if (threadIdx.x == 0) status[b] = st;
+void launch_sweep(const float* G, float* Ginv, int32_t* status, int r, float eps, int64_t B, bool only_flagged,
+                  hipStream_t st) {
+  const int f = only_flagged ? 1 : 0;
+  if (r <= 64)
+    hipLaunchKernelGGL(sweep_inverse_kernel<4>, dim3((unsigned)B), dim3(256), 0, st, G, Ginv, status, r, eps, f);
+  else
+    hipLaunchKernelGGL(sweep_inverse_kernel<8>, dim3((unsigned)B), dim3(256), 0, st, G, Ginv, status, r, eps, f);
 }
 
 // ===========================================================================
@@ -1021,10 +1066,9 @@ __global__ __launch_bounds__(1024) void ns_inverse_kernel(const float* G, float*
   }
   if (st == DYRA_SOLVE_OK && !(ok && converged)) {
     // Newton-Schulz stalled above tolerance (fp32 with a very ill-conditioned
-    // G) or broke down: solve by the sweep instead, flagged in the status.
-    __syncthreads();
-    const int sst = sweep_inverse_1024(Gb, Ginv + b * r * r, r, eps, reinterpret_cast<float(*)[128]>(Ts), red);
-    if (tid == 0) status[b] = sst == DYRA_SOLVE_OK ? DYRA_SOLVE_FALLBACK : sst;
+    // G) or broke down: flag the segment; the sweep launched after this
+    // kernel solves it.
+    if (tid == 0) status[b] = DYRA_SOLVE_FALLBACK;
     return;
   }
   const bool good = st == DYRA_SOLVE_OK;
@@ -1192,11 +1236,13 @@ void forward_residual(const dyra_spec& s, const char* plan, const void* X, int64
   E.mark(2, st);
   // S4: Ginv_b (unless solved above), M'_b = Ginv_b M_b
   if (!solved) {
-    if (ns)
+    if (ns) {
       hipLaunchKernelGGL(ns_inverse_kernel, dim3((unsigned)B), dim3(1024), 0, st, G, Gi, nullptr, nullptr, stat,
                          r, eps, 60, 2e-6f);
-    else
-      hipLaunchKernelGGL(sweep_inverse_kernel, dim3((unsigned)B), dim3(SW_NT), 0, st, G, Gi, stat, r, eps);
+      launch_sweep(G, Gi, stat, r, eps, B, true, st);
+    } else {
+      launch_sweep(G, Gi, stat, r, eps, B, false, st);
+    }
   }
   hipLaunchKernelGGL(apply_inverse_kernel<T>, dim3((unsigned)(cdiv(c1, 64) * B)), dim3(256),
                      (size_t)(r * r + r * 64) * 4, st, Gi, M, Mp, r, c1);
