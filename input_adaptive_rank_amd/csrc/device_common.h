@@ -45,10 +45,12 @@ template <> struct TT<float> {
   __device__ static __forceinline__ float from_f(float v) { return v; }
 };
 
-// Operand tiles in LDS: one row = 128 bytes = 8 chunks of 16 bytes; the chunk
-// index is XOR-swizzled with the row so that 8 consecutive rows reading the
-// same logical chunk hit 8 different bank groups.
-__device__ __forceinline__ int lds_off(int row, int chunk) { return row * 128 + (((chunk ^ row) & 7) << 4); }
+// Operand tiles in LDS: one row = 128 bytes = 8 chunks of 16 bytes.  The LDS
+// serves a 16-byte-per-lane read 16 lanes at a time from a 256-byte bank
+// window (two rows), so the chunk index is XOR-swizzled with row / 2: 16
+// consecutive rows reading the same logical chunk then cover all 16 slots of
+// the window (row parity picks the half, row / 2 the slot).
+__device__ __forceinline__ int lds_off(int row, int chunk) { return row * 128 + (((chunk ^ (row >> 1)) & 7) << 4); }
 
 // Output staging tiles: rows of CPR chunks (CPR a multiple of 8); the low
 // three bits of the chunk index are XOR-swizzled with the row.

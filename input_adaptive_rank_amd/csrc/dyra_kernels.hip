@@ -110,7 +110,7 @@ __global__ __launch_bounds__(C::NT) void s1_lowrank_kernel(const typename C::ele
 // S6 (low-rank): Y = T V + L R_b + bias, segments handled by row masks
 // ===========================================================================
 
-template <class C>
+template <class C, bool STREAM = true>
 __global__ __launch_bounds__(C::NT) void s6_lowrank_kernel(const typename C::elem* TL,
                                                            const typename C::elem* Vt,
                                                            const typename C::elem* Rt,
@@ -145,7 +145,7 @@ __global__ __launch_bounds__(C::NT) void s6_lowrank_kernel(const typename C::ele
   f32x16 acc[C::FM][C::FN];
   gemm_mainloop<C>(src, total, lds, acc);
   stage_out<C>(lds, acc, bias ? bias + n0 : nullptr, (int)(c2 - n0));
-  copy_out<C>(lds, reinterpret_cast<char*>(Y) + (m0 * c2 + n0) * E, c2 * E,
+  copy_out<C, STREAM>(lds, reinterpret_cast<char*>(Y) + (m0 * c2 + n0) * E, c2 * E,
               (int)imin64(C::BM, n - m0), (c2 - n0) * E);
 }
 
@@ -341,7 +341,7 @@ __global__ __launch_bounds__(C::NT) void s6_blast_kernel(const bf16_t* Wp, int64
   f32x16 acc[C::FM][C::FN];
   gemm_mainloop<C>(src, total, lds, acc);
   stage_out<C>(lds, acc, bias ? bias + n0 : nullptr, (int)(c2 - n0));
-  copy_out<C>(lds, reinterpret_cast<char*>(Y) + (m0 * c2 + n0) * E, c2 * E, (int)imin64(C::BM, n - m0),
+  copy_out<C, true>(lds, reinterpret_cast<char*>(Y) + (m0 * c2 + n0) * E, c2 * E, (int)imin64(C::BM, n - m0),
               (c2 - n0) * E);
 }
 

@@ -218,14 +218,22 @@ __device__ __forceinline__ void stage_out(char* lds, const f32x16 (&acc)[C::FM][
 // Copies the staged tile to global rows: dst = byte address of the tile's
 // (0, 0) element, ldb = bytes between rows; rows >= rows_valid and bytes >=
 // colbytes_valid are not written.
-template <class C>
+// STREAM: the destination is a final output nobody reads back soon; its
+// lines are stored non-temporally so they do not evict the operands that the
+// other workgroups of the XCD are still reading from L2.  Every wave store
+// covers whole 128-byte lines, which the non-temporal path needs to stay
+// efficient.
+template <class C, bool STREAM = false>
 __device__ __forceinline__ void copy_out(const char* lds, char* dst, int64_t ldb, int rows_valid,
                                          int64_t colbytes_valid) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
   for (int c = threadIdx.x; c < C::BM * C::CPR; c += C::NT) {
     const int row = c / C::CPR, ch = c % C::CPR;
     if (row < rows_valid && (int64_t)ch * 16 < colbytes_valid) {
-      *reinterpret_cast<uint4*>(dst + row * ldb + ch * 16) =
-          *reinterpret_cast<const uint4*>(lds + row * (C::CPR * 16) + stage_chunk(row, ch) * 16);
+      const uint4 v = *reinterpret_cast<const uint4*>(lds + row * (C::CPR * 16) + stage_chunk(row, ch) * 16);
+      char* p = dst + row * ldb + ch * 16;
+      if constexpr (STREAM) __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4*>(p));
+      else *reinterpret_cast<uint4*>(p) = v;
     }
   }
 }
