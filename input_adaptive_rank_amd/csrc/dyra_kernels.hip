@@ -844,7 +844,7 @@ __device__ __forceinline__ void s3_gram(const bf16_t* __restrict__ Lt, int64_t l
   const int nsteps = (int)((hi - a0 + 15) / 16);
   const int s0 = w * nsteps / 4, s1 = (w + 1) * nsteps / 4;
   // PF token steps per round: their loads are all issued before the MFMAs
-  constexpr int PF = NB <= 2 ? 4 : 2;
+  constexpr int PF = NB <= 2 ? 8 : 2;
   for (int st0 = s0; st0 < s1; st0 += PF) {
     uint4 f[PF][NB];
 #pragma unroll
@@ -1150,6 +1150,7 @@ __global__ __launch_bounds__(256) void apply_inverse_kernel(const float* __restr
 // ===========================================================================
 
 typedef GemmCfg<bf16_t, 128, 128, 2, 2> CfgB;   // bf16 GEMMs
+typedef GemmCfg<bf16_t, 160, 320, 5, 2> CfgB1W; // bf16 S1 when 256 < k + r <= 320: whole [T | L] row per tile
 typedef GemmCfg<bf16_t, 256, 256, 2, 4> CfgB6;  // bf16 fused output GEMM (short K, wide output)
 typedef GemmCfg<float, 64, 64, 2, 2> CfgF;      // fp32 GEMMs
 typedef GemmCfg<bf16_t, 64, 128, 2, 2> CfgB3;   // S3, bf16
@@ -1266,11 +1267,23 @@ int forward_lowrank(const dyra_spec& s, const char* plan, const void* X, const v
   T* Rt = reinterpret_cast<T*>(ws + WL.Rt);
   E.mark(0, st);
   {  // S1: [T | L] = X [U | P], L^T
-    const int tiles_n = (int)cdiv(k + r, C::BN);
-    const int64_t tiles = cdiv(n, C::BM) * tiles_n;
-    hipLaunchKernelGGL(s1_lowrank_kernel<C>, dim3((unsigned)tiles), dim3(C::NT), 0, st,
-                       reinterpret_cast<const T*>(X), reinterpret_cast<const T*>(plan + PL.UPt), TL, Lt, n, c1, k,
-                       r, lt_pitch(n), tiles_n, (int64_t)(k + r));
+    auto launch = [&](auto cfg) {
+      typedef decltype(cfg) C1;
+      const int tiles_n = (int)cdiv(k + r, C1::BN);
+      const int64_t tiles = cdiv(n, C1::BM) * tiles_n;
+      hipLaunchKernelGGL(s1_lowrank_kernel<C1>, dim3((unsigned)tiles), dim3(C1::NT), 0, st,
+                         reinterpret_cast<const T*>(X), reinterpret_cast<const T*>(plan + PL.UPt), TL, Lt, n, c1, k,
+                         r, lt_pitch(n), tiles_n, (int64_t)(k + r));
+    };
+    // 128 x 128 tiles leave k + r in (256, 320] as 2.5 column tiles and, at
+    // ViT-L sizes, more tiles than two per CU: one 160 x 320 tile per row
+    // block instead (a single round, X read once per row block)
+    if constexpr (TT<T>::ESZ == 2) {
+      if (k + r > 256 && k + r <= 320) launch(CfgB1W());
+      else launch(C());
+    } else {
+      launch(C());
+    }
   }
   E.mark(1, st);
   forward_residual<C, C3>(s, plan, X, B, seg, eps, solver, ws, st, E);

@@ -32,6 +32,8 @@ SMALL = [
     sc(W["vitb_fc1"], name="many_short_segments", B=37, s=13, c1=128, c2=136, k=16, r=8),
     sc(W["vitb_fc1"], name="wide_k", B=2, s=300, c1=512, c2=256, k=200, r=56),
     sc(W["vitl_fc1"], name="r128_ns", B=2, s=300, c1=256, c2=384, k=64, r=128, solver="ns"),
+    # k + r = 320: the 160 x 320 first-stage tile, ragged in rows
+    sc(W["vitl_fc1"], name="wide_first_stage_tile", B=3, s=150, c1=384, c2=384, k=256, r=64),
 ]
 
 
