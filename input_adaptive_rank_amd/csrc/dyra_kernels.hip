@@ -110,8 +110,11 @@ __global__ __launch_bounds__(C::NT) void s1_lowrank_kernel(const typename C::ele
 // S6 (low-rank): Y = T V + L R_b + bias, segments handled by row masks
 // ===========================================================================
 
-template <class C, bool STREAM = true>
-__global__ __launch_bounds__(C::NT) void s6_lowrank_kernel(const typename C::elem* TL,
+// ONE_STAGE: single operand stage.  WPE: minimum waves per SIMD the
+// registers must allow (the second launch bound), i.e. how many workgroups
+// share a CU; their epilogues then overlap each other's k-loops.
+template <class C, bool ONE_STAGE = false, bool STREAM = true, int WPE = 1>
+__global__ __launch_bounds__(C::NT, WPE) void s6_lowrank_kernel(const typename C::elem* TL,
                                                            const typename C::elem* Vt,
                                                            const typename C::elem* Rt,
                                                            const typename C::elem* bias,
@@ -120,7 +123,7 @@ __global__ __launch_bounds__(C::NT) void s6_lowrank_kernel(const typename C::ele
                                                            int tiles_n) {
   typedef typename C::elem T;
   constexpr int E = TT<T>::ESZ;
-  __shared__ __attribute__((aligned(16))) char lds[C::LDS];
+  __shared__ __attribute__((aligned(16))) char lds[ONE_STAGE ? C::LDS1 : C::LDS];
   const int t = xcd_tile_id(blockIdx.x, gridDim.x);
   const int64_t m0 = (int64_t)(t / tiles_n) * C::BM, n0 = (int64_t)(t % tiles_n) * C::BN;
   const int64_t lda = (int64_t)(k + r) * E;
@@ -143,7 +146,8 @@ __global__ __launch_bounds__(C::NT) void s6_lowrank_kernel(const typename C::ele
     ph.b = OpK{reinterpret_cast<const char*>(Rt + b * r), B * r * E, n0, 0, c2, (int64_t)r * E};
   };
   f32x16 acc[C::FM][C::FN];
-  gemm_mainloop<C>(src, total, lds, acc);
+  if constexpr (ONE_STAGE) gemm_mainloop1<C>(src, total, lds, acc);
+  else gemm_mainloop<C>(src, total, lds, acc);
   stage_out<C>(lds, acc, bias ? bias + n0 : nullptr, (int)(c2 - n0));
   copy_out<C, STREAM>(lds, reinterpret_cast<char*>(Y) + (m0 * c2 + n0) * E, c2 * E,
               (int)imin64(C::BM, n - m0), (c2 - n0) * E);
@@ -1151,7 +1155,10 @@ __global__ __launch_bounds__(256) void apply_inverse_kernel(const float* __restr
 
 typedef GemmCfg<bf16_t, 128, 128, 2, 2> CfgB;   // bf16 GEMMs
 typedef GemmCfg<bf16_t, 160, 320, 5, 2> CfgB1W; // bf16 S1 when 256 < k + r <= 320: whole [T | L] row per tile
-typedef GemmCfg<bf16_t, 256, 256, 2, 4> CfgB6;  // bf16 fused output GEMM (short K, wide output)
+// bf16 fused output GEMM: short reduction (k + r), 270 MB written; single
+// operand stage, three workgroups per CU
+typedef GemmCfg<bf16_t, 128, 128, 2, 2> CfgB6;
+constexpr int S6_WPE = 3;
 typedef GemmCfg<float, 64, 64, 2, 2> CfgF;      // fp32 GEMMs
 typedef GemmCfg<bf16_t, 64, 128, 2, 2> CfgB3;   // S3, bf16
 typedef GemmCfg<float, 64, 64, 2, 2> CfgF3;     // S3, fp32
@@ -1291,7 +1298,8 @@ int forward_lowrank(const dyra_spec& s, const char* plan, const void* X, const v
   {  // S6: Y = T V + L R_b + bias
     const int tiles_n = (int)cdiv(c2, C6::BN);
     const int64_t tiles = cdiv(n, C6::BM) * tiles_n;
-    hipLaunchKernelGGL(s6_lowrank_kernel<C6>, dim3((unsigned)tiles), dim3(C6::NT), 0, st, TL,
+    constexpr bool BF = TT<T>::ESZ == 2;
+    hipLaunchKernelGGL((s6_lowrank_kernel<C6, BF, true, BF ? S6_WPE : 1>), dim3((unsigned)tiles), dim3(C6::NT), 0, st, TL,
                        reinterpret_cast<const T*>(plan + PL.Vt), Rt, reinterpret_cast<const T*>(bias),
                        reinterpret_cast<T*>(Y), n, c2, k, r, seg, B, tiles_n);
   }

@@ -39,6 +39,8 @@ struct GemmCfg {
   static constexpr int CPR = BN * TT<T>::ESZ / 16;
   static constexpr int LDS_OUT = BM * CPR * 16;
   static constexpr int LDS = LDS_OPS > LDS_OUT ? LDS_OPS : LDS_OUT;
+  // single-stage pipeline (gemm_mainloop1): one operand stage
+  static constexpr int LDS1 = STAGE > LDS_OUT ? STAGE : LDS_OUT;
   static_assert(ACH * NT == BM * 8, "A tile chunks must divide over the threads");
   static_assert(BCH * NT == BN * 8, "B tile chunks must divide over the threads");
   static_assert(FM * 32 == WM && FN * 32 == WN, "wave tile must be a multiple of 32x32");
@@ -164,6 +166,44 @@ __device__ __forceinline__ void gemm_mainloop(const Src& src, int total, char* l
       store_tile<C>(lds + ((t + 1) & 1) * C::STAGE, r, tid);
       __syncthreads();
     }
+  }
+}
+
+// Single-stage variant: registers prefetch k-tile t + 1 while t is computed
+// from the one LDS stage (two barriers per k-tile).  Half the operand LDS of
+// gemm_mainloop, so twice as many workgroups fit on a CU; with short
+// reductions (a few k-tiles per output tile) the extra resident workgroups,
+// whose epilogues overlap each other's k-loops, outweigh the second barrier.
+template <class C, class Src>
+__device__ __forceinline__ void gemm_mainloop1(const Src& src, int total, char* lds,
+                                               f32x16 (&acc)[C::FM][C::FN]) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wm = w / C::NWN, wn = w % C::NWN;
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[fm][fn][v] = 0.f;
+  if (total <= 0) return;
+  TileRegs<C> r;
+  {
+    Phase ph;
+    int kt;
+    src(0, ph, kt);
+    load_tile<C>(ph, kt, r, tid);
+  }
+  for (int t = 0; t < total; ++t) {
+    store_tile<C>(lds, r, tid);
+    __syncthreads();
+    if (t + 1 < total) {
+      Phase ph;
+      int kt;
+      src(t + 1, ph, kt);
+      load_tile<C>(ph, kt, r, tid);
+    }
+    compute_tile<C>(lds, acc, lane, wm, wn);
+    __syncthreads();
   }
 }
 
