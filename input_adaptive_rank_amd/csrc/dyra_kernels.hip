@@ -34,14 +34,16 @@ __host__ __device__ __forceinline__ int64_t imax64(int64_t a, int64_t b) { retur
 // generic single-phase GEMM: C[M x N] = A[M x K] B[N x K]^T (+ bias[N])
 // ===========================================================================
 
-template <class C>
-__global__ __launch_bounds__(C::NT) void gemm_tn_kernel(const char* A, int64_t lda, const char* B,
+// ONE_STAGE / WPE: as for the fused output GEMM (single operand stage, at
+// least WPE waves per SIMD worth of registers).
+template <class C, bool ONE_STAGE = false, int WPE = 1>
+__global__ __launch_bounds__(C::NT, WPE) void gemm_tn_kernel(const char* A, int64_t lda, const char* B,
                                                         int64_t ldb, char* Cg, int64_t ldc, int64_t M,
                                                         int64_t N, int64_t K,
                                                         const typename C::elem* bias, int tiles_n,
                                                         int64_t sA, int64_t sB, int64_t sC, int tiles_per_batch) {
   typedef typename C::elem T;
-  __shared__ __attribute__((aligned(16))) char lds[C::LDS];
+  __shared__ __attribute__((aligned(16))) char lds[ONE_STAGE ? C::LDS1 : C::LDS];
   // batch z: A += z sA, B += z sB, C += z sC (byte strides)
   const int z = blockIdx.x / tiles_per_batch;
   const int t = xcd_tile_id(blockIdx.x % tiles_per_batch, tiles_per_batch);
@@ -56,7 +58,8 @@ __global__ __launch_bounds__(C::NT) void gemm_tn_kernel(const char* A, int64_t l
     kt = tt;
   };
   f32x16 acc[C::FM][C::FN];
-  gemm_mainloop<C>(src, ktiles(kb), lds, acc);
+  if constexpr (ONE_STAGE) gemm_mainloop1<C>(src, ktiles(kb), lds, acc);
+  else gemm_mainloop<C>(src, ktiles(kb), lds, acc);
   stage_out<C>(lds, acc, bias ? bias + n0 : nullptr, (int)(N - n0));
   copy_out<C>(lds, Cg + m0 * ldc + n0 * TT<T>::ESZ, ldc, (int)imin64(C::BM, M - m0),
               (N - n0) * TT<T>::ESZ);
@@ -1176,7 +1179,9 @@ void launch_gemm_tn(const void* A, int64_t lda_el, const void* B, int64_t ldb_el
   const int tiles_n = (int)cdiv(N, C::BN);
   const int64_t tiles = cdiv(M, C::BM) * tiles_n;
   if (tiles <= 0 || batch <= 0) return;
-  hipLaunchKernelGGL(gemm_tn_kernel<C>, dim3((unsigned)(tiles * batch)), dim3(C::NT), 0, st,
+  // bf16 128 x 128 tiles: single operand stage, three workgroups per CU
+  constexpr bool ONE = E == 2 && C::BM == 128 && C::BN == 128;
+  hipLaunchKernelGGL((gemm_tn_kernel<C, ONE, ONE ? 3 : 1>), dim3((unsigned)(tiles * batch)), dim3(C::NT), 0, st,
                      reinterpret_cast<const char*>(A), lda_el * E, reinterpret_cast<const char*>(B), ldb_el * E,
                      reinterpret_cast<char*>(Cm), ldc_el * E, M, N, K, reinterpret_cast<const T*>(bias), tiles_n,
                      sA * E, sB * E, sC * E, (int)tiles);
