@@ -35,24 +35,49 @@ WORKLOAD_TEXT = {
     "vitb_fc1": "ViT-B/16 MLP fc1",
     "vitl_fc1": "ViT-L/16 MLP fc1",
     "vitl_fc2": "ViT-L/16 MLP fc2",
+    "monarch": "Monarch 32 x (32 x 32) layer at the ViT-L token count",
+    "lm_blast": "LM prefill QKV-shaped layer, BLAST 16 x 16 grid, rank 128",
 }
 STAGES = ["stage1_X_UP", "token_reductions_M_G", "solve_apply", "right_factor_R", "fused_output_Y"]
 
 
 def stage_work(w):
-    """Algorithmic flops and HBM bytes of each stage for one launch (one
-    batch of B segments); bf16 = 2 bytes, fp32 = 4 bytes.  Low-rank."""
+    """Algorithmic flops and HBM bytes of each event-timed stage for one
+    launch (one batch of B segments); bf16 = 2 bytes, fp32 = 4 bytes."""
+    from input_adaptive_rank_amd import synth
     e = 2 if w.dtype == 1 else 4
-    n, c1, c2, k, r, B = w.n, w.c1, w.c2, w.k, w.r, w.B
-    N = k + r
-    return {
-        "stage1_X_UP": (2 * n * c1 * N, e * (n * c1 + N * c1 + n * N + r * n)),
-        "token_reductions_M_G": (2 * n * r * c1 + 2 * n * r * r,
-                                 e * (n * c1 + r * n) + 4 * (B * r * c1 + B * r * r)),
-        "solve_apply": (B * (2 * r ** 3 + 2 * r * r * c1), 4 * (2 * B * r * r + B * r * c1) + e * B * r * c1),
-        "right_factor_R": (2 * c2 * B * r * c1, e * (c2 * c1 + B * r * c1 + c2 * B * r)),
-        "fused_output_Y": (2 * n * N * c2, e * (n * N + c2 * k + c2 * B * r + c2 + n * c2)),
-    }
+    n, c1, c2, r, B = w.n, w.c1, w.c2, w.r, w.B
+    # shared by every structure: M_b, G_b; the r x r solve and M' = Ginv M;
+    # R^T = W_res^T M'^T for all segments at once
+    s3 = (2 * n * r * c1 + 2 * n * r * r, e * (n * c1 + r * n) + 4 * (B * r * c1 + B * r * r))
+    s4 = (B * (2 * r ** 3 + 2 * r * r * c1), 4 * (2 * B * r * r + B * r * c1) + e * B * r * c1)
+    s5 = (2 * c2 * B * r * c1, e * (c2 * c1 + B * r * c1 + c2 * B * r))
+    if w.kind == synth.KIND_MONARCH:
+        m = w.mblk   # c = m^2: stage 1 and stage 2 are m block products of m x m
+        s1 = (2 * n * c1 * m + 2 * n * c1 * r, e * (n * c1 + c1 * m + c1 * r + n * (c1 + r) + r * n))
+        s6 = (2 * n * c2 * m + 2 * n * r * c2, e * (n * (c1 + r) + c2 * m + c2 * B * r + c2 + n * c2))
+    elif w.kind == synth.KIND_BLAST:
+        nr = w.nb * w.rb  # Z = X blockdiag(U_i): n x (nb rb); coupling W' = Z S (full S)
+        s1 = (2 * n * c1 * w.rb + 2 * n * c1 * r, e * (n * c1 + c1 * w.rb + c1 * r + n * (nr + r) + r * n))
+        cpl = (2 * n * nr * nr, e * (2 * n * nr + nr * nr))
+        s5 = (s5[0] + cpl[0], s5[1] + cpl[1])   # the coupling GEMM runs in the same event interval
+        s6 = (2 * n * w.rb * c2 + 2 * n * r * c2, e * (n * nr + n * r + c2 * w.rb + c2 * B * r + c2 + n * c2))
+    else:
+        N = w.k + r
+        s1 = (2 * n * c1 * N, e * (n * c1 + N * c1 + n * N + r * n))
+        s6 = (2 * n * N * c2, e * (n * N + c2 * w.k + c2 * B * r + c2 + n * c2))
+    return {"stage1_X_UP": s1, "token_reductions_M_G": s3, "solve_apply": s4, "right_factor_R": s5,
+            "fused_output_Y": s6}
+
+
+def STRUCT_TEXT(w):
+    return {0: f"low-rank k={w.k}", 1: f"Monarch {w.mblk} x ({w.mblk} x {w.mblk})",
+            2: f"BLAST {w.nb} x {w.nb} grid, rb={w.rb}"}[w.kind]
+
+
+OUTPUT_KERNEL = {0: "s6_lowrank_kernel (fused T V + L R_b + bias)",
+                 1: "s6_monarch_kernel (stage 2 + L R_b + bias)",
+                 2: "s6_blast_kernel (W'_j V_j^T + L R_b + bias)"}
 
 
 def kernel_source_hash():
@@ -91,7 +116,7 @@ def cpu_baseline(w, budget_s=12.0):
     except Exception:   # noqa: BLE001
         threads = os.cpu_count()
     inp = synth.make_inputs(w)
-    prep = O.prepare(inp.W, w.kind, w.r, k=w.k)
+    prep = O.prepare(inp.W, w.kind, w.r, k=w.k, mblk=w.mblk, nb=w.nb, rb=w.rb)
     t0 = time.perf_counter()
     runs = 0
     while True:
@@ -111,6 +136,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="vitl_fc1")
+    ap.add_argument("--solver", choices=["auto", "chol", "ns"], default=None,
+                    help="r x r solver (default: the workload's own choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -127,13 +154,13 @@ def main():
     from input_adaptive_rank_amd import synth
 
     w = synth.WORKLOADS[args.workload]
-    assert w.kind == synth.KIND_LOWRANK, "bench workload must be a low-rank layer"
     dev = torch.device("cuda:0")
     inp = synth.make_inputs(w)
     t0 = time.perf_counter()
     factors = D.prepare(inp.W, D.spec_of(w))
     prep_s = time.perf_counter() - t0
-    layer = D.DyraLayer(D.spec_of(w), factors, w.dtype, bias=inp.bias, device=dev)
+    solver = args.solver or w.solver
+    layer = D.DyraLayer(D.spec_of(w), factors, w.dtype, bias=inp.bias, device=dev, solver=D.SOLVERS[solver])
     tdt = D.torch_dtype(w.dtype)
     # 4 input/output buffer sets so X is not cache-resident from the previous step
     NB = 4
@@ -193,7 +220,7 @@ def main():
         roof = {"bound": "mfma", "achieved": round(fl / t6 / 1e12, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = traffic
-    roof["kernel"] = "s6_lowrank_kernel (fused T V + L R_b + bias)"
+    roof["kernel"] = OUTPUT_KERNEL[w.kind]
     roof["mfma_frac"] = round(fl / t6 / 1e12 / PEAK_BF16_TFLOPS, 4)
 
     # dense comparators on the same shape: library MFMA GEMM and torch.matmul (hipBLASLt)
@@ -248,9 +275,9 @@ def main():
         "dtype": "bf16" if w.dtype == synth.DT_BF16 else "f32",
         "data": "synthetic",
         "config": {"workload": f"{w.name}: {WORKLOAD_TEXT.get(w.name, 'DyRA layer')}, B={w.B} x {w.s} tokens, "
-                               f"{w.c1}->{w.c2}, low-rank k={w.k}, r={w.r}, "
+                               f"{w.c1}->{w.c2}, {STRUCT_TEXT(w)}, r={w.r}, "
                                f"{'bf16' if w.dtype == synth.DT_BF16 else 'fp32'}, fp32 accumulate",
-                   "global_batch": w.B, "seq_len": w.s, "tokens": w.n},
+                   "global_batch": w.B, "seq_len": w.s, "tokens": w.n, "solver": solver},
         "tflops": round(total_flops / (ms * 1e-3) / 1e12, 1),
         "pct_bf16_peak": round(100 * total_flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
         "roofline": roof,

@@ -68,7 +68,7 @@ extern "C" {
 #define DYRA_BF16 1
 
 /* r x r solver choice for dyra_forward */
-#define DYRA_SOLVER_AUTO 0   /* Cholesky for r < 128, Newton-Schulz for r >= 128 */
+#define DYRA_SOLVER_AUTO 0   /* the sweep (the faster solver on MI355X at every r <= 128) */
 #define DYRA_SOLVER_CHOL 1
 #define DYRA_SOLVER_NS   2
 

@@ -930,25 +930,28 @@ __global__ __launch_bounds__(S3_NT, NRB <= 4 ? 2 : 1) void s3_reduce_solve_kerne
 // only_flagged, segments whose status is not DYRA_SOLVE_FALLBACK are left
 // alone: the Newton-Schulz kernel flags the segments it could not solve, and
 // those keep the FALLBACK status when the sweep succeeds.
-template <int TB>
-__global__ __launch_bounds__(256) void sweep_inverse_kernel(const float* G, float* Ginv, int32_t* status, int r,
-                                                            float eps, int only_flagged) {
+template <int NT, int TB>
+__global__ __launch_bounds__(NT) void sweep_inverse_kernel(const float* G, float* Ginv, int32_t* status, int r,
+                                                           float eps, int only_flagged) {
   __shared__ SweepLds sl;
   const int64_t b = blockIdx.x;
   // every thread reads the flag before the sweep's first barrier; thread 0
   // rewrites it only after the sweep
   if (only_flagged && status[b] != DYRA_SOLVE_FALLBACK) return;
-  const int st = sweep_inverse<256, TB>(G + b * r * r, Ginv + b * r * r, r, eps, sl);
+  const int st = sweep_inverse<NT, TB>(G + b * r * r, Ginv + b * r * r, r, eps, sl);
   if (threadIdx.x == 0) status[b] = (only_flagged && st == DYRA_SOLVE_OK) ? DYRA_SOLVE_FALLBACK : st;
 }
 
+// r <= 64: 256 threads of 4 x 4 tiles; r <= 128: 1024 threads of 4 x 4 tiles
+// (four waves per SIMD hide part of the pivot blocks' dependent latency).
 void launch_sweep(const float* G, float* Ginv, int32_t* status, int r, float eps, int64_t B, bool only_flagged,
                   hipStream_t st) {
   const int f = only_flagged ? 1 : 0;
   if (r <= 64)
-    hipLaunchKernelGGL(sweep_inverse_kernel<4>, dim3((unsigned)B), dim3(256), 0, st, G, Ginv, status, r, eps, f);
+    hipLaunchKernelGGL((sweep_inverse_kernel<256, 4>), dim3((unsigned)B), dim3(256), 0, st, G, Ginv, status, r, eps, f);
   else
-    hipLaunchKernelGGL(sweep_inverse_kernel<8>, dim3((unsigned)B), dim3(256), 0, st, G, Ginv, status, r, eps, f);
+    hipLaunchKernelGGL((sweep_inverse_kernel<1024, 4>), dim3((unsigned)B), dim3(1024), 0, st, G, Ginv, status, r, eps,
+                       f);
 }
 
 // ===========================================================================
@@ -1230,7 +1233,11 @@ void forward_residual(const dyra_spec& s, const char* plan, const void* X, int64
   T* Rt = reinterpret_cast<T*>(ws + WL.Rt);
   int32_t* stat = reinterpret_cast<int32_t*>(ws + WL.status);
   const int64_t ldt = lt_pitch(n);
-  const bool ns = solver == DYRA_SOLVER_NS || (solver == DYRA_SOLVER_AUTO && r >= 128);
+  // AUTO takes the sweep at every supported r: on MI355X the fp64 sweep on one
+  // workgroup beats fp32 Newton-Schulz, which the per-CU fp32 MFMA rate
+  // bounds, at r = 64 and r = 128 alike (23 vs 222 us for 32 solves at r = 64,
+  // 99 vs 257 us for one at r = 128); Newton-Schulz stays selectable.
+  const bool ns = solver == DYRA_SOLVER_NS;
   // S3: M_b, G_b (bf16: with the sweep solve in the same launch)
   bool solved = false;
   if constexpr (BF) {
