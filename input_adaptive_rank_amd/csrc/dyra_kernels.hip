@@ -36,7 +36,7 @@ __host__ __device__ __forceinline__ int64_t imax64(int64_t a, int64_t b) { retur
 
 // ONE_STAGE / WPE: as for the fused output GEMM (single operand stage, at
 // least WPE waves per SIMD worth of registers).
-template <class C, bool ONE_STAGE = false, int WPE = 1>
+template <class C, bool ONE_STAGE = false, int WPE = 1, bool DMA = false>
 __global__ __launch_bounds__(C::NT, WPE) void gemm_tn_kernel(const char* A, int64_t lda, const char* B,
                                                         int64_t ldb, char* Cg, int64_t ldc, int64_t M,
                                                         int64_t N, int64_t K,
@@ -58,7 +58,8 @@ __global__ __launch_bounds__(C::NT, WPE) void gemm_tn_kernel(const char* A, int6
     kt = tt;
   };
   f32x16 acc[C::FM][C::FN];
-  if constexpr (ONE_STAGE) gemm_mainloop1<C>(src, ktiles(kb), lds, acc);
+  if constexpr (DMA) gemm_mainloop1_dma<C>(src, ktiles(kb), lds, acc);
+  else if constexpr (ONE_STAGE) gemm_mainloop1<C>(src, ktiles(kb), lds, acc);
   else gemm_mainloop<C>(src, ktiles(kb), lds, acc);
   stage_out<C>(lds, acc, bias ? bias + n0 : nullptr, (int)(N - n0));
   copy_out<C>(lds, Cg + m0 * ldc + n0 * TT<T>::ESZ, ldc, (int)imin64(C::BM, M - m0),
@@ -116,7 +117,7 @@ __global__ __launch_bounds__(C::NT) void s1_lowrank_kernel(const typename C::ele
 // ONE_STAGE: single operand stage.  WPE: minimum waves per SIMD the
 // registers must allow (the second launch bound), i.e. how many workgroups
 // share a CU; their epilogues then overlap each other's k-loops.
-template <class C, bool ONE_STAGE = false, bool STREAM = true, int WPE = 1>
+template <class C, bool ONE_STAGE = false, bool STREAM = true, int WPE = 1, bool DMA = false>
 __global__ __launch_bounds__(C::NT, WPE) void s6_lowrank_kernel(const typename C::elem* TL,
                                                            const typename C::elem* Vt,
                                                            const typename C::elem* Rt,
@@ -149,7 +150,8 @@ __global__ __launch_bounds__(C::NT, WPE) void s6_lowrank_kernel(const typename C
     ph.b = OpK{reinterpret_cast<const char*>(Rt + b * r), B * r * E, n0, 0, c2, (int64_t)r * E};
   };
   f32x16 acc[C::FM][C::FN];
-  if constexpr (ONE_STAGE) gemm_mainloop1<C>(src, total, lds, acc);
+  if constexpr (DMA) gemm_mainloop1_dma<C>(src, total, lds, acc);
+  else if constexpr (ONE_STAGE) gemm_mainloop1<C>(src, total, lds, acc);
   else gemm_mainloop<C>(src, total, lds, acc);
   stage_out<C>(lds, acc, bias ? bias + n0 : nullptr, (int)(c2 - n0));
   copy_out<C, STREAM>(lds, reinterpret_cast<char*>(Y) + (m0 * c2 + n0) * E, c2 * E,
@@ -1162,9 +1164,9 @@ __global__ __launch_bounds__(256) void apply_inverse_kernel(const float* __restr
 typedef GemmCfg<bf16_t, 128, 128, 2, 2> CfgB;   // bf16 GEMMs
 typedef GemmCfg<bf16_t, 160, 320, 5, 2> CfgB1W; // bf16 S1 when 256 < k + r <= 320: whole [T | L] row per tile
 // bf16 fused output GEMM: short reduction (k + r), 270 MB written; single
-// operand stage, three workgroups per CU
+// operand stage loaded straight into LDS, four workgroups per CU
 typedef GemmCfg<bf16_t, 128, 128, 2, 2> CfgB6;
-constexpr int S6_WPE = 3;
+constexpr int S6_WPE = 4;
 typedef GemmCfg<float, 64, 64, 2, 2> CfgF;      // fp32 GEMMs
 typedef GemmCfg<bf16_t, 64, 128, 2, 2> CfgB3;   // S3, bf16
 typedef GemmCfg<float, 64, 64, 2, 2> CfgF3;     // S3, fp32
@@ -1182,9 +1184,10 @@ void launch_gemm_tn(const void* A, int64_t lda_el, const void* B, int64_t ldb_el
   const int tiles_n = (int)cdiv(N, C::BN);
   const int64_t tiles = cdiv(M, C::BM) * tiles_n;
   if (tiles <= 0 || batch <= 0) return;
-  // bf16 128 x 128 tiles: single operand stage, three workgroups per CU
+  // bf16 128 x 128 tiles: single operand stage loaded straight into LDS,
+  // four workgroups per CU
   constexpr bool ONE = E == 2 && C::BM == 128 && C::BN == 128;
-  hipLaunchKernelGGL((gemm_tn_kernel<C, ONE, ONE ? 3 : 1>), dim3((unsigned)(tiles * batch)), dim3(C::NT), 0, st,
+  hipLaunchKernelGGL((gemm_tn_kernel<C, ONE, ONE ? 4 : 1, ONE>), dim3((unsigned)(tiles * batch)), dim3(C::NT), 0, st,
                      reinterpret_cast<const char*>(A), lda_el * E, reinterpret_cast<const char*>(B), ldb_el * E,
                      reinterpret_cast<char*>(Cm), ldc_el * E, M, N, K, reinterpret_cast<const T*>(bias), tiles_n,
                      sA * E, sB * E, sC * E, (int)tiles);
@@ -1311,7 +1314,7 @@ int forward_lowrank(const dyra_spec& s, const char* plan, const void* X, const v
     const int tiles_n = (int)cdiv(c2, C6::BN);
     const int64_t tiles = cdiv(n, C6::BM) * tiles_n;
     constexpr bool BF = TT<T>::ESZ == 2;
-    hipLaunchKernelGGL((s6_lowrank_kernel<C6, BF, true, BF ? S6_WPE : 1>), dim3((unsigned)tiles), dim3(C6::NT), 0, st, TL,
+    hipLaunchKernelGGL((s6_lowrank_kernel<C6, BF, true, BF ? S6_WPE : 1, BF>), dim3((unsigned)tiles), dim3(C6::NT), 0, st, TL,
                        reinterpret_cast<const T*>(plan + PL.Vt), Rt, reinterpret_cast<const T*>(bias),
                        reinterpret_cast<T*>(Y), n, c2, k, r, seg, B, tiles_n);
   }

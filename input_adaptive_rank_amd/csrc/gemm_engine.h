@@ -207,6 +207,59 @@ __device__ __forceinline__ void gemm_mainloop1(const Src& src, int total, char* 
   }
 }
 
+// One k-tile of both operands straight from memory into an LDS stage
+// (buffer loads with the LDS as destination; no registers), in the
+// store_tile layout: wave w fills 8-row blocks w, w + NW, ..., lane L of a
+// block the 16-byte slot L % 8 of row L / 8, which lds_off assigns to chunk
+// (L % 8) ^ ((row / 2) % 8).  Chunks outside the operand read as zero.
+template <class C>
+__device__ __forceinline__ void dma_tile(const Phase& ph, int kt, char* stage, int lane, int w) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  constexpr int NW = C::NT / 64;
+  const int kb = kt * 128;
+  auto one = [&](const OpK& o, char* base, int nblk) {
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(o);
+#pragma unroll
+    for (int j = 0; j < nblk; ++j) {
+      const int blk = w + j * NW;
+      const int row = blk * 8 + (lane >> 3);
+      const int chunk = (lane & 7) ^ ((row >> 1) & 7);
+      const int64_t grow = o.row0 + row;
+      const int kk = kb + chunk * 16;
+      const bool ok = grow >= o.row_lo && grow < o.row_hi && kk < o.kbytes;
+      const int off = ok ? (int)(row * o.ld) + kk : (int)0x80000000u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(base + blk * 1024), 16, off, 0, 0, 0);
+    }
+  };
+  one(ph.a, stage, C::ACH);
+  one(ph.b, stage + C::BM * 128, C::BCH);
+}
+
+// Single stage fed by dma_tile: no operand registers at all (so more
+// workgroups fit on a CU); the load latency of a k-tile is hidden by the
+// other resident workgroups rather than inside this one.
+template <class C, class Src>
+__device__ __forceinline__ void gemm_mainloop1_dma(const Src& src, int total, char* lds,
+                                                   f32x16 (&acc)[C::FM][C::FN]) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wm = w / C::NWN, wn = w % C::NWN;
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[fm][fn][v] = 0.f;
+  for (int t = 0; t < total; ++t) {
+    Phase ph;
+    int kt;
+    src(t, ph, kt);
+    dma_tile<C>(ph, kt, lds, lane, w);
+    __syncthreads();   // waits for this wave's loads; then every wave's have landed
+    compute_tile<C>(lds, acc, lane, wm, wn);
+    __syncthreads();   // every wave is done reading before the next k-tile lands
+  }
+}
+
 __device__ __forceinline__ int ktiles(int64_t kbytes) { return (int)((kbytes + 127) >> 7); }
 
 // Writes acc (+ bias[col] when bias != nullptr; bias points at the tile's
