@@ -71,15 +71,15 @@ __global__ __launch_bounds__(C::NT, WPE) void gemm_tn_kernel(const char* A, int6
 // ===========================================================================
 
 // TL: output rows of pitch ldo elements (columns [0, k) = T, [k, k + r) = L).
-template <class C>
-__global__ __launch_bounds__(C::NT) void s1_lowrank_kernel(const typename C::elem* X,
+template <class C, bool ONE_STAGE = false, int WPE = 1, bool DMA = false>
+__global__ __launch_bounds__(C::NT, WPE) void s1_lowrank_kernel(const typename C::elem* X,
                                                            const typename C::elem* UPt,
                                                            typename C::elem* TL, typename C::elem* Lt,
                                                            int64_t n, int64_t c1, int k, int r,
                                                            int64_t ldt, int tiles_n, int64_t ldo) {
   typedef typename C::elem T;
   constexpr int E = TT<T>::ESZ, KPC = TT<T>::KPC;
-  __shared__ __attribute__((aligned(16))) char lds[C::LDS];
+  __shared__ __attribute__((aligned(16))) char lds[ONE_STAGE ? C::LDS1 : C::LDS];
   const int t = xcd_tile_id(blockIdx.x, gridDim.x);
   const int64_t m0 = (int64_t)(t / tiles_n) * C::BM, n0 = (int64_t)(t % tiles_n) * C::BN;
   const int64_t N = k + r;
@@ -89,7 +89,9 @@ __global__ __launch_bounds__(C::NT) void s1_lowrank_kernel(const typename C::ele
     kt = t;
   };
   f32x16 acc[C::FM][C::FN];
-  gemm_mainloop<C>(src, ktiles(c1 * E), lds, acc);
+  if constexpr (DMA) gemm_mainloop1_dma<C>(src, ktiles(c1 * E), lds, acc);
+  else if constexpr (ONE_STAGE) gemm_mainloop1<C>(src, ktiles(c1 * E), lds, acc);
+  else gemm_mainloop<C>(src, ktiles(c1 * E), lds, acc);
   stage_out<C>(lds, acc, nullptr, 0);
   copy_out<C>(lds, reinterpret_cast<char*>(TL) + (m0 * ldo + n0) * E, ldo * E,
               (int)imin64(C::BM, n - m0), (N - n0) * E);
@@ -1110,17 +1112,22 @@ __global__ __launch_bounds__(256) void apply_inverse_kernel(const float* __restr
                                                             int r, int64_t c1) {
   // tile: all r rows x 64 columns; thread = 4 rows x 4 columns per pass
   extern __shared__ __attribute__((aligned(16))) float sh[];
-  float* Gs = sh;               // [q][p] = Ginv[p][q]
-  float* Ms = sh + r * r;       // [q][c]
+  const int P = r + 4;          // padded pitch: the transposing stores spread over the banks
+  float* Gs = sh;               // [q][p] = Ginv[p][q], pitch P
+  float* Ms = sh + r * P;       // [q][c]
   const int64_t tiles = (c1 + 63) / 64;
   const int64_t b = blockIdx.x / tiles;
   const int64_t c0 = (blockIdx.x % tiles) * 64;
   const int tid = threadIdx.x;
   const float* Gb = Ginv + b * r * r;
   const float* Mb = M + b * r * c1;
-  for (int e = tid; e < r * r; e += 256) {
-    const int p = e / r, q = e % r;
-    Gs[q * r + p] = Gb[e];
+  for (int e4 = tid; e4 < r * r / 4; e4 += 256) {   // r % 4 == 0
+    const float4 v = *reinterpret_cast<const float4*>(Gb + e4 * 4);
+    const int p = (e4 * 4) / r, q = (e4 * 4) % r;
+    Gs[(q + 0) * P + p] = v.x;
+    Gs[(q + 1) * P + p] = v.y;
+    Gs[(q + 2) * P + p] = v.z;
+    Gs[(q + 3) * P + p] = v.w;
   }
   for (int e = tid; e < r * 16; e += 256) {
     const int q = e >> 4, c4 = (e & 15) * 4;
@@ -1133,7 +1140,7 @@ __global__ __launch_bounds__(256) void apply_inverse_kernel(const float* __restr
   for (int pq = tid >> 4; pq * 4 < r; pq += 16) {   // row quad
     float acc[4][4] = {};
     for (int q = 0; q < r; ++q) {
-      const float4 g4 = *reinterpret_cast<const float4*>(Gs + q * r + pq * 4);
+      const float4 g4 = *reinterpret_cast<const float4*>(Gs + q * P + pq * 4);
       const float4 m4 = *reinterpret_cast<const float4*>(Ms + q * 64 + cq * 4);
       const float gv[4] = {g4.x, g4.y, g4.z, g4.w}, mv[4] = {m4.x, m4.y, m4.z, m4.w};
 #pragma unroll
@@ -1268,7 +1275,7 @@ void forward_residual(const dyra_spec& s, const char* plan, const void* X, int64
     }
   }
   hipLaunchKernelGGL(apply_inverse_kernel<T>, dim3((unsigned)(cdiv(c1, 64) * B)), dim3(256),
-                     (size_t)(r * r + r * 64) * 4, st, Gi, M, Mp, r, c1);
+                     (size_t)(r * (r + 4) + r * 64) * 4, st, Gi, M, Mp, r, c1);
   E.mark(3, st);
   // S5: R^T (c2 x B r) = W_res^T (c2 x c1) . M' (B r x c1)^T
   launch_gemm_tn<C>(Wrt, c1, Mp, c1, Rt, B * r, c2, B * r, c1, nullptr, st);
