@@ -171,20 +171,23 @@ __global__ __launch_bounds__(C::NT, WPE) void s6_lowrank_kernel(const typename C
 
 constexpr int MO = 32;
 
-// Stage 1 + L: one pass over X.  A wave owns 32 rows; for each group of 8
-// blocks a it accumulates U_a (32 x 32 each) and then writes the permuted
-// V[row][j*32 + a0 .. a0 + 7] as one 16-byte store per (row, j).  L = X P is
-// accumulated across all 32 blocks (K slice a*32 .. a*32 + 31 per block).
+// Stage 1 + L: one pass over X.  A workgroup owns 32 rows; wave w takes the
+// 8 blocks a = 8w .. 8w + 7: it accumulates U_a (32 x 32 each), writes the
+// permuted V[row][j*32 + 8w .. 8w + 7] as one 16-byte store per (row, j), and
+// accumulates its K slice (a*32 .. a*32 + 31 for its 8 blocks) of L = X P.
+// The four partial L sums are added through LDS in a fixed order; wave 0
+// writes L and L^T.
 template <int RB>
-__global__ __launch_bounds__(256) void s1_monarch_kernel(const bf16_t* __restrict__ X,
+__global__ __launch_bounds__(256, 2) void s1_monarch_kernel(const bf16_t* __restrict__ X,
                                                          const bf16_t* __restrict__ B1t,
                                                          const bf16_t* __restrict__ Pt,
                                                          bf16_t* __restrict__ A, bf16_t* __restrict__ Lt,
                                                          int64_t n, int r, int64_t ldt) {
   constexpr int C = MO * MO;
+  __shared__ float part[3][RB][16][64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int l = lane & 31, g = lane >> 5;
-  const int64_t row = (int64_t)blockIdx.x * 128 + w * 32 + l;
+  const int64_t row = (int64_t)blockIdx.x * 32 + l;
   const bool rok = row < n;
   const int64_t lda = C + r;
   f32x16 lacc[RB];
@@ -192,43 +195,53 @@ __global__ __launch_bounds__(256) void s1_monarch_kernel(const bf16_t* __restric
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int v = 0; v < 16; ++v) lacc[rb][v] = 0.f;
-  for (int ag = 0; ag < MO / 8; ++ag) {
-    f32x16 uacc[8];
+  f32x16 uacc[8];
 #pragma unroll
-    for (int ai = 0; ai < 8; ++ai) {
+  for (int ai = 0; ai < 8; ++ai) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) uacc[ai][v] = 0.f;
-      const int a = ag * 8 + ai;
+    for (int v = 0; v < 16; ++v) uacc[ai][v] = 0.f;
+    const int a = w * 8 + ai;
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int kk = a * MO + 16 * s + 8 * g;
-        const uint4 xa = rok ? *reinterpret_cast<const uint4*>(X + row * C + kk) : zero4();
-        const uint4 b1 = *reinterpret_cast<const uint4*>(B1t + ((int64_t)a * MO + l) * MO + 16 * s + 8 * g);
-        TT<bf16_t>::mma(uacc[ai], b1, xa);
+    for (int s = 0; s < 2; ++s) {
+      const int kk = a * MO + 16 * s + 8 * g;
+      const uint4 xa = rok ? *reinterpret_cast<const uint4*>(X + row * C + kk) : zero4();
+      const uint4 b1 = *reinterpret_cast<const uint4*>(B1t + ((int64_t)a * MO + l) * MO + 16 * s + 8 * g);
+      TT<bf16_t>::mma(uacc[ai], b1, xa);
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          const int p = rb * 32 + l;
-          const uint4 pb = p < r ? *reinterpret_cast<const uint4*>(Pt + (int64_t)p * C + kk) : zero4();
-          TT<bf16_t>::mma(lacc[rb], pb, xa);
-        }
+      for (int rb = 0; rb < RB; ++rb) {
+        const int p = rb * 32 + l;
+        const uint4 pb = p < r ? *reinterpret_cast<const uint4*>(Pt + (int64_t)p * C + kk) : zero4();
+        TT<bf16_t>::mma(lacc[rb], pb, xa);
       }
     }
-    if (rok) {
-      // lane holds U[row][a*32 + j] for j = 8q + 4g + e (reg 4q + e), a = ag*8 + ai
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int j = 8 * q + 4 * g + e;
-          uint32_t pk[4];
-#pragma unroll
-          for (int h = 0; h < 4; ++h)
-            pk[h] = (uint32_t)f2bf(uacc[2 * h][4 * q + e]) | ((uint32_t)f2bf(uacc[2 * h + 1][4 * q + e]) << 16);
-          *reinterpret_cast<uint4*>(A + row * lda + j * MO + ag * 8) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-        }
-    }
   }
-  if (!rok) return;
+  if (rok) {
+    // lane holds U[row][a*32 + j] for j = 8q + 4g + e (reg 4q + e), a = 8w + ai
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = 8 * q + 4 * g + e;
+        uint32_t pk[4];
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+          pk[h] = (uint32_t)f2bf(uacc[2 * h][4 * q + e]) | ((uint32_t)f2bf(uacc[2 * h + 1][4 * q + e]) << 16);
+        *reinterpret_cast<uint4*>(A + row * lda + j * MO + w * 8) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+      }
+  }
+  // L partials: waves 1..3 -> LDS, wave 0 adds them in order
+  if (w > 0) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) part[w - 1][rb][v][lane] = lacc[rb][v];
+  }
+  __syncthreads();
+  if (w != 0 || !rok) return;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) lacc[rb][v] = ((lacc[rb][v] + part[0][rb][v][lane]) + part[1][rb][v][lane]) + part[2][rb][v][lane];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -237,8 +250,8 @@ __global__ __launch_bounds__(256) void s1_monarch_kernel(const bf16_t* __restric
       if (p0 >= r) continue;
       const float v[4] = {lacc[rb][4 * q], lacc[rb][4 * q + 1], lacc[rb][4 * q + 2], lacc[rb][4 * q + 3]};
       uint2 pk;
-      pk.x = (uint32_t)f2bf(lacc[rb][4 * q]) | ((uint32_t)f2bf(lacc[rb][4 * q + 1]) << 16);
-      pk.y = (uint32_t)f2bf(lacc[rb][4 * q + 2]) | ((uint32_t)f2bf(lacc[rb][4 * q + 3]) << 16);
+      pk.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+      pk.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
       *reinterpret_cast<uint2*>(A + row * lda + C + p0) = pk;
 #pragma unroll
       for (int e = 0; e < 4; ++e) Lt[(int64_t)(p0 + e) * ldt + row] = f2bf(v[e]);
@@ -1332,7 +1345,7 @@ int forward_lowrank(const dyra_spec& s, const char* plan, const void* X, const v
 template <int RB>
 void launch_monarch(const bf16_t* X, const char* plan, const PlanLayout& PL, bf16_t* A, bf16_t* Lt, int64_t n,
                     int r, int64_t ldt, hipStream_t st) {
-  hipLaunchKernelGGL((s1_monarch_kernel<RB>), dim3((unsigned)cdiv(n, 128)), dim3(256), 0, st, X,
+  hipLaunchKernelGGL((s1_monarch_kernel<RB>), dim3((unsigned)cdiv(n, 32)), dim3(256), 0, st, X,
                      reinterpret_cast<const bf16_t*>(plan + PL.B1t), reinterpret_cast<const bf16_t*>(plan + PL.Pt),
                      A, Lt, n, r, ldt);
 }
