@@ -106,7 +106,7 @@ def counters_traffic(workload, kernel_hash):
     return d.get("fused_output_traffic_bytes")
 
 
-def cpu_baseline(w, budget_s=12.0):
+def cpu_baseline(w, budget_s=12.0, t=1.0):
     """The float64 oracle forward on the host cores, on the same workload."""
     from input_adaptive_rank_amd import synth
     from oracle import dyra_oracle as O
@@ -120,13 +120,13 @@ def cpu_baseline(w, budget_s=12.0):
     t0 = time.perf_counter()
     runs = 0
     while True:
-        O.forward(inp.X, prep, inp.bias, w.B, w.s, eps=1e-6)
+        O.forward(inp.X, prep, inp.bias, w.B, w.s, eps=1e-6, t=t)
         runs += 1
         el = time.perf_counter() - t0
         if el >= budget_s or runs >= 3:
             break
     return {"value": round(w.n * runs / el, 1), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"full {w.name} batch ({w.B} x {w.s} tokens), float64 numpy oracle forward, "
+            "sample": f"full {w.name} batch ({w.B} x {w.s} tokens), float64 numpy oracle forward (ALS t = {t}), "
                       f"{runs} run(s) in {el:.2f} s (prepare excluded)"}
 
 
@@ -138,6 +138,8 @@ def main():
     ap.add_argument("--workload", default="vitl_fc1")
     ap.add_argument("--solver", choices=["auto", "chol", "ns"], default=None,
                     help="r x r solver (default: the workload's own choice)")
+    ap.add_argument("--als-half-steps", type=int, default=2,
+                    help="2 t ALS half-steps (2: t = 1, the default; 3: t = 1.5; 4: t = 2; low-rank bf16)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -160,7 +162,9 @@ def main():
     factors = D.prepare(inp.W, D.spec_of(w))
     prep_s = time.perf_counter() - t0
     solver = args.solver or w.solver
-    layer = D.DyraLayer(D.spec_of(w), factors, w.dtype, bias=inp.bias, device=dev, solver=D.SOLVERS[solver])
+    layer = D.DyraLayer(D.spec_of(w), factors, w.dtype, bias=inp.bias, device=dev, solver=D.SOLVERS[solver],
+                        half_steps=args.als_half_steps)
+    als = args.als_half_steps != 2
     tdt = D.torch_dtype(w.dtype)
     # 4 input/output buffer sets so X is not cache-resident from the previous step
     NB = 4
@@ -190,38 +194,43 @@ def main():
     ms = start.elapsed_time(end) / K
     # timed region 2: the same K steps with HIP events recorded between the
     # stages on the launch stream (per-stage times and the roofline kernel time)
-    start.record(stream)
-    for i in range(K):
-        layer.forward_events(Xs[i % NB], w.B, w.s, Ys[i % NB], ev[i], stream)
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms_events = start.elapsed_time(end) / K
-    stage_ms = {STAGES[j]: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(K)]))
-                for j in range(5)}
+    # -- for the t = 1 forward, whose stage boundaries the events mark
+    ms_events, stage_ms = None, None
+    if not als:
+        start.record(stream)
+        for i in range(K):
+            layer.forward_events(Xs[i % NB], w.B, w.s, Ys[i % NB], ev[i], stream)
+        end.record(stream)
+        torch.cuda.synchronize()
+        ms_events = start.elapsed_time(end) / K
+        stage_ms = {STAGES[j]: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(K)]))
+                    for j in range(5)}
     status = layer.status(w.B, w.s)
 
     work = stage_work(w)
-    stages = {}
-    for name, (fl, by) in work.items():
-        t = stage_ms[name] * 1e-3
-        stages[name] = {"ms": round(stage_ms[name], 5), "TFLOP/s": round(fl / t / 1e12, 1),
-                        "GB/s": round(by / t / 1e9, 1), "gflop": round(fl / 1e9, 3), "mb": round(by / 1e6, 2)}
     total_flops = sum(v[0] for v in work.values())
-
-    # roofline of the dominant kernel: the fused output GEMM (Y = [T|L][V;R_b] + bias)
-    fl, by = work["fused_output_Y"]
-    t6 = stage_ms["fused_output_Y"] * 1e-3
-    t_mfma, t_hbm = fl / (PEAK_BF16_TFLOPS * 1e12), by / (PEAK_HBM_GBS * 1e9)
     khash = kernel_source_hash()
-    traffic = counters_traffic(w.name, khash)
-    if t_hbm >= t_mfma:
-        roof = {"bound": "hbm", "achieved": round(by / t6 / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s"}
-    else:
-        roof = {"bound": "mfma", "achieved": round(fl / t6 / 1e12, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
-    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = traffic
-    roof["kernel"] = OUTPUT_KERNEL[w.kind]
-    roof["mfma_frac"] = round(fl / t6 / 1e12 / PEAK_BF16_TFLOPS, 4)
+    stages, roof = None, None
+    if not als:
+        stages = {}
+        for name, (fl, by) in work.items():
+            t = stage_ms[name] * 1e-3
+            stages[name] = {"ms": round(stage_ms[name], 5), "TFLOP/s": round(fl / t / 1e12, 1),
+                            "GB/s": round(by / t / 1e9, 1), "gflop": round(fl / 1e9, 3), "mb": round(by / 1e6, 2)}
+        # roofline of the dominant kernel: the fused output GEMM (Y = [T|L][V;R_b] + bias)
+        fl, by = work["fused_output_Y"]
+        t6 = stage_ms["fused_output_Y"] * 1e-3
+        t_mfma, t_hbm = fl / (PEAK_BF16_TFLOPS * 1e12), by / (PEAK_HBM_GBS * 1e9)
+        traffic = counters_traffic(w.name, khash)
+        if t_hbm >= t_mfma:
+            roof = {"bound": "hbm", "achieved": round(by / t6 / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+        else:
+            roof = {"bound": "mfma", "achieved": round(fl / t6 / 1e12, 1), "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s"}
+        roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+        roof["traffic"] = traffic
+        roof["kernel"] = OUTPUT_KERNEL[w.kind]
+        roof["mfma_frac"] = round(fl / t6 / 1e12 / PEAK_BF16_TFLOPS, 4)
 
     # dense comparators on the same shape: library MFMA GEMM and torch.matmul (hipBLASLt)
     dense = None
@@ -258,7 +267,7 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
 
-    cpu = None if args.no_cpu_baseline else cpu_baseline(w)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, t=args.als_half_steps / 2)
 
     out = {
         "metric": "DyRA layer tokens/s + % bf16 MFMA peak at ViT-L shape; speedup vs dense XW",
@@ -268,7 +277,7 @@ def main():
         "steps": K,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 5),
-        "ms_per_step_with_stage_events": round(ms_events, 5),
+        "ms_per_step_with_stage_events": None if ms_events is None else round(ms_events, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -277,9 +286,10 @@ def main():
         "config": {"workload": f"{w.name}: {WORKLOAD_TEXT.get(w.name, 'DyRA layer')}, B={w.B} x {w.s} tokens, "
                                f"{w.c1}->{w.c2}, {STRUCT_TEXT(w)}, r={w.r}, "
                                f"{'bf16' if w.dtype == synth.DT_BF16 else 'fp32'}, fp32 accumulate",
-                   "global_batch": w.B, "seq_len": w.s, "tokens": w.n, "solver": solver},
-        "tflops": round(total_flops / (ms * 1e-3) / 1e12, 1),
-        "pct_bf16_peak": round(100 * total_flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+                   "global_batch": w.B, "seq_len": w.s, "tokens": w.n, "solver": solver,
+                   "als_t": args.als_half_steps / 2},
+        "tflops": None if als else round(total_flops / (ms * 1e-3) / 1e12, 1),
+        "pct_bf16_peak": None if als else round(100 * total_flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
         "roofline": roof,
         "cpu_baseline": cpu,
         "dense": dense,

@@ -197,6 +197,27 @@ int dyra_forward(const dyra_spec* spec, const void* plan, const void* X, const v
                  int32_t solver, void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * More ALS iterations than the default one.  half_steps = 2 t: 2 is exactly
+ * dyra_forward (t = 1: L from the precomputed thin matrix, then R); 3 is
+ * t = 1.5 (then L again, L_b = X_b (W_res R_b^T)(R_b R_b^T + lambda I)^-1,
+ * lambda = ridge_eps * trace(R_b R_b^T) / r, solved by the sweep); 4 is
+ * t = 2 (then R again from the new L).  Y uses the last L and R.  Low-rank
+ * structure and bf16 only: EINVAL for another structure or half_steps
+ * outside 2..4, EDTYPE for fp32.  The workspace must hold
+ * dyra_workspace_size_als bytes for the same half_steps; otherwise the
+ * arguments, ownership and errors are those of dyra_forward.
+ * Source: nanless.github.io DyRA digest, "what the low-rank objective of the
+ * residual product is" (alternating least squares, the fix-R solve for L
+ * and the fix-L solve for R); paperlayer.ai 2.2 and E.3 (more iterations
+ * lower the error).
+ */
+int dyra_workspace_size_als(const dyra_spec* spec, int64_t B, int64_t s, int32_t dtype, int32_t half_steps,
+                            size_t* bytes);
+int dyra_forward_als(const dyra_spec* spec, const void* plan, const void* X, const void* bias, void* Y,
+                     int64_t B, int64_t s, int32_t dtype, float ridge_eps, int32_t solver, int32_t half_steps,
+                     void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * dyra_forward with stage-boundary events, a profiling aid.  events[i] are
  * caller-created hipEvent_t handles (passed as void*; NULL entries skipped;
  * nevents <= 6 used): events[0] is recorded on `stream` before the first

@@ -161,6 +161,74 @@ __global__ __launch_bounds__(C::NT, WPE) void s6_lowrank_kernel(const typename C
 }
 
 // ===========================================================================
+// Left ALS step (t > 1): L_b = X_b W_res R_b^T (R_b R_b^T + lambda I)^-1.
+// The thin products R_b R_b^T and R_b W_res^T come from the token-reduction
+// kernel in relative addressing (R_b's rows as "L^T", W_res^T as "X",
+// c2 playing the token axis); the inverse is applied by apply_inverse_kernel
+// (Z_b^T = (K_b + lambda I)^-1 Q_b^T); then L_b = X_b Z_b here.
+// ===========================================================================
+
+// out [cols x rows] = in [rows x cols]^T, 16-bit elements, 64 x 64 tiles
+// through LDS (the padded pitch keeps the column reads off one bank).
+__global__ __launch_bounds__(256) void transpose_b16_kernel(const bf16_t* __restrict__ in, bf16_t* __restrict__ out,
+                                                            int64_t rows, int64_t cols) {
+  __shared__ bf16_t tile[64][66];
+  const int64_t tiles_c = (cols + 63) / 64;
+  const int64_t r0 = (int64_t)(blockIdx.x / tiles_c) * 64, c0 = (int64_t)(blockIdx.x % tiles_c) * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int y = ty; y < 64; y += 4) {
+    const int64_t rr = r0 + y, cc = c0 + tx;
+    tile[y][tx] = (rr < rows && cc < cols) ? in[rr * cols + cc] : (bf16_t)0;
+  }
+  __syncthreads();
+  for (int y = ty; y < 64; y += 4) {
+    const int64_t oc = c0 + y, orr = r0 + tx;   // out row oc, column orr
+    if (oc < cols && orr < rows) out[oc * rows + orr] = tile[tx][y];
+  }
+}
+
+// L_b = X_b Z_b for every segment: out [n x r] at TL columns k .. k + r - 1
+// (pitch ldo) and L^T.  Zt: [B r x c1] (Z_b^T, row-major).  A tile whose rows
+// span several segments accumulates one k-loop per segment with the rows of
+// the others masked off.
+template <class C>
+__global__ __launch_bounds__(C::NT) void s1_left_kernel(const bf16_t* X, const bf16_t* Zt, bf16_t* TL, bf16_t* Lt,
+                                                        int64_t n, int64_t c1, int k, int r, int64_t seg, int64_t B,
+                                                        int64_t ldt, int tiles_n, int64_t ldo) {
+  constexpr int E = 2, KPC = 8;
+  __shared__ __attribute__((aligned(16))) char lds[C::LDS];
+  const int t = xcd_tile_id(blockIdx.x, gridDim.x);
+  const int64_t m0 = (int64_t)(t / tiles_n) * C::BM, n0 = (int64_t)(t % tiles_n) * C::BN;
+  const int64_t bfirst = m0 / seg;
+  const int64_t blast = imin64(B - 1, (imin64(m0 + C::BM, n) - 1) / seg);
+  const int nkc = ktiles(c1 * E);
+  const int total = (int)(blast - bfirst + 1) * nkc;
+  auto src = [=](int tt, Phase& ph, int& kt) {
+    const int64_t b = bfirst + tt / nkc;
+    kt = tt % nkc;
+    ph.a = OpK{reinterpret_cast<const char*>(X), c1 * E, m0, b * seg, imin64((b + 1) * seg, n), c1 * E};
+    ph.b = OpK{reinterpret_cast<const char*>(Zt + b * r * c1), c1 * E, n0, 0, r, c1 * E};
+  };
+  f32x16 acc[C::FM][C::FN];
+  gemm_mainloop<C>(src, total, lds, acc);
+  stage_out<C>(lds, acc, nullptr, 0);
+  copy_out<C>(lds, reinterpret_cast<char*>(TL) + (m0 * ldo + k + n0) * E, ldo * E, (int)imin64(C::BM, n - m0),
+              (r - n0) * E);
+  // the same columns, transposed: Lt[j][m0 + rows]
+  const int ncol = (int)imin64(C::BN, r - n0);
+  const int groups = C::BM / KPC;
+  for (int c = threadIdx.x; c < ncol * groups; c += C::NT) {
+    const int jl = c / groups, rg = c % groups;
+    const int64_t row = m0 + (int64_t)rg * KPC;
+    if (row >= ldt) continue;
+    bf16_t v[KPC];
+#pragma unroll
+    for (int e = 0; e < KPC; ++e) v[e] = staged_elem<C>(lds, rg * KPC + e, jl);
+    *reinterpret_cast<uint4*>(Lt + (n0 + jl) * ldt + row) = *reinterpret_cast<const uint4*>(v);
+  }
+}
+
+// ===========================================================================
 // Monarch static branch (m = 32 blocks of 32 x 32, c = 1024), bf16.
 // W_hat = blockdiag(B1_a) . Pi . blockdiag(B2_j), Pi the reshape(32, 32)
 // transpose: u_a = x_a B1_a, v[j*32 + a] = u[a*32 + j], y_j = v_j B2_j.
@@ -731,10 +799,12 @@ struct S3Lds {
   static constexpr int BYTES = G_END > 64 * 1024 ? G_END : 64 * 1024;
 };
 
+// tbase: the token index of column 0 of the L^T rows (0 unless the rows are
+// addressed relative to the segment).
 template <int NRB>
 __device__ __forceinline__ void s3_m_strip(const bf16_t* __restrict__ Lt, int64_t ldt,
                                            const bf16_t* __restrict__ X, int64_t c1, int r, int64_t lo,
-                                           int64_t hi, int64_t c0, float* __restrict__ Mb, char* lds) {
+                                           int64_t hi, int64_t c0, float* __restrict__ Mb, char* lds, int64_t tbase) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int j = lane & 15, g = lane >> 4;
   f32x4 acc[NRB][8];
@@ -757,7 +827,7 @@ __device__ __forceinline__ void s3_m_strip(const bf16_t* __restrict__ Lt, int64_
 #pragma unroll
     for (int ib = 0; ib < NRB; ++ib) {
       const int row = ib * 16 + j;
-      uint4 v = (row < r && t0 < ldt) ? *reinterpret_cast<const uint4*>(Lt + row * ldt + t0) : zero4();
+      uint4 v = (row < r && t0 - tbase < ldt) ? *reinterpret_cast<const uint4*>(Lt + row * ldt + t0) : zero4();
       av[ib] = mask_tokens<bf16_t>(v, t0, lo, hi);
     }
   };
@@ -854,7 +924,7 @@ __device__ __forceinline__ void s3_m_strip(const bf16_t* __restrict__ Lt, int64_
 // L^T rows with 32x32x16 MFMAs; the 4 waves split the tokens.
 template <int NB>
 __device__ __forceinline__ void s3_gram(const bf16_t* __restrict__ Lt, int64_t ldt, int r, int64_t lo, int64_t hi,
-                                        float* Gs, char* lds) {
+                                        float* Gs, char* lds, int64_t tbase) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l = lane & 31, g = lane >> 5;
   f32x16 acc[NB][NB];
@@ -878,7 +948,7 @@ __device__ __forceinline__ void s3_gram(const bf16_t* __restrict__ Lt, int64_t l
 #pragma unroll
       for (int rb = 0; rb < NB; ++rb) {
         const int row = rb * 32 + l;
-        uint4 v = (in && row < r && t0 < ldt) ? *reinterpret_cast<const uint4*>(Lt + row * ldt + t0) : zero4();
+        uint4 v = (in && row < r && t0 - tbase < ldt) ? *reinterpret_cast<const uint4*>(Lt + row * ldt + t0) : zero4();
         f[u][rb] = mask_tokens<bf16_t>(v, t0, lo, hi);
       }
     }
@@ -917,15 +987,26 @@ template <int NRB, int NB>
 __global__ __launch_bounds__(S3_NT, NRB <= 4 ? 2 : 1) void s3_reduce_solve_kernel(
     const bf16_t* __restrict__ Lt, int64_t ldt, const bf16_t* __restrict__ X, int64_t c1, int r, int64_t seg,
     int64_t n, int64_t B, float* __restrict__ M, float* __restrict__ G, float* __restrict__ Gi,
-    int32_t* __restrict__ status, float eps, int do_sweep, int strips) {
+    int32_t* __restrict__ status, float eps, int do_sweep, int strips, int64_t lt_seg_rows, int x_rel) {
   __shared__ __attribute__((aligned(16))) char lds[S3Lds<NB>::BYTES];
   SweepLds* sl = reinterpret_cast<SweepLds*>(lds + S3Lds<NB>::SW_OFF);
   const int64_t bid = blockIdx.x;
+  // Relative addressing (the left ALS step reuses this kernel): segment b's
+  // L^T rows start at row b * lt_seg_rows with their token 0 at column 0, and
+  // with x_rel the segment's X rows start at row 0 of X.
+  auto seg_ptrs = [&](int64_t b, int64_t lo, const bf16_t*& Ltb, const bf16_t*& Xb, int64_t& tbase) {
+    Ltb = lt_seg_rows ? Lt + b * lt_seg_rows * ldt - lo : Lt;
+    Xb = x_rel ? X - lo * c1 : X;
+    tbase = lt_seg_rows ? lo : 0;
+  };
   if (bid < B) {
     const int64_t b = bid;
     const int64_t lo = b * seg, hi = imin64((b + 1) * seg, n);
+    const bf16_t *Ltb, *Xb;
+    int64_t tbase;
+    seg_ptrs(b, lo, Ltb, Xb, tbase);
     float* Gs = reinterpret_cast<float*>(lds + S3Lds<NB>::G_OFF);
-    s3_gram<NB>(Lt, ldt, r, lo, hi, Gs, lds);
+    s3_gram<NB>(Ltb, ldt, r, lo, hi, Gs, lds, tbase);
     // publish G (the Newton-Schulz path and diagnostics read it)
     for (int e = threadIdx.x; e < r * r; e += S3_NT) G[b * r * r + e] = Gs[e];
     if (do_sweep) {
@@ -940,7 +1021,10 @@ __global__ __launch_bounds__(S3_NT, NRB <= 4 ? 2 : 1) void s3_reduce_solve_kerne
   const int64_t b = u / strips;
   const int64_t c0 = (u % strips) * S3_STRIP;
   const int64_t lo = b * seg, hi = imin64((b + 1) * seg, n);
-  s3_m_strip<NRB>(Lt, ldt, X, c1, r, lo, hi, c0, M + b * r * c1, lds);
+  const bf16_t *Ltb, *Xb;
+  int64_t tbase;
+  seg_ptrs(b, lo, Ltb, Xb, tbase);
+  s3_m_strip<NRB>(Ltb, ldt, Xb, c1, r, lo, hi, c0, M + b * r * c1, lds, tbase);
 }
 
 // S4a as its own launch: one 256-thread workgroup per segment.  With
@@ -1229,10 +1313,10 @@ struct StageEvents {
 template <int NRB, int NB>
 void launch_s3_bf16(const bf16_t* Lt, int64_t ldt, const bf16_t* X, int64_t c1, int r, int64_t seg, int64_t n,
                     int64_t B, float* M, float* G, float* Gi, int32_t* stat, float eps, bool sweep,
-                    hipStream_t st) {
+                    hipStream_t st, int64_t lt_seg_rows = 0, bool x_rel = false) {
   const int strips = (int)cdiv(c1, S3_STRIP);
   hipLaunchKernelGGL((s3_reduce_solve_kernel<NRB, NB>), dim3((unsigned)(B + B * strips)), dim3(S3_NT), 0, st, Lt,
-                     ldt, X, c1, r, seg, n, B, M, G, Gi, stat, eps, sweep ? 1 : 0, strips);
+                     ldt, X, c1, r, seg, n, B, M, G, Gi, stat, eps, sweep ? 1 : 0, strips, lt_seg_rows, x_rel ? 1 : 0);
 }
 
 // S3, S4 and S5, shared by every structure: M_b, G_b, Ginv_b, M'_b and
@@ -1294,10 +1378,47 @@ void forward_residual(const dyra_spec& s, const char* plan, const void* X, int64
   launch_gemm_tn<C>(Wrt, c1, Mp, c1, Rt, B * r, c2, B * r, c1, nullptr, st);
 }
 
+typedef GemmCfg<bf16_t, 128, 64, 2, 2> CfgL;   // left ALS step: L_b = X_b Z_b (r <= 64 columns per tile)
+
+// One left ALS half-step on the bf16 workspace: R^T -> R; K_b = R_b R_b^T and
+// Q_b^T = R_b W_res^T (fp32) with (K_b + lambda_b I)^-1 by the sweep; Z_b^T;
+// then L_b = X_b Z_b overwrites L (and L^T) in the workspace.
+void left_step_bf16(const dyra_spec& s, const char* plan, const bf16_t* X, int64_t B, int64_t seg, float eps,
+                    char* ws, hipStream_t st, int half_steps) {
+  const PlanLayout PL = plan_layout(s, DYRA_BF16);
+  const WsLayout WL = ws_layout(s, B, seg, DYRA_BF16, half_steps);
+  const int64_t n = B * seg, c1 = s.c1, c2 = s.c2;
+  const int k = s.k, r = s.r;
+  const bf16_t* Rt = reinterpret_cast<const bf16_t*>(ws + WL.Rt);
+  bf16_t* R = reinterpret_cast<bf16_t*>(ws + WL.R);
+  float* K = reinterpret_cast<float*>(ws + WL.K);
+  float* Kinv = reinterpret_cast<float*>(ws + WL.Kinv);
+  float* Qt = reinterpret_cast<float*>(ws + WL.Qt);
+  bf16_t* Zt = reinterpret_cast<bf16_t*>(ws + WL.Zt);
+  int32_t* kst = reinterpret_cast<int32_t*>(ws + WL.kstatus);
+  const bf16_t* Wrt = reinterpret_cast<const bf16_t*>(plan + PL.Wrt);
+  // R [B r x c2] = (R^T [c2 x B r])^T
+  hipLaunchKernelGGL(transpose_b16_kernel, dim3((unsigned)(cdiv(c2, 64) * cdiv(B * r, 64))), dim3(256), 0, st, Rt, R,
+                     c2, B * r);
+  // K_b, Q_b^T, (K_b + lambda I)^-1: c2 is the reduction ("token") axis
+  const int64_t nn = B * c2;
+  if (r <= 16) launch_s3_bf16<1, 1>(R, c2, Wrt, c1, r, c2, nn, B, Qt, K, Kinv, kst, eps, true, st, r, true);
+  else if (r <= 32) launch_s3_bf16<2, 1>(R, c2, Wrt, c1, r, c2, nn, B, Qt, K, Kinv, kst, eps, true, st, r, true);
+  else if (r <= 64) launch_s3_bf16<4, 2>(R, c2, Wrt, c1, r, c2, nn, B, Qt, K, Kinv, kst, eps, true, st, r, true);
+  else launch_s3_bf16<8, 4>(R, c2, Wrt, c1, r, c2, nn, B, Qt, K, Kinv, kst, eps, true, st, r, true);
+  hipLaunchKernelGGL(apply_inverse_kernel<bf16_t>, dim3((unsigned)(cdiv(c1, 64) * B)), dim3(256),
+                     (size_t)(r * (r + 4) + r * 64) * 4, st, Kinv, Qt, Zt, r, c1);
+  // L_b = X_b Z_b into [T | L] and L^T
+  const int tiles_n = (int)cdiv(r, CfgL::BN);
+  hipLaunchKernelGGL(s1_left_kernel<CfgL>, dim3((unsigned)(cdiv(n, CfgL::BM) * tiles_n)), dim3(CfgL::NT), 0, st, X,
+                     Zt, reinterpret_cast<bf16_t*>(ws + WL.A), reinterpret_cast<bf16_t*>(ws + WL.Lt), n, c1, k, r,
+                     seg, B, lt_pitch(n), tiles_n, (int64_t)(k + r));
+}
+
 template <class C, class C3, class C6>
 int forward_lowrank(const dyra_spec& s, const char* plan, const void* X, const void* bias, void* Y,
                     int64_t B, int64_t seg, float eps, int solver, char* ws, hipStream_t st,
-                    const StageEvents& E) {
+                    const StageEvents& E, int half_steps = 2) {
   typedef typename C::elem T;
   const int dtype = TT<T>::ESZ == 2 ? DYRA_BF16 : DYRA_F32;
   const PlanLayout PL = plan_layout(s, dtype);
@@ -1329,6 +1450,13 @@ int forward_lowrank(const dyra_spec& s, const char* plan, const void* X, const v
   }
   E.mark(1, st);
   forward_residual<C, C3>(s, plan, X, B, seg, eps, solver, ws, st, E);
+  // further ALS half-steps: left (L from R), right (R from L), ...
+  if constexpr (TT<T>::ESZ == 2) {
+    for (int h = 2; h < half_steps; ++h) {
+      if (h % 2 == 0) left_step_bf16(s, plan, reinterpret_cast<const bf16_t*>(X), B, seg, eps, ws, st, half_steps);
+      else forward_residual<C, C3>(s, plan, X, B, seg, eps, solver, ws, st, StageEvents{nullptr, 0});
+    }
+  }
   E.mark(4, st);
   {  // S6: Y = T V + L R_b + bias
     const int tiles_n = (int)cdiv(c2, C6::BN);
@@ -1431,8 +1559,17 @@ int forward_blast(const dyra_spec& s, const char* plan, const void* X, const voi
   return hipGetLastError() == hipSuccess ? DYRA_OK : DYRA_EHIP;
 }
 
+// half_steps: 2 t of the ALS (2: t = 1; 3: t = 1.5; 4: t = 2); beyond 2 only
+// for the low-rank structure in bf16.
+int check_als(const dyra_spec& spec, int32_t dtype, int32_t half_steps) {
+  if (half_steps < 2 || half_steps > 4) return DYRA_EINVAL;
+  if (half_steps > 2 && spec.kind != DYRA_LOWRANK) return DYRA_EINVAL;
+  if (half_steps > 2 && dtype != DYRA_BF16) return DYRA_EDTYPE;
+  return DYRA_OK;
+}
+
 int check_forward_args(const dyra_spec* spec, const void* plan, const void* X, void* Y, int64_t B, int64_t s,
-                       int32_t dtype, float eps, int32_t solver, void* ws, size_t ws_bytes) {
+                       int32_t dtype, float eps, int32_t solver, void* ws, size_t ws_bytes, int32_t half_steps = 2) {
   if (!spec || !plan || !X || !Y || !ws) return DYRA_EINVAL;
   int rc = validate_spec(spec);
   if (rc) return rc;
@@ -1445,7 +1582,9 @@ int check_forward_args(const dyra_spec* spec, const void* plan, const void* X, v
   if ((reinterpret_cast<uintptr_t>(plan) | reinterpret_cast<uintptr_t>(X) | reinterpret_cast<uintptr_t>(Y) |
        reinterpret_cast<uintptr_t>(ws)) & 15)
     return DYRA_EINVAL;
-  if (ws_bytes < ws_layout(*spec, B, s, dtype).total) return DYRA_EWORKSPACE;
+  rc = check_als(*spec, dtype, half_steps);
+  if (rc) return rc;
+  if (ws_bytes < ws_layout(*spec, B, s, dtype, half_steps).total) return DYRA_EWORKSPACE;
   return DYRA_OK;
 }
 
@@ -1462,11 +1601,25 @@ extern "C" int dyra_workspace_size(const dyra_spec* spec, int64_t B, int64_t s, 
   return DYRA_OK;
 }
 
+extern "C" int dyra_workspace_size_als(const dyra_spec* spec, int64_t B, int64_t s, int32_t dtype,
+                                       int32_t half_steps, size_t* bytes) {
+  if (!spec || !bytes) return DYRA_EINVAL;
+  int rc = validate_spec(spec);
+  if (rc) return rc;
+  rc = validate_dtype(*spec, dtype);
+  if (rc) return rc;
+  rc = check_als(*spec, dtype, half_steps);
+  if (rc) return rc;
+  if (B <= 0 || s <= 0 || B * s >= ((int64_t)1 << 31)) return DYRA_ESHAPE;
+  *bytes = ws_layout(*spec, B, s, dtype, half_steps).total;
+  return DYRA_OK;
+}
+
 namespace {
 int forward_impl(const dyra_spec* spec, const void* plan, const void* X, const void* bias, void* Y, int64_t B,
                  int64_t s, int32_t dtype, float ridge_eps, int32_t solver, void* workspace, size_t ws_bytes,
-                 void* stream, const StageEvents& E) {
-  int rc = check_forward_args(spec, plan, X, Y, B, s, dtype, ridge_eps, solver, workspace, ws_bytes);
+                 void* stream, const StageEvents& E, int32_t half_steps = 2) {
+  int rc = check_forward_args(spec, plan, X, Y, B, s, dtype, ridge_eps, solver, workspace, ws_bytes, half_steps);
   if (rc) return rc;
   if (bias && (reinterpret_cast<uintptr_t>(bias) & 15)) return DYRA_EINVAL;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
@@ -1476,7 +1629,8 @@ int forward_impl(const dyra_spec* spec, const void* plan, const void* X, const v
     return forward_monarch(*spec, plan_c, X, bias, Y, B, s, ridge_eps, solver, ws, st, E);
   if (spec->kind == DYRA_BLAST) return forward_blast(*spec, plan_c, X, bias, Y, B, s, ridge_eps, solver, ws, st, E);
   if (dtype == DYRA_BF16)
-    return forward_lowrank<CfgB, CfgB3, CfgB6>(*spec, plan_c, X, bias, Y, B, s, ridge_eps, solver, ws, st, E);
+    return forward_lowrank<CfgB, CfgB3, CfgB6>(*spec, plan_c, X, bias, Y, B, s, ridge_eps, solver, ws, st, E,
+                                               half_steps);
   return forward_lowrank<CfgF, CfgF3, CfgF>(*spec, plan_c, X, bias, Y, B, s, ridge_eps, solver, ws, st, E);
 }
 }  // namespace
@@ -1486,6 +1640,13 @@ extern "C" int dyra_forward(const dyra_spec* spec, const void* plan, const void*
                             void* workspace, size_t ws_bytes, void* stream) {
   return forward_impl(spec, plan, X, bias, Y, B, s, dtype, ridge_eps, solver, workspace, ws_bytes, stream,
                       StageEvents{nullptr, 0});
+}
+
+extern "C" int dyra_forward_als(const dyra_spec* spec, const void* plan, const void* X, const void* bias, void* Y,
+                                int64_t B, int64_t s, int32_t dtype, float ridge_eps, int32_t solver,
+                                int32_t half_steps, void* workspace, size_t ws_bytes, void* stream) {
+  return forward_impl(spec, plan, X, bias, Y, B, s, dtype, ridge_eps, solver, workspace, ws_bytes, stream,
+                      StageEvents{nullptr, 0}, half_steps);
 }
 
 extern "C" int dyra_forward_events(const dyra_spec* spec, const void* plan, const void* X, const void* bias,

@@ -108,10 +108,13 @@ inline PlanLayout plan_layout(const dyra_spec& s, int dtype) {
 struct WsLayout {
   int64_t wa = 0;
   size_t A = 0, Wp = 0, Lt = 0, G = 0, M = 0, Ginv = 0, Mp = 0, Rt = 0, status = 0;
+  // left ALS steps (half_steps > 2): R [B r x c2], K and Kinv [B x r x r]
+  // fp32, Q^T [B x r x c1] fp32, Z^T [B x r x c1], their status words [B]
+  size_t R = 0, K = 0, Kinv = 0, Qt = 0, Zt = 0, kstatus = 0;
   size_t total = 0;
 };
 
-inline WsLayout ws_layout(const dyra_spec& s, int64_t B, int64_t seg, int dtype) {
+inline WsLayout ws_layout(const dyra_spec& s, int64_t B, int64_t seg, int dtype, int half_steps = 2) {
   WsLayout W;
   const size_t e = elem_bytes(dtype);
   const size_t n = (size_t)(B * seg), r = (size_t)s.r, c1 = (size_t)s.c1, c2 = (size_t)s.c2;
@@ -135,6 +138,14 @@ inline WsLayout ws_layout(const dyra_spec& s, int64_t B, int64_t seg, int dtype)
   W.Mp = take((size_t)B * r * c1 * e);
   W.Rt = take(c2 * (size_t)B * r * e);
   W.status = take((size_t)B * 4);
+  if (half_steps > 2) {
+    W.R = take((size_t)B * r * c2 * e);
+    W.K = take((size_t)B * r * r * 4);
+    W.Kinv = take((size_t)B * r * r * 4);
+    W.Qt = take((size_t)B * r * c1 * 4);
+    W.Zt = take((size_t)B * r * c1 * e);
+    W.kstatus = take((size_t)B * 4);
+  }
   W.total = off;
   return W;
 }

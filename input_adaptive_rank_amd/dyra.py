@@ -85,6 +85,8 @@ def lib():
             "dyra_solver_status": [SP, P, I64, I64, I32, ctypes.POINTER(I32), P],
             "dyra_dense_ref": [P, P, P, P, I64, I64, I64, I32, P],
             "dyra_workspace_offsets": [SP, I64, I64, I32, ctypes.POINTER(WsOffsets)],
+            "dyra_workspace_size_als": [SP, I64, I64, I32, I32, ctypes.POINTER(SZ)],
+            "dyra_forward_als": [SP, P, P, P, P, I64, I64, I32, ctypes.c_float, I32, I32, P, SZ, P],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -224,6 +226,22 @@ def forward(spec: Spec, plan, X, bias, Y, B: int, s: int, dtype: int, eps: float
     _check("dyra_forward", rc)
 
 
+def workspace_size_als(spec: Spec, B: int, s: int, dtype: int, half_steps: int) -> int:
+    n = ctypes.c_size_t()
+    _check("dyra_workspace_size_als",
+           lib().dyra_workspace_size_als(ctypes.byref(spec), B, s, dtype, half_steps, ctypes.byref(n)))
+    return n.value
+
+
+def forward_als(spec: Spec, plan, X, bias, Y, B: int, s: int, dtype: int, eps: float, solver: int,
+                half_steps: int, workspace, stream=None):
+    """The forward with 2 t = half_steps ALS half-steps (asynchronous)."""
+    rc = lib().dyra_forward_als(ctypes.byref(spec), _dev(plan, "plan"), _dev(X, "X"), _dev(bias, "bias"),
+                                _dev(Y, "Y"), B, s, dtype, eps, solver, half_steps, _dev(workspace, "workspace"),
+                                workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("dyra_forward_als", rc)
+
+
 def forward_events(spec: Spec, plan, X, bias, Y, B: int, s: int, dtype: int, eps: float, solver: int,
                    workspace, events, stream=None):
     """dyra_forward recording stage-boundary events (torch.cuda.Event objects
@@ -263,9 +281,10 @@ class DyraLayer:
     """A prepared DyRA layer resident on one GPU: device plan + workspace."""
 
     def __init__(self, spec: Spec, factors: dict, dtype: int, bias: np.ndarray | None = None,
-                 device="cuda", eps: float = 1e-6, solver: int = SOLVER_AUTO):
+                 device="cuda", eps: float = 1e-6, solver: int = SOLVER_AUTO, half_steps: int = 2):
         torch = _torch()
         self.spec, self.dtype, self.eps, self.solver = spec, dtype, eps, solver
+        self.half_steps = half_steps   # 2 t ALS half-steps (2: t = 1)
         self.device = torch.device(device)
         host = plan_pack(spec, factors, dtype)
         self.plan = torch.from_numpy(host).to(self.device)
@@ -277,7 +296,8 @@ class DyraLayer:
         torch = _torch()
         key = (B, s)
         if self._ws_key != key:
-            n = workspace_size(self.spec, B, s, self.dtype)
+            n = (workspace_size(self.spec, B, s, self.dtype) if self.half_steps == 2 else
+                 workspace_size_als(self.spec, B, s, self.dtype, self.half_steps))
             if self._ws is None or self._ws.numel() < n:
                 self._ws = torch.empty(n, dtype=torch.uint8, device=self.device)
             self._ws_key = key
@@ -289,7 +309,11 @@ class DyraLayer:
             raise ValueError("X dtype does not match the plan dtype")
         Y = out if out is not None else torch.empty((B * s, self.spec.c2), dtype=X.dtype, device=X.device)
         ws = self.workspace(B, s)
-        forward(self.spec, self.plan, X, self.bias, Y, B, s, self.dtype, self.eps, self.solver, ws, stream)
+        if self.half_steps == 2:
+            forward(self.spec, self.plan, X, self.bias, Y, B, s, self.dtype, self.eps, self.solver, ws, stream)
+        else:
+            forward_als(self.spec, self.plan, X, self.bias, Y, B, s, self.dtype, self.eps, self.solver,
+                        self.half_steps, ws, stream)
         return Y
 
     def forward_events(self, X, B: int, s: int, out, events, stream=None):

@@ -45,9 +45,10 @@ def rounded_prep(prep, dtype):
     return dict(prep, static=st, P=rnd(prep["P"]), W_res=rnd(prep["W_res"]))
 
 
-def gpu_forward(w, factors, X, bias, eps=1e-6, solver="auto", repeat=1):
+def gpu_forward(w, factors, X, bias, eps=1e-6, solver="auto", repeat=1, half_steps=2):
     import torch
-    layer = D.DyraLayer(D.spec_of(w), factors, w.dtype, bias=bias, eps=eps, solver=D.SOLVERS[solver])
+    layer = D.DyraLayer(D.spec_of(w), factors, w.dtype, bias=bias, eps=eps, solver=D.SOLVERS[solver],
+                        half_steps=half_steps)
     Xd = D.to_device(X, w.dtype)
     outs = []
     for _ in range(repeat):
@@ -58,20 +59,22 @@ def gpu_forward(w, factors, X, bias, eps=1e-6, solver="auto", repeat=1):
     return outs, status
 
 
-def run_same_factor_case(w, eps=1e-6, solver="auto", tol=None, inputs=None, prep=None):
+def run_same_factor_case(w, eps=1e-6, solver="auto", tol=None, inputs=None, prep=None, half_steps=2):
     """Same-factor parity: GPU forward vs oracle forward on identical inputs
-    and identical (rounded) factors.  Returns (err, status, Y_gpu, Y_oracle)."""
+    and identical (rounded) factors, with t = half_steps / 2 ALS iterations.
+    Returns (err, status, Y_gpu, Y_oracle)."""
     t0 = time.time()
     inp = inputs if inputs is not None else synth.make_inputs(w)
     if prep is None:
         prep = oracle_prepare(w, inp.W)
     rp = rounded_prep(prep, w.dtype)
-    Y_or = O.forward(inp.X, rp, inp.bias, w.B, w.s, eps=eps)
+    Y_or = O.forward(inp.X, rp, inp.bias, w.B, w.s, eps=eps, t=half_steps / 2)
     t1 = time.time()
-    (Yg,), status = gpu_forward(w, host_factors_from_oracle(prep), inp.X, inp.bias, eps=eps, solver=solver)
+    (Yg,), status = gpu_forward(w, host_factors_from_oracle(prep), inp.X, inp.bias, eps=eps, solver=solver,
+                                half_steps=half_steps)
     err = O.rel_fro(Yg, Y_or)
     log(f"  case {w.name} B={w.B} s={w.s} c1={w.c1} c2={w.c2} r={w.r} k={w.k} dtype={w.dtype} "
-        f"solver={solver}: rel_fro={err:.3e} status={np.unique(status).tolist()} "
+        f"solver={solver} t={half_steps / 2}: rel_fro={err:.3e} status={np.unique(status).tolist()} "
         f"(oracle {t1 - t0:.1f}s, gpu {time.time() - t1:.1f}s)")
     tol = TOL[w.dtype] if tol is None else tol
     assert np.all(np.isfinite(Yg)), "non-finite output"

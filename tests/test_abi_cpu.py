@@ -128,3 +128,31 @@ def test_prepare_rejects_missing_outputs():
     rc = D.lib().dyra_prepare(ctypes.byref(spec), W.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
                               ctypes.byref(hf), 1)
     assert rc == -1
+
+
+def test_als_entry_points_validate_on_host():
+    """dyra_workspace_size_als / dyra_forward_als reject what they do not
+    support before any HIP call: half_steps outside 2..4, a structure other
+    than low-rank, fp32."""
+    L = D.lib()
+    lowrank = D.make_spec(synth.KIND_LOWRANK, 256, 512, 16, k=32)
+    monarch = D.make_spec(synth.KIND_MONARCH, 1024, 1024, 16, mblk=32)
+    n = ctypes.c_size_t()
+    for h, rc in ((2, 0), (3, 0), (4, 0), (1, -1), (5, -1)):
+        assert L.dyra_workspace_size_als(ctypes.byref(lowrank), 2, 64, synth.DT_BF16, h, ctypes.byref(n)) == rc
+    assert L.dyra_workspace_size_als(ctypes.byref(lowrank), 2, 64, synth.DT_F32, 3, ctypes.byref(n)) == -6
+    assert L.dyra_workspace_size_als(ctypes.byref(monarch), 2, 64, synth.DT_BF16, 3, ctypes.byref(n)) == -1
+    sizes = []
+    for h in (2, 3, 4):
+        L.dyra_workspace_size_als(ctypes.byref(lowrank), 2, 64, synth.DT_BF16, h, ctypes.byref(n))
+        sizes.append(n.value)
+    base = ctypes.c_size_t()
+    L.dyra_workspace_size(ctypes.byref(lowrank), 2, 64, synth.DT_BF16, ctypes.byref(base))
+    assert sizes[0] == base.value and sizes[1] == sizes[2] > sizes[0]
+    # forward: argument errors come back before any device work
+    assert L.dyra_forward_als(ctypes.byref(lowrank), 16, 16, None, 16, 2, 64, synth.DT_BF16, 1e-6, 0, 7, 16,
+                              1 << 30, None) == -1
+    assert L.dyra_forward_als(ctypes.byref(lowrank), 16, 16, None, 16, 2, 64, synth.DT_F32, 1e-6, 0, 3, 16,
+                              1 << 30, None) == -6
+    assert L.dyra_forward_als(ctypes.byref(lowrank), 16, 16, None, 16, 2, 64, synth.DT_BF16, 1e-6, 0, 3, 16,
+                              sizes[0], None) == -3
