@@ -253,7 +253,10 @@ def main():
 
         it = max(10, K // 2)
         ms_ref = timeit(lambda i: D.dense_ref(Xs[i % NB], Wt, bias_d, Ys[i % NB], w.dtype), it)
-        ms_torch = timeit(lambda i: torch.addmm(bias_d, Xs[i % NB], Wt.t(), out=Yd), it)
+        if bias_d is not None:
+            ms_torch = timeit(lambda i: torch.addmm(bias_d, Xs[i % NB], Wt.t(), out=Yd), it)
+        else:
+            ms_torch = timeit(lambda i: torch.matmul(Xs[i % NB], Wt.t(), out=Yd), it)
         best = min(ms_ref, ms_torch)
         dense = {"dyra_dense_ref_ms": round(ms_ref, 5), "torch_matmul_ms": round(ms_torch, 5),
                  "dense_gflop": round(2 * w.n * w.c1 * w.c2 / 1e9, 1),
