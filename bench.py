@@ -76,6 +76,7 @@ def STRUCT_TEXT(w):
 
 
 OUTPUT_KERNEL = {0: "s6_lowrank_kernel (fused T V + L R_b + bias)",
+                 "0bf16": "s6_lowrank_ws_kernel (persistent, wave-specialised T V + L R_b + bias)",
                  1: "s6_monarch_kernel (stage 2 + L R_b + bias)",
                  2: "s6_blast_kernel (W'_j V_j^T + L R_b + bias)"}
 
@@ -229,7 +230,7 @@ def main():
                     "unit": "TFLOP/s"}
         roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
         roof["traffic"] = traffic
-        roof["kernel"] = OUTPUT_KERNEL[w.kind]
+        roof["kernel"] = OUTPUT_KERNEL["0bf16" if (w.kind == 0 and w.dtype == synth.DT_BF16) else w.kind]
         roof["mfma_frac"] = round(fl / t6 / 1e12 / PEAK_BF16_TFLOPS, 4)
 
     # dense comparators on the same shape: library MFMA GEMM and torch.matmul (hipBLASLt)

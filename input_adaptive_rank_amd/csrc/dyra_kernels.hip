@@ -17,10 +17,12 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <type_traits>
 
 #include "../../include/dyra.h"
 #include "device_common.h"
 #include "gemm_engine.h"
+#include "lds_dma.h"
 #include "spec.h"
 
 using namespace dyra_spec_util;
@@ -158,6 +160,262 @@ __global__ __launch_bounds__(C::NT, WPE) void s6_lowrank_kernel(const typename C
   stage_out<C>(lds, acc, bias ? bias + n0 : nullptr, (int)(c2 - n0));
   copy_out<C, STREAM>(lds, reinterpret_cast<char*>(Y) + (m0 * c2 + n0) * E, c2 * E,
               (int)imin64(C::BM, n - m0), (c2 - n0) * E);
+}
+
+// ---------------------------------------------------------------------------
+// S6 (low-rank, bf16), persistent and wave-specialised.
+//
+// One workgroup per CU walks a contiguous range of BM x BN output tiles of
+// its XCD (workgroups are dispatched round-robin over the 8 XCDs, so the
+// tiles an XCD works on at a time share their T|L rows and V^T / R_b rows in
+// its L2).  The k-tiles of consecutive tiles (nk0 of [T|V], then nkr per
+// segment the tile overlaps) form one stream that flows through an NS-slot
+// LDS ring:
+//   * NL loader waves issue LDS-DMA loads NS - 1 k-tiles ahead and wait on
+//     them (vmcnt);
+//   * the compute waves run the MFMAs and the epilogue stores and never wait
+//     on vmcnt.  On gfx9 vmcnt counts loads and stores in one queue, so a
+//     wave that both stored Y and waited for its next operands would wait
+//     for its 256 KB of streaming stores first.
+// One barrier per k-tile hands a landed slot to the compute waves and the
+// slot they finished back to the loaders.  Each slot carries the tile's bias
+// in a 256-byte tail; the first MFMA of a tile takes it as its addend, so the
+// epilogue only converts, stages 32 rows per wave in that wave's part of the
+// consumed slot, and writes whole 128-byte lines non-temporally.
+// ---------------------------------------------------------------------------
+template <class C, int NS, int NL, bool HAS_BIAS>
+__global__ __launch_bounds__(C::NT + NL * 64, 1) void s6_lowrank_ws_kernel(
+    const bf16_t* __restrict__ TL, const bf16_t* __restrict__ Vt, const bf16_t* __restrict__ Rt,
+    const bf16_t* __restrict__ bias, bf16_t* __restrict__ Y, int n, int c2, int k, int r, int seg, int B,
+    int tiles_n, int tiles) {
+  static_assert(NS >= 2 && NS <= 4, "ring depth");
+  static_assert(NL % 2 == 0 && (C::BM / 8) % NL == 0 && (C::BN / 8) % NL == 0, "loader blocks");
+  constexpr int NWC = C::NT / 64;                            // compute waves
+  constexpr int LA = C::BM / 8 / NL, LB = C::BN / 8 / NL;    // 1 KB blocks per loader per k-tile
+  constexpr int PTL = LA + LB + 1;                           // DMAs per loader lane per k-tile
+  constexpr int TAIL = 256;
+  static_assert(C::BN * 2 == TAIL, "bias tail: one 4-byte DMA lane per column pair");
+  constexpr int SLOT = C::STAGE + TAIL;
+  constexpr int RING = NS * SLOT;
+  constexpr int WAREA = C::STAGE / NWC;                      // per-wave staging area
+  constexpr int RB = C::WN * 2;                              // staged row bytes
+  static_assert(RB == 128 && WAREA >= 32 * RB, "per-wave staging of 32 rows of 128 bytes");
+  __shared__ __attribute__((aligned(1024))) char ring[RING];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = lane & 31, gq = lane >> 5;
+  const int lda = (k + r) * 2, kE = k * 2, rE = r * 2, ldr = B * rE;
+  const int nk0 = (kE + 127) >> 7, nkr = (rE + 127) >> 7;
+  const int G8 = gridDim.x >> 3, xcd = blockIdx.x & 7, lw = blockIdx.x >> 3;
+  const int chunk = (tiles + 7) >> 3;
+  const int hi_tile = min(tiles, (xcd + 1) * chunk);
+  auto open = [&](int t, int& m0, int& n0, int& tot, int& b0) {
+    const int tm = t / tiles_n;
+    m0 = tm * C::BM;
+    n0 = (t - tm * tiles_n) * C::BN;
+    b0 = m0 / seg;
+    const int bl = min(B - 1, (min(m0 + C::BM, n) - 1) / seg);
+    tot = nk0 + (bl - b0 + 1) * nkr;
+  };
+  int ct = xcd * chunk + lw, ckt = 0, ctot = 0, cm0 = 0, cn0 = 0, cb0 = 0;
+  bool live = ct < hi_tile;
+  if (live) open(ct, cm0, cn0, ctot, cb0);
+  if (w >= NWC) {
+    // ------------------------------ loaders ------------------------------
+    const int q = w - NWC;
+    const uint32_t ring_s = lds_addr(ring);
+    // loader q fills 8-row blocks q + j NL of each operand: lane L loads row
+    // 8 (q + j NL) + L / 8 at 16-byte chunk (L % 8) ^ ((row / 2) % 8) (the
+    // lds_off swizzle), which is the same chunk for every j as NL is even
+    const int row0 = q * 8 + (lane >> 3);
+    const int ch16 = ((lane & 7) ^ ((row0 >> 1) & 7)) << 4;
+    const int a_v = row0 * lda + ch16, v_v = row0 * kE + ch16, r_v = row0 * ldr + ch16;
+    int it = ct, ikt = 0, itot = ctot, im0 = cm0, in0 = cn0, ib = cb0, ikr = 0;
+    auto issue = [&](uint32_t slot) {
+      const uint32_t la = ring_s + slot;
+      const bool live_i = it < hi_tile;
+      const char* abase;
+      const char* bbase;
+      int kb, kbytes, alo, ahi, b_v, bld;
+      if (ikt < nk0) {   // [T | V] part
+        kb = ikt << 7; kbytes = kE;
+        abase = reinterpret_cast<const char*>(TL) + (int64_t)im0 * lda;
+        bbase = reinterpret_cast<const char*>(Vt) + (int64_t)in0 * kE;
+        alo = -im0; ahi = n - im0; b_v = v_v; bld = kE;
+      } else {           // [L_b | R_b] part of segment ib
+        kb = ikr << 7; kbytes = rE;
+        abase = reinterpret_cast<const char*>(TL) + (int64_t)im0 * lda + kE;
+        bbase = reinterpret_cast<const char*>(Rt) + (int64_t)ib * rE + (int64_t)in0 * ldr;
+        alo = ib * seg - im0; ahi = min((ib + 1) * seg, n) - im0; b_v = r_v; bld = ldr;
+      }
+      // past the last tile every lane reads out of range: the DMA count (and
+      // with it every wait) stays the same at each step
+      const bool fullk = kb + 128 <= kbytes;
+      const bool afast = live_i && fullk && alo <= 0 && ahi >= C::BM;
+      const bool bfast = live_i && fullk && in0 + C::BN <= c2;
+      const bool kok = ch16 < kbytes - kb;
+      const i32x4v ars = rsrc_words(abase, 0x7fffffffu), brs = rsrc_words(bbase, 0x7fffffffu);
+#pragma unroll
+      for (int j = 0; j < LA; ++j) {
+        const int jr = j * NL * 8;
+        int v = a_v;
+        if (!afast) v = live_i && kok && row0 + jr >= alo && row0 + jr < ahi ? a_v : (int)0x80000000u;
+        dma16(ars, v, jr * lda + kb, la + (q + j * NL) * 1024);
+      }
+#pragma unroll
+      for (int j = 0; j < LB; ++j) {
+        const int jr = j * NL * 8;
+        int v = b_v;
+        if (!bfast) v = live_i && kok && in0 + row0 + jr < c2 ? b_v : (int)0x80000000u;
+        dma16(brs, v, jr * bld + kb, la + C::BM * 128 + (q + j * NL) * 1024);
+      }
+      // the tile's bias into the slot tail (every loader writes the same bytes)
+      const i32x4v rsb = rsrc_words(bias + in0, HAS_BIAS && live_i ? (uint32_t)(c2 - in0) * 2u : 0u);
+      dma4(rsb, lane * 4, 0, la + C::STAGE);
+      if (live_i) {
+        ++ikt;
+        if (ikt > nk0 && ++ikr == nkr) { ikr = 0; ++ib; }
+        if (ikt == itot) {
+          it += G8; ikt = 0; ikr = 0;
+          if (it < hi_tile) open(it, im0, in0, itot, ib);
+        }
+      }
+    };
+    uint32_t slot_i = 0;
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s) {
+      issue(slot_i);
+      slot_i += SLOT;
+    }
+    while (live) {
+      wait_vm_lgkm0<(NS - 2) * PTL>();   // this loader's part of k-tile t has landed
+      bare_barrier();                     // ... everyone's; slot t - 1 is free again
+      issue(slot_i);
+      slot_i = slot_i + SLOT == RING ? 0u : slot_i + SLOT;
+      if (++ckt == ctot) {
+        bare_barrier();                   // the compute waves' epilogue barrier
+        ct += G8;
+        ckt = 0;
+        live = ct < hi_tile;
+        if (live) open(ct, cm0, cn0, ctot, cb0);
+      }
+    }
+    wait_vm_lgkm0<0>();                   // no DMA may still be writing LDS at exit
+    return;
+  }
+  // ------------------------------- compute -------------------------------
+  const int wm = w / C::NWN, wn = w % C::NWN;
+  const int h = (l >> 1) & 7;
+  f32x16 acc[C::FM][C::FN];
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[fm][fn][v] = 0.f;
+  // acc (+)= one k-tile of the slot.  Lane (l, g) reads chunk 2 ks + g of
+  // rows l + 32 f, whose swizzled position depends on l only; substep ks + 1
+  // is read while ks runs.  FIRST: the first MFMA of each block adds the bias
+  // tuple instead of acc.
+  auto compute = [&](const char* stage, auto first, const f32x16 (&cinit)[C::FN]) {
+    constexpr bool FIRST = decltype(first)::value;
+    const char* as = stage + (wm * C::WM + l) * 128;
+    const char* bs = stage + C::BM * 128 + (wn * C::WN + l) * 128;
+    uint4 af[2][C::FM], bfr[2][C::FN];
+    auto load = [&](int ks, int buf) {
+      const int co = (((2 * ks + gq) ^ h) & 7) << 4;
+#pragma unroll
+      for (int fm = 0; fm < C::FM; ++fm) af[buf][fm] = *reinterpret_cast<const uint4*>(as + fm * 4096 + co);
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn) bfr[buf][fn] = *reinterpret_cast<const uint4*>(bs + fn * 4096 + co);
+    };
+    load(0, 0);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      if (ks + 1 < 4) load(ks + 1, (ks + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn)
+          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8_t, bfr[ks & 1][fn]), __builtin_bit_cast(bf16x8_t, af[ks & 1][fm]),
+              (FIRST && ks == 0) ? cinit[fn] : acc[fm][fn], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  uint32_t slot_c = 0;
+  while (live) {
+    wait_lgkm0();
+    bare_barrier();
+    const char* stage = ring + slot_c;
+    if (HAS_BIAS && ckt == 0) {
+      f32x16 cinit[C::FN];
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const uint2 b2 = *reinterpret_cast<const uint2*>(stage + C::STAGE + (wn * C::WN + fn * 32 + 8 * qq + 4 * gq) * 2);
+          cinit[fn][4 * qq + 0] = __uint_as_float(b2.x << 16);
+          cinit[fn][4 * qq + 1] = __uint_as_float(b2.x & 0xffff0000u);
+          cinit[fn][4 * qq + 2] = __uint_as_float(b2.y << 16);
+          cinit[fn][4 * qq + 3] = __uint_as_float(b2.y & 0xffff0000u);
+        }
+      compute(stage, std::true_type(), cinit);
+    } else {
+      compute(stage, std::false_type(), acc[0]);
+    }
+    if (++ckt == ctot) {
+      char* st = ring + slot_c;
+      const int rows_valid = min(C::BM, n - cm0);
+      const int colbytes = min(C::BN * 2, (c2 - cn0) * 2);
+      const __amdgpu_buffer_rsrc_t yrs = __builtin_amdgcn_make_buffer_rsrc(
+          reinterpret_cast<char*>(Y) + ((int64_t)cm0 * c2 + cn0) * 2, (short)0, 0x7fffffff, 0x00020000);
+      const int ldy = c2 * 2;
+      wait_lgkm0();
+      bare_barrier();                     // every compute wave is done reading slot t
+      char* wa = st + w * WAREA;
+#pragma unroll
+      for (int fm = 0; fm < C::FM; ++fm) {
+        // rows l of this 32-row block: chunk c of row l at ((c ^ l) % 8)
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) {
+            const int col = fn * 32 + 8 * qq + 4 * gq;
+            uint2 pk;
+            pk.x = pack_bf16x2(acc[fm][fn][4 * qq + 0], acc[fm][fn][4 * qq + 1]);
+            pk.y = pack_bf16x2(acc[fm][fn][4 * qq + 2], acc[fm][fn][4 * qq + 3]);
+            *reinterpret_cast<uint2*>(wa + l * RB + (((col >> 3) ^ (l & 7)) & 7) * 16 + (col & 4) * 2) = pk;
+          }
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int i = 0; i < 32 * 8 / 64; ++i) {
+          const int c = lane + i * 64;
+          const int rr = c >> 3, ch = c & 7;
+          const uint4 v = *reinterpret_cast<const uint4*>(wa + rr * RB + ((ch ^ (rr & 7)) & 7) * 16);
+          const int row = wm * C::WM + fm * 32 + rr;
+          const bool ok = row < rows_valid && wn * C::WN * 2 + ch * 16 < colbytes;
+          const int off = ok ? row * ldy + wn * C::WN * 2 + ch * 16 : (int)0x80000000u;
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4v, v), yrs, off, 0, 2);   // nt
+        }
+        __builtin_amdgcn_wave_barrier();
+      }
+      if constexpr (!HAS_BIAS) {
+#pragma unroll
+        for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+          for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[fm][fn][v] = 0.f;
+      }
+      ct += G8;
+      ckt = 0;
+      live = ct < hi_tile;
+      if (live) open(ct, cm0, cn0, ctot, cb0);
+    }
+    slot_c = slot_c + SLOT == RING ? 0u : slot_c + SLOT;
+  }
 }
 
 // ===========================================================================
@@ -1277,6 +1535,47 @@ typedef GemmCfg<float, 64, 64, 2, 2> CfgF3;     // S3, fp32
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// 256 x 128 tiles: 4 compute waves of 128 x 64, 4 loaders, 3-slot ring (148 KB)
+typedef GemmCfg<bf16_t, 256, 128, 2, 2> CfgB6W;
+constexpr int S6W_NS = 3, S6W_NL = 4;
+
+// Whether the persistent S6 applies: every 32-bit offset it forms stays in range.
+bool s6_ws_fits(int64_t n, int64_t c2, int k, int r, int64_t B) {
+  const int64_t lda = (int64_t)(k + r) * 2, ldr = B * r * 2, ldy = c2 * 2;
+  const int64_t tiles = cdiv(n, CfgB6W::BM) * cdiv(c2, CfgB6W::BN);
+  return n < ((int64_t)1 << 30) && lda * CfgB6W::BM < ((int64_t)1 << 30) && ldr * CfgB6W::BN < ((int64_t)1 << 30) &&
+         ldy * CfgB6W::BM < ((int64_t)1 << 30) && tiles < ((int64_t)1 << 30);
+}
+
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cus[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cus[dev] = v;
+  }
+  return cus[dev];
+}
+
+void launch_s6_ws(const bf16_t* TL, const bf16_t* Vt, const bf16_t* Rt, const bf16_t* bias, bf16_t* Y, int64_t n,
+                  int64_t c2, int k, int r, int64_t seg, int64_t B, hipStream_t st) {
+  typedef CfgB6W C;
+  const int tiles_n = (int)cdiv(c2, C::BN);
+  const int tiles = (int)(cdiv(n, C::BM) * tiles_n);
+  const int cus = device_cus();
+  // a multiple of 8 workgroups (one per CU): the tile ranges are per XCD
+  const int grid = cus >= 16 ? (cus / 8) * 8 : 8;
+  if (bias)
+    hipLaunchKernelGGL((s6_lowrank_ws_kernel<C, S6W_NS, S6W_NL, true>), dim3(grid), dim3(C::NT + S6W_NL * 64), 0, st,
+                       TL, Vt, Rt, bias, Y, (int)n, (int)c2, k, r, (int)seg, (int)B, tiles_n, tiles);
+  else
+    hipLaunchKernelGGL((s6_lowrank_ws_kernel<C, S6W_NS, S6W_NL, false>), dim3(grid), dim3(C::NT + S6W_NL * 64), 0, st,
+                       TL, Vt, Rt, bias, Y, (int)n, (int)c2, k, r, (int)seg, (int)B, tiles_n, tiles);
+}
+
+
 // C[M x N] (+)= A[M x K] B[N x K]^T (+ bias) for `batch` problems whose
 // operands are `sA/sB/sC` elements apart.
 template <class C>
@@ -1462,9 +1761,14 @@ int forward_lowrank(const dyra_spec& s, const char* plan, const void* X, const v
     const int tiles_n = (int)cdiv(c2, C6::BN);
     const int64_t tiles = cdiv(n, C6::BM) * tiles_n;
     constexpr bool BF = TT<T>::ESZ == 2;
-    hipLaunchKernelGGL((s6_lowrank_kernel<C6, BF, true, BF ? S6_WPE : 1, BF>), dim3((unsigned)tiles), dim3(C6::NT), 0, st, TL,
-                       reinterpret_cast<const T*>(plan + PL.Vt), Rt, reinterpret_cast<const T*>(bias),
-                       reinterpret_cast<T*>(Y), n, c2, k, r, seg, B, tiles_n);
+    if (BF && s6_ws_fits(n, c2, k, r, B) && device_cus() >= 8)
+      launch_s6_ws(reinterpret_cast<const bf16_t*>(TL), reinterpret_cast<const bf16_t*>(plan + PL.Vt),
+                   reinterpret_cast<const bf16_t*>(Rt), reinterpret_cast<const bf16_t*>(bias),
+                   reinterpret_cast<bf16_t*>(Y), n, c2, k, r, seg, B, st);
+    else
+      hipLaunchKernelGGL((s6_lowrank_kernel<C6, BF, true, BF ? S6_WPE : 1, BF>), dim3((unsigned)tiles), dim3(C6::NT), 0,
+                         st, TL, reinterpret_cast<const T*>(plan + PL.Vt), Rt, reinterpret_cast<const T*>(bias),
+                         reinterpret_cast<T*>(Y), n, c2, k, r, seg, B, tiles_n);
   }
   E.mark(5, st);
   return hipGetLastError() == hipSuccess ? DYRA_OK : DYRA_EHIP;
