@@ -1673,7 +1673,14 @@ void forward_residual(const dyra_spec& s, const char* plan, const void* X, int64
   hipLaunchKernelGGL(apply_inverse_kernel<T>, dim3((unsigned)(cdiv(c1, 64) * B)), dim3(256),
                      (size_t)(r * (r + 4) + r * 64) * 4, st, Gi, M, Mp, r, c1);
   E.mark(3, st);
-  // S5: R^T (c2 x B r) = W_res^T (c2 x c1) . M' (B r x c1)^T
+  // S5: R^T (c2 x B r) = W_res^T (c2 x c1) . M' (B r x c1)^T; bf16: the
+  // persistent output kernel with one segment, no residual part and no bias
+  if constexpr (BF) {
+    if (s6_ws_fits(c2, B * r, (int)c1, 0, 1) && device_cus() >= 8) {
+      launch_s6_ws(Wrt, Mp, nullptr, nullptr, Rt, c2, B * r, (int)c1, 0, c2, 1, st);
+      return;
+    }
+  }
   launch_gemm_tn<C>(Wrt, c1, Mp, c1, Rt, B * r, c2, B * r, c1, nullptr, st);
 }
 

@@ -34,6 +34,12 @@ SMALL = [
     sc(W["vitl_fc1"], name="r128_ns", B=2, s=300, c1=256, c2=384, k=64, r=128, solver="ns"),
     # k + r = 320: the 160 x 320 first-stage tile, ragged in rows
     sc(W["vitl_fc1"], name="wide_first_stage_tile", B=3, s=150, c1=384, c2=384, k=256, r=64),
+    # bf16 without bias: the persistent output kernel's zero-addend variant
+    sc(W["vitb_fc1"], name="ragged_bf16_nobias", B=3, s=77, c1=192, c2=200, k=24, r=16, bias=False),
+    # about 4.5 output tiles per persistent workgroup, a segment boundary inside tiles
+    sc(W["vitl_fc1"], name="persistent_several_tiles", B=10, s=900, c1=256, c2=4096, k=64, r=32),
+    sc(W["vitl_fc1"], name="persistent_several_tiles_nobias", B=10, s=900, c1=256, c2=4096, k=64, r=32,
+       bias=False),
 ]
 
 
