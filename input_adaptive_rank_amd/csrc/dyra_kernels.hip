@@ -1245,7 +1245,8 @@ template <int NRB, int NB>
 __global__ __launch_bounds__(S3_NT, NRB <= 4 ? 2 : 1) void s3_reduce_solve_kernel(
     const bf16_t* __restrict__ Lt, int64_t ldt, const bf16_t* __restrict__ X, int64_t c1, int r, int64_t seg,
     int64_t n, int64_t B, float* __restrict__ M, float* __restrict__ G, float* __restrict__ Gi,
-    int32_t* __restrict__ status, float eps, int do_sweep, int strips, int64_t lt_seg_rows, int x_rel) {
+    int32_t* __restrict__ status, float eps, int do_sweep, int strips, int64_t lt_seg_rows, int x_rel,
+    const float* __restrict__ gpart, int gchunks) {
   __shared__ __attribute__((aligned(16))) char lds[S3Lds<NB>::BYTES];
   SweepLds* sl = reinterpret_cast<SweepLds*>(lds + S3Lds<NB>::SW_OFF);
   const int64_t bid = blockIdx.x;
@@ -1264,7 +1265,44 @@ __global__ __launch_bounds__(S3_NT, NRB <= 4 ? 2 : 1) void s3_reduce_solve_kerne
     int64_t tbase;
     seg_ptrs(b, lo, Ltb, Xb, tbase);
     float* Gs = reinterpret_cast<float*>(lds + S3Lds<NB>::G_OFF);
-    s3_gram<NB>(Ltb, ldt, r, lo, hi, Gs, lds, tbase);
+    if (gpart) {
+      // G_b = sum of the segment's chunk partials, in chunk order
+      // (float4 columns; up to 8 chunks of loads in flight per thread)
+      const float* gp = gpart + b * gchunks * r * r;
+      const int nq = r * r / 4;   // r % 8 == 0
+      for (int e0 = threadIdx.x; e0 < nq; e0 += 4 * S3_NT) {
+        float4 acc[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int c0 = 0; c0 < gchunks; c0 += 8) {
+          float4 v[8][4];
+#pragma unroll
+          for (int c = 0; c < 8; ++c)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int e = e0 + i * S3_NT;
+              v[c][i] = (c0 + c < gchunks && e < nq)
+                            ? reinterpret_cast<const float4*>(gp + (int64_t)(c0 + c) * r * r)[e]
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+#pragma unroll
+          for (int c = 0; c < 8; ++c)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              acc[i].x += v[c][i].x;
+              acc[i].y += v[c][i].y;
+              acc[i].z += v[c][i].z;
+              acc[i].w += v[c][i].w;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (e0 + i * S3_NT < nq) reinterpret_cast<float4*>(Gs)[e0 + i * S3_NT] = acc[i];
+      }
+      __syncthreads();
+    } else {
+      s3_gram<NB>(Ltb, ldt, r, lo, hi, Gs, lds, tbase);
+    }
     // publish G (the Newton-Schulz path and diagnostics read it)
     for (int e = threadIdx.x; e < r * r; e += S3_NT) G[b * r * r + e] = Gs[e];
     if (do_sweep) {
@@ -1283,6 +1321,69 @@ __global__ __launch_bounds__(S3_NT, NRB <= 4 ? 2 : 1) void s3_reduce_solve_kerne
   int64_t tbase;
   seg_ptrs(b, lo, Ltb, Xb, tbase);
   s3_m_strip<NRB>(Ltb, ldt, Xb, c1, r, lo, hi, c0, M + b * r * c1, lds, tbase);
+}
+
+// Gram partials over token chunks: workgroup (b, c) writes
+// sum_{t in chunk c of segment b} L_t^T L_t, so the solve role of the token
+// reduction only adds a few r x r partials before its sweep instead of
+// streaming the segment's L^T itself (which put the Gram's load latency on the
+// critical path of that launch).
+template <int NB>
+__global__ __launch_bounds__(64) void gram_partial_kernel(const bf16_t* __restrict__ Lt, int64_t ldt, int r,
+                                                          int64_t seg, int64_t n, int gchunks, int64_t gchunk,
+                                                          float* __restrict__ Gp) {
+  // one wave per chunk: every token step's L^T loads are issued before the
+  // MFMAs, and the 32 x 32 blocks go from the accumulators straight to memory
+  constexpr int MAXST = 16;   // gchunk <= 256 tokens = 16 steps of 16
+  const int lane = threadIdx.x, l = lane & 31, g = lane >> 5;
+  const int64_t b = blockIdx.x / gchunks, c = blockIdx.x % gchunks;
+  const int64_t lo = b * seg + c * gchunk;
+  const int64_t hi = imin64(imin64(lo + gchunk, (b + 1) * seg), n);
+  f32x16 acc[NB][NB];
+#pragma unroll
+  for (int a = 0; a < NB; ++a)
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[a][bb][v] = 0.f;
+  const int64_t a0 = lo & ~(int64_t)7;
+  const int nsteps = lo < hi ? (int)((hi - a0 + 15) / 16) : 0;
+  for (int st0 = 0; st0 < nsteps; st0 += MAXST / NB) {
+    constexpr int PF = MAXST / NB;
+    uint4 f[PF][NB];
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+      const int64_t t0 = a0 + 16 * (int64_t)(st0 + u) + 8 * g;
+      const bool in = st0 + u < nsteps;
+#pragma unroll
+      for (int rb = 0; rb < NB; ++rb) {
+        const int row = rb * 32 + l;
+        const uint4 v = (in && row < r && t0 < ldt) ? *reinterpret_cast<const uint4*>(Lt + row * ldt + t0) : zero4();
+        f[u][rb] = mask_tokens<bf16_t>(v, t0, lo, hi);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < PF; ++u)
+#pragma unroll
+      for (int a = 0; a < NB; ++a)
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb)
+          acc[a][bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, f[u][a]),
+                                                               __builtin_bit_cast(bf16x8_t, f[u][bb]), acc[a][bb],
+                                                               0, 0, 0);
+  }
+  // accumulator element v of lane (l, g) in block (a, bb) is
+  // G[a 32 + 8 (v / 4) + 4 g + v % 4][bb 32 + l]
+  float* out = Gp + (int64_t)blockIdx.x * r * r;
+#pragma unroll
+  for (int a = 0; a < NB; ++a)
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int i = a * 32 + (v >> 2) * 8 + g * 4 + (v & 3), jj = bb * 32 + l;
+        if (i < r && jj < r) out[i * r + jj] = acc[a][bb][v];
+      }
 }
 
 // S4a as its own launch: one 256-thread workgroup per segment.  With
@@ -1612,10 +1713,15 @@ struct StageEvents {
 template <int NRB, int NB>
 void launch_s3_bf16(const bf16_t* Lt, int64_t ldt, const bf16_t* X, int64_t c1, int r, int64_t seg, int64_t n,
                     int64_t B, float* M, float* G, float* Gi, int32_t* stat, float eps, bool sweep,
-                    hipStream_t st, int64_t lt_seg_rows = 0, bool x_rel = false) {
+                    hipStream_t st, int64_t lt_seg_rows = 0, bool x_rel = false, float* gpart = nullptr,
+                    int gchunks = 0, int64_t gchunk = 0) {
   const int strips = (int)cdiv(c1, S3_STRIP);
+  if (gpart)   // Gram partials first (absolute L^T addressing only)
+    hipLaunchKernelGGL((gram_partial_kernel<NB>), dim3((unsigned)(B * gchunks)), dim3(64), 0, st, Lt, ldt, r,
+                       seg, n, gchunks, gchunk, gpart);
   hipLaunchKernelGGL((s3_reduce_solve_kernel<NRB, NB>), dim3((unsigned)(B + B * strips)), dim3(S3_NT), 0, st, Lt,
-                     ldt, X, c1, r, seg, n, B, M, G, Gi, stat, eps, sweep ? 1 : 0, strips, lt_seg_rows, x_rel ? 1 : 0);
+                     ldt, X, c1, r, seg, n, B, M, G, Gi, stat, eps, sweep ? 1 : 0, strips, lt_seg_rows, x_rel ? 1 : 0,
+                     gpart, gchunks);
 }
 
 // S3, S4 and S5, shared by every structure: M_b, G_b, Ginv_b, M'_b and
@@ -1648,10 +1754,13 @@ void forward_residual(const dyra_spec& s, const char* plan, const void* X, int64
   bool solved = false;
   if constexpr (BF) {
     const bf16_t* Xb = reinterpret_cast<const bf16_t*>(X);
-    if (r <= 16) launch_s3_bf16<1, 1>(Lt, ldt, Xb, c1, r, seg, n, B, M, G, Gi, stat, eps, !ns, st);
-    else if (r <= 32) launch_s3_bf16<2, 1>(Lt, ldt, Xb, c1, r, seg, n, B, M, G, Gi, stat, eps, !ns, st);
-    else if (r <= 64) launch_s3_bf16<4, 2>(Lt, ldt, Xb, c1, r, seg, n, B, M, G, Gi, stat, eps, !ns, st);
-    else launch_s3_bf16<8, 4>(Lt, ldt, Xb, c1, r, seg, n, B, M, G, Gi, stat, eps, !ns, st);
+    float* Gp = reinterpret_cast<float*>(ws + WL.Gp);
+    const int gc = (int)WL.gchunks;
+    const int64_t gk = WL.gchunk;
+    if (r <= 16) launch_s3_bf16<1, 1>(Lt, ldt, Xb, c1, r, seg, n, B, M, G, Gi, stat, eps, !ns, st, 0, false, Gp, gc, gk);
+    else if (r <= 32) launch_s3_bf16<2, 1>(Lt, ldt, Xb, c1, r, seg, n, B, M, G, Gi, stat, eps, !ns, st, 0, false, Gp, gc, gk);
+    else if (r <= 64) launch_s3_bf16<4, 2>(Lt, ldt, Xb, c1, r, seg, n, B, M, G, Gi, stat, eps, !ns, st, 0, false, Gp, gc, gk);
+    else launch_s3_bf16<8, 4>(Lt, ldt, Xb, c1, r, seg, n, B, M, G, Gi, stat, eps, !ns, st, 0, false, Gp, gc, gk);
     solved = !ns;
   } else {
     const int tr = (int)cdiv(r, C3::BM), tcm = (int)cdiv(c1, C3::BN), tcg = (int)cdiv(r, C3::BN);

@@ -108,6 +108,9 @@ inline PlanLayout plan_layout(const dyra_spec& s, int dtype) {
 struct WsLayout {
   int64_t wa = 0;
   size_t A = 0, Wp = 0, Lt = 0, G = 0, M = 0, Ginv = 0, Mp = 0, Rt = 0, status = 0;
+  // Gram partials [B][gchunks][r x r] fp32 over token chunks of gchunk tokens
+  size_t Gp = 0;
+  int64_t gchunk = 0, gchunks = 0;
   // left ALS steps (half_steps > 2): R [B r x c2], K and Kinv [B x r x r]
   // fp32, Q^T [B x r x c1] fp32, Z^T [B x r x c1], their status words [B]
   size_t R = 0, K = 0, Kinv = 0, Qt = 0, Zt = 0, kstatus = 0;
@@ -138,6 +141,9 @@ inline WsLayout ws_layout(const dyra_spec& s, int64_t B, int64_t seg, int dtype,
   W.Mp = take((size_t)B * r * c1 * e);
   W.Rt = take(c2 * (size_t)B * r * e);
   W.status = take((size_t)B * 4);
+  W.gchunk = s.r > 64 ? 256 : 128;
+  W.gchunks = (seg + W.gchunk - 1) / W.gchunk;
+  W.Gp = take((size_t)B * (size_t)W.gchunks * r * r * 4);
   if (half_steps > 2) {
     W.R = take((size_t)B * r * c2 * e);
     W.K = take((size_t)B * r * r * 4);
