@@ -209,17 +209,45 @@ __global__ __launch_bounds__(C::NT + NL * 64, 1) void s6_lowrank_ws_kernel(
   const int G8 = gridDim.x >> 3, xcd = blockIdx.x & 7, lw = blockIdx.x >> 3;
   const int chunk = (tiles + 7) >> 3;
   const int hi_tile = min(tiles, (xcd + 1) * chunk);
-  auto open = [&](int t, int& m0, int& n0, int& tot, int& b0) {
-    const int tm = t / tiles_n;
-    m0 = tm * C::BM;
-    n0 = (t - tm * tiles_n) * C::BN;
-    b0 = m0 / seg;
-    const int bl = min(B - 1, (min(m0 + C::BM, n) - 1) / seg);
-    tot = nk0 + (bl - b0 + 1) * nkr;
+  // Tile cursors advance by G8 tiles without integer division: the row and
+  // column steps are precomputed, and the first and last segment of the
+  // tile's rows move forward with the rows.
+  const int dtm = G8 / tiles_n, dtn = G8 - dtm * tiles_n;
+  struct Cur {
+    int t, tm, tn, m0, n0, b0, bl, tot;
   };
-  int ct = xcd * chunk + lw, ckt = 0, ctot = 0, cm0 = 0, cn0 = 0, cb0 = 0;
-  bool live = ct < hi_tile;
-  if (live) open(ct, cm0, cn0, ctot, cb0);
+  auto settle = [&](Cur& c) {   // segments, k-tile count of the tile at (tm, tn)
+    c.m0 = c.tm * C::BM;
+    c.n0 = c.tn * C::BN;
+    while ((c.b0 + 1) * seg <= c.m0) ++c.b0;
+    const int last = min(c.m0 + C::BM, n) - 1;
+    if (c.bl < c.b0) c.bl = c.b0;
+    while (c.bl + 1 < B && (c.bl + 1) * seg <= last) ++c.bl;
+    c.tot = nk0 + (c.bl - c.b0 + 1) * nkr;
+  };
+  auto start = [&](Cur& c, int t) {
+    c.t = t;
+    c.tm = t / tiles_n;
+    c.tn = t - c.tm * tiles_n;
+    c.b0 = 0;
+    c.bl = 0;
+    if (t < hi_tile) {
+      c.b0 = (c.tm * C::BM) / seg;
+      c.bl = c.b0;
+      settle(c);
+    }
+  };
+  auto advance = [&](Cur& c) {
+    c.t += G8;
+    c.tm += dtm;
+    c.tn += dtn;
+    if (c.tn >= tiles_n) { c.tn -= tiles_n; ++c.tm; }
+    if (c.t < hi_tile) settle(c);
+  };
+  Cur cc;
+  start(cc, xcd * chunk + lw);
+  int ckt = 0;
+  bool live = cc.t < hi_tile;
   if (w >= NWC) {
     // ------------------------------ loaders ------------------------------
     const int q = w - NWC;
@@ -230,10 +258,12 @@ __global__ __launch_bounds__(C::NT + NL * 64, 1) void s6_lowrank_ws_kernel(
     const int row0 = q * 8 + (lane >> 3);
     const int ch16 = ((lane & 7) ^ ((row0 >> 1) & 7)) << 4;
     const int a_v = row0 * lda + ch16, v_v = row0 * kE + ch16, r_v = row0 * ldr + ch16;
-    int it = ct, ikt = 0, itot = ctot, im0 = cm0, in0 = cn0, ib = cb0, ikr = 0;
+    Cur ic = cc;
+    int ikt = 0, ib = cc.b0, ikr = 0;
     auto issue = [&](uint32_t slot) {
       const uint32_t la = ring_s + slot;
-      const bool live_i = it < hi_tile;
+      const bool live_i = ic.t < hi_tile;
+      const int im0 = ic.m0, in0 = ic.n0;
       const char* abase;
       const char* bbase;
       int kb, kbytes, alo, ahi, b_v, bld;
@@ -255,19 +285,28 @@ __global__ __launch_bounds__(C::NT + NL * 64, 1) void s6_lowrank_ws_kernel(
       const bool bfast = live_i && fullk && in0 + C::BN <= c2;
       const bool kok = ch16 < kbytes - kb;
       const i32x4v ars = rsrc_words(abase, 0x7fffffffu), brs = rsrc_words(bbase, 0x7fffffffu);
+      // interior tiles take the branch without any per-lane test
+      if (afast) {
 #pragma unroll
-      for (int j = 0; j < LA; ++j) {
-        const int jr = j * NL * 8;
-        int v = a_v;
-        if (!afast) v = live_i && kok && row0 + jr >= alo && row0 + jr < ahi ? a_v : (int)0x80000000u;
-        dma16(ars, v, jr * lda + kb, la + (q + j * NL) * 1024);
+        for (int j = 0; j < LA; ++j) dma16(ars, a_v, j * NL * 8 * lda + kb, la + (q + j * NL) * 1024);
+      } else {
+#pragma unroll
+        for (int j = 0; j < LA; ++j) {
+          const int jr = j * NL * 8;
+          const int v = live_i && kok && row0 + jr >= alo && row0 + jr < ahi ? a_v : (int)0x80000000u;
+          dma16(ars, v, jr * lda + kb, la + (q + j * NL) * 1024);
+        }
       }
+      if (bfast) {
 #pragma unroll
-      for (int j = 0; j < LB; ++j) {
-        const int jr = j * NL * 8;
-        int v = b_v;
-        if (!bfast) v = live_i && kok && in0 + row0 + jr < c2 ? b_v : (int)0x80000000u;
-        dma16(brs, v, jr * bld + kb, la + C::BM * 128 + (q + j * NL) * 1024);
+        for (int j = 0; j < LB; ++j) dma16(brs, b_v, j * NL * 8 * bld + kb, la + C::BM * 128 + (q + j * NL) * 1024);
+      } else {
+#pragma unroll
+        for (int j = 0; j < LB; ++j) {
+          const int jr = j * NL * 8;
+          const int v = live_i && kok && in0 + row0 + jr < c2 ? b_v : (int)0x80000000u;
+          dma16(brs, v, jr * bld + kb, la + C::BM * 128 + (q + j * NL) * 1024);
+        }
       }
       // the tile's bias into the slot tail (every loader writes the same bytes)
       const i32x4v rsb = rsrc_words(bias + in0, HAS_BIAS && live_i ? (uint32_t)(c2 - in0) * 2u : 0u);
@@ -275,9 +314,9 @@ __global__ __launch_bounds__(C::NT + NL * 64, 1) void s6_lowrank_ws_kernel(
       if (live_i) {
         ++ikt;
         if (ikt > nk0 && ++ikr == nkr) { ikr = 0; ++ib; }
-        if (ikt == itot) {
-          it += G8; ikt = 0; ikr = 0;
-          if (it < hi_tile) open(it, im0, in0, itot, ib);
+        if (ikt == ic.tot) {
+          advance(ic);
+          ikt = 0; ikr = 0; ib = ic.b0;
         }
       }
     };
@@ -292,12 +331,11 @@ __global__ __launch_bounds__(C::NT + NL * 64, 1) void s6_lowrank_ws_kernel(
       bare_barrier();                     // ... everyone's; slot t - 1 is free again
       issue(slot_i);
       slot_i = slot_i + SLOT == RING ? 0u : slot_i + SLOT;
-      if (++ckt == ctot) {
+      if (++ckt == cc.tot) {
         bare_barrier();                   // the compute waves' epilogue barrier
-        ct += G8;
+        advance(cc);
         ckt = 0;
-        live = ct < hi_tile;
-        if (live) open(ct, cm0, cn0, ctot, cb0);
+        live = cc.t < hi_tile;
       }
     }
     wait_vm_lgkm0<0>();                   // no DMA may still be writing LDS at exit
@@ -365,12 +403,12 @@ __global__ __launch_bounds__(C::NT + NL * 64, 1) void s6_lowrank_ws_kernel(
     } else {
       compute(stage, std::false_type(), acc[0]);
     }
-    if (++ckt == ctot) {
+    if (++ckt == cc.tot) {
       char* st = ring + slot_c;
-      const int rows_valid = min(C::BM, n - cm0);
-      const int colbytes = min(C::BN * 2, (c2 - cn0) * 2);
+      const int rows_valid = min(C::BM, n - cc.m0);
+      const int colbytes = min(C::BN * 2, (c2 - cc.n0) * 2);
       const __amdgpu_buffer_rsrc_t yrs = __builtin_amdgcn_make_buffer_rsrc(
-          reinterpret_cast<char*>(Y) + ((int64_t)cm0 * c2 + cn0) * 2, (short)0, 0x7fffffff, 0x00020000);
+          reinterpret_cast<char*>(Y) + ((int64_t)cc.m0 * c2 + cc.n0) * 2, (short)0, 0x7fffffff, 0x00020000);
       const int ldy = c2 * 2;
       wait_lgkm0();
       bare_barrier();                     // every compute wave is done reading slot t
@@ -409,10 +447,9 @@ __global__ __launch_bounds__(C::NT + NL * 64, 1) void s6_lowrank_ws_kernel(
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[fm][fn][v] = 0.f;
       }
-      ct += G8;
+      advance(cc);
       ckt = 0;
-      live = ct < hi_tile;
-      if (live) open(ct, cm0, cn0, ctot, cb0);
+      live = cc.t < hi_tile;
     }
     slot_c = slot_c + SLOT == RING ? 0u : slot_c + SLOT;
   }
