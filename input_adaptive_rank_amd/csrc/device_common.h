@@ -52,9 +52,18 @@ template <> struct TT<float> {
 // the window (row parity picks the half, row / 2 the slot).
 __device__ __forceinline__ int lds_off(int row, int chunk) { return row * 128 + (((chunk ^ (row >> 1)) & 7) << 4); }
 
-// Output staging tiles: rows of CPR chunks (CPR a multiple of 8); the low
-// three bits of the chunk index are XOR-swizzled with the row.
-__device__ __forceinline__ int stage_chunk(int row, int chunk) { return (chunk & ~7) | ((chunk ^ row) & 7); }
+// Output staging tiles: rows of CPR 16-byte chunks (CPR a multiple of 8).
+// The epilogue writes 8 bytes per lane with lanes l = 0..31 on rows l, so the
+// swizzle spreads consecutive rows over the 256-byte bank window: with CPR a
+// multiple of 16 every row starts at the same window offset and the chunk is
+// XORed with row % 16 (16 slots, 2-way at 64 lanes); otherwise rows alternate
+// window halves and the low three bits are XORed with row / 2.
+template <int CPR>
+__device__ __forceinline__ int stage_chunk(int row, int chunk) {
+  static_assert(CPR % 8 == 0, "staging rows are whole 128-byte groups");
+  if constexpr (CPR % 16 == 0) return chunk ^ (row & 15);
+  else return (chunk & ~7) | ((chunk ^ (row >> 1)) & 7);
+}
 
 // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
 // L2).  Renumber so that consecutive tile ids run on the same XCD and share

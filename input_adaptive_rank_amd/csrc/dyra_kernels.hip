@@ -415,7 +415,8 @@ __global__ __launch_bounds__(C::NT + NL * 64, 1) void s6_lowrank_ws_kernel(
       char* wa = st + w * WAREA;
 #pragma unroll
       for (int fm = 0; fm < C::FM; ++fm) {
-        // rows l of this 32-row block: chunk c of row l at ((c ^ l) % 8)
+        // rows l of this 32-row block: chunk c of row l at ((c ^ l / 2) % 8),
+        // which spreads the 8-byte writes of the 32 rows over the bank window
 #pragma unroll
         for (int fn = 0; fn < C::FN; ++fn)
 #pragma unroll
@@ -424,14 +425,14 @@ __global__ __launch_bounds__(C::NT + NL * 64, 1) void s6_lowrank_ws_kernel(
             uint2 pk;
             pk.x = pack_bf16x2(acc[fm][fn][4 * qq + 0], acc[fm][fn][4 * qq + 1]);
             pk.y = pack_bf16x2(acc[fm][fn][4 * qq + 2], acc[fm][fn][4 * qq + 3]);
-            *reinterpret_cast<uint2*>(wa + l * RB + (((col >> 3) ^ (l & 7)) & 7) * 16 + (col & 4) * 2) = pk;
+            *reinterpret_cast<uint2*>(wa + l * RB + (((col >> 3) ^ (l >> 1)) & 7) * 16 + (col & 4) * 2) = pk;
           }
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int i = 0; i < 32 * 8 / 64; ++i) {
           const int c = lane + i * 64;
           const int rr = c >> 3, ch = c & 7;
-          const uint4 v = *reinterpret_cast<const uint4*>(wa + rr * RB + ((ch ^ (rr & 7)) & 7) * 16);
+          const uint4 v = *reinterpret_cast<const uint4*>(wa + rr * RB + ((ch ^ (rr >> 1)) & 7) * 16);
           const int row = wm * C::WM + fm * 32 + rr;
           const bool ok = row < rows_valid && wn * C::WN * 2 + ch * 16 < colbytes;
           const int off = ok ? row * ldy + wn * C::WN * 2 + ch * 16 : (int)0x80000000u;

@@ -297,10 +297,10 @@ __device__ __forceinline__ void stage_out(char* lds, const f32x16 (&acc)[C::FM][
           pk.x = (uint32_t)f2bf(v0) | ((uint32_t)f2bf(v1) << 16);
           pk.y = (uint32_t)f2bf(v2) | ((uint32_t)f2bf(v3) << 16);
           const int chunk = col >> 3;
-          *reinterpret_cast<uint2*>(rowp + stage_chunk(row, chunk) * 16 + (col & 4) * 2) = pk;
+          *reinterpret_cast<uint2*>(rowp + stage_chunk<C::CPR>(row, chunk) * 16 + (col & 4) * 2) = pk;
         } else {
           const int chunk = col >> 2;
-          *reinterpret_cast<float4*>(rowp + stage_chunk(row, chunk) * 16) = make_float4(v0, v1, v2, v3);
+          *reinterpret_cast<float4*>(rowp + stage_chunk<C::CPR>(row, chunk) * 16) = make_float4(v0, v1, v2, v3);
         }
       }
     }
@@ -323,7 +323,7 @@ __device__ __forceinline__ void copy_out(const char* lds, char* dst, int64_t ldb
   for (int c = threadIdx.x; c < C::BM * C::CPR; c += C::NT) {
     const int row = c / C::CPR, ch = c % C::CPR;
     if (row < rows_valid && (int64_t)ch * 16 < colbytes_valid) {
-      const uint4 v = *reinterpret_cast<const uint4*>(lds + row * (C::CPR * 16) + stage_chunk(row, ch) * 16);
+      const uint4 v = *reinterpret_cast<const uint4*>(lds + row * (C::CPR * 16) + stage_chunk<C::CPR>(row, ch) * 16);
       char* p = dst + row * ldb + ch * 16;
       if constexpr (STREAM) __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4*>(p));
       else *reinterpret_cast<uint4*>(p) = v;
@@ -336,5 +336,5 @@ template <class C>
 __device__ __forceinline__ typename C::elem staged_elem(const char* lds, int row, int col) {
   typedef typename C::elem T;
   const int byte = col * TT<T>::ESZ;
-  return *reinterpret_cast<const T*>(lds + row * (C::CPR * 16) + stage_chunk(row, byte >> 4) * 16 + (byte & 15));
+  return *reinterpret_cast<const T*>(lds + row * (C::CPR * 16) + stage_chunk<C::CPR>(row, byte >> 4) * 16 + (byte & 15));
 }
