@@ -114,6 +114,157 @@ __global__ __launch_bounds__(C::NT, WPE) void s1_lowrank_kernel(const typename C
   }
 }
 
+// ---------------------------------------------------------------------------
+// S1 (bf16, k + r = 320): [T | L] = X [U | P] and L^T, one 160 x 320 tile
+// per workgroup (a single round of row blocks on 256 CUs; X is read once).
+// Eight symmetric waves (two per SIMD) each compute 80 x 80 of the tile as
+// 5 x 5 blocks of 16x16x32 MFMAs (5 + 5 fragments per 25 MFMAs), fed by a
+// 4-slot ring of 32-wide k-tiles that every wave fills with LDS-DMA loads
+// three k-tiles ahead.  Nothing is stored before the last k-tile, so a
+// wave's wait for its part of a slot is a plain vmcnt count.  The barrier
+// that publishes k-tile t + 1 comes before the MFMAs of k-tile t (whose
+// fragments are already in registers), so the next fragments are read while
+// they run.  The epilogue stages the tile in the ring and writes whole rows
+// of [T | L] and whole token runs of L^T.
+// ---------------------------------------------------------------------------
+constexpr int S1T_BM = 160, S1T_BN = 320, S1T_BK = 32;
+__global__ __launch_bounds__(512, 1) void s1_tile_kernel(const bf16_t* __restrict__ X,
+                                                         const bf16_t* __restrict__ UPt, bf16_t* __restrict__ A,
+                                                         bf16_t* __restrict__ Lt, int n, int c1, int k, int r,
+                                                         int64_t ldt) {
+  constexpr int BM = S1T_BM, BN = S1T_BN, RBY = S1T_BK * 2;   // 64-byte k-tile rows
+  constexpr int NS = 4, NW = 8, FB = 5;                       // ring slots, waves, 16-blocks per wave side
+  constexpr int ABLK = BM * RBY / 1024, BBLK = BN * RBY / 1024;   // 10 + 20 one-KB blocks
+  constexpr int SLOT_BLK = 32, SLOT = SLOT_BLK * 1024;        // + 2 zero-filled pads
+  constexpr int D = SLOT_BLK / NW;                            // DMAs per wave per k-tile
+  constexpr int SP = BN * 2 + 16;                             // staged row pitch (bytes)
+  static_assert(ABLK + BBLK <= SLOT_BLK && SLOT_BLK % NW == 0 && 3 * D < 64, "slot");
+  static_assert(BM * SP <= NS * SLOT, "staging fits the ring");
+  static_assert(2 * FB * 16 == BM && 4 * FB * 16 == BN, "2 x 4 waves of 80 x 80");
+  __shared__ __attribute__((aligned(1024))) char ring[NS * SLOT];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = w >> 2, wn = w & 3;
+  const int l16 = lane & 15, kg = lane >> 4;
+  const int m0 = blockIdx.x * BM;
+  const int rows = min(BM, n - m0);
+  const int nkt = c1 / S1T_BK;                                // c1 % 64 == 0: nkt even
+  const int ldx = c1 * 2;                                     // bytes per X / UPt row
+  const uint32_t ring_s = lds_addr(ring);
+  // Slot block b < ABLK holds X rows 16 b .. 16 b + 15, block ABLK + b UPt
+  // rows 16 b ..; the rest are pads.  Lane L of a block writes row 16 b + L / 4
+  // at physical chunk L % 4, which holds logical chunk (L % 4) ^ ((row / 4) % 4).
+  const i32x4v xrs = rsrc_words(reinterpret_cast<const char*>(X) + (int64_t)m0 * ldx, (uint32_t)rows * ldx);
+  const i32x4v urs = rsrc_words(UPt, (uint32_t)BN * ldx);
+  const i32x4v zrs = rsrc_words(UPt, 0u);
+  const int brow = lane >> 2, pc = lane & 3;
+  int voff[D];
+#pragma unroll
+  for (int j = 0; j < D; ++j) {
+    const int blk = w * D + j;
+    const int row = (blk < ABLK ? blk : blk - ABLK) * 16 + brow;
+    voff[j] = row * ldx + (pc ^ ((row >> 2) & 3)) * 16;
+  }
+  // this wave's descriptors, chosen once (in SGPRs)
+  i32x4v drs[D];
+#pragma unroll
+  for (int j = 0; j < D; ++j) {
+    const int blk = w * D + j;
+    drs[j] = blk >= ABLK + BBLK ? zrs : blk < ABLK ? xrs : urs;
+    drs[j].x = __builtin_amdgcn_readfirstlane(drs[j].x);
+    drs[j].y = __builtin_amdgcn_readfirstlane(drs[j].y);
+    drs[j].z = __builtin_amdgcn_readfirstlane(drs[j].z);
+    drs[j].w = __builtin_amdgcn_readfirstlane(drs[j].w);
+  }
+  // k-tiles past the end read at an offset past every descriptor's records
+  auto issue = [&](int kt, int slot) {
+    const int soff = kt < nkt ? kt * RBY : 0x7fff0000;
+    const uint32_t la = ring_s + slot * SLOT + w * D * 1024;
+#pragma unroll
+    for (int j = 0; j < D; ++j) dma16(drs[j], voff[j], soff, la + j * 1024);
+  };
+  // fragments: block f of this wave's rows (A) or columns (B), lane (l16, kg):
+  // row 16 f + l16 at logical chunk kg
+  uint4 af[2][FB], bfr[2][FB];
+  auto load_frags = [&](int slot, int buf) {
+    const char* st = ring + slot * SLOT;
+#pragma unroll
+    for (int f = 0; f < FB; ++f) {
+      const int ra = wm * 80 + f * 16 + l16, rb = wn * 80 + f * 16 + l16;
+      af[buf][f] = *reinterpret_cast<const uint4*>(st + ra * RBY + ((kg ^ ((ra >> 2) & 3)) << 4));
+      bfr[buf][f] = *reinterpret_cast<const uint4*>(st + ABLK * 1024 + rb * RBY + ((kg ^ ((rb >> 2) & 3)) << 4));
+    }
+  };
+  f32x4 acc[FB][FB];
+#pragma unroll
+  for (int a = 0; a < FB; ++a)
+#pragma unroll
+    for (int b = 0; b < FB; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s0 = 0; s0 < NS; ++s0) issue(s0, s0);
+  wait_vm_lgkm0<3 * D>();                 // k-tile 0 (three slots were issued after it)
+  bare_barrier();
+  load_frags(0, 0);
+  // two k-tiles per trip: fragment buffers 0 and 1 alternate statically
+  auto step = [&](int kt, auto cur) {
+    constexpr int C = decltype(cur)::value, NX = 1 - C;
+    wait_vm_lgkm0<2 * D>();               // this wave's part of k-tile kt + 1; fragments of kt
+    bare_barrier();                       // k-tile kt + 1 everywhere; slot kt is read
+    issue(kt + NS, kt & (NS - 1));
+    if (kt + 1 < nkt) load_frags((kt + 1) & (NS - 1), NX);
+    __builtin_amdgcn_sched_barrier(0);
+    // lane (l16, kg) of block (a, b) receives row 16 a + l16, columns
+    // 16 b + 4 kg .. + 3 (the B fragment is the first operand)
+#pragma unroll
+    for (int a = 0; a < FB; ++a)
+#pragma unroll
+      for (int b = 0; b < FB; ++b)
+        acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, bfr[C][b]),
+                                                            __builtin_bit_cast(bf16x8_t, af[C][a]), acc[a][b], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  for (int kt = 0; kt < nkt; kt += 2) {
+    step(kt, std::integral_constant<int, 0>());
+    step(kt + 1, std::integral_constant<int, 1>());
+  }
+  wait_vm_lgkm0<0>();                     // the trailing zero-fill loads too
+  bare_barrier();
+  // stage the tile (bf16, row pitch SP)
+#pragma unroll
+  for (int a = 0; a < FB; ++a)
+#pragma unroll
+    for (int b = 0; b < FB; ++b) {
+      const int row = wm * 80 + a * 16 + l16, col = wn * 80 + b * 16 + 4 * kg;
+      uint2 pk;
+      pk.x = pack_bf16x2(acc[a][b][0], acc[a][b][1]);
+      pk.y = pack_bf16x2(acc[a][b][2], acc[a][b][3]);
+      *reinterpret_cast<uint2*>(ring + row * SP + col * 2) = pk;
+    }
+  __syncthreads();
+  // [T | L] rows: 40 chunks of 16 bytes each
+  for (int q = tid; q < BM * (BN / 8); q += NW * 64) {
+    const int row = q / (BN / 8), c = q - row * (BN / 8);
+    if (row >= rows) break;
+    const uint4 v = *reinterpret_cast<const uint4*>(ring + row * SP + c * 16);
+    *reinterpret_cast<uint4*>(A + (int64_t)(m0 + row) * BN + c * 8) = v;
+  }
+  // L^T: row j holds tokens m0 .. m0 + 159 (tokens past n hold zeros: their
+  // X rows were read as zeros) in runs of 8
+  for (int q = tid; q < r * (BM / 8); q += NW * 64) {
+    const int j = q / (BM / 8), t8 = (q - j * (BM / 8)) * 8;
+    if (m0 + t8 >= ldt) continue;
+    uint32_t h[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) h[e] = *reinterpret_cast<const uint16_t*>(ring + (t8 + e) * SP + (k + j) * 2);
+    uint4 v;
+    v.x = h[0] | (h[1] << 16);
+    v.y = h[2] | (h[3] << 16);
+    v.z = h[4] | (h[5] << 16);
+    v.w = h[6] | (h[7] << 16);
+    *reinterpret_cast<uint4*>(Lt + (int64_t)j * ldt + m0 + t8) = v;
+  }
+}
+
 // ===========================================================================
 // S6 (low-rank): Y = T V + L R_b + bias, segments handled by row masks
 // ===========================================================================
@@ -1895,7 +2046,13 @@ int forward_lowrank(const dyra_spec& s, const char* plan, const void* X, const v
     // ViT-L sizes, more tiles than two per CU: one 160 x 320 tile per row
     // block instead (a single round, X read once per row block)
     if constexpr (TT<T>::ESZ == 2) {
-      if (k + r > 256 && k + r <= 320) launch(CfgB1W());
+      if (k + r == S1T_BN && c1 % (2 * S1T_BK) == 0 && (int64_t)S1T_BN * c1 * 2 < ((int64_t)1 << 31) &&
+          (int64_t)S1T_BM * c1 * 2 < ((int64_t)1 << 31))
+        hipLaunchKernelGGL(s1_tile_kernel, dim3((unsigned)cdiv(n, S1T_BM)), dim3(512), 0, st,
+                           reinterpret_cast<const bf16_t*>(X), reinterpret_cast<const bf16_t*>(plan + PL.UPt),
+                           reinterpret_cast<bf16_t*>(TL), reinterpret_cast<bf16_t*>(Lt), (int)n, (int)c1, k, r,
+                           lt_pitch(n));
+      else if (k + r > 256 && k + r <= 320) launch(CfgB1W());
       else launch(C());
     } else {
       launch(C());

@@ -40,6 +40,12 @@ SMALL = [
     sc(W["vitl_fc1"], name="persistent_several_tiles", B=10, s=900, c1=256, c2=4096, k=64, r=32),
     sc(W["vitl_fc1"], name="persistent_several_tiles_nobias", B=10, s=900, c1=256, c2=4096, k=64, r=32,
        bias=False),
+    # r = 64, k = 256 / 128, long segments: several 256 x 128 output tiles per
+    # persistent workgroup with segment boundaries inside tiles and a ragged
+    # last row block (with and without bias); then ragged columns (c2 = 1000)
+    sc(W["vitl_fc1"], name="a_stationary_k256", B=7, s=1029, c1=512, c2=4096, k=256, r=64),
+    sc(W["vitl_fc1"], name="a_stationary_k128_nobias", B=9, s=700, c1=256, c2=4096, k=128, r=64, bias=False),
+    sc(W["vitl_fc1"], name="a_stationary_ragged_cols", B=2, s=600, c1=384, c2=1000, k=256, r=64),
 ]
 
 
