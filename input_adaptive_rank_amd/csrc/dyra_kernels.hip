@@ -248,20 +248,20 @@ __global__ __launch_bounds__(512, 1) void s1_tile_kernel(const bf16_t* __restric
     const uint4 v = *reinterpret_cast<const uint4*>(ring + row * SP + c * 16);
     *reinterpret_cast<uint4*>(A + (int64_t)(m0 + row) * BN + c * 8) = v;
   }
-  // L^T: row j holds tokens m0 .. m0 + 159 (tokens past n hold zeros: their
-  // X rows were read as zeros) in runs of 8
-  for (int q = tid; q < r * (BM / 8); q += NW * 64) {
-    const int j = q / (BM / 8), t8 = (q - j * (BM / 8)) * 8;
-    if (m0 + t8 >= ldt) continue;
-    uint32_t h[8];
+  // L^T (tokens past n hold zeros: their X rows were read as zeros), in
+  // 8 x 8 blocks: 8 token rows of 8 L columns read as 16-byte chunks, an
+  // in-register transpose, 8 runs of 8 tokens.  Neighbouring lanes take
+  // neighbouring column blocks (distinct banks); the 8 lanes of one column
+  // block write a 128-byte run of each L^T row.
+  for (int q = tid; q < (BM / 8) * (r / 8); q += NW * 64) {
+    const int j8 = (q % (r / 8)) * 8, tt = (q / (r / 8)) * 8;
+    if (m0 + tt >= ldt) continue;
+    uint4 in[8], out[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) h[e] = *reinterpret_cast<const uint16_t*>(ring + (t8 + e) * SP + (k + j) * 2);
-    uint4 v;
-    v.x = h[0] | (h[1] << 16);
-    v.y = h[2] | (h[3] << 16);
-    v.z = h[4] | (h[5] << 16);
-    v.w = h[6] | (h[7] << 16);
-    *reinterpret_cast<uint4*>(Lt + (int64_t)j * ldt + m0 + t8) = v;
+    for (int e = 0; e < 8; ++e) in[e] = *reinterpret_cast<const uint4*>(ring + (tt + e) * SP + (k + j8) * 2);
+    transpose8x8_b16(in, out);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) *reinterpret_cast<uint4*>(Lt + (int64_t)(j8 + c) * ldt + m0 + tt) = out[c];
   }
 }
 
