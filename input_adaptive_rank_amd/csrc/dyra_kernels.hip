@@ -114,6 +114,24 @@ __global__ __launch_bounds__(C::NT, WPE) void s1_lowrank_kernel(const typename C
   }
 }
 
+// Tokens of an 8-token run (t0 ..) outside [lo, hi) set to zero.
+template <typename T>
+__device__ __forceinline__ uint4 mask_tokens(uint4 v, int64_t t0, int64_t lo, int64_t hi) {
+  constexpr int KPC = TT<T>::KPC;
+  if (t0 >= lo && t0 + KPC <= hi) return v;
+  if (t0 + KPC <= lo || t0 >= hi) return zero4();
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int e = 0; e < KPC; ++e) {
+    const int64_t tt = t0 + e;
+    if (tt < lo || tt >= hi) {
+      if constexpr (KPC == 8) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+      else w[e] = 0u;
+    }
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // ---------------------------------------------------------------------------
 // S1 (bf16, k + r = 320): [T | L] = X [U | P] and L^T, one 160 x 320 tile
 // per workgroup (a single round of row blocks on 256 CUs; X is read once).
@@ -125,13 +143,17 @@ __global__ __launch_bounds__(C::NT, WPE) void s1_lowrank_kernel(const typename C
 // that publishes k-tile t + 1 comes before the MFMAs of k-tile t (whose
 // fragments are already in registers), so the next fragments are read while
 // they run.  The epilogue stages the tile in the ring and writes whole rows
-// of [T | L] and whole token runs of L^T.
+// of [T | L] and whole token runs of L^T.  With Gp (r = 32 or 64, segments of
+// at least 160 tokens) it also leaves the tile's Gram partials
+// L_t^T L_t, one per segment the tile meets (slot 0: the segment of its first
+// row, slot 1: the next one), at Gp[(tile * 2 + slot) r^2], which the token
+// reduction adds up instead of streaming L^T for the Gram once more.
 // ---------------------------------------------------------------------------
 constexpr int S1T_BM = 160, S1T_BN = 320, S1T_BK = 32;
 __global__ __launch_bounds__(512, 1) void s1_tile_kernel(const bf16_t* __restrict__ X,
                                                          const bf16_t* __restrict__ UPt, bf16_t* __restrict__ A,
                                                          bf16_t* __restrict__ Lt, int n, int c1, int k, int r,
-                                                         int64_t ldt) {
+                                                         int64_t ldt, float* __restrict__ Gp, int seg) {
   constexpr int BM = S1T_BM, BN = S1T_BN, RBY = S1T_BK * 2;   // 64-byte k-tile rows
   constexpr int NS = 4, NW = 8, FB = 5;                       // ring slots, waves, 16-blocks per wave side
   constexpr int ABLK = BM * RBY / 1024, BBLK = BN * RBY / 1024;   // 10 + 20 one-KB blocks
@@ -140,6 +162,9 @@ __global__ __launch_bounds__(512, 1) void s1_tile_kernel(const bf16_t* __restric
   constexpr int SP = BN * 2 + 16;                             // staged row pitch (bytes)
   static_assert(ABLK + BBLK <= SLOT_BLK && SLOT_BLK % NW == 0 && 3 * D < 64, "slot");
   static_assert(BM * SP <= NS * SLOT, "staging fits the ring");
+  constexpr int LTP = BM * 2 + 16;                            // L^T tile row pitch (bytes), 64 rows
+  constexpr int LT_OFF = BM * SP;                             // after the staged tile
+  static_assert(LT_OFF % 16 == 0 && LT_OFF + 64 * LTP <= NS * SLOT, "L^T tile fits the ring");
   static_assert(2 * FB * 16 == BM && 4 * FB * 16 == BN, "2 x 4 waves of 80 x 80");
   __shared__ __attribute__((aligned(1024))) char ring[NS * SLOT];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -262,7 +287,39 @@ __global__ __launch_bounds__(512, 1) void s1_tile_kernel(const bf16_t* __restric
     transpose8x8_b16(in, out);
 #pragma unroll
     for (int c = 0; c < 8; ++c) *reinterpret_cast<uint4*>(Lt + (int64_t)(j8 + c) * ldt + m0 + tt) = out[c];
+    if (Gp) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) *reinterpret_cast<uint4*>(ring + LT_OFF + (j8 + c) * LTP + tt * 2) = out[c];
+    }
   }
+  if (!Gp) return;
+  // Gram partials: waves 0 .. 3 take the first segment's tokens of the tile,
+  // waves 4 .. 7 the next segment's (if the tile reaches it); wave w & 3 one
+  // 32 x 32 block of the r x r partial
+  __syncthreads();
+  const int b0 = m0 / seg, bnd = (b0 + 1) * seg - m0;        // tile-local first token of segment b0 + 1
+  const int slot = w >> 2, blk = w & 3, nbr = r >> 5;
+  const int tlo = slot ? bnd : 0, thi = slot ? rows : min(bnd, rows);
+  if (blk >= nbr * nbr || tlo >= thi) return;
+  const int ib = blk / nbr, jb = blk - ib * nbr;
+  const int l = lane & 31, g = lane >> 5;
+  f32x16 gacc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) gacc[v] = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < BM / 16; ++ks) {
+    const int t0 = ks * 16 + 8 * g;
+    const uint4 fa = mask_tokens<bf16_t>(
+        *reinterpret_cast<const uint4*>(ring + LT_OFF + (ib * 32 + l) * LTP + t0 * 2), t0, tlo, thi);
+    const uint4 fb = mask_tokens<bf16_t>(
+        *reinterpret_cast<const uint4*>(ring + LT_OFF + (jb * 32 + l) * LTP + t0 * 2), t0, tlo, thi);
+    gacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fa), __builtin_bit_cast(bf16x8_t, fb),
+                                                   gacc, 0, 0, 0);
+  }
+  // element v of lane (l, g): G[ib 32 + 8 (v / 4) + 4 g + v % 4][jb 32 + l]
+  float* out = Gp + ((int64_t)blockIdx.x * 2 + slot) * r * r;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) out[(ib * 32 + (v >> 2) * 8 + g * 4 + (v & 3)) * r + jb * 32 + l] = gacc[v];
 }
 
 // ===========================================================================
@@ -891,23 +948,6 @@ __global__ __launch_bounds__(C::NT) void s6_blast_kernel(const bf16_t* Wp, int64
 // token-major, so its tiles are transposed on the way into LDS.
 // ===========================================================================
 
-template <typename T>
-__device__ __forceinline__ uint4 mask_tokens(uint4 v, int64_t t0, int64_t lo, int64_t hi) {
-  constexpr int KPC = TT<T>::KPC;
-  if (t0 >= lo && t0 + KPC <= hi) return v;
-  if (t0 + KPC <= lo || t0 >= hi) return zero4();
-  uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-  for (int e = 0; e < KPC; ++e) {
-    const int64_t tt = t0 + e;
-    if (tt < lo || tt >= hi) {
-      if constexpr (KPC == 8) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
-      else w[e] = 0u;
-    }
-  }
-  return make_uint4(w[0], w[1], w[2], w[3]);
-}
-
 template <class C>
 __global__ __launch_bounds__(C::NT) void s3_gram_kernel(const typename C::elem* Lt, int64_t ldt,
                                                         const typename C::elem* X, int64_t c1, int r,
@@ -1435,7 +1475,7 @@ __global__ __launch_bounds__(S3_NT, NRB <= 4 ? 2 : 1) void s3_reduce_solve_kerne
     const bf16_t* __restrict__ Lt, int64_t ldt, const bf16_t* __restrict__ X, int64_t c1, int r, int64_t seg,
     int64_t n, int64_t B, float* __restrict__ M, float* __restrict__ G, float* __restrict__ Gi,
     int32_t* __restrict__ status, float eps, int do_sweep, int strips, int64_t lt_seg_rows, int x_rel,
-    const float* __restrict__ gpart, int gchunks) {
+    const float* __restrict__ gpart, int gchunks, int64_t gprows) {
   __shared__ __attribute__((aligned(16))) char lds[S3Lds<NB>::BYTES];
   SweepLds* sl = reinterpret_cast<SweepLds*>(lds + S3Lds<NB>::SW_OFF);
   const int64_t bid = blockIdx.x;
@@ -1455,24 +1495,36 @@ __global__ __launch_bounds__(S3_NT, NRB <= 4 ? 2 : 1) void s3_reduce_solve_kerne
     seg_ptrs(b, lo, Ltb, Xb, tbase);
     float* Gs = reinterpret_cast<float*>(lds + S3Lds<NB>::G_OFF);
     if (gpart) {
-      // G_b = sum of the segment's chunk partials, in chunk order
-      // (float4 columns; up to 8 chunks of loads in flight per thread)
-      const float* gp = gpart + b * gchunks * r * r;
+      // G_b = sum of the segment's partials, in order (float4 columns; up to
+      // 8 partials' loads in flight per thread): gchunks token chunks of the
+      // segment, or (gprows > 0) the first stage's per-tile partials of the
+      // tiles of gprows tokens that the segment meets, in slot 1 of its first
+      // tile when that tile starts in the previous segment, else in slot 0
       const int nq = r * r / 4;   // r % 8 == 0
+      const int64_t rb_lo = gprows > 0 ? lo / gprows : 0;
+      const int nparts = gprows > 0 ? (int)((hi - 1) / gprows - rb_lo + 1) : gchunks;
+      auto part_ptr = [&](int p) -> const float4* {
+        int64_t idx;
+        if (gprows > 0) {
+          const int64_t rb = rb_lo + p;
+          idx = rb * 2 + ((p == 0 && lo > rb * gprows) ? 1 : 0);
+        } else {
+          idx = b * gchunks + p;
+        }
+        return reinterpret_cast<const float4*>(gpart + idx * r * r);
+      };
       for (int e0 = threadIdx.x; e0 < nq; e0 += 4 * S3_NT) {
         float4 acc[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int c0 = 0; c0 < gchunks; c0 += 8) {
+        for (int c0 = 0; c0 < nparts; c0 += 8) {
           float4 v[8][4];
 #pragma unroll
           for (int c = 0; c < 8; ++c)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int e = e0 + i * S3_NT;
-              v[c][i] = (c0 + c < gchunks && e < nq)
-                            ? reinterpret_cast<const float4*>(gp + (int64_t)(c0 + c) * r * r)[e]
-                            : make_float4(0.f, 0.f, 0.f, 0.f);
+              v[c][i] = (c0 + c < nparts && e < nq) ? part_ptr(c0 + c)[e] : make_float4(0.f, 0.f, 0.f, 0.f);
             }
 #pragma unroll
           for (int c = 0; c < 8; ++c)
@@ -1903,21 +1955,23 @@ template <int NRB, int NB>
 void launch_s3_bf16(const bf16_t* Lt, int64_t ldt, const bf16_t* X, int64_t c1, int r, int64_t seg, int64_t n,
                     int64_t B, float* M, float* G, float* Gi, int32_t* stat, float eps, bool sweep,
                     hipStream_t st, int64_t lt_seg_rows = 0, bool x_rel = false, float* gpart = nullptr,
-                    int gchunks = 0, int64_t gchunk = 0) {
+                    int gchunks = 0, int64_t gchunk = 0, int64_t gprows = 0) {
   const int strips = (int)cdiv(c1, S3_STRIP);
-  if (gpart)   // Gram partials first (absolute L^T addressing only)
+  if (gpart && gprows == 0)   // chunk Gram partials first (absolute L^T addressing only)
     hipLaunchKernelGGL((gram_partial_kernel<NB>), dim3((unsigned)(B * gchunks)), dim3(64), 0, st, Lt, ldt, r,
                        seg, n, gchunks, gchunk, gpart);
   hipLaunchKernelGGL((s3_reduce_solve_kernel<NRB, NB>), dim3((unsigned)(B + B * strips)), dim3(S3_NT), 0, st, Lt,
                      ldt, X, c1, r, seg, n, B, M, G, Gi, stat, eps, sweep ? 1 : 0, strips, lt_seg_rows, x_rel ? 1 : 0,
-                     gpart, gchunks);
+                     gpart, gchunks, gprows);
 }
 
 // S3, S4 and S5, shared by every structure: M_b, G_b, Ginv_b, M'_b and
 // R^T = W_res^T M'^T.  Needs L^T (Lt, pitch ldt) and X.
 template <class C, class C3>
+// gram_rows > 0: the first stage left Gram partials per tile of that many
+// tokens in the workspace (else the chunk Gram kernel computes them here).
 void forward_residual(const dyra_spec& s, const char* plan, const void* X, int64_t B, int64_t seg, float eps,
-                      int solver, char* ws, hipStream_t st, const StageEvents& E) {
+                      int solver, char* ws, hipStream_t st, const StageEvents& E, int64_t gram_rows = 0) {
   typedef typename C::elem T;
   constexpr bool BF = TT<T>::ESZ == 2;
   const int dtype = BF ? DYRA_BF16 : DYRA_F32;
@@ -1946,10 +2000,10 @@ void forward_residual(const dyra_spec& s, const char* plan, const void* X, int64
     float* Gp = reinterpret_cast<float*>(ws + WL.Gp);
     const int gc = (int)WL.gchunks;
     const int64_t gk = WL.gchunk;
-    if (r <= 16) launch_s3_bf16<1, 1>(Lt, ldt, Xb, c1, r, seg, n, B, M, G, Gi, stat, eps, !ns, st, 0, false, Gp, gc, gk);
-    else if (r <= 32) launch_s3_bf16<2, 1>(Lt, ldt, Xb, c1, r, seg, n, B, M, G, Gi, stat, eps, !ns, st, 0, false, Gp, gc, gk);
-    else if (r <= 64) launch_s3_bf16<4, 2>(Lt, ldt, Xb, c1, r, seg, n, B, M, G, Gi, stat, eps, !ns, st, 0, false, Gp, gc, gk);
-    else launch_s3_bf16<8, 4>(Lt, ldt, Xb, c1, r, seg, n, B, M, G, Gi, stat, eps, !ns, st, 0, false, Gp, gc, gk);
+    if (r <= 16) launch_s3_bf16<1, 1>(Lt, ldt, Xb, c1, r, seg, n, B, M, G, Gi, stat, eps, !ns, st, 0, false, Gp, gc, gk, gram_rows);
+    else if (r <= 32) launch_s3_bf16<2, 1>(Lt, ldt, Xb, c1, r, seg, n, B, M, G, Gi, stat, eps, !ns, st, 0, false, Gp, gc, gk, gram_rows);
+    else if (r <= 64) launch_s3_bf16<4, 2>(Lt, ldt, Xb, c1, r, seg, n, B, M, G, Gi, stat, eps, !ns, st, 0, false, Gp, gc, gk, gram_rows);
+    else launch_s3_bf16<8, 4>(Lt, ldt, Xb, c1, r, seg, n, B, M, G, Gi, stat, eps, !ns, st, 0, false, Gp, gc, gk, gram_rows);
     solved = !ns;
   } else {
     const int tr = (int)cdiv(r, C3::BM), tcm = (int)cdiv(c1, C3::BN), tcg = (int)cdiv(r, C3::BN);
@@ -2032,6 +2086,7 @@ int forward_lowrank(const dyra_spec& s, const char* plan, const void* X, const v
   T* TL = reinterpret_cast<T*>(ws + WL.A);
   T* Lt = reinterpret_cast<T*>(ws + WL.Lt);
   T* Rt = reinterpret_cast<T*>(ws + WL.Rt);
+  int64_t gram_rows = 0;
   E.mark(0, st);
   {  // S1: [T | L] = X [U | P], L^T
     auto launch = [&](auto cfg) {
@@ -2047,19 +2102,23 @@ int forward_lowrank(const dyra_spec& s, const char* plan, const void* X, const v
     // block instead (a single round, X read once per row block)
     if constexpr (TT<T>::ESZ == 2) {
       if (k + r == S1T_BN && c1 % (2 * S1T_BK) == 0 && (int64_t)S1T_BN * c1 * 2 < ((int64_t)1 << 31) &&
-          (int64_t)S1T_BM * c1 * 2 < ((int64_t)1 << 31))
+          (int64_t)S1T_BM * c1 * 2 < ((int64_t)1 << 31)) {
+        // Gram partials from the tile epilogue when a tile meets at most two
+        // segments and r fills whole 32 x 32 blocks
+        const bool gram = (r == 32 || r == 64) && seg >= S1T_BM;
+        if (gram) gram_rows = S1T_BM;
         hipLaunchKernelGGL(s1_tile_kernel, dim3((unsigned)cdiv(n, S1T_BM)), dim3(512), 0, st,
                            reinterpret_cast<const bf16_t*>(X), reinterpret_cast<const bf16_t*>(plan + PL.UPt),
                            reinterpret_cast<bf16_t*>(TL), reinterpret_cast<bf16_t*>(Lt), (int)n, (int)c1, k, r,
-                           lt_pitch(n));
-      else if (k + r > 256 && k + r <= 320) launch(CfgB1W());
+                           lt_pitch(n), gram ? reinterpret_cast<float*>(ws + WL.Gp) : nullptr, (int)seg);
+      } else if (k + r > 256 && k + r <= 320) launch(CfgB1W());
       else launch(C());
     } else {
       launch(C());
     }
   }
   E.mark(1, st);
-  forward_residual<C, C3>(s, plan, X, B, seg, eps, solver, ws, st, E);
+  forward_residual<C, C3>(s, plan, X, B, seg, eps, solver, ws, st, E, gram_rows);
   // further ALS half-steps: left (L from R), right (R from L), ...
   if constexpr (TT<T>::ESZ == 2) {
     for (int h = 2; h < half_steps; ++h) {

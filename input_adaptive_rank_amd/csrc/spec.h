@@ -2,6 +2,7 @@
 // packed device plan and of the forward workspace.
 #pragma once
 
+#include <algorithm>
 #include <cstddef>
 #include <cstdint>
 
@@ -143,7 +144,8 @@ inline WsLayout ws_layout(const dyra_spec& s, int64_t B, int64_t seg, int dtype,
   W.status = take((size_t)B * 4);
   W.gchunk = s.r > 64 ? 256 : 128;
   W.gchunks = (seg + W.gchunk - 1) / W.gchunk;
-  W.Gp = take((size_t)B * (size_t)W.gchunks * r * r * 4);
+  // token-chunk partials, or two per 160-token first-stage tile
+  W.Gp = take(std::max((size_t)B * (size_t)W.gchunks, ((n + 159) / 160) * 2) * r * r * 4);
   if (half_steps > 2) {
     W.R = take((size_t)B * r * c2 * e);
     W.K = take((size_t)B * r * r * 4);

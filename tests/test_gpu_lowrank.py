@@ -46,6 +46,9 @@ SMALL = [
     sc(W["vitl_fc1"], name="a_stationary_k256", B=7, s=1029, c1=512, c2=4096, k=256, r=64),
     sc(W["vitl_fc1"], name="a_stationary_k128_nobias", B=9, s=700, c1=256, c2=4096, k=128, r=64, bias=False),
     sc(W["vitl_fc1"], name="a_stationary_ragged_cols", B=2, s=600, c1=384, c2=1000, k=256, r=64),
+    # first-stage Gram partials: 170-token segments, so nearly every 160-row
+    # tile meets two segments (both partial slots in use)
+    sc(W["vitl_fc1"], name="first_stage_gram_short_segments", B=20, s=170, c1=384, c2=512, k=256, r=64),
 ]
 
 
