@@ -1487,8 +1487,30 @@ __global__ __launch_bounds__(S3_NT, NRB <= 4 ? 2 : 1) void s3_reduce_solve_kerne
     Xb = x_rel ? X - lo * c1 : X;
     tbase = lt_seg_rows ? lo : 0;
   };
-  if (bid < B) {
-    const int64_t b = bid;
+  // Roles: B solve workgroups, then B * strips strip workgroups.  Workgroups
+  // go to the 8 XCDs in turn (block id mod 8); when B is a multiple of 8,
+  // segment b's solve role and all its strips run on XCD b mod 8, so the
+  // strips of a segment share one L2 copy of its L^T rows instead of every
+  // XCD fetching every segment's rows from HBM.
+  int64_t b, strip;   // strip < 0: solve role
+  if ((B & 7) == 0) {
+    const int64_t x = bid & 7, j = bid >> 3, per = B >> 3;
+    if (j < per) {
+      b = x + 8 * j;
+      strip = -1;
+    } else {
+      const int64_t u = j - per;
+      b = x + 8 * (u / strips);
+      strip = u % strips;
+    }
+  } else if (bid < B) {
+    b = bid;
+    strip = -1;
+  } else {
+    b = (bid - B) / strips;
+    strip = (bid - B) % strips;
+  }
+  if (strip < 0) {
     const int64_t lo = b * seg, hi = imin64((b + 1) * seg, n);
     const bf16_t *Ltb, *Xb;
     int64_t tbase;
@@ -1554,9 +1576,7 @@ __global__ __launch_bounds__(S3_NT, NRB <= 4 ? 2 : 1) void s3_reduce_solve_kerne
     }
     return;
   }
-  const int64_t u = bid - B;
-  const int64_t b = u / strips;
-  const int64_t c0 = (u % strips) * S3_STRIP;
+  const int64_t c0 = strip * S3_STRIP;
   const int64_t lo = b * seg, hi = imin64((b + 1) * seg, n);
   const bf16_t *Ltb, *Xb;
   int64_t tbase;
