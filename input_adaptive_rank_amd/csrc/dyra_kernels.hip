@@ -466,65 +466,83 @@ __global__ __launch_bounds__(C::NT + NL * 64, 1) void s6_lowrank_ws_kernel(
     const int row0 = q * 8 + (lane >> 3);
     const int ch16 = ((lane & 7) ^ ((row0 >> 1) & 7)) << 4;
     const int a_v = row0 * lda + ch16, v_v = row0 * kE + ch16, r_v = row0 * ldr + ch16;
+    // Issue state: the k-tiles of a tile come in parts, [T | V] (nk0
+    // k-tiles) and then [L_b | R_b] per segment b the tile meets (nkr each);
+    // descriptors, row bounds and fast-path flags are set once per part, so
+    // a k-tile costs its DMAs and a k offset.  Block j of this loader sits
+    // j NL 8 rows below its block 0, an offset the scalar operand carries.
     Cur ic = cc;
-    int ikt = 0, ib = cc.b0, ikr = 0;
-    auto issue = [&](uint32_t slot) {
-      const uint32_t la = ring_s + slot;
-      const bool live_i = ic.t < hi_tile;
-      const int im0 = ic.m0, in0 = ic.n0;
-      const char* abase;
-      const char* bbase;
-      int kb, kbytes, alo, ahi, b_v, bld;
-      if (ikt < nk0) {   // [T | V] part
-        kb = ikt << 7; kbytes = kE;
-        abase = reinterpret_cast<const char*>(TL) + (int64_t)im0 * lda;
-        bbase = reinterpret_cast<const char*>(Vt) + (int64_t)in0 * kE;
-        alo = -im0; ahi = n - im0; b_v = v_v; bld = kE;
-      } else {           // [L_b | R_b] part of segment ib
-        kb = ikr << 7; kbytes = rE;
-        abase = reinterpret_cast<const char*>(TL) + (int64_t)im0 * lda + kE;
-        bbase = reinterpret_cast<const char*>(Rt) + (int64_t)ib * rE + (int64_t)in0 * ldr;
-        alo = ib * seg - im0; ahi = min((ib + 1) * seg, n) - im0; b_v = r_v; bld = ldr;
-      }
-      // past the last tile every lane reads out of range: the DMA count (and
-      // with it every wait) stays the same at each step
-      const bool fullk = kb + 128 <= kbytes;
-      const bool afast = live_i && fullk && alo <= 0 && ahi >= C::BM;
-      const bool bfast = live_i && fullk && in0 + C::BN <= c2;
-      const bool kok = ch16 < kbytes - kb;
-      const i32x4v ars = rsrc_words(abase, 0x7fffffffu), brs = rsrc_words(bbase, 0x7fffffffu);
-      // interior tiles take the branch without any per-lane test
-      if (afast) {
-#pragma unroll
-        for (int j = 0; j < LA; ++j) dma16(ars, a_v, j * NL * 8 * lda + kb, la + (q + j * NL) * 1024);
+    const int sA = NL * 8 * lda, sV = NL * 8 * kE, sR = NL * 8 * ldr;
+    const uint32_t lq0 = ring_s + q * 1024;   // this loader's block 0 in slot 0
+    int p_kind = 0, p_left = 0, p_kb = 0, p_kbytes = 0, p_alo = 0, p_ahi = 0, p_ib = 0;
+    int p_fa = 0, p_fb = 0, p_live = 0;   // ints, not bools: kept in registers
+    i32x4v p_ars, p_brs, p_rsb;
+    auto set_tv = [&]() __attribute__((always_inline)) {
+      p_live = ic.t < hi_tile ? 1 : 0;
+      p_kind = 0; p_left = nk0; p_kb = 0; p_kbytes = kE; p_ib = ic.b0;
+      p_ars = rsrc_words(reinterpret_cast<const char*>(TL) + (int64_t)ic.m0 * lda, 0x7fffffffu);
+      p_brs = rsrc_words(reinterpret_cast<const char*>(Vt) + (int64_t)ic.n0 * kE, 0x7fffffffu);
+      p_rsb = rsrc_words(bias + ic.n0, HAS_BIAS && p_live ? (uint32_t)(c2 - ic.n0) * 2u : 0u);
+      p_alo = -ic.m0; p_ahi = n - ic.m0;
+      p_fa = p_live && p_ahi >= C::BM ? 1 : 0;
+      p_fb = p_live && ic.n0 + C::BN <= c2 ? 1 : 0;
+    };
+    auto set_lr = [&](int ibx) __attribute__((always_inline)) {
+      p_kind = 1; p_left = nkr; p_kb = 0; p_kbytes = rE; p_ib = ibx;
+      p_ars = rsrc_words(reinterpret_cast<const char*>(TL) + (int64_t)ic.m0 * lda + kE, 0x7fffffffu);
+      p_brs = rsrc_words(reinterpret_cast<const char*>(Rt) + (int64_t)ibx * rE + (int64_t)ic.n0 * ldr, 0x7fffffffu);
+      p_alo = ibx * seg - ic.m0; p_ahi = min((ibx + 1) * seg, n) - ic.m0;
+      p_fa = p_live && p_alo <= 0 && p_ahi >= C::BM ? 1 : 0;
+    };
+    set_tv();
+    // one k-tile into the slot at byte offset `slot`; past the last tile
+    // every lane reads out of range, so the DMA count (and with it every
+    // wait) stays the same at each step
+    auto issue = [&](uint32_t slot) __attribute__((always_inline)) {
+      const uint32_t lb = lq0 + slot;
+      const bool fullk = p_kb + 128 <= p_kbytes;
+      const bool kok = ch16 < p_kbytes - p_kb;
+      // interior parts take the branch without any per-lane test
+      if (p_fa && fullk) {
+        static_for<0, LA>([&](auto jc) __attribute__((always_inline)) {
+          constexpr int j = decltype(jc)::value;
+          dma16k<j * NL * 1024>(p_ars, a_v, p_kb + j * sA, lb);
+        });
       } else {
-#pragma unroll
-        for (int j = 0; j < LA; ++j) {
-          const int jr = j * NL * 8;
-          const int v = live_i && kok && row0 + jr >= alo && row0 + jr < ahi ? a_v : (int)0x80000000u;
-          dma16(ars, v, jr * lda + kb, la + (q + j * NL) * 1024);
-        }
+        static_for<0, LA>([&](auto jc) __attribute__((always_inline)) {
+          constexpr int j = decltype(jc)::value;
+          const int rr = row0 + j * NL * 8;
+          const int v = p_live && kok && rr >= p_alo && rr < p_ahi ? a_v : (int)0x80000000u;
+          dma16k<j * NL * 1024>(p_ars, v, p_kb + j * sA, lb);
+        });
       }
-      if (bfast) {
-#pragma unroll
-        for (int j = 0; j < LB; ++j) dma16(brs, b_v, j * NL * 8 * bld + kb, la + C::BM * 128 + (q + j * NL) * 1024);
-      } else {
-#pragma unroll
-        for (int j = 0; j < LB; ++j) {
-          const int jr = j * NL * 8;
-          const int v = live_i && kok && in0 + row0 + jr < c2 ? b_v : (int)0x80000000u;
-          dma16(brs, v, jr * bld + kb, la + C::BM * 128 + (q + j * NL) * 1024);
+      auto bdmas = [&](int vb, int sb) __attribute__((always_inline)) {
+        if (p_fb && fullk) {
+          static_for<0, LB>([&](auto jc) __attribute__((always_inline)) {
+            constexpr int j = decltype(jc)::value;
+            dma16k<C::BM * 128 + j * NL * 1024>(p_brs, vb, p_kb + j * sb, lb);
+          });
+        } else {
+          static_for<0, LB>([&](auto jc) __attribute__((always_inline)) {
+            constexpr int j = decltype(jc)::value;
+            const int v = p_live && kok && ic.n0 + row0 + j * NL * 8 < c2 ? vb : (int)0x80000000u;
+            dma16k<C::BM * 128 + j * NL * 1024>(p_brs, v, p_kb + j * sb, lb);
+          });
         }
-      }
+      };
+      if (p_kind == 0) bdmas(v_v, sV);
+      else bdmas(r_v, sR);
       // the tile's bias into the slot tail (every loader writes the same bytes)
-      const i32x4v rsb = rsrc_words(bias + in0, HAS_BIAS && live_i ? (uint32_t)(c2 - in0) * 2u : 0u);
-      dma4(rsb, lane * 4, 0, la + C::STAGE);
-      if (live_i) {
-        ++ikt;
-        if (ikt > nk0 && ++ikr == nkr) { ikr = 0; ++ib; }
-        if (ikt == ic.tot) {
-          advance(ic);
-          ikt = 0; ikr = 0; ib = ic.b0;
+      dma4(p_rsb, lane * 4, 0, ring_s + slot + C::STAGE);
+      if (p_live) {
+        p_kb += 128;
+        if (--p_left == 0) {
+          if (p_kind == 0) set_lr(ic.b0);
+          else if (p_ib < ic.bl) set_lr(p_ib + 1);
+          else {
+            advance(ic);
+            set_tv();
+          }
         }
       }
     };

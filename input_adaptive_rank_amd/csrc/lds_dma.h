@@ -8,6 +8,8 @@
 // s_waitcnt vmcnt(N) in the issuing wave followed by a barrier.
 #pragma once
 
+#include <type_traits>
+
 #include "device_common.h"
 
 typedef int i32x4v __attribute__((ext_vector_type(4)));
@@ -37,6 +39,22 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 __device__ __forceinline__ void dma16(i32x4v rs, int voff, int soff, uint32_t la) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :: "s"(la), "v"(voff), "s"(rs), "s"(soff) : "memory");
+}
+// dma16 with the LDS address formed as lbase + IMM in M0 itself (one scalar
+// instruction per DMA, no SGPR for the sum).
+template <int IMM>
+__device__ __forceinline__ void dma16k(i32x4v rs, int voff, int soff, uint32_t lbase) {
+  asm volatile("s_add_u32 m0, %0, %4\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(lbase), "v"(voff), "s"(rs), "s"(soff), "n"(IMM) : "scc", "memory");
+}
+// Calls f(std::integral_constant<int, J>) for J = J0 .. N - 1 (compile-time
+// indices for dma16k).
+template <int J, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (J < N) {
+    f(std::integral_constant<int, J>());
+    static_for<J + 1, N>(f);
+  }
 }
 // 4 bytes per lane into LDS at la + 4 * lane.
 __device__ __forceinline__ void dma4(i32x4v rs, int voff, int soff, uint32_t la) {
