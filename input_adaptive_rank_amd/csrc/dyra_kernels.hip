@@ -1306,7 +1306,7 @@ struct S3Lds {
 
 // tbase: the token index of column 0 of the L^T rows (0 unless the rows are
 // addressed relative to the segment).
-template <int NRB>
+template <int NRB, bool B32>
 __device__ __forceinline__ void s3_m_strip(const bf16_t* __restrict__ Lt, int64_t ldt,
                                            const bf16_t* __restrict__ X, int64_t c1, int r, int64_t lo,
                                            int64_t hi, int64_t c0, float* __restrict__ Mb, char* lds, int64_t tbase) {
@@ -1322,18 +1322,50 @@ __device__ __forceinline__ void s3_m_strip(const bf16_t* __restrict__ Lt, int64_
   const int s0 = w * nsteps / 4, s1 = (w + 1) * nsteps / 4;
   const int64_t col = c0 + 8 * j;
   const bool colok = col < c1;
+  // Branch-free buffer loads relative to the step's first token (32-bit
+  // offsets): X rows outside [lo, hi) and L^T rows past r or ldt read as
+  // zero, so every load of a step is in flight at once.  A zero X row
+  // cancels its token's L^T column, so L^T is masked only on the steps that
+  // reach past the segment (where it may hold unwritten padding past n).
   auto load = [&](int st, uint4 (&xv)[8], uint4 (&av)[NRB]) {
-    const int64_t t0 = a0 + 32 * (int64_t)st + 8 * g;
+    const int64_t ts = a0 + 32 * (int64_t)st;
+    const int64_t t0 = ts + 8 * g;
+    if constexpr (B32) {
+      const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<bf16_t*>(X + ts * c1), (short)0, 0x7fffffff, 0x00020000);
+      const __amdgpu_buffer_rsrc_t lr = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<bf16_t*>(Lt + ts), (short)0, 0x7fffffff, 0x00020000);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int64_t tt = t0 + e;
-      xv[e] = (colok && tt >= lo && tt < hi) ? *reinterpret_cast<const uint4*>(X + tt * c1 + col) : zero4();
+      for (int e = 0; e < 8; ++e) {
+        const int64_t tt = t0 + e;
+        const int off = colok && tt >= lo && tt < hi ? ((8 * g + e) * (int)c1 + (int)col) * 2 : (int)0x80000000u;
+        xv[e] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
+      }
+#pragma unroll
+      for (int ib = 0; ib < NRB; ++ib) {
+        const int row = ib * 16 + j;
+        const int off = row < r && t0 - tbase < ldt ? (row * (int)ldt + 8 * g) * 2 : (int)0x80000000u;
+        av[ib] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(lr, off, 0, 0));
+      }
+    } else {   // offsets past 32 bits: 64-bit loads, every L^T column masked
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int64_t tt = t0 + e;
+        xv[e] = (colok && tt >= lo && tt < hi) ? *reinterpret_cast<const uint4*>(X + tt * c1 + col) : zero4();
+      }
+#pragma unroll
+      for (int ib = 0; ib < NRB; ++ib) {
+        const int row = ib * 16 + j;
+        const uint4 v = (row < r && t0 - tbase < ldt) ? *reinterpret_cast<const uint4*>(Lt + row * ldt + t0) : zero4();
+        av[ib] = mask_tokens<bf16_t>(v, t0, lo, hi);
+      }
     }
+  };
+  auto edge_mask = [&](int st, uint4 (&av)[NRB]) {
+    const int64_t ts = a0 + 32 * (int64_t)st;
+    if (B32 && (ts < lo || ts + 32 > hi)) {
 #pragma unroll
-    for (int ib = 0; ib < NRB; ++ib) {
-      const int row = ib * 16 + j;
-      uint4 v = (row < r && t0 - tbase < ldt) ? *reinterpret_cast<const uint4*>(Lt + row * ldt + t0) : zero4();
-      av[ib] = mask_tokens<bf16_t>(v, t0, lo, hi);
+      for (int ib = 0; ib < NRB; ++ib) av[ib] = mask_tokens<bf16_t>(av[ib], ts + 8 * g, lo, hi);
     }
   };
   if constexpr (NRB <= 2) {
@@ -1347,6 +1379,7 @@ __device__ __forceinline__ void s3_m_strip(const bf16_t* __restrict__ Lt, int64_
         uint4 ac[NRB];
 #pragma unroll
         for (int ib = 0; ib < NRB; ++ib) ac[ib] = av[ib];
+        edge_mask(st, ac);
         if (st + 1 < s1) load(st + 1, xv, av);
 #pragma unroll
         for (int ib = 0; ib < NRB; ++ib)
@@ -1359,6 +1392,7 @@ __device__ __forceinline__ void s3_m_strip(const bf16_t* __restrict__ Lt, int64_
     for (int st = s0; st < s1; ++st) {
       uint4 xv[8], av[NRB], bv[8];
       load(st, xv, av);
+      edge_mask(st, av);
       transpose8x8_b16(xv, bv);
 #pragma unroll
       for (int ib = 0; ib < NRB; ++ib)
@@ -1599,7 +1633,11 @@ __global__ __launch_bounds__(S3_NT, NRB <= 4 ? 2 : 1) void s3_reduce_solve_kerne
   const bf16_t *Ltb, *Xb;
   int64_t tbase;
   seg_ptrs(b, lo, Ltb, Xb, tbase);
-  s3_m_strip<NRB>(Ltb, ldt, Xb, c1, r, lo, hi, c0, M + b * r * c1, lds, tbase);
+  // 32-bit buffer offsets reach every X row of a 32-token step and every
+  // L^T row of a step
+  const bool b32 = 32 * c1 * 2 < ((int64_t)1 << 31) && ((int64_t)r * ldt + 64) * 2 < ((int64_t)1 << 31);
+  if (b32) s3_m_strip<NRB, true>(Ltb, ldt, Xb, c1, r, lo, hi, c0, M + b * r * c1, lds, tbase);
+  else s3_m_strip<NRB, false>(Ltb, ldt, Xb, c1, r, lo, hi, c0, M + b * r * c1, lds, tbase);
 }
 
 // Gram partials over token chunks: workgroup (b, c) writes
