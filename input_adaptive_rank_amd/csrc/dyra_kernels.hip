@@ -1732,20 +1732,234 @@ void launch_sweep(const float* G, float* Ginv, int32_t* status, int r, float eps
 }
 
 // ===========================================================================
-// S4a': Newton-Schulz inverse on fp32 MFMA (one workgroup per segment,
-// 16 waves, each owning one 32x32 block of the 128 x 128 iterate).
-// Jacobi-scaled A' = D^-1/2 (G + lambda I) D^-1/2 (unit diagonal, padded
-// with the identity up to 128); X_0 = I / ||A'||_F;
+// S4a': Newton-Schulz inverse (one workgroup of 8 waves per segment; wave
+// (bi, h) owns rows 32 bi .. + 31 and columns 64 h .. + 63 of the 128 x 128
+// iterate).  Jacobi-scaled A' = D^-1/2 (G + lambda I) D^-1/2 (unit
+// diagonal, padded with the identity up to 128); X_0 = I / ||A'||_F;
 // X_{k+1} = X_k (2 I - A' X_k) until ||I - A' X_k||_F <= tol or the error
-// stalls at the fp32 floor; Ginv = D^-1/2 X D^-1/2.
+// stops decreasing; the fp32 polish below finishes it (Ginv = D^-1/2 X
+// D^-1/2).  The products run on bf16 MFMAs in split
+// precision: each operand is held as hi + lo bf16 (about 16 significant
+// bits) and P Q is formed as Phi Qhi + Phi Qlo + Plo Qhi with fp32
+// accumulation, three bf16 MFMAs where an fp32 MFMA product would cost
+// sixteen at gfx950's rates.  X and T = A' X stay in LDS as hi / lo bf16,
+// stored transposed (row c holds column c) so that every MFMA operand is one
+// 16-byte row read; X_k is a polynomial in A', hence symmetric, so its
+// stored rows also serve as the rows of X in X T.  Split precision leaves a
+// floor near 1e-5 relative (higher for ill-conditioned A'), so this phase
+// hands X over once ||I - A' X||_F < 5e-2 or stops decreasing, and writes it
+// (A' space) to Ginv for the polish.
 // ===========================================================================
 
+constexpr int NSS_N = 128;
+__device__ __forceinline__ int nss_off(int row, int k) {   // bf16 element (row, k), 16-byte chunks swizzled
+  return row * 256 + ((((k >> 3) ^ row) & 15) << 4) + ((k & 7) << 1);
+}
+__device__ __forceinline__ void split_bf16(float x, uint16_t& h, uint16_t& l) {
+  h = f2bf(x);
+  l = f2bf(x - bf2f(h));
+}
+__global__ __launch_bounds__(512) void ns_inverse_kernel(const float* G, float* Ginv, int32_t* status, int r, float eps,
+                                                          int maxit, float tol) {
+  __shared__ __attribute__((aligned(16))) char XS[2][NSS_N * 256];   // X hi / lo, stored transposed
+  __shared__ __attribute__((aligned(16))) char TS[2][NSS_N * 256];   // T hi / lo, stored transposed
+  __shared__ float dsc[NSS_N];
+  __shared__ float red[16];
+  const int64_t b = blockIdx.x;
+  const float* Gb = G + b * r * r;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l = lane & 31, g = lane >> 5;
+  const int bi = w >> 1, bh2 = w & 1;   // rows bi 32 .. + 31, columns bh2 64 .. + 63 (two 32 x 32 blocks)
+  const float dv = tid < r ? Gb[tid * r + tid] : 0.f;
+  const float tr = block_sum<512>(dv, red);
+  const float lam = eps * tr / (float)r;
+  float badf = 0.f;
+  if (tid < NSS_N) {
+    const float d = tid < r ? dv + lam : 1.f;
+    dsc[tid] = d > 0.f ? rsqrtf(d) : 0.f;
+    if (!(d > 0.f) || !isfinite(d)) badf = 1.f;
+  }
+  badf = block_sum<512>(badf, red);
+  int st = DYRA_SOLVE_OK;
+  if (tr == 0.f) st = DYRA_SOLVE_ZERO;
+  else if (!(tr > 0.f) || !isfinite(tr) || badf > 0.f) st = DYRA_SOLVE_NOT_SPD;
+  // A' = D^-1/2 (G + lambda I) D^-1/2, padded with I: fragments of rows
+  // bi 32 + l, k = 16 ks + 8 g .. + 7, split into bf16 hi / lo
+  uint4 Ahi[8], Alo[8];
+  float fro2 = 0.f;
+  const int arow = bi * 32 + l;
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    uint16_t h[8], lo[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int col = 16 * ks + 8 * g + e;
+      float v;
+      if (arow < r && col < r) v = (Gb[arow * r + col] + (arow == col ? lam : 0.f)) * dsc[arow] * dsc[col];
+      else v = arow == col ? 1.f : 0.f;
+      if (bh2 == 0) fro2 += v * v;
+      split_bf16(v, h[e], lo[e]);
+    }
+    Ahi[ks] = make_uint4(h[0] | (uint32_t)h[1] << 16, h[2] | (uint32_t)h[3] << 16, h[4] | (uint32_t)h[5] << 16, h[6] | (uint32_t)h[7] << 16);
+    Alo[ks] = make_uint4(lo[0] | (uint32_t)lo[1] << 16, lo[2] | (uint32_t)lo[3] << 16, lo[4] | (uint32_t)lo[5] << 16, lo[6] | (uint32_t)lo[7] << 16);
+  }
+  fro2 = block_sum<512>(fro2, red);
+  const float x0 = 1.f / sqrtf(fro2);
+  // this wave's block: accumulator element v of lane (l, g) is (rr, cc) with
+  // rr = bi 32 + 8 (v / 4) + 4 g + v % 4, cc = bj 32 + l; stored at row cc,
+  // k = rr (four consecutive v at one 8-byte place)
+  auto store_blk = [&](char (*S)[NSS_N * 256], int cc, const float (&x)[16]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint16_t h[4], lo[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) split_bf16(x[4 * q + e], h[e], lo[e]);
+      const int off = nss_off(cc, bi * 32 + 8 * q + 4 * g);
+      *reinterpret_cast<uint2*>(S[0] + off) = make_uint2(h[0] | (uint32_t)h[1] << 16, h[2] | (uint32_t)h[3] << 16);
+      *reinterpret_cast<uint2*>(S[1] + off) = make_uint2(lo[0] | (uint32_t)lo[1] << 16, lo[2] | (uint32_t)lo[3] << 16);
+    }
+  };
+  auto load_blk = [&](char (*S)[NSS_N * 256], int cc, float (&x)[16]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int off = nss_off(cc, bi * 32 + 8 * q + 4 * g);
+      const uint2 h = *reinterpret_cast<const uint2*>(S[0] + off), lo = *reinterpret_cast<const uint2*>(S[1] + off);
+      const uint32_t hw[2] = {h.x, h.y}, lw[2] = {lo.x, lo.y};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t hb = (hw[e >> 1] >> (16 * (e & 1))) & 0xffffu, lb = (lw[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+        x[4 * q + e] = __uint_as_float(hb << 16) + __uint_as_float(lb << 16);
+      }
+    }
+  };
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int cc = bh2 * 64 + 32 * j + l;
+    float x[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int rr = bi * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
+      x[v] = rr == cc ? x0 : 0.f;
+    }
+    store_blk(XS, cc, x);
+  }
+  __syncthreads();
+  // acc = P Q over k: P rows from (regs or LDS rows prow), Q columns = LDS rows qrow
+  auto frag = [&](const char (*S)[NSS_N * 256], int row, int ks, uint4& h, uint4& lo) {
+    const int off = row * 256 + ((((2 * ks + g)) ^ row) & 15) * 16;
+    h = *reinterpret_cast<const uint4*>(S[0] + off);
+    lo = *reinterpret_cast<const uint4*>(S[1] + off);
+  };
+  auto mm3 = [&](f32x16 acc, uint4 ah, uint4 al, uint4 bh, uint4 bl) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ah), __builtin_bit_cast(bf16x8_t, bh), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ah), __builtin_bit_cast(bf16x8_t, bl), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, al), __builtin_bit_cast(bf16x8_t, bh), acc, 0, 0, 0);
+    return acc;
+  };
+  float prev = 1e30f;
+  int it = 0;
+  bool ok = st == DYRA_SOLVE_OK;
+  bool converged = false;
+  while (ok && it < maxit) {
+    // T = A' X (this wave's two blocks); X column cc is stored as row cc
+    f32x16 acc[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[j][v] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        uint4 bh, bl;
+        frag(XS, bh2 * 64 + 32 * j + l, ks, bh, bl);
+        acc[j] = mm3(acc[j], Ahi[ks], Alo[ks], bh, bl);
+      }
+    float e2 = 0.f;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int cc = bh2 * 64 + 32 * j + l;
+      float tv[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int rr = bi * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
+        const float d = (rr == cc ? 1.f : 0.f) - acc[j][v];
+        e2 += d * d;
+        tv[v] = acc[j][v];
+      }
+      store_blk(TS, cc, tv);
+    }
+    e2 = block_sum<512>(e2, red);   // barriers: T complete afterwards
+    const float err = sqrtf(e2);
+    if (!isfinite(err)) {
+      ok = false;
+      break;
+    }
+    // hand over to the fp32 polish once the error is small enough for its
+    // quadratic phase, or as soon as split precision stops reducing it
+    if (err <= tol || err < 5e-2f || err >= prev) {
+      converged = true;
+      break;
+    }
+    prev = err;
+    // X <- 2 X - X T: X row bi 32 + l (X symmetric: its stored row), T column cc
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[j][v] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      uint4 ah, al;
+      frag(XS, arow, ks, ah, al);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        uint4 bh, bl;
+        frag(TS, bh2 * 64 + 32 * j + l, ks, bh, bl);
+        acc[j] = mm3(acc[j], ah, al, bh, bl);
+      }
+    }
+    float xo[2][16];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) load_blk(XS, bh2 * 64 + 32 * j + l, xo[j]);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) xo[j][v] = 2.f * xo[j][v] - acc[j][v];
+      store_blk(XS, bh2 * 64 + 32 * j + l, xo[j]);
+    }
+    __syncthreads();
+    ++it;
+  }
+  (void)converged;
+  if (st == DYRA_SOLVE_OK && !ok) {   // broke down: the sweep re-solves the segment
+    if (tid == 0) status[b] = DYRA_SOLVE_FALLBACK;
+    return;
+  }
+  // the iterate in A' space for the fp32 polish (zeros unless solvable)
+  const bool good = st == DYRA_SOLVE_OK;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int cc = bh2 * 64 + 32 * j + l;
+    float x[16];
+    load_blk(XS, cc, x);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int rr = bi * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
+      if (rr < r && cc < r) Ginv[b * r * r + rr * r + cc] = good ? x[v] : 0.f;
+    }
+  }
+  if (tid == 0) status[b] = st;
+}
+
+// Newton-Schulz polish in fp32: continues from the split-precision iterate
+// (two or three iterations from there reach the fp32 floor) and decides
+// convergence as the fp32 iteration does.
 constexpr int NS_N = 128;
 constexpr int NS_P = 129;   // padded LDS pitch (odd: row-strided reads spread over banks)
 
-__global__ __launch_bounds__(1024) void ns_inverse_kernel(const float* G, float* Ginv, bf16_t* Ghi, bf16_t* Glo,
-                                                          int32_t* status, int r, float eps, int maxit,
-                                                          float tol) {
+__global__ __launch_bounds__(1024) void ns_polish_kernel(const float* G, float* Ginv, int32_t* status, int r, float eps,
+                                                         int maxit, float tol) {
   __shared__ float Xs[NS_N * NS_P];
   __shared__ float Ts[NS_N * NS_P];
   __shared__ float dsc[NS_N];
@@ -1755,6 +1969,9 @@ __global__ __launch_bounds__(1024) void ns_inverse_kernel(const float* G, float*
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l = lane & 31, g = lane >> 5;
   const int bi = w >> 2, bj = w & 3;
+  // every thread reads the status before the first barrier; thread 0
+  // rewrites it only at the end
+  if (status[b] != DYRA_SOLVE_OK) return;
 
   // trace, ridge and Jacobi scaling
   const float dv = tid < r ? Gb[tid * r + tid] : 0.f;
@@ -1783,10 +2000,11 @@ __global__ __launch_bounds__(1024) void ns_inverse_kernel(const float* G, float*
     if (bj == 0) fro2 += v * v;   // waves with bj == 0 cover every row band once
   }
   fro2 = block_sum<1024>(fro2, red);
-  const float x0 = 1.f / sqrtf(fro2);
+  (void)fro2;
+  // X_0: the split-precision iterate (A' space), padded with the identity
   for (int e = tid; e < NS_N * NS_N; e += 1024) {
     const int i = e / NS_N, j = e % NS_N;
-    Xs[i * NS_P + j] = i == j ? x0 : 0.f;
+    Xs[i * NS_P + j] = i < r && j < r ? Ginv[b * r * r + i * r + j] : (i == j ? 1.f : 0.f);
   }
   __syncthreads();
   float prev = 1e30f;
@@ -1862,15 +2080,11 @@ __global__ __launch_bounds__(1024) void ns_inverse_kernel(const float* G, float*
   for (int e = tid; e < r * r; e += 1024) {
     const int i = e / r, j = e % r;
     const float v = good ? dsc[i] * Xs[i * NS_P + j] * dsc[j] : 0.f;
-    if (Ginv) Ginv[b * r * r + e] = v;
-    if (Ghi) {
-      const bf16_t h = f2bf(v);
-      Ghi[b * r * r + e] = h;
-      Glo[b * r * r + e] = f2bf(v - bf2f(h));
-    }
+    Ginv[b * r * r + e] = v;
   }
   if (tid == 0) status[b] = st;
 }
+
 
 // ===========================================================================
 // S4b: M'_b = Ginv_b M_b in fp32, stored as T (the S5 GEMM operand).
@@ -2065,9 +2279,10 @@ void forward_residual(const dyra_spec& s, const char* plan, const void* X, int64
   int32_t* stat = reinterpret_cast<int32_t*>(ws + WL.status);
   const int64_t ldt = lt_pitch(n);
   // AUTO takes the sweep at every supported r: on MI355X the fp64 sweep on one
-  // workgroup beats fp32 Newton-Schulz, which the per-CU fp32 MFMA rate
-  // bounds, at r = 64 and r = 128 alike (23 vs 222 us for 32 solves at r = 64,
-  // 99 vs 257 us for one at r = 128); Newton-Schulz stays selectable.
+  // workgroup beats Newton-Schulz (split-precision phase plus fp32 polish),
+  // whose one solve per CU the per-CU MFMA rate bounds, at r = 64 and r = 128
+  // alike (one r = 128 solve: about 100 us against 140 us); Newton-Schulz
+  // stays selectable.
   const bool ns = solver == DYRA_SOLVER_NS;
   // S3: M_b, G_b (bf16: with the sweep solve in the same launch)
   bool solved = false;
@@ -2091,8 +2306,10 @@ void forward_residual(const dyra_spec& s, const char* plan, const void* X, int64
   // S4: Ginv_b (unless solved above), M'_b = Ginv_b M_b
   if (!solved) {
     if (ns) {
-      hipLaunchKernelGGL(ns_inverse_kernel, dim3((unsigned)B), dim3(1024), 0, st, G, Gi, nullptr, nullptr, stat,
-                         r, eps, 60, 2e-6f);
+      // split-precision Newton-Schulz to its floor, the fp32 polish from there,
+      // then the sweep for any segment the polish flags
+      hipLaunchKernelGGL(ns_inverse_kernel, dim3((unsigned)B), dim3(512), 0, st, G, Gi, stat, r, eps, 40, 2e-6f);
+      hipLaunchKernelGGL(ns_polish_kernel, dim3((unsigned)B), dim3(1024), 0, st, G, Gi, stat, r, eps, 60, 2e-6f);
       launch_sweep(G, Gi, stat, r, eps, B, true, st);
     } else {
       launch_sweep(G, Gi, stat, r, eps, B, false, st);
