@@ -32,6 +32,12 @@ SMALL = [
     sc(W["vitb_fc1"], name="many_short_segments", B=37, s=13, c1=128, c2=136, k=16, r=8),
     sc(W["vitb_fc1"], name="wide_k", B=2, s=300, c1=512, c2=256, k=200, r=56),
     sc(W["vitl_fc1"], name="r128_ns", B=2, s=300, c1=256, c2=384, k=64, r=128, solver="ns"),
+    # fp32 storage through Newton-Schulz: split-precision phase, then the
+    # fp32 polish to its floor (the fp32 bar applies)
+    sc(W["vitb_fc1"], name="ragged_fp32_ns", B=3, s=77, c1=192, c2=200, k=24, r=16, dtype=synth.DT_F32,
+       solver="ns"),
+    sc(W["vitl_fc1"], name="r128_ns_fp32", B=2, s=300, c1=256, c2=384, k=64, r=128, dtype=synth.DT_F32,
+       solver="ns"),
     # k + r = 320: the 160 x 320 first-stage tile, ragged in rows
     sc(W["vitl_fc1"], name="wide_first_stage_tile", B=3, s=150, c1=384, c2=384, k=256, r=64),
     # bf16 without bias: the persistent output kernel's zero-addend variant
