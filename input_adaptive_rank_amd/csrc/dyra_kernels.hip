@@ -150,6 +150,8 @@ __device__ __forceinline__ uint4 mask_tokens(uint4 v, int64_t t0, int64_t lo, in
 // reduction adds up instead of streaming L^T for the Gram once more.
 // ---------------------------------------------------------------------------
 constexpr int S1T_BM = 160, S1T_BN = 320, S1T_BK = 32;
+// waves w with (w & S1T_LATE) != 0 issue their k-tile DMAs after two rows of MFMAs
+constexpr int S1T_LATE = 4;
 __global__ __launch_bounds__(512, 1) void s1_tile_kernel(const bf16_t* __restrict__ X,
                                                          const bf16_t* __restrict__ UPt, bf16_t* __restrict__ A,
                                                          bf16_t* __restrict__ Lt, int n, int c1, int k, int r,
@@ -235,17 +237,27 @@ __global__ __launch_bounds__(512, 1) void s1_tile_kernel(const bf16_t* __restric
     constexpr int C = decltype(cur)::value, NX = 1 - C;
     wait_vm_lgkm0<2 * D>();               // this wave's part of k-tile kt + 1; fragments of kt
     bare_barrier();                       // k-tile kt + 1 everywhere; slot kt is read
-    issue(kt + NS, kt & (NS - 1));
+    // Half of the waves issue their DMAs now, the other half after two rows
+    // of MFMAs: a wave waiting on the address path cannot issue MFMAs, and
+    // the two waves of a SIMD then do not wait at the same time.
+    const bool late = (w & S1T_LATE) != 0;
+    if (!late) issue(kt + NS, kt & (NS - 1));
     if (kt + 1 < nkt) load_frags((kt + 1) & (NS - 1), NX);
     __builtin_amdgcn_sched_barrier(0);
     // lane (l16, kg) of block (a, b) receives row 16 a + l16, columns
     // 16 b + 4 kg .. + 3 (the B fragment is the first operand)
 #pragma unroll
-    for (int a = 0; a < FB; ++a)
+    for (int a = 0; a < FB; ++a) {
 #pragma unroll
       for (int b = 0; b < FB; ++b)
         acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, bfr[C][b]),
                                                             __builtin_bit_cast(bf16x8_t, af[C][a]), acc[a][b], 0, 0, 0);
+      if (a == 1) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (late) issue(kt + NS, kt & (NS - 1));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
     __builtin_amdgcn_sched_barrier(0);
   };
   for (int kt = 0; kt < nkt; kt += 2) {
