@@ -136,9 +136,9 @@ __device__ __forceinline__ uint4 mask_tokens(uint4 v, int64_t t0, int64_t lo, in
 // S1 (bf16, k + r = 320): [T | L] = X [U | P] and L^T, one 160 x 320 tile
 // per workgroup (a single round of row blocks on 256 CUs; X is read once).
 // Eight symmetric waves (two per SIMD) each compute 80 x 80 of the tile as
-// 5 x 5 blocks of 16x16x32 MFMAs (5 + 5 fragments per 25 MFMAs), fed by a
-// 4-slot ring of 32-wide k-tiles that every wave fills with LDS-DMA loads
-// three k-tiles ahead.  Nothing is stored before the last k-tile, so a
+// 5 x 5 blocks of 16x16x32 MFMAs (5 + 5 fragments per 25 MFMAs), fed with
+// LDS-DMA loads three 32-wide k-tiles ahead by every wave: a 4-slot ring of
+// UPt k-tiles and a 3-region ring of X k-tile pairs (whole 128-byte lines).  Nothing is stored before the last k-tile, so a
 // wave's wait for its part of a slot is a plain vmcnt count.  The barrier
 // that publishes k-tile t + 1 comes before the MFMAs of k-tile t (whose
 // fragments are already in registers), so the next fragments are read while
@@ -149,7 +149,6 @@ __device__ __forceinline__ uint4 mask_tokens(uint4 v, int64_t t0, int64_t lo, in
 // row, slot 1: the next one), at Gp[(tile * 2 + slot) r^2], which the token
 // reduction adds up instead of streaming L^T for the Gram once more.
 // ---------------------------------------------------------------------------
-constexpr int S1T_BM = 160, S1T_BN = 320, S1T_BK = 32;
 // waves w with (w & S1T_LATE) != 0 issue their k-tile DMAs after two rows of MFMAs
 constexpr int S1T_LATE = 4;
 __global__ __launch_bounds__(512, 1) void s1_tile_kernel(const bf16_t* __restrict__ X,
@@ -157,18 +156,18 @@ __global__ __launch_bounds__(512, 1) void s1_tile_kernel(const bf16_t* __restric
                                                          bf16_t* __restrict__ Lt, int n, int c1, int k, int r,
                                                          int64_t ldt, float* __restrict__ Gp, int seg) {
   constexpr int BM = S1T_BM, BN = S1T_BN, RBY = S1T_BK * 2;   // 64-byte k-tile rows
-  constexpr int NS = 4, NW = 8, FB = 5;                       // ring slots, waves, 16-blocks per wave side
-  constexpr int ABLK = BM * RBY / 1024, BBLK = BN * RBY / 1024;   // 10 + 20 one-KB blocks
-  constexpr int SLOT_BLK = 32, SLOT = SLOT_BLK * 1024;        // + 2 zero-filled pads
-  constexpr int D = SLOT_BLK / NW;                            // DMAs per wave per k-tile
+  constexpr int NS = 4, NP = 3, NW = 8, FB = 5;   // UPt slots, X pair regions, waves, 16-blocks per wave side
+  constexpr int USLOT = BN * RBY, XPAIR = BM * 2 * RBY;       // 20 KB each
+  constexpr int XOFF = NS * USLOT, RING = XOFF + NP * XPAIR;  // 140 KB
+  constexpr int DW = 5;                                       // DMA blocks per wave
   constexpr int SP = BN * 2 + 16;                             // staged row pitch (bytes)
-  static_assert(ABLK + BBLK <= SLOT_BLK && SLOT_BLK % NW == 0 && 3 * D < 64, "slot");
-  static_assert(BM * SP <= NS * SLOT, "staging fits the ring");
+  static_assert(USLOT == 20 * 1024 && XPAIR == 20 * 1024, "20 UPt + 20 X one-KB blocks over 8 waves");
+  static_assert(BM * SP <= RING, "staging fits the ring");
   constexpr int LTP = BM * 2 + 16;                            // L^T tile row pitch (bytes), 64 rows
   constexpr int LT_OFF = BM * SP;                             // after the staged tile
-  static_assert(LT_OFF % 16 == 0 && LT_OFF + 64 * LTP <= NS * SLOT, "L^T tile fits the ring");
+  static_assert(LT_OFF % 16 == 0 && LT_OFF + 64 * LTP <= RING, "L^T tile fits the ring");
   static_assert(2 * FB * 16 == BM && 4 * FB * 16 == BN, "2 x 4 waves of 80 x 80");
-  __shared__ __attribute__((aligned(1024))) char ring[NS * SLOT];
+  __shared__ __attribute__((aligned(1024))) char ring[RING];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = w >> 2, wn = w & 3;
@@ -176,50 +175,72 @@ __global__ __launch_bounds__(512, 1) void s1_tile_kernel(const bf16_t* __restric
   const int m0 = blockIdx.x * BM;
   const int rows = min(BM, n - m0);
   const int nkt = c1 / S1T_BK;                                // c1 % 64 == 0: nkt even
-  const int ldx = c1 * 2;                                     // bytes per X / UPt row
+  const int ldx = c1 * 2;                                     // bytes per X row
   const uint32_t ring_s = lds_addr(ring);
-  // Slot block b < ABLK holds X rows 16 b .. 16 b + 15, block ABLK + b UPt
-  // rows 16 b ..; the rest are pads.  Lane L of a block writes row 16 b + L / 4
-  // at physical chunk L % 4, which holds logical chunk (L % 4) ^ ((row / 4) % 4).
+  // UPt is k-tile-major in the plan: k-tile t is one 20 KB run, 320 rows of
+  // 64 bytes, loaded into UPt slot t % 4.  X is loaded two k-tiles at a time,
+  // so that every row segment is a whole 128-byte line: 160 rows of 128 bytes
+  // in pair region (t / 2) % 3.  One-KB blocks: UPt block b holds rows
+  // 16 b .. 16 b + 15, lane L writing row 16 b + L / 4 at physical chunk L % 4,
+  // which holds logical chunk (L % 4) ^ ((row / 4) % 4); X block b holds rows
+  // 8 b .. 8 b + 7, lane L writing row 8 b + L / 8 at physical chunk L % 8,
+  // which holds logical chunk (L % 8) ^ ((row / 2) % 8) (chunks 0-3 the even
+  // k-tile, 4-7 the odd one).  Both make a 16-lane fragment read of 16
+  // consecutive rows conflict-free.  Waves 0-3 take 3 UPt and 2 X blocks,
+  // waves 4-7 2 and 3: for an even k-tile a wave issues its UPt blocks and its
+  // blocks of the pair's X (5 DMAs), for an odd one its UPt blocks (nU).
   const i32x4v xrs = rsrc_words(reinterpret_cast<const char*>(X) + (int64_t)m0 * ldx, (uint32_t)rows * ldx);
   const i32x4v urs = rsrc_words(UPt, (uint32_t)BN * ldx);
-  const i32x4v zrs = rsrc_words(UPt, 0u);
-  const int brow = lane >> 2, pc = lane & 3;
-  int voff[D];
+  const int nU = w < 4 ? 3 : 2;
+  const int u0 = w < 4 ? 3 * w : 2 * w + 4, x0 = w < 4 ? 2 * w : 3 * w - 4;
+  int voff[DW], loff[DW];
+  i32x4v drs[DW];
 #pragma unroll
-  for (int j = 0; j < D; ++j) {
-    const int blk = w * D + j;
-    const int row = (blk < ABLK ? blk : blk - ABLK) * 16 + brow;
-    voff[j] = row * ldx + (pc ^ ((row >> 2) & 3)) * 16;
-  }
-  // this wave's descriptors, chosen once (in SGPRs)
-  i32x4v drs[D];
-#pragma unroll
-  for (int j = 0; j < D; ++j) {
-    const int blk = w * D + j;
-    drs[j] = blk >= ABLK + BBLK ? zrs : blk < ABLK ? xrs : urs;
+  for (int j = 0; j < DW; ++j) {
+    const bool isu = j < nU;
+    const int blk = isu ? u0 + j : x0 + j - nU;
+    if (isu) {
+      const int row = 16 * blk + (lane >> 2);
+      voff[j] = row * RBY + (((lane & 3) ^ ((row >> 2) & 3)) << 4);
+    } else {
+      const int row = 8 * blk + (lane >> 3);
+      voff[j] = row * ldx + (((lane & 7) ^ ((row >> 1) & 7)) << 4);
+    }
+    loff[j] = __builtin_amdgcn_readfirstlane(blk * 1024);
+    drs[j] = isu ? urs : xrs;
     drs[j].x = __builtin_amdgcn_readfirstlane(drs[j].x);
     drs[j].y = __builtin_amdgcn_readfirstlane(drs[j].y);
     drs[j].z = __builtin_amdgcn_readfirstlane(drs[j].z);
     drs[j].w = __builtin_amdgcn_readfirstlane(drs[j].w);
   }
+  // k-tile t's DMAs (with EV, t even: the X of k-tiles t and t + 1 too);
   // k-tiles past the end read at an offset past every descriptor's records
-  auto issue = [&](int kt, int slot) {
-    const int soff = kt < nkt ? kt * RBY : 0x7fff0000;
-    const uint32_t la = ring_s + slot * SLOT + w * D * 1024;
+  auto issue = [&](int t, auto ev) {
+    constexpr bool EV = decltype(ev)::value;
+    const bool live = t < nkt;
+    const int su = live ? t * USLOT : 0x7fff0000;
+    const int sx = live ? t * RBY : 0x7fff0000;
+    const uint32_t lu = ring_s + (t & (NS - 1)) * USLOT;
+    const uint32_t lx = ring_s + XOFF + ((t >> 1) % NP) * XPAIR;
 #pragma unroll
-    for (int j = 0; j < D; ++j) dma16(drs[j], voff[j], soff, la + j * 1024);
+    for (int j = 0; j < DW; ++j) {
+      if (j < nU) dma16(drs[j], voff[j], su, lu + loff[j]);
+      else if (EV) dma16(drs[j], voff[j], sx, lx + loff[j]);
+    }
   };
-  // fragments: block f of this wave's rows (A) or columns (B), lane (l16, kg):
-  // row 16 f + l16 at logical chunk kg
+  // fragments of k-tile t (H = t % 2): block f of this wave's rows (A) or
+  // columns (B), lane (l16, kg): row 16 f + l16 at logical chunk kg of the
+  // k-tile
   uint4 af[2][FB], bfr[2][FB];
-  auto load_frags = [&](int slot, int buf) {
-    const char* st = ring + slot * SLOT;
+  auto load_frags = [&](int t, auto hb) {
+    constexpr int H = decltype(hb)::value;
+    const char* su = ring + (t & (NS - 1)) * USLOT;
+    const char* sx = ring + XOFF + ((t >> 1) % NP) * XPAIR;
 #pragma unroll
     for (int f = 0; f < FB; ++f) {
       const int ra = wm * 80 + f * 16 + l16, rb = wn * 80 + f * 16 + l16;
-      af[buf][f] = *reinterpret_cast<const uint4*>(st + ra * RBY + ((kg ^ ((ra >> 2) & 3)) << 4));
-      bfr[buf][f] = *reinterpret_cast<const uint4*>(st + ABLK * 1024 + rb * RBY + ((kg ^ ((rb >> 2) & 3)) << 4));
+      af[H][f] = *reinterpret_cast<const uint4*>(sx + ra * (2 * RBY) + (((H * 4 + kg) ^ ((ra >> 1) & 7)) << 4));
+      bfr[H][f] = *reinterpret_cast<const uint4*>(su + rb * RBY + ((kg ^ ((rb >> 2) & 3)) << 4));
     }
   };
   f32x4 acc[FB][FB];
@@ -227,22 +248,31 @@ __global__ __launch_bounds__(512, 1) void s1_tile_kernel(const bf16_t* __restric
   for (int a = 0; a < FB; ++a)
 #pragma unroll
     for (int b = 0; b < FB; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int s0 = 0; s0 < NS; ++s0) issue(s0, s0);
-  wait_vm_lgkm0<3 * D>();                 // k-tile 0 (three slots were issued after it)
+  using Even = std::integral_constant<bool, true>;
+  using Odd = std::integral_constant<bool, false>;
+  issue(0, Even());
+  issue(1, Odd());
+  issue(2, Even());
+  issue(3, Odd());
+  // k-tile 0 (UPt and the X pair in its DMAs; k-tiles 1 .. 3 issued after it)
+  if (w < 4) wait_vm_lgkm0<3 + 5 + 3>();
+  else wait_vm_lgkm0<2 + 5 + 2>();
   bare_barrier();
-  load_frags(0, 0);
+  load_frags(0, std::integral_constant<int, 0>());
   // two k-tiles per trip: fragment buffers 0 and 1 alternate statically
   auto step = [&](int kt, auto cur) {
     constexpr int C = decltype(cur)::value, NX = 1 - C;
-    wait_vm_lgkm0<2 * D>();               // this wave's part of k-tile kt + 1; fragments of kt
-    bare_barrier();                       // k-tile kt + 1 everywhere; slot kt is read
+    // this wave's part of k-tile kt + 1 (the DMAs of the two k-tiles issued
+    // after it stay in flight); fragments of kt
+    if (w < 4) wait_vm_lgkm0<5 + 3>();
+    else wait_vm_lgkm0<5 + 2>();
+    bare_barrier();                       // k-tile kt + 1 everywhere; k-tile kt is read
     // Half of the waves issue their DMAs now, the other half after two rows
     // of MFMAs: a wave waiting on the address path cannot issue MFMAs, and
     // the two waves of a SIMD then do not wait at the same time.
     const bool late = (w & S1T_LATE) != 0;
-    if (!late) issue(kt + NS, kt & (NS - 1));
-    if (kt + 1 < nkt) load_frags((kt + 1) & (NS - 1), NX);
+    if (!late) issue(kt + NS, std::integral_constant<bool, C == 0>());
+    if (kt + 1 < nkt) load_frags(kt + 1, std::integral_constant<int, NX>());
     __builtin_amdgcn_sched_barrier(0);
     // lane (l16, kg) of block (a, b) receives row 16 a + l16, columns
     // 16 b + 4 kg .. + 3 (the B fragment is the first operand)
@@ -254,7 +284,7 @@ __global__ __launch_bounds__(512, 1) void s1_tile_kernel(const bf16_t* __restric
                                                             __builtin_bit_cast(bf16x8_t, af[C][a]), acc[a][b], 0, 0, 0);
       if (a == 1) {
         __builtin_amdgcn_sched_barrier(0);
-        if (late) issue(kt + NS, kt & (NS - 1));
+        if (late) issue(kt + NS, std::integral_constant<bool, C == 0>());
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -2413,8 +2443,7 @@ int forward_lowrank(const dyra_spec& s, const char* plan, const void* X, const v
     // ViT-L sizes, more tiles than two per CU: one 160 x 320 tile per row
     // block instead (a single round, X read once per row block)
     if constexpr (TT<T>::ESZ == 2) {
-      if (k + r == S1T_BN && c1 % (2 * S1T_BK) == 0 && (int64_t)S1T_BN * c1 * 2 < ((int64_t)1 << 31) &&
-          (int64_t)S1T_BM * c1 * 2 < ((int64_t)1 << 31)) {
+      if (s1_tile_shape(s, DYRA_BF16)) {
         // Gram partials from the tile epilogue when a tile meets at most two
         // segments and r fills whole 32 x 32 blocks
         const bool gram = (r == 32 || r == 64) && seg >= S1T_BM;

@@ -252,9 +252,9 @@ extern "C" int dyra_plan_pack(const dyra_spec* spec, const dyra_host_factors* f,
     if (!f->U || !f->V) return DYRA_EINVAL;
     const int64_t k = s.k;
     for (int64_t q = 0; q < k; ++q)
-      for (int64_t i = 0; i < c1; ++i) put(host_plan, L.UPt, (size_t)(q * c1 + i), f->U[i * k + q], dtype);
+      for (int64_t i = 0; i < c1; ++i) put(host_plan, L.UPt, upt_index(s, dtype, q, i), f->U[i * k + q], dtype);
     for (int64_t p = 0; p < r; ++p)
-      for (int64_t i = 0; i < c1; ++i) put(host_plan, L.UPt, (size_t)((k + p) * c1 + i), f->P[i * r + p], dtype);
+      for (int64_t i = 0; i < c1; ++i) put(host_plan, L.UPt, upt_index(s, dtype, k + p, i), f->P[i * r + p], dtype);
     for (int64_t j = 0; j < c2; ++j)
       for (int64_t q = 0; q < k; ++q) put(host_plan, L.Vt, (size_t)(j * k + q), f->V[q * c2 + j], dtype);
   } else if (s.kind == DYRA_MONARCH) {

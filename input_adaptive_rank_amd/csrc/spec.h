@@ -54,11 +54,28 @@ inline int validate_dtype(const dyra_spec& s, int dtype) {
 
 // ---- packed device plan --------------------------------------------------
 // low-rank : UPt [(k+r) x c1] ([U | P]^T), Vt [c2 x k] (V^T), Wrt [c2 x c1] (W_res^T)
+//            For the 160 x 320 first-stage tile (bf16, k + r = 320, c1 a
+//            multiple of 64) UPt is stored k-tile-major instead: 32-column
+//            k-tiles, each a contiguous [(k+r) x 32] block.
 // Monarch  : B1t [m][m][m] (B1t[a][j][i] = B1[a][i][j]), Pt [r x c],
 //            B2t [m][m][m] (B2t[j][l][a] = B2[j][a][l]), Wrt [c x c]
 // BLAST    : Ubt [nb][rb][c1/nb] (U_i^T), Pt [r x c1],
 //            St [(nb rb) x (nb rb)] (St[j rb + q][i rb + p] = S[i][j][p][q]),
 //            Vb [nb][c2/nb][rb] (as prepared), Wrt [c2 x c1]
+// Shape of the first-stage tile kernel: 160 token rows x 320 = k + r output
+// columns per workgroup, 32-column k-tiles.
+constexpr int S1T_BM = 160, S1T_BN = 320, S1T_BK = 32;
+inline bool s1_tile_shape(const dyra_spec& s, int dtype) {
+  return s.kind == DYRA_LOWRANK && dtype == DYRA_BF16 && s.k + s.r == S1T_BN && s.c1 % (2 * S1T_BK) == 0 &&
+         (int64_t)S1T_BN * s.c1 * 2 < ((int64_t)1 << 31) && (int64_t)S1T_BM * s.c1 * 2 < ((int64_t)1 << 31);
+}
+// Element index of UPt[q][i] (row q of [U | P]^T, input column i).
+inline size_t upt_index(const dyra_spec& s, int dtype, int64_t q, int64_t i) {
+  if (s1_tile_shape(s, dtype))
+    return (size_t)((i / S1T_BK) * S1T_BN * S1T_BK + q * S1T_BK + i % S1T_BK);
+  return (size_t)(q * s.c1 + i);
+}
+
 struct PlanLayout {
   size_t UPt = 0, Vt = 0, B1t = 0, B2t = 0, Pt = 0, Ubt = 0, St = 0, Vb = 0, Wrt = 0;
   size_t total = 0;

@@ -115,6 +115,22 @@ def test_plan_pack_lowrank_layout():
         np.testing.assert_array_equal(Wrt, rnd(f["Wres"].T))
 
 
+def test_plan_pack_tiled_upt():
+    """bf16 plans with k + r = 320 and c1 a multiple of 64 (the 160 x 320
+    first-stage tile) hold [U | P]^T k-tile-major: c1 / 32 blocks of
+    (k + r) x 32; fp32 plans of the same spec keep the row layout."""
+    c1, c2, k, r = 384, 384, 256, 64
+    spec = D.make_spec(synth.KIND_LOWRANK, c1, c2, r, k=k)
+    f = D.prepare(_w(2, c1, c2), spec)
+    UPt = np.concatenate([f["U"].T, f["P"].T])
+    vals = synth.bf16_to_f64(D.plan_pack(spec, f, synth.DT_BF16).view(np.uint16))
+    tiled = vals[:(k + r) * c1].reshape(c1 // 32, k + r, 32)
+    for t in range(c1 // 32):
+        np.testing.assert_array_equal(tiled[t], _bf16(UPt[:, 32 * t:32 * t + 32]))
+    vals32 = D.plan_pack(spec, f, synth.DT_F32).view(np.float32).astype(np.float64)
+    np.testing.assert_array_equal(vals32[:(k + r) * c1].reshape(k + r, c1), synth.round_f32(UPt))
+
+
 def test_bf16_rounding_of_pack_matches_generator_rounding():
     """Library rounding (fp64 -> fp32 -> bf16, RNE) equals the generator's."""
     rng = np.random.default_rng(3)
