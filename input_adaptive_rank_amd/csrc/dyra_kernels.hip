@@ -2136,62 +2136,87 @@ __global__ __launch_bounds__(1024) void ns_polish_kernel(const float* G, float* 
 // L_b is ill-conditioned.
 // ===========================================================================
 
+// One wave per (segment, 16-row block of M', 64-column tile), on
+// v_mfma_f32_16x16x4f32 with both operands read straight from memory.  The
+// reduction index is permuted so that each lane's operands are float4 runs:
+// in 16-wide chunk t, lane group g = lane / 16 holds q = 16 t + 4 g + e for
+// e = 0..3, and MFMA e of the chunk takes element e of the lane's Ginv run
+// (row 16 rb + lane % 16) and of its M runs (rows q, columns
+// c0 + 4 (lane % 16) .. + 3).  MFMA e of column block jb therefore sums
+// over q = 16 t + e, + 4, + 8, + 12 and writes column c0 + 4 (lane % 16) + jb;
+// the accumulator of lane (i, g) holds rows 16 rb + 4 g .. + 3 of those
+// columns.  The next chunk is loaded before the current one is multiplied.
+constexpr int AI_WAVES = 4;
 template <typename T>
-__global__ __launch_bounds__(256) void apply_inverse_kernel(const float* __restrict__ Ginv,
-                                                            const float* __restrict__ M, T* __restrict__ Mp,
-                                                            int r, int64_t c1) {
-  // tile: all r rows x 64 columns; thread = 4 rows x 4 columns per pass
-  extern __shared__ __attribute__((aligned(16))) float sh[];
-  const int P = r + 4;          // padded pitch: the transposing stores spread over the banks
-  float* Gs = sh;               // [q][p] = Ginv[p][q], pitch P
-  float* Ms = sh + r * P;       // [q][c]
-  const int64_t tiles = (c1 + 63) / 64;
-  const int64_t b = blockIdx.x / tiles;
-  const int64_t c0 = (blockIdx.x % tiles) * 64;
-  const int tid = threadIdx.x;
+__global__ __launch_bounds__(64 * AI_WAVES) void apply_inverse_kernel(const float* __restrict__ Ginv,
+                                                                      const float* __restrict__ M,
+                                                                      T* __restrict__ Mp, int r, int64_t c1,
+                                                                      int64_t tasks) {
+  const int lane = threadIdx.x & 63;
+  const int64_t task = (int64_t)blockIdx.x * AI_WAVES + (threadIdx.x >> 6);
+  if (task >= tasks) return;
+  const int nrb = (r + 15) >> 4;
+  const int64_t tiles = (c1 + 63) >> 6;
+  const int rb = (int)(task % nrb);             // the waves of a workgroup share an M tile
+  const int64_t ct = (task / nrb) % tiles, b = task / (nrb * tiles);
+  const int i = lane & 15, g = lane >> 4;
   const float* Gb = Ginv + b * r * r;
   const float* Mb = M + b * r * c1;
-  for (int e4 = tid; e4 < r * r / 4; e4 += 256) {   // r % 4 == 0
-    const float4 v = *reinterpret_cast<const float4*>(Gb + e4 * 4);
-    const int p = (e4 * 4) / r, q = (e4 * 4) % r;
-    Gs[(q + 0) * P + p] = v.x;
-    Gs[(q + 1) * P + p] = v.y;
-    Gs[(q + 2) * P + p] = v.z;
-    Gs[(q + 3) * P + p] = v.w;
-  }
-  for (int e = tid; e < r * 16; e += 256) {
-    const int q = e >> 4, c4 = (e & 15) * 4;
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (c0 + c4 < c1) v = *reinterpret_cast<const float4*>(Mb + q * c1 + c0 + c4);
-    *reinterpret_cast<float4*>(Ms + q * 64 + c4) = v;
-  }
-  __syncthreads();
-  const int cq = tid & 15;                      // column quad
-  for (int pq = tid >> 4; pq * 4 < r; pq += 16) {   // row quad
-    float acc[4][4] = {};
-    for (int q = 0; q < r; ++q) {
-      const float4 g4 = *reinterpret_cast<const float4*>(Gs + q * P + pq * 4);
-      const float4 m4 = *reinterpret_cast<const float4*>(Ms + q * 64 + cq * 4);
-      const float gv[4] = {g4.x, g4.y, g4.z, g4.w}, mv[4] = {m4.x, m4.y, m4.z, m4.w};
+  const int64_t col = ct * 64 + 4 * i;          // c1 % 8 == 0: all four columns or none
+  const bool cok = col < c1;
+  const int row = rb * 16 + i;
+  const int nt = (r + 15) >> 4;
+  auto load = [&](int t, float4& a, float4 (&m)[4]) {
+    const int q0 = 16 * t + 4 * g;              // r % 4 == 0: all four q or none
+    a = (row < r && q0 < r) ? *reinterpret_cast<const float4*>(Gb + (int64_t)row * r + q0)
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+    for (int e = 0; e < 4; ++e)
+      m[e] = (cok && q0 < r) ? *reinterpret_cast<const float4*>(Mb + (int64_t)(q0 + e) * c1 + col)
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
+  };
+  f32x4 acc[4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) acc[a][c] = fmaf(gv[a], mv[c], acc[a][c]);
+  for (int jb = 0; jb < 4; ++jb) acc[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float4 a, m[4];
+  load(0, a, m);
+  for (int t = 0; t < nt; ++t) {
+    float4 an, mn[4];
+    if (t + 1 < nt) load(t + 1, an, mn);
+    const float av[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float mv[4] = {m[e].x, m[e].y, m[e].z, m[e].w};
+#pragma unroll
+      for (int jb = 0; jb < 4; ++jb) acc[jb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[e], mv[jb], acc[jb], 0, 0, 0);
     }
-    if (c0 + cq * 4 >= c1) continue;
+    if (t + 1 < nt) {
+      a = an;
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      T* dst = Mp + (b * r + pq * 4 + a) * c1 + c0 + cq * 4;
-      if constexpr (TT<T>::ESZ == 2) {
-        uint2 pk;
-        pk.x = (uint32_t)f2bf(acc[a][0]) | ((uint32_t)f2bf(acc[a][1]) << 16);
-        pk.y = (uint32_t)f2bf(acc[a][2]) | ((uint32_t)f2bf(acc[a][3]) << 16);
-        *reinterpret_cast<uint2*>(dst) = pk;
-      } else {
-        *reinterpret_cast<float4*>(dst) = make_float4(acc[a][0], acc[a][1], acc[a][2], acc[a][3]);
-      }
+      for (int e = 0; e < 4; ++e) m[e] = mn[e];
     }
   }
+  if (!cok) return;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int orow = rb * 16 + 4 * g + v;
+    if (orow >= r) continue;
+    T* dst = Mp + (b * r + orow) * c1 + col;
+    if constexpr (TT<T>::ESZ == 2) {
+      uint2 pk;
+      pk.x = (uint32_t)f2bf(acc[0][v]) | ((uint32_t)f2bf(acc[1][v]) << 16);
+      pk.y = (uint32_t)f2bf(acc[2][v]) | ((uint32_t)f2bf(acc[3][v]) << 16);
+      *reinterpret_cast<uint2*>(dst) = pk;
+    } else {
+      *reinterpret_cast<float4*>(dst) = make_float4(acc[0][v], acc[1][v], acc[2][v], acc[3][v]);
+    }
+  }
+}
+
+// grid for apply_inverse_kernel over B segments of r x c1
+inline void launch_apply_inverse_dims(int64_t B, int r, int64_t c1, int64_t& tasks, unsigned& blocks) {
+  tasks = B * ((r + 15) / 16) * ((c1 + 63) / 64);
+  blocks = (unsigned)((tasks + AI_WAVES - 1) / AI_WAVES);
 }
 
 // ===========================================================================
@@ -2364,8 +2389,12 @@ void forward_residual(const dyra_spec& s, const char* plan, const void* X, int64
       launch_sweep(G, Gi, stat, r, eps, B, false, st);
     }
   }
-  hipLaunchKernelGGL(apply_inverse_kernel<T>, dim3((unsigned)(cdiv(c1, 64) * B)), dim3(256),
-                     (size_t)(r * (r + 4) + r * 64) * 4, st, Gi, M, Mp, r, c1);
+  {
+    int64_t tasks;
+    unsigned blocks;
+    launch_apply_inverse_dims(B, r, c1, tasks, blocks);
+    hipLaunchKernelGGL(apply_inverse_kernel<T>, dim3(blocks), dim3(64 * AI_WAVES), 0, st, Gi, M, Mp, r, c1, tasks);
+  }
   E.mark(3, st);
   // S5: R^T (c2 x B r) = W_res^T (c2 x c1) . M' (B r x c1)^T; bf16: the
   // persistent output kernel with one segment, no residual part and no bias
@@ -2406,8 +2435,13 @@ void left_step_bf16(const dyra_spec& s, const char* plan, const bf16_t* X, int64
   else if (r <= 32) launch_s3_bf16<2, 1>(R, c2, Wrt, c1, r, c2, nn, B, Qt, K, Kinv, kst, eps, true, st, r, true);
   else if (r <= 64) launch_s3_bf16<4, 2>(R, c2, Wrt, c1, r, c2, nn, B, Qt, K, Kinv, kst, eps, true, st, r, true);
   else launch_s3_bf16<8, 4>(R, c2, Wrt, c1, r, c2, nn, B, Qt, K, Kinv, kst, eps, true, st, r, true);
-  hipLaunchKernelGGL(apply_inverse_kernel<bf16_t>, dim3((unsigned)(cdiv(c1, 64) * B)), dim3(256),
-                     (size_t)(r * (r + 4) + r * 64) * 4, st, Kinv, Qt, Zt, r, c1);
+  {
+    int64_t tasks;
+    unsigned blocks;
+    launch_apply_inverse_dims(B, r, c1, tasks, blocks);
+    hipLaunchKernelGGL(apply_inverse_kernel<bf16_t>, dim3(blocks), dim3(64 * AI_WAVES), 0, st, Kinv, Qt, Zt, r, c1,
+                       tasks);
+  }
   // L_b = X_b Z_b into [T | L] and L^T
   const int tiles_n = (int)cdiv(r, CfgL::BN);
   hipLaunchKernelGGL(s1_left_kernel<CfgL>, dim3((unsigned)(cdiv(n, CfgL::BM) * tiles_n)), dim3(CfgL::NT), 0, st, X,
