@@ -68,6 +68,78 @@ __global__ __launch_bounds__(C::NT, WPE) void gemm_tn_kernel(const char* A, int6
               (N - n0) * TT<T>::ESZ);
 }
 
+// Slice z of a split-K C = A B^T (bf16 operands, 128 x 128 tiles, single
+// operand stage as above): the fp32 sums over K elements
+// [z kslice, z kslice + kslice) into P + z M N (row pitch N, N % 4 == 0),
+// straight from the accumulators.
+template <class C>
+__global__ __launch_bounds__(C::NT, 4) void gemm_tn_splitk_kernel(const char* A, int64_t lda, const char* B,
+                                                                  int64_t ldb, float* P, int64_t M, int64_t N,
+                                                                  int64_t K, int64_t kslice, int tiles_n,
+                                                                  int tiles) {
+  static_assert(TT<typename C::elem>::ESZ == 2, "bf16 operands");
+  __shared__ __attribute__((aligned(16))) char lds[C::LDS1];
+  const int z = blockIdx.x / tiles;
+  const int t = xcd_tile_id(blockIdx.x % tiles, tiles);
+  const int64_t m0 = (int64_t)(t / tiles_n) * C::BM, n0 = (int64_t)(t % tiles_n) * C::BN;
+  const int64_t k0 = z * kslice, kb = imin64(kslice, K - k0) * 2;
+  A += k0 * 2;
+  B += k0 * 2;
+  auto src = [=](int tt, Phase& ph, int& kt) {
+    ph.a = OpK{A, lda, m0, 0, M, kb};
+    ph.b = OpK{B, ldb, n0, 0, N, kb};
+    kt = tt;
+  };
+  f32x16 acc[C::FM][C::FN];
+  gemm_mainloop1_dma<C>(src, ktiles(kb), lds, acc);
+  // accumulator (fm, fn) element 4 q + e: row wm WM + 32 fm + lane % 32,
+  // column wn WN + 32 fn + 8 q + 4 (lane / 32) + e
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int wm = w / C::NWN, wn = w % C::NWN, l = lane & 31, g = lane >> 5;
+  float* Pz = P + z * M * N;
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm) {
+    const int64_t row = m0 + wm * C::WM + fm * 32 + l;
+    if (row >= M) continue;
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t col = n0 + wn * C::WN + fn * 32 + 8 * q + 4 * g;
+        if (col < N)
+          *reinterpret_cast<float4*>(Pz + row * N + col) =
+              make_float4(acc[fm][fn][4 * q], acc[fm][fn][4 * q + 1], acc[fm][fn][4 * q + 2], acc[fm][fn][4 * q + 3]);
+      }
+  }
+}
+
+// out[i] = bf16(sum over z < slices of P[z MN + i]), eight elements per
+// thread (MN % 8 == 0).
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ P, bf16_t* __restrict__ out,
+                                                            int64_t MN, int slices) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (i >= MN) return;
+  float4 a = *reinterpret_cast<const float4*>(P + i), b = *reinterpret_cast<const float4*>(P + i + 4);
+  for (int z = 1; z < slices; ++z) {
+    const float4 u = *reinterpret_cast<const float4*>(P + z * MN + i);
+    const float4 v = *reinterpret_cast<const float4*>(P + z * MN + i + 4);
+    a.x += u.x;
+    a.y += u.y;
+    a.z += u.z;
+    a.w += u.w;
+    b.x += v.x;
+    b.y += v.y;
+    b.z += v.z;
+    b.w += v.w;
+  }
+  uint4 pk;
+  pk.x = (uint32_t)f2bf(a.x) | ((uint32_t)f2bf(a.y) << 16);
+  pk.y = (uint32_t)f2bf(a.z) | ((uint32_t)f2bf(a.w) << 16);
+  pk.z = (uint32_t)f2bf(b.x) | ((uint32_t)f2bf(b.y) << 16);
+  pk.w = (uint32_t)f2bf(b.z) | ((uint32_t)f2bf(b.w) << 16);
+  *reinterpret_cast<uint4*>(out + i) = pk;
+}
+
 // ===========================================================================
 // S1 (low-rank): [T | L] = X [U_f | P], plus L^T (token-contiguous) for S3
 // ===========================================================================
@@ -2396,9 +2468,24 @@ void forward_residual(const dyra_spec& s, const char* plan, const void* X, int64
     hipLaunchKernelGGL(apply_inverse_kernel<T>, dim3(blocks), dim3(64 * AI_WAVES), 0, st, Gi, M, Mp, r, c1, tasks);
   }
   E.mark(3, st);
-  // S5: R^T (c2 x B r) = W_res^T (c2 x c1) . M' (B r x c1)^T; bf16: the
-  // persistent output kernel with one segment, no residual part and no bias
+  // S5: R^T (c2 x B r) = W_res^T (c2 x c1) . M' (B r x c1)^T; bf16: split
+  // over K when the output has few tiles, else the persistent output kernel
+  // with one segment, no residual part and no bias
   if constexpr (BF) {
+    const S5Split sp = s5_split(c2, B * r, c1);
+    if (sp.slices > 1) {
+      typedef CfgB Cs;
+      float* Pk = reinterpret_cast<float*>(ws + WL.Pk);
+      const int tiles_n = (int)cdiv(B * r, Cs::BN);
+      const int tiles = (int)(cdiv(c2, Cs::BM) * tiles_n);
+      hipLaunchKernelGGL(gemm_tn_splitk_kernel<Cs>, dim3((unsigned)(tiles * sp.slices)), dim3(Cs::NT), 0, st,
+                         reinterpret_cast<const char*>(Wrt), c1 * 2, reinterpret_cast<const char*>(Mp), c1 * 2, Pk,
+                         c2, B * r, c1, sp.kslice, tiles_n, tiles);
+      const int64_t mn = c2 * B * r;
+      hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)cdiv(mn, 256 * 8)), dim3(256), 0, st, Pk,
+                         reinterpret_cast<bf16_t*>(Rt), mn, sp.slices);
+      return;
+    }
     if (s6_ws_fits(c2, B * r, (int)c1, 0, 1) && device_cus() >= 8) {
       launch_s6_ws(Wrt, Mp, nullptr, nullptr, Rt, c2, B * r, (int)c1, 0, c2, 1, st);
       return;

@@ -111,6 +111,35 @@ inline PlanLayout plan_layout(const dyra_spec& s, int dtype) {
   return L;
 }
 
+// Right-factor GEMM R^T [c2 x nr] (nr = B r, reduction over K = c1) in bf16:
+// when even 128 x 128 output tiles would leave most of a 256-CU chip idle,
+// K is cut into `slices` runs of `kslice` (a multiple of 64) whose fp32
+// partial products are summed afterwards.  slices == 1: a single pass.
+struct S5Split {
+  int slices = 1;
+  int64_t kslice = 0;
+};
+inline S5Split s5_split(int64_t c2, int64_t nr, int64_t K) {
+  S5Split sp;
+  sp.kslice = K;
+  const int64_t wide = ((c2 + 255) / 256) * ((nr + 127) / 128);
+  const int64_t tiles = ((c2 + 127) / 128) * ((nr + 127) / 128);
+  if (wide >= 256 || tiles >= 256) return sp;
+  // about two workgroups per CU; at least 256 of K per slice; the fp32
+  // partials (slices x nr x 4 bytes per output row) at most four times the
+  // W_res^T bytes (K x 2 per row).  Measured on MI355X: a 1024 x 2048
+  // output with K = 4096 gains with 4 slices (54 -> 42 us); a 1024 x 2048
+  // output with K = 1024, whose partials would be 16 times W_res^T, loses.
+  int64_t want = std::min<int64_t>((512 + tiles - 1) / tiles, 16);
+  want = std::min<int64_t>(want, std::max<int64_t>(1, K / 256));
+  want = std::min<int64_t>(want, 2 * K / std::max<int64_t>(nr, 1));
+  if (want <= 1) return sp;
+  sp.kslice = ((K + want - 1) / want + 63) / 64 * 64;
+  sp.slices = (int)((K + sp.kslice - 1) / sp.kslice);
+  if (sp.slices <= 1) sp.kslice = K;
+  return sp;
+}
+
 // ---- forward workspace -----------------------------------------------------
 // A    [n x wa]   stage-1 output: low-rank [T | L] (wa = k + r); Monarch
 //                 [V | L] (wa = c + r, V the permuted stage-1 output);
@@ -123,9 +152,10 @@ inline PlanLayout plan_layout(const dyra_spec& s, int dtype) {
 // Mp   [B x r x c1] dtype      M'_b = Ginv_b M_b
 // Rt   [c2 x B r] dtype        R_b^T for every segment, R_b = M'_b W_res
 // status [B] int32
+// Pk   [slices x c2 x B r] fp32  right-factor split-K partials (bf16 only)
 struct WsLayout {
   int64_t wa = 0;
-  size_t A = 0, Wp = 0, Lt = 0, G = 0, M = 0, Ginv = 0, Mp = 0, Rt = 0, status = 0;
+  size_t A = 0, Wp = 0, Lt = 0, G = 0, M = 0, Ginv = 0, Mp = 0, Rt = 0, status = 0, Pk = 0;
   // Gram partials [B][gchunks][r x r] fp32 over token chunks of gchunk tokens
   size_t Gp = 0;
   int64_t gchunk = 0, gchunks = 0;
@@ -163,6 +193,10 @@ inline WsLayout ws_layout(const dyra_spec& s, int64_t B, int64_t seg, int dtype,
   W.gchunks = (seg + W.gchunk - 1) / W.gchunk;
   // token-chunk partials, or two per 160-token first-stage tile
   W.Gp = take(std::max((size_t)B * (size_t)W.gchunks, ((n + 159) / 160) * 2) * r * r * 4);
+  if (dtype == DYRA_BF16) {
+    const S5Split sp = s5_split((int64_t)c2, B * (int64_t)r, (int64_t)c1);
+    if (sp.slices > 1) W.Pk = take((size_t)sp.slices * c2 * (size_t)B * r * 4);
+  }
   if (half_steps > 2) {
     W.R = take((size_t)B * r * c2 * e);
     W.K = take((size_t)B * r * r * 4);

@@ -31,6 +31,9 @@ SMALL = [
     sc(W["vitb_fc1"], name="one_small_tile", B=1, s=20, c1=64, c2=64, k=8, r=8),
     sc(W["vitb_fc1"], name="many_short_segments", B=37, s=13, c1=128, c2=136, k=16, r=8),
     sc(W["vitb_fc1"], name="wide_k", B=2, s=300, c1=512, c2=256, k=200, r=56),
+    # right factor split over K: 3 slices of 384, 384 and 232 (ragged), on a
+    # 200 x 32 output (ragged 128 x 128 tiles)
+    sc(W["vitb_fc1"], name="split_k_right_factor", B=2, s=100, c1=1000, c2=200, k=64, r=16),
     sc(W["vitl_fc1"], name="r128_ns", B=2, s=300, c1=256, c2=384, k=64, r=128, solver="ns"),
     # fp32 storage through Newton-Schulz: split-precision phase, then the
     # fp32 polish to its floor (the fp32 bar applies)
