@@ -2208,7 +2208,7 @@ __global__ __launch_bounds__(1024) void ns_polish_kernel(const float* G, float* 
 // L_b is ill-conditioned.
 // ===========================================================================
 
-// One wave per (segment, 16-row block of M', 64-column tile), on
+// One wave per (segment, RB 16-row blocks of M', 64-column tile), on
 // v_mfma_f32_16x16x4f32 with both operands read straight from memory.  The
 // reduction index is permuted so that each lane's operands are float4 runs:
 // in 16-wide chunk t, lane group g = lane / 16 holds q = 16 t + 4 g + e for
@@ -2217,9 +2217,10 @@ __global__ __launch_bounds__(1024) void ns_polish_kernel(const float* G, float* 
 // c0 + 4 (lane % 16) .. + 3).  MFMA e of column block jb therefore sums
 // over q = 16 t + e, + 4, + 8, + 12 and writes column c0 + 4 (lane % 16) + jb;
 // the accumulator of lane (i, g) holds rows 16 rb + 4 g .. + 3 of those
-// columns.  The next chunk is loaded before the current one is multiplied.
+// columns.  The RB row blocks of a wave share its M loads.  The next chunk
+// is loaded before the current one is multiplied.
 constexpr int AI_WAVES = 4;
-template <typename T>
+template <typename T, int RB>
 __global__ __launch_bounds__(64 * AI_WAVES) void apply_inverse_kernel(const float* __restrict__ Ginv,
                                                                       const float* __restrict__ M,
                                                                       T* __restrict__ Mp, int r, int64_t c1,
@@ -2227,68 +2228,89 @@ __global__ __launch_bounds__(64 * AI_WAVES) void apply_inverse_kernel(const floa
   const int lane = threadIdx.x & 63;
   const int64_t task = (int64_t)blockIdx.x * AI_WAVES + (threadIdx.x >> 6);
   if (task >= tasks) return;
-  const int nrb = (r + 15) >> 4;
+  const int ngr = (r + 16 * RB - 1) / (16 * RB);  // row-block groups
   const int64_t tiles = (c1 + 63) >> 6;
-  const int rb = (int)(task % nrb);             // the waves of a workgroup share an M tile
-  const int64_t ct = (task / nrb) % tiles, b = task / (nrb * tiles);
+  const int grp = (int)(task % ngr);            // the waves of a workgroup share an M tile
+  const int64_t ct = (task / ngr) % tiles, b = task / (ngr * tiles);
   const int i = lane & 15, g = lane >> 4;
   const float* Gb = Ginv + b * r * r;
   const float* Mb = M + b * r * c1;
   const int64_t col = ct * 64 + 4 * i;          // c1 % 8 == 0: all four columns or none
   const bool cok = col < c1;
-  const int row = rb * 16 + i;
   const int nt = (r + 15) >> 4;
-  auto load = [&](int t, float4& a, float4 (&m)[4]) {
+  auto load = [&](int t, float4 (&a)[RB], float4 (&m)[4]) {
     const int q0 = 16 * t + 4 * g;              // r % 4 == 0: all four q or none
-    a = (row < r && q0 < r) ? *reinterpret_cast<const float4*>(Gb + (int64_t)row * r + q0)
-                            : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int j = 0; j < RB; ++j) {
+      const int row = (grp * RB + j) * 16 + i;
+      a[j] = (row < r && q0 < r) ? *reinterpret_cast<const float4*>(Gb + (int64_t)row * r + q0)
+                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       m[e] = (cok && q0 < r) ? *reinterpret_cast<const float4*>(Mb + (int64_t)(q0 + e) * c1 + col)
                              : make_float4(0.f, 0.f, 0.f, 0.f);
   };
-  f32x4 acc[4];
+  f32x4 acc[RB][4];
 #pragma unroll
-  for (int jb = 0; jb < 4; ++jb) acc[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float4 a, m[4];
+  for (int j = 0; j < RB; ++j)
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) acc[j][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float4 a[RB], m[4];
   load(0, a, m);
   for (int t = 0; t < nt; ++t) {
-    float4 an, mn[4];
+    float4 an[RB], mn[4];
     if (t + 1 < nt) load(t + 1, an, mn);
-    const float av[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float mv[4] = {m[e].x, m[e].y, m[e].z, m[e].w};
 #pragma unroll
-      for (int jb = 0; jb < 4; ++jb) acc[jb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[e], mv[jb], acc[jb], 0, 0, 0);
+      for (int j = 0; j < RB; ++j) {
+        const float av = e == 0 ? a[j].x : e == 1 ? a[j].y : e == 2 ? a[j].z : a[j].w;
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) acc[j][jb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, mv[jb], acc[j][jb], 0, 0, 0);
+      }
     }
     if (t + 1 < nt) {
-      a = an;
+#pragma unroll
+      for (int j = 0; j < RB; ++j) a[j] = an[j];
 #pragma unroll
       for (int e = 0; e < 4; ++e) m[e] = mn[e];
     }
   }
   if (!cok) return;
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int orow = rb * 16 + 4 * g + v;
-    if (orow >= r) continue;
-    T* dst = Mp + (b * r + orow) * c1 + col;
-    if constexpr (TT<T>::ESZ == 2) {
-      uint2 pk;
-      pk.x = (uint32_t)f2bf(acc[0][v]) | ((uint32_t)f2bf(acc[1][v]) << 16);
-      pk.y = (uint32_t)f2bf(acc[2][v]) | ((uint32_t)f2bf(acc[3][v]) << 16);
-      *reinterpret_cast<uint2*>(dst) = pk;
-    } else {
-      *reinterpret_cast<float4*>(dst) = make_float4(acc[0][v], acc[1][v], acc[2][v], acc[3][v]);
+  for (int j = 0; j < RB; ++j)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int orow = (grp * RB + j) * 16 + 4 * g + v;
+      if (orow >= r) continue;
+      T* dst = Mp + (b * r + orow) * c1 + col;
+      if constexpr (TT<T>::ESZ == 2) {
+        uint2 pk;
+        pk.x = (uint32_t)f2bf(acc[j][0][v]) | ((uint32_t)f2bf(acc[j][1][v]) << 16);
+        pk.y = (uint32_t)f2bf(acc[j][2][v]) | ((uint32_t)f2bf(acc[j][3][v]) << 16);
+        *reinterpret_cast<uint2*>(dst) = pk;
+      } else {
+        *reinterpret_cast<float4*>(dst) = make_float4(acc[j][0][v], acc[j][1][v], acc[j][2][v], acc[j][3][v]);
+      }
     }
-  }
 }
 
-// grid for apply_inverse_kernel over B segments of r x c1
-inline void launch_apply_inverse_dims(int64_t B, int r, int64_t c1, int64_t& tasks, unsigned& blocks) {
-  tasks = B * ((r + 15) / 16) * ((c1 + 63) / 64);
-  blocks = (unsigned)((tasks + AI_WAVES - 1) / AI_WAVES);
+// M'_b = Ginv_b M_b for B segments of r x c1: four row blocks per wave when
+// that still leaves at least two waves per SIMD of a 256-CU chip, else one.
+template <typename T>
+void launch_apply_inverse(const float* Gi, const float* M, T* Mp, int64_t B, int r, int64_t c1, hipStream_t st) {
+  const int64_t tiles = (c1 + 63) / 64, nrb = (r + 15) / 16;
+  const int64_t wide = B * tiles * ((nrb + 3) / 4);
+  if (nrb >= 4 && wide >= 2048) {
+    hipLaunchKernelGGL((apply_inverse_kernel<T, 4>), dim3((unsigned)((wide + AI_WAVES - 1) / AI_WAVES)),
+                       dim3(64 * AI_WAVES), 0, st, Gi, M, Mp, r, c1, wide);
+  } else {
+    const int64_t tasks = B * tiles * nrb;
+    hipLaunchKernelGGL((apply_inverse_kernel<T, 1>), dim3((unsigned)((tasks + AI_WAVES - 1) / AI_WAVES)),
+                       dim3(64 * AI_WAVES), 0, st, Gi, M, Mp, r, c1, tasks);
+  }
 }
 
 // ===========================================================================
@@ -2461,12 +2483,7 @@ void forward_residual(const dyra_spec& s, const char* plan, const void* X, int64
       launch_sweep(G, Gi, stat, r, eps, B, false, st);
     }
   }
-  {
-    int64_t tasks;
-    unsigned blocks;
-    launch_apply_inverse_dims(B, r, c1, tasks, blocks);
-    hipLaunchKernelGGL(apply_inverse_kernel<T>, dim3(blocks), dim3(64 * AI_WAVES), 0, st, Gi, M, Mp, r, c1, tasks);
-  }
+  launch_apply_inverse<T>(Gi, M, Mp, B, r, c1, st);
   E.mark(3, st);
   // S5: R^T (c2 x B r) = W_res^T (c2 x c1) . M' (B r x c1)^T; bf16: split
   // over K when the output has few tiles, else the persistent output kernel
@@ -2522,13 +2539,7 @@ void left_step_bf16(const dyra_spec& s, const char* plan, const bf16_t* X, int64
   else if (r <= 32) launch_s3_bf16<2, 1>(R, c2, Wrt, c1, r, c2, nn, B, Qt, K, Kinv, kst, eps, true, st, r, true);
   else if (r <= 64) launch_s3_bf16<4, 2>(R, c2, Wrt, c1, r, c2, nn, B, Qt, K, Kinv, kst, eps, true, st, r, true);
   else launch_s3_bf16<8, 4>(R, c2, Wrt, c1, r, c2, nn, B, Qt, K, Kinv, kst, eps, true, st, r, true);
-  {
-    int64_t tasks;
-    unsigned blocks;
-    launch_apply_inverse_dims(B, r, c1, tasks, blocks);
-    hipLaunchKernelGGL(apply_inverse_kernel<bf16_t>, dim3(blocks), dim3(64 * AI_WAVES), 0, st, Kinv, Qt, Zt, r, c1,
-                       tasks);
-  }
+  launch_apply_inverse<bf16_t>(Kinv, Qt, Zt, B, r, c1, st);
   // L_b = X_b Z_b into [T | L] and L^T
   const int tiles_n = (int)cdiv(r, CfgL::BN);
   hipLaunchKernelGGL(s1_left_kernel<CfgL>, dim3((unsigned)(cdiv(n, CfgL::BM) * tiles_n)), dim3(CfgL::NT), 0, st, X,
