@@ -962,8 +962,19 @@ __global__ __launch_bounds__(256, 2) void s1_monarch_kernel(const bf16_t* __rest
     }
 }
 
-// Stage 2 fused with the residual correction and bias: a wave computes 32
-// rows x 128 output columns (4 blocks j): y_j = V_j B2_j + L R_b[:, j] + bias.
+// Stage 2 fused with the residual correction and bias: a workgroup computes
+// 128 rows x 128 output columns (4 blocks j), a wave 32 rows of them:
+// y_j = V_j B2_j + L R_b[:, j] + bias.  The workgroup's B2_j blocks and, one
+// segment at a time, its 128 columns of R_b^T are copied into LDS as whole
+// rows (a 16-byte-per-lane load then covers eight 128-byte lines instead of
+// one 32-byte piece of 32 rows), and the output tile is staged in LDS so that
+// each store writes four whole 256-byte row segments.  Row pitches of
+// 80 bytes (B2) and 2 r + 16 bytes (R^T) keep the 32-row fragment reads free
+// of bank conflicts.
+constexpr int S6M_B2P = MO * 2 + 16, S6M_YP = 128 * 2 + 16;
+constexpr int S6M_RT_OFF = 4 * MO * S6M_B2P;                       // after the B2 blocks
+constexpr int S6M_LDS = S6M_RT_OFF + 128 * (128 * 2 + 16);        // r <= 128
+static_assert(128 * S6M_YP <= S6M_LDS, "output staging fits");
 template <int RB>
 __global__ __launch_bounds__(256) void s6_monarch_kernel(const bf16_t* __restrict__ A,
                                                          const bf16_t* __restrict__ B2t,
@@ -971,14 +982,24 @@ __global__ __launch_bounds__(256) void s6_monarch_kernel(const bf16_t* __restric
                                                          const bf16_t* __restrict__ bias, bf16_t* __restrict__ Y,
                                                          int64_t n, int r, int64_t seg, int64_t B) {
   constexpr int C = MO * MO;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  __shared__ __attribute__((aligned(16))) char sm[S6M_LDS];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l = lane & 31, g = lane >> 5;
   const int tiles_n = C / 128;
-  const int64_t m0 = (int64_t)(blockIdx.x / tiles_n) * 128 + w * 32;
+  const int64_t mw = (int64_t)(blockIdx.x / tiles_n) * 128;        // the workgroup's first row
+  const int64_t m0 = mw + w * 32;
   const int j0 = (blockIdx.x % tiles_n) * 4;
   const int64_t row = m0 + l;
   const bool rok = row < n;
   const int64_t lda = C + r;
+  const int RP = r * 2 + 16;                                       // R^T row pitch in LDS
+  // B2t rows (j, l) for j = j0 .. j0 + 3: one contiguous 8 KB run
+  for (int q = tid; q < 4 * MO * (MO / 8); q += 256) {
+    const int rr = q / (MO / 8), u = q % (MO / 8);
+    *reinterpret_cast<uint4*>(sm + rr * S6M_B2P + u * 16) =
+        *reinterpret_cast<const uint4*>(B2t + ((int64_t)j0 * MO + rr) * MO + u * 8);
+  }
+  __syncthreads();
   f32x16 acc[4];
 #pragma unroll
   for (int jb = 0; jb < 4; ++jb)
@@ -991,41 +1012,60 @@ __global__ __launch_bounds__(256) void s6_monarch_kernel(const bf16_t* __restric
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const uint4 va = rok ? *reinterpret_cast<const uint4*>(A + row * lda + j * MO + 16 * s + 8 * g) : zero4();
-      const uint4 b2 = *reinterpret_cast<const uint4*>(B2t + ((int64_t)j * MO + l) * MO + 16 * s + 8 * g);
+      const uint4 b2 = *reinterpret_cast<const uint4*>(sm + (jb * MO + l) * S6M_B2P + (16 * s + 8 * g) * 2);
       TT<bf16_t>::mma(acc[jb], b2, va);
     }
   }
-  // L R_b for every segment overlapping this wave's 32 rows
-  if (m0 < n) {
-    const int64_t bf = m0 / seg, bl = imin64(B - 1, (imin64(m0 + 32, n) - 1) / seg);
-    for (int64_t b = bf; b <= bl; ++b) {
-      const bool in = rok && row >= b * seg && row < (b + 1) * seg;
-      for (int k0 = 0; k0 < r; k0 += 16) {
-        const int kk = k0 + 8 * g;
-        const uint4 la = (in && kk < r) ? *reinterpret_cast<const uint4*>(A + row * lda + C + kk) : zero4();
+  // L R_b for every segment overlapping the workgroup's 128 rows
+  const int64_t wend = imin64(mw + 128, n);
+  const int64_t bf = mw / seg, bl = imin64(B - 1, (wend - 1) / seg);
+  const int ru = r / 8;                                            // 16-byte runs per R^T row
+  for (int64_t b = bf; b <= bl; ++b) {
+    __syncthreads();                                               // the previous R^T block is read
+    for (int q = tid; q < 128 * ru; q += 256) {
+      const int c = q / ru, u = q - c * ru;
+      *reinterpret_cast<uint4*>(sm + S6M_RT_OFF + c * RP + u * 16) =
+          *reinterpret_cast<const uint4*>(Rt + ((int64_t)j0 * MO + c) * (B * r) + b * r + u * 8);
+    }
+    __syncthreads();
+    if (m0 >= wend || m0 + 32 <= b * seg || m0 >= (b + 1) * seg) continue;   // wave-uniform
+    const bool in = rok && row >= b * seg && row < (b + 1) * seg;
+    for (int k0 = 0; k0 < r; k0 += 16) {
+      const int kk = k0 + 8 * g;
+      const uint4 la = (in && kk < r) ? *reinterpret_cast<const uint4*>(A + row * lda + C + kk) : zero4();
 #pragma unroll
-        for (int jb = 0; jb < 4; ++jb) {
-          const int64_t col = (int64_t)(j0 + jb) * MO + l;
-          const uint4 rt = kk < r ? *reinterpret_cast<const uint4*>(Rt + col * (B * r) + b * r + kk) : zero4();
-          TT<bf16_t>::mma(acc[jb], rt, la);
-        }
+      for (int jb = 0; jb < 4; ++jb) {
+        const uint4 rt = kk < r ? *reinterpret_cast<const uint4*>(sm + S6M_RT_OFF + (jb * MO + l) * RP + kk * 2)
+                                : zero4();
+        TT<bf16_t>::mma(acc[jb], rt, la);
       }
     }
   }
-  if (!rok) return;
+  __syncthreads();                                                 // LDS free for the output tile
+  // accumulator (jb) element 4 q + e: row l, column 32 jb + 8 q + 4 g + e
 #pragma unroll
   for (int jb = 0; jb < 4; ++jb)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int col = (j0 + jb) * MO + 8 * q + 4 * g;
+      const int cl = jb * MO + 8 * q + 4 * g;
       float v[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = acc[jb][4 * q + e] + (bias ? bf2f(bias[col + e]) : 0.f);
+      for (int e = 0; e < 4; ++e) v[e] = acc[jb][4 * q + e] + (bias ? bf2f(bias[j0 * MO + cl + e]) : 0.f);
       uint2 pk;
       pk.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
       pk.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
-      *reinterpret_cast<uint2*>(Y + row * C + col) = pk;
+      *reinterpret_cast<uint2*>(sm + (w * 32 + l) * S6M_YP + cl * 2) = pk;
     }
+  __syncthreads();
+  // this wave's 32 rows: 16 lanes per 256-byte row segment, 4 rows per store
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int rl = i * 4 + (lane >> 4), ch = lane & 15;
+    const int64_t yr = m0 + rl;
+    if (yr < n)
+      *reinterpret_cast<uint4*>(Y + yr * C + j0 * MO + ch * 8) =
+          *reinterpret_cast<const uint4*>(sm + (w * 32 + rl) * S6M_YP + ch * 16);
+  }
 }
 
 // ===========================================================================
