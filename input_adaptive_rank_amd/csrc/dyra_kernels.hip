@@ -868,19 +868,21 @@ __global__ __launch_bounds__(C::NT) void s1_left_kernel(const bf16_t* X, const b
 // Monarch static branch (m = 32 blocks of 32 x 32, c = 1024), bf16.
 // W_hat = blockdiag(B1_a) . Pi . blockdiag(B2_j), Pi the reshape(32, 32)
 // transpose: u_a = x_a B1_a, v[j*32 + a] = u[a*32 + j], y_j = v_j B2_j.
-// Both kernels feed the MFMA straight from global memory (each 32 x 32
-// operand block is one 16-byte load per lane per k-step) -- the work is
-// bound by streaming X, V and Y, not by the tiny block products.
+// The block products are tiny: both kernels are bound by the vector-memory
+// address path and by streaming X, V and Y, so weights come in fragment order
+// or through LDS and V and Y leave as whole rows.
 // ===========================================================================
 
 constexpr int MO = 32;
 
 // Stage 1 + L: one pass over X.  A workgroup owns 32 rows; wave w takes the
-// 8 blocks a = 8w .. 8w + 7: it accumulates U_a (32 x 32 each), writes the
-// permuted V[row][j*32 + 8w .. 8w + 7] as one 16-byte store per (row, j), and
-// accumulates its K slice (a*32 .. a*32 + 31 for its 8 blocks) of L = X P.
-// The four partial L sums are added through LDS in a fixed order; wave 0
-// writes L and L^T.
+// 8 blocks a = 8w .. 8w + 7: it accumulates U_a (32 x 32 each), puts the
+// permuted V[row][j*32 + 8w .. 8w + 7] into an LDS copy of the 32 V rows
+// (written out as whole rows), and accumulates its K slice (a*32 .. a*32 + 31
+// for its 8 blocks) of L = X P.  B1t and Pt are in fragment order: a wave's
+// operand of one MFMA step is one contiguous 1 KB run.  The four partial L
+// sums are added through LDS in a fixed order; wave 0 writes L and L^T.
+constexpr int S1M_VP = MO * MO * 2 + 16;                  // V row pitch in LDS (bytes)
 template <int RB>
 __global__ __launch_bounds__(256, 2) void s1_monarch_kernel(const bf16_t* __restrict__ X,
                                                          const bf16_t* __restrict__ B1t,
@@ -888,7 +890,9 @@ __global__ __launch_bounds__(256, 2) void s1_monarch_kernel(const bf16_t* __rest
                                                          bf16_t* __restrict__ A, bf16_t* __restrict__ Lt,
                                                          int64_t n, int r, int64_t ldt) {
   constexpr int C = MO * MO;
-  __shared__ float part[3][RB][16][64];
+  static_assert(3 * RB * 16 * 64 * 4 <= 32 * S1M_VP, "L partials fit the V staging");
+  __shared__ __attribute__((aligned(16))) char sm[32 * S1M_VP];
+  float* part = reinterpret_cast<float*>(sm);             // [3][RB][16][64], after V is written out
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int l = lane & 31, g = lane >> 5;
   const int64_t row = (int64_t)blockIdx.x * 32 + l;
@@ -909,43 +913,53 @@ __global__ __launch_bounds__(256, 2) void s1_monarch_kernel(const bf16_t* __rest
     for (int s = 0; s < 2; ++s) {
       const int kk = a * MO + 16 * s + 8 * g;
       const uint4 xa = rok ? *reinterpret_cast<const uint4*>(X + row * C + kk) : zero4();
-      const uint4 b1 = *reinterpret_cast<const uint4*>(B1t + ((int64_t)a * MO + l) * MO + 16 * s + 8 * g);
+      const uint4 b1 = *reinterpret_cast<const uint4*>(B1t + ((a * 2 + s) * 64 + lane) * 8);
       TT<bf16_t>::mma(uacc[ai], b1, xa);
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         const int p = rb * 32 + l;
-        const uint4 pb = p < r ? *reinterpret_cast<const uint4*>(Pt + (int64_t)p * C + kk) : zero4();
+        const uint4 pb =
+            p < r ? *reinterpret_cast<const uint4*>(Pt + ((int64_t)((rb * MO + a) * 2 + s) * 64 + lane) * 8) : zero4();
         TT<bf16_t>::mma(lacc[rb], pb, xa);
       }
     }
   }
-  if (rok) {
-    // lane holds U[row][a*32 + j] for j = 8q + 4g + e (reg 4q + e), a = 8w + ai
+  // lane holds U[row][a*32 + j] for j = 8q + 4g + e (reg 4q + e), a = 8w + ai
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+  for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = 8 * q + 4 * g + e;
-        uint32_t pk[4];
+    for (int e = 0; e < 4; ++e) {
+      const int j = 8 * q + 4 * g + e;
+      uint32_t pk[4];
 #pragma unroll
-        for (int h = 0; h < 4; ++h)
-          pk[h] = (uint32_t)f2bf(uacc[2 * h][4 * q + e]) | ((uint32_t)f2bf(uacc[2 * h + 1][4 * q + e]) << 16);
-        *reinterpret_cast<uint4*>(A + row * lda + j * MO + w * 8) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-      }
+      for (int h = 0; h < 4; ++h)
+        pk[h] = (uint32_t)f2bf(uacc[2 * h][4 * q + e]) | ((uint32_t)f2bf(uacc[2 * h + 1][4 * q + e]) << 16);
+      *reinterpret_cast<uint4*>(sm + l * S1M_VP + (j * MO + w * 8) * 2) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    }
+  __syncthreads();
+  // the 32 V rows: 128 runs of 16 bytes each, a wave instruction 1 KB of one row
+  for (int c = threadIdx.x; c < 32 * (C / 8); c += 256) {
+    const int rl = c / (C / 8), ch = c % (C / 8);
+    const int64_t vr = (int64_t)blockIdx.x * 32 + rl;
+    if (vr < n)
+      *reinterpret_cast<uint4*>(A + vr * lda + ch * 8) = *reinterpret_cast<const uint4*>(sm + rl * S1M_VP + ch * 16);
   }
+  __syncthreads();
   // L partials: waves 1..3 -> LDS, wave 0 adds them in order
   if (w > 0) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) part[w - 1][rb][v][lane] = lacc[rb][v];
+      for (int v = 0; v < 16; ++v) part[(((w - 1) * RB + rb) * 16 + v) * 64 + lane] = lacc[rb][v];
   }
   __syncthreads();
   if (w != 0 || !rok) return;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) lacc[rb][v] = ((lacc[rb][v] + part[0][rb][v][lane]) + part[1][rb][v][lane]) + part[2][rb][v][lane];
+    for (int v = 0; v < 16; ++v)
+      lacc[rb][v] = ((lacc[rb][v] + part[((0 * RB + rb) * 16 + v) * 64 + lane]) + part[((1 * RB + rb) * 16 + v) * 64 + lane]) +
+                    part[((2 * RB + rb) * 16 + v) * 64 + lane];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll

@@ -260,15 +260,21 @@ extern "C" int dyra_plan_pack(const dyra_spec* spec, const dyra_host_factors* f,
   } else if (s.kind == DYRA_MONARCH) {
     if (!f->B1 || !f->B2) return DYRA_EINVAL;
     const int64_t m = s.mblk;
+    // fragment order (m = 32): element k = 16 s + 8 g + e of the reduction,
+    // output column l, lane l + 32 g of 32x32x16 step s
+    auto frag = [](int64_t blk, int64_t k, int64_t l) {
+      return (size_t)(((blk * 2 + k / 16) * 64 + l + 32 * ((k / 8) % 2)) * 8 + k % 8);
+    };
     for (int64_t a = 0; a < m; ++a)
       for (int64_t i = 0; i < m; ++i)
         for (int64_t j = 0; j < m; ++j) {
-          put(host_plan, L.B1t, (size_t)((a * m + j) * m + i), f->B1[(a * m + i) * m + j], dtype);
+          put(host_plan, L.B1t, frag(a, i, j), f->B1[(a * m + i) * m + j], dtype);
           // B2 block a plays the role of j here: B2t[a][l=j][row=i] = B2[a][i][j]
           put(host_plan, L.B2t, (size_t)((a * m + j) * m + i), f->B2[(a * m + i) * m + j], dtype);
         }
     for (int64_t p = 0; p < r; ++p)
-      for (int64_t i = 0; i < c1; ++i) put(host_plan, L.Pt, (size_t)(p * c1 + i), f->P[i * r + p], dtype);
+      for (int64_t i = 0; i < c1; ++i)
+        put(host_plan, L.Pt, frag((p / 32) * m + i / m, i % m, p % 32), f->P[i * r + p], dtype);
   } else {
     if (!f->Ub || !f->S || !f->Vb) return DYRA_EINVAL;
     const int64_t nb = s.nb, rb = s.rb, b1 = c1 / nb, b2 = c2 / nb;

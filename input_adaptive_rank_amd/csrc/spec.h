@@ -57,7 +57,11 @@ inline int validate_dtype(const dyra_spec& s, int dtype) {
 //            For the 160 x 320 first-stage tile (bf16, k + r = 320, c1 a
 //            multiple of 64) UPt is stored k-tile-major instead: 32-column
 //            k-tiles, each a contiguous [(k+r) x 32] block.
-// Monarch  : B1t [m][m][m] (B1t[a][j][i] = B1[a][i][j]), Pt [r x c],
+// Monarch  : B1t and Pt in MFMA fragment order (each 16-byte run one lane's
+//            operand of one 32x32x16 step, the 64 lanes of a step one 1 KB
+//            run): B1t[((a 2 + s) 64 + l + 32 g) 8 + e] = B1[a][16 s + 8 g + e][l],
+//            Pt[(((q 32 + a) 2 + s) 64 + l + 32 g) 8 + e] = P[32 a + 16 s + 8 g + e][32 q + l]
+//            (zero for 32 q + l >= r; r rounded up to a multiple of 32 rows);
 //            B2t [m][m][m] (B2t[j][l][a] = B2[j][a][l]), Wrt [c x c]
 // BLAST    : Ubt [nb][rb][c1/nb] (U_i^T), Pt [r x c1],
 //            St [(nb rb) x (nb rb)] (St[j rb + q][i rb + p] = S[i][j][p][q]),
@@ -97,7 +101,7 @@ inline PlanLayout plan_layout(const dyra_spec& s, int dtype) {
   } else if (s.kind == DYRA_MONARCH) {
     const size_t m = (size_t)s.mblk;
     L.B1t = take(m * m * m);
-    L.Pt = take(r * c1);
+    L.Pt = take((r + 31) / 32 * 32 * c1);
     L.B2t = take(m * m * m);
   } else {
     const size_t nb = (size_t)s.nb, rb = (size_t)s.rb;

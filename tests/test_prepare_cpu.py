@@ -131,6 +131,29 @@ def test_plan_pack_tiled_upt():
     np.testing.assert_array_equal(vals32[:(k + r) * c1].reshape(k + r, c1), synth.round_f32(UPt))
 
 
+def test_plan_pack_monarch_fragment_order():
+    """Monarch bf16 plans hold B1 and P in MFMA fragment order: the 16-byte
+    run of lane l + 32 g in step s of block a holds rows 16 s + 8 g .. + 7 of
+    column l (P: of column 32 q + l, zero past r; r padded to 32 rows)."""
+    m, r = 32, 40
+    c = m * m
+    spec = D.make_spec(synth.KIND_MONARCH, c, c, r, mblk=m)
+    rng = np.random.default_rng(5)
+    f = {"B1": rng.standard_normal((m, m, m)), "B2": rng.standard_normal((m, m, m)),
+         "P": rng.standard_normal((c, r)), "Wres": rng.standard_normal((c, c))}
+    vals = synth.bf16_to_f64(D.plan_pack(spec, f, synth.DT_BF16).view(np.uint16))
+    b1 = vals[:m * m * m].reshape(m, 2, 2, m, 8)          # [a][s][g][l][e]
+    want = _bf16(f["B1"]).reshape(m, 2, 2, 8, m).transpose(0, 1, 2, 4, 3)
+    np.testing.assert_array_equal(b1, want)
+    off = (m * m * m * 2 + 255) // 256 * 256 // 2
+    nq = (r + 31) // 32
+    pt = vals[off:off + nq * 32 * c].reshape(nq, m, 2, 2, 32, 8)   # [q][a][s][g][l][e]
+    Ppad = np.zeros((c, nq * 32))
+    Ppad[:, :r] = f["P"]
+    want = _bf16(Ppad).reshape(m, 2, 2, 8, nq, 32).transpose(4, 0, 1, 2, 5, 3)
+    np.testing.assert_array_equal(pt, want)
+
+
 def test_bf16_rounding_of_pack_matches_generator_rounding():
     """Library rounding (fp64 -> fp32 -> bf16, RNE) equals the generator's."""
     rng = np.random.default_rng(3)
