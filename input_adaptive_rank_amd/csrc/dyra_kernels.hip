@@ -2271,10 +2271,12 @@ __global__ __launch_bounds__(1024) void ns_polish_kernel(const float* G, float* 
 // c0 + 4 (lane % 16) .. + 3).  MFMA e of column block jb therefore sums
 // over q = 16 t + e, + 4, + 8, + 12 and writes column c0 + 4 (lane % 16) + jb;
 // the accumulator of lane (i, g) holds rows 16 rb + 4 g .. + 3 of those
-// columns.  The RB row blocks of a wave share its M loads.  The next chunk
-// is loaded before the current one is multiplied.
+// columns.  The RB row blocks of a wave share its M loads.  With NTC > 0
+// (r <= 16 NTC) every chunk is loaded before the first product, so a wave
+// waits on memory once; otherwise the next chunk is loaded before the
+// current one is multiplied.
 constexpr int AI_WAVES = 4;
-template <typename T, int RB>
+template <typename T, int RB, int NTC = 0>
 __global__ __launch_bounds__(64 * AI_WAVES) void apply_inverse_kernel(const float* __restrict__ Ginv,
                                                                       const float* __restrict__ M,
                                                                       T* __restrict__ Mp, int r, int64_t c1,
@@ -2310,11 +2312,7 @@ __global__ __launch_bounds__(64 * AI_WAVES) void apply_inverse_kernel(const floa
   for (int j = 0; j < RB; ++j)
 #pragma unroll
     for (int jb = 0; jb < 4; ++jb) acc[j][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float4 a[RB], m[4];
-  load(0, a, m);
-  for (int t = 0; t < nt; ++t) {
-    float4 an[RB], mn[4];
-    if (t + 1 < nt) load(t + 1, an, mn);
+  auto mul = [&](const float4 (&a)[RB], const float4 (&m)[4]) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float mv[4] = {m[e].x, m[e].y, m[e].z, m[e].w};
@@ -2325,12 +2323,27 @@ __global__ __launch_bounds__(64 * AI_WAVES) void apply_inverse_kernel(const floa
         for (int jb = 0; jb < 4; ++jb) acc[j][jb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, mv[jb], acc[j][jb], 0, 0, 0);
       }
     }
+  };
+  if constexpr (NTC > 0) {
+    float4 a[NTC][RB], m[NTC][4];                // chunks past r load as zeros
+#pragma unroll
+    for (int t = 0; t < NTC; ++t) load(t, a[t], m[t]);
+#pragma unroll
+    for (int t = 0; t < NTC; ++t) mul(a[t], m[t]);
+  } else {
+  float4 a[RB], m[4];
+  load(0, a, m);
+  for (int t = 0; t < nt; ++t) {
+    float4 an[RB], mn[4];
+    if (t + 1 < nt) load(t + 1, an, mn);
+    mul(a, m);
     if (t + 1 < nt) {
 #pragma unroll
       for (int j = 0; j < RB; ++j) a[j] = an[j];
 #pragma unroll
       for (int e = 0; e < 4; ++e) m[e] = mn[e];
     }
+  }
   }
   if (!cok) return;
 #pragma unroll
@@ -2362,8 +2375,13 @@ void launch_apply_inverse(const float* Gi, const float* M, T* Mp, int64_t B, int
                        dim3(64 * AI_WAVES), 0, st, Gi, M, Mp, r, c1, wide);
   } else {
     const int64_t tasks = B * tiles * nrb;
-    hipLaunchKernelGGL((apply_inverse_kernel<T, 1>), dim3((unsigned)((tasks + AI_WAVES - 1) / AI_WAVES)),
-                       dim3(64 * AI_WAVES), 0, st, Gi, M, Mp, r, c1, tasks);
+    const dim3 grid((unsigned)((tasks + AI_WAVES - 1) / AI_WAVES)), block(64 * AI_WAVES);
+    if (r <= 32)
+      hipLaunchKernelGGL((apply_inverse_kernel<T, 1, 2>), grid, block, 0, st, Gi, M, Mp, r, c1, tasks);
+    else if (r <= 64)
+      hipLaunchKernelGGL((apply_inverse_kernel<T, 1, 4>), grid, block, 0, st, Gi, M, Mp, r, c1, tasks);
+    else
+      hipLaunchKernelGGL((apply_inverse_kernel<T, 1>), grid, block, 0, st, Gi, M, Mp, r, c1, tasks);
   }
 }
 
