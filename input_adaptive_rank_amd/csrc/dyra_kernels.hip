@@ -140,6 +140,50 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   *reinterpret_cast<uint4*>(out + i) = pk;
 }
 
+// L = bf16(sum over z < slices of P[z][t][p]) for 64 tokens per workgroup
+// (r <= 128): rows into L (pitch ldo) for t < n, and L^T (pitch ldt) through
+// an LDS transpose for t < ldt, tokens past n as zeros.
+__global__ __launch_bounds__(256) void splitk_reduce_lt_kernel(const float* __restrict__ P, int slices, int64_t n,
+                                                               int r, bf16_t* __restrict__ L, int64_t ldo,
+                                                               bf16_t* __restrict__ Lt, int64_t ldt) {
+  __shared__ __attribute__((aligned(16))) bf16_t tr[128][64 + 8];
+  const int64_t t0 = (int64_t)blockIdx.x * 64;
+  const int ru = r / 8;
+  for (int q = threadIdx.x; q < 64 * ru; q += 256) {
+    const int tl = q / ru, p0 = (q - tl * ru) * 8;
+    const int64_t t = t0 + tl;
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (t < n) {
+      for (int z = 0; z < slices; ++z) {
+        const float* src = P + ((int64_t)z * n + t) * r + p0;
+        const float4 a = *reinterpret_cast<const float4*>(src), b = *reinterpret_cast<const float4*>(src + 4);
+        v[0] += a.x;
+        v[1] += a.y;
+        v[2] += a.z;
+        v[3] += a.w;
+        v[4] += b.x;
+        v[5] += b.y;
+        v[6] += b.z;
+        v[7] += b.w;
+      }
+    }
+    bf16_t h[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      h[e] = f2bf(v[e]);
+      tr[p0 + e][tl] = h[e];
+    }
+    if (t < n) *reinterpret_cast<uint4*>(L + t * ldo + p0) = *reinterpret_cast<const uint4*>(h);
+  }
+  __syncthreads();
+  // L^T rows p: 64 tokens = 8 runs of 16 bytes
+  for (int q = threadIdx.x; q < r * 8; q += 256) {
+    const int p = q >> 3, u = q & 7;
+    if (t0 + u * 8 < ldt)
+      *reinterpret_cast<uint4*>(Lt + (int64_t)p * ldt + t0 + u * 8) = *reinterpret_cast<const uint4*>(&tr[p][u * 8]);
+  }
+}
+
 // ===========================================================================
 // S1 (low-rank): [T | L] = X [U_f | P], plus L^T (token-contiguous) for S3
 // ===========================================================================
@@ -2748,9 +2792,20 @@ int forward_blast(const dyra_spec& s, const char* plan, const void* X, const voi
   {
     const int tiles_n = (int)cdiv(r, CfgB::BN);
     const int64_t tiles = cdiv(n, CfgB::BM) * tiles_n;
-    hipLaunchKernelGGL(s1_lowrank_kernel<CfgB>, dim3((unsigned)tiles), dim3(CfgB::NT), 0, st, Xb,
-                       reinterpret_cast<const bf16_t*>(plan + PL.Pt), ZL + NR, Lt, n, c1, 0, r, lt_pitch(n), tiles_n,
-                       ldzl);
+    // L = X P has r columns only: split over K when its tiles are few
+    const S5Split sl = s5_split(n, r, c1);
+    if (sl.slices > 1) {
+      float* Pk = reinterpret_cast<float*>(ws + WL.Pk);
+      hipLaunchKernelGGL(gemm_tn_splitk_kernel<CfgB>, dim3((unsigned)(tiles * sl.slices)), dim3(CfgB::NT), 0, st,
+                         reinterpret_cast<const char*>(Xb), c1 * 2, plan + PL.Pt, c1 * 2, Pk, n, (int64_t)r, c1,
+                         sl.kslice, tiles_n, (int)tiles);
+      hipLaunchKernelGGL(splitk_reduce_lt_kernel, dim3((unsigned)cdiv(lt_pitch(n), 64)), dim3(256), 0, st, Pk,
+                         sl.slices, n, r, ZL + NR, ldzl, Lt, lt_pitch(n));
+    } else {
+      hipLaunchKernelGGL(s1_lowrank_kernel<CfgB>, dim3((unsigned)tiles), dim3(CfgB::NT), 0, st, Xb,
+                         reinterpret_cast<const bf16_t*>(plan + PL.Pt), ZL + NR, Lt, n, c1, 0, r, lt_pitch(n),
+                         tiles_n, ldzl);
+    }
   }
   E.mark(1, st);
   forward_residual<CfgB, CfgB3>(s, plan, X, B, seg, eps, solver, ws, st, E);

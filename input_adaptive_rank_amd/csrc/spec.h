@@ -156,7 +156,8 @@ inline S5Split s5_split(int64_t c2, int64_t nr, int64_t K) {
 // Mp   [B x r x c1] dtype      M'_b = Ginv_b M_b
 // Rt   [c2 x B r] dtype        R_b^T for every segment, R_b = M'_b W_res
 // status [B] int32
-// Pk   [slices x c2 x B r] fp32  right-factor split-K partials (bf16 only)
+// Pk   [slices x c2 x B r] fp32  right-factor split-K partials (bf16 only);
+//      BLAST also [slices x n x r] for L = X P split over K
 struct WsLayout {
   int64_t wa = 0;
   size_t A = 0, Wp = 0, Lt = 0, G = 0, M = 0, Ginv = 0, Mp = 0, Rt = 0, status = 0, Pk = 0;
@@ -198,8 +199,14 @@ inline WsLayout ws_layout(const dyra_spec& s, int64_t B, int64_t seg, int dtype,
   // token-chunk partials, or two per 160-token first-stage tile
   W.Gp = take(std::max((size_t)B * (size_t)W.gchunks, ((n + 159) / 160) * 2) * r * r * 4);
   if (dtype == DYRA_BF16) {
+    // shared by the right factor and (BLAST) L = X P, which never overlap
     const S5Split sp = s5_split((int64_t)c2, B * (int64_t)r, (int64_t)c1);
-    if (sp.slices > 1) W.Pk = take((size_t)sp.slices * c2 * (size_t)B * r * 4);
+    size_t pk = sp.slices > 1 ? (size_t)sp.slices * c2 * (size_t)B * r * 4 : 0;
+    if (s.kind == DYRA_BLAST) {
+      const S5Split sl = s5_split((int64_t)n, (int64_t)r, (int64_t)c1);
+      if (sl.slices > 1) pk = std::max(pk, (size_t)sl.slices * n * r * 4);
+    }
+    if (pk) W.Pk = take(pk);
   }
   if (half_steps > 2) {
     W.R = take((size_t)B * r * c2 * e);
