@@ -140,20 +140,22 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   *reinterpret_cast<uint4*>(out + i) = pk;
 }
 
-// L = bf16(sum over z < slices of P[z][t][p]) for 64 tokens per workgroup
+// L = bf16(sum over z < slices of P[z][t][p]) for SRL_T tokens per workgroup
 // (r <= 128): rows into L (pitch ldo) for t < n, and L^T (pitch ldt) through
 // an LDS transpose for t < ldt, tokens past n as zeros.
+constexpr int SRL_T = 16;
 __global__ __launch_bounds__(256) void splitk_reduce_lt_kernel(const float* __restrict__ P, int slices, int64_t n,
                                                                int r, bf16_t* __restrict__ L, int64_t ldo,
                                                                bf16_t* __restrict__ Lt, int64_t ldt) {
-  __shared__ __attribute__((aligned(16))) bf16_t tr[128][64 + 8];
-  const int64_t t0 = (int64_t)blockIdx.x * 64;
+  __shared__ __attribute__((aligned(16))) bf16_t tr[128][SRL_T + 8];
+  const int64_t t0 = (int64_t)blockIdx.x * SRL_T;
   const int ru = r / 8;
-  for (int q = threadIdx.x; q < 64 * ru; q += 256) {
+  for (int q = threadIdx.x; q < SRL_T * ru; q += 256) {
     const int tl = q / ru, p0 = (q - tl * ru) * 8;
     const int64_t t = t0 + tl;
     float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (t < n) {
+#pragma unroll 4
       for (int z = 0; z < slices; ++z) {
         const float* src = P + ((int64_t)z * n + t) * r + p0;
         const float4 a = *reinterpret_cast<const float4*>(src), b = *reinterpret_cast<const float4*>(src + 4);
@@ -176,9 +178,9 @@ __global__ __launch_bounds__(256) void splitk_reduce_lt_kernel(const float* __re
     if (t < n) *reinterpret_cast<uint4*>(L + t * ldo + p0) = *reinterpret_cast<const uint4*>(h);
   }
   __syncthreads();
-  // L^T rows p: 64 tokens = 8 runs of 16 bytes
-  for (int q = threadIdx.x; q < r * 8; q += 256) {
-    const int p = q >> 3, u = q & 7;
+  // L^T rows p: SRL_T tokens in runs of 16 bytes
+  for (int q = threadIdx.x; q < r * (SRL_T / 8); q += 256) {
+    const int p = q / (SRL_T / 8), u = q % (SRL_T / 8);
     if (t0 + u * 8 < ldt)
       *reinterpret_cast<uint4*>(Lt + (int64_t)p * ldt + t0 + u * 8) = *reinterpret_cast<const uint4*>(&tr[p][u * 8]);
   }
@@ -2799,7 +2801,7 @@ int forward_blast(const dyra_spec& s, const char* plan, const void* X, const voi
       hipLaunchKernelGGL(gemm_tn_splitk_kernel<CfgB>, dim3((unsigned)(tiles * sl.slices)), dim3(CfgB::NT), 0, st,
                          reinterpret_cast<const char*>(Xb), c1 * 2, plan + PL.Pt, c1 * 2, Pk, n, (int64_t)r, c1,
                          sl.kslice, tiles_n, (int)tiles);
-      hipLaunchKernelGGL(splitk_reduce_lt_kernel, dim3((unsigned)cdiv(lt_pitch(n), 64)), dim3(256), 0, st, Pk,
+      hipLaunchKernelGGL(splitk_reduce_lt_kernel, dim3((unsigned)cdiv(lt_pitch(n), SRL_T)), dim3(256), 0, st, Pk,
                          sl.slices, n, r, ZL + NR, ldzl, Lt, lt_pitch(n));
     } else {
       hipLaunchKernelGGL(s1_lowrank_kernel<CfgB>, dim3((unsigned)tiles), dim3(CfgB::NT), 0, st, Xb,
