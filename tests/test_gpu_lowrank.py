@@ -34,6 +34,11 @@ SMALL = [
     # right factor split over K: 3 slices of 384, 384 and 232 (ragged), on a
     # 200 x 32 output (ragged 128 x 128 tiles)
     sc(W["vitb_fc1"], name="split_k_right_factor", B=2, s=100, c1=1000, c2=200, k=64, r=16),
+    # M' = Ginv M with four 16-row blocks per wave (32 segments x 64 column
+    # tiles) and r = 56 (the last block ragged); right factor in 4 K slices
+    sc(W["vitb_fc1"], name="apply_four_blocks_ragged_r", B=32, s=64, c1=4096, c2=256, k=64, r=56),
+    # r = 40: reduction chunks past r load as zeros in the load-all path
+    sc(W["vitb_fc1"], name="apply_r40", B=3, s=77, c1=192, c2=200, k=24, r=40),
     sc(W["vitl_fc1"], name="r128_ns", B=2, s=300, c1=256, c2=384, k=64, r=128, solver="ns"),
     # fp32 storage through Newton-Schulz: split-precision phase, then the
     # fp32 polish to its floor (the fp32 bar applies)
