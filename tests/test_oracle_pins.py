@@ -75,6 +75,24 @@ def test_hand_worked_blast(case):
     np.testing.assert_allclose(O.blast_apply(X, f), np.array(case["Y"], float), atol=1e-12)
 
 
+@pytest.mark.parametrize("case", _golden()["als"], ids=lambda c: c["name"])
+def test_hand_worked_als(case):
+    """More ALS half-steps on the diag3 example (t = 1.5: L, R, L; t = 2:
+    L, R, L, R), values derived by hand.  The sign of R0 is free, so the
+    factors are compared up to one common sign; Y is sign free."""
+    X = np.array(case["X"], float)
+    W = np.array(case["W"], float)
+    prep = _prep_lowrank(W, case["k"], case["r"])
+    Y = O.forward(X, prep, None, 1, X.shape[0], eps=case["eps"], t=case["t"])
+    np.testing.assert_allclose(Y, np.array(case["Y"], float), rtol=0, atol=1e-12)
+    L, R = O.als(X, prep["W_res"], prep["R0"], case["t"], case["eps"], P=prep["P"])
+    for name, got in (("L", L[:, 0]), ("R", R[0])):
+        if name in case:
+            want = np.array(case[name], float)
+            sgn = np.sign(got[np.argmax(np.abs(want))]) * np.sign(want[np.argmax(np.abs(want))])
+            np.testing.assert_allclose(sgn * got, want, rtol=0, atol=1e-12)
+
+
 # ---------------------------------------------------------------------------
 # The R update is exact least squares ([P5] objective; [P2] 2.2 ridge)
 # ---------------------------------------------------------------------------
@@ -120,6 +138,24 @@ def test_left_step_is_bruteforce_least_squares():
     L = O.left_step(X, prep["W_res"], R, 0.0)
     T = X @ prep["W_res"]
     L_bf = np.linalg.lstsq(R.T, T.T, rcond=None)[0].T     # min ||T - L R|| over L
+    np.testing.assert_allclose(L, L_bf, rtol=1e-9, atol=1e-12)
+
+
+@pytest.mark.parametrize("eps", [1e-3, 0.3])
+def test_left_step_with_ridge_is_augmented_least_squares(eps):
+    """eps > 0, r = 3: L minimises ||X W_res - L R||^2 + lambda ||L||^2 with
+    lambda = eps trace(R R^T) / r, i.e. least squares on the augmented system
+    [R^T; sqrt(lambda) I] L^T = [(X W_res)^T; 0] on an explicit X W_res."""
+    rng = _rng(5)
+    W, *_ = _power_law_w(rng, 20, 30)
+    X = _aniso_x(rng, 25, 20)
+    prep = _prep_lowrank(W, 5, 3)
+    R = rng.standard_normal((3, 30)) * np.array([[3.0], [1.0], [0.2]])
+    L = O.left_step(X, prep["W_res"], R, eps)
+    T = X @ prep["W_res"]
+    lam = eps * np.sum(R * R) / 3
+    A = np.vstack([R.T, np.sqrt(lam) * np.eye(3)])
+    L_bf = np.linalg.lstsq(A, np.vstack([T.T, np.zeros((3, T.shape[0]))]), rcond=None)[0].T
     np.testing.assert_allclose(L, L_bf, rtol=1e-9, atol=1e-12)
 
 
@@ -176,6 +212,47 @@ def test_als_error_non_increasing_in_t():
         L, R = O.als(X, prep["W_res"], prep["R0"], t, 0.0, P=prep["P"])
         errs.append(np.linalg.norm(T - L @ R))
     assert all(b <= a * (1 + 1e-12) for a, b in zip(errs, errs[1:]))
+
+
+@pytest.mark.parametrize("eps", [0.0, 1e-6, 0.05])
+def test_als_half_steps_are_stationary(eps):
+    """t = 1.5 ends on a left step: (X W_res - L R) R^T = lambda_L L with
+    lambda_L = eps trace(R R^T) / r for the R of the preceding right step;
+    t = 2 ends on a right step: L^T (X W_res - L R) = lambda R with
+    lambda = eps trace(L^T L) / r.  Both are the normal equations of the
+    half-step just taken (the pages' alternating least squares)."""
+    rng = _rng(31)
+    W, *_ = _power_law_w(rng, 40, 36)
+    X = _aniso_x(rng, 70, 40)
+    r = 5
+    prep = _prep_lowrank(W, 8, r)
+    T = X @ prep["W_res"]
+    scale = np.abs(T).max() * np.abs(prep["W_res"]).max() * 100
+    L, R = O.als(X, prep["W_res"], prep["R0"], 1.5, eps, P=prep["P"])
+    lam_l = eps * np.trace(R @ R.T) / r
+    np.testing.assert_allclose((T - L @ R) @ R.T, lam_l * L, atol=1e-11 * scale)
+    assert np.linalg.norm(L - X @ prep["P"]) > 1e-3 * np.linalg.norm(L)   # the left step moved L
+    L2, R2 = O.als(X, prep["W_res"], prep["R0"], 2.0, eps, P=prep["P"])
+    np.testing.assert_allclose(L2, L, atol=0)                              # same first three half-steps
+    lam_r = eps * np.trace(L2.T @ L2) / r
+    np.testing.assert_allclose(L2.T @ (T - L2 @ R2), lam_r * R2, atol=1e-11 * scale)
+
+
+def test_als_error_strictly_decreases_on_a_generic_case():
+    """On a generic input each extra half-step strictly lowers the error of
+    L R against X W_res, so Y(1.5) differs from Y(1) and Y(2) from Y(1.5)."""
+    rng = _rng(32)
+    W, *_ = _power_law_w(rng, 48, 40)
+    X = _aniso_x(rng, 80, 48)
+    prep = _prep_lowrank(W, 8, 6)
+    T = X @ prep["W_res"]
+    errs, Ys = [], []
+    for t in (1.0, 1.5, 2.0):
+        L, R = O.als(X, prep["W_res"], prep["R0"], t, 1e-6, P=prep["P"])
+        errs.append(np.linalg.norm(T - L @ R))
+        Ys.append(O.forward(X, prep, None, 1, 80, eps=1e-6, t=t))
+    assert errs[1] < errs[0] * (1 - 1e-3) and errs[2] < errs[1] * (1 - 1e-4)
+    assert O.rel_fro(Ys[1], Ys[0]) > 1e-3 and O.rel_fro(Ys[2], Ys[1]) > 1e-4
 
 
 # ---------------------------------------------------------------------------
@@ -328,6 +405,29 @@ def test_blast_fit_recovers_exact_blast_and_coupling_is_projection():
         for j in range(nb):
             Eij = E[i * b1:(i + 1) * b1, j * b2:(j + 1) * b2]
             np.testing.assert_allclose(g2["U"][i].T @ Eij @ g2["V"][j], 0, atol=1e-12)
+
+
+def test_blast_bases_are_top_singular_subspaces_of_block_rows_and_columns():
+    """On a generic W, U_i spans the top-rb left singular subspace of the whole
+    block row i and V_j the top-rb right singular subspace of the whole block
+    column j: the projection errors equal the singular-value tails
+    (Eckart-Young), which no other rb-dimensional basis attains."""
+    rng = _rng(65)
+    nb, b1, b2, rb = 3, 7, 6, 2
+    W = rng.standard_normal((nb * b1, nb * b2))
+    f = O.fit_blast(W, nb, rb)
+    for i in range(nb):
+        Wi = W[i * b1:(i + 1) * b1, :]
+        Ui = f["U"][i]
+        np.testing.assert_allclose(Ui.T @ Ui, np.eye(rb), atol=1e-12)
+        tail = np.sum(np.linalg.svd(Wi, compute_uv=False)[rb:] ** 2)
+        np.testing.assert_allclose(np.linalg.norm(Wi - Ui @ (Ui.T @ Wi)) ** 2, tail, rtol=1e-10)
+    for j in range(nb):
+        Wj = W[:, j * b2:(j + 1) * b2]
+        Vj = f["V"][j]
+        np.testing.assert_allclose(Vj.T @ Vj, np.eye(rb), atol=1e-12)
+        tail = np.sum(np.linalg.svd(Wj, compute_uv=False)[rb:] ** 2)
+        np.testing.assert_allclose(np.linalg.norm(Wj - (Wj @ Vj) @ Vj.T) ** 2, tail, rtol=1e-10)
 
 
 # ---------------------------------------------------------------------------
