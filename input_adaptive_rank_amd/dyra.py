@@ -210,6 +210,62 @@ def _dev(t, name):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _expect_shape(t, name, shape, dtype):
+    """Raises ValueError unless tensor t has exactly this shape and dtype.
+    The library receives bare pointers, so a wrong size would read or write
+    past a buffer on the device: every size is checked here first."""
+    if t is None or not hasattr(t, "shape"):
+        raise ValueError(f"{name} must be a tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _expect_bytes(t, name, nbytes):
+    """A raw byte buffer (plan, workspace): 1-D uint8 of at least nbytes."""
+    torch = _torch()
+    if t is None or not hasattr(t, "shape"):
+        raise ValueError(f"{name} must be a tensor")
+    if t.dtype != torch.uint8 or t.dim() != 1:
+        raise ValueError(f"{name} must be a 1-D uint8 tensor")
+    if t.numel() < nbytes:
+        raise ValueError(f"{name} holds {t.numel()} bytes, needs {nbytes}")
+
+
+def _expect_device(tensors, device):
+    """Every (name, tensor) is contiguous and on the GPU `device`."""
+    for name, t in tensors:
+        if t is None:
+            continue
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if t.device != device:
+            raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _check_forward_tensors(spec: Spec, plan, X, bias, Y, B: int, s: int, dtype: int, workspace, ws_bytes):
+    """Shapes and dtypes of every argument first, then contiguity and device.
+    ws_bytes: a function of nothing giving the workspace bytes needed."""
+    if not (isinstance(B, int) and isinstance(s, int)) or B <= 0 or s <= 0:
+        raise ValueError("B and s must be positive integers")
+    ws_bytes = ws_bytes()
+    td = torch_dtype(dtype)
+    n = B * s
+    _expect_shape(X, "X", (n, spec.c1), td)
+    _expect_shape(Y, "Y", (n, spec.c2), td)
+    if bias is not None:
+        _expect_shape(bias, "bias", (spec.c2,), td)
+    _expect_bytes(plan, "plan", plan_size(spec, dtype))
+    _expect_bytes(workspace, "workspace", ws_bytes)
+    _expect_device([("X", X), ("Y", Y), ("bias", bias), ("plan", plan), ("workspace", workspace)], X.device)
+    if Y.data_ptr() < X.data_ptr() + X.numel() * X.element_size() and \
+            X.data_ptr() < Y.data_ptr() + Y.numel() * Y.element_size():
+        raise ValueError("Y must not overlap X")
+
+
 def _stream(stream):
     torch = _torch()
     if stream is None:
@@ -220,6 +276,8 @@ def _stream(stream):
 def forward(spec: Spec, plan, X, bias, Y, B: int, s: int, dtype: int, eps: float = 1e-6,
             solver: int = SOLVER_AUTO, workspace=None, stream=None):
     """Launches the DyRA forward (asynchronous on `stream`)."""
+    _check_forward_tensors(spec, plan, X, bias, Y, B, s, dtype, workspace,
+                           lambda: workspace_size(spec, B, s, dtype))
     rc = lib().dyra_forward(ctypes.byref(spec), _dev(plan, "plan"), _dev(X, "X"), _dev(bias, "bias"),
                             _dev(Y, "Y"), B, s, dtype, eps, solver, _dev(workspace, "workspace"),
                             workspace.numel() * workspace.element_size(), _stream(stream))
@@ -236,6 +294,8 @@ def workspace_size_als(spec: Spec, B: int, s: int, dtype: int, half_steps: int) 
 def forward_als(spec: Spec, plan, X, bias, Y, B: int, s: int, dtype: int, eps: float, solver: int,
                 half_steps: int, workspace, stream=None):
     """The forward with 2 t = half_steps ALS half-steps (asynchronous)."""
+    _check_forward_tensors(spec, plan, X, bias, Y, B, s, dtype, workspace,
+                           lambda: workspace_size_als(spec, B, s, dtype, half_steps))
     rc = lib().dyra_forward_als(ctypes.byref(spec), _dev(plan, "plan"), _dev(X, "X"), _dev(bias, "bias"),
                                 _dev(Y, "Y"), B, s, dtype, eps, solver, half_steps, _dev(workspace, "workspace"),
                                 workspace.numel() * workspace.element_size(), _stream(stream))
@@ -246,6 +306,8 @@ def forward_events(spec: Spec, plan, X, bias, Y, B: int, s: int, dtype: int, eps
                    workspace, events, stream=None):
     """dyra_forward recording stage-boundary events (torch.cuda.Event objects
     that have been recorded once, so their HIP handles exist)."""
+    _check_forward_tensors(spec, plan, X, bias, Y, B, s, dtype, workspace,
+                           lambda: workspace_size(spec, B, s, dtype))
     arr = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
     rc = lib().dyra_forward_events(ctypes.byref(spec), _dev(plan, "plan"), _dev(X, "X"), _dev(bias, "bias"),
                                    _dev(Y, "Y"), B, s, dtype, eps, solver, _dev(workspace, "workspace"),
@@ -263,8 +325,18 @@ def solver_status(spec: Spec, workspace, B: int, s: int, dtype: int, stream=None
 
 
 def dense_ref(X, Wt, bias, Y, dtype: int, stream=None):
+    """Y = X W + bias with Wt = W^T (asynchronous)."""
+    td = torch_dtype(dtype)
+    if X is None or X.dim() != 2 or Wt is None or Wt.dim() != 2:
+        raise ValueError("X and Wt must be 2-D GPU tensors")
     n, c1 = X.shape
     c2 = Wt.shape[0]
+    _expect_shape(X, "X", (n, c1), td)
+    _expect_shape(Wt, "Wt", (c2, c1), td)
+    _expect_shape(Y, "Y", (n, c2), td)
+    if bias is not None:
+        _expect_shape(bias, "bias", (c2,), td)
+    _expect_device([("X", X), ("Wt", Wt), ("Y", Y), ("bias", bias)], X.device)
     rc = lib().dyra_dense_ref(_dev(X, "X"), _dev(Wt, "Wt"), _dev(bias, "bias"), _dev(Y, "Y"), n, c1, c2,
                               dtype, _stream(stream))
     _check("dyra_dense_ref", rc)
@@ -288,6 +360,7 @@ class DyraLayer:
         self.device = torch.device(device)
         host = plan_pack(spec, factors, dtype)
         self.plan = torch.from_numpy(host).to(self.device)
+        self.device = self.plan.device          # "cuda" -> "cuda:<index>"
         self.bias = None if bias is None else to_device(bias, dtype, self.device)
         self._ws = None
         self._ws_key = None
@@ -307,6 +380,8 @@ class DyraLayer:
         torch = _torch()
         if X.dtype != torch_dtype(self.dtype):
             raise ValueError("X dtype does not match the plan dtype")
+        if X.device != self.device:
+            raise ValueError(f"X is on {X.device}, the layer on {self.device}")
         Y = out if out is not None else torch.empty((B * s, self.spec.c2), dtype=X.dtype, device=X.device)
         ws = self.workspace(B, s)
         if self.half_steps == 2:

@@ -156,3 +156,53 @@ def test_als_entry_points_validate_on_host():
                               1 << 30, None) == -6
     assert L.dyra_forward_als(ctypes.byref(lowrank), 16, 16, None, 16, 2, 64, synth.DT_BF16, 1e-6, 0, 3, 16,
                               sizes[0], None) == -3
+
+
+# ---------------------------------------------------------------------------
+# the Python binding checks every tensor before a pointer reaches the library
+# ---------------------------------------------------------------------------
+
+def _bind_args(B=2, s=50, dtype=synth.DT_BF16):
+    import torch
+    spec = _lowrank()
+    td = D.torch_dtype(dtype)
+    n = B * s
+    return dict(spec=spec, plan=torch.zeros(D.plan_size(spec, dtype), dtype=torch.uint8),
+                X=torch.zeros((n, spec.c1), dtype=td), bias=torch.zeros(spec.c2, dtype=td),
+                Y=torch.zeros((n, spec.c2), dtype=td), B=B, s=s, dtype=dtype,
+                workspace=torch.zeros(D.workspace_size(spec, B, s, dtype), dtype=torch.uint8))
+
+
+@pytest.mark.parametrize("change,msg", [
+    (lambda a: a.update(X=a["X"][:-1]), "X must have shape"),
+    (lambda a: a.update(X=a["X"].float()), "X must be"),
+    (lambda a: a.update(Y=a["Y"][:, :-8]), "Y must have shape"),
+    (lambda a: a.update(bias=a["bias"][:-8]), "bias must have shape"),
+    (lambda a: a.update(plan=a["plan"][:-1]), "plan holds"),
+    (lambda a: a.update(workspace=a["workspace"][:-1]), "workspace holds"),
+    (lambda a: a.update(workspace=a["workspace"].view(-1, 2)), "workspace must be a 1-D uint8"),
+    (lambda a: a.update(B=3), "X must have shape"),
+    (lambda a: a.update(s=0), "B and s must be positive"),
+    (lambda a: None, "must be a GPU tensor"),                 # right sizes, host memory
+])
+def test_binding_rejects_bad_tensors_before_the_library(change, msg):
+    a = _bind_args()
+    change(a)
+    with pytest.raises(ValueError, match=msg):
+        D.forward(a["spec"], a["plan"], a["X"], a["bias"], a["Y"], a["B"], a["s"], a["dtype"],
+                  workspace=a["workspace"])
+
+
+def test_binding_checks_als_workspace_and_dense_ref():
+    import torch
+    a = _bind_args()
+    with pytest.raises(ValueError, match="workspace holds"):
+        D.forward_als(a["spec"], a["plan"], a["X"], a["bias"], a["Y"], a["B"], a["s"], a["dtype"], 1e-6, 0, 3,
+                      a["workspace"])
+    X = torch.zeros((10, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="Wt must have shape"):
+        D.dense_ref(X, torch.zeros((96, 72), dtype=torch.bfloat16), None,
+                    torch.zeros((10, 96), dtype=torch.bfloat16), synth.DT_BF16)
+    with pytest.raises(ValueError, match="Y must have shape"):
+        D.dense_ref(X, torch.zeros((96, 64), dtype=torch.bfloat16), None,
+                    torch.zeros((10, 88), dtype=torch.bfloat16), synth.DT_BF16)
