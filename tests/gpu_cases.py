@@ -19,10 +19,13 @@ TOL = {synth.DT_F32: 1e-4, synth.DT_BF16: 2e-2}
 # tile fails even where the correction L R is a few percent of Y:
 #   per segment   ||dY_b|| <= TOL ||Y_b||
 #   correction    ||dY_b|| <= ALPHA u ||Y_b|| + BETA ||(L R)_b||
-#   elementwise   |dY| <= C_ELEM u (|X_b| |static factors| + |L_b| |R_b| + |bias|)
+#   elementwise   |dY| <= C_ELEM u (|X_b| |static factors| + a_b |L_b| |R_b| + |bias|)
 # with dY = Y_gpu - Y_oracle and u the storage unit: bf16 rounds to nearest
 # with u = 2^-8 relative; the fp32 path's unit is taken as 2^-16, a fifth of
 # its 1e-4 bar (its error is accumulation and solve rounding, not storage).
+# a_b = 1 + cond(L_b) s 2^-24 / u: G_b and M_b are fp32 sums over the s
+# tokens of a segment (relative rounding up to s 2^-24), and the projection
+# onto span(L_b) that the solve forms moves by that much times cond(L_b).
 # The derivation of ALPHA, BETA and C_ELEM is in the design notes (tolerances).
 UNIT = {synth.DT_F32: 2.0 ** -16, synth.DT_BF16: 2.0 ** -8}
 ALPHA, BETA, C_ELEM = 1.5, 0.1, 4.0
@@ -93,7 +96,10 @@ def oracle_terms(w, X, rp, bias, eps=1e-6, t=1.0):
         L, R = O.als(Xb, rp["W_res"], rp["R0"], t, eps, P=rp["P"] if t >= 1 else None)
         corr[rows] = L @ R
         Y[rows] = base + corr[rows]
-        mag[rows] = O.static_apply(rp["kind"], np.abs(Xb), af) + np.abs(L) @ np.abs(R)
+        sv = np.linalg.svd(L, compute_uv=False)
+        cond = sv[0] / sv[-1] if sv[-1] > 0 else np.inf
+        amp = 1.0 + min(cond, 1e12) * w.s * 2.0 ** -24 / UNIT[w.dtype]
+        mag[rows] = O.static_apply(rp["kind"], np.abs(Xb), af) + amp * (np.abs(L) @ np.abs(R))
     if bias is not None:
         Y += bias[None, :]
         mag += np.abs(bias)[None, :]
