@@ -234,6 +234,30 @@ int dyra_forward_events(const dyra_spec* spec, const void* plan, const void* X, 
                         void* const* events, int32_t nevents);
 
 /*
+ * dyra_forward without a workspace argument and without any allocation, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  The workspace is a
+ * static device array inside the library of DYRA_NOALLOC_MAX_WORKSPACE
+ * bytes (64 MiB: enough for B = 32 segments of 1029 tokens at 1024 -> 4096,
+ * k = 256, r = 64); a call whose dyra_workspace_size exceeds it returns
+ * DYRA_EWORKSPACE before any HIP call.  Each GPU holds its own copy from the
+ * first call made with that device current until the process ends; the
+ * library takes the copy's address then (hipGetSymbolAddress) and calls no
+ * allocating routine.  `stream` must belong to the current device.
+ *   status_out: device int32[B] receiving the per-segment solver status
+ *               words (DYRA_SOLVE_*), or NULL.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (different streams or threads) race and give undefined results;
+ * serialise them.  Every byte a call reads from the array is written earlier
+ * in the same call, so nothing needs clearing between calls.  Other
+ * arguments, results and errors as for dyra_forward.
+ */
+#define DYRA_NOALLOC_MAX_WORKSPACE ((size_t)64 << 20)
+int dyra_forward_noalloc(const dyra_spec* spec, const void* plan, const void* X, const void* bias, void* Y,
+                         int64_t B, int64_t s, int32_t dtype, float ridge_eps, int32_t solver,
+                         int32_t* status_out, void* stream);
+
+/*
  * Copies the B per-segment solver status words of the last dyra_forward on
  * this workspace to host_out[B] (synchronises `stream`).  Errors: EINVAL, EHIP.
  */

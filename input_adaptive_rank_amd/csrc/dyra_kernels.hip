@@ -17,6 +17,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <mutex>
 #include <type_traits>
 
 #include "../../include/dyra.h"
@@ -2932,6 +2933,58 @@ extern "C" int dyra_forward_events(const dyra_spec* spec, const void* plan, cons
   if (nevents < 0 || (nevents > 0 && !events)) return DYRA_EINVAL;
   return forward_impl(spec, plan, X, bias, Y, B, s, dtype, ridge_eps, solver, workspace, ws_bytes, stream,
                       StageEvents{events, nevents});
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free forward: the workspace is this file-scope device array,
+// one copy per GPU the library runs on, held until the process ends.  Host
+// code never passes the array's name to a kernel or copy (on the host it is
+// a stand-in, not a device address): each device's address comes from
+// hipGetSymbolAddress, taken once per device on the first call made with
+// that device current, and only that address is used.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) char scratch[DYRA_NOALLOC_MAX_WORKSPACE];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {nullptr};
+
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DYRA_EHIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return DYRA_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DYRA_OK;
+}
+}  // namespace
+
+extern "C" int dyra_forward_noalloc(const dyra_spec* spec, const void* plan, const void* X, const void* bias,
+                                    void* Y, int64_t B, int64_t s, int32_t dtype, float ridge_eps, int32_t solver,
+                                    int32_t* status_out, void* stream) {
+  // every argument and the size limit are checked before any HIP call
+  const void* not_null = plan;
+  int rc = check_forward_args(spec, plan, X, Y, B, s, dtype, ridge_eps, solver, const_cast<void*>(not_null),
+                              (size_t)DYRA_NOALLOC_MAX_WORKSPACE);
+  if (rc) return rc;
+  if (bias && (reinterpret_cast<uintptr_t>(bias) & 15)) return DYRA_EINVAL;
+  if (status_out && (reinterpret_cast<uintptr_t>(status_out) & 3)) return DYRA_EINVAL;
+  void* ws = nullptr;
+  rc = scratch_address(&ws);
+  if (rc) return rc;
+  rc = forward_impl(spec, plan, X, bias, Y, B, s, dtype, ridge_eps, solver, ws, (size_t)DYRA_NOALLOC_MAX_WORKSPACE,
+                    stream, StageEvents{nullptr, 0});
+  if (rc || !status_out) return rc;
+  const WsLayout WL = ws_layout(*spec, B, s, dtype);
+  if (hipMemcpyAsync(status_out, reinterpret_cast<const char*>(ws) + WL.status, (size_t)B * 4,
+                     hipMemcpyDeviceToDevice, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return DYRA_EHIP;
+  return DYRA_OK;
 }
 
 extern "C" int dyra_solver_status(const dyra_spec* spec, const void* workspace, int64_t B, int64_t s,

@@ -87,6 +87,7 @@ def lib():
             "dyra_workspace_offsets": [SP, I64, I64, I32, ctypes.POINTER(WsOffsets)],
             "dyra_workspace_size_als": [SP, I64, I64, I32, I32, ctypes.POINTER(SZ)],
             "dyra_forward_als": [SP, P, P, P, P, I64, I64, I32, ctypes.c_float, I32, I32, P, SZ, P],
+            "dyra_forward_noalloc": [SP, P, P, P, P, I64, I64, I32, ctypes.c_float, I32, P, P],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -259,7 +260,8 @@ def _check_forward_tensors(spec: Spec, plan, X, bias, Y, B: int, s: int, dtype: 
     if bias is not None:
         _expect_shape(bias, "bias", (spec.c2,), td)
     _expect_bytes(plan, "plan", plan_size(spec, dtype))
-    _expect_bytes(workspace, "workspace", ws_bytes)
+    if workspace is not None or ws_bytes:
+        _expect_bytes(workspace, "workspace", ws_bytes)
     _expect_device([("X", X), ("Y", Y), ("bias", bias), ("plan", plan), ("workspace", workspace)], X.device)
     if Y.data_ptr() < X.data_ptr() + X.numel() * X.element_size() and \
             X.data_ptr() < Y.data_ptr() + Y.numel() * Y.element_size():
@@ -300,6 +302,26 @@ def forward_als(spec: Spec, plan, X, bias, Y, B: int, s: int, dtype: int, eps: f
                                 _dev(Y, "Y"), B, s, dtype, eps, solver, half_steps, _dev(workspace, "workspace"),
                                 workspace.numel() * workspace.element_size(), _stream(stream))
     _check("dyra_forward_als", rc)
+
+
+NOALLOC_MAX_WORKSPACE = 64 << 20   # DYRA_NOALLOC_MAX_WORKSPACE
+
+
+def forward_noalloc(spec: Spec, plan, X, bias, Y, B: int, s: int, dtype: int, eps: float = 1e-6,
+                    solver: int = SOLVER_AUTO, status=None, stream=None):
+    """The forward on the library's static device workspace (no allocation,
+    asynchronous).  status: optional device int32 tensor [B] that receives
+    the per-segment solver status words.  Calls overlapping in time on one
+    GPU share that workspace and race."""
+    torch = _torch()
+    _check_forward_tensors(spec, plan, X, bias, Y, B, s, dtype, None, lambda: 0)
+    if status is not None:
+        _expect_shape(status, "status", (B,), torch.int32)
+        _expect_device([("status", status)], X.device)
+    rc = lib().dyra_forward_noalloc(ctypes.byref(spec), _dev(plan, "plan"), _dev(X, "X"), _dev(bias, "bias"),
+                                    _dev(Y, "Y"), B, s, dtype, eps, solver, _dev(status, "status"),
+                                    _stream(stream))
+    _check("dyra_forward_noalloc", rc)
 
 
 def forward_events(spec: Spec, plan, X, bias, Y, B: int, s: int, dtype: int, eps: float, solver: int,

@@ -206,3 +206,19 @@ def test_binding_checks_als_workspace_and_dense_ref():
     with pytest.raises(ValueError, match="Y must have shape"):
         D.dense_ref(X, torch.zeros((96, 64), dtype=torch.bfloat16), None,
                     torch.zeros((10, 88), dtype=torch.bfloat16), synth.DT_BF16)
+
+
+def test_noalloc_rejects_calls_past_its_static_workspace_before_any_hip_call():
+    """dyra_forward_noalloc checks its arguments and the size limit first:
+    fake (never dereferenced) aligned addresses, so no HIP call may happen."""
+    L = D.lib()
+    big = D.make_spec(synth.KIND_LOWRANK, 4096, 1024, 64, k=256)      # 32 x 1029 tokens: ~116 MiB
+    assert D.workspace_size(big, 32, 1029, synth.DT_BF16) > D.NOALLOC_MAX_WORKSPACE
+    args = (1 << 12, 1 << 13, None, 1 << 14, 32, 1029, synth.DT_BF16, 1e-6, 0, None, None)
+    assert L.dyra_forward_noalloc(ctypes.byref(big), *args) == -3
+    ok = D.make_spec(synth.KIND_LOWRANK, 1024, 4096, 64, k=256)       # 32 x 1029 tokens: ~60 MiB fits
+    assert D.workspace_size(ok, 32, 1029, synth.DT_BF16) <= D.NOALLOC_MAX_WORKSPACE
+    bad = (1 << 12, 1 << 13, None, 1 << 14, 32, 1029, synth.DT_BF16, -1.0, 0, None, None)
+    assert L.dyra_forward_noalloc(ctypes.byref(ok), *bad) == -1        # negative ridge
+    unaligned = (1 << 12, 1 << 13, None, 1 << 14, 32, 1029, synth.DT_BF16, 1e-6, 0, 6, None)
+    assert L.dyra_forward_noalloc(ctypes.byref(ok), *unaligned) == -1  # misaligned status_out
