@@ -69,12 +69,15 @@ extern "C" {
 
 /* r x r solver choice for dyra_forward */
 #define DYRA_SOLVER_AUTO 0   /* the sweep (the faster solver on MI355X at every r <= 128) */
-#define DYRA_SOLVER_CHOL 1
-#define DYRA_SOLVER_NS   2
+#define DYRA_SOLVER_CHOL 1   /* Cholesky: G + lambda I = C C^T, W = C^-1, Ginv = W^T W (fp64) */
+#define DYRA_SOLVER_NS   2   /* Newton-Schulz, falling back to the sweep where it stalls   */
 
 /* per-segment solver status words (dyra_solver_status) */
 #define DYRA_SOLVE_OK        0
-#define DYRA_SOLVE_NOT_SPD   1   /* Cholesky met a pivot <= 0: R_b := 0, Y_b = X_b W_hat + bias */
+#define DYRA_SOLVE_NOT_SPD   1   /* a pivot <= 0, a non-finite G_b (a NaN or Inf in X_b), or */
+                                 /* at ridge_eps = 0 a pivot <= 2^-16 of its diagonal:       */
+                                 /* R_b := 0, Y_b = X_b W_hat + bias (a row of X_b that is   */
+                                 /* not finite still gives a non-finite row of Y_b)           */
 #define DYRA_SOLVE_NOCONV    2   /* reserved: an iterative solve without a usable result */
 #define DYRA_SOLVE_ZERO      3   /* trace(G_b) == 0 (X_b P == 0): R_b := 0               */
 #define DYRA_SOLVE_FALLBACK  4   /* Newton-Schulz did not reach its tolerance in fp32;    */
@@ -182,6 +185,9 @@ int dyra_workspace_offsets(const dyra_spec* spec, int64_t B, int64_t s, int32_t 
  *   bias:      device [c2], dtype, or NULL.
  *   Y:         device [B*s][c2], dtype (written; must not alias X).
  *   ridge_eps: lambda_b = ridge_eps * trace(G_b) / r (>= 0; 1e-6 typical).
+ *              0 means no ridge: a G_b whose pivot falls to 2^-16 of its
+ *              diagonal (rank-deficient L_b, e.g. s < r) counts as singular
+ *              and segment b gets status NOT_SPD and R_b = 0.
  *   solver:    DYRA_SOLVER_*.
  *   workspace: device, >= dyra_workspace_size bytes; holds the per-segment
  *              solver status words read by dyra_solver_status.

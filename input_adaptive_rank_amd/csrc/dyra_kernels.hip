@@ -1342,8 +1342,15 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 constexpr int SW_BK = 4;
 struct SweepLds {
   double pv[2][SW_BK][128];
+  double diag0[128];   // diagonal of G before the ridge (rank test at eps = 0)
   float red[16];
 };
+
+// eps = 0 (no ridge): a pivot d_j at or below 2^-16 times the diagonal G_jj
+// (sin^2 of the angle between column j of L and the span of the earlier
+// columns) marks G as singular: status NOT_SPD and R_b = 0.  With a ridge,
+// only a non-positive or non-finite pivot does.
+constexpr double kSingularPivotRel = 1.0 / 65536.0;
 
 // 1 / D for D > 0: hardware reciprocal estimate refined by two Newton steps
 // (x <- x + x (1 - D x)), which reach full double precision.
@@ -1377,9 +1384,12 @@ __device__ __forceinline__ int sweep_inverse(const float* Gb, float* Ob, int r, 
       const bool v = own && i0 + x < r && j0 + y < r;
       const float g = v ? Gb[(i0 + x) * r + j0 + y] : 0.f;
       a[x][y] = g;
-      if (v && x + i0 == y + j0) trf += g;
+      if (v && x + i0 == y + j0) {
+        trf += g;
+        sh.diag0[i0 + x] = g;
+      }
     }
-  const float tr = block_sum<NT>(trf, sh.red);
+  const float tr = block_sum<NT>(trf, sh.red);   // its barriers also publish diag0
   int st = DYRA_SOLVE_OK;
   if (tr == 0.f) st = DYRA_SOLVE_ZERO;
   else if (!(tr > 0.f) || !isfinite(tr)) st = DYRA_SOLVE_NOT_SPD;
@@ -1420,6 +1430,7 @@ __device__ __forceinline__ int sweep_inverse(const float* Gb, float* Ob, int r, 
       for (int p = 0; p < SW_BK; ++p) {
         const double D = Q[p][p];
         if (!(D > 0.0) || !isfinite(D)) bad = true;
+        if (eps == 0.f && !(D > kSingularPivotRel * sh.diag0[kb + p])) bad = true;
         const double invD = recip_pos(D);
         double c[SW_BK];
 #pragma unroll
@@ -1491,6 +1502,258 @@ __device__ __forceinline__ int sweep_inverse(const float* Gb, float* Ob, int r, 
 #pragma unroll
     for (int y = 0; y < TB; ++y)
       if (own && i0 + x < r && j0 + y < r) Ob[(i0 + x) * r + j0 + y] = st == DYRA_SOLVE_OK ? (float)-a[x][y] : 0.f;
+  return st;
+}
+
+// ===========================================================================
+// S4a (Cholesky route): (G + lambda I)^-1 from the Cholesky factor, in fp64,
+// with the sweep's tile distribution (thread t owns a TB x TB tile) and its
+// double-buffered broadcast of SW_BK rows per barrier:
+//   1. factor A = G + lambda I = C C^T, right-looking by SW_BK-column panels:
+//      every thread factors the panel's diagonal block C_KK itself (from the
+//      broadcast pivot rows), forms the panel rows L_iK = A_iK C_KK^-T for its
+//      own rows and columns (A_iK = A_Ki by symmetry, read from the broadcast
+//      rows) and updates its trailing tile A_IJ -= L_IK L_JK^T; the panel is
+//      written to LDS as a packed lower triangle (fp64);
+//   2. W = C^-1 by blocked forward substitution on the identity (C W = I):
+//      the threads holding block row K solve it with C_KK, broadcast it, and
+//      every lower row block subtracts C_IK W_K;
+//   3. (G + lambda I)^-1 = W^T W, accumulated from W's broadcast row blocks.
+// The apply that follows (M' = Ginv M on fp32 MFMAs) is the two triangular
+// solves C^-T (C^-1 M) with the triangular inverses formed explicitly.
+// Three sequences of r / SW_BK barrier steps against the sweep's one: on
+// this chip the sweep is the faster route and AUTO takes it.
+// ===========================================================================
+
+__device__ __forceinline__ int packed_lower(int i, int j) { return ((i * (i + 1)) >> 1) + j; }
+
+// Needs r % TB == 0, r <= 128, ceil(r / TB)^2 <= NT and Cp: LDS for
+// r (r + 1) / 2 doubles.  Returns the status (same in every thread).
+template <int NT, int TB>
+__device__ __forceinline__ int chol_inverse(const float* Gb, float* Ob, int r, float eps, SweepLds& sh,
+                                            double* Cp) {
+  constexpr int PB = SW_BK;
+  static_assert(TB % PB == 0 && TB % 2 == 0, "tile");
+  const int tid = threadIdx.x;
+  const int tpr = (r + TB - 1) / TB;
+  const int i0 = (tid / tpr) * TB, j0 = (tid % tpr) * TB;
+  const bool own = i0 < r;
+  double a[TB][TB];
+  float trf = 0.f;
+#pragma unroll
+  for (int x = 0; x < TB; ++x)
+#pragma unroll
+    for (int y = 0; y < TB; ++y) {
+      const bool v = own && i0 + x < r && j0 + y < r;
+      const float g = v ? Gb[(i0 + x) * r + j0 + y] : 0.f;
+      a[x][y] = g;
+      if (v && x + i0 == y + j0) {
+        trf += g;
+        sh.diag0[i0 + x] = g;
+      }
+    }
+  const float tr = block_sum<NT>(trf, sh.red);   // its barriers also publish diag0
+  int st = DYRA_SOLVE_OK;
+  if (tr == 0.f) st = DYRA_SOLVE_ZERO;
+  else if (!(tr > 0.f) || !isfinite(tr)) st = DYRA_SOLVE_NOT_SPD;
+  auto publish_row = [&](double (&t)[TB][TB], int x, int k0, int buf) {
+    const int i = i0 + x;
+    if (own && i >= k0 && i < k0 + PB) {
+#pragma unroll
+      for (int y = 0; y < TB; y += 2)
+        *reinterpret_cast<double2*>(&sh.pv[buf][i - k0][j0 + y]) = make_double2(t[x][y], t[x][y + 1]);
+    }
+  };
+  if (st == DYRA_SOLVE_OK) {
+    const double lam = (double)(eps * tr / (float)r);
+#pragma unroll
+    for (int x = 0; x < TB; ++x)
+#pragma unroll
+      for (int y = 0; y < TB; ++y)
+        if (own && x + i0 == y + j0) a[x][y] += lam;
+    // ---- 1. A = C C^T ----
+#pragma unroll
+    for (int x = 0; x < TB; ++x) publish_row(a, x, 0, 0);
+    __syncthreads();
+    for (int kb = 0, blk = 0; kb < r; kb += PB, ++blk) {
+      const double(*buf)[128] = sh.pv[blk & 1];
+      double Ck[PB][PB], ic[PB];
+      bool bad = false;
+#pragma unroll
+      for (int p = 0; p < PB; ++p) {
+        double d = buf[p][kb + p];
+#pragma unroll
+        for (int q = 0; q < p; ++q) d = fma(-Ck[p][q], Ck[p][q], d);
+        const bool ok = d > 0.0 && isfinite(d) && (eps > 0.f || d > kSingularPivotRel * sh.diag0[kb + p]);
+        if (!ok) bad = true;
+        const double c = sqrt(ok ? d : 1.0);
+        ic[p] = recip_pos(c);
+        Ck[p][p] = c;
+#pragma unroll
+        for (int i = p + 1; i < PB; ++i) {
+          double v = buf[i][kb + p];
+#pragma unroll
+          for (int q = 0; q < p; ++q) v = fma(-Ck[i][q], Ck[p][q], v);
+          Ck[i][p] = v * ic[p];
+        }
+      }
+      if (bad) {   // uniform: every thread read the same pivot block
+        st = DYRA_SOLVE_NOT_SPD;
+        break;
+      }
+      // Zk = C_KK^-1 (lower), so L_iK[p] = sum_q A_iK[q] Zk[p][q]
+      double Zk[PB][PB];
+#pragma unroll
+      for (int q = 0; q < PB; ++q)
+#pragma unroll
+        for (int p = 0; p < PB; ++p) {
+          if (p < q) {
+            Zk[p][q] = 0.0;
+          } else {
+            double v = p == q ? 1.0 : 0.0;
+#pragma unroll
+            for (int t = q; t < p; ++t) v = fma(-Ck[p][t], Zk[t][q], v);
+            Zk[p][q] = v * ic[p];
+          }
+        }
+      double li[TB][PB], lj[TB][PB];
+#pragma unroll
+      for (int x = 0; x < TB; ++x) {
+        double aq[PB], bq[PB];
+#pragma unroll
+        for (int q = 0; q < PB; ++q) {
+          aq[q] = own ? buf[q][i0 + x] : 0.0;
+          bq[q] = buf[q][j0 + x];
+        }
+#pragma unroll
+        for (int p = 0; p < PB; ++p) {
+          double u = 0.0, v = 0.0;
+#pragma unroll
+          for (int q = 0; q <= p; ++q) {
+            u = fma(aq[q], Zk[p][q], u);
+            v = fma(bq[q], Zk[p][q], v);
+          }
+          li[x][p] = u;
+          lj[x][p] = v;
+        }
+      }
+      // the panel into the packed factor: the tile whose columns hold block K
+      if (own && j0 <= kb && kb < j0 + TB) {
+        const int oi = kb - i0;
+#pragma unroll
+        for (int x = 0; x < TB; ++x) {
+          const int i = i0 + x;
+          if (i >= kb + PB) {
+#pragma unroll
+            for (int p = 0; p < PB; ++p) Cp[packed_lower(i, kb + p)] = li[x][p];
+          } else if (oi == (x & ~(PB - 1))) {
+#pragma unroll
+            for (int p = 0; p <= (x & (PB - 1)); ++p) Cp[packed_lower(i, kb + p)] = Ck[x & (PB - 1)][p];
+          }
+        }
+      }
+#pragma unroll
+      for (int x = 0; x < TB; ++x)
+#pragma unroll
+        for (int y = 0; y < TB; ++y)
+          if (own && i0 + x >= kb + PB && j0 + y >= kb + PB) {
+            double v = a[x][y];
+#pragma unroll
+            for (int p = 0; p < PB; ++p) v = fma(-li[x][p], lj[y][p], v);
+            a[x][y] = v;
+          }
+#pragma unroll
+      for (int x = 0; x < TB; ++x) publish_row(a, x, kb + PB, (blk + 1) & 1);
+      __syncthreads();
+    }
+  }
+  if (st == DYRA_SOLVE_OK) {
+    // ---- 2. W = C^-1 (C W = I), row block by row block ----
+#pragma unroll
+    for (int x = 0; x < TB; ++x)
+#pragma unroll
+      for (int y = 0; y < TB; ++y) a[x][y] = (own && i0 + x == j0 + y) ? 1.0 : 0.0;
+    for (int kb = 0, blk = 0; kb < r; kb += PB, ++blk) {
+      const int oi = kb - i0;
+      if (own && oi >= 0 && oi < TB) {
+        double ck[PB][PB], icd[PB];
+#pragma unroll
+        for (int p = 0; p < PB; ++p) {
+#pragma unroll
+          for (int q = 0; q <= p; ++q) ck[p][q] = Cp[packed_lower(kb + p, kb + q)];
+          icd[p] = recip_pos(ck[p][p]);
+        }
+#pragma unroll
+        for (int x = 0; x < TB; ++x)
+          if (oi == (x & ~(PB - 1))) {
+            const int p = x & (PB - 1);
+#pragma unroll
+            for (int y = 0; y < TB; ++y) {
+              double v = a[x][y];
+#pragma unroll
+              for (int q = 0; q < PB; ++q)
+                if (q < p) v = fma(-ck[p][q], a[(x & ~(PB - 1)) + q][y], v);
+              a[x][y] = v * icd[p];
+            }
+          }
+      }
+#pragma unroll
+      for (int x = 0; x < TB; ++x) publish_row(a, x, kb, blk & 1);
+      __syncthreads();
+      const double(*buf)[128] = sh.pv[blk & 1];
+#pragma unroll
+      for (int x = 0; x < TB; ++x) {
+        const int i = i0 + x;
+        if (own && i >= kb + PB) {
+          double c[PB];
+#pragma unroll
+          for (int p = 0; p < PB; ++p) c[p] = Cp[packed_lower(i, kb + p)];
+#pragma unroll
+          for (int y = 0; y < TB; ++y) {
+            double v = a[x][y];
+#pragma unroll
+            for (int p = 0; p < PB; ++p) v = fma(-c[p], buf[p][j0 + y], v);
+            a[x][y] = v;
+          }
+        }
+      }
+    }
+    __syncthreads();
+    // ---- 3. (G + lambda I)^-1 = W^T W ----
+    double g[TB][TB];
+#pragma unroll
+    for (int x = 0; x < TB; ++x)
+#pragma unroll
+      for (int y = 0; y < TB; ++y) g[x][y] = 0.0;
+    for (int kb = 0, blk = 0; kb < r; kb += PB, ++blk) {
+#pragma unroll
+      for (int x = 0; x < TB; ++x) publish_row(a, x, kb, blk & 1);
+      __syncthreads();
+      const double(*buf)[128] = sh.pv[blk & 1];
+#pragma unroll
+      for (int x = 0; x < TB; ++x) {
+        double wi[PB];
+#pragma unroll
+        for (int p = 0; p < PB; ++p) wi[p] = own ? buf[p][i0 + x] : 0.0;
+#pragma unroll
+        for (int y = 0; y < TB; ++y) {
+          double v = g[x][y];
+#pragma unroll
+          for (int p = 0; p < PB; ++p) v = fma(wi[p], buf[p][j0 + y], v);
+          g[x][y] = v;
+        }
+      }
+    }
+#pragma unroll
+    for (int x = 0; x < TB; ++x)
+#pragma unroll
+      for (int y = 0; y < TB; ++y) a[x][y] = g[x][y];
+  }
+#pragma unroll
+  for (int x = 0; x < TB; ++x)
+#pragma unroll
+    for (int y = 0; y < TB; ++y)
+      if (own && i0 + x < r && j0 + y < r) Ob[(i0 + x) * r + j0 + y] = st == DYRA_SOLVE_OK ? (float)a[x][y] : 0.f;
   return st;
 }
 
@@ -1737,11 +2000,14 @@ __device__ __forceinline__ void s3_gram(const bf16_t* __restrict__ Lt, int64_t l
   __syncthreads();
 }
 
-template <int NRB, int NB>
+// SOLVE: the r x r solve its solve role runs (0 none, 1 the sweep, 2 the
+// Cholesky route), a template parameter so each instantiation carries the
+// registers of its own solver only.
+template <int NRB, int NB, int SOLVE>
 __global__ __launch_bounds__(S3_NT, NRB <= 4 ? 2 : 1) void s3_reduce_solve_kernel(
     const bf16_t* __restrict__ Lt, int64_t ldt, const bf16_t* __restrict__ X, int64_t c1, int r, int64_t seg,
     int64_t n, int64_t B, float* __restrict__ M, float* __restrict__ G, float* __restrict__ Gi,
-    int32_t* __restrict__ status, float eps, int do_sweep, int strips, int64_t lt_seg_rows, int x_rel,
+    int32_t* __restrict__ status, float eps, int strips, int64_t lt_seg_rows, int x_rel,
     const float* __restrict__ gpart, int gchunks, int64_t gprows) {
   __shared__ __attribute__((aligned(16))) char lds[S3Lds<NB>::BYTES];
   SweepLds* sl = reinterpret_cast<SweepLds*>(lds + S3Lds<NB>::SW_OFF);
@@ -1835,10 +2101,17 @@ __global__ __launch_bounds__(S3_NT, NRB <= 4 ? 2 : 1) void s3_reduce_solve_kerne
     }
     // publish G (the Newton-Schulz path and diagnostics read it)
     for (int e = threadIdx.x; e < r * r; e += S3_NT) G[b * r * r + e] = Gs[e];
-    if (do_sweep) {
-      // TB x TB tiles: ceil(r / TB)^2 <= 256 threads for r <= 32 NB
+    if constexpr (SOLVE != 0) {
+      // TB x TB tiles: ceil(r / TB)^2 <= 256 threads for r <= 32 NB.  The
+      // Cholesky route keeps its packed factor in the LDS below the sweep's
+      // buffers (G has been read into registers by then)
       constexpr int TB = NB <= 2 ? 4 : 8;
-      const int st = sweep_inverse<S3_NT, TB>(Gs, Gi + b * r * r, r, eps, *sl);
+      static_assert(32 * NB * (32 * NB + 1) / 2 * 8 <= S3Lds<NB>::SW_OFF, "packed factor fits");
+      int st;
+      if constexpr (SOLVE == 2)
+        st = chol_inverse<S3_NT, TB>(Gs, Gi + b * r * r, r, eps, *sl, reinterpret_cast<double*>(lds));
+      else
+        st = sweep_inverse<S3_NT, TB>(Gs, Gi + b * r * r, r, eps, *sl);
       if (threadIdx.x == 0) status[b] = st;
     }
     return;
@@ -1944,6 +2217,27 @@ void launch_sweep(const float* G, float* Ginv, int32_t* status, int r, float eps
   else
     hipLaunchKernelGGL((sweep_inverse_kernel<1024, 4>), dim3((unsigned)B), dim3(1024), 0, st, G, Ginv, status, r, eps,
                        f);
+}
+
+// The Cholesky route as its own launch (fp32 storage): one workgroup per
+// segment, the packed factor in LDS.
+template <int NT, int TB, int RMAX>
+__global__ __launch_bounds__(NT) void chol_inverse_kernel(const float* G, float* Ginv, int32_t* status, int r,
+                                                          float eps) {
+  __shared__ SweepLds sl;
+  __shared__ double cp[RMAX * (RMAX + 1) / 2];
+  const int64_t b = blockIdx.x;
+  const int st = chol_inverse<NT, TB>(G + b * r * r, Ginv + b * r * r, r, eps, sl, cp);
+  if (threadIdx.x == 0) status[b] = st;
+}
+
+void launch_chol(const float* G, float* Ginv, int32_t* status, int r, float eps, int64_t B, hipStream_t st) {
+  if (r <= 64)
+    hipLaunchKernelGGL((chol_inverse_kernel<256, 4, 64>), dim3((unsigned)B), dim3(256), 0, st, G, Ginv, status, r,
+                       eps);
+  else   // 8 x 8 tiles: 256 threads, registers for both tiles without spills
+    hipLaunchKernelGGL((chol_inverse_kernel<256, 8, 128>), dim3((unsigned)B), dim3(256), 0, st, G, Ginv, status, r,
+                       eps);
 }
 
 // ===========================================================================
@@ -2327,7 +2621,8 @@ template <typename T, int RB, int NTC = 0>
 __global__ __launch_bounds__(64 * AI_WAVES) void apply_inverse_kernel(const float* __restrict__ Ginv,
                                                                       const float* __restrict__ M,
                                                                       T* __restrict__ Mp, int r, int64_t c1,
-                                                                      int64_t tasks) {
+                                                                      int64_t tasks,
+                                                                      const int32_t* __restrict__ status) {
   const int lane = threadIdx.x & 63;
   const int64_t task = (int64_t)blockIdx.x * AI_WAVES + (threadIdx.x >> 6);
   if (task >= tasks) return;
@@ -2335,6 +2630,12 @@ __global__ __launch_bounds__(64 * AI_WAVES) void apply_inverse_kernel(const floa
   const int64_t tiles = (c1 + 63) >> 6;
   const int grp = (int)(task % ngr);            // the waves of a workgroup share an M tile
   const int64_t ct = (task / ngr) % tiles, b = task / (ngr * tiles);
+  // a segment without a solve (NOT_SPD, ZERO) gets M'_b = 0, hence R_b = 0
+  // exactly, even where M_b is not finite: its output is the static branch,
+  // and the zero rows that mask it inside a neighbour's output tile never
+  // meet a non-finite R_b
+  const int sb = status[b];
+  const bool solved = sb == DYRA_SOLVE_OK || sb == DYRA_SOLVE_FALLBACK;
   const int i = lane & 15, g = lane >> 4;
   const float* Gb = Ginv + b * r * r;
   const float* Mb = M + b * r * c1;
@@ -2371,7 +2672,9 @@ __global__ __launch_bounds__(64 * AI_WAVES) void apply_inverse_kernel(const floa
       }
     }
   };
-  if constexpr (NTC > 0) {
+  if (!solved) {
+    // accumulators stay zero
+  } else if constexpr (NTC > 0) {
     float4 a[NTC][RB], m[NTC][4];                // chunks past r load as zeros
 #pragma unroll
     for (int t = 0; t < NTC; ++t) load(t, a[t], m[t]);
@@ -2414,21 +2717,22 @@ __global__ __launch_bounds__(64 * AI_WAVES) void apply_inverse_kernel(const floa
 // M'_b = Ginv_b M_b for B segments of r x c1: four row blocks per wave when
 // that still leaves at least two waves per SIMD of a 256-CU chip, else one.
 template <typename T>
-void launch_apply_inverse(const float* Gi, const float* M, T* Mp, int64_t B, int r, int64_t c1, hipStream_t st) {
+void launch_apply_inverse(const float* Gi, const float* M, T* Mp, int64_t B, int r, int64_t c1, const int32_t* stat,
+                          hipStream_t st) {
   const int64_t tiles = (c1 + 63) / 64, nrb = (r + 15) / 16;
   const int64_t wide = B * tiles * ((nrb + 3) / 4);
   if (nrb >= 4 && wide >= 2048) {
     hipLaunchKernelGGL((apply_inverse_kernel<T, 4>), dim3((unsigned)((wide + AI_WAVES - 1) / AI_WAVES)),
-                       dim3(64 * AI_WAVES), 0, st, Gi, M, Mp, r, c1, wide);
+                       dim3(64 * AI_WAVES), 0, st, Gi, M, Mp, r, c1, wide, stat);
   } else {
     const int64_t tasks = B * tiles * nrb;
     const dim3 grid((unsigned)((tasks + AI_WAVES - 1) / AI_WAVES)), block(64 * AI_WAVES);
     if (r <= 32)
-      hipLaunchKernelGGL((apply_inverse_kernel<T, 1, 2>), grid, block, 0, st, Gi, M, Mp, r, c1, tasks);
+      hipLaunchKernelGGL((apply_inverse_kernel<T, 1, 2>), grid, block, 0, st, Gi, M, Mp, r, c1, tasks, stat);
     else if (r <= 64)
-      hipLaunchKernelGGL((apply_inverse_kernel<T, 1, 4>), grid, block, 0, st, Gi, M, Mp, r, c1, tasks);
+      hipLaunchKernelGGL((apply_inverse_kernel<T, 1, 4>), grid, block, 0, st, Gi, M, Mp, r, c1, tasks, stat);
     else
-      hipLaunchKernelGGL((apply_inverse_kernel<T, 1>), grid, block, 0, st, Gi, M, Mp, r, c1, tasks);
+      hipLaunchKernelGGL((apply_inverse_kernel<T, 1>), grid, block, 0, st, Gi, M, Mp, r, c1, tasks, stat);
   }
 }
 
@@ -2524,16 +2828,20 @@ struct StageEvents {
 
 template <int NRB, int NB>
 void launch_s3_bf16(const bf16_t* Lt, int64_t ldt, const bf16_t* X, int64_t c1, int r, int64_t seg, int64_t n,
-                    int64_t B, float* M, float* G, float* Gi, int32_t* stat, float eps, bool sweep,
+                    int64_t B, float* M, float* G, float* Gi, int32_t* stat, float eps, int solve_mode,
                     hipStream_t st, int64_t lt_seg_rows = 0, bool x_rel = false, float* gpart = nullptr,
                     int gchunks = 0, int64_t gchunk = 0, int64_t gprows = 0) {
   const int strips = (int)cdiv(c1, S3_STRIP);
   if (gpart && gprows == 0)   // chunk Gram partials first (absolute L^T addressing only)
     hipLaunchKernelGGL((gram_partial_kernel<NB>), dim3((unsigned)(B * gchunks)), dim3(64), 0, st, Lt, ldt, r,
                        seg, n, gchunks, gchunk, gpart);
-  hipLaunchKernelGGL((s3_reduce_solve_kernel<NRB, NB>), dim3((unsigned)(B + B * strips)), dim3(S3_NT), 0, st, Lt,
-                     ldt, X, c1, r, seg, n, B, M, G, Gi, stat, eps, sweep ? 1 : 0, strips, lt_seg_rows, x_rel ? 1 : 0,
-                     gpart, gchunks, gprows);
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3((unsigned)(B + B * strips)), dim3(S3_NT), 0, st, Lt, ldt, X, c1, r, seg, n, B, M,
+                       G, Gi, stat, eps, strips, lt_seg_rows, x_rel ? 1 : 0, gpart, gchunks, gprows);
+  };
+  if (solve_mode == 2) go(s3_reduce_solve_kernel<NRB, NB, 2>);
+  else if (solve_mode == 1) go(s3_reduce_solve_kernel<NRB, NB, 1>);
+  else go(s3_reduce_solve_kernel<NRB, NB, 0>);
 }
 
 // S3, S4 and S5, shared by every structure: M_b, G_b, Ginv_b, M'_b and
@@ -2565,6 +2873,9 @@ void forward_residual(const dyra_spec& s, const char* plan, const void* X, int64
   // alike (one r = 128 solve: about 100 us against 140 us); Newton-Schulz
   // stays selectable.
   const bool ns = solver == DYRA_SOLVER_NS;
+  // solve inside the token-reduction launch: 1 the sweep, 2 the Cholesky
+  // route, 0 none (Newton-Schulz runs after it)
+  const int mode = ns ? 0 : (solver == DYRA_SOLVER_CHOL ? 2 : 1);
   // S3: M_b, G_b (bf16: with the sweep solve in the same launch)
   bool solved = false;
   if constexpr (BF) {
@@ -2572,10 +2883,10 @@ void forward_residual(const dyra_spec& s, const char* plan, const void* X, int64
     float* Gp = reinterpret_cast<float*>(ws + WL.Gp);
     const int gc = (int)WL.gchunks;
     const int64_t gk = WL.gchunk;
-    if (r <= 16) launch_s3_bf16<1, 1>(Lt, ldt, Xb, c1, r, seg, n, B, M, G, Gi, stat, eps, !ns, st, 0, false, Gp, gc, gk, gram_rows);
-    else if (r <= 32) launch_s3_bf16<2, 1>(Lt, ldt, Xb, c1, r, seg, n, B, M, G, Gi, stat, eps, !ns, st, 0, false, Gp, gc, gk, gram_rows);
-    else if (r <= 64) launch_s3_bf16<4, 2>(Lt, ldt, Xb, c1, r, seg, n, B, M, G, Gi, stat, eps, !ns, st, 0, false, Gp, gc, gk, gram_rows);
-    else launch_s3_bf16<8, 4>(Lt, ldt, Xb, c1, r, seg, n, B, M, G, Gi, stat, eps, !ns, st, 0, false, Gp, gc, gk, gram_rows);
+    if (r <= 16) launch_s3_bf16<1, 1>(Lt, ldt, Xb, c1, r, seg, n, B, M, G, Gi, stat, eps, mode, st, 0, false, Gp, gc, gk, gram_rows);
+    else if (r <= 32) launch_s3_bf16<2, 1>(Lt, ldt, Xb, c1, r, seg, n, B, M, G, Gi, stat, eps, mode, st, 0, false, Gp, gc, gk, gram_rows);
+    else if (r <= 64) launch_s3_bf16<4, 2>(Lt, ldt, Xb, c1, r, seg, n, B, M, G, Gi, stat, eps, mode, st, 0, false, Gp, gc, gk, gram_rows);
+    else launch_s3_bf16<8, 4>(Lt, ldt, Xb, c1, r, seg, n, B, M, G, Gi, stat, eps, mode, st, 0, false, Gp, gc, gk, gram_rows);
     solved = !ns;
   } else {
     const int tr = (int)cdiv(r, C3::BM), tcm = (int)cdiv(c1, C3::BN), tcg = (int)cdiv(r, C3::BN);
@@ -2598,11 +2909,13 @@ void forward_residual(const dyra_spec& s, const char* plan, const void* X, int64
       hipLaunchKernelGGL(ns_polish_kernel, dim3((unsigned)B), dim3(1024), 0, st, G, Gi, stat, r, eps, 60, tol,
                          accept);
       launch_sweep(G, Gi, stat, r, eps, B, true, st);
+    } else if (solver == DYRA_SOLVER_CHOL) {
+      launch_chol(G, Gi, stat, r, eps, B, st);
     } else {
       launch_sweep(G, Gi, stat, r, eps, B, false, st);
     }
   }
-  launch_apply_inverse<T>(Gi, M, Mp, B, r, c1, st);
+  launch_apply_inverse<T>(Gi, M, Mp, B, r, c1, stat, st);
   E.mark(3, st);
   // S5: R^T (c2 x B r) = W_res^T (c2 x c1) . M' (B r x c1)^T; bf16: split
   // over K when the output has few tiles, else the persistent output kernel
@@ -2654,11 +2967,11 @@ void left_step_bf16(const dyra_spec& s, const char* plan, const bf16_t* X, int64
                      c2, B * r);
   // K_b, Q_b^T, (K_b + lambda I)^-1: c2 is the reduction ("token") axis
   const int64_t nn = B * c2;
-  if (r <= 16) launch_s3_bf16<1, 1>(R, c2, Wrt, c1, r, c2, nn, B, Qt, K, Kinv, kst, eps, true, st, r, true);
-  else if (r <= 32) launch_s3_bf16<2, 1>(R, c2, Wrt, c1, r, c2, nn, B, Qt, K, Kinv, kst, eps, true, st, r, true);
-  else if (r <= 64) launch_s3_bf16<4, 2>(R, c2, Wrt, c1, r, c2, nn, B, Qt, K, Kinv, kst, eps, true, st, r, true);
-  else launch_s3_bf16<8, 4>(R, c2, Wrt, c1, r, c2, nn, B, Qt, K, Kinv, kst, eps, true, st, r, true);
-  launch_apply_inverse<bf16_t>(Kinv, Qt, Zt, B, r, c1, st);
+  if (r <= 16) launch_s3_bf16<1, 1>(R, c2, Wrt, c1, r, c2, nn, B, Qt, K, Kinv, kst, eps, 1, st, r, true);
+  else if (r <= 32) launch_s3_bf16<2, 1>(R, c2, Wrt, c1, r, c2, nn, B, Qt, K, Kinv, kst, eps, 1, st, r, true);
+  else if (r <= 64) launch_s3_bf16<4, 2>(R, c2, Wrt, c1, r, c2, nn, B, Qt, K, Kinv, kst, eps, 1, st, r, true);
+  else launch_s3_bf16<8, 4>(R, c2, Wrt, c1, r, c2, nn, B, Qt, K, Kinv, kst, eps, 1, st, r, true);
+  launch_apply_inverse<bf16_t>(Kinv, Qt, Zt, B, r, c1, kst, st);
   // L_b = X_b Z_b into [T | L] and L^T
   const int tiles_n = (int)cdiv(r, CfgL::BN);
   hipLaunchKernelGGL(s1_left_kernel<CfgL>, dim3((unsigned)(cdiv(n, CfgL::BM) * tiles_n)), dim3(CfgL::NT), 0, st, X,

@@ -27,8 +27,9 @@ design notes as well):
   * R0 = top-r right singular vectors of W_res (orthonormal rows), so the
     first left step is L = X P with P = W_res R0^T.
   * ridge: lambda = eps * trace(G) / r added to G = L^T L; trace(G) == 0
-    gives R = 0.  eps == 0 solves the normal equations by minimum-norm
-    least squares.
+    gives R = 0.  eps == 0 (no ridge) solves the normal equations by
+    Cholesky when G is numerically nonsingular (every pivot above 2^-16 of
+    its diagonal) and otherwise drops the correction (R = 0).
   * Monarch: W_hat = blockdiag(B1_a) . Pi . blockdiag(B2_j), Pi the
     reshape(m, m)-transpose permutation, each (a, j) block of W fitted by
     its rank-1 truncated SVD.
@@ -222,11 +223,35 @@ def ridge(K: np.ndarray, eps: float) -> float:
     return eps * np.trace(K) / r
 
 
+# eps == 0 only: a Cholesky pivot d_j (the squared distance of column j of L
+# from the span of the earlier columns) at or below SINGULAR_PIVOT_REL times
+# the diagonal K_jj (the squared length of column j) marks K as singular.
+SINGULAR_PIVOT_REL = 2.0 ** -16
+
+
+def gram_is_singular(K: np.ndarray) -> bool:
+    """Numerical rank test of an unridged Gram matrix K = L^T L: a Cholesky
+    pivot d_j <= SINGULAR_PIVOT_REL * K_jj (sin^2 of the angle between column
+    j and the earlier columns), or a non-positive pivot."""
+    r = K.shape[0]
+    C = np.zeros_like(K)
+    for j in range(r):
+        d = K[j, j] - C[j, :j] @ C[j, :j]
+        if not d > SINGULAR_PIVOT_REL * K[j, j]:
+            return True
+        C[j, j] = np.sqrt(d)
+        C[j + 1:, j] = (K[j + 1:, j] - C[j + 1:, :j] @ C[j, :j]) / C[j, j]
+    return False
+
+
 def spd_solve(K: np.ndarray, rhs: np.ndarray, eps: float) -> np.ndarray:
     """Solve (K + lambda I) Z = rhs for symmetric PSD K.
 
     eps > 0: Cholesky solve ([P2] 2.4 names Cholesky for small r).
-    eps == 0: minimum-norm least squares on the normal equations.
+    eps == 0 (no ridge; the pages always add one): the Cholesky solve of the
+    normal equations when K is numerically nonsingular (gram_is_singular),
+    else Z = 0: the correction is dropped rather than fitted to a singular
+    system, so the output falls back to the static branch.
     trace(K) == 0: Z = 0.
     """
     if not np.any(K):
@@ -234,7 +259,9 @@ def spd_solve(K: np.ndarray, rhs: np.ndarray, eps: float) -> np.ndarray:
     if eps > 0:
         lam = ridge(K, eps)
         return sla.cho_solve(sla.cho_factor(K + lam * np.eye(K.shape[0]), lower=True), rhs)
-    return np.linalg.lstsq(K, rhs, rcond=None)[0]
+    if gram_is_singular(K):
+        return np.zeros_like(rhs)
+    return sla.cho_solve(sla.cho_factor(K, lower=True), rhs)
 
 
 def right_step(X: np.ndarray, W_res: np.ndarray, L: np.ndarray, eps: float) -> np.ndarray:

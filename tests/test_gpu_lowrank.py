@@ -9,7 +9,8 @@ from input_adaptive_rank_amd import dyra as D
 from input_adaptive_rank_amd import synth
 from oracle import dyra_oracle as O
 
-from gpu_cases import TOL, gpu_forward, log, oracle_prepare, rounded_prep, run_same_factor_case
+from gpu_cases import (TOL, gpu_forward, host_factors_from_oracle, log, oracle_prepare, rounded_prep,
+                       run_same_factor_case)
 
 pytestmark = pytest.mark.gpu
 
@@ -151,3 +152,84 @@ def test_dense_ref(dtype):
     err = O.rel_fro(Y.float().cpu().numpy().astype(float), ref)
     # fp32: accumulation rounding only; bf16: plus the output rounding (2^-9)
     assert err <= (1e-5 if dtype == synth.DT_F32 else 4e-3), err
+
+
+# ---------------------------------------------------------------------------
+# the Cholesky route (DYRA_SOLVER_CHOL): factor, triangular inverse, W^T W
+# ---------------------------------------------------------------------------
+
+CHOL = [sc(W["vitb_fc1"], name=f"chol_r{r}", B=3, s=150, c1=256, c2=264, k=32, r=r, solver="chol")
+        for r in (8, 16, 32, 56, 64)] + [
+    sc(W["vitl_fc1"], name="chol_r128", B=2, s=300, c1=256, c2=384, k=64, r=128, solver="chol"),
+    sc(W["vitb_fc1"], name="chol_fp32_r16", B=3, s=77, c1=192, c2=200, k=24, r=16, dtype=synth.DT_F32,
+       solver="chol"),
+    sc(W["vitl_fc1"], name="chol_fp32_r128", B=2, s=300, c1=256, c2=384, k=64, r=128, dtype=synth.DT_F32,
+       solver="chol"),
+]
+
+
+@pytest.mark.parametrize("w", CHOL, ids=lambda w: w.name)
+def test_cholesky_route(w):
+    err, status, _, _ = run_same_factor_case(w, solver="chol")
+    assert np.all(status == D.SOLVE_OK)
+
+
+def test_cholesky_route_full_size_vitl():
+    err, status, _, _ = run_same_factor_case(W["vitl_fc1"], solver="chol")
+    assert np.all(status == D.SOLVE_OK)
+
+
+# ---------------------------------------------------------------------------
+# no ridge (eps = 0): a numerically singular G_b drops the correction
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("solver", ["auto", "chol"])
+@pytest.mark.parametrize("dtype", [synth.DT_BF16, synth.DT_F32])
+def test_unridged_segment_shorter_than_rank_drops_the_correction(solver, dtype):
+    """s < r at eps = 0: G_b has rank s, a pivot falls below 2^-16 of its
+    diagonal, the status is NOT_SPD and Y_b = X_b W_hat + bias, as in the
+    oracle's reading of an unridged singular system."""
+    w = sc(W["vitb_fc1"], name=f"s_lt_r_eps0_{solver}", B=6, s=5, c1=128, c2=128, k=16, r=16, dtype=dtype)
+    err, status, Yg, Y_or = run_same_factor_case(w, eps=0.0, solver=solver)
+    assert np.all(status == D.SOLVE_NOT_SPD), status
+    inp = synth.make_inputs(w)
+    rp = rounded_prep(oracle_prepare(w, inp.W), w.dtype)
+    static = O.static_apply(w.kind, inp.X, rp["static"]) + inp.bias
+    np.testing.assert_array_equal(Y_or, static)
+
+
+@pytest.mark.parametrize("solver", ["auto", "chol"])
+def test_unridged_full_rank_segments_solve(solver):
+    w = sc(W["vitb_fc1"], name=f"eps0_full_rank_{solver}", B=3, s=200, c1=256, c2=264, k=32, r=32)
+    err, status, _, _ = run_same_factor_case(w, eps=0.0, solver=solver)
+    assert np.all(status == D.SOLVE_OK)
+
+
+def test_non_finite_input_stays_in_its_segment():
+    """A NaN in one token of segment 1: that segment's trace is NaN, its
+    status NOT_SPD and R_1 = 0, so only the NaN token's own output row is
+    non-finite and the segment's other rows are the static branch
+    X_b W_hat + bias; every other segment's output is bit for bit that of
+    the clean input (tiles shared across the segment boundary included)."""
+    import torch  # noqa: F401
+    w = sc(W["vitb_fc1"], name="nan_segment", B=4, s=100, c1=256, c2=264, k=32, r=16)
+    inp = synth.make_inputs(w)
+    prep = oracle_prepare(w, inp.W)
+    f = host_factors_from_oracle(prep)
+    (clean,), st_clean = gpu_forward(w, f, inp.X, inp.bias)
+    Xn = inp.X.copy()
+    Xn[150, 7] = np.nan
+    (dirty,), st = gpu_forward(w, f, Xn, inp.bias)
+    seg1 = dirty[100:200]
+    bad_rows = np.where(~np.isfinite(seg1).all(axis=1))[0].tolist()
+    log(f"  nan_segment: status clean {st_clean.tolist()} dirty {st.tolist()}; non-finite rows of segment 1: "
+        f"{bad_rows}")
+    assert st_clean.tolist() == [D.SOLVE_OK] * 4
+    assert st.tolist() == [D.SOLVE_OK, D.SOLVE_NOT_SPD, D.SOLVE_OK, D.SOLVE_OK]
+    assert bad_rows == [50]
+    rp = rounded_prep(prep, w.dtype)
+    keep = np.r_[100:150, 151:200]
+    static = O.static_apply(w.kind, inp.X[keep], rp["static"]) + inp.bias
+    assert O.rel_fro(dirty[keep], static) <= TOL[w.dtype]
+    for b in (0, 2, 3):
+        np.testing.assert_array_equal(dirty[b * 100:(b + 1) * 100], clean[b * 100:(b + 1) * 100])

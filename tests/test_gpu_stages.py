@@ -20,6 +20,9 @@ CASES = [
     sc(W["vitl_fc1"], name="stage_r64", B=4, s=257, c1=256, c2=512, k=64, r=64),
     sc(W["vitl_fc1"], name="stage_r128_ns", B=2, s=300, c1=256, c2=384, k=64, r=128, solver="ns"),
     sc(W["vitl_fc1"], name="stage_r128_chol", B=2, s=300, c1=256, c2=384, k=64, r=128, solver="chol"),
+    sc(W["vitl_fc1"], name="stage_r64_chol", B=4, s=257, c1=256, c2=512, k=64, r=64, solver="chol"),
+    sc(W["vitb_fc1"], name="stage_fp32_chol", B=3, s=77, c1=192, c2=200, k=24, r=16, dtype=synth.DT_F32,
+       solver="chol"),
     sc(W["vitb_fc1"], name="stage_fp32", B=3, s=77, c1=192, c2=200, k=24, r=16, dtype=synth.DT_F32),
     sc(W["vitl_fc1"], name="stage_k256_r64", B=3, s=150, c1=384, c2=384, k=256, r=64),
 ]

@@ -512,6 +512,36 @@ def test_cholesky_textbook_matches_definition():
     np.testing.assert_allclose(C, sla.cholesky(G, lower=True), atol=1e-12)
 
 
+@pytest.mark.parametrize("sin2,singular", [(2.0 ** -15, False), (2.0 ** -17, True), (0.0, True)])
+def test_unridged_solve_rank_test_on_two_columns(sin2, singular):
+    """eps = 0: two unit columns at an angle theta give K = [[1, c], [c, 1]]
+    with Cholesky pivots 1 and 1 - c^2 = sin^2 theta; the system counts as
+    singular exactly when sin^2 theta <= 2^-16, and then the solve gives 0."""
+    c = np.sqrt(1.0 - sin2)
+    K = np.array([[1.0, c], [c, 1.0]])
+    assert O.gram_is_singular(K) == singular
+    rhs = np.array([[1.0, 2.0], [3.0, -1.0]])
+    Z = O.spd_solve(K, rhs, 0.0)
+    if singular:
+        assert not np.any(Z)
+    else:
+        np.testing.assert_allclose(K @ Z, rhs, atol=1e-9 / sin2)
+
+
+def test_unridged_forward_with_fewer_tokens_than_rank_falls_back_to_static():
+    """s < r at eps = 0: L_b has rank s < r, G_b is singular, R_b = 0 and the
+    segment's output is exactly X_b W_hat + bias; with a ridge it is not."""
+    rng = _rng(83)
+    W, *_ = _power_law_w(rng, 24, 32)
+    prep = _prep_lowrank(W, 4, 6)
+    X = _aniso_x(rng, 2 * 4, 24)                                  # 2 segments of 4 tokens, r = 6
+    bias = rng.standard_normal(32)
+    Y0 = O.forward(X, prep, bias, 2, 4, eps=0.0)
+    np.testing.assert_allclose(Y0, X @ prep["W_hat"] + bias, atol=1e-12)
+    Y6 = O.forward(X, prep, bias, 2, 4, eps=1e-6)
+    assert O.rel_fro(Y6, X @ prep["W_hat"] + bias) > 1e-3
+
+
 def test_spd_solve_zero_trace_guard():
     G = np.zeros((3, 3))
     H = np.ones((3, 4))
