@@ -68,6 +68,15 @@ def lib():
     """Loads libdyra.so (built by input_adaptive_rank_amd.build)."""
     global _lib
     if _lib is None:
+        # One HIP runtime per process: PyTorch ships its own libamdhip64
+        # (same soname as the system one that libdyra.so is linked against).
+        # Loading torch first lets the dynamic loader satisfy libdyra.so's
+        # dependency with torch's copy; loading libdyra.so first would map a
+        # second runtime beside torch's, and that one finds no device.
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with python -m input_adaptive_rank_amd.build")
         L = ctypes.CDLL(LIB_PATH)

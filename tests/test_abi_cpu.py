@@ -222,3 +222,19 @@ def test_noalloc_rejects_calls_past_its_static_workspace_before_any_hip_call():
     assert L.dyra_forward_noalloc(ctypes.byref(ok), *bad) == -1        # negative ridge
     unaligned = (1 << 12, 1 << 13, None, 1 << 14, 32, 1029, synth.DT_BF16, 1e-6, 0, 6, None)
     assert L.dyra_forward_noalloc(ctypes.byref(ok), *unaligned) == -1  # misaligned status_out
+
+
+def test_one_hip_runtime_per_process_whatever_the_import_order():
+    """The binding loads libdyra.so after torch, so the process maps a single
+    libamdhip64 (torch's) even when the library is asked for first."""
+    import subprocess
+    import sys
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "from input_adaptive_rank_amd import dyra\n"
+            "dyra.lib()\n"
+            "import torch\n"
+            "paths = {l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}\n"
+            "print(len(paths), sorted(paths))\n") % D.os.path.dirname(D.os.path.dirname(D.LIB_PATH))
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.split()[0] == "1", out.stdout
