@@ -139,6 +139,35 @@ int dyra_prepare_sizes(const dyra_spec* spec, dyra_sizes* out);
 int dyra_prepare(const dyra_spec* spec, const double* W, dyra_host_factors* out,
                  int32_t nthreads);
 
+/*
+ * Offline preparation with an input-aware static start (low-rank only): the
+ * static factors minimise the output error on calibration rows instead of
+ * the weight error.  A transform S (c1 x c1) is built from the rows, and
+ * W_hat = S^-1 SVD_k(S W), split as U = S^-1 U_k sqrt(sigma),
+ * V = sqrt(sigma) V_k^T; the residual, R0 and P follow from W_hat as in
+ * dyra_prepare, and the device forward is unchanged.
+ *   X_cal: host [n_cal][c1] float64 calibration rows (read only, finite).
+ *   mode:  DYRA_INPUT_AWARE_DIAG: S = diag(channel RMS over the rows), each
+ *          raised to at least 1e-6 of the largest;
+ *          DYRA_INPUT_AWARE_CHOL: S = C^T with C C^T = X_cal^T X_cal / n_cal
+ *          + delta I, delta = 1e-6 trace(X_cal^T X_cal / n_cal) / c1, so that
+ *          ||S (W - W_hat)||_F = ||X_cal (W - W_hat)||_F / sqrt(n_cal) up to
+ *          delta: W_hat is the best rank-k fit in that norm.
+ *   out:   as for dyra_prepare (U, V, P, R0, Wres, res_sv).
+ * Errors: EINVAL (null pointer, structure not low-rank, unknown mode,
+ * non-finite or all-zero X_cal), ESHAPE (n_cal <= 0 or spec sizes),
+ * ENOCONV.
+ * Source: paperlayer.ai App. B (input-aware decomposition with activation-
+ * based diagonal scaling or a Cholesky factor of the input covariance) and
+ * nanless.github.io DyRA digest, "how the existing structured-matrix
+ * methods differ" (transform from calibration activations, truncated SVD
+ * of the transformed weight) and its input-aware x DyRA paragraph.
+ */
+#define DYRA_INPUT_AWARE_DIAG 1
+#define DYRA_INPUT_AWARE_CHOL 2
+int dyra_prepare_input_aware(const dyra_spec* spec, const double* W, const double* X_cal, int64_t n_cal,
+                             int32_t mode, dyra_host_factors* out, int32_t nthreads);
+
 /* Bytes of the packed device plan for (spec, dtype).  Errors: EINVAL, ESHAPE, EDTYPE. */
 int dyra_plan_size(const dyra_spec* spec, int32_t dtype, size_t* bytes);
 

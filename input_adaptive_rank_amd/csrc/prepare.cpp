@@ -172,7 +172,135 @@ inline void put(void* base, size_t byte_off, size_t idx, double v, int dtype) {
   }
 }
 
+// W_res = W - W_hat; R0 = top-r right singular vectors of W_res and
+// P = W_res R0^T, written to out (with res_sv).
+int finish_residual(Pool& pool, const dyra_spec& s, const Mat& Wm, const Mat& What, dyra_host_factors* out) {
+  Mat Wres(s.c1, s.c2);
+  for (size_t i = 0; i < Wres.a.size(); ++i) Wres.a[i] = Wm.a[i] - What.a[i];
+  Mat Ud, V;
+  std::vector<double> rho;
+  if (!dyra_host::svd_top(pool, Wres, s.r, Ud, rho, V, false, true)) return DYRA_ENOCONV;
+  Mat P = dyra_host::matmul(pool, Wres, V);     // c1 x r
+  for (int q = 0; q < s.r; ++q) {
+    for (int64_t j = 0; j < s.c2; ++j) out->R0[(size_t)q * s.c2 + j] = V(j, q);
+    out->res_sv[q] = rho[(size_t)q];
+  }
+  std::memcpy(out->P, P.a.data(), sizeof(double) * P.a.size());
+  std::memcpy(out->Wres, Wres.a.data(), sizeof(double) * Wres.a.size());
+  return DYRA_OK;
+}
+
+// Lower Cholesky factor of a symmetric positive definite K (n x n), column
+// by column; the rows below each pivot run in parallel.  False if a pivot is
+// not positive.
+bool cholesky_lower(Pool& pool, const Mat& K, Mat& C) {
+  const int64_t n = K.rows;
+  C = K;
+  for (int64_t j = 0; j < n; ++j) {
+    const double* cj = C.row(j);
+    double d = C(j, j);
+    for (int64_t q = 0; q < j; ++q) d -= cj[q] * cj[q];
+    if (!(d > 0.0) || !std::isfinite(d)) return false;
+    const double piv = std::sqrt(d);
+    C(j, j) = piv;
+    pool.parallel_for(n - j - 1, [&](int64_t a, int64_t b) {
+      for (int64_t i = j + 1 + a; i < j + 1 + b; ++i) {
+        double* ci = C.row(i);
+        double v = ci[j];
+        for (int64_t q = 0; q < j; ++q) v -= ci[q] * cj[q];
+        ci[j] = v / piv;
+      }
+    });
+  }
+  for (int64_t i = 0; i < n; ++i)
+    for (int64_t j = i + 1; j < n; ++j) C(i, j) = 0.0;
+  return true;
+}
+
 }  // namespace
+
+extern "C" int dyra_prepare_input_aware(const dyra_spec* spec, const double* W, const double* X_cal,
+                                        int64_t n_cal, int32_t mode, dyra_host_factors* out, int32_t nthreads) {
+  if (!spec || !W || !X_cal || !out) return DYRA_EINVAL;
+  int rc = validate_spec(spec);
+  if (rc) return rc;
+  const dyra_spec& s = *spec;
+  if (s.kind != DYRA_LOWRANK) return DYRA_EINVAL;
+  if (mode != DYRA_INPUT_AWARE_DIAG && mode != DYRA_INPUT_AWARE_CHOL) return DYRA_EINVAL;
+  if (n_cal <= 0) return DYRA_ESHAPE;
+  if (!out->U || !out->V || !out->P || !out->R0 || !out->Wres || !out->res_sv) return DYRA_EINVAL;
+  try {
+    Pool pool(nthreads);
+    const int64_t c1 = s.c1, c2 = s.c2;
+    Mat Wm(c1, c2);
+    std::memcpy(Wm.a.data(), W, sizeof(double) * (size_t)(c1 * c2));
+    Mat Xc(n_cal, c1);
+    std::memcpy(Xc.a.data(), X_cal, sizeof(double) * (size_t)(n_cal * c1));
+    for (double v : Xc.a)
+      if (!std::isfinite(v)) return DYRA_EINVAL;
+    // S W, and later U_f = S^-1 (U_k sqrt(sigma))
+    Mat SW(c1, c2), Ct;
+    std::vector<double> sdiag;
+    if (mode == DYRA_INPUT_AWARE_DIAG) {
+      sdiag.assign((size_t)c1, 0.0);
+      for (int64_t t = 0; t < n_cal; ++t)
+        for (int64_t i = 0; i < c1; ++i) sdiag[(size_t)i] += Xc(t, i) * Xc(t, i);
+      double mx = 0.0;
+      for (auto& v : sdiag) {
+        v = std::sqrt(v / (double)n_cal);
+        mx = std::max(mx, v);
+      }
+      if (!(mx > 0.0)) return DYRA_EINVAL;
+      for (auto& v : sdiag) v = std::max(v, 1e-6 * mx);
+      for (int64_t i = 0; i < c1; ++i)
+        for (int64_t j = 0; j < c2; ++j) SW(i, j) = sdiag[(size_t)i] * Wm(i, j);
+    } else {
+      Mat K = dyra_host::gram_cols(pool, Xc);    // X^T X
+      double tr = 0.0;
+      for (int64_t i = 0; i < c1; ++i) tr += K(i, i);
+      if (!(tr > 0.0)) return DYRA_EINVAL;
+      for (auto& v : K.a) v /= (double)n_cal;
+      for (int64_t i = 0; i < c1; ++i) K(i, i) += 1e-6 * tr / (double)n_cal / (double)c1;
+      Mat C;
+      if (!cholesky_lower(pool, K, C)) return DYRA_ENOCONV;
+      SW = dyra_host::matmul_tn(pool, C, Wm);     // C^T W
+      Ct = dyra_host::transpose(pool, C);          // S = C^T, upper triangular
+    }
+    Mat U, V;
+    std::vector<double> sv;
+    if (!dyra_host::svd_top(pool, SW, s.k, U, sv, V)) return DYRA_ENOCONV;
+    const int k = s.k;
+    Mat Uf(c1, k), Vf(k, c2);
+    for (int q = 0; q < k; ++q) {
+      const double rs = std::sqrt(sv[(size_t)q]);
+      for (int64_t i = 0; i < c1; ++i) Uf(i, q) = U(i, q) * rs;
+      for (int64_t j = 0; j < c2; ++j) Vf(q, j) = rs * V(j, q);
+    }
+    if (mode == DYRA_INPUT_AWARE_DIAG) {
+      for (int64_t i = 0; i < c1; ++i)
+        for (int q = 0; q < k; ++q) Uf(i, q) /= sdiag[(size_t)i];
+    } else {
+      // back substitution C^T x = b for each of the k columns
+      pool.parallel_for(k, [&](int64_t q0, int64_t q1) {
+        for (int64_t q = q0; q < q1; ++q)
+          for (int64_t i = c1 - 1; i >= 0; --i) {
+            const double* ct = Ct.row(i);
+            double v = Uf(i, q);
+            for (int64_t j = i + 1; j < c1; ++j) v -= ct[j] * Uf(j, q);
+            Uf(i, q) = v / ct[i];
+          }
+      });
+    }
+    Mat What = dyra_host::matmul(pool, Uf, Vf);
+    std::memcpy(out->U, Uf.a.data(), sizeof(double) * Uf.a.size());
+    std::memcpy(out->V, Vf.a.data(), sizeof(double) * Vf.a.size());
+    rc = finish_residual(pool, s, Wm, What, out);
+    if (rc) return rc;
+  } catch (...) {
+    return DYRA_EINVAL;
+  }
+  return DYRA_OK;
+}
 
 extern "C" int dyra_prepare(const dyra_spec* spec, const double* W, dyra_host_factors* out,
                             int32_t nthreads) {
@@ -206,20 +334,8 @@ extern "C" int dyra_prepare(const dyra_spec* spec, const double* W, dyra_host_fa
       std::memcpy(out->S, S.data(), sizeof(double) * S.size());
       std::memcpy(out->Vb, Vb.data(), sizeof(double) * Vb.size());
     }
-    // W_res = W - W_hat
-    Mat Wres(s.c1, s.c2);
-    for (size_t i = 0; i < Wres.a.size(); ++i) Wres.a[i] = Wm.a[i] - What.a[i];
-    // R0 = top-r right singular vectors of W_res, P = W_res R0^T
-    Mat Ud, V;
-    std::vector<double> rho;
-    if (!dyra_host::svd_top(pool, Wres, s.r, Ud, rho, V, false, true)) return DYRA_ENOCONV;
-    Mat P = dyra_host::matmul(pool, Wres, V);     // c1 x r
-    for (int q = 0; q < s.r; ++q) {
-      for (int64_t j = 0; j < s.c2; ++j) out->R0[(size_t)q * s.c2 + j] = V(j, q);
-      out->res_sv[q] = rho[(size_t)q];
-    }
-    std::memcpy(out->P, P.a.data(), sizeof(double) * P.a.size());
-    std::memcpy(out->Wres, Wres.a.data(), sizeof(double) * Wres.a.size());
+    rc = finish_residual(pool, s, Wm, What, out);
+    if (rc) return rc;
   } catch (...) {
     return DYRA_EINVAL;
   }

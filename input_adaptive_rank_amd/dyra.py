@@ -85,6 +85,8 @@ def lib():
         sig = {
             "dyra_prepare_sizes": [SP, ctypes.POINTER(Sizes)],
             "dyra_prepare": [SP, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(HostFactors), I32],
+            "dyra_prepare_input_aware": [SP, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
+                                         I64, I32, ctypes.POINTER(HostFactors), I32],
             "dyra_plan_size": [SP, I32, ctypes.POINTER(SZ)],
             "dyra_plan_pack": [SP, ctypes.POINTER(HostFactors), I32, P],
             "dyra_workspace_size": [SP, I64, I64, I32, ctypes.POINTER(SZ)],
@@ -165,6 +167,29 @@ def prepare(W: np.ndarray, spec: Spec, nthreads: int = 0) -> dict:
     out = {f: np.zeros(shapes[f]) for f in _FACTORS if sizes[f] > 0}
     hf = _host_factors(spec, out)
     _check("dyra_prepare", lib().dyra_prepare(ctypes.byref(spec), _dptr(W), ctypes.byref(hf), nthreads))
+    return out
+
+
+INPUT_AWARE_DIAG, INPUT_AWARE_CHOL = 1, 2
+INPUT_AWARE = {"diag": INPUT_AWARE_DIAG, "chol": INPUT_AWARE_CHOL}
+
+
+def prepare_input_aware(W: np.ndarray, spec: Spec, X_cal: np.ndarray, mode: int, nthreads: int = 0) -> dict:
+    """Offline fit with an input-aware static start from calibration rows
+    X_cal (n_cal x c1).  Returns float64 arrays keyed like dyra_host_factors."""
+    W = np.ascontiguousarray(W, dtype=np.float64)
+    X_cal = np.ascontiguousarray(X_cal, dtype=np.float64)
+    if W.shape != (spec.c1, spec.c2):
+        raise ValueError(f"W must be {spec.c1} x {spec.c2}")
+    if X_cal.ndim != 2 or X_cal.shape[1] != spec.c1:
+        raise ValueError(f"X_cal must be n_cal x {spec.c1}")
+    sizes = prepare_sizes(spec)
+    shapes = _factor_shapes(spec)
+    out = {f: np.zeros(shapes[f]) for f in _FACTORS if sizes[f] > 0}
+    hf = _host_factors(spec, out)
+    _check("dyra_prepare_input_aware",
+           lib().dyra_prepare_input_aware(ctypes.byref(spec), _dptr(W), _dptr(X_cal), X_cal.shape[0], mode,
+                                          ctypes.byref(hf), nthreads))
     return out
 
 

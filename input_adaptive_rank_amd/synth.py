@@ -171,6 +171,20 @@ def make_inputs(w: Workload, n_rows: int | None = None) -> Inputs:
                   W_exact=W_exact, spectrum=s)
 
 
+def make_calibration(w: Workload, n_cal: int) -> np.ndarray:
+    """n_cal calibration rows from the workload's input law: the same outlier
+    channels and channel scales as make_inputs (drawn from the same seed),
+    rows from an independent stream (seed + 1000003), storage-rounded."""
+    rng = np.random.default_rng(w.seed)
+    outliers = rng.choice(w.c1, w.n_out, replace=False) if w.n_out > 0 else np.zeros(0, int)
+    rz = np.random.default_rng(w.seed + 1000003)
+    if w.heavy_tail:
+        Z = rz.standard_t(4.0, size=(n_cal, w.c1)) / np.sqrt(2.0)
+    else:
+        Z = rz.standard_normal((n_cal, w.c1))
+    return round_storage(Z * channel_scales(w.c1, outliers), w.dtype)
+
+
 def orthonormal_rows_input(rng: np.random.Generator, n: int, c1: int, scale: float = 1.0):
     """X with X^T X = scale^2 I (n >= c1): scaled Haar-orthonormal columns."""
     return scale * haar_columns(rng.standard_normal((n, c1)))

@@ -168,6 +168,43 @@ def blast_apply(X: np.ndarray, f: dict) -> np.ndarray:
     return np.hstack(out)
 
 
+# ---------------------------------------------------------------------------
+# Input-aware static start ([P2] App. B "Background on Structured Matrices";
+# [P5] "how the existing structured-matrix methods differ": a transform S
+# built from calibration activations, the weight written through S and its
+# inverse, and a truncated SVD of the transformed weight).  With Y = X W the
+# transform acts on the input side: W_hat = S^-1 SVD_k(S W), which for
+# S^T S = X_cal^T X_cal / n is the rank-k W_hat closest to W in the
+# calibration output norm ||X_cal (W - W_hat)||_F.
+# ---------------------------------------------------------------------------
+
+INPUT_AWARE_DIAG = 1      # S = diag(channel RMS over the calibration rows)
+INPUT_AWARE_CHOL = 2      # S = C^T, C C^T = X_cal^T X_cal / n + delta I
+CALIB_RIDGE = 1e-6        # delta = CALIB_RIDGE * trace(X_cal^T X_cal / n) / c1
+CALIB_FLOOR = 1e-6        # a channel RMS below CALIB_FLOOR * the largest is raised to it
+
+
+def input_transform(X_cal: np.ndarray, mode: int) -> np.ndarray:
+    """The c1 x c1 transform S of an input-aware fit."""
+    n, c1 = X_cal.shape
+    if mode == INPUT_AWARE_DIAG:
+        rms = np.sqrt(np.mean(X_cal * X_cal, axis=0))
+        return np.diag(np.maximum(rms, CALIB_FLOOR * rms.max()))
+    if mode == INPUT_AWARE_CHOL:
+        K = X_cal.T @ X_cal / n
+        K = K + CALIB_RIDGE * np.trace(K) / c1 * np.eye(c1)
+        return cholesky_lower(K).T
+    raise ValueError(mode)
+
+
+def fit_lowrank_input_aware(W: np.ndarray, k: int, S: np.ndarray) -> dict:
+    """W_hat = S^-1 SVD_k(S W), split as U_f = S^-1 U_k sqrt(s_k),
+    V_f = sqrt(s_k) V_k^T (the sqrt(sigma) split of the plain fit)."""
+    U, s, Vt = np.linalg.svd(S @ W, full_matrices=False)
+    rs = np.sqrt(s[:k])
+    return {"U": np.linalg.solve(S, U[:, :k] * rs), "V": rs[:, None] * Vt[:k], "sv": s}
+
+
 def static_dense(kind: int, f: dict) -> np.ndarray:
     return {KIND_LOWRANK: lowrank_dense, KIND_MONARCH: monarch_dense,
             KIND_BLAST: blast_dense}[kind](f)
@@ -201,9 +238,15 @@ def residual_init(W_res: np.ndarray, r: int):
     return R0, W_res @ R0.T, rho[:r]
 
 
-def prepare(W: np.ndarray, kind: int, r: int, k=0, mblk=0, nb=0, rb=0) -> dict:
-    """W = W_hat + W_res; R0, P from the residual  ([P5] split equation)."""
-    f = fit_static(kind, W, k=k, mblk=mblk, nb=nb, rb=rb)
+def prepare(W: np.ndarray, kind: int, r: int, k=0, mblk=0, nb=0, rb=0, calib=None) -> dict:
+    """W = W_hat + W_res; R0, P from the residual  ([P5] split equation).
+    calib = (X_cal, mode): the input-aware static start (low-rank only)."""
+    if calib is not None:
+        if kind != KIND_LOWRANK:
+            raise ValueError("the input-aware fit is a truncated SVD: low-rank only")
+        f = fit_lowrank_input_aware(W, k, input_transform(calib[0], calib[1]))
+    else:
+        f = fit_static(kind, W, k=k, mblk=mblk, nb=nb, rb=rb)
     W_hat = static_dense(kind, f)
     W_res = W - W_hat
     R0, P, rho = residual_init(W_res, r)

@@ -233,3 +233,24 @@ def test_non_finite_input_stays_in_its_segment():
     assert O.rel_fro(dirty[keep], static) <= TOL[w.dtype]
     for b in (0, 2, 3):
         np.testing.assert_array_equal(dirty[b * 100:(b + 1) * 100], clean[b * 100:(b + 1) * 100])
+
+
+# ---------------------------------------------------------------------------
+# input-aware static start: a prepare-only variant, the forward is unchanged
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("mode", [D.INPUT_AWARE_DIAG, D.INPUT_AWARE_CHOL])
+def test_input_aware_start(mode):
+    """Same-factor parity with the oracle's input-aware prepare, and the
+    library's own input-aware prepare end to end against the oracle's."""
+    w = sc(W["vitl_fc1"], name=f"input_aware_{mode}", B=4, s=257, c1=256, c2=512, k=64, r=32)
+    inp = synth.make_inputs(w)
+    Xc = synth.make_calibration(w, 1024)
+    prep = O.prepare(inp.W, w.kind, w.r, k=w.k, calib=(Xc, mode))
+    err, status, _, _ = run_same_factor_case(w, inputs=inp, prep=prep)
+    assert np.all(status == D.SOLVE_OK)
+    f = D.prepare_input_aware(inp.W, D.spec_of(w), Xc, mode)
+    (Yg,), status = gpu_forward(w, f, inp.X, inp.bias)
+    e2e = O.rel_fro(Yg, O.forward(inp.X, prep, inp.bias, w.B, w.s, eps=1e-6))
+    log(f"  input-aware mode {mode}: end to end rel_fro {e2e:.3e}")
+    assert e2e <= TOL[w.dtype] and np.all(status == D.SOLVE_OK)

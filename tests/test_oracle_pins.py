@@ -431,6 +431,66 @@ def test_blast_bases_are_top_singular_subspaces_of_block_rows_and_columns():
 
 
 # ---------------------------------------------------------------------------
+# input-aware static start ([P2] App. B; [P5] structured-matrix section)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("mode", [O.INPUT_AWARE_DIAG, O.INPUT_AWARE_CHOL])
+def test_input_aware_hand_worked(mode):
+    """W = diag(2, 1), k = 1, calibration rows [1, 3] and [1, -3]: channel RMS
+    (1, 3) and X^T X / n = diag(1, 9), so S = diag(1, 3) in both modes (up to
+    the tiny ridge).  S W = diag(2, 3) keeps the 3 at (1, 1): W_hat =
+    S^-1 diag(0, 3) = diag(0, 1), where the plain truncated SVD keeps
+    diag(2, 0).  Derived by hand."""
+    W = np.diag([2.0, 1.0])
+    Xc = np.array([[1.0, 3.0], [1.0, -3.0]])
+    prep = O.prepare(W, O.KIND_LOWRANK, 1, k=1, calib=(Xc, mode))
+    np.testing.assert_allclose(prep["W_hat"], np.diag([0.0, 1.0]), atol=1e-6)
+    np.testing.assert_allclose(O.prepare(W, O.KIND_LOWRANK, 1, k=1)["W_hat"], np.diag([2.0, 0.0]), atol=1e-12)
+
+
+@pytest.mark.parametrize("mode", [O.INPUT_AWARE_DIAG, O.INPUT_AWARE_CHOL])
+def test_input_aware_with_isotropic_calibration_is_the_plain_fit(mode):
+    rng = _rng(90)
+    W, *_ = _power_law_w(rng, 24, 30)
+    Xc = synth.orthonormal_rows_input(rng, 48, 24, 2.5)       # X^T X / n = const I
+    ia = O.prepare(W, O.KIND_LOWRANK, 3, k=5, calib=(Xc, mode))
+    np.testing.assert_allclose(ia["W_hat"], _prep_lowrank(W, 5, 3)["W_hat"], atol=1e-9)
+
+
+def test_input_aware_cholesky_fit_is_optimal_in_the_calibration_norm():
+    """||X_cal (W - W_hat)||_F^2 / n equals the singular-value tail of C^T W
+    (Eckart-Young in the weighted norm) and is below the plain fit's."""
+    rng = _rng(91)
+    W, *_ = _power_law_w(rng, 20, 28)
+    Xc = _aniso_x(rng, 200, 20)
+    k = 6
+    ia = O.prepare(W, O.KIND_LOWRANK, 3, k=k, calib=(Xc, O.INPUT_AWARE_CHOL))
+    n, c1 = Xc.shape
+    K = Xc.T @ Xc / n
+    C = np.linalg.cholesky(K + O.CALIB_RIDGE * np.trace(K) / c1 * np.eye(c1))
+    tail = np.sum(np.linalg.svd(C.T @ W, compute_uv=False)[k:] ** 2)
+    E = W - ia["W_hat"]
+    np.testing.assert_allclose(np.linalg.norm(C.T @ E) ** 2, tail, rtol=1e-9)
+    plain = W - _prep_lowrank(W, k, 3)["W_hat"]
+    assert np.linalg.norm(Xc @ E) < np.linalg.norm(Xc @ plain)
+    assert np.linalg.matrix_rank(ia["W_hat"], tol=1e-9) == k
+
+
+def test_input_aware_diagonal_fit_is_optimal_in_the_scaled_norm():
+    rng = _rng(92)
+    W, *_ = _power_law_w(rng, 20, 28)
+    Xc = _aniso_x(rng, 100, 20)
+    k = 4
+    ia = O.prepare(W, O.KIND_LOWRANK, 3, k=k, calib=(Xc, O.INPUT_AWARE_DIAG))
+    s = np.sqrt(np.mean(Xc ** 2, axis=0))
+    tail = np.sum(np.linalg.svd(s[:, None] * W, compute_uv=False)[k:] ** 2)
+    np.testing.assert_allclose(np.linalg.norm(s[:, None] * (W - ia["W_hat"])) ** 2, tail, rtol=1e-9)
+    # the residual split stays exact: W_hat + W_res = W, P = W_res R0^T
+    np.testing.assert_allclose(ia["W_hat"] + ia["W_res"], W, atol=1e-12)
+    np.testing.assert_allclose(ia["P"], ia["W_res"] @ ia["R0"].T, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
 # invariances (readings: per-segment solve, relative ridge, R0 rotation)
 # ---------------------------------------------------------------------------
 

@@ -166,3 +166,46 @@ def test_bf16_rounding_of_pack_matches_generator_rounding():
     off += (c2 * k * 2 + 255) // 256 * 256 // 2
     got = buf[off:off + c1 * c2].reshape(c2, c1)
     np.testing.assert_array_equal(got, synth.bf16_bits(vals.T))
+
+
+# ---------------------------------------------------------------------------
+# input-aware static start (dyra_prepare_input_aware) against the oracle
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("c1,c2,k,r", [(64, 96, 16, 8), (96, 64, 24, 16)])
+def test_prepare_input_aware_matches_oracle(mode, c1, c2, k, r):
+    W = _w(c1 * 7 + c2, c1, c2)
+    w = synth.scaled(synth.WORKLOADS["vitb_fc1"], c1=c1, c2=c2, k=k, r=r)
+    Xc = synth.make_calibration(w, 300)
+    spec = D.make_spec(synth.KIND_LOWRANK, c1, c2, r, k=k)
+    f = D.prepare_input_aware(W, spec, Xc, mode, nthreads=4)
+    o = O.prepare(W, O.KIND_LOWRANK, r, k=k, calib=(Xc, mode))
+    np.testing.assert_allclose(f["U"] @ f["V"], o["W_hat"], atol=1e-9)
+    # sqrt(sigma) split of the transformed weight: S U_f and V_f^T have equal column norms
+    S = O.input_transform(Xc, mode)
+    np.testing.assert_allclose(np.linalg.norm(S @ f["U"], axis=0), np.linalg.norm(f["V"], axis=1), rtol=1e-8)
+    _check_common(f, o, W, r)
+
+
+def test_prepare_input_aware_rejects_bad_arguments():
+    import ctypes
+    spec = D.make_spec(synth.KIND_LOWRANK, 64, 96, 8, k=16)
+    W = _w(3, 64, 96)
+    Xc = np.ones((10, 64))
+    with pytest.raises(D.DyraError, match="EINVAL"):
+        D.prepare_input_aware(W, spec, Xc, 3)                                   # unknown mode
+    with pytest.raises(D.DyraError, match="EINVAL"):
+        D.prepare_input_aware(W, spec, np.zeros((10, 64)), 1)                   # all-zero rows
+    bad = Xc.copy()
+    bad[2, 5] = np.nan
+    with pytest.raises(D.DyraError, match="EINVAL"):
+        D.prepare_input_aware(W, spec, bad, 2)                                  # non-finite rows
+    mon = D.make_spec(synth.KIND_MONARCH, 64, 64, 8, mblk=8)
+    with pytest.raises(D.DyraError, match="EINVAL"):
+        D.prepare_input_aware(_w(4, 64, 64), mon, Xc, 1)                        # not low-rank
+    hf = D.HostFactors()
+    assert D.lib().dyra_prepare_input_aware(ctypes.byref(spec), D._dptr(W), D._dptr(Xc), 10, 1,
+                                            ctypes.byref(hf), 1) == -1          # null outputs
+    assert D.lib().dyra_prepare_input_aware(ctypes.byref(spec), D._dptr(W), D._dptr(Xc), 0, 1,
+                                            ctypes.byref(hf), 1) == -2          # no rows
