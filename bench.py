@@ -37,6 +37,7 @@ WORKLOAD_TEXT = {
     "vitl_fc2": "ViT-L/16 MLP fc2",
     "monarch": "Monarch 32 x (32 x 32) layer at the ViT-L token count",
     "lm_blast": "LM prefill QKV-shaped layer, BLAST 16 x 16 grid, rank 128",
+    "lm_blast_diag": "LM prefill QKV-shaped layer, BLAST 16 x 16 grid, rank 128, diagonal couplings",
 }
 STAGES = ["stage1_X_UP", "token_reductions_M_G", "solve_apply", "right_factor_R", "fused_output_Y"]
 
@@ -56,10 +57,13 @@ def stage_work(w):
         m = w.mblk   # c = m^2: stage 1 and stage 2 are m block products of m x m
         s1 = (2 * n * c1 * m + 2 * n * c1 * r, e * (n * c1 + c1 * m + c1 * r + n * (c1 + r) + r * n))
         s6 = (2 * n * c2 * m + 2 * n * r * c2, e * (n * (c1 + r) + c2 * m + c2 * B * r + c2 + n * c2))
-    elif w.kind == synth.KIND_BLAST:
-        nr = w.nb * w.rb  # Z = X blockdiag(U_i): n x (nb rb); coupling W' = Z S (full S)
+    elif w.kind in (synth.KIND_BLAST, synth.KIND_BLAST_DIAG):
+        nr = w.nb * w.rb  # Z = X blockdiag(U_i): n x (nb rb); coupling W' = Z S
         s1 = (2 * n * c1 * w.rb + 2 * n * c1 * r, e * (n * c1 + c1 * w.rb + c1 * r + n * (nr + r) + r * n))
-        cpl = (2 * n * nr * nr, e * (2 * n * nr + nr * nr))
+        if w.kind == synth.KIND_BLAST:     # full rb x rb couplings: one (nb rb)^2 GEMM
+            cpl = (2 * n * nr * nr, e * (2 * n * nr + nr * nr))
+        else:                              # diagonal couplings: nb^2 rb weights
+            cpl = (2 * n * w.nb * nr, e * (2 * n * nr + w.nb * nr))
         s5 = (s5[0] + cpl[0], s5[1] + cpl[1])   # the coupling GEMM runs in the same event interval
         s6 = (2 * n * w.rb * c2 + 2 * n * r * c2, e * (n * nr + n * r + c2 * w.rb + c2 * B * r + c2 + n * c2))
     else:
@@ -72,13 +76,15 @@ def stage_work(w):
 
 def STRUCT_TEXT(w):
     return {0: f"low-rank k={w.k}", 1: f"Monarch {w.mblk} x ({w.mblk} x {w.mblk})",
-            2: f"BLAST {w.nb} x {w.nb} grid, rb={w.rb}"}[w.kind]
+            2: f"BLAST {w.nb} x {w.nb} grid, rb={w.rb}",
+            3: f"BLAST {w.nb} x {w.nb} grid, rb={w.rb}, diagonal couplings"}[w.kind]
 
 
 OUTPUT_KERNEL = {0: "s6_lowrank_kernel (fused T V + L R_b + bias)",
                  "0bf16": "s6_lowrank_ws_kernel (persistent, wave-specialised T V + L R_b + bias)",
                  1: "s6_monarch_kernel (stage 2 + L R_b + bias)",
-                 2: "s6_blast_kernel (W'_j V_j^T + L R_b + bias)"}
+                 2: "s6_blast_kernel (W'_j V_j^T + L R_b + bias)",
+                 3: "s6_blast_kernel (W'_j V_j^T + L R_b + bias)"}
 
 
 def kernel_source_hash():

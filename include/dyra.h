@@ -37,7 +37,8 @@
  *   - Size constraints: c1, c2, k, r multiples of 8; 1 <= r <= min(c1, c2);
  *     r <= 128.  Low-rank: k + r <= min(c1, c2).  Monarch: c1 == c2 ==
  *     mblk^2 with mblk == 32 (bf16 only).  BLAST: nb divides c1 and c2,
- *     rb <= min(c1, c2) / nb, rb multiple of 32 (bf16 only).
+ *     rb <= min(c1, c2) / nb, rb multiple of 8, c2 / nb multiple of 128
+ *     (bf16 only); BLAST_DIAG also nb rb <= 32768.
  */
 #ifndef DYRA_H
 #define DYRA_H
@@ -62,6 +63,7 @@ extern "C" {
 #define DYRA_LOWRANK 0
 #define DYRA_MONARCH 1
 #define DYRA_BLAST   2
+#define DYRA_BLAST_DIAG 3   /* BLAST with diagonal couplings S_ij = diag(s_ij) */
 
 /* storage / arithmetic type */
 #define DYRA_F32  0
@@ -84,7 +86,7 @@ extern "C" {
                                  /* R_b solved by the sweep instead (result valid)        */
 
 typedef struct {
-  int32_t kind;   /* DYRA_LOWRANK / DYRA_MONARCH / DYRA_BLAST                  */
+  int32_t kind;   /* DYRA_LOWRANK / DYRA_MONARCH / DYRA_BLAST / DYRA_BLAST_DIAG */
   int32_t k;      /* low-rank: static rank                                     */
   int32_t mblk;   /* Monarch: block count == block size m, c1 == c2 == m*m     */
   int32_t nb;     /* BLAST: nb x nb block grid                                 */
@@ -111,6 +113,8 @@ typedef struct {
  *        (= blockdiag(B1) . Pi . blockdiag(B2), Pi the reshape-transpose)
  *   Ub [nb][c1/nb][rb], S [nb][nb][rb][rb], Vb [nb][c2/nb][rb]:
  *        block (i, j) of W_hat = Ub[i] S[i][j] Vb[j]^T
+ *        (DYRA_BLAST_DIAG: S [nb][nb][rb], the diagonals:
+ *        block (i, j) = Ub[i] diag(S[i][j]) Vb[j]^T)
  *   P [c1][r] = W_res R0^T,  R0 [r][c2] (orthonormal rows),  Wres [c1][c2],
  *   res_sv [r] = top singular values of W_res (descending).
  */
@@ -128,8 +132,10 @@ int dyra_prepare_sizes(const dyra_spec* spec, dyra_sizes* out);
  * Offline preparation on the host (float64, not part of the timed forward).
  * Fits W_hat by structure (low-rank: truncated SVD; Monarch: rank-1 SVD of
  * each m x m block; BLAST: shared bases from block-row / block-column SVDs
- * and least-squares couplings), forms W_res = W - W_hat, takes R0 = top-r
- * right singular vectors of W_res and P = W_res R0^T.
+ * and least-squares couplings, for BLAST_DIAG the least-squares diagonal
+ * couplings for those bases, diag(Ub[i]^T W_ij Vb[j])), forms
+ * W_res = W - W_hat, takes R0 = top-r right singular vectors of W_res and
+ * P = W_res R0^T.
  *   W: host [c1][c2] float64 (read only).  out: caller-allocated arrays.
  *   nthreads: host worker threads (<= 0: hardware concurrency).
  * Errors: EINVAL, ESHAPE, ENOCONV.

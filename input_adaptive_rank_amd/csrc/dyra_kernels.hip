@@ -1136,6 +1136,52 @@ __global__ __launch_bounds__(256) void s6_monarch_kernel(const bf16_t* __restric
 // The tile width divides b2, so every tile lies inside one block column.
 // ===========================================================================
 
+// Diagonal couplings (DYRA_BLAST_DIAG): W'_j[t][p] = sum_i Z_i[t][p] s_ij[p]
+// for every token t, output block j and p < rb, an elementwise weighted sum
+// over the nb input blocks (2 n nb^2 rb flops, HBM bound: Z read once, W'
+// written once).  A workgroup stages ZT token rows of Z in LDS; thread
+// chunks of 8 outputs (16 bytes) walk the NR = nb rb outputs of each row.
+// Sd: [nb (j)][nb (i)][rb]; fp32 accumulation, bf16 W'.
+constexpr int BDC_LDS = 64 * 1024;
+__global__ __launch_bounds__(256) void blast_diag_coupling_kernel(const bf16_t* __restrict__ Z, int64_t ldz,
+                                                                  const bf16_t* __restrict__ Sd,
+                                                                  bf16_t* __restrict__ Wp, int64_t ldw, int64_t n,
+                                                                  int nb, int rb, int zt) {
+  __shared__ __attribute__((aligned(16))) bf16_t zs[BDC_LDS / 2];
+  const int NR = nb * rb, chunks = NR / 8, rc = rb / 8;
+  for (int64_t t0 = (int64_t)blockIdx.x * zt; t0 < n; t0 += (int64_t)gridDim.x * zt) {
+    const int rows = (int)imin64(zt, n - t0);
+    __syncthreads();   // the previous rows are consumed
+    for (int e = threadIdx.x; e < rows * chunks; e += 256) {
+      const int row = e / chunks, c = e % chunks;
+      *reinterpret_cast<uint4*>(zs + row * NR + 8 * c) =
+          *reinterpret_cast<const uint4*>(Z + (t0 + row) * ldz + 8 * c);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < rows * chunks; e += 256) {
+      const int row = e / chunks, c = e % chunks;
+      const int j = c / rc, p8 = (c % rc) * 8;
+      float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < nb; ++i) {
+        const uint4 zv = *reinterpret_cast<const uint4*>(zs + row * NR + i * rb + p8);
+        const uint4 sv = *reinterpret_cast<const uint4*>(Sd + ((int64_t)j * nb + i) * rb + p8);
+        const uint32_t zw[4] = {zv.x, zv.y, zv.z, zv.w}, sw[4] = {sv.x, sv.y, sv.z, sv.w};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          acc[2 * h] = fmaf(bf2f((bf16_t)(zw[h] & 0xffffu)), bf2f((bf16_t)(sw[h] & 0xffffu)), acc[2 * h]);
+          acc[2 * h + 1] = fmaf(bf2f((bf16_t)(zw[h] >> 16)), bf2f((bf16_t)(sw[h] >> 16)), acc[2 * h + 1]);
+        }
+      }
+      uint4 o;
+      o.x = (uint32_t)f2bf(acc[0]) | ((uint32_t)f2bf(acc[1]) << 16);
+      o.y = (uint32_t)f2bf(acc[2]) | ((uint32_t)f2bf(acc[3]) << 16);
+      o.z = (uint32_t)f2bf(acc[4]) | ((uint32_t)f2bf(acc[5]) << 16);
+      o.w = (uint32_t)f2bf(acc[6]) | ((uint32_t)f2bf(acc[7]) << 16);
+      *reinterpret_cast<uint4*>(Wp + (t0 + row) * ldw + j * rb + p8) = o;
+    }
+  }
+}
+
 template <class C>
 __global__ __launch_bounds__(C::NT) void s6_blast_kernel(const bf16_t* Wp, int64_t ldw, const bf16_t* ZL,
                                                          int64_t ldzl, int64_t loff, const bf16_t* Vb,
@@ -3125,8 +3171,16 @@ int forward_blast(const dyra_spec& s, const char* plan, const void* X, const voi
   }
   E.mark(1, st);
   forward_residual<CfgB, CfgB3>(s, plan, X, B, seg, eps, solver, ws, st, E);
-  // coupling W' = Z S (dense over the nb x nb grid of rb x rb blocks)
-  launch_gemm_tn<CfgB>(ZL, ldzl, plan + PL.St, NR, Wp, NR, n, NR, NR, nullptr, st);
+  if (s.kind == DYRA_BLAST_DIAG) {
+    // coupling W'_j = sum_i Z_i diag(s_ij): elementwise over the block grid
+    const int zt = (int)std::max<int64_t>(1, std::min<int64_t>(8, (BDC_LDS / 2) / NR));
+    const int64_t groups = cdiv(n, zt);
+    hipLaunchKernelGGL(blast_diag_coupling_kernel, dim3((unsigned)std::min<int64_t>(groups, 4096)), dim3(256), 0, st,
+                       ZL, ldzl, reinterpret_cast<const bf16_t*>(plan + PL.St), Wp, NR, n, nb, rb, zt);
+  } else {
+    // coupling W' = Z S (dense over the nb x nb grid of rb x rb blocks)
+    launch_gemm_tn<CfgB>(ZL, ldzl, plan + PL.St, NR, Wp, NR, n, NR, NR, nullptr, st);
+  }
   E.mark(4, st);
   {
     typedef CfgB6 C6;
@@ -3217,7 +3271,7 @@ int forward_impl(const dyra_spec* spec, const void* plan, const void* X, const v
   char* ws = reinterpret_cast<char*>(workspace);
   if (spec->kind == DYRA_MONARCH)
     return forward_monarch(*spec, plan_c, X, bias, Y, B, s, ridge_eps, solver, ws, st, E);
-  if (spec->kind == DYRA_BLAST) return forward_blast(*spec, plan_c, X, bias, Y, B, s, ridge_eps, solver, ws, st, E);
+  if (is_blast(spec->kind)) return forward_blast(*spec, plan_c, X, bias, Y, B, s, ridge_eps, solver, ws, st, E);
   if (dtype == DYRA_BF16)
     return forward_lowrank<CfgB, CfgB3, CfgB6>(*spec, plan_c, X, bias, Y, B, s, ridge_eps, solver, ws, st, E,
                                                half_steps);

@@ -44,7 +44,7 @@ extern "C" int dyra_prepare_sizes(const dyra_spec* spec, dyra_sizes* out) {
     out->B2 = out->B1;
   } else {
     out->Ub = s.c1 * s.rb;                       // nb * (c1/nb) * rb
-    out->S = (int64_t)s.nb * s.nb * s.rb * s.rb;
+    out->S = (int64_t)s.nb * s.nb * s.rb * (s.kind == DYRA_BLAST_DIAG ? 1 : s.rb);
     out->Vb = s.c2 * s.rb;
   }
   out->P = s.c1 * s.r;
@@ -106,8 +106,9 @@ bool fit_monarch(Pool& pool, const Mat& W, int m, std::vector<double>& B1, std::
 }
 
 // BLAST: U_i = top-rb left singular vectors of block row i, V_j = top-rb
-// right singular vectors of block column j, S_ij = U_i^T W_ij V_j.
-bool fit_blast(Pool& pool, const Mat& W, int nb, int rb, std::vector<double>& Ub,
+// right singular vectors of block column j, S_ij = U_i^T W_ij V_j; with
+// diagonal couplings only diag(U_i^T W_ij V_j) (S holds [nb][nb][rb]).
+bool fit_blast(Pool& pool, const Mat& W, int nb, int rb, bool diag, std::vector<double>& Ub,
                std::vector<double>& S, std::vector<double>& Vb, Mat& What) {
   const int64_t b1 = W.rows / nb, b2 = W.cols / nb;
   std::vector<Mat> U((size_t)nb), V((size_t)nb);
@@ -128,7 +129,7 @@ bool fit_blast(Pool& pool, const Mat& W, int nb, int rb, std::vector<double>& Ub
   }
   Ub.assign((size_t)(nb * b1 * rb), 0.0);
   Vb.assign((size_t)(nb * b2 * rb), 0.0);
-  S.assign((size_t)nb * nb * rb * rb, 0.0);
+  S.assign((size_t)nb * nb * rb * (diag ? 1 : rb), 0.0);
   for (int i = 0; i < nb; ++i)
     std::memcpy(Ub.data() + (size_t)i * b1 * rb, U[(size_t)i].a.data(), sizeof(double) * (size_t)(b1 * rb));
   for (int j = 0; j < nb; ++j)
@@ -144,7 +145,15 @@ bool fit_blast(Pool& pool, const Mat& W, int nb, int rb, std::vector<double>& Ub
         std::memcpy(Wij.row(a), W.row(i * b1 + a) + j * b2, sizeof(double) * (size_t)b2);
       Mat T = dyra_host::matmul_tn(one, U[(size_t)i], Wij);      // rb x b2
       Mat Sij = dyra_host::matmul(one, T, V[(size_t)j]);          // rb x rb
-      std::memcpy(S.data() + (size_t)t * rb * rb, Sij.a.data(), sizeof(double) * (size_t)(rb * rb));
+      if (diag) {
+        for (int p = 0; p < rb; ++p) {
+          S[(size_t)t * rb + p] = Sij(p, p);
+          for (int q = 0; q < rb; ++q)
+            if (q != p) Sij(p, q) = 0.0;
+        }
+      } else {
+        std::memcpy(S.data() + (size_t)t * rb * rb, Sij.a.data(), sizeof(double) * (size_t)(rb * rb));
+      }
       Mat US = dyra_host::matmul(one, U[(size_t)i], Sij);        // b1 x rb
       Mat Wh = dyra_host::matmul_nt(one, US, V[(size_t)j]);      // b1 x b2
       for (int64_t a = 0; a < b1; ++a)
@@ -311,7 +320,7 @@ extern "C" int dyra_prepare(const dyra_spec* spec, const double* W, dyra_host_fa
   if (!out->P || !out->R0 || !out->Wres || !out->res_sv) return DYRA_EINVAL;
   if (s.kind == DYRA_LOWRANK && (!out->U || !out->V)) return DYRA_EINVAL;
   if (s.kind == DYRA_MONARCH && (!out->B1 || !out->B2)) return DYRA_EINVAL;
-  if (s.kind == DYRA_BLAST && (!out->Ub || !out->S || !out->Vb)) return DYRA_EINVAL;
+  if (is_blast(s.kind) && (!out->Ub || !out->S || !out->Vb)) return DYRA_EINVAL;
   try {
     Pool pool(nthreads);
     Mat Wm(s.c1, s.c2);
@@ -329,7 +338,7 @@ extern "C" int dyra_prepare(const dyra_spec* spec, const double* W, dyra_host_fa
       std::memcpy(out->B2, B2.data(), sizeof(double) * B2.size());
     } else {
       std::vector<double> Ub, S, Vb;
-      if (!fit_blast(pool, Wm, s.nb, s.rb, Ub, S, Vb, What)) return DYRA_ENOCONV;
+      if (!fit_blast(pool, Wm, s.nb, s.rb, s.kind == DYRA_BLAST_DIAG, Ub, S, Vb, What)) return DYRA_ENOCONV;
       std::memcpy(out->Ub, Ub.data(), sizeof(double) * Ub.size());
       std::memcpy(out->S, S.data(), sizeof(double) * S.size());
       std::memcpy(out->Vb, Vb.data(), sizeof(double) * Vb.size());
@@ -401,12 +410,19 @@ extern "C" int dyra_plan_pack(const dyra_spec* spec, const dyra_host_factors* f,
     for (int64_t p = 0; p < r; ++p)
       for (int64_t i = 0; i < c1; ++i) put(host_plan, L.Pt, (size_t)(p * c1 + i), f->P[i * r + p], dtype);
     const int64_t NR = nb * rb;
-    for (int64_t i = 0; i < nb; ++i)
-      for (int64_t j = 0; j < nb; ++j)
-        for (int64_t p = 0; p < rb; ++p)
-          for (int64_t q = 0; q < rb; ++q)
-            put(host_plan, L.St, (size_t)((j * rb + q) * NR + i * rb + p),
-                f->S[((i * nb + j) * rb + p) * rb + q], dtype);
+    if (s.kind == DYRA_BLAST_DIAG) {
+      for (int64_t i = 0; i < nb; ++i)
+        for (int64_t j = 0; j < nb; ++j)
+          for (int64_t p = 0; p < rb; ++p)
+            put(host_plan, L.St, (size_t)((j * nb + i) * rb + p), f->S[(i * nb + j) * rb + p], dtype);
+    } else {
+      for (int64_t i = 0; i < nb; ++i)
+        for (int64_t j = 0; j < nb; ++j)
+          for (int64_t p = 0; p < rb; ++p)
+            for (int64_t q = 0; q < rb; ++q)
+              put(host_plan, L.St, (size_t)((j * rb + q) * NR + i * rb + p),
+                  f->S[((i * nb + j) * rb + p) * rb + q], dtype);
+    }
     for (int64_t t = 0; t < nb * b2 * rb; ++t) put(host_plan, L.Vb, (size_t)t, f->Vb[t], dtype);
   }
   for (int64_t i = 0; i < c1; ++i)

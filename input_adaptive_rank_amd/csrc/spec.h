@@ -31,6 +31,7 @@ inline int validate_spec(const dyra_spec* sp) {
       if (s.mblk <= 0 || s.c1 != s.c2 || s.c1 != (int64_t)s.mblk * s.mblk) return DYRA_ESHAPE;
       break;
     case DYRA_BLAST:
+    case DYRA_BLAST_DIAG:
       if (s.nb <= 0 || s.rb <= 0 || s.c1 % s.nb || s.c2 % s.nb) return DYRA_ESHAPE;
       if (s.rb > s.c1 / s.nb || s.rb > s.c2 / s.nb) return DYRA_ESHAPE;
       break;
@@ -40,14 +41,17 @@ inline int validate_spec(const dyra_spec* sp) {
   return DYRA_OK;
 }
 
+inline bool is_blast(int kind) { return kind == DYRA_BLAST || kind == DYRA_BLAST_DIAG; }
+
 // Structures / dtypes the device path implements.
 inline int validate_dtype(const dyra_spec& s, int dtype) {
   if (dtype != DYRA_F32 && dtype != DYRA_BF16) return DYRA_EINVAL;
   if (s.kind == DYRA_MONARCH) {
     if (dtype != DYRA_BF16 || s.mblk != 32) return DYRA_EDTYPE;
   }
-  if (s.kind == DYRA_BLAST) {
+  if (is_blast(s.kind)) {
     if (dtype != DYRA_BF16 || s.rb % 8 || (s.c1 / s.nb) % 8 || (s.c2 / s.nb) % 128) return DYRA_EDTYPE;
+    if (s.kind == DYRA_BLAST_DIAG && (int64_t)s.nb * s.rb > 32768) return DYRA_EDTYPE;
   }
   return DYRA_OK;
 }
@@ -64,7 +68,8 @@ inline int validate_dtype(const dyra_spec& s, int dtype) {
 //            (zero for 32 q + l >= r; r rounded up to a multiple of 32 rows);
 //            B2t [m][m][m] (B2t[j][l][a] = B2[j][a][l]), Wrt [c x c]
 // BLAST    : Ubt [nb][rb][c1/nb] (U_i^T), Pt [r x c1],
-//            St [(nb rb) x (nb rb)] (St[j rb + q][i rb + p] = S[i][j][p][q]),
+//            St [(nb rb) x (nb rb)] (St[j rb + q][i rb + p] = S[i][j][p][q]);
+//            BLAST_DIAG: St [nb][nb][rb] (St[j][i][p] = S[i][j][p]),
 //            Vb [nb][c2/nb][rb] (as prepared), Wrt [c2 x c1]
 // Shape of the first-stage tile kernel: 160 token rows x 320 = k + r output
 // columns per workgroup, 32-column k-tiles.
@@ -107,7 +112,7 @@ inline PlanLayout plan_layout(const dyra_spec& s, int dtype) {
     const size_t nb = (size_t)s.nb, rb = (size_t)s.rb;
     L.Ubt = take(nb * rb * (c1 / nb));
     L.Pt = take(r * c1);
-    L.St = take(nb * rb * nb * rb);
+    L.St = take(s.kind == DYRA_BLAST_DIAG ? nb * nb * rb : nb * rb * nb * rb);
     L.Vb = take(nb * (c2 / nb) * rb);
   }
   L.Wrt = take(c2 * c1);
@@ -186,7 +191,7 @@ inline WsLayout ws_layout(const dyra_spec& s, int64_t B, int64_t seg, int dtype,
   else stat = (int64_t)s.nb * s.rb;
   W.wa = stat + s.r;
   W.A = take(n * (size_t)W.wa * e);
-  if (s.kind == DYRA_BLAST) W.Wp = take(n * (size_t)stat * e);
+  if (is_blast(s.kind)) W.Wp = take(n * (size_t)stat * e);
   W.Lt = take(r * ((n + 255) / 256 * 256) * e);   // token pitch padded to 256
   W.G = take((size_t)B * r * r * 4);
   W.M = take((size_t)B * r * c1 * 4);
@@ -202,7 +207,7 @@ inline WsLayout ws_layout(const dyra_spec& s, int64_t B, int64_t seg, int dtype,
     // shared by the right factor and (BLAST) L = X P, which never overlap
     const S5Split sp = s5_split((int64_t)c2, B * (int64_t)r, (int64_t)c1);
     size_t pk = sp.slices > 1 ? (size_t)sp.slices * c2 * (size_t)B * r * 4 : 0;
-    if (s.kind == DYRA_BLAST) {
+    if (is_blast(s.kind)) {
       const S5Split sl = s5_split((int64_t)n, (int64_t)r, (int64_t)c1);
       if (sl.slices > 1) pk = std::max(pk, (size_t)sl.slices * n * r * 4);
     }

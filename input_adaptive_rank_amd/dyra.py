@@ -20,7 +20,7 @@ import re
 
 import numpy as np
 
-from .synth import DT_BF16, DT_F32, KIND_BLAST, KIND_LOWRANK, KIND_MONARCH  # noqa: F401
+from .synth import DT_BF16, DT_F32, KIND_BLAST, KIND_BLAST_DIAG, KIND_LOWRANK, KIND_MONARCH  # noqa: F401
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdyra.so")
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "dyra.h")
@@ -144,7 +144,9 @@ def prepare_sizes(spec: Spec) -> dict:
 def _factor_shapes(spec: Spec) -> dict:
     m, nb, rb = spec.mblk, spec.nb, spec.rb
     return {"U": (spec.c1, spec.k), "V": (spec.k, spec.c2), "B1": (m, m, m), "B2": (m, m, m),
-            "Ub": (nb, spec.c1 // max(nb, 1), rb), "S": (nb, nb, rb, rb), "Vb": (nb, spec.c2 // max(nb, 1), rb),
+            "Ub": (nb, spec.c1 // max(nb, 1), rb),
+            "S": (nb, nb, rb) if spec.kind == KIND_BLAST_DIAG else (nb, nb, rb, rb),
+            "Vb": (nb, spec.c2 // max(nb, 1), rb),
             "P": (spec.c1, spec.r), "R0": (spec.r, spec.c2), "Wres": (spec.c1, spec.c2), "res_sv": (spec.r,)}
 
 

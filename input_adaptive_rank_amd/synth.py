@@ -32,6 +32,7 @@ import numpy as np
 KIND_LOWRANK = 0
 KIND_MONARCH = 1
 KIND_BLAST = 2
+KIND_BLAST_DIAG = 3
 
 DT_F32 = 0
 DT_BF16 = 1
@@ -73,6 +74,9 @@ WORKLOADS = {
     "monarch": Workload("monarch", 1004, 32, 1029, 1024, 1024, KIND_MONARCH, 64, mblk=32),
     "lm_blast": Workload("lm_blast", 1005, 1, 4096, 4096, 12288, KIND_BLAST, 128, nb=16, rb=128,
                          n_out=16, heavy_tail=True, solver="ns"),
+    # the same layer with diagonal couplings S_ij = diag(s_ij)
+    "lm_blast_diag": Workload("lm_blast_diag", 1005, 1, 4096, 4096, 12288, KIND_BLAST_DIAG, 128, nb=16,
+                              rb=128, n_out=16, heavy_tail=True, solver="ns"),
 }
 
 

@@ -52,6 +52,7 @@ import scipy.linalg as sla
 KIND_LOWRANK = 0
 KIND_MONARCH = 1
 KIND_BLAST = 2
+KIND_BLAST_DIAG = 3     # BLAST with diagonal couplings S_ij = diag(s_ij)
 
 
 # ---------------------------------------------------------------------------
@@ -123,12 +124,15 @@ def monarch_apply(X: np.ndarray, f: dict) -> np.ndarray:
     return y.reshape(n, m * m)
 
 
-def fit_blast(W: np.ndarray, nb: int, rb: int) -> dict:
+def fit_blast(W: np.ndarray, nb: int, rb: int, diagonal: bool = False) -> dict:
     """BLAST fit on an nb x nb block grid with shared rank-rb bases.
 
     U[i] (c1/nb x rb): top-rb left singular vectors of block row i.
     V[j] (c2/nb x rb): top-rb right singular vectors of block column j.
-    S[i, j] = U[i]^T W_ij V[j]: the least-squares coupling for these bases.
+    S[i, j] = U[i]^T W_ij V[j]: the least-squares coupling for these bases;
+    with diagonal couplings only its diagonal is kept, which is the
+    least-squares diagonal coupling for orthonormal bases (entry p fits the
+    rank-one term u_p v_p^T, and those terms are orthonormal).
     """
     c1, c2 = W.shape
     b1, b2 = c1 // nb, c2 // nb
@@ -144,6 +148,8 @@ def fit_blast(W: np.ndarray, nb: int, rb: int) -> dict:
     for i in range(nb):
         for j in range(nb):
             S[i, j] = U[i].T @ W[i * b1:(i + 1) * b1, j * b2:(j + 1) * b2] @ V[j]
+            if diagonal:
+                S[i, j] = np.diag(np.diag(S[i, j]))
     return {"U": U, "V": V, "S": S}
 
 
@@ -207,12 +213,12 @@ def fit_lowrank_input_aware(W: np.ndarray, k: int, S: np.ndarray) -> dict:
 
 def static_dense(kind: int, f: dict) -> np.ndarray:
     return {KIND_LOWRANK: lowrank_dense, KIND_MONARCH: monarch_dense,
-            KIND_BLAST: blast_dense}[kind](f)
+            KIND_BLAST: blast_dense, KIND_BLAST_DIAG: blast_dense}[kind](f)
 
 
 def static_apply(kind: int, X: np.ndarray, f: dict) -> np.ndarray:
     return {KIND_LOWRANK: lowrank_apply, KIND_MONARCH: monarch_apply,
-            KIND_BLAST: blast_apply}[kind](X, f)
+            KIND_BLAST: blast_apply, KIND_BLAST_DIAG: blast_apply}[kind](X, f)
 
 
 def fit_static(kind: int, W: np.ndarray, k=0, mblk=0, nb=0, rb=0) -> dict:
@@ -220,8 +226,8 @@ def fit_static(kind: int, W: np.ndarray, k=0, mblk=0, nb=0, rb=0) -> dict:
         return fit_lowrank(W, k)
     if kind == KIND_MONARCH:
         return fit_monarch(W, mblk)
-    if kind == KIND_BLAST:
-        return fit_blast(W, nb, rb)
+    if kind in (KIND_BLAST, KIND_BLAST_DIAG):
+        return fit_blast(W, nb, rb, diagonal=kind == KIND_BLAST_DIAG)
     raise ValueError(kind)
 
 

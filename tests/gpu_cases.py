@@ -47,6 +47,8 @@ def host_factors_from_oracle(prep) -> dict:
         f.update(U=st["U"], V=st["V"])
     elif prep["kind"] == O.KIND_MONARCH:
         f.update(B1=st["B1"], B2=st["B2"])
+    elif prep["kind"] == O.KIND_BLAST_DIAG:
+        f.update(Ub=st["U"], Vb=st["V"], S=np.ascontiguousarray(np.diagonal(st["S"], axis1=2, axis2=3)))
     else:
         f.update(Ub=st["U"], Vb=st["V"], S=st["S"])
     return f

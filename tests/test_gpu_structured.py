@@ -39,6 +39,28 @@ BLAST = [
 ]
 
 
+BLAST_DIAG = [
+    sc(W["lm_blast_diag"], name="blast_diag_small", B=2, s=200, c1=512, c2=1536, nb=4, rb=32, r=32,
+       solver="auto", n_out=4),
+    # nb rb = 1024: 32 token rows staged per pass of the coupling kernel,
+    # a ragged last group (n = 300)
+    sc(W["lm_blast_diag"], name="blast_diag_ragged", B=3, s=100, c1=1024, c2=2048, nb=8, rb=128, r=16,
+       solver="auto", n_out=4),
+]
+
+
+@pytest.mark.parametrize("w", BLAST_DIAG, ids=lambda w: w.name)
+def test_blast_diag_small(w):
+    err, status, _, _ = run_same_factor_case(w, solver=w.solver)
+    assert np.all(status == D.SOLVE_OK)
+
+
+def test_blast_diag_full_size():
+    w = W["lm_blast_diag"]
+    err, status, _, _ = run_same_factor_case(w, solver=w.solver)
+    assert np.all(status == D.SOLVE_OK)
+
+
 @pytest.mark.parametrize("w", MONARCH, ids=lambda w: w.name)
 def test_monarch_small(w):
     err, status, _, _ = run_same_factor_case(w, solver=w.solver)

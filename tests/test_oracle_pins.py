@@ -407,6 +407,45 @@ def test_blast_fit_recovers_exact_blast_and_coupling_is_projection():
             np.testing.assert_allclose(g2["U"][i].T @ Eij @ g2["V"][j], 0, atol=1e-12)
 
 
+def test_blast_diagonal_fit_recovers_exact_diagonal_blast_and_is_entrywise_optimal():
+    """Diagonal couplings.  W_ij = U_i diag(a_i b_j c) V_j^T with orthonormal
+    bases and c decreasing: the Gram of block row i is U_i diag(a_i^2
+    sum_j b_j^2 c^2) U_i^T, so its singular vectors are U_i's columns in the
+    same order for every i (likewise V_j), and the fit recovers W.  (A
+    generic diagonal-BLAST W is not identifiable by the one-pass bases: they
+    are fixed only up to a rotation, which a diagonal coupling cannot
+    absorb.)  On a generic W the couplings are diagonal, each entry is the
+    projection u_p^T W_ij v_p (the residual has no component on the
+    rank-one terms u_p v_p^T), equal to the full-coupling fit's diagonal,
+    and the full-coupling fit is closer."""
+    rng = _rng(66)
+    nb, b1, b2, rb = 3, 6, 8, 2
+    f = {"U": np.stack([synth.haar_columns(rng.standard_normal((b1, rb))) for _ in range(nb)]),
+         "V": np.stack([synth.haar_columns(rng.standard_normal((b2, rb))) for _ in range(nb)]),
+         "S": np.zeros((nb, nb, rb, rb))}
+    a, b, c = rng.uniform(0.5, 2.0, nb), rng.uniform(0.5, 2.0, nb), np.array([3.0, 1.0])
+    for i in range(nb):
+        for j in range(nb):
+            f["S"][i, j] = np.diag(a[i] * b[j] * c)
+    W = O.blast_dense(f)
+    g = O.fit_static(O.KIND_BLAST_DIAG, W, nb=nb, rb=rb)
+    np.testing.assert_allclose(O.blast_dense(g), W, atol=1e-10)
+    W2 = rng.standard_normal((nb * b1, nb * b2))
+    d = O.fit_static(O.KIND_BLAST_DIAG, W2, nb=nb, rb=rb)
+    full = O.fit_static(O.KIND_BLAST, W2, nb=nb, rb=rb)
+    E = W2 - O.blast_dense(d)
+    for i in range(nb):
+        for j in range(nb):
+            Sij = d["S"][i, j]
+            np.testing.assert_array_equal(Sij, np.diag(np.diag(Sij)))
+            Eij = E[i * b1:(i + 1) * b1, j * b2:(j + 1) * b2]
+            np.testing.assert_allclose(np.diag(d["U"][i].T @ Eij @ d["V"][j]), 0, atol=1e-12)
+            np.testing.assert_allclose(np.diag(Sij), np.diag(full["S"][i, j]), atol=1e-12)
+    assert np.linalg.norm(W2 - O.blast_dense(full)) < np.linalg.norm(E)
+    X = rng.standard_normal((5, nb * b1))
+    np.testing.assert_allclose(O.static_apply(O.KIND_BLAST_DIAG, X, d), X @ O.blast_dense(d), atol=1e-12)
+
+
 def test_blast_bases_are_top_singular_subspaces_of_block_rows_and_columns():
     """On a generic W, U_i spans the top-rb left singular subspace of the whole
     block row i and V_j the top-rb right singular subspace of the whole block

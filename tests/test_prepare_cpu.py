@@ -209,3 +209,18 @@ def test_prepare_input_aware_rejects_bad_arguments():
                                             ctypes.byref(hf), 1) == -1          # null outputs
     assert D.lib().dyra_prepare_input_aware(ctypes.byref(spec), D._dptr(W), D._dptr(Xc), 0, 1,
                                             ctypes.byref(hf), 1) == -2          # no rows
+
+
+def test_prepare_blast_diagonal_couplings_match_oracle():
+    c1, c2, nb, rb, r = 64, 512, 4, 8, 8
+    W = _w(77, c1, c2)
+    spec = D.make_spec(synth.KIND_BLAST_DIAG, c1, c2, r, nb=nb, rb=rb)
+    f = D.prepare(W, spec, nthreads=4)
+    assert f["S"].shape == (nb, nb, rb)
+    o = O.prepare(W, O.KIND_BLAST_DIAG, r, nb=nb, rb=rb)
+    g = {"U": f["Ub"], "V": f["Vb"], "S": np.stack([[np.diag(f["S"][i, j]) for j in range(nb)] for i in range(nb)])}
+    np.testing.assert_allclose(O.blast_dense(g), o["W_hat"], atol=1e-9)
+    _check_common(f, o, W, r)
+    # the device plan stores the diagonals only: St[j][i][p] = S[i][j][p]
+    assert D.plan_size(spec, synth.DT_BF16) < D.plan_size(D.make_spec(synth.KIND_BLAST, c1, c2, r, nb=nb, rb=rb),
+                                                          synth.DT_BF16)
