@@ -199,7 +199,7 @@ int dyra_workspace_size(const dyra_spec* spec, int64_t B, int64_t s, int32_t dty
  *   Lt     [r][lt_pitch] L transposed (token-contiguous), dtype
  *   G      [B][r][r]    fp32  L_b^T L_b
  *   M      [B][r][c1]   fp32  L_b^T X_b
- *   Ginv   [B][r][r]    fp32  (G_b + lambda_b I)^-1
+ *   Ginv   [B][r][r]    fp64  (G_b + lambda_b I)^-1
  *   Mp     [B][r][c1]   dtype Ginv_b M_b
  *   Rt     [c2][B r]    dtype R_b^T, R_b = Mp_b W_res
  *   status [B]          int32 solver status words

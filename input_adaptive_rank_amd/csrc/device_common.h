@@ -9,11 +9,35 @@ typedef uint16_t bf16_t;
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf2f(bf16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
 // fp32 -> bf16, round to nearest even (gfx950 v_cvt_pk_bf16_f32).
 __device__ __forceinline__ bf16_t f2bf(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
+
+// Token segments of a forward: uniform runs of `seg` rows when off is null,
+// else rows [off[b], off[b + 1]) of a device offsets array (off[0] = 0,
+// off[B] = n, every segment at least one row).  Passed by value.
+struct SegMap {
+  const int32_t* off;
+  int64_t seg, B, n;
+  __device__ __forceinline__ int64_t lo(int64_t b) const { return off ? (int64_t)off[b] : b * seg; }
+  __device__ __forceinline__ int64_t hi(int64_t b) const {
+    return off ? (int64_t)off[b + 1] : ((b + 1) * seg < n ? (b + 1) * seg : n);
+  }
+  // the segment holding `row` (0 <= row < n)
+  __device__ __forceinline__ int64_t of(int64_t row) const {
+    if (!off) return row / seg;
+    int64_t a = 0, z = B;   // off[a] <= row < off[z]
+    while (z - a > 1) {
+      const int64_t mid = (a + z) >> 1;
+      if ((int64_t)off[mid] <= row) a = mid;
+      else z = mid;
+    }
+    return a;
+  }
+};
 
 // Element traits.  A 16-byte chunk holds KPC elements; one "k-substep" of the
 // MMA covers two chunks (lanes 0-31 read chunk 2s, lanes 32-63 chunk 2s+1).

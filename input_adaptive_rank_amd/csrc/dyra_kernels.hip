@@ -16,6 +16,7 @@
 //                                       never written to memory
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <cmath>
 #include <mutex>
 #include <type_traits>
@@ -273,7 +274,7 @@ constexpr int S1T_LATE = 4;
 __global__ __launch_bounds__(512, 1) void s1_tile_kernel(const bf16_t* __restrict__ X,
                                                          const bf16_t* __restrict__ UPt, bf16_t* __restrict__ A,
                                                          bf16_t* __restrict__ Lt, int n, int c1, int k, int r,
-                                                         int64_t ldt, float* __restrict__ Gp, int seg) {
+                                                         int64_t ldt, float* __restrict__ Gp, SegMap sg) {
   constexpr int BM = S1T_BM, BN = S1T_BN, RBY = S1T_BK * 2;   // 64-byte k-tile rows
   constexpr int NS = 4, NP = 3, NW = 8, FB = 5;   // UPt slots, X pair regions, waves, 16-blocks per wave side
   constexpr int USLOT = BN * RBY, XPAIR = BM * 2 * RBY;       // 20 KB each
@@ -458,7 +459,8 @@ __global__ __launch_bounds__(512, 1) void s1_tile_kernel(const bf16_t* __restric
   // waves 4 .. 7 the next segment's (if the tile reaches it); wave w & 3 one
   // 32 x 32 block of the r x r partial
   __syncthreads();
-  const int b0 = m0 / seg, bnd = (b0 + 1) * seg - m0;        // tile-local first token of segment b0 + 1
+  const int64_t b0 = sg.of(m0);
+  const int bnd = (int)(sg.hi(b0) - m0);                       // tile-local first token of segment b0 + 1
   const int slot = w >> 2, blk = w & 3, nbr = r >> 5;
   const int tlo = slot ? bnd : 0, thi = slot ? rows : min(bnd, rows);
   if (blk >= nbr * nbr || tlo >= thi) return;
@@ -496,7 +498,7 @@ __global__ __launch_bounds__(C::NT, WPE) void s6_lowrank_kernel(const typename C
                                                            const typename C::elem* Rt,
                                                            const typename C::elem* bias,
                                                            typename C::elem* Y, int64_t n, int64_t c2,
-                                                           int k, int r, int64_t seg, int64_t B,
+                                                           int k, int r, SegMap sg, int64_t B,
                                                            int tiles_n) {
   typedef typename C::elem T;
   constexpr int E = TT<T>::ESZ;
@@ -504,8 +506,8 @@ __global__ __launch_bounds__(C::NT, WPE) void s6_lowrank_kernel(const typename C
   const int t = xcd_tile_id(blockIdx.x, gridDim.x);
   const int64_t m0 = (int64_t)(t / tiles_n) * C::BM, n0 = (int64_t)(t % tiles_n) * C::BN;
   const int64_t lda = (int64_t)(k + r) * E;
-  const int64_t bfirst = m0 / seg;
-  const int64_t blast = imin64(B - 1, (imin64(m0 + C::BM, n) - 1) / seg);
+  const int64_t bfirst = sg.of(imin64(m0, n - 1));
+  const int64_t blast = imin64(B - 1, sg.of(imin64(m0 + C::BM, n) - 1));
   const char* TLc = reinterpret_cast<const char*>(TL);
   const int nk0 = ktiles((int64_t)k * E), nkr = ktiles((int64_t)r * E);
   const int total = nk0 + (int)(blast - bfirst + 1) * nkr;
@@ -519,7 +521,7 @@ __global__ __launch_bounds__(C::NT, WPE) void s6_lowrank_kernel(const typename C
     const int u = t - nk0;
     const int64_t b = bfirst + u / nkr;
     kt = u % nkr;
-    ph.a = OpK{TLc + (int64_t)k * E, lda, m0, b * seg, imin64((b + 1) * seg, n), (int64_t)r * E};
+    ph.a = OpK{TLc + (int64_t)k * E, lda, m0, sg.lo(b), sg.hi(b), (int64_t)r * E};
     ph.b = OpK{reinterpret_cast<const char*>(Rt + b * r), B * r * E, n0, 0, c2, (int64_t)r * E};
   };
   f32x16 acc[C::FM][C::FN];
@@ -555,7 +557,7 @@ __global__ __launch_bounds__(C::NT, WPE) void s6_lowrank_kernel(const typename C
 template <class C, int NS, int NL, bool HAS_BIAS>
 __global__ __launch_bounds__(C::NT + NL * 64, 1) void s6_lowrank_ws_kernel(
     const bf16_t* __restrict__ TL, const bf16_t* __restrict__ Vt, const bf16_t* __restrict__ Rt,
-    const bf16_t* __restrict__ bias, bf16_t* __restrict__ Y, int n, int c2, int k, int r, int seg, int B,
+    const bf16_t* __restrict__ bias, bf16_t* __restrict__ Y, int n, int c2, int k, int r, SegMap sg, int B,
     int tiles_n, int tiles) {
   static_assert(NS >= 2 && NS <= 4, "ring depth");
   static_assert(NL % 2 == 0 && (C::BM / 8) % NL == 0 && (C::BN / 8) % NL == 0, "loader blocks");
@@ -588,10 +590,10 @@ __global__ __launch_bounds__(C::NT + NL * 64, 1) void s6_lowrank_ws_kernel(
   auto settle = [&](Cur& c) {   // segments, k-tile count of the tile at (tm, tn)
     c.m0 = c.tm * C::BM;
     c.n0 = c.tn * C::BN;
-    while ((c.b0 + 1) * seg <= c.m0) ++c.b0;
+    while (sg.lo(c.b0 + 1) <= c.m0) ++c.b0;
     const int last = min(c.m0 + C::BM, n) - 1;
     if (c.bl < c.b0) c.bl = c.b0;
-    while (c.bl + 1 < B && (c.bl + 1) * seg <= last) ++c.bl;
+    while (c.bl + 1 < B && sg.lo(c.bl + 1) <= last) ++c.bl;
     c.tot = nk0 + (c.bl - c.b0 + 1) * nkr;
   };
   auto start = [&](Cur& c, int t) {
@@ -601,7 +603,7 @@ __global__ __launch_bounds__(C::NT + NL * 64, 1) void s6_lowrank_ws_kernel(
     c.b0 = 0;
     c.bl = 0;
     if (t < hi_tile) {
-      c.b0 = (c.tm * C::BM) / seg;
+      c.b0 = (int)sg.of(c.tm * C::BM);
       c.bl = c.b0;
       settle(c);
     }
@@ -652,7 +654,7 @@ __global__ __launch_bounds__(C::NT + NL * 64, 1) void s6_lowrank_ws_kernel(
       p_kind = 1; p_left = nkr; p_kb = 0; p_kbytes = rE; p_ib = ibx;
       p_ars = rsrc_words(reinterpret_cast<const char*>(TL) + (int64_t)ic.m0 * lda + kE, 0x7fffffffu);
       p_brs = rsrc_words(reinterpret_cast<const char*>(Rt) + (int64_t)ibx * rE + (int64_t)ic.n0 * ldr, 0x7fffffffu);
-      p_alo = ibx * seg - ic.m0; p_ahi = min((ibx + 1) * seg, n) - ic.m0;
+      p_alo = (int)sg.lo(ibx) - ic.m0; p_ahi = (int)sg.hi(ibx) - ic.m0;
       p_fa = p_live && p_alo <= 0 && p_ahi >= C::BM ? 1 : 0;
     };
     set_tv();
@@ -1041,7 +1043,7 @@ __global__ __launch_bounds__(256) void s6_monarch_kernel(const bf16_t* __restric
                                                          const bf16_t* __restrict__ B2t,
                                                          const bf16_t* __restrict__ Rt,
                                                          const bf16_t* __restrict__ bias, bf16_t* __restrict__ Y,
-                                                         int64_t n, int r, int64_t seg, int64_t B) {
+                                                         int64_t n, int r, SegMap sg, int64_t B) {
   constexpr int C = MO * MO;
   __shared__ __attribute__((aligned(16))) char sm[S6M_LDS];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -1079,7 +1081,7 @@ __global__ __launch_bounds__(256) void s6_monarch_kernel(const bf16_t* __restric
   }
   // L R_b for every segment overlapping the workgroup's 128 rows
   const int64_t wend = imin64(mw + 128, n);
-  const int64_t bf = mw / seg, bl = imin64(B - 1, (wend - 1) / seg);
+  const int64_t bf = sg.of(mw), bl = imin64(B - 1, sg.of(wend - 1));
   const int ru = r / 8;                                            // 16-byte runs per R^T row
   for (int64_t b = bf; b <= bl; ++b) {
     __syncthreads();                                               // the previous R^T block is read
@@ -1089,8 +1091,9 @@ __global__ __launch_bounds__(256) void s6_monarch_kernel(const bf16_t* __restric
           *reinterpret_cast<const uint4*>(Rt + ((int64_t)j0 * MO + c) * (B * r) + b * r + u * 8);
     }
     __syncthreads();
-    if (m0 >= wend || m0 + 32 <= b * seg || m0 >= (b + 1) * seg) continue;   // wave-uniform
-    const bool in = rok && row >= b * seg && row < (b + 1) * seg;
+    const int64_t blo = sg.lo(b), bhi = sg.hi(b);
+    if (m0 >= wend || m0 + 32 <= blo || m0 >= bhi) continue;   // wave-uniform
+    const bool in = rok && row >= blo && row < bhi;
     for (int k0 = 0; k0 < r; k0 += 16) {
       const int kk = k0 + 8 * g;
       const uint4 la = (in && kk < r) ? *reinterpret_cast<const uint4*>(A + row * lda + C + kk) : zero4();
@@ -1187,14 +1190,14 @@ __global__ __launch_bounds__(C::NT) void s6_blast_kernel(const bf16_t* Wp, int64
                                                          int64_t ldzl, int64_t loff, const bf16_t* Vb,
                                                          const bf16_t* Rt, const bf16_t* bias, bf16_t* Y,
                                                          int64_t n, int64_t c2, int64_t b2, int rb, int r,
-                                                         int64_t seg, int64_t B, int tiles_n) {
+                                                         SegMap sg, int64_t B, int tiles_n) {
   constexpr int E = 2;
   __shared__ __attribute__((aligned(16))) char lds[C::LDS];
   const int t = xcd_tile_id(blockIdx.x, gridDim.x);
   const int64_t m0 = (int64_t)(t / tiles_n) * C::BM, n0 = (int64_t)(t % tiles_n) * C::BN;
   const int64_t j = n0 / b2;
-  const int64_t bfirst = m0 / seg;
-  const int64_t blast = imin64(B - 1, (imin64(m0 + C::BM, n) - 1) / seg);
+  const int64_t bfirst = sg.of(m0);
+  const int64_t blast = imin64(B - 1, sg.of(imin64(m0 + C::BM, n) - 1));
   const int nk0 = ktiles((int64_t)rb * E), nkr = ktiles((int64_t)r * E);
   const int total = nk0 + (int)(blast - bfirst + 1) * nkr;
   const char* Wpc = reinterpret_cast<const char*>(Wp + j * rb);
@@ -1210,7 +1213,7 @@ __global__ __launch_bounds__(C::NT) void s6_blast_kernel(const bf16_t* Wp, int64
     const int u = tt - nk0;
     const int64_t b = bfirst + u / nkr;
     kt = u % nkr;
-    ph.a = OpK{Lc, ldzl * E, m0, b * seg, imin64((b + 1) * seg, n), (int64_t)r * E};
+    ph.a = OpK{Lc, ldzl * E, m0, sg.lo(b), sg.hi(b), (int64_t)r * E};
     ph.b = OpK{reinterpret_cast<const char*>(Rt + b * r), B * r * E, n0, 0, c2, (int64_t)r * E};
   };
   f32x16 acc[C::FM][C::FN];
@@ -1230,7 +1233,7 @@ __global__ __launch_bounds__(C::NT) void s6_blast_kernel(const bf16_t* Wp, int64
 template <class C>
 __global__ __launch_bounds__(C::NT) void s3_gram_kernel(const typename C::elem* Lt, int64_t ldt,
                                                         const typename C::elem* X, int64_t c1, int r,
-                                                        int64_t seg, int64_t n, float* M, float* G,
+                                                        SegMap sg, int64_t n, float* M, float* G,
                                                         int tiles_r, int tiles_cm, int tiles_cg) {
   typedef typename C::elem T;
   constexpr int E = TT<T>::ESZ, KPC = TT<T>::KPC, BKE = 8 * KPC;
@@ -1247,7 +1250,7 @@ __global__ __launch_bounds__(C::NT) void s3_gram_kernel(const typename C::elem* 
   const bool is_g = tc >= tiles_cm;
   const int p0 = tr * C::BM;
   const int64_t c0 = (int64_t)(is_g ? tc - tiles_cm : tc) * C::BN;
-  const int64_t lo = b * seg, hi = imin64((b + 1) * seg, n);
+  const int64_t lo = sg.lo(b), hi = sg.hi(b);
   const int64_t kt0 = lo / BKE, kt1 = (hi + BKE - 1) / BKE;
 
   f32x16 acc[C::FM][C::FN];
@@ -1408,14 +1411,14 @@ __device__ __forceinline__ double recip_pos(double D) {
   return fma(x, e, x);
 }
 
-// Gb: r x r row-major fp32 (global or LDS); Ob: r x r row-major fp32,
+// Gb: r x r row-major fp32 (global or LDS); Ob: r x r row-major fp64,
 // receives the inverse (zeros unless the status is OK).  The arithmetic is
 // fp64: the ridge bounds cond(G + lambda I) only by about r / eps (~1e8 for
 // eps = 1e-6), past what fp32 elimination survives.  Needs r % SW_BK == 0,
 // r <= 128 and ceil(r / TB)^2 <= NT.  Returns the status (same in every
 // thread).
 template <int NT, int TB>
-__device__ __forceinline__ int sweep_inverse(const float* Gb, float* Ob, int r, float eps, SweepLds& sh) {
+__device__ __forceinline__ int sweep_inverse(const float* Gb, double* Ob, int r, float eps, SweepLds& sh) {
   static_assert(TB % SW_BK == 0 && TB % 2 == 0, "tile");
   const int tid = threadIdx.x;
   const int tpr = (r + TB - 1) / TB;
@@ -1547,7 +1550,7 @@ __device__ __forceinline__ int sweep_inverse(const float* Gb, float* Ob, int r, 
   for (int x = 0; x < TB; ++x)
 #pragma unroll
     for (int y = 0; y < TB; ++y)
-      if (own && i0 + x < r && j0 + y < r) Ob[(i0 + x) * r + j0 + y] = st == DYRA_SOLVE_OK ? (float)-a[x][y] : 0.f;
+      if (own && i0 + x < r && j0 + y < r) Ob[(i0 + x) * r + j0 + y] = st == DYRA_SOLVE_OK ? -a[x][y] : 0.0;
   return st;
 }
 
@@ -1576,7 +1579,7 @@ __device__ __forceinline__ int packed_lower(int i, int j) { return ((i * (i + 1)
 // Needs r % TB == 0, r <= 128, ceil(r / TB)^2 <= NT and Cp: LDS for
 // r (r + 1) / 2 doubles.  Returns the status (same in every thread).
 template <int NT, int TB>
-__device__ __forceinline__ int chol_inverse(const float* Gb, float* Ob, int r, float eps, SweepLds& sh,
+__device__ __forceinline__ int chol_inverse(const float* Gb, double* Ob, int r, float eps, SweepLds& sh,
                                             double* Cp) {
   constexpr int PB = SW_BK;
   static_assert(TB % PB == 0 && TB % 2 == 0, "tile");
@@ -1799,7 +1802,7 @@ __device__ __forceinline__ int chol_inverse(const float* Gb, float* Ob, int r, f
   for (int x = 0; x < TB; ++x)
 #pragma unroll
     for (int y = 0; y < TB; ++y)
-      if (own && i0 + x < r && j0 + y < r) Ob[(i0 + x) * r + j0 + y] = st == DYRA_SOLVE_OK ? (float)a[x][y] : 0.f;
+      if (own && i0 + x < r && j0 + y < r) Ob[(i0 + x) * r + j0 + y] = st == DYRA_SOLVE_OK ? a[x][y] : 0.0;
   return st;
 }
 
@@ -2051,8 +2054,8 @@ __device__ __forceinline__ void s3_gram(const bf16_t* __restrict__ Lt, int64_t l
 // registers of its own solver only.
 template <int NRB, int NB, int SOLVE>
 __global__ __launch_bounds__(S3_NT, NRB <= 4 ? 2 : 1) void s3_reduce_solve_kernel(
-    const bf16_t* __restrict__ Lt, int64_t ldt, const bf16_t* __restrict__ X, int64_t c1, int r, int64_t seg,
-    int64_t n, int64_t B, float* __restrict__ M, float* __restrict__ G, float* __restrict__ Gi,
+    const bf16_t* __restrict__ Lt, int64_t ldt, const bf16_t* __restrict__ X, int64_t c1, int r, SegMap sg,
+    int64_t n, int64_t B, float* __restrict__ M, float* __restrict__ G, double* __restrict__ Gi,
     int32_t* __restrict__ status, float eps, int strips, int64_t lt_seg_rows, int x_rel,
     const float* __restrict__ gpart, int gchunks, int64_t gprows) {
   __shared__ __attribute__((aligned(16))) char lds[S3Lds<NB>::BYTES];
@@ -2090,7 +2093,7 @@ __global__ __launch_bounds__(S3_NT, NRB <= 4 ? 2 : 1) void s3_reduce_solve_kerne
     strip = (bid - B) % strips;
   }
   if (strip < 0) {
-    const int64_t lo = b * seg, hi = imin64((b + 1) * seg, n);
+    const int64_t lo = sg.lo(b), hi = sg.hi(b);
     const bf16_t *Ltb, *Xb;
     int64_t tbase;
     seg_ptrs(b, lo, Ltb, Xb, tbase);
@@ -2163,7 +2166,7 @@ __global__ __launch_bounds__(S3_NT, NRB <= 4 ? 2 : 1) void s3_reduce_solve_kerne
     return;
   }
   const int64_t c0 = strip * S3_STRIP;
-  const int64_t lo = b * seg, hi = imin64((b + 1) * seg, n);
+  const int64_t lo = sg.lo(b), hi = sg.hi(b);
   const bf16_t *Ltb, *Xb;
   int64_t tbase;
   seg_ptrs(b, lo, Ltb, Xb, tbase);
@@ -2181,15 +2184,15 @@ __global__ __launch_bounds__(S3_NT, NRB <= 4 ? 2 : 1) void s3_reduce_solve_kerne
 // critical path of that launch).
 template <int NB>
 __global__ __launch_bounds__(64) void gram_partial_kernel(const bf16_t* __restrict__ Lt, int64_t ldt, int r,
-                                                          int64_t seg, int64_t n, int gchunks, int64_t gchunk,
+                                                          SegMap sg, int64_t n, int gchunks, int64_t gchunk,
                                                           float* __restrict__ Gp) {
   // one wave per chunk: every token step's L^T loads are issued before the
   // MFMAs, and the 32 x 32 blocks go from the accumulators straight to memory
   constexpr int MAXST = 16;   // gchunk <= 256 tokens = 16 steps of 16
   const int lane = threadIdx.x, l = lane & 31, g = lane >> 5;
   const int64_t b = blockIdx.x / gchunks, c = blockIdx.x % gchunks;
-  const int64_t lo = b * seg + c * gchunk;
-  const int64_t hi = imin64(imin64(lo + gchunk, (b + 1) * seg), n);
+  const int64_t lo = sg.lo(b) + c * gchunk;
+  const int64_t hi = imin64(lo + gchunk, sg.hi(b));
   f32x16 acc[NB][NB];
 #pragma unroll
   for (int a = 0; a < NB; ++a)
@@ -2242,7 +2245,7 @@ __global__ __launch_bounds__(64) void gram_partial_kernel(const bf16_t* __restri
 // alone: the Newton-Schulz kernel flags the segments it could not solve, and
 // those keep the FALLBACK status when the sweep succeeds.
 template <int NT, int TB>
-__global__ __launch_bounds__(NT) void sweep_inverse_kernel(const float* G, float* Ginv, int32_t* status, int r,
+__global__ __launch_bounds__(NT) void sweep_inverse_kernel(const float* G, double* Ginv, int32_t* status, int r,
                                                            float eps, int only_flagged) {
   __shared__ SweepLds sl;
   const int64_t b = blockIdx.x;
@@ -2255,7 +2258,7 @@ __global__ __launch_bounds__(NT) void sweep_inverse_kernel(const float* G, float
 
 // r <= 64: 256 threads of 4 x 4 tiles; r <= 128: 1024 threads of 4 x 4 tiles
 // (four waves per SIMD hide part of the pivot blocks' dependent latency).
-void launch_sweep(const float* G, float* Ginv, int32_t* status, int r, float eps, int64_t B, bool only_flagged,
+void launch_sweep(const float* G, double* Ginv, int32_t* status, int r, float eps, int64_t B, bool only_flagged,
                   hipStream_t st) {
   const int f = only_flagged ? 1 : 0;
   if (r <= 64)
@@ -2268,7 +2271,7 @@ void launch_sweep(const float* G, float* Ginv, int32_t* status, int r, float eps
 // The Cholesky route as its own launch (fp32 storage): one workgroup per
 // segment, the packed factor in LDS.
 template <int NT, int TB, int RMAX>
-__global__ __launch_bounds__(NT) void chol_inverse_kernel(const float* G, float* Ginv, int32_t* status, int r,
+__global__ __launch_bounds__(NT) void chol_inverse_kernel(const float* G, double* Ginv, int32_t* status, int r,
                                                           float eps) {
   __shared__ SweepLds sl;
   __shared__ double cp[RMAX * (RMAX + 1) / 2];
@@ -2277,7 +2280,7 @@ __global__ __launch_bounds__(NT) void chol_inverse_kernel(const float* G, float*
   if (threadIdx.x == 0) status[b] = st;
 }
 
-void launch_chol(const float* G, float* Ginv, int32_t* status, int r, float eps, int64_t B, hipStream_t st) {
+void launch_chol(const float* G, double* Ginv, int32_t* status, int r, float eps, int64_t B, hipStream_t st) {
   if (r <= 64)
     hipLaunchKernelGGL((chol_inverse_kernel<256, 4, 64>), dim3((unsigned)B), dim3(256), 0, st, G, Ginv, status, r,
                        eps);
@@ -2314,7 +2317,7 @@ __device__ __forceinline__ void split_bf16(float x, uint16_t& h, uint16_t& l) {
   h = f2bf(x);
   l = f2bf(x - bf2f(h));
 }
-__global__ __launch_bounds__(512) void ns_inverse_kernel(const float* G, float* Ginv, int32_t* status, int r, float eps,
+__global__ __launch_bounds__(512) void ns_inverse_kernel(const float* G, float* Xit, int32_t* status, int r, float eps,
                                                           int maxit, float tol) {
   __shared__ __attribute__((aligned(16))) char XS[2][NSS_N * 256];   // X hi / lo, stored transposed
   __shared__ __attribute__((aligned(16))) char TS[2][NSS_N * 256];   // T hi / lo, stored transposed
@@ -2501,7 +2504,7 @@ __global__ __launch_bounds__(512) void ns_inverse_kernel(const float* G, float* 
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int rr = bi * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
-      if (rr < r && cc < r) Ginv[b * r * r + rr * r + cc] = good ? x[v] : 0.f;
+      if (rr < r && cc < r) Xit[b * r * r + rr * r + cc] = good ? x[v] : 0.f;
     }
   }
   if (tid == 0) status[b] = st;
@@ -2514,7 +2517,8 @@ __global__ __launch_bounds__(512) void ns_inverse_kernel(const float* G, float* 
 constexpr int NS_N = 128;
 constexpr int NS_P = 129;   // padded LDS pitch (odd: row-strided reads spread over banks)
 
-__global__ __launch_bounds__(1024) void ns_polish_kernel(const float* G, float* Ginv, int32_t* status, int r, float eps,
+__global__ __launch_bounds__(1024) void ns_polish_kernel(const float* G, const float* Xit, double* Ginv,
+                                                         int32_t* status, int r, float eps,
                                                          int maxit, float tol, float accept) {
   __shared__ float Xs[NS_N * NS_P];
   __shared__ float Ts[NS_N * NS_P];
@@ -2560,7 +2564,7 @@ __global__ __launch_bounds__(1024) void ns_polish_kernel(const float* G, float* 
   // X_0: the split-precision iterate (A' space), padded with the identity
   for (int e = tid; e < NS_N * NS_N; e += 1024) {
     const int i = e / NS_N, j = e % NS_N;
-    Xs[i * NS_P + j] = i < r && j < r ? Ginv[b * r * r + i * r + j] : (i == j ? 1.f : 0.f);
+    Xs[i * NS_P + j] = i < r && j < r ? Xit[b * r * r + i * r + j] : (i == j ? 1.f : 0.f);
   }
   __syncthreads();
   float prev = 1e30f;
@@ -2635,8 +2639,7 @@ __global__ __launch_bounds__(1024) void ns_polish_kernel(const float* G, float* 
   const bool good = st == DYRA_SOLVE_OK;
   for (int e = tid; e < r * r; e += 1024) {
     const int i = e / r, j = e % r;
-    const float v = good ? dsc[i] * Xs[i * NS_P + j] * dsc[j] : 0.f;
-    Ginv[b * r * r + e] = v;
+    Ginv[b * r * r + e] = good ? (double)dsc[i] * (double)Xs[i * NS_P + j] * (double)dsc[j] : 0.0;
   }
   if (tid == 0) status[b] = st;
 }
@@ -2664,7 +2667,7 @@ __global__ __launch_bounds__(1024) void ns_polish_kernel(const float* G, float* 
 // current one is multiplied.
 constexpr int AI_WAVES = 4;
 template <typename T, int RB, int NTC = 0>
-__global__ __launch_bounds__(64 * AI_WAVES) void apply_inverse_kernel(const float* __restrict__ Ginv,
+__global__ __launch_bounds__(64 * AI_WAVES) void apply_inverse_kernel(const double* __restrict__ Ginv,
                                                                       const float* __restrict__ M,
                                                                       T* __restrict__ Mp, int r, int64_t c1,
                                                                       int64_t tasks,
@@ -2683,54 +2686,57 @@ __global__ __launch_bounds__(64 * AI_WAVES) void apply_inverse_kernel(const floa
   const int sb = status[b];
   const bool solved = sb == DYRA_SOLVE_OK || sb == DYRA_SOLVE_FALLBACK;
   const int i = lane & 15, g = lane >> 4;
-  const float* Gb = Ginv + b * r * r;
+  const double* Gb = Ginv + b * r * r;
   const float* Mb = M + b * r * c1;
   const int64_t col = ct * 64 + 4 * i;          // c1 % 8 == 0: all four columns or none
   const bool cok = col < c1;
   const int nt = (r + 15) >> 4;
-  auto load = [&](int t, float4 (&a)[RB], float4 (&m)[4]) {
+  auto load = [&](int t, double4 (&a)[RB], float4 (&m)[4]) {
     const int q0 = 16 * t + 4 * g;              // r % 4 == 0: all four q or none
 #pragma unroll
     for (int j = 0; j < RB; ++j) {
       const int row = (grp * RB + j) * 16 + i;
-      a[j] = (row < r && q0 < r) ? *reinterpret_cast<const float4*>(Gb + (int64_t)row * r + q0)
-                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+      a[j] = (row < r && q0 < r) ? *reinterpret_cast<const double4*>(Gb + (int64_t)row * r + q0)
+                                 : make_double4(0.0, 0.0, 0.0, 0.0);
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       m[e] = (cok && q0 < r) ? *reinterpret_cast<const float4*>(Mb + (int64_t)(q0 + e) * c1 + col)
                              : make_float4(0.f, 0.f, 0.f, 0.f);
   };
-  f32x4 acc[RB][4];
+  f64x4 acc[RB][4];
 #pragma unroll
   for (int j = 0; j < RB; ++j)
 #pragma unroll
-    for (int jb = 0; jb < 4; ++jb) acc[j][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto mul = [&](const float4 (&a)[RB], const float4 (&m)[4]) {
+    for (int jb = 0; jb < 4; ++jb) acc[j][jb] = f64x4{0.0, 0.0, 0.0, 0.0};
+  auto mul = [&](const double4 (&a)[RB], const float4 (&m)[4]) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float mv[4] = {m[e].x, m[e].y, m[e].z, m[e].w};
+      const double mv[4] = {m[e].x, m[e].y, m[e].z, m[e].w};
 #pragma unroll
       for (int j = 0; j < RB; ++j) {
-        const float av = e == 0 ? a[j].x : e == 1 ? a[j].y : e == 2 ? a[j].z : a[j].w;
+        const double av = e == 0 ? a[j].x : e == 1 ? a[j].y : e == 2 ? a[j].z : a[j].w;
 #pragma unroll
-        for (int jb = 0; jb < 4; ++jb) acc[j][jb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, mv[jb], acc[j][jb], 0, 0, 0);
+        for (int jb = 0; jb < 4; ++jb) acc[j][jb] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, mv[jb], acc[j][jb], 0, 0, 0);
       }
     }
   };
   if (!solved) {
     // accumulators stay zero
   } else if constexpr (NTC > 0) {
-    float4 a[NTC][RB], m[NTC][4];                // chunks past r load as zeros
+    double4 a[NTC][RB];
+    float4 m[NTC][4];                            // chunks past r load as zeros
 #pragma unroll
     for (int t = 0; t < NTC; ++t) load(t, a[t], m[t]);
 #pragma unroll
     for (int t = 0; t < NTC; ++t) mul(a[t], m[t]);
   } else {
-  float4 a[RB], m[4];
+  double4 a[RB];
+  float4 m[4];
   load(0, a, m);
   for (int t = 0; t < nt; ++t) {
-    float4 an[RB], mn[4];
+    double4 an[RB];
+    float4 mn[4];
     if (t + 1 < nt) load(t + 1, an, mn);
     mul(a, m);
     if (t + 1 < nt) {
@@ -2746,16 +2752,19 @@ __global__ __launch_bounds__(64 * AI_WAVES) void apply_inverse_kernel(const floa
   for (int j = 0; j < RB; ++j)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const int orow = (grp * RB + j) * 16 + 4 * g + v;
+      // v_mfma_f64_16x16x4f64 interleaves its accumulator rows: element v
+      // of lane (i, g) is row g + 4 v, column i
+      const int orow = (grp * RB + j) * 16 + g + 4 * v;
       if (orow >= r) continue;
       T* dst = Mp + (b * r + orow) * c1 + col;
       if constexpr (TT<T>::ESZ == 2) {
         uint2 pk;
-        pk.x = (uint32_t)f2bf(acc[j][0][v]) | ((uint32_t)f2bf(acc[j][1][v]) << 16);
-        pk.y = (uint32_t)f2bf(acc[j][2][v]) | ((uint32_t)f2bf(acc[j][3][v]) << 16);
+        pk.x = (uint32_t)f2bf((float)acc[j][0][v]) | ((uint32_t)f2bf((float)acc[j][1][v]) << 16);
+        pk.y = (uint32_t)f2bf((float)acc[j][2][v]) | ((uint32_t)f2bf((float)acc[j][3][v]) << 16);
         *reinterpret_cast<uint2*>(dst) = pk;
       } else {
-        *reinterpret_cast<float4*>(dst) = make_float4(acc[j][0][v], acc[j][1][v], acc[j][2][v], acc[j][3][v]);
+        *reinterpret_cast<float4*>(dst) = make_float4((float)acc[j][0][v], (float)acc[j][1][v],
+                                                      (float)acc[j][2][v], (float)acc[j][3][v]);
       }
     }
 }
@@ -2763,7 +2772,7 @@ __global__ __launch_bounds__(64 * AI_WAVES) void apply_inverse_kernel(const floa
 // M'_b = Ginv_b M_b for B segments of r x c1: four row blocks per wave when
 // that still leaves at least two waves per SIMD of a 256-CU chip, else one.
 template <typename T>
-void launch_apply_inverse(const float* Gi, const float* M, T* Mp, int64_t B, int r, int64_t c1, const int32_t* stat,
+void launch_apply_inverse(const double* Gi, const float* M, T* Mp, int64_t B, int r, int64_t c1, const int32_t* stat,
                           hipStream_t st) {
   const int64_t tiles = (c1 + 63) / 64, nrb = (r + 15) / 16;
   const int64_t wide = B * tiles * ((nrb + 3) / 4);
@@ -2798,6 +2807,24 @@ typedef GemmCfg<float, 64, 64, 2, 2> CfgF3;     // S3, fp32
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Host view of a forward's segments: B uniform segments of `seg` rows, or
+// ragged ones given by a device copy of the row offsets (off_dev, [B + 1]).
+struct SegInfo {
+  int64_t B = 0, n = 0, seg = 0, max_len = 0, min_len = 0;
+  const int32_t* off_dev = nullptr;
+  SegMap map() const { return SegMap{off_dev, seg, B, n}; }
+  WsLayout layout(const dyra_spec& s, int dtype, int half_steps = 2) const {
+    return ws_layout_n(s, B, n, max_len, dtype, half_steps);
+  }
+  static SegInfo uniform(int64_t B, int64_t seg) {
+    SegInfo si;
+    si.B = B;
+    si.n = B * seg;
+    si.seg = si.max_len = si.min_len = seg;
+    return si;
+  }
+};
+
 // 256 x 128 tiles: 4 compute waves of 128 x 64, 4 loaders, 3-slot ring (148 KB)
 typedef GemmCfg<bf16_t, 256, 128, 2, 2> CfgB6W;
 constexpr int S6W_NS = 3, S6W_NL = 4;
@@ -2823,7 +2850,7 @@ int device_cus() {
 }
 
 void launch_s6_ws(const bf16_t* TL, const bf16_t* Vt, const bf16_t* Rt, const bf16_t* bias, bf16_t* Y, int64_t n,
-                  int64_t c2, int k, int r, int64_t seg, int64_t B, hipStream_t st) {
+                  int64_t c2, int k, int r, SegMap sg, int64_t B, hipStream_t st) {
   typedef CfgB6W C;
   const int tiles_n = (int)cdiv(c2, C::BN);
   const int tiles = (int)(cdiv(n, C::BM) * tiles_n);
@@ -2832,10 +2859,10 @@ void launch_s6_ws(const bf16_t* TL, const bf16_t* Vt, const bf16_t* Rt, const bf
   const int grid = cus >= 16 ? (cus / 8) * 8 : 8;
   if (bias)
     hipLaunchKernelGGL((s6_lowrank_ws_kernel<C, S6W_NS, S6W_NL, true>), dim3(grid), dim3(C::NT + S6W_NL * 64), 0, st,
-                       TL, Vt, Rt, bias, Y, (int)n, (int)c2, k, r, (int)seg, (int)B, tiles_n, tiles);
+                       TL, Vt, Rt, bias, Y, (int)n, (int)c2, k, r, sg, (int)B, tiles_n, tiles);
   else
     hipLaunchKernelGGL((s6_lowrank_ws_kernel<C, S6W_NS, S6W_NL, false>), dim3(grid), dim3(C::NT + S6W_NL * 64), 0, st,
-                       TL, Vt, Rt, bias, Y, (int)n, (int)c2, k, r, (int)seg, (int)B, tiles_n, tiles);
+                       TL, Vt, Rt, bias, Y, (int)n, (int)c2, k, r, sg, (int)B, tiles_n, tiles);
 }
 
 
@@ -2873,16 +2900,16 @@ struct StageEvents {
 };
 
 template <int NRB, int NB>
-void launch_s3_bf16(const bf16_t* Lt, int64_t ldt, const bf16_t* X, int64_t c1, int r, int64_t seg, int64_t n,
-                    int64_t B, float* M, float* G, float* Gi, int32_t* stat, float eps, int solve_mode,
+void launch_s3_bf16(const bf16_t* Lt, int64_t ldt, const bf16_t* X, int64_t c1, int r, SegMap sg, int64_t n,
+                    int64_t B, float* M, float* G, double* Gi, int32_t* stat, float eps, int solve_mode,
                     hipStream_t st, int64_t lt_seg_rows = 0, bool x_rel = false, float* gpart = nullptr,
                     int gchunks = 0, int64_t gchunk = 0, int64_t gprows = 0) {
   const int strips = (int)cdiv(c1, S3_STRIP);
   if (gpart && gprows == 0)   // chunk Gram partials first (absolute L^T addressing only)
     hipLaunchKernelGGL((gram_partial_kernel<NB>), dim3((unsigned)(B * gchunks)), dim3(64), 0, st, Lt, ldt, r,
-                       seg, n, gchunks, gchunk, gpart);
+                       sg, n, gchunks, gchunk, gpart);
   auto go = [&](auto kern) {
-    hipLaunchKernelGGL(kern, dim3((unsigned)(B + B * strips)), dim3(S3_NT), 0, st, Lt, ldt, X, c1, r, seg, n, B, M,
+    hipLaunchKernelGGL(kern, dim3((unsigned)(B + B * strips)), dim3(S3_NT), 0, st, Lt, ldt, X, c1, r, sg, n, B, M,
                        G, Gi, stat, eps, strips, lt_seg_rows, x_rel ? 1 : 0, gpart, gchunks, gprows);
   };
   if (solve_mode == 2) go(s3_reduce_solve_kernel<NRB, NB, 2>);
@@ -2895,20 +2922,22 @@ void launch_s3_bf16(const bf16_t* Lt, int64_t ldt, const bf16_t* X, int64_t c1, 
 template <class C, class C3>
 // gram_rows > 0: the first stage left Gram partials per tile of that many
 // tokens in the workspace (else the chunk Gram kernel computes them here).
-void forward_residual(const dyra_spec& s, const char* plan, const void* X, int64_t B, int64_t seg, float eps,
+void forward_residual(const dyra_spec& s, const char* plan, const void* X, const SegInfo& si, float eps,
                       int solver, char* ws, hipStream_t st, const StageEvents& E, int64_t gram_rows = 0) {
   typedef typename C::elem T;
   constexpr bool BF = TT<T>::ESZ == 2;
   const int dtype = BF ? DYRA_BF16 : DYRA_F32;
   const PlanLayout PL = plan_layout(s, dtype);
-  const WsLayout WL = ws_layout(s, B, seg, dtype);
-  const int64_t n = B * seg, c1 = s.c1, c2 = s.c2;
+  const WsLayout WL = si.layout(s, dtype);
+  const int64_t B = si.B, n = si.n, c1 = s.c1, c2 = s.c2;
+  const SegMap sg = si.map();
   const int r = s.r;
   const T* Wrt = reinterpret_cast<const T*>(plan + PL.Wrt);
   T* Lt = reinterpret_cast<T*>(ws + WL.Lt);
   float* G = reinterpret_cast<float*>(ws + WL.G);
   float* M = reinterpret_cast<float*>(ws + WL.M);
-  float* Gi = reinterpret_cast<float*>(ws + WL.Ginv);
+  double* Gi = reinterpret_cast<double*>(ws + WL.Ginv);
+  float* Xit = reinterpret_cast<float*>(ws + WL.Xit);
   T* Mp = reinterpret_cast<T*>(ws + WL.Mp);
   T* Rt = reinterpret_cast<T*>(ws + WL.Rt);
   int32_t* stat = reinterpret_cast<int32_t*>(ws + WL.status);
@@ -2929,16 +2958,16 @@ void forward_residual(const dyra_spec& s, const char* plan, const void* X, int64
     float* Gp = reinterpret_cast<float*>(ws + WL.Gp);
     const int gc = (int)WL.gchunks;
     const int64_t gk = WL.gchunk;
-    if (r <= 16) launch_s3_bf16<1, 1>(Lt, ldt, Xb, c1, r, seg, n, B, M, G, Gi, stat, eps, mode, st, 0, false, Gp, gc, gk, gram_rows);
-    else if (r <= 32) launch_s3_bf16<2, 1>(Lt, ldt, Xb, c1, r, seg, n, B, M, G, Gi, stat, eps, mode, st, 0, false, Gp, gc, gk, gram_rows);
-    else if (r <= 64) launch_s3_bf16<4, 2>(Lt, ldt, Xb, c1, r, seg, n, B, M, G, Gi, stat, eps, mode, st, 0, false, Gp, gc, gk, gram_rows);
-    else launch_s3_bf16<8, 4>(Lt, ldt, Xb, c1, r, seg, n, B, M, G, Gi, stat, eps, mode, st, 0, false, Gp, gc, gk, gram_rows);
+    if (r <= 16) launch_s3_bf16<1, 1>(Lt, ldt, Xb, c1, r, sg, n, B, M, G, Gi, stat, eps, mode, st, 0, false, Gp, gc, gk, gram_rows);
+    else if (r <= 32) launch_s3_bf16<2, 1>(Lt, ldt, Xb, c1, r, sg, n, B, M, G, Gi, stat, eps, mode, st, 0, false, Gp, gc, gk, gram_rows);
+    else if (r <= 64) launch_s3_bf16<4, 2>(Lt, ldt, Xb, c1, r, sg, n, B, M, G, Gi, stat, eps, mode, st, 0, false, Gp, gc, gk, gram_rows);
+    else launch_s3_bf16<8, 4>(Lt, ldt, Xb, c1, r, sg, n, B, M, G, Gi, stat, eps, mode, st, 0, false, Gp, gc, gk, gram_rows);
     solved = !ns;
   } else {
     const int tr = (int)cdiv(r, C3::BM), tcm = (int)cdiv(c1, C3::BN), tcg = (int)cdiv(r, C3::BN);
     const int64_t grid = B * tr * (tcm + tcg);
     hipLaunchKernelGGL(s3_gram_kernel<C3>, dim3((unsigned)grid), dim3(C3::NT), 0, st, Lt, ldt,
-                       reinterpret_cast<const T*>(X), c1, r, seg, n, M, G, tr, tcm, tcg);
+                       reinterpret_cast<const T*>(X), c1, r, sg, n, M, G, tr, tcm, tcg);
   }
   E.mark(2, st);
   // S4: Ginv_b (unless solved above), M'_b = Ginv_b M_b
@@ -2951,8 +2980,8 @@ void forward_residual(const dyra_spec& s, const char* plan, const void* X, int64
       // (fp32 storage: a stall above 1e-5 goes to the fp64 sweep, so an
       // ill-conditioned G still gives an fp32-accurate inverse)
       const float tol = BF ? 1e-4f : 2e-6f, accept = BF ? 1e-2f : 1e-5f;
-      hipLaunchKernelGGL(ns_inverse_kernel, dim3((unsigned)B), dim3(512), 0, st, G, Gi, stat, r, eps, 40, tol);
-      hipLaunchKernelGGL(ns_polish_kernel, dim3((unsigned)B), dim3(1024), 0, st, G, Gi, stat, r, eps, 60, tol,
+      hipLaunchKernelGGL(ns_inverse_kernel, dim3((unsigned)B), dim3(512), 0, st, G, Xit, stat, r, eps, 40, tol);
+      hipLaunchKernelGGL(ns_polish_kernel, dim3((unsigned)B), dim3(1024), 0, st, G, Xit, Gi, stat, r, eps, 60, tol,
                          accept);
       launch_sweep(G, Gi, stat, r, eps, B, true, st);
     } else if (solver == DYRA_SOLVER_CHOL) {
@@ -2982,7 +3011,7 @@ void forward_residual(const dyra_spec& s, const char* plan, const void* X, int64
       return;
     }
     if (s6_ws_fits(c2, B * r, (int)c1, 0, 1) && device_cus() >= 8) {
-      launch_s6_ws(Wrt, Mp, nullptr, nullptr, Rt, c2, B * r, (int)c1, 0, c2, 1, st);
+      launch_s6_ws(Wrt, Mp, nullptr, nullptr, Rt, c2, B * r, (int)c1, 0, SegMap{nullptr, c2, 1, c2}, 1, st);
       return;
     }
   }
@@ -3003,7 +3032,7 @@ void left_step_bf16(const dyra_spec& s, const char* plan, const bf16_t* X, int64
   const bf16_t* Rt = reinterpret_cast<const bf16_t*>(ws + WL.Rt);
   bf16_t* R = reinterpret_cast<bf16_t*>(ws + WL.R);
   float* K = reinterpret_cast<float*>(ws + WL.K);
-  float* Kinv = reinterpret_cast<float*>(ws + WL.Kinv);
+  double* Kinv = reinterpret_cast<double*>(ws + WL.Kinv);
   float* Qt = reinterpret_cast<float*>(ws + WL.Qt);
   bf16_t* Zt = reinterpret_cast<bf16_t*>(ws + WL.Zt);
   int32_t* kst = reinterpret_cast<int32_t*>(ws + WL.kstatus);
@@ -3013,10 +3042,10 @@ void left_step_bf16(const dyra_spec& s, const char* plan, const bf16_t* X, int64
                      c2, B * r);
   // K_b, Q_b^T, (K_b + lambda I)^-1: c2 is the reduction ("token") axis
   const int64_t nn = B * c2;
-  if (r <= 16) launch_s3_bf16<1, 1>(R, c2, Wrt, c1, r, c2, nn, B, Qt, K, Kinv, kst, eps, 1, st, r, true);
-  else if (r <= 32) launch_s3_bf16<2, 1>(R, c2, Wrt, c1, r, c2, nn, B, Qt, K, Kinv, kst, eps, 1, st, r, true);
-  else if (r <= 64) launch_s3_bf16<4, 2>(R, c2, Wrt, c1, r, c2, nn, B, Qt, K, Kinv, kst, eps, 1, st, r, true);
-  else launch_s3_bf16<8, 4>(R, c2, Wrt, c1, r, c2, nn, B, Qt, K, Kinv, kst, eps, 1, st, r, true);
+  if (r <= 16) launch_s3_bf16<1, 1>(R, c2, Wrt, c1, r, SegMap{nullptr, c2, B, nn}, nn, B, Qt, K, Kinv, kst, eps, 1, st, r, true);
+  else if (r <= 32) launch_s3_bf16<2, 1>(R, c2, Wrt, c1, r, SegMap{nullptr, c2, B, nn}, nn, B, Qt, K, Kinv, kst, eps, 1, st, r, true);
+  else if (r <= 64) launch_s3_bf16<4, 2>(R, c2, Wrt, c1, r, SegMap{nullptr, c2, B, nn}, nn, B, Qt, K, Kinv, kst, eps, 1, st, r, true);
+  else launch_s3_bf16<8, 4>(R, c2, Wrt, c1, r, SegMap{nullptr, c2, B, nn}, nn, B, Qt, K, Kinv, kst, eps, 1, st, r, true);
   launch_apply_inverse<bf16_t>(Kinv, Qt, Zt, B, r, c1, kst, st);
   // L_b = X_b Z_b into [T | L] and L^T
   const int tiles_n = (int)cdiv(r, CfgL::BN);
@@ -3027,13 +3056,13 @@ void left_step_bf16(const dyra_spec& s, const char* plan, const bf16_t* X, int64
 
 template <class C, class C3, class C6>
 int forward_lowrank(const dyra_spec& s, const char* plan, const void* X, const void* bias, void* Y,
-                    int64_t B, int64_t seg, float eps, int solver, char* ws, hipStream_t st,
+                    const SegInfo& si, float eps, int solver, char* ws, hipStream_t st,
                     const StageEvents& E, int half_steps = 2) {
   typedef typename C::elem T;
   const int dtype = TT<T>::ESZ == 2 ? DYRA_BF16 : DYRA_F32;
   const PlanLayout PL = plan_layout(s, dtype);
-  const WsLayout WL = ws_layout(s, B, seg, dtype);
-  const int64_t n = B * seg, c1 = s.c1, c2 = s.c2;
+  const WsLayout WL = si.layout(s, dtype);
+  const int64_t B = si.B, seg = si.seg, n = si.n, c1 = s.c1, c2 = s.c2;
   const int k = s.k, r = s.r;
   T* TL = reinterpret_cast<T*>(ws + WL.A);
   T* Lt = reinterpret_cast<T*>(ws + WL.Lt);
@@ -3056,12 +3085,12 @@ int forward_lowrank(const dyra_spec& s, const char* plan, const void* X, const v
       if (s1_tile_shape(s, DYRA_BF16)) {
         // Gram partials from the tile epilogue when a tile meets at most two
         // segments and r fills whole 32 x 32 blocks
-        const bool gram = (r == 32 || r == 64) && seg >= S1T_BM;
+        const bool gram = (r == 32 || r == 64) && si.min_len >= S1T_BM;
         if (gram) gram_rows = S1T_BM;
         hipLaunchKernelGGL(s1_tile_kernel, dim3((unsigned)cdiv(n, S1T_BM)), dim3(512), 0, st,
                            reinterpret_cast<const bf16_t*>(X), reinterpret_cast<const bf16_t*>(plan + PL.UPt),
                            reinterpret_cast<bf16_t*>(TL), reinterpret_cast<bf16_t*>(Lt), (int)n, (int)c1, k, r,
-                           lt_pitch(n), gram ? reinterpret_cast<float*>(ws + WL.Gp) : nullptr, (int)seg);
+                           lt_pitch(n), gram ? reinterpret_cast<float*>(ws + WL.Gp) : nullptr, si.map());
       } else if (k + r > 256 && k + r <= 320) launch(CfgB1W());
       else launch(C());
     } else {
@@ -3069,12 +3098,12 @@ int forward_lowrank(const dyra_spec& s, const char* plan, const void* X, const v
     }
   }
   E.mark(1, st);
-  forward_residual<C, C3>(s, plan, X, B, seg, eps, solver, ws, st, E, gram_rows);
+  forward_residual<C, C3>(s, plan, X, si, eps, solver, ws, st, E, gram_rows);
   // further ALS half-steps: left (L from R), right (R from L), ...
   if constexpr (TT<T>::ESZ == 2) {
     for (int h = 2; h < half_steps; ++h) {
       if (h % 2 == 0) left_step_bf16(s, plan, reinterpret_cast<const bf16_t*>(X), B, seg, eps, ws, st, half_steps);
-      else forward_residual<C, C3>(s, plan, X, B, seg, eps, solver, ws, st, StageEvents{nullptr, 0});
+      else forward_residual<C, C3>(s, plan, X, si, eps, solver, ws, st, StageEvents{nullptr, 0});
     }
   }
   E.mark(4, st);
@@ -3085,11 +3114,11 @@ int forward_lowrank(const dyra_spec& s, const char* plan, const void* X, const v
     if (BF && s6_ws_fits(n, c2, k, r, B) && device_cus() >= 8)
       launch_s6_ws(reinterpret_cast<const bf16_t*>(TL), reinterpret_cast<const bf16_t*>(plan + PL.Vt),
                    reinterpret_cast<const bf16_t*>(Rt), reinterpret_cast<const bf16_t*>(bias),
-                   reinterpret_cast<bf16_t*>(Y), n, c2, k, r, seg, B, st);
+                   reinterpret_cast<bf16_t*>(Y), n, c2, k, r, si.map(), B, st);
     else
       hipLaunchKernelGGL((s6_lowrank_kernel<C6, BF, true, BF ? S6_WPE : 1, BF>), dim3((unsigned)tiles), dim3(C6::NT), 0,
                          st, TL, reinterpret_cast<const T*>(plan + PL.Vt), Rt, reinterpret_cast<const T*>(bias),
-                         reinterpret_cast<T*>(Y), n, c2, k, r, seg, B, tiles_n);
+                         reinterpret_cast<T*>(Y), n, c2, k, r, si.map(), B, tiles_n);
   }
   E.mark(5, st);
   return hipGetLastError() == hipSuccess ? DYRA_OK : DYRA_EHIP;
@@ -3105,16 +3134,16 @@ void launch_monarch(const bf16_t* X, const char* plan, const PlanLayout& PL, bf1
 
 template <int RB>
 void launch_monarch6(const bf16_t* A, const char* plan, const PlanLayout& PL, const bf16_t* Rt, const bf16_t* bias,
-                     bf16_t* Y, int64_t n, int r, int64_t seg, int64_t B, hipStream_t st) {
+                     bf16_t* Y, int64_t n, int r, SegMap sg, int64_t B, hipStream_t st) {
   hipLaunchKernelGGL((s6_monarch_kernel<RB>), dim3((unsigned)(cdiv(n, 128) * (MO * MO / 128))), dim3(256), 0, st,
-                     A, reinterpret_cast<const bf16_t*>(plan + PL.B2t), Rt, bias, Y, n, r, seg, B);
+                     A, reinterpret_cast<const bf16_t*>(plan + PL.B2t), Rt, bias, Y, n, r, sg, B);
 }
 
-int forward_monarch(const dyra_spec& s, const char* plan, const void* X, const void* bias, void* Y, int64_t B,
-                    int64_t seg, float eps, int solver, char* ws, hipStream_t st, const StageEvents& E) {
+int forward_monarch(const dyra_spec& s, const char* plan, const void* X, const void* bias, void* Y,
+                    const SegInfo& si, float eps, int solver, char* ws, hipStream_t st, const StageEvents& E) {
   const PlanLayout PL = plan_layout(s, DYRA_BF16);
-  const WsLayout WL = ws_layout(s, B, seg, DYRA_BF16);
-  const int64_t n = B * seg;
+  const WsLayout WL = si.layout(s, DYRA_BF16);
+  const int64_t B = si.B, n = si.n;
   const int r = s.r;
   bf16_t* A = reinterpret_cast<bf16_t*>(ws + WL.A);
   bf16_t* Lt = reinterpret_cast<bf16_t*>(ws + WL.Lt);
@@ -3125,23 +3154,23 @@ int forward_monarch(const dyra_spec& s, const char* plan, const void* X, const v
   else if (r <= 64) launch_monarch<2>(Xb, plan, PL, A, Lt, n, r, ldt, st);
   else launch_monarch<4>(Xb, plan, PL, A, Lt, n, r, ldt, st);
   E.mark(1, st);
-  forward_residual<CfgB, CfgB3>(s, plan, X, B, seg, eps, solver, ws, st, E);
+  forward_residual<CfgB, CfgB3>(s, plan, X, si, eps, solver, ws, st, E);
   E.mark(4, st);
   const bf16_t* Rt = reinterpret_cast<const bf16_t*>(ws + WL.Rt);
   const bf16_t* bb = reinterpret_cast<const bf16_t*>(bias);
   bf16_t* Yb = reinterpret_cast<bf16_t*>(Y);
-  if (r <= 32) launch_monarch6<1>(A, plan, PL, Rt, bb, Yb, n, r, seg, B, st);
-  else if (r <= 64) launch_monarch6<2>(A, plan, PL, Rt, bb, Yb, n, r, seg, B, st);
-  else launch_monarch6<4>(A, plan, PL, Rt, bb, Yb, n, r, seg, B, st);
+  if (r <= 32) launch_monarch6<1>(A, plan, PL, Rt, bb, Yb, n, r, si.map(), B, st);
+  else if (r <= 64) launch_monarch6<2>(A, plan, PL, Rt, bb, Yb, n, r, si.map(), B, st);
+  else launch_monarch6<4>(A, plan, PL, Rt, bb, Yb, n, r, si.map(), B, st);
   E.mark(5, st);
   return hipGetLastError() == hipSuccess ? DYRA_OK : DYRA_EHIP;
 }
 
-int forward_blast(const dyra_spec& s, const char* plan, const void* X, const void* bias, void* Y, int64_t B,
-                  int64_t seg, float eps, int solver, char* ws, hipStream_t st, const StageEvents& E) {
+int forward_blast(const dyra_spec& s, const char* plan, const void* X, const void* bias, void* Y,
+                  const SegInfo& si, float eps, int solver, char* ws, hipStream_t st, const StageEvents& E) {
   const PlanLayout PL = plan_layout(s, DYRA_BF16);
-  const WsLayout WL = ws_layout(s, B, seg, DYRA_BF16);
-  const int64_t n = B * seg, c1 = s.c1, c2 = s.c2;
+  const WsLayout WL = si.layout(s, DYRA_BF16);
+  const int64_t B = si.B, n = si.n, c1 = s.c1, c2 = s.c2;
   const int r = s.r, nb = s.nb, rb = s.rb;
   const int64_t b1 = c1 / nb, b2 = c2 / nb, NR = (int64_t)nb * rb, ldzl = NR + r;
   bf16_t* ZL = reinterpret_cast<bf16_t*>(ws + WL.A);
@@ -3170,7 +3199,7 @@ int forward_blast(const dyra_spec& s, const char* plan, const void* X, const voi
     }
   }
   E.mark(1, st);
-  forward_residual<CfgB, CfgB3>(s, plan, X, B, seg, eps, solver, ws, st, E);
+  forward_residual<CfgB, CfgB3>(s, plan, X, si, eps, solver, ws, st, E);
   if (s.kind == DYRA_BLAST_DIAG) {
     // coupling W'_j = sum_i Z_i diag(s_ij): elementwise over the block grid
     const int zt = (int)std::max<int64_t>(1, std::min<int64_t>(8, (BDC_LDS / 2) / NR));
@@ -3190,13 +3219,13 @@ int forward_blast(const dyra_spec& s, const char* plan, const void* X, const voi
       const int64_t tiles = cdiv(n, C6::BM) * tiles_n;
       hipLaunchKernelGGL(s6_blast_kernel<C6>, dim3((unsigned)tiles), dim3(C6::NT), 0, st, Wp, NR, ZL, ldzl, NR,
                          reinterpret_cast<const bf16_t*>(plan + PL.Vb), Rt, reinterpret_cast<const bf16_t*>(bias),
-                         reinterpret_cast<bf16_t*>(Y), n, c2, b2, rb, r, seg, B, tiles_n);
+                         reinterpret_cast<bf16_t*>(Y), n, c2, b2, rb, r, si.map(), B, tiles_n);
     } else {
       const int tiles_n = (int)(c2 / CfgB::BN);
       const int64_t tiles = cdiv(n, CfgB::BM) * tiles_n;
       hipLaunchKernelGGL(s6_blast_kernel<CfgB>, dim3((unsigned)tiles), dim3(CfgB::NT), 0, st, Wp, NR, ZL, ldzl, NR,
                          reinterpret_cast<const bf16_t*>(plan + PL.Vb), Rt, reinterpret_cast<const bf16_t*>(bias),
-                         reinterpret_cast<bf16_t*>(Y), n, c2, b2, rb, r, seg, B, tiles_n);
+                         reinterpret_cast<bf16_t*>(Y), n, c2, b2, rb, r, si.map(), B, tiles_n);
     }
   }
   E.mark(5, st);
@@ -3260,24 +3289,95 @@ extern "C" int dyra_workspace_size_als(const dyra_spec* spec, int64_t B, int64_t
 }
 
 namespace {
+// The forward on validated arguments.
+int dispatch(const dyra_spec* spec, const void* plan, const void* X, const void* bias, void* Y, const SegInfo& si,
+             int32_t dtype, float ridge_eps, int32_t solver, void* workspace, void* stream, const StageEvents& E,
+             int32_t half_steps) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const char* plan_c = reinterpret_cast<const char*>(plan);
+  char* ws = reinterpret_cast<char*>(workspace);
+  if (spec->kind == DYRA_MONARCH)
+    return forward_monarch(*spec, plan_c, X, bias, Y, si, ridge_eps, solver, ws, st, E);
+  if (is_blast(spec->kind)) return forward_blast(*spec, plan_c, X, bias, Y, si, ridge_eps, solver, ws, st, E);
+  if (dtype == DYRA_BF16)
+    return forward_lowrank<CfgB, CfgB3, CfgB6>(*spec, plan_c, X, bias, Y, si, ridge_eps, solver, ws, st, E,
+                                               half_steps);
+  return forward_lowrank<CfgF, CfgF3, CfgF>(*spec, plan_c, X, bias, Y, si, ridge_eps, solver, ws, st, E);
+}
+
 int forward_impl(const dyra_spec* spec, const void* plan, const void* X, const void* bias, void* Y, int64_t B,
                  int64_t s, int32_t dtype, float ridge_eps, int32_t solver, void* workspace, size_t ws_bytes,
                  void* stream, const StageEvents& E, int32_t half_steps = 2) {
   int rc = check_forward_args(spec, plan, X, Y, B, s, dtype, ridge_eps, solver, workspace, ws_bytes, half_steps);
   if (rc) return rc;
   if (bias && (reinterpret_cast<uintptr_t>(bias) & 15)) return DYRA_EINVAL;
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const char* plan_c = reinterpret_cast<const char*>(plan);
-  char* ws = reinterpret_cast<char*>(workspace);
-  if (spec->kind == DYRA_MONARCH)
-    return forward_monarch(*spec, plan_c, X, bias, Y, B, s, ridge_eps, solver, ws, st, E);
-  if (is_blast(spec->kind)) return forward_blast(*spec, plan_c, X, bias, Y, B, s, ridge_eps, solver, ws, st, E);
-  if (dtype == DYRA_BF16)
-    return forward_lowrank<CfgB, CfgB3, CfgB6>(*spec, plan_c, X, bias, Y, B, s, ridge_eps, solver, ws, st, E,
-                                               half_steps);
-  return forward_lowrank<CfgF, CfgF3, CfgF>(*spec, plan_c, X, bias, Y, B, s, ridge_eps, solver, ws, st, E);
+  return dispatch(spec, plan, X, bias, Y, SegInfo::uniform(B, s), dtype, ridge_eps, solver, workspace, stream, E,
+                  half_steps);
+}
+
+// Ragged segments from host row offsets off[0 .. B] (off[0] = 0, every
+// segment at least one row, off[B] = n < 2^31); off_dev is the caller's
+// device copy (may be null when only sizes are wanted).
+int varlen_info(int64_t B, const int64_t* off, const int32_t* off_dev, SegInfo& si) {
+  if (!off) return DYRA_EINVAL;
+  if (B <= 0 || B >= ((int64_t)1 << 31)) return DYRA_ESHAPE;
+  if (off[0] != 0) return DYRA_ESHAPE;
+  int64_t mx = 0, mn = INT64_MAX;
+  for (int64_t b = 0; b < B; ++b) {
+    const int64_t len = off[b + 1] - off[b];
+    if (len < 1) return DYRA_ESHAPE;
+    mx = std::max(mx, len);
+    mn = std::min(mn, len);
+  }
+  if (off[B] >= ((int64_t)1 << 31)) return DYRA_ESHAPE;
+  if (off_dev && (reinterpret_cast<uintptr_t>(off_dev) & 3)) return DYRA_EINVAL;
+  si = SegInfo{};
+  si.B = B;
+  si.n = off[B];
+  si.seg = 0;
+  si.max_len = mx;
+  si.min_len = mn;
+  si.off_dev = off_dev;
+  return DYRA_OK;
 }
 }  // namespace
+
+extern "C" int dyra_workspace_size_varlen(const dyra_spec* spec, int64_t B, const int64_t* offsets, int32_t dtype,
+                                          size_t* bytes) {
+  if (!spec || !bytes) return DYRA_EINVAL;
+  int rc = validate_spec(spec);
+  if (rc) return rc;
+  rc = validate_dtype(*spec, dtype);
+  if (rc) return rc;
+  SegInfo si;
+  rc = varlen_info(B, offsets, nullptr, si);
+  if (rc) return rc;
+  *bytes = si.layout(*spec, dtype).total;
+  return DYRA_OK;
+}
+
+extern "C" int dyra_forward_varlen(const dyra_spec* spec, const void* plan, const void* X, const void* bias,
+                                   void* Y, int64_t B, const int64_t* offsets, const int32_t* offsets_dev,
+                                   int32_t dtype, float ridge_eps, int32_t solver, int32_t* status_out,
+                                   void* workspace, size_t ws_bytes, void* stream) {
+  if (!offsets_dev) return DYRA_EINVAL;
+  SegInfo si;
+  int rc = varlen_info(B, offsets, offsets_dev, si);
+  if (rc) return rc;
+  // the uniform checks with one segment of all n rows, then the ragged size
+  rc = check_forward_args(spec, plan, X, Y, 1, si.n, dtype, ridge_eps, solver, workspace, (size_t)-1);
+  if (rc) return rc;
+  if (bias && (reinterpret_cast<uintptr_t>(bias) & 15)) return DYRA_EINVAL;
+  if (status_out && (reinterpret_cast<uintptr_t>(status_out) & 3)) return DYRA_EINVAL;
+  const WsLayout WL = si.layout(*spec, dtype);
+  if (ws_bytes < WL.total) return DYRA_EWORKSPACE;
+  rc = dispatch(spec, plan, X, bias, Y, si, dtype, ridge_eps, solver, workspace, stream, StageEvents{nullptr, 0}, 2);
+  if (rc || !status_out) return rc;
+  if (hipMemcpyAsync(status_out, reinterpret_cast<const char*>(workspace) + WL.status, (size_t)B * 4,
+                     hipMemcpyDeviceToDevice, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return DYRA_EHIP;
+  return DYRA_OK;
+}
 
 extern "C" int dyra_forward(const dyra_spec* spec, const void* plan, const void* X, const void* bias, void* Y,
                             int64_t B, int64_t s, int32_t dtype, float ridge_eps, int32_t solver,

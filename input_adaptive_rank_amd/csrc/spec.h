@@ -157,7 +157,10 @@ inline S5Split s5_split(int64_t c2, int64_t nr, int64_t K) {
 // Lt   [r x n256] L transposed (token-contiguous, pitch n rounded up to 256)
 // G    [B x r x r] fp32        Gram matrices L_b^T L_b
 // M    [B x r x c1] fp32       L_b^T X_b
-// Ginv [B x r x r] fp32        (G_b + lambda_b I)^-1
+// Ginv [B x r x r] fp64        (G_b + lambda_b I)^-1 (fp64: near-singular G_b
+//                              put 1 / lambda_b-sized entries in it that
+//                              cancel in Ginv M; fp32 rounding would not)
+// Xit  [B x r x r] fp32        Newton-Schulz iterate handed to its polish
 // Mp   [B x r x c1] dtype      M'_b = Ginv_b M_b
 // Rt   [c2 x B r] dtype        R_b^T for every segment, R_b = M'_b W_res
 // status [B] int32
@@ -165,20 +168,23 @@ inline S5Split s5_split(int64_t c2, int64_t nr, int64_t K) {
 //      BLAST also [slices x n x r] for L = X P split over K
 struct WsLayout {
   int64_t wa = 0;
-  size_t A = 0, Wp = 0, Lt = 0, G = 0, M = 0, Ginv = 0, Mp = 0, Rt = 0, status = 0, Pk = 0;
+  size_t A = 0, Wp = 0, Lt = 0, G = 0, M = 0, Ginv = 0, Mp = 0, Rt = 0, status = 0, Pk = 0, Xit = 0;
   // Gram partials [B][gchunks][r x r] fp32 over token chunks of gchunk tokens
   size_t Gp = 0;
   int64_t gchunk = 0, gchunks = 0;
-  // left ALS steps (half_steps > 2): R [B r x c2], K and Kinv [B x r x r]
-  // fp32, Q^T [B x r x c1] fp32, Z^T [B x r x c1], their status words [B]
+  // left ALS steps (half_steps > 2): R [B r x c2], K [B x r x r] fp32 and
+  // Kinv fp64, Q^T [B x r x c1] fp32, Z^T [B x r x c1], their status words [B]
   size_t R = 0, K = 0, Kinv = 0, Qt = 0, Zt = 0, kstatus = 0;
   size_t total = 0;
 };
 
-inline WsLayout ws_layout(const dyra_spec& s, int64_t B, int64_t seg, int dtype, int half_steps = 2) {
+// B segments of n rows in all, the longest max_len rows.
+inline WsLayout ws_layout_n(const dyra_spec& s, int64_t B, int64_t n_rows, int64_t max_len, int dtype,
+                            int half_steps = 2) {
   WsLayout W;
   const size_t e = elem_bytes(dtype);
-  const size_t n = (size_t)(B * seg), r = (size_t)s.r, c1 = (size_t)s.c1, c2 = (size_t)s.c2;
+  const int64_t seg = max_len;
+  const size_t n = (size_t)n_rows, r = (size_t)s.r, c1 = (size_t)s.c1, c2 = (size_t)s.c2;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
@@ -195,7 +201,8 @@ inline WsLayout ws_layout(const dyra_spec& s, int64_t B, int64_t seg, int dtype,
   W.Lt = take(r * ((n + 255) / 256 * 256) * e);   // token pitch padded to 256
   W.G = take((size_t)B * r * r * 4);
   W.M = take((size_t)B * r * c1 * 4);
-  W.Ginv = take((size_t)B * r * r * 4);
+  W.Ginv = take((size_t)B * r * r * 8);
+  W.Xit = take((size_t)B * r * r * 4);
   W.Mp = take((size_t)B * r * c1 * e);
   W.Rt = take(c2 * (size_t)B * r * e);
   W.status = take((size_t)B * 4);
@@ -216,13 +223,18 @@ inline WsLayout ws_layout(const dyra_spec& s, int64_t B, int64_t seg, int dtype,
   if (half_steps > 2) {
     W.R = take((size_t)B * r * c2 * e);
     W.K = take((size_t)B * r * r * 4);
-    W.Kinv = take((size_t)B * r * r * 4);
+    W.Kinv = take((size_t)B * r * r * 8);
     W.Qt = take((size_t)B * r * c1 * 4);
     W.Zt = take((size_t)B * r * c1 * e);
     W.kstatus = take((size_t)B * 4);
   }
   W.total = off;
   return W;
+}
+
+// B segments of seg rows each.
+inline WsLayout ws_layout(const dyra_spec& s, int64_t B, int64_t seg, int dtype, int half_steps = 2) {
+  return ws_layout_n(s, B, B * seg, seg, dtype, half_steps);
 }
 
 }  // namespace dyra_spec_util

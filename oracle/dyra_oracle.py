@@ -359,18 +359,28 @@ def als(X: np.ndarray, W_res: np.ndarray, R0: np.ndarray, t: float, eps: float,
 # [P2] 2.4: bias is merged with the base projection and the correction)
 # ---------------------------------------------------------------------------
 
+def segment_rows(B: int, s: int, offsets=None) -> list:
+    """Row ranges of the segments: B runs of s rows, or rows offsets[b] ..
+    offsets[b + 1] - 1 (ragged segments, e.g. prompts of mixed length)."""
+    if offsets is None:
+        return [(b * s, (b + 1) * s) for b in range(B)]
+    return [(int(offsets[b]), int(offsets[b + 1])) for b in range(len(offsets) - 1)]
+
+
 def forward(X: np.ndarray, prep: dict, bias: np.ndarray | None, B: int, s: int,
-            eps: float = 1e-6, t: float = 1.0) -> np.ndarray:
-    """Y = X W_hat + L R + bias, with (L, R) from ALS on each segment."""
+            eps: float = 1e-6, t: float = 1.0, offsets=None) -> np.ndarray:
+    """Y = X W_hat + L R + bias, with (L, R) from ALS on each segment
+    (B segments of s rows, or the ragged segments of `offsets`)."""
     n, c1 = X.shape
-    assert n == B * s
+    rows = segment_rows(B, s, offsets)
+    assert rows[0][0] == 0 and rows[-1][1] == n
     kind, f, W_res, R0, P = prep["kind"], prep["static"], prep["W_res"], prep["R0"], prep["P"]
     Y = np.empty((n, W_res.shape[1]))
-    for b in range(B):
-        Xb = X[b * s:(b + 1) * s]
+    for lo, hi in rows:
+        Xb = X[lo:hi]
         base = static_apply(kind, Xb, f)
         L, R = als(Xb, W_res, R0, t, eps, P=P if t >= 1 else None)
-        Y[b * s:(b + 1) * s] = base + L @ R
+        Y[lo:hi] = base + L @ R
     if bias is not None:
         Y += bias[None, :]
     return Y

@@ -238,3 +238,32 @@ def test_one_hip_runtime_per_process_whatever_the_import_order():
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
     assert out.returncode == 0, out.stderr
     assert out.stdout.split()[0] == "1", out.stdout
+
+
+@pytest.mark.parametrize("off,code", [
+    ([0, 10, 25, 40], 0),
+    ([1, 10, 25, 40], -2),          # does not start at row 0
+    ([0, 10, 10, 40], -2),          # an empty segment
+    ([0, 30, 20, 40], -2),          # decreasing
+])
+def test_varlen_offsets_validation(off, code):
+    spec = _lowrank()
+    a = np.array(off, dtype=np.int64)
+    n = ctypes.c_size_t()
+    assert D.lib().dyra_workspace_size_varlen(ctypes.byref(spec), len(off) - 1,
+                                              a.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), synth.DT_BF16,
+                                              ctypes.byref(n)) == code
+
+
+def test_varlen_workspace_matches_uniform_and_forward_rejects_before_hip():
+    spec = _lowrank()
+    assert D.workspace_size_varlen(spec, [0, 50, 100], synth.DT_BF16) == D.workspace_size(spec, 2, 50, synth.DT_BF16)
+    a = np.array([0, 50, 100], dtype=np.int64)
+    P = ctypes.POINTER(ctypes.c_int64)
+    L = D.lib()
+    # null device offsets, then a workspace one byte short: rejected before any HIP call
+    assert L.dyra_forward_varlen(ctypes.byref(spec), 1 << 12, 1 << 13, None, 1 << 14, 2, a.ctypes.data_as(P), None,
+                                 synth.DT_BF16, 1e-6, 0, None, 1 << 15, 1 << 40, None) == -1
+    need = D.workspace_size_varlen(spec, a, synth.DT_BF16)
+    assert L.dyra_forward_varlen(ctypes.byref(spec), 1 << 12, 1 << 13, None, 1 << 14, 2, a.ctypes.data_as(P),
+                                 1 << 16, synth.DT_BF16, 1e-6, 0, None, 1 << 15, need - 1, None) == -3

@@ -42,7 +42,7 @@ def test_terms_sum_to_the_oracle_forward(kind, t):
             O.KIND_BLAST: sc(W["lm_blast"], B=2, s=60, c1=128, c2=256, nb=4, rb=8, r=8, n_out=2)}[kind]
     inp = synth.make_inputs(base)
     rp = rounded_prep(oracle_prepare(base, inp.W), base.dtype)
-    Y, corr, mag = oracle_terms(base, inp.X, rp, inp.bias, eps=1e-6, t=t)
+    Y, corr, mag, _ = oracle_terms(base, inp.X, rp, inp.bias, eps=1e-6, t=t)
     assert np.array_equal(Y, O.forward(inp.X, rp, inp.bias, base.B, base.s, eps=1e-6, t=t))
     assert np.all(mag >= np.abs(Y) * (1 - 1e-12))
 
@@ -57,7 +57,7 @@ def test_checker_accepts_storage_rounding(vitl4):
 
 def test_whole_output_ratio_misses_what_the_checker_finds(vitl4):
     w, _, _, terms, Y_like = vitl4
-    Y, corr, _ = terms
+    Y, corr, _, _ = terms
     s = w.s
     dropped = Y_like.copy()
     dropped[2 * s:3 * s] -= corr[2 * s:3 * s]                  # segment 2 without L R
@@ -82,3 +82,22 @@ def test_checker_separates_t_1p5_from_t_1(vitl4):
     Y15 = synth.round_bf16(T @ rp["static"]["V"] + terms15[1] + inp.bias)
     m, fails = parity_report(w, Y15, terms15)
     assert not fails, fails
+
+
+def test_checker_still_sees_a_dropped_correction_on_an_ill_conditioned_segment():
+    """A segment with as many tokens as r has cond(L_b) in the hundreds, so it
+    gets the conditioning allowance; without its correction it still fails."""
+    w = sc(W["vitb_fc1"], name="ill", B=1, s=982, c1=256, c2=264, k=32, r=16)
+    off = [0, 437, 453, 982]                                # segment 1: 16 = r tokens
+    inp = synth.make_inputs(w)
+    rp = rounded_prep(oracle_prepare(w, inp.W), w.dtype)
+    terms = oracle_terms(w, inp.X, rp, inp.bias, offsets=off)
+    Y, corr, _, conds = terms
+    assert 2.0 ** -8 * conds[1] > 0.25 and 2.0 ** -8 * conds[0] < 0.25
+    ok = synth.round_bf16(Y)
+    m, fails = parity_report(w, ok, terms, offsets=off)
+    assert not fails and m["ill_conditioned_segments"] == 1, fails
+    bad = ok.copy()
+    bad[437:453] -= corr[437:453]
+    m, fails = parity_report(w, bad, terms, offsets=off)
+    assert any(f.startswith("segment 1") for f in fails), fails

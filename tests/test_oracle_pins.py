@@ -574,6 +574,19 @@ def test_row_permutation_equivariance_and_segment_independence():
         np.testing.assert_allclose(Yb, Y[b * 20:(b + 1) * 20], atol=1e-13)
 
 
+def test_ragged_segments_are_independent_forwards():
+    """Segments given by row offsets: each is its own ALS solve, so the
+    ragged forward is the concatenation of one-segment forwards, and uniform
+    offsets reproduce the B x s forward bit for bit."""
+    rng, _, prep, X, bias = _setup()
+    off = [0, 1, 9, 23, 60]                       # lengths 1, 8, 14, 37 (one shorter than r = 5)
+    Y = O.forward(X, prep, bias, 0, 0, offsets=off)
+    for lo, hi in zip(off[:-1], off[1:]):
+        np.testing.assert_array_equal(Y[lo:hi], O.forward(X[lo:hi], prep, bias, 1, hi - lo))
+    np.testing.assert_array_equal(O.forward(X, prep, bias, 0, 0, offsets=[0, 20, 40, 60]),
+                                  O.forward(X, prep, bias, 3, 20))
+
+
 def test_rotation_of_initial_right_factor_changes_nothing():
     rng, _, prep, X, bias = _setup()
     Q = synth.haar_columns(rng.standard_normal((5, 5)))
