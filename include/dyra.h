@@ -203,10 +203,13 @@ int dyra_workspace_size(const dyra_spec* spec, int64_t B, int64_t s, int32_t dty
  *   Mp     [B][r][c1]   dtype Ginv_b M_b
  *   Rt     [c2][B r]    dtype R_b^T, R_b = Mp_b W_res
  *   status [B]          int32 solver status words
+ *   prec   [B]          int32 1 where Mp_b was formed in fp64 (the solve met
+ *                       a relative pivot below 2^-5, or Newton-Schulz
+ *                       solved it), 0 where in fp32
  * Errors: EINVAL, ESHAPE, EDTYPE.
  */
 typedef struct {
-  int64_t A, Wp, Lt, G, M, Ginv, Mp, Rt, status, total, wa, lt_pitch;
+  int64_t A, Wp, Lt, G, M, Ginv, Mp, Rt, status, total, wa, lt_pitch, prec;
 } dyra_ws_offsets;
 
 int dyra_workspace_offsets(const dyra_spec* spec, int64_t B, int64_t s, int32_t dtype,
@@ -297,6 +300,33 @@ int dyra_forward_events(const dyra_spec* spec, const void* plan, const void* X, 
 int dyra_forward_noalloc(const dyra_spec* spec, const void* plan, const void* X, const void* bias, void* Y,
                          int64_t B, int64_t s, int32_t dtype, float ridge_eps, int32_t solver,
                          int32_t* status_out, void* stream);
+
+/*
+ * Ragged segments: dyra_forward over B segments of different lengths, one
+ * per input of a batch that was concatenated token-wise (each input gets its
+ * own low-rank correction, as for uniform segments).
+ *   offsets:     host int64[B + 1], offsets[0] = 0, strictly increasing
+ *                (every segment at least one row), offsets[B] = n < 2^31;
+ *                segment b = rows [offsets[b], offsets[b + 1]).
+ *   offsets_dev: device int32[B + 1] holding the same values (4-byte
+ *                aligned; read by the kernels, never written).
+ *   X: device [n][c1]; Y: device [n][c2]; status_out: device int32[B] that
+ *   receives the per-segment DYRA_SOLVE_* words, or NULL.
+ *   workspace: device, >= dyra_workspace_size_varlen bytes.
+ * Other arguments as for dyra_forward.  Errors (before any HIP call):
+ * EINVAL (NULL offsets or offsets_dev, misaligned pointers), ESHAPE
+ * (offsets[0] != 0, an empty segment, n >= 2^31), EDTYPE, EWORKSPACE; EHIP
+ * if a launch fails.  The host and device offsets must agree: the library
+ * does not compare them.
+ * Source: nanless.github.io DyRA digest (the per-input correction L1 R1);
+ * paperlayer.ai 2.2.
+ */
+int dyra_workspace_size_varlen(const dyra_spec* spec, int64_t B, const int64_t* offsets,
+                               int32_t dtype, size_t* bytes);
+int dyra_forward_varlen(const dyra_spec* spec, const void* plan, const void* X, const void* bias,
+                        void* Y, int64_t B, const int64_t* offsets, const int32_t* offsets_dev,
+                        int32_t dtype, float ridge_eps, int32_t solver, int32_t* status_out,
+                        void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * Copies the B per-segment solver status words of the last dyra_forward on

@@ -925,22 +925,25 @@ __global__ __launch_bounds__(C::NT) void s1_left_kernel(const bf16_t* X, const b
 constexpr int MO = 32;
 
 // Stage 1 + L: one pass over X.  A workgroup owns 32 rows; wave w takes the
-// 8 blocks a = 8w .. 8w + 7: it accumulates U_a (32 x 32 each), puts the
-// permuted V[row][j*32 + 8w .. 8w + 7] into an LDS copy of the 32 V rows
-// (written out as whole rows), and accumulates its K slice (a*32 .. a*32 + 31
-// for its 8 blocks) of L = X P.  B1t and Pt are in fragment order: a wave's
-// operand of one MFMA step is one contiguous 1 KB run.  The four partial L
-// sums are added through LDS in a fixed order; wave 0 writes L and L^T.
+// 8 blocks a = 8w .. 8w + 7 and accumulates its K slice (a*32 .. a*32 + 31
+// for its 8 blocks) of L = X P.  With WITH_V it also accumulates U_a
+// (32 x 32 each) and puts the permuted V[row][j*32 + 8w .. 8w + 7] into an
+// LDS copy of the 32 V rows, written out as whole rows (the two-pass Monarch
+// output); without it only L is formed and the output kernel recomputes V
+// from X.  B1t and Pt are in fragment order: a wave's operand of one MFMA
+// step is one contiguous 1 KB run.  The four partial L sums are added
+// through LDS in a fixed order; wave 0 writes L and L^T.
 constexpr int S1M_VP = MO * MO * 2 + 16;                  // V row pitch in LDS (bytes)
-template <int RB>
+template <int RB, bool WITH_V>
 __global__ __launch_bounds__(256, 2) void s1_monarch_kernel(const bf16_t* __restrict__ X,
                                                          const bf16_t* __restrict__ B1t,
                                                          const bf16_t* __restrict__ Pt,
                                                          bf16_t* __restrict__ A, bf16_t* __restrict__ Lt,
                                                          int64_t n, int r, int64_t ldt) {
   constexpr int C = MO * MO;
-  static_assert(3 * RB * 16 * 64 * 4 <= 32 * S1M_VP, "L partials fit the V staging");
-  __shared__ __attribute__((aligned(16))) char sm[32 * S1M_VP];
+  constexpr int PART = 3 * RB * 16 * 64 * 4;
+  constexpr int SMB = WITH_V ? (32 * S1M_VP > PART ? 32 * S1M_VP : PART) : PART;
+  __shared__ __attribute__((aligned(16))) char sm[SMB];
   float* part = reinterpret_cast<float*>(sm);             // [3][RB][16][64], after V is written out
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int l = lane & 31, g = lane >> 5;
@@ -952,18 +955,22 @@ __global__ __launch_bounds__(256, 2) void s1_monarch_kernel(const bf16_t* __rest
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int v = 0; v < 16; ++v) lacc[rb][v] = 0.f;
-  f32x16 uacc[8];
+  f32x16 uacc[WITH_V ? 8 : 1];
 #pragma unroll
   for (int ai = 0; ai < 8; ++ai) {
+    if constexpr (WITH_V) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) uacc[ai][v] = 0.f;
+      for (int v = 0; v < 16; ++v) uacc[ai][v] = 0.f;
+    }
     const int a = w * 8 + ai;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int kk = a * MO + 16 * s + 8 * g;
       const uint4 xa = rok ? *reinterpret_cast<const uint4*>(X + row * C + kk) : zero4();
-      const uint4 b1 = *reinterpret_cast<const uint4*>(B1t + ((a * 2 + s) * 64 + lane) * 8);
-      TT<bf16_t>::mma(uacc[ai], b1, xa);
+      if constexpr (WITH_V) {
+        const uint4 b1 = *reinterpret_cast<const uint4*>(B1t + ((a * 2 + s) * 64 + lane) * 8);
+        TT<bf16_t>::mma(uacc[ai], b1, xa);
+      }
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         const int p = rb * 32 + l;
@@ -973,27 +980,29 @@ __global__ __launch_bounds__(256, 2) void s1_monarch_kernel(const bf16_t* __rest
       }
     }
   }
-  // lane holds U[row][a*32 + j] for j = 8q + 4g + e (reg 4q + e), a = 8w + ai
+  if constexpr (WITH_V) {
+    // lane holds U[row][a*32 + j] for j = 8q + 4g + e (reg 4q + e), a = 8w + ai
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < 4; ++q)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int j = 8 * q + 4 * g + e;
-      uint32_t pk[4];
+      for (int e = 0; e < 4; ++e) {
+        const int j = 8 * q + 4 * g + e;
+        uint32_t pk[4];
 #pragma unroll
-      for (int h = 0; h < 4; ++h)
-        pk[h] = (uint32_t)f2bf(uacc[2 * h][4 * q + e]) | ((uint32_t)f2bf(uacc[2 * h + 1][4 * q + e]) << 16);
-      *reinterpret_cast<uint4*>(sm + l * S1M_VP + (j * MO + w * 8) * 2) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+        for (int h = 0; h < 4; ++h)
+          pk[h] = (uint32_t)f2bf(uacc[2 * h][4 * q + e]) | ((uint32_t)f2bf(uacc[2 * h + 1][4 * q + e]) << 16);
+        *reinterpret_cast<uint4*>(sm + l * S1M_VP + (j * MO + w * 8) * 2) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+      }
+    __syncthreads();
+    // the 32 V rows: 128 runs of 16 bytes each, a wave instruction 1 KB of one row
+    for (int c = threadIdx.x; c < 32 * (C / 8); c += 256) {
+      const int rl = c / (C / 8), ch = c % (C / 8);
+      const int64_t vr = (int64_t)blockIdx.x * 32 + rl;
+      if (vr < n)
+        *reinterpret_cast<uint4*>(A + vr * lda + ch * 8) = *reinterpret_cast<const uint4*>(sm + rl * S1M_VP + ch * 16);
     }
-  __syncthreads();
-  // the 32 V rows: 128 runs of 16 bytes each, a wave instruction 1 KB of one row
-  for (int c = threadIdx.x; c < 32 * (C / 8); c += 256) {
-    const int rl = c / (C / 8), ch = c % (C / 8);
-    const int64_t vr = (int64_t)blockIdx.x * 32 + rl;
-    if (vr < n)
-      *reinterpret_cast<uint4*>(A + vr * lda + ch * 8) = *reinterpret_cast<const uint4*>(sm + rl * S1M_VP + ch * 16);
+    __syncthreads();
   }
-  __syncthreads();
   // L partials: waves 1..3 -> LDS, wave 0 adds them in order
   if (w > 0) {
 #pragma unroll
@@ -1129,6 +1138,131 @@ __global__ __launch_bounds__(256) void s6_monarch_kernel(const bf16_t* __restric
     if (yr < n)
       *reinterpret_cast<uint4*>(Y + yr * C + j0 * MO + ch * 8) =
           *reinterpret_cast<const uint4*>(sm + (w * 32 + rl) * S6M_YP + ch * 16);
+  }
+}
+
+// One-pass Monarch output: a workgroup owns 32 rows and all 1024 output
+// columns, and recomputes stage 1 from X instead of reading a stored V.
+//   phase 1: wave w forms U_a = x_a B1_a for a = 8w .. 8w + 7 (as the first
+//            stage does) and writes the permuted V[row][j*32 + a] into an LDS
+//            copy of the 32 V rows;
+//   phase 2: wave w forms y_j = V_j B2_j + L R_b[:, j] for j = 8w .. 8w + 7,
+//            V_j from LDS (bytes 512 w .. 512 w + 511 of each row: the
+//            wave's own slice, so it then stages its output rows there
+//            without a workgroup barrier), B2t and R^T rows straight from L2
+//            (each lane's 16-byte runs of one 128-byte line are read by the
+//            same wave in consecutive k steps);
+//   store:   the bias is added on packing, and every store instruction
+//            writes two whole 512-byte row slices.
+// X is read once here and once by the first stage (L only), V never touches
+// HBM.
+__global__ __launch_bounds__(256, 2) void s6_monarch_fused_kernel(const bf16_t* __restrict__ X,
+                                                               const bf16_t* __restrict__ B1t,
+                                                               const bf16_t* __restrict__ B2t,
+                                                               const bf16_t* __restrict__ A,
+                                                               const bf16_t* __restrict__ Rt,
+                                                               const bf16_t* __restrict__ bias,
+                                                               bf16_t* __restrict__ Y, int64_t n, int r, SegMap sg,
+                                                               int64_t B) {
+  constexpr int C = MO * MO;
+  __shared__ __attribute__((aligned(16))) char sm[32 * S1M_VP];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int l = lane & 31, g = lane >> 5;
+  const int64_t m0 = (int64_t)blockIdx.x * 32;
+  const int64_t row = m0 + l;
+  const bool rok = row < n;
+  const int64_t lda = C + r;
+  f32x16 acc[8];
+  // ---- phase 1: U_a for the wave's 8 blocks, permuted into LDS ----
+#pragma unroll
+  for (int ai = 0; ai < 8; ++ai) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[ai][v] = 0.f;
+    const int a = w * 8 + ai;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int kk = a * MO + 16 * s + 8 * g;
+      const uint4 xa = rok ? *reinterpret_cast<const uint4*>(X + row * C + kk) : zero4();
+      const uint4 b1 = *reinterpret_cast<const uint4*>(B1t + ((a * 2 + s) * 64 + lane) * 8);
+      TT<bf16_t>::mma(acc[ai], b1, xa);
+    }
+  }
+  // lane holds U[row][a*32 + j] for j = 8q + 4g + e (reg 4q + e), a = 8w + ai
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int j = 8 * q + 4 * g + e;
+      uint32_t pk[4];
+#pragma unroll
+      for (int h = 0; h < 4; ++h)
+        pk[h] = (uint32_t)f2bf(acc[2 * h][4 * q + e]) | ((uint32_t)f2bf(acc[2 * h + 1][4 * q + e]) << 16);
+      *reinterpret_cast<uint4*>(sm + l * S1M_VP + (j * MO + w * 8) * 2) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    }
+  __syncthreads();
+  // ---- phase 2: y_j = V_j B2_j (K = 32: two 16-wide k steps) ----
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[jj][v] = 0.f;
+    const int j = w * 8 + jj;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const uint4 va = *reinterpret_cast<const uint4*>(sm + l * S1M_VP + (j * MO + 16 * s + 8 * g) * 2);
+      const uint4 b2 = *reinterpret_cast<const uint4*>(B2t + ((int64_t)(j * MO + l) * MO + 16 * s + 8 * g));
+      TT<bf16_t>::mma(acc[jj], b2, va);
+    }
+  }
+  // + L R_b for every segment meeting the 32 rows
+  const int64_t mend = imin64(m0 + 32, n);
+  const int64_t bf = sg.of(imin64(m0, n - 1)), bl = imin64(B - 1, sg.of(mend - 1));
+  const int64_t ldr = B * r;
+  for (int64_t b = bf; b <= bl; ++b) {
+    const int64_t blo = sg.lo(b), bhi = sg.hi(b);
+    const bool in = rok && row >= blo && row < bhi;
+    for (int k0 = 0; k0 < r; k0 += 16) {
+      const int kk = k0 + 8 * g;
+      const uint4 la = (in && kk < r) ? *reinterpret_cast<const uint4*>(A + row * lda + C + kk) : zero4();
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int c = (w * 8 + jj) * MO + l;
+        const uint4 rt = kk < r ? *reinterpret_cast<const uint4*>(Rt + (int64_t)c * ldr + b * r + kk) : zero4();
+        TT<bf16_t>::mma(acc[jj], rt, la);
+      }
+    }
+  }
+  // ---- stage the wave's 32 x 256 output slice over its own V slice ----
+  // accumulator (jj) element 4 q + e: row l, column 32 (8w + jj) + 8 q + 4 g + e
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int cl = (w * 8 + jj) * MO + 8 * q + 4 * g;
+      float v[4];
+      if (bias) {
+        const uint2 bb = *reinterpret_cast<const uint2*>(bias + cl);
+        v[0] = acc[jj][4 * q] + __uint_as_float(bb.x << 16);
+        v[1] = acc[jj][4 * q + 1] + __uint_as_float(bb.x & 0xffff0000u);
+        v[2] = acc[jj][4 * q + 2] + __uint_as_float(bb.y << 16);
+        v[3] = acc[jj][4 * q + 3] + __uint_as_float(bb.y & 0xffff0000u);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = acc[jj][4 * q + e];
+      }
+      uint2 pk;
+      pk.x = pack_bf16x2(v[0], v[1]);
+      pk.y = pack_bf16x2(v[2], v[3]);
+      *reinterpret_cast<uint2*>(sm + l * S1M_VP + cl * 2) = pk;
+    }
+  __builtin_amdgcn_wave_barrier();
+  // 32 rows x 512 bytes: 32 lanes per row slice, two rows per store
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int rl = 2 * i + (lane >> 5), ch = lane & 31;
+    const int64_t yr = m0 + rl;
+    if (yr < n)
+      *reinterpret_cast<uint4*>(Y + yr * C + w * 256 + ch * 8) =
+          *reinterpret_cast<const uint4*>(sm + rl * S1M_VP + w * 512 + ch * 16);
   }
 }
 
@@ -1395,6 +1529,11 @@ struct SweepLds {
   float red[16];
 };
 
+// A solve whose smallest relative pivot d_j / A_jj (A = G + lambda I) falls
+// below this is applied in fp64 (near-singular A: Ginv's entries of order
+// 1 / lambda cancel in Ginv M).
+constexpr double kWidePivot = 1.0 / 32.0;
+
 // eps = 0 (no ridge): a pivot d_j at or below 2^-16 times the diagonal G_jj
 // (sin^2 of the angle between column j of L and the span of the earlier
 // columns) marks G as singular: status NOT_SPD and R_b = 0.  With a ridge,
@@ -1418,7 +1557,8 @@ __device__ __forceinline__ double recip_pos(double D) {
 // r <= 128 and ceil(r / TB)^2 <= NT.  Returns the status (same in every
 // thread).
 template <int NT, int TB>
-__device__ __forceinline__ int sweep_inverse(const float* Gb, double* Ob, int r, float eps, SweepLds& sh) {
+__device__ __forceinline__ int sweep_inverse(const float* Gb, double* Ob, float* Ob32, int r, float eps,
+                                             SweepLds& sh, double& rho) {
   static_assert(TB % SW_BK == 0 && TB % 2 == 0, "tile");
   const int tid = threadIdx.x;
   const int tpr = (r + TB - 1) / TB;
@@ -1452,6 +1592,7 @@ __device__ __forceinline__ int sweep_inverse(const float* Gb, double* Ob, int r,
           *reinterpret_cast<double2*>(&sh.pv[buf][i - k0][j0 + y]) = make_double2(a[x][y], a[x][y + 1]);
     }
   };
+  rho = 1.0;
   if (st == DYRA_SOLVE_OK) {
     const double lam = (double)(eps * tr / (float)r);
 #pragma unroll
@@ -1480,6 +1621,7 @@ __device__ __forceinline__ int sweep_inverse(const float* Gb, double* Ob, int r,
         const double D = Q[p][p];
         if (!(D > 0.0) || !isfinite(D)) bad = true;
         if (eps == 0.f && !(D > kSingularPivotRel * sh.diag0[kb + p])) bad = true;
+        rho = fmin(rho, D / (sh.diag0[kb + p] + lam));
         const double invD = recip_pos(D);
         double c[SW_BK];
 #pragma unroll
@@ -1550,7 +1692,11 @@ __device__ __forceinline__ int sweep_inverse(const float* Gb, double* Ob, int r,
   for (int x = 0; x < TB; ++x)
 #pragma unroll
     for (int y = 0; y < TB; ++y)
-      if (own && i0 + x < r && j0 + y < r) Ob[(i0 + x) * r + j0 + y] = st == DYRA_SOLVE_OK ? -a[x][y] : 0.0;
+      if (own && i0 + x < r && j0 + y < r) {
+        const double v = st == DYRA_SOLVE_OK ? -a[x][y] : 0.0;
+        Ob[(i0 + x) * r + j0 + y] = v;
+        Ob32[(i0 + x) * r + j0 + y] = (float)v;
+      }
   return st;
 }
 
@@ -1579,8 +1725,8 @@ __device__ __forceinline__ int packed_lower(int i, int j) { return ((i * (i + 1)
 // Needs r % TB == 0, r <= 128, ceil(r / TB)^2 <= NT and Cp: LDS for
 // r (r + 1) / 2 doubles.  Returns the status (same in every thread).
 template <int NT, int TB>
-__device__ __forceinline__ int chol_inverse(const float* Gb, double* Ob, int r, float eps, SweepLds& sh,
-                                            double* Cp) {
+__device__ __forceinline__ int chol_inverse(const float* Gb, double* Ob, float* Ob32, int r, float eps,
+                                            SweepLds& sh, double* Cp, double& rho) {
   constexpr int PB = SW_BK;
   static_assert(TB % PB == 0 && TB % 2 == 0, "tile");
   const int tid = threadIdx.x;
@@ -1613,6 +1759,7 @@ __device__ __forceinline__ int chol_inverse(const float* Gb, double* Ob, int r, 
         *reinterpret_cast<double2*>(&sh.pv[buf][i - k0][j0 + y]) = make_double2(t[x][y], t[x][y + 1]);
     }
   };
+  rho = 1.0;
   if (st == DYRA_SOLVE_OK) {
     const double lam = (double)(eps * tr / (float)r);
 #pragma unroll
@@ -1634,6 +1781,7 @@ __device__ __forceinline__ int chol_inverse(const float* Gb, double* Ob, int r, 
 #pragma unroll
         for (int q = 0; q < p; ++q) d = fma(-Ck[p][q], Ck[p][q], d);
         const bool ok = d > 0.0 && isfinite(d) && (eps > 0.f || d > kSingularPivotRel * sh.diag0[kb + p]);
+        rho = fmin(rho, d / (sh.diag0[kb + p] + lam));
         if (!ok) bad = true;
         const double c = sqrt(ok ? d : 1.0);
         ic[p] = recip_pos(c);
@@ -1802,7 +1950,11 @@ __device__ __forceinline__ int chol_inverse(const float* Gb, double* Ob, int r, 
   for (int x = 0; x < TB; ++x)
 #pragma unroll
     for (int y = 0; y < TB; ++y)
-      if (own && i0 + x < r && j0 + y < r) Ob[(i0 + x) * r + j0 + y] = st == DYRA_SOLVE_OK ? a[x][y] : 0.0;
+      if (own && i0 + x < r && j0 + y < r) {
+        const double v = st == DYRA_SOLVE_OK ? a[x][y] : 0.0;
+        Ob[(i0 + x) * r + j0 + y] = v;
+        Ob32[(i0 + x) * r + j0 + y] = (float)v;
+      }
   return st;
 }
 
@@ -2056,7 +2208,9 @@ template <int NRB, int NB, int SOLVE>
 __global__ __launch_bounds__(S3_NT, NRB <= 4 ? 2 : 1) void s3_reduce_solve_kernel(
     const bf16_t* __restrict__ Lt, int64_t ldt, const bf16_t* __restrict__ X, int64_t c1, int r, SegMap sg,
     int64_t n, int64_t B, float* __restrict__ M, float* __restrict__ G, double* __restrict__ Gi,
-    int32_t* __restrict__ status, float eps, int strips, int64_t lt_seg_rows, int x_rel,
+    float* __restrict__ Gi32,
+    int32_t* __restrict__ status, int32_t* __restrict__ prec, float eps, int strips, int64_t lt_seg_rows,
+    int x_rel,
     const float* __restrict__ gpart, int gchunks, int64_t gprows) {
   __shared__ __attribute__((aligned(16))) char lds[S3Lds<NB>::BYTES];
   SweepLds* sl = reinterpret_cast<SweepLds*>(lds + S3Lds<NB>::SW_OFF);
@@ -2157,11 +2311,16 @@ __global__ __launch_bounds__(S3_NT, NRB <= 4 ? 2 : 1) void s3_reduce_solve_kerne
       constexpr int TB = NB <= 2 ? 4 : 8;
       static_assert(32 * NB * (32 * NB + 1) / 2 * 8 <= S3Lds<NB>::SW_OFF, "packed factor fits");
       int st;
+      double rho;
       if constexpr (SOLVE == 2)
-        st = chol_inverse<S3_NT, TB>(Gs, Gi + b * r * r, r, eps, *sl, reinterpret_cast<double*>(lds));
+        st = chol_inverse<S3_NT, TB>(Gs, Gi + b * r * r, Gi32 + b * r * r, r, eps, *sl,
+                                     reinterpret_cast<double*>(lds), rho);
       else
-        st = sweep_inverse<S3_NT, TB>(Gs, Gi + b * r * r, r, eps, *sl);
-      if (threadIdx.x == 0) status[b] = st;
+        st = sweep_inverse<S3_NT, TB>(Gs, Gi + b * r * r, Gi32 + b * r * r, r, eps, *sl, rho);
+      if (threadIdx.x == 0) {
+        status[b] = st;
+        prec[b] = st == DYRA_SOLVE_OK && rho < kWidePivot ? 1 : 0;
+      }
     }
     return;
   }
@@ -2245,48 +2404,59 @@ __global__ __launch_bounds__(64) void gram_partial_kernel(const bf16_t* __restri
 // alone: the Newton-Schulz kernel flags the segments it could not solve, and
 // those keep the FALLBACK status when the sweep succeeds.
 template <int NT, int TB>
-__global__ __launch_bounds__(NT) void sweep_inverse_kernel(const float* G, double* Ginv, int32_t* status, int r,
-                                                           float eps, int only_flagged) {
+__global__ __launch_bounds__(NT) void sweep_inverse_kernel(const float* G, double* Ginv, float* Ginv32,
+                                                           int32_t* status, int32_t* prec, int r, float eps,
+                                                           int only_flagged) {
   __shared__ SweepLds sl;
   const int64_t b = blockIdx.x;
   // every thread reads the flag before the sweep's first barrier; thread 0
   // rewrites it only after the sweep
   if (only_flagged && status[b] != DYRA_SOLVE_FALLBACK) return;
-  const int st = sweep_inverse<NT, TB>(G + b * r * r, Ginv + b * r * r, r, eps, sl);
-  if (threadIdx.x == 0) status[b] = (only_flagged && st == DYRA_SOLVE_OK) ? DYRA_SOLVE_FALLBACK : st;
+  double rho;
+  const int st = sweep_inverse<NT, TB>(G + b * r * r, Ginv + b * r * r, Ginv32 + b * r * r, r, eps, sl, rho);
+  if (threadIdx.x == 0) {
+    status[b] = (only_flagged && st == DYRA_SOLVE_OK) ? DYRA_SOLVE_FALLBACK : st;
+    prec[b] = st == DYRA_SOLVE_OK && rho < kWidePivot ? 1 : 0;
+  }
 }
 
 // r <= 64: 256 threads of 4 x 4 tiles; r <= 128: 1024 threads of 4 x 4 tiles
 // (four waves per SIMD hide part of the pivot blocks' dependent latency).
-void launch_sweep(const float* G, double* Ginv, int32_t* status, int r, float eps, int64_t B, bool only_flagged,
-                  hipStream_t st) {
+void launch_sweep(const float* G, double* Ginv, float* Ginv32, int32_t* status, int32_t* prec, int r, float eps,
+                  int64_t B, bool only_flagged, hipStream_t st) {
   const int f = only_flagged ? 1 : 0;
   if (r <= 64)
-    hipLaunchKernelGGL((sweep_inverse_kernel<256, 4>), dim3((unsigned)B), dim3(256), 0, st, G, Ginv, status, r, eps, f);
+    hipLaunchKernelGGL((sweep_inverse_kernel<256, 4>), dim3((unsigned)B), dim3(256), 0, st, G, Ginv, Ginv32, status, prec,
+                       r, eps, f);
   else
-    hipLaunchKernelGGL((sweep_inverse_kernel<1024, 4>), dim3((unsigned)B), dim3(1024), 0, st, G, Ginv, status, r, eps,
-                       f);
+    hipLaunchKernelGGL((sweep_inverse_kernel<1024, 4>), dim3((unsigned)B), dim3(1024), 0, st, G, Ginv, Ginv32, status,
+                       prec, r, eps, f);
 }
 
 // The Cholesky route as its own launch (fp32 storage): one workgroup per
 // segment, the packed factor in LDS.
 template <int NT, int TB, int RMAX>
-__global__ __launch_bounds__(NT) void chol_inverse_kernel(const float* G, double* Ginv, int32_t* status, int r,
-                                                          float eps) {
+__global__ __launch_bounds__(NT) void chol_inverse_kernel(const float* G, double* Ginv, float* Ginv32,
+                                                          int32_t* status, int32_t* prec, int r, float eps) {
   __shared__ SweepLds sl;
   __shared__ double cp[RMAX * (RMAX + 1) / 2];
   const int64_t b = blockIdx.x;
-  const int st = chol_inverse<NT, TB>(G + b * r * r, Ginv + b * r * r, r, eps, sl, cp);
-  if (threadIdx.x == 0) status[b] = st;
+  double rho;
+  const int st = chol_inverse<NT, TB>(G + b * r * r, Ginv + b * r * r, Ginv32 + b * r * r, r, eps, sl, cp, rho);
+  if (threadIdx.x == 0) {
+    status[b] = st;
+    prec[b] = st == DYRA_SOLVE_OK && rho < kWidePivot ? 1 : 0;
+  }
 }
 
-void launch_chol(const float* G, double* Ginv, int32_t* status, int r, float eps, int64_t B, hipStream_t st) {
+void launch_chol(const float* G, double* Ginv, float* Ginv32, int32_t* status, int32_t* prec, int r, float eps,
+                 int64_t B, hipStream_t st) {
   if (r <= 64)
-    hipLaunchKernelGGL((chol_inverse_kernel<256, 4, 64>), dim3((unsigned)B), dim3(256), 0, st, G, Ginv, status, r,
-                       eps);
+    hipLaunchKernelGGL((chol_inverse_kernel<256, 4, 64>), dim3((unsigned)B), dim3(256), 0, st, G, Ginv, Ginv32, status,
+                       prec, r, eps);
   else   // 8 x 8 tiles: 256 threads, registers for both tiles without spills
-    hipLaunchKernelGGL((chol_inverse_kernel<256, 8, 128>), dim3((unsigned)B), dim3(256), 0, st, G, Ginv, status, r,
-                       eps);
+    hipLaunchKernelGGL((chol_inverse_kernel<256, 8, 128>), dim3((unsigned)B), dim3(256), 0, st, G, Ginv, Ginv32, status,
+                       prec, r, eps);
 }
 
 // ===========================================================================
@@ -2518,7 +2688,8 @@ constexpr int NS_N = 128;
 constexpr int NS_P = 129;   // padded LDS pitch (odd: row-strided reads spread over banks)
 
 __global__ __launch_bounds__(1024) void ns_polish_kernel(const float* G, const float* Xit, double* Ginv,
-                                                         int32_t* status, int r, float eps,
+                                                         float* Ginv32, int32_t* status, int32_t* prec, int r,
+                                                         float eps,
                                                          int maxit, float tol, float accept) {
   __shared__ float Xs[NS_N * NS_P];
   __shared__ float Ts[NS_N * NS_P];
@@ -2639,9 +2810,14 @@ __global__ __launch_bounds__(1024) void ns_polish_kernel(const float* G, const f
   const bool good = st == DYRA_SOLVE_OK;
   for (int e = tid; e < r * r; e += 1024) {
     const int i = e / r, j = e % r;
-    Ginv[b * r * r + e] = good ? (double)dsc[i] * (double)Xs[i * NS_P + j] * (double)dsc[j] : 0.0;
+    const double v = good ? (double)dsc[i] * (double)Xs[i * NS_P + j] * (double)dsc[j] : 0.0;
+    Ginv[b * r * r + e] = v;
+    Ginv32[b * r * r + e] = (float)v;
   }
-  if (tid == 0) status[b] = st;
+  if (tid == 0) {
+    status[b] = st;
+    prec[b] = 1;   // no pivots to judge the conditioning by: the fp64 apply
+  }
 }
 
 
@@ -2652,26 +2828,37 @@ __global__ __launch_bounds__(1024) void ns_polish_kernel(const float* G, const f
 // L_b is ill-conditioned.
 // ===========================================================================
 
-// One wave per (segment, RB 16-row blocks of M', 64-column tile), on
-// v_mfma_f32_16x16x4f32 with both operands read straight from memory.  The
-// reduction index is permuted so that each lane's operands are float4 runs:
-// in 16-wide chunk t, lane group g = lane / 16 holds q = 16 t + 4 g + e for
-// e = 0..3, and MFMA e of the chunk takes element e of the lane's Ginv run
-// (row 16 rb + lane % 16) and of its M runs (rows q, columns
-// c0 + 4 (lane % 16) .. + 3).  MFMA e of column block jb therefore sums
-// over q = 16 t + e, + 4, + 8, + 12 and writes column c0 + 4 (lane % 16) + jb;
-// the accumulator of lane (i, g) holds rows 16 rb + 4 g .. + 3 of those
-// columns.  The RB row blocks of a wave share its M loads.  With NTC > 0
+// One wave per (segment, RB 16-row blocks of M', 64-column tile), with both
+// operands read straight from memory.  The reduction index is permuted so
+// that each lane's operands are 4-element runs: in 16-wide chunk t, lane
+// group g = lane / 16 holds q = 16 t + 4 g + e for e = 0..3, and MFMA e of
+// the chunk takes element e of the lane's Ginv run (row 16 rb + lane % 16)
+// and of its M runs (rows q, columns c0 + 4 (lane % 16) .. + 3).  MFMA e of
+// column block jb therefore sums over q = 16 t + e, + 4, + 8, + 12 and
+// writes column c0 + 4 (lane % 16) + jb.
+//
+// Precision per segment (prec[b], set by the solve): a well-conditioned
+// G_b + lambda_b I runs on v_mfma_f32_16x16x4f32 with Ginv rounded to fp32
+// (its rounding and the fp32 sums stay far below the storage rounding of M');
+// a segment whose solve met a relative pivot below 2^-5 (near-singular:
+// fewer tokens than r, or nearly collinear columns of L_b) runs on
+// v_mfma_f64_16x16x4f64, since there Ginv has entries of order 1 / lambda_b
+// that cancel in Ginv M.  The fp32 path's RB row blocks share the wave's M
+// loads (accumulator of lane (i, g): rows 4 g .. + 3); the fp64 path takes
+// the RB blocks one at a time (its accumulator rows are interleaved: row
+// g + 4 v), which keeps its registers below the fp32 path's.  With NTC > 0
 // (r <= 16 NTC) every chunk is loaded before the first product, so a wave
 // waits on memory once; otherwise the next chunk is loaded before the
 // current one is multiplied.
 constexpr int AI_WAVES = 4;
 template <typename T, int RB, int NTC = 0>
 __global__ __launch_bounds__(64 * AI_WAVES) void apply_inverse_kernel(const double* __restrict__ Ginv,
+                                                                      const float* __restrict__ Ginv32,
                                                                       const float* __restrict__ M,
                                                                       T* __restrict__ Mp, int r, int64_t c1,
                                                                       int64_t tasks,
-                                                                      const int32_t* __restrict__ status) {
+                                                                      const int32_t* __restrict__ status,
+                                                                      const int32_t* __restrict__ prec) {
   const int lane = threadIdx.x & 63;
   const int64_t task = (int64_t)blockIdx.x * AI_WAVES + (threadIdx.x >> 6);
   if (task >= tasks) return;
@@ -2685,109 +2872,157 @@ __global__ __launch_bounds__(64 * AI_WAVES) void apply_inverse_kernel(const doub
   // meet a non-finite R_b
   const int sb = status[b];
   const bool solved = sb == DYRA_SOLVE_OK || sb == DYRA_SOLVE_FALLBACK;
+  const bool wide = solved && prec[b] != 0;
   const int i = lane & 15, g = lane >> 4;
   const double* Gb = Ginv + b * r * r;
+  const float* Gb32 = Ginv32 + b * r * r;
   const float* Mb = M + b * r * c1;
   const int64_t col = ct * 64 + 4 * i;          // c1 % 8 == 0: all four columns or none
   const bool cok = col < c1;
   const int nt = (r + 15) >> 4;
-  auto load = [&](int t, double4 (&a)[RB], float4 (&m)[4]) {
+  auto load_m = [&](int t, float4 (&m)[4]) {
     const int q0 = 16 * t + 4 * g;              // r % 4 == 0: all four q or none
-#pragma unroll
-    for (int j = 0; j < RB; ++j) {
-      const int row = (grp * RB + j) * 16 + i;
-      a[j] = (row < r && q0 < r) ? *reinterpret_cast<const double4*>(Gb + (int64_t)row * r + q0)
-                                 : make_double4(0.0, 0.0, 0.0, 0.0);
-    }
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       m[e] = (cok && q0 < r) ? *reinterpret_cast<const float4*>(Mb + (int64_t)(q0 + e) * c1 + col)
                              : make_float4(0.f, 0.f, 0.f, 0.f);
   };
-  f64x4 acc[RB][4];
+  auto load_g = [&](int t, int row) -> double4 {
+    const int q0 = 16 * t + 4 * g;
+    return (row < r && q0 < r) ? *reinterpret_cast<const double4*>(Gb + (int64_t)row * r + q0)
+                               : make_double4(0.0, 0.0, 0.0, 0.0);
+  };
+  auto store_row = [&](int orow, float v0, float v1, float v2, float v3) {
+    T* dst = Mp + (b * r + orow) * c1 + col;
+    if constexpr (TT<T>::ESZ == 2) {
+      uint2 pk;
+      pk.x = (uint32_t)f2bf(v0) | ((uint32_t)f2bf(v1) << 16);
+      pk.y = (uint32_t)f2bf(v2) | ((uint32_t)f2bf(v3) << 16);
+      *reinterpret_cast<uint2*>(dst) = pk;
+    } else {
+      *reinterpret_cast<float4*>(dst) = make_float4(v0, v1, v2, v3);
+    }
+  };
+  if (wide) {
+    // ---- fp64: one 16-row block and one of the lane's four columns at a
+    // time, loops kept rolled (this rare path must not raise the kernel's
+    // register count above the fp32 path's) ----
+#pragma unroll 1
+    for (int j = 0; j < RB; ++j) {
+      const int row = (grp * RB + j) * 16 + i;
+#pragma unroll 1
+      for (int jb = 0; jb < 4; ++jb) {
+        f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll 1
+        for (int t = 0; t < nt; ++t) {
+          const int q0 = 16 * t + 4 * g;
+          const double4 a = load_g(t, row);
+          const bool qok = cok && q0 < r;
+          const float* mp = Mb + (int64_t)q0 * c1 + col + jb;
+          const double m0 = qok ? mp[0] : 0.f, m1 = qok ? mp[c1] : 0.f, m2 = qok ? mp[2 * c1] : 0.f,
+                       m3 = qok ? mp[3 * c1] : 0.f;
+          acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a.x, m0, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a.y, m1, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a.z, m2, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a.w, m3, acc, 0, 0, 0);
+        }
+        if (cok) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int orow = (grp * RB + j) * 16 + g + 4 * v;
+            if (orow < r) {
+              T* dst = Mp + (b * r + orow) * c1 + col + jb;
+              if constexpr (TT<T>::ESZ == 2) *reinterpret_cast<uint16_t*>(dst) = f2bf((float)acc[v]);
+              else *dst = (float)acc[v];
+            }
+          }
+        }
+      }
+    }
+    return;
+  }
+  // ---- fp32 (zeros for an unsolved segment) ----
+  auto load = [&](int t, float4 (&a)[RB], float4 (&m)[4]) {
+#pragma unroll
+    for (int j = 0; j < RB; ++j) {
+      const int row = (grp * RB + j) * 16 + i, q0 = 16 * t + 4 * g;
+      a[j] = (row < r && q0 < r) ? *reinterpret_cast<const float4*>(Gb32 + (int64_t)row * r + q0)
+                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    load_m(t, m);
+  };
+  f32x4 acc[RB][4];
 #pragma unroll
   for (int j = 0; j < RB; ++j)
 #pragma unroll
-    for (int jb = 0; jb < 4; ++jb) acc[j][jb] = f64x4{0.0, 0.0, 0.0, 0.0};
-  auto mul = [&](const double4 (&a)[RB], const float4 (&m)[4]) {
+    for (int jb = 0; jb < 4; ++jb) acc[j][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto mul = [&](const float4 (&a)[RB], const float4 (&m)[4]) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const double mv[4] = {m[e].x, m[e].y, m[e].z, m[e].w};
+      const float mv[4] = {m[e].x, m[e].y, m[e].z, m[e].w};
 #pragma unroll
       for (int j = 0; j < RB; ++j) {
-        const double av = e == 0 ? a[j].x : e == 1 ? a[j].y : e == 2 ? a[j].z : a[j].w;
+        const float av = e == 0 ? a[j].x : e == 1 ? a[j].y : e == 2 ? a[j].z : a[j].w;
 #pragma unroll
-        for (int jb = 0; jb < 4; ++jb) acc[j][jb] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, mv[jb], acc[j][jb], 0, 0, 0);
+        for (int jb = 0; jb < 4; ++jb) acc[j][jb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, mv[jb], acc[j][jb], 0, 0, 0);
       }
     }
   };
   if (!solved) {
     // accumulators stay zero
   } else if constexpr (NTC > 0) {
-    double4 a[NTC][RB];
-    float4 m[NTC][4];                            // chunks past r load as zeros
+    float4 a[NTC][RB], m[NTC][4];                // chunks past r load as zeros
 #pragma unroll
     for (int t = 0; t < NTC; ++t) load(t, a[t], m[t]);
 #pragma unroll
     for (int t = 0; t < NTC; ++t) mul(a[t], m[t]);
   } else {
-  double4 a[RB];
-  float4 m[4];
-  load(0, a, m);
-  for (int t = 0; t < nt; ++t) {
-    double4 an[RB];
-    float4 mn[4];
-    if (t + 1 < nt) load(t + 1, an, mn);
-    mul(a, m);
-    if (t + 1 < nt) {
+    float4 a[RB], m[4];
+    load(0, a, m);
+    for (int t = 0; t < nt; ++t) {
+      float4 an[RB], mn[4];
+      if (t + 1 < nt) load(t + 1, an, mn);
+      mul(a, m);
+      if (t + 1 < nt) {
 #pragma unroll
-      for (int j = 0; j < RB; ++j) a[j] = an[j];
+        for (int j = 0; j < RB; ++j) a[j] = an[j];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) m[e] = mn[e];
+        for (int e = 0; e < 4; ++e) m[e] = mn[e];
+      }
     }
-  }
   }
   if (!cok) return;
 #pragma unroll
   for (int j = 0; j < RB; ++j)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      // v_mfma_f64_16x16x4f64 interleaves its accumulator rows: element v
-      // of lane (i, g) is row g + 4 v, column i
-      const int orow = (grp * RB + j) * 16 + g + 4 * v;
-      if (orow >= r) continue;
-      T* dst = Mp + (b * r + orow) * c1 + col;
-      if constexpr (TT<T>::ESZ == 2) {
-        uint2 pk;
-        pk.x = (uint32_t)f2bf((float)acc[j][0][v]) | ((uint32_t)f2bf((float)acc[j][1][v]) << 16);
-        pk.y = (uint32_t)f2bf((float)acc[j][2][v]) | ((uint32_t)f2bf((float)acc[j][3][v]) << 16);
-        *reinterpret_cast<uint2*>(dst) = pk;
-      } else {
-        *reinterpret_cast<float4*>(dst) = make_float4((float)acc[j][0][v], (float)acc[j][1][v],
-                                                      (float)acc[j][2][v], (float)acc[j][3][v]);
-      }
+      const int orow = (grp * RB + j) * 16 + 4 * g + v;
+      if (orow < r) store_row(orow, acc[j][0][v], acc[j][1][v], acc[j][2][v], acc[j][3][v]);
     }
 }
 
 // M'_b = Ginv_b M_b for B segments of r x c1: four row blocks per wave when
 // that still leaves at least two waves per SIMD of a 256-CU chip, else one.
 template <typename T>
-void launch_apply_inverse(const double* Gi, const float* M, T* Mp, int64_t B, int r, int64_t c1, const int32_t* stat,
-                          hipStream_t st) {
+void launch_apply_inverse(const double* Gi, const float* Gi32, const float* M, T* Mp, int64_t B, int r, int64_t c1,
+                          const int32_t* stat, const int32_t* prec, hipStream_t st) {
   const int64_t tiles = (c1 + 63) / 64, nrb = (r + 15) / 16;
   const int64_t wide = B * tiles * ((nrb + 3) / 4);
   if (nrb >= 4 && wide >= 2048) {
     hipLaunchKernelGGL((apply_inverse_kernel<T, 4>), dim3((unsigned)((wide + AI_WAVES - 1) / AI_WAVES)),
-                       dim3(64 * AI_WAVES), 0, st, Gi, M, Mp, r, c1, wide, stat);
+                       dim3(64 * AI_WAVES), 0, st, Gi, Gi32, M, Mp, r, c1, wide, stat, prec);
   } else {
     const int64_t tasks = B * tiles * nrb;
     const dim3 grid((unsigned)((tasks + AI_WAVES - 1) / AI_WAVES)), block(64 * AI_WAVES);
     if (r <= 32)
-      hipLaunchKernelGGL((apply_inverse_kernel<T, 1, 2>), grid, block, 0, st, Gi, M, Mp, r, c1, tasks, stat);
+      hipLaunchKernelGGL((apply_inverse_kernel<T, 1, 2>), grid, block, 0, st, Gi, Gi32, M, Mp, r, c1, tasks, stat,
+                         prec);
     else if (r <= 64)
-      hipLaunchKernelGGL((apply_inverse_kernel<T, 1, 4>), grid, block, 0, st, Gi, M, Mp, r, c1, tasks, stat);
+      hipLaunchKernelGGL((apply_inverse_kernel<T, 1, 4>), grid, block, 0, st, Gi, Gi32, M, Mp, r, c1, tasks, stat,
+                         prec);
     else
-      hipLaunchKernelGGL((apply_inverse_kernel<T, 1>), grid, block, 0, st, Gi, M, Mp, r, c1, tasks, stat);
+      hipLaunchKernelGGL((apply_inverse_kernel<T, 1>), grid, block, 0, st, Gi, Gi32, M, Mp, r, c1, tasks, stat,
+                         prec);
   }
 }
 
@@ -2901,7 +3136,9 @@ struct StageEvents {
 
 template <int NRB, int NB>
 void launch_s3_bf16(const bf16_t* Lt, int64_t ldt, const bf16_t* X, int64_t c1, int r, SegMap sg, int64_t n,
-                    int64_t B, float* M, float* G, double* Gi, int32_t* stat, float eps, int solve_mode,
+                    int64_t B, float* M, float* G, double* Gi, float* Gi32, int32_t* stat, int32_t* prec,
+                    float eps,
+                    int solve_mode,
                     hipStream_t st, int64_t lt_seg_rows = 0, bool x_rel = false, float* gpart = nullptr,
                     int gchunks = 0, int64_t gchunk = 0, int64_t gprows = 0) {
   const int strips = (int)cdiv(c1, S3_STRIP);
@@ -2910,7 +3147,8 @@ void launch_s3_bf16(const bf16_t* Lt, int64_t ldt, const bf16_t* X, int64_t c1, 
                        sg, n, gchunks, gchunk, gpart);
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, dim3((unsigned)(B + B * strips)), dim3(S3_NT), 0, st, Lt, ldt, X, c1, r, sg, n, B, M,
-                       G, Gi, stat, eps, strips, lt_seg_rows, x_rel ? 1 : 0, gpart, gchunks, gprows);
+                       G, Gi, Gi32, stat, prec, eps, strips, lt_seg_rows, x_rel ? 1 : 0, gpart, gchunks,
+                       gprows);
   };
   if (solve_mode == 2) go(s3_reduce_solve_kernel<NRB, NB, 2>);
   else if (solve_mode == 1) go(s3_reduce_solve_kernel<NRB, NB, 1>);
@@ -2937,10 +3175,12 @@ void forward_residual(const dyra_spec& s, const char* plan, const void* X, const
   float* G = reinterpret_cast<float*>(ws + WL.G);
   float* M = reinterpret_cast<float*>(ws + WL.M);
   double* Gi = reinterpret_cast<double*>(ws + WL.Ginv);
+  float* Gi32 = reinterpret_cast<float*>(ws + WL.Gi32);
   float* Xit = reinterpret_cast<float*>(ws + WL.Xit);
   T* Mp = reinterpret_cast<T*>(ws + WL.Mp);
   T* Rt = reinterpret_cast<T*>(ws + WL.Rt);
   int32_t* stat = reinterpret_cast<int32_t*>(ws + WL.status);
+  int32_t* prec = reinterpret_cast<int32_t*>(ws + WL.prec);
   const int64_t ldt = lt_pitch(n);
   // AUTO takes the sweep at every supported r: on MI355X the fp64 sweep on one
   // workgroup beats Newton-Schulz (split-precision phase plus fp32 polish),
@@ -2958,10 +3198,10 @@ void forward_residual(const dyra_spec& s, const char* plan, const void* X, const
     float* Gp = reinterpret_cast<float*>(ws + WL.Gp);
     const int gc = (int)WL.gchunks;
     const int64_t gk = WL.gchunk;
-    if (r <= 16) launch_s3_bf16<1, 1>(Lt, ldt, Xb, c1, r, sg, n, B, M, G, Gi, stat, eps, mode, st, 0, false, Gp, gc, gk, gram_rows);
-    else if (r <= 32) launch_s3_bf16<2, 1>(Lt, ldt, Xb, c1, r, sg, n, B, M, G, Gi, stat, eps, mode, st, 0, false, Gp, gc, gk, gram_rows);
-    else if (r <= 64) launch_s3_bf16<4, 2>(Lt, ldt, Xb, c1, r, sg, n, B, M, G, Gi, stat, eps, mode, st, 0, false, Gp, gc, gk, gram_rows);
-    else launch_s3_bf16<8, 4>(Lt, ldt, Xb, c1, r, sg, n, B, M, G, Gi, stat, eps, mode, st, 0, false, Gp, gc, gk, gram_rows);
+    if (r <= 16) launch_s3_bf16<1, 1>(Lt, ldt, Xb, c1, r, sg, n, B, M, G, Gi, Gi32, stat, prec, eps, mode, st, 0, false, Gp, gc, gk, gram_rows);
+    else if (r <= 32) launch_s3_bf16<2, 1>(Lt, ldt, Xb, c1, r, sg, n, B, M, G, Gi, Gi32, stat, prec, eps, mode, st, 0, false, Gp, gc, gk, gram_rows);
+    else if (r <= 64) launch_s3_bf16<4, 2>(Lt, ldt, Xb, c1, r, sg, n, B, M, G, Gi, Gi32, stat, prec, eps, mode, st, 0, false, Gp, gc, gk, gram_rows);
+    else launch_s3_bf16<8, 4>(Lt, ldt, Xb, c1, r, sg, n, B, M, G, Gi, Gi32, stat, prec, eps, mode, st, 0, false, Gp, gc, gk, gram_rows);
     solved = !ns;
   } else {
     const int tr = (int)cdiv(r, C3::BM), tcm = (int)cdiv(c1, C3::BN), tcg = (int)cdiv(r, C3::BN);
@@ -2981,16 +3221,18 @@ void forward_residual(const dyra_spec& s, const char* plan, const void* X, const
       // ill-conditioned G still gives an fp32-accurate inverse)
       const float tol = BF ? 1e-4f : 2e-6f, accept = BF ? 1e-2f : 1e-5f;
       hipLaunchKernelGGL(ns_inverse_kernel, dim3((unsigned)B), dim3(512), 0, st, G, Xit, stat, r, eps, 40, tol);
-      hipLaunchKernelGGL(ns_polish_kernel, dim3((unsigned)B), dim3(1024), 0, st, G, Xit, Gi, stat, r, eps, 60, tol,
+      hipLaunchKernelGGL(ns_polish_kernel, dim3((unsigned)B), dim3(1024), 0, st, G, Xit, Gi, Gi32, stat, prec, r, eps,
+                         60,
+                         tol,
                          accept);
-      launch_sweep(G, Gi, stat, r, eps, B, true, st);
+      launch_sweep(G, Gi, Gi32, stat, prec, r, eps, B, true, st);
     } else if (solver == DYRA_SOLVER_CHOL) {
-      launch_chol(G, Gi, stat, r, eps, B, st);
+      launch_chol(G, Gi, Gi32, stat, prec, r, eps, B, st);
     } else {
-      launch_sweep(G, Gi, stat, r, eps, B, false, st);
+      launch_sweep(G, Gi, Gi32, stat, prec, r, eps, B, false, st);
     }
   }
-  launch_apply_inverse<T>(Gi, M, Mp, B, r, c1, stat, st);
+  launch_apply_inverse<T>(Gi, Gi32, M, Mp, B, r, c1, stat, prec, st);
   E.mark(3, st);
   // S5: R^T (c2 x B r) = W_res^T (c2 x c1) . M' (B r x c1)^T; bf16: split
   // over K when the output has few tiles, else the persistent output kernel
@@ -3033,20 +3275,22 @@ void left_step_bf16(const dyra_spec& s, const char* plan, const bf16_t* X, int64
   bf16_t* R = reinterpret_cast<bf16_t*>(ws + WL.R);
   float* K = reinterpret_cast<float*>(ws + WL.K);
   double* Kinv = reinterpret_cast<double*>(ws + WL.Kinv);
+  float* Ki32 = reinterpret_cast<float*>(ws + WL.Ki32);
   float* Qt = reinterpret_cast<float*>(ws + WL.Qt);
   bf16_t* Zt = reinterpret_cast<bf16_t*>(ws + WL.Zt);
   int32_t* kst = reinterpret_cast<int32_t*>(ws + WL.kstatus);
+  int32_t* kpr = reinterpret_cast<int32_t*>(ws + WL.kprec);
   const bf16_t* Wrt = reinterpret_cast<const bf16_t*>(plan + PL.Wrt);
   // R [B r x c2] = (R^T [c2 x B r])^T
   hipLaunchKernelGGL(transpose_b16_kernel, dim3((unsigned)(cdiv(c2, 64) * cdiv(B * r, 64))), dim3(256), 0, st, Rt, R,
                      c2, B * r);
   // K_b, Q_b^T, (K_b + lambda I)^-1: c2 is the reduction ("token") axis
   const int64_t nn = B * c2;
-  if (r <= 16) launch_s3_bf16<1, 1>(R, c2, Wrt, c1, r, SegMap{nullptr, c2, B, nn}, nn, B, Qt, K, Kinv, kst, eps, 1, st, r, true);
-  else if (r <= 32) launch_s3_bf16<2, 1>(R, c2, Wrt, c1, r, SegMap{nullptr, c2, B, nn}, nn, B, Qt, K, Kinv, kst, eps, 1, st, r, true);
-  else if (r <= 64) launch_s3_bf16<4, 2>(R, c2, Wrt, c1, r, SegMap{nullptr, c2, B, nn}, nn, B, Qt, K, Kinv, kst, eps, 1, st, r, true);
-  else launch_s3_bf16<8, 4>(R, c2, Wrt, c1, r, SegMap{nullptr, c2, B, nn}, nn, B, Qt, K, Kinv, kst, eps, 1, st, r, true);
-  launch_apply_inverse<bf16_t>(Kinv, Qt, Zt, B, r, c1, kst, st);
+  if (r <= 16) launch_s3_bf16<1, 1>(R, c2, Wrt, c1, r, SegMap{nullptr, c2, B, nn}, nn, B, Qt, K, Kinv, Ki32, kst, kpr, eps, 1, st, r, true);
+  else if (r <= 32) launch_s3_bf16<2, 1>(R, c2, Wrt, c1, r, SegMap{nullptr, c2, B, nn}, nn, B, Qt, K, Kinv, Ki32, kst, kpr, eps, 1, st, r, true);
+  else if (r <= 64) launch_s3_bf16<4, 2>(R, c2, Wrt, c1, r, SegMap{nullptr, c2, B, nn}, nn, B, Qt, K, Kinv, Ki32, kst, kpr, eps, 1, st, r, true);
+  else launch_s3_bf16<8, 4>(R, c2, Wrt, c1, r, SegMap{nullptr, c2, B, nn}, nn, B, Qt, K, Kinv, Ki32, kst, kpr, eps, 1, st, r, true);
+  launch_apply_inverse<bf16_t>(Kinv, Ki32, Qt, Zt, B, r, c1, kst, kpr, st);
   // L_b = X_b Z_b into [T | L] and L^T
   const int tiles_n = (int)cdiv(r, CfgL::BN);
   hipLaunchKernelGGL(s1_left_kernel<CfgL>, dim3((unsigned)(cdiv(n, CfgL::BM) * tiles_n)), dim3(CfgL::NT), 0, st, X,
@@ -3124,19 +3368,33 @@ int forward_lowrank(const dyra_spec& s, const char* plan, const void* X, const v
   return hipGetLastError() == hipSuccess ? DYRA_OK : DYRA_EHIP;
 }
 
+// The one-pass output (V recomputed from X) is the default; the two-pass
+// form (V stored by the first stage) stays for comparison.
+constexpr bool kMonarchOnePass = true;
+
 template <int RB>
 void launch_monarch(const bf16_t* X, const char* plan, const PlanLayout& PL, bf16_t* A, bf16_t* Lt, int64_t n,
                     int r, int64_t ldt, hipStream_t st) {
-  hipLaunchKernelGGL((s1_monarch_kernel<RB>), dim3((unsigned)cdiv(n, 32)), dim3(256), 0, st, X,
-                     reinterpret_cast<const bf16_t*>(plan + PL.B1t), reinterpret_cast<const bf16_t*>(plan + PL.Pt),
-                     A, Lt, n, r, ldt);
+  const bf16_t* B1t = reinterpret_cast<const bf16_t*>(plan + PL.B1t);
+  const bf16_t* Pt = reinterpret_cast<const bf16_t*>(plan + PL.Pt);
+  if (kMonarchOnePass)
+    hipLaunchKernelGGL((s1_monarch_kernel<RB, false>), dim3((unsigned)cdiv(n, 32)), dim3(256), 0, st, X, B1t, Pt, A,
+                       Lt, n, r, ldt);
+  else
+    hipLaunchKernelGGL((s1_monarch_kernel<RB, true>), dim3((unsigned)cdiv(n, 32)), dim3(256), 0, st, X, B1t, Pt, A,
+                       Lt, n, r, ldt);
 }
 
 template <int RB>
-void launch_monarch6(const bf16_t* A, const char* plan, const PlanLayout& PL, const bf16_t* Rt, const bf16_t* bias,
-                     bf16_t* Y, int64_t n, int r, SegMap sg, int64_t B, hipStream_t st) {
-  hipLaunchKernelGGL((s6_monarch_kernel<RB>), dim3((unsigned)(cdiv(n, 128) * (MO * MO / 128))), dim3(256), 0, st,
-                     A, reinterpret_cast<const bf16_t*>(plan + PL.B2t), Rt, bias, Y, n, r, sg, B);
+void launch_monarch6(const bf16_t* X, const bf16_t* A, const char* plan, const PlanLayout& PL, const bf16_t* Rt,
+                     const bf16_t* bias, bf16_t* Y, int64_t n, int r, SegMap sg, int64_t B, hipStream_t st) {
+  if (kMonarchOnePass)
+    hipLaunchKernelGGL(s6_monarch_fused_kernel, dim3((unsigned)cdiv(n, 32)), dim3(256), 0, st, X,
+                       reinterpret_cast<const bf16_t*>(plan + PL.B1t), reinterpret_cast<const bf16_t*>(plan + PL.B2t),
+                       A, Rt, bias, Y, n, r, sg, B);
+  else
+    hipLaunchKernelGGL((s6_monarch_kernel<RB>), dim3((unsigned)(cdiv(n, 128) * (MO * MO / 128))), dim3(256), 0, st,
+                       A, reinterpret_cast<const bf16_t*>(plan + PL.B2t), Rt, bias, Y, n, r, sg, B);
 }
 
 int forward_monarch(const dyra_spec& s, const char* plan, const void* X, const void* bias, void* Y,
@@ -3159,9 +3417,9 @@ int forward_monarch(const dyra_spec& s, const char* plan, const void* X, const v
   const bf16_t* Rt = reinterpret_cast<const bf16_t*>(ws + WL.Rt);
   const bf16_t* bb = reinterpret_cast<const bf16_t*>(bias);
   bf16_t* Yb = reinterpret_cast<bf16_t*>(Y);
-  if (r <= 32) launch_monarch6<1>(A, plan, PL, Rt, bb, Yb, n, r, si.map(), B, st);
-  else if (r <= 64) launch_monarch6<2>(A, plan, PL, Rt, bb, Yb, n, r, si.map(), B, st);
-  else launch_monarch6<4>(A, plan, PL, Rt, bb, Yb, n, r, si.map(), B, st);
+  if (r <= 32) launch_monarch6<1>(Xb, A, plan, PL, Rt, bb, Yb, n, r, si.map(), B, st);
+  else if (r <= 64) launch_monarch6<2>(Xb, A, plan, PL, Rt, bb, Yb, n, r, si.map(), B, st);
+  else launch_monarch6<4>(Xb, A, plan, PL, Rt, bb, Yb, n, r, si.map(), B, st);
   E.mark(5, st);
   return hipGetLastError() == hipSuccess ? DYRA_OK : DYRA_EHIP;
 }

@@ -451,5 +451,6 @@ extern "C" int dyra_workspace_offsets(const dyra_spec* spec, int64_t B, int64_t 
   out->total = (int64_t)W.total;
   out->wa = W.wa;
   out->lt_pitch = (B * s + 255) / 256 * 256;
+  out->prec = (int64_t)W.prec;
   return DYRA_OK;
 }

@@ -160,6 +160,8 @@ inline S5Split s5_split(int64_t c2, int64_t nr, int64_t K) {
 // Ginv [B x r x r] fp64        (G_b + lambda_b I)^-1 (fp64: near-singular G_b
 //                              put 1 / lambda_b-sized entries in it that
 //                              cancel in Ginv M; fp32 rounding would not)
+// Gi32 [B x r x r] fp32        the same inverse rounded to fp32 (read by the
+//                              fp32 apply of well-conditioned segments)
 // Xit  [B x r x r] fp32        Newton-Schulz iterate handed to its polish
 // Mp   [B x r x c1] dtype      M'_b = Ginv_b M_b
 // Rt   [c2 x B r] dtype        R_b^T for every segment, R_b = M'_b W_res
@@ -169,6 +171,8 @@ inline S5Split s5_split(int64_t c2, int64_t nr, int64_t K) {
 struct WsLayout {
   int64_t wa = 0;
   size_t A = 0, Wp = 0, Lt = 0, G = 0, M = 0, Ginv = 0, Mp = 0, Rt = 0, status = 0, Pk = 0, Xit = 0;
+  // per-segment precision of M' = Ginv M (0 fp32, 1 fp64), set by the solve
+  size_t prec = 0, kprec = 0, Gi32 = 0, Ki32 = 0;
   // Gram partials [B][gchunks][r x r] fp32 over token chunks of gchunk tokens
   size_t Gp = 0;
   int64_t gchunk = 0, gchunks = 0;
@@ -202,10 +206,12 @@ inline WsLayout ws_layout_n(const dyra_spec& s, int64_t B, int64_t n_rows, int64
   W.G = take((size_t)B * r * r * 4);
   W.M = take((size_t)B * r * c1 * 4);
   W.Ginv = take((size_t)B * r * r * 8);
+  W.Gi32 = take((size_t)B * r * r * 4);
   W.Xit = take((size_t)B * r * r * 4);
   W.Mp = take((size_t)B * r * c1 * e);
   W.Rt = take(c2 * (size_t)B * r * e);
   W.status = take((size_t)B * 4);
+  W.prec = take((size_t)B * 4);
   W.gchunk = s.r > 64 ? 256 : 128;
   W.gchunks = (seg + W.gchunk - 1) / W.gchunk;
   // token-chunk partials, or two per 160-token first-stage tile
@@ -224,9 +230,11 @@ inline WsLayout ws_layout_n(const dyra_spec& s, int64_t B, int64_t n_rows, int64
     W.R = take((size_t)B * r * c2 * e);
     W.K = take((size_t)B * r * r * 4);
     W.Kinv = take((size_t)B * r * r * 8);
+    W.Ki32 = take((size_t)B * r * r * 4);
     W.Qt = take((size_t)B * r * c1 * 4);
     W.Zt = take((size_t)B * r * c1 * e);
     W.kstatus = take((size_t)B * 4);
+    W.kprec = take((size_t)B * 4);
   }
   W.total = off;
   return W;

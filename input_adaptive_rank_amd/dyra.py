@@ -50,7 +50,7 @@ _FACTORS = ("U", "V", "B1", "B2", "Ub", "S", "Vb", "P", "R0", "Wres", "res_sv")
 
 class WsOffsets(ctypes.Structure):
     _fields_ = [(f, ctypes.c_int64) for f in ("A", "Wp", "Lt", "G", "M", "Ginv", "Mp", "Rt", "status", "total",
-                                                "wa", "lt_pitch")]
+                                                "wa", "lt_pitch", "prec")]
 
 
 class Sizes(ctypes.Structure):

@@ -25,7 +25,20 @@ CASES = [
        solver="chol"),
     sc(W["vitb_fc1"], name="stage_fp32", B=3, s=77, c1=192, c2=200, k=24, r=16, dtype=synth.DT_F32),
     sc(W["vitl_fc1"], name="stage_k256_r64", B=3, s=150, c1=384, c2=384, k=256, r=64),
+    # fewer tokens than r: G_b is singular but for the ridge, the solve's
+    # smallest relative pivot is ~eps and M' is formed in fp64
+    sc(W["vitl_fc1"], name="stage_short_fp64", B=3, s=40, c1=256, c2=512, k=64, r=64),
+    sc(W["vitl_fc1"], name="stage_short_fp64_chol", B=3, s=40, c1=256, c2=512, k=64, r=64, solver="chol"),
 ]
+
+WIDE_PIVOT = 2.0 ** -5     # relative pivot below which the library applies Ginv in fp64
+
+
+def _min_relative_pivot(A):
+    """Smallest d_j / A_jj over the pivots d_j of the unpivoted LDL^T of the
+    SPD matrix A (= C_jj^2 for its Cholesky factor C)."""
+    C = np.linalg.cholesky(A)
+    return float(np.min(np.diag(C) ** 2 / np.diag(A)))
 
 
 def _rel(a, b):
@@ -82,7 +95,9 @@ def test_stages(w):
     Mp = _read(ws, o["Mp"], (B, r, c1), sd)
     Rt = _read(ws, o["Rt"], (c2, B * r), sd)
     st = _read(ws, o["status"], (B,), "i32")
+    prec = _read(ws, o["prec"], (B,), "i32")
     e3g = e3m = e4 = e4b = e5 = 0.0
+    rhos = []
     for b in range(B):
         Lb, Xb = L[b * s:(b + 1) * s], inp.X[b * s:(b + 1) * s]
         e3g = max(e3g, _rel(G[b], Lb.T @ Lb))
@@ -90,11 +105,24 @@ def test_stages(w):
         lam = 1e-6 * np.trace(G[b]) / r
         Ainv = np.linalg.inv(G[b] + lam * np.eye(r))
         e4 = max(e4, _rel(Gi[b], Ainv))
-        # storage rounding plus the fp64 forward-error bound of length-r dot
-        # products (the product runs on fp64 MFMAs)
+        rho = _min_relative_pivot(G[b].astype(np.float64) + lam * np.eye(r))
+        rhos.append(rho)
+        # the precision flag follows the smallest relative pivot (Newton-Schulz
+        # has no pivots and always takes fp64); near the threshold either is
+        # allowed
+        if w.solver == "ns":
+            assert prec[b] == 1
+        elif rho < WIDE_PIVOT / 2:
+            assert prec[b] == 1, (b, rho)
+        elif rho > WIDE_PIVOT * 2:
+            assert prec[b] == 0, (b, rho)
+        # storage rounding plus the forward-error bound of length-r dot
+        # products: fp64 MFMAs on the fp64 inverse, or fp32 MFMAs on the
+        # inverse rounded to fp32 (one more rounding of each term)
         ref4 = Gi[b] @ M[b]
+        acc_u = 2.0 ** -52 if prec[b] else 2.0 ** -24
         bound = (2.0 ** -8 if w.dtype == synth.DT_BF16 else 2.0 ** -23) * np.abs(ref4) + \
-            r * 2.0 ** -52 * (np.abs(Gi[b]) @ np.abs(M[b]))
+            (r + 1) * acc_u * (np.abs(Gi[b]) @ np.abs(M[b]))
         ratio = np.abs(Mp[b] - ref4) / (bound + 1e-30)
         if float(np.max(ratio)) > e4b:
             i, j = np.unravel_index(np.argmax(ratio), ratio.shape)
@@ -114,7 +142,8 @@ def test_stages(w):
     if e4b > 0:
         log(f"  worst M' element (b, i, j, gpu, ref, |Ginv||M|, max |dM'| / |Ginv||M|): {worst4}")
     log(f"  {w.name}: S1 {e1:.2e} S3(G) {e3g:.2e} S3(M) {e3m:.2e} S4(Ginv) {e4:.2e} S4(M') {e4b:.2e} "
-        f"(bound ratio) S5 {e5:.2e} S6 {e6:.2e} cond(G) max {max(conds):.1e} status {st.tolist()}")
+        f"(bound ratio) S5 {e5:.2e} S6 {e6:.2e} cond(G) max {max(conds):.1e} status {st.tolist()} "
+        f"min relative pivot {min(rhos):.1e} prec {prec.tolist()}")
     assert e1 <= tol_store
     assert e3g <= 1e-5 and e3m <= 1e-5
     assert e4 <= 1e-6 * max(conds) + 1e-5
