@@ -245,9 +245,10 @@ int dyra_forward(const dyra_spec* spec, const void* plan, const void* X, const v
  * dyra_forward (t = 1: L from the precomputed thin matrix, then R); 3 is
  * t = 1.5 (then L again, L_b = X_b (W_res R_b^T)(R_b R_b^T + lambda I)^-1,
  * lambda = ridge_eps * trace(R_b R_b^T) / r, solved by the sweep); 4 is
- * t = 2 (then R again from the new L).  Y uses the last L and R.  Low-rank
- * structure and bf16 only: EINVAL for another structure or half_steps
- * outside 2..4, EDTYPE for fp32.  The workspace must hold
+ * t = 2 (then R again from the new L).  Y uses the last L and R.  Every
+ * structure (the left step does not involve the static branch), bf16 only,
+ * uniform segments: EINVAL for half_steps outside 2..4, EDTYPE for fp32.
+ * The workspace must hold
  * dyra_workspace_size_als bytes for the same half_steps; otherwise the
  * arguments, ownership and errors are those of dyra_forward.
  * Source: nanless.github.io DyRA digest, "what the low-rank objective of the

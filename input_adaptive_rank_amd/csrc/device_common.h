@@ -22,9 +22,17 @@ __device__ __forceinline__ bf16_t f2bf(float f) { return __builtin_bit_cast(bf16
 struct SegMap {
   const int32_t* off;
   int64_t seg, B, n;
-  __device__ __forceinline__ int64_t lo(int64_t b) const { return off ? (int64_t)off[b] : b * seg; }
+  // The offsets are read through the constant address space: with a
+  // wave-uniform index that is a scalar load, counted by lgkmcnt, so a wave
+  // that looks up a segment never waits for its own outstanding vector
+  // stores (vmcnt); they are never written while a kernel runs.
+  __device__ __forceinline__ int64_t at(int64_t i) const {
+    return (int64_t)reinterpret_cast<const __attribute__((address_space(4))) int32_t*>(
+        reinterpret_cast<uintptr_t>(off))[i];
+  }
+  __device__ __forceinline__ int64_t lo(int64_t b) const { return off ? at(b) : b * seg; }
   __device__ __forceinline__ int64_t hi(int64_t b) const {
-    return off ? (int64_t)off[b + 1] : ((b + 1) * seg < n ? (b + 1) * seg : n);
+    return off ? at(b + 1) : ((b + 1) * seg < n ? (b + 1) * seg : n);
   }
   // the segment holding `row` (0 <= row < n)
   __device__ __forceinline__ int64_t of(int64_t row) const {
@@ -32,7 +40,7 @@ struct SegMap {
     int64_t a = 0, z = B;   // off[a] <= row < off[z]
     while (z - a > 1) {
       const int64_t mid = (a + z) >> 1;
-      if ((int64_t)off[mid] <= row) a = mid;
+      if (at(mid) <= row) a = mid;
       else z = mid;
     }
     return a;

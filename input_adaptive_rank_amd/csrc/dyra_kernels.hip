@@ -917,34 +917,28 @@ __global__ __launch_bounds__(C::NT) void s1_left_kernel(const bf16_t* X, const b
 // Monarch static branch (m = 32 blocks of 32 x 32, c = 1024), bf16.
 // W_hat = blockdiag(B1_a) . Pi . blockdiag(B2_j), Pi the reshape(32, 32)
 // transpose: u_a = x_a B1_a, v[j*32 + a] = u[a*32 + j], y_j = v_j B2_j.
-// The block products are tiny: both kernels are bound by the vector-memory
-// address path and by streaming X, V and Y, so weights come in fragment order
-// or through LDS and V and Y leave as whole rows.
+// The block products are tiny: both kernels are bound by streaming X and Y
+// and by load latency, so X is loaded for a whole row block at once, weights
+// come in fragment order a few products ahead, and Y leaves as whole rows.
 // ===========================================================================
 
 constexpr int MO = 32;
 
-// Stage 1 + L: one pass over X.  A workgroup owns 32 rows; wave w takes the
-// 8 blocks a = 8w .. 8w + 7 and accumulates its K slice (a*32 .. a*32 + 31
-// for its 8 blocks) of L = X P.  With WITH_V it also accumulates U_a
-// (32 x 32 each) and puts the permuted V[row][j*32 + 8w .. 8w + 7] into an
-// LDS copy of the 32 V rows, written out as whole rows (the two-pass Monarch
-// output); without it only L is formed and the output kernel recomputes V
-// from X.  B1t and Pt are in fragment order: a wave's operand of one MFMA
-// step is one contiguous 1 KB run.  The four partial L sums are added
-// through LDS in a fixed order; wave 0 writes L and L^T.
-constexpr int S1M_VP = MO * MO * 2 + 16;                  // V row pitch in LDS (bytes)
-template <int RB, bool WITH_V>
+// First stage (L only): one pass over X.  A workgroup owns 32 rows; wave w
+// takes the 8 blocks a = 8w .. 8w + 7 and accumulates its K slice
+// (a*32 .. a*32 + 31 for its 8 blocks) of L = X P; the output kernel
+// recomputes the Monarch stage 1 from X, so V is never stored.  Pt is in
+// fragment order: a wave's operand of one MFMA step is one contiguous 1 KB
+// run.  The four partial L sums are added through LDS in a fixed order;
+// wave 0 writes L and L^T.
+constexpr int S1M_VP = MO * MO * 2 + 16;                  // V row pitch in LDS (bytes), output kernel
+template <int RB>
 __global__ __launch_bounds__(256, 2) void s1_monarch_kernel(const bf16_t* __restrict__ X,
-                                                         const bf16_t* __restrict__ B1t,
                                                          const bf16_t* __restrict__ Pt,
                                                          bf16_t* __restrict__ A, bf16_t* __restrict__ Lt,
                                                          int64_t n, int r, int64_t ldt) {
   constexpr int C = MO * MO;
-  constexpr int PART = 3 * RB * 16 * 64 * 4;
-  constexpr int SMB = WITH_V ? (32 * S1M_VP > PART ? 32 * S1M_VP : PART) : PART;
-  __shared__ __attribute__((aligned(16))) char sm[SMB];
-  float* part = reinterpret_cast<float*>(sm);             // [3][RB][16][64], after V is written out
+  __shared__ __attribute__((aligned(16))) float part[3 * RB * 16 * 64];   // waves 1..3's partial L
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int l = lane & 31, g = lane >> 5;
   const int64_t row = (int64_t)blockIdx.x * 32 + l;
@@ -955,53 +949,26 @@ __global__ __launch_bounds__(256, 2) void s1_monarch_kernel(const bf16_t* __rest
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int v = 0; v < 16; ++v) lacc[rb][v] = 0.f;
-  f32x16 uacc[WITH_V ? 8 : 1];
+  // the 16 X loads first (rows past n read row n - 1, zeroed below): one wait on HBM
+  const int64_t rowc = rok ? row : n - 1;
+  uint4 xr[8][2];
 #pragma unroll
-  for (int ai = 0; ai < 8; ++ai) {
-    if constexpr (WITH_V) {
+  for (int ai = 0; ai < 8; ++ai)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) uacc[ai][v] = 0.f;
-    }
-    const int a = w * 8 + ai;
+    for (int s = 0; s < 2; ++s)
+      xr[ai][s] = *reinterpret_cast<const uint4*>(X + rowc * C + (w * 8 + ai) * MO + 16 * s + 8 * g);
+  // Pt fragments (L2-resident, fragment order); Pt holds whole 32-row groups
+  // (rows past r zero), so its test is wave-uniform
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int kk = a * MO + 16 * s + 8 * g;
-      const uint4 xa = rok ? *reinterpret_cast<const uint4*>(X + row * C + kk) : zero4();
-      if constexpr (WITH_V) {
-        const uint4 b1 = *reinterpret_cast<const uint4*>(B1t + ((a * 2 + s) * 64 + lane) * 8);
-        TT<bf16_t>::mma(uacc[ai], b1, xa);
-      }
+  for (int q = 0; q < 16; ++q) {
+    const int a = w * 8 + (q >> 1), s = q & 1;
+    const uint4 xa = rok ? xr[q >> 1][s] : zero4();
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const int p = rb * 32 + l;
-        const uint4 pb =
-            p < r ? *reinterpret_cast<const uint4*>(Pt + ((int64_t)((rb * MO + a) * 2 + s) * 64 + lane) * 8) : zero4();
+    for (int rb = 0; rb < RB; ++rb)
+      if (rb * 32 < r) {
+        const uint4 pb = *reinterpret_cast<const uint4*>(Pt + ((int64_t)((rb * MO + a) * 2 + s) * 64 + lane) * 8);
         TT<bf16_t>::mma(lacc[rb], pb, xa);
       }
-    }
-  }
-  if constexpr (WITH_V) {
-    // lane holds U[row][a*32 + j] for j = 8q + 4g + e (reg 4q + e), a = 8w + ai
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = 8 * q + 4 * g + e;
-        uint32_t pk[4];
-#pragma unroll
-        for (int h = 0; h < 4; ++h)
-          pk[h] = (uint32_t)f2bf(uacc[2 * h][4 * q + e]) | ((uint32_t)f2bf(uacc[2 * h + 1][4 * q + e]) << 16);
-        *reinterpret_cast<uint4*>(sm + l * S1M_VP + (j * MO + w * 8) * 2) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-      }
-    __syncthreads();
-    // the 32 V rows: 128 runs of 16 bytes each, a wave instruction 1 KB of one row
-    for (int c = threadIdx.x; c < 32 * (C / 8); c += 256) {
-      const int rl = c / (C / 8), ch = c % (C / 8);
-      const int64_t vr = (int64_t)blockIdx.x * 32 + rl;
-      if (vr < n)
-        *reinterpret_cast<uint4*>(A + vr * lda + ch * 8) = *reinterpret_cast<const uint4*>(sm + rl * S1M_VP + ch * 16);
-    }
-    __syncthreads();
   }
   // L partials: waves 1..3 -> LDS, wave 0 adds them in order
   if (w > 0) {
@@ -1032,113 +999,6 @@ __global__ __launch_bounds__(256, 2) void s1_monarch_kernel(const bf16_t* __rest
 #pragma unroll
       for (int e = 0; e < 4; ++e) Lt[(int64_t)(p0 + e) * ldt + row] = f2bf(v[e]);
     }
-}
-
-// Stage 2 fused with the residual correction and bias: a workgroup computes
-// 128 rows x 128 output columns (4 blocks j), a wave 32 rows of them:
-// y_j = V_j B2_j + L R_b[:, j] + bias.  The workgroup's B2_j blocks and, one
-// segment at a time, its 128 columns of R_b^T are copied into LDS as whole
-// rows (a 16-byte-per-lane load then covers eight 128-byte lines instead of
-// one 32-byte piece of 32 rows), and the output tile is staged in LDS so that
-// each store writes four whole 256-byte row segments.  Row pitches of
-// 80 bytes (B2) and 2 r + 16 bytes (R^T) keep the 32-row fragment reads free
-// of bank conflicts.
-constexpr int S6M_B2P = MO * 2 + 16, S6M_YP = 128 * 2 + 16;
-constexpr int S6M_RT_OFF = 4 * MO * S6M_B2P;                       // after the B2 blocks
-constexpr int S6M_LDS = S6M_RT_OFF + 128 * (128 * 2 + 16);        // r <= 128
-static_assert(128 * S6M_YP <= S6M_LDS, "output staging fits");
-template <int RB>
-__global__ __launch_bounds__(256) void s6_monarch_kernel(const bf16_t* __restrict__ A,
-                                                         const bf16_t* __restrict__ B2t,
-                                                         const bf16_t* __restrict__ Rt,
-                                                         const bf16_t* __restrict__ bias, bf16_t* __restrict__ Y,
-                                                         int64_t n, int r, SegMap sg, int64_t B) {
-  constexpr int C = MO * MO;
-  __shared__ __attribute__((aligned(16))) char sm[S6M_LDS];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int l = lane & 31, g = lane >> 5;
-  const int tiles_n = C / 128;
-  const int64_t mw = (int64_t)(blockIdx.x / tiles_n) * 128;        // the workgroup's first row
-  const int64_t m0 = mw + w * 32;
-  const int j0 = (blockIdx.x % tiles_n) * 4;
-  const int64_t row = m0 + l;
-  const bool rok = row < n;
-  const int64_t lda = C + r;
-  const int RP = r * 2 + 16;                                       // R^T row pitch in LDS
-  // B2t rows (j, l) for j = j0 .. j0 + 3: one contiguous 8 KB run
-  for (int q = tid; q < 4 * MO * (MO / 8); q += 256) {
-    const int rr = q / (MO / 8), u = q % (MO / 8);
-    *reinterpret_cast<uint4*>(sm + rr * S6M_B2P + u * 16) =
-        *reinterpret_cast<const uint4*>(B2t + ((int64_t)j0 * MO + rr) * MO + u * 8);
-  }
-  __syncthreads();
-  f32x16 acc[4];
-#pragma unroll
-  for (int jb = 0; jb < 4; ++jb)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) acc[jb][v] = 0.f;
-  // V_j B2_j (K = 32: two 16-wide k steps)
-#pragma unroll
-  for (int jb = 0; jb < 4; ++jb) {
-    const int j = j0 + jb;
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const uint4 va = rok ? *reinterpret_cast<const uint4*>(A + row * lda + j * MO + 16 * s + 8 * g) : zero4();
-      const uint4 b2 = *reinterpret_cast<const uint4*>(sm + (jb * MO + l) * S6M_B2P + (16 * s + 8 * g) * 2);
-      TT<bf16_t>::mma(acc[jb], b2, va);
-    }
-  }
-  // L R_b for every segment overlapping the workgroup's 128 rows
-  const int64_t wend = imin64(mw + 128, n);
-  const int64_t bf = sg.of(mw), bl = imin64(B - 1, sg.of(wend - 1));
-  const int ru = r / 8;                                            // 16-byte runs per R^T row
-  for (int64_t b = bf; b <= bl; ++b) {
-    __syncthreads();                                               // the previous R^T block is read
-    for (int q = tid; q < 128 * ru; q += 256) {
-      const int c = q / ru, u = q - c * ru;
-      *reinterpret_cast<uint4*>(sm + S6M_RT_OFF + c * RP + u * 16) =
-          *reinterpret_cast<const uint4*>(Rt + ((int64_t)j0 * MO + c) * (B * r) + b * r + u * 8);
-    }
-    __syncthreads();
-    const int64_t blo = sg.lo(b), bhi = sg.hi(b);
-    if (m0 >= wend || m0 + 32 <= blo || m0 >= bhi) continue;   // wave-uniform
-    const bool in = rok && row >= blo && row < bhi;
-    for (int k0 = 0; k0 < r; k0 += 16) {
-      const int kk = k0 + 8 * g;
-      const uint4 la = (in && kk < r) ? *reinterpret_cast<const uint4*>(A + row * lda + C + kk) : zero4();
-#pragma unroll
-      for (int jb = 0; jb < 4; ++jb) {
-        const uint4 rt = kk < r ? *reinterpret_cast<const uint4*>(sm + S6M_RT_OFF + (jb * MO + l) * RP + kk * 2)
-                                : zero4();
-        TT<bf16_t>::mma(acc[jb], rt, la);
-      }
-    }
-  }
-  __syncthreads();                                                 // LDS free for the output tile
-  // accumulator (jb) element 4 q + e: row l, column 32 jb + 8 q + 4 g + e
-#pragma unroll
-  for (int jb = 0; jb < 4; ++jb)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int cl = jb * MO + 8 * q + 4 * g;
-      float v[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = acc[jb][4 * q + e] + (bias ? bf2f(bias[j0 * MO + cl + e]) : 0.f);
-      uint2 pk;
-      pk.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
-      pk.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
-      *reinterpret_cast<uint2*>(sm + (w * 32 + l) * S6M_YP + cl * 2) = pk;
-    }
-  __syncthreads();
-  // this wave's 32 rows: 16 lanes per 256-byte row segment, 4 rows per store
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int rl = i * 4 + (lane >> 4), ch = lane & 15;
-    const int64_t yr = m0 + rl;
-    if (yr < n)
-      *reinterpret_cast<uint4*>(Y + yr * C + j0 * MO + ch * 8) =
-          *reinterpret_cast<const uint4*>(sm + (w * 32 + rl) * S6M_YP + ch * 16);
-  }
 }
 
 // One-pass Monarch output: a workgroup owns 32 rows and all 1024 output
@@ -1174,18 +1034,31 @@ __global__ __launch_bounds__(256, 2) void s6_monarch_fused_kernel(const bf16_t* 
   const int64_t lda = C + r;
   f32x16 acc[8];
   // ---- phase 1: U_a for the wave's 8 blocks, permuted into LDS ----
+  // All 16 X loads are issued before the first product (rows past n read
+  // row n - 1 and are zeroed afterwards), so a wave waits on HBM once.
+  const int64_t rowc = rok ? row : n - 1;
+  uint4 xa[8][2];
 #pragma unroll
-  for (int ai = 0; ai < 8; ++ai) {
+  for (int ai = 0; ai < 8; ++ai)
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      xa[ai][s] = *reinterpret_cast<const uint4*>(X + rowc * C + (w * 8 + ai) * MO + 16 * s + 8 * g);
+  // B1t fragments (L2-resident) stream four products ahead of the MFMAs
+  auto ld_b1 = [&](int q) {   // q = 2 ai + s
+    return *reinterpret_cast<const uint4*>(B1t + (((w * 8 + (q >> 1)) * 2 + (q & 1)) * 64 + lane) * 8);
+  };
+  uint4 bq[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) bq[q] = ld_b1(q);
+#pragma unroll
+  for (int ai = 0; ai < 8; ++ai)
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[ai][v] = 0.f;
-    const int a = w * 8 + ai;
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int kk = a * MO + 16 * s + 8 * g;
-      const uint4 xa = rok ? *reinterpret_cast<const uint4*>(X + row * C + kk) : zero4();
-      const uint4 b1 = *reinterpret_cast<const uint4*>(B1t + ((a * 2 + s) * 64 + lane) * 8);
-      TT<bf16_t>::mma(acc[ai], b1, xa);
-    }
+  for (int q = 0; q < 16; ++q) {
+    const uint4 cur = bq[q & 3];
+    if (q + 4 < 16) bq[q & 3] = ld_b1(q + 4);
+    TT<bf16_t>::mma(acc[q >> 1], cur, rok ? xa[q >> 1][q & 1] : zero4());
   }
   // lane holds U[row][a*32 + j] for j = 8q + 4g + e (reg 4q + e), a = 8w + ai
 #pragma unroll
@@ -1200,7 +1073,14 @@ __global__ __launch_bounds__(256, 2) void s6_monarch_fused_kernel(const bf16_t* 
       *reinterpret_cast<uint4*>(sm + l * S1M_VP + (j * MO + w * 8) * 2) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
     }
   __syncthreads();
-  // ---- phase 2: y_j = V_j B2_j (K = 32: two 16-wide k steps) ----
+  // ---- phase 2: y_j = V_j B2_j (K = 32: two 16-wide k steps); the B2t
+  // loads of all 8 blocks are issued first ----
+  uint4 b2[8][2];
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj)
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      b2[jj][s] = *reinterpret_cast<const uint4*>(B2t + ((int64_t)((w * 8 + jj) * MO + l) * MO + 16 * s + 8 * g));
 #pragma unroll
   for (int jj = 0; jj < 8; ++jj) {
 #pragma unroll
@@ -1209,8 +1089,7 @@ __global__ __launch_bounds__(256, 2) void s6_monarch_fused_kernel(const bf16_t* 
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const uint4 va = *reinterpret_cast<const uint4*>(sm + l * S1M_VP + (j * MO + 16 * s + 8 * g) * 2);
-      const uint4 b2 = *reinterpret_cast<const uint4*>(B2t + ((int64_t)(j * MO + l) * MO + 16 * s + 8 * g));
-      TT<bf16_t>::mma(acc[jj], b2, va);
+      TT<bf16_t>::mma(acc[jj], b2[jj][s], va);
     }
   }
   // + L R_b for every segment meeting the 32 rows
@@ -1220,15 +1099,20 @@ __global__ __launch_bounds__(256, 2) void s6_monarch_fused_kernel(const bf16_t* 
   for (int64_t b = bf; b <= bl; ++b) {
     const int64_t blo = sg.lo(b), bhi = sg.hi(b);
     const bool in = rok && row >= blo && row < bhi;
+    // r % 16 == 0 (r a multiple of 8 split over the two lane halves is not
+    // enough: a k step past r reads a clamped column and is zeroed)
     for (int k0 = 0; k0 < r; k0 += 16) {
       const int kk = k0 + 8 * g;
-      const uint4 la = (in && kk < r) ? *reinterpret_cast<const uint4*>(A + row * lda + C + kk) : zero4();
+      const bool kok = kk < r;
+      const int kc = kok ? kk : 0;
+      uint4 rt[8];
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const int c = (w * 8 + jj) * MO + l;
-        const uint4 rt = kk < r ? *reinterpret_cast<const uint4*>(Rt + (int64_t)c * ldr + b * r + kk) : zero4();
-        TT<bf16_t>::mma(acc[jj], rt, la);
-      }
+      for (int jj = 0; jj < 8; ++jj)
+        rt[jj] = *reinterpret_cast<const uint4*>(Rt + (int64_t)((w * 8 + jj) * MO + l) * ldr + b * r + kc);
+      uint4 la = *reinterpret_cast<const uint4*>(A + rowc * lda + C + kc);
+      if (!(in && kok)) la = zero4();
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) TT<bf16_t>::mma(acc[jj], kok ? rt[jj] : zero4(), la);
     }
   }
   // ---- stage the wave's 32 x 256 output slice over its own V slice ----
@@ -2838,22 +2722,19 @@ __global__ __launch_bounds__(1024) void ns_polish_kernel(const float* G, const f
 // writes column c0 + 4 (lane % 16) + jb.
 //
 // Precision per segment (prec[b], set by the solve): a well-conditioned
-// G_b + lambda_b I runs on v_mfma_f32_16x16x4f32 with Ginv rounded to fp32
-// (its rounding and the fp32 sums stay far below the storage rounding of M');
-// a segment whose solve met a relative pivot below 2^-5 (near-singular:
-// fewer tokens than r, or nearly collinear columns of L_b) runs on
-// v_mfma_f64_16x16x4f64, since there Ginv has entries of order 1 / lambda_b
-// that cancel in Ginv M.  The fp32 path's RB row blocks share the wave's M
-// loads (accumulator of lane (i, g): rows 4 g .. + 3); the fp64 path takes
-// the RB blocks one at a time (its accumulator rows are interleaved: row
-// g + 4 v), which keeps its registers below the fp32 path's.  With NTC > 0
-// (r <= 16 NTC) every chunk is loaded before the first product, so a wave
-// waits on memory once; otherwise the next chunk is loaded before the
-// current one is multiplied.
+// G_b + lambda_b I runs here, on v_mfma_f32_16x16x4f32 with the fp32 copy
+// of Ginv (its rounding and the fp32 sums stay far below the storage
+// rounding of M'); a segment whose solve met a relative pivot below 2^-5
+// (near-singular: fewer tokens than r, or nearly collinear columns of L_b)
+// is left to apply_inverse_f64_kernel, since there Ginv has entries of
+// order 1 / lambda_b that cancel in Ginv M.  The RB row blocks share the
+// wave's M loads (accumulator of lane (i, g): rows 4 g .. + 3).  With
+// NTC > 0 (r <= 16 NTC) every chunk is loaded before the first product, so
+// a wave waits on memory once; otherwise the next chunk is loaded before
+// the current one is multiplied.
 constexpr int AI_WAVES = 4;
 template <typename T, int RB, int NTC = 0>
-__global__ __launch_bounds__(64 * AI_WAVES) void apply_inverse_kernel(const double* __restrict__ Ginv,
-                                                                      const float* __restrict__ Ginv32,
+__global__ __launch_bounds__(64 * AI_WAVES) void apply_inverse_kernel(const float* __restrict__ Ginv32,
                                                                       const float* __restrict__ M,
                                                                       T* __restrict__ Mp, int r, int64_t c1,
                                                                       int64_t tasks,
@@ -2874,7 +2755,6 @@ __global__ __launch_bounds__(64 * AI_WAVES) void apply_inverse_kernel(const doub
   const bool solved = sb == DYRA_SOLVE_OK || sb == DYRA_SOLVE_FALLBACK;
   const bool wide = solved && prec[b] != 0;
   const int i = lane & 15, g = lane >> 4;
-  const double* Gb = Ginv + b * r * r;
   const float* Gb32 = Ginv32 + b * r * r;
   const float* Mb = M + b * r * c1;
   const int64_t col = ct * 64 + 4 * i;          // c1 % 8 == 0: all four columns or none
@@ -2887,11 +2767,6 @@ __global__ __launch_bounds__(64 * AI_WAVES) void apply_inverse_kernel(const doub
       m[e] = (cok && q0 < r) ? *reinterpret_cast<const float4*>(Mb + (int64_t)(q0 + e) * c1 + col)
                              : make_float4(0.f, 0.f, 0.f, 0.f);
   };
-  auto load_g = [&](int t, int row) -> double4 {
-    const int q0 = 16 * t + 4 * g;
-    return (row < r && q0 < r) ? *reinterpret_cast<const double4*>(Gb + (int64_t)row * r + q0)
-                               : make_double4(0.0, 0.0, 0.0, 0.0);
-  };
   auto store_row = [&](int orow, float v0, float v1, float v2, float v3) {
     T* dst = Mp + (b * r + orow) * c1 + col;
     if constexpr (TT<T>::ESZ == 2) {
@@ -2903,44 +2778,7 @@ __global__ __launch_bounds__(64 * AI_WAVES) void apply_inverse_kernel(const doub
       *reinterpret_cast<float4*>(dst) = make_float4(v0, v1, v2, v3);
     }
   };
-  if (wide) {
-    // ---- fp64: one 16-row block and one of the lane's four columns at a
-    // time, loops kept rolled (this rare path must not raise the kernel's
-    // register count above the fp32 path's) ----
-#pragma unroll 1
-    for (int j = 0; j < RB; ++j) {
-      const int row = (grp * RB + j) * 16 + i;
-#pragma unroll 1
-      for (int jb = 0; jb < 4; ++jb) {
-        f64x4 acc = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll 1
-        for (int t = 0; t < nt; ++t) {
-          const int q0 = 16 * t + 4 * g;
-          const double4 a = load_g(t, row);
-          const bool qok = cok && q0 < r;
-          const float* mp = Mb + (int64_t)q0 * c1 + col + jb;
-          const double m0 = qok ? mp[0] : 0.f, m1 = qok ? mp[c1] : 0.f, m2 = qok ? mp[2 * c1] : 0.f,
-                       m3 = qok ? mp[3 * c1] : 0.f;
-          acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a.x, m0, acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a.y, m1, acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a.z, m2, acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a.w, m3, acc, 0, 0, 0);
-        }
-        if (cok) {
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int orow = (grp * RB + j) * 16 + g + 4 * v;
-            if (orow < r) {
-              T* dst = Mp + (b * r + orow) * c1 + col + jb;
-              if constexpr (TT<T>::ESZ == 2) *reinterpret_cast<uint16_t*>(dst) = f2bf((float)acc[v]);
-              else *dst = (float)acc[v];
-            }
-          }
-        }
-      }
-    }
-    return;
-  }
+  if (wide) return;                           // apply_inverse_f64_kernel's segment
   // ---- fp32 (zeros for an unsolved segment) ----
   auto load = [&](int t, float4 (&a)[RB], float4 (&m)[4]) {
 #pragma unroll
@@ -3001,6 +2839,74 @@ __global__ __launch_bounds__(64 * AI_WAVES) void apply_inverse_kernel(const doub
     }
 }
 
+// M'_b = Ginv_b M_b in fp64 for the segments the solve flagged (prec[b] = 1;
+// every other wave returns at once): one wave per (segment, 16-row block,
+// 64-column tile), the same reduction-index permutation as the fp32 kernel,
+// on v_mfma_f64_16x16x4f64 (operands one double per lane, k = lane / 16;
+// accumulator rows interleaved: element v of lane (i, g) is row g + 4 v).
+__global__ __launch_bounds__(64 * AI_WAVES) void apply_inverse_f64_kernel(const double* __restrict__ Ginv,
+                                                                          const float* __restrict__ M,
+                                                                          bf16_t* __restrict__ Mp16,
+                                                                          float* __restrict__ Mp32, int r,
+                                                                          int64_t c1, int64_t tasks,
+                                                                          const int32_t* __restrict__ status,
+                                                                          const int32_t* __restrict__ prec) {
+  const int lane = threadIdx.x & 63;
+  const int64_t task = (int64_t)blockIdx.x * AI_WAVES + (threadIdx.x >> 6);
+  if (task >= tasks) return;
+  const int nrb = (r + 15) >> 4;
+  const int64_t tiles = (c1 + 63) >> 6;
+  const int rb = (int)(task % nrb);
+  const int64_t ct = (task / nrb) % tiles, b = task / (nrb * tiles);
+  const int sb = status[b];
+  if (!((sb == DYRA_SOLVE_OK || sb == DYRA_SOLVE_FALLBACK) && prec[b] != 0)) return;
+  const int i = lane & 15, g = lane >> 4;
+  const double* Gb = Ginv + b * r * r;
+  const float* Mb = M + b * r * c1;
+  const int64_t col = ct * 64 + 4 * i;          // c1 % 8 == 0: all four columns or none
+  const bool cok = col < c1;
+  const int row = rb * 16 + i;
+  const int nt = (r + 15) >> 4;
+  f64x4 acc[4];
+#pragma unroll
+  for (int jb = 0; jb < 4; ++jb) acc[jb] = f64x4{0.0, 0.0, 0.0, 0.0};
+  for (int t = 0; t < nt; ++t) {
+    const int q0 = 16 * t + 4 * g;              // r % 4 == 0: all four q or none
+    const bool qok = q0 < r;
+    const double4 a = (row < r && qok) ? *reinterpret_cast<const double4*>(Gb + (int64_t)row * r + q0)
+                                       : make_double4(0.0, 0.0, 0.0, 0.0);
+    float4 m[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      m[e] = (cok && qok) ? *reinterpret_cast<const float4*>(Mb + (int64_t)(q0 + e) * c1 + col)
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const double av = e == 0 ? a.x : e == 1 ? a.y : e == 2 ? a.z : a.w;
+      acc[0] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, (double)m[e].x, acc[0], 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, (double)m[e].y, acc[1], 0, 0, 0);
+      acc[2] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, (double)m[e].z, acc[2], 0, 0, 0);
+      acc[3] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, (double)m[e].w, acc[3], 0, 0, 0);
+    }
+  }
+  if (!cok) return;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int orow = rb * 16 + g + 4 * v;
+    if (orow >= r) continue;
+    const int64_t o = (b * r + orow) * c1 + col;
+    if (Mp16) {
+      uint2 pk;
+      pk.x = (uint32_t)f2bf((float)acc[0][v]) | ((uint32_t)f2bf((float)acc[1][v]) << 16);
+      pk.y = (uint32_t)f2bf((float)acc[2][v]) | ((uint32_t)f2bf((float)acc[3][v]) << 16);
+      *reinterpret_cast<uint2*>(Mp16 + o) = pk;
+    } else {
+      *reinterpret_cast<float4*>(Mp32 + o) =
+          make_float4((float)acc[0][v], (float)acc[1][v], (float)acc[2][v], (float)acc[3][v]);
+    }
+  }
+}
+
 // M'_b = Ginv_b M_b for B segments of r x c1: four row blocks per wave when
 // that still leaves at least two waves per SIMD of a 256-CU chip, else one.
 template <typename T>
@@ -3010,20 +2916,26 @@ void launch_apply_inverse(const double* Gi, const float* Gi32, const float* M, T
   const int64_t wide = B * tiles * ((nrb + 3) / 4);
   if (nrb >= 4 && wide >= 2048) {
     hipLaunchKernelGGL((apply_inverse_kernel<T, 4>), dim3((unsigned)((wide + AI_WAVES - 1) / AI_WAVES)),
-                       dim3(64 * AI_WAVES), 0, st, Gi, Gi32, M, Mp, r, c1, wide, stat, prec);
+                       dim3(64 * AI_WAVES), 0, st, Gi32, M, Mp, r, c1, wide, stat, prec);
   } else {
     const int64_t tasks = B * tiles * nrb;
     const dim3 grid((unsigned)((tasks + AI_WAVES - 1) / AI_WAVES)), block(64 * AI_WAVES);
     if (r <= 32)
-      hipLaunchKernelGGL((apply_inverse_kernel<T, 1, 2>), grid, block, 0, st, Gi, Gi32, M, Mp, r, c1, tasks, stat,
-                         prec);
+      hipLaunchKernelGGL((apply_inverse_kernel<T, 1, 2>), grid, block, 0, st, Gi32, M, Mp, r, c1, tasks, stat, prec);
     else if (r <= 64)
-      hipLaunchKernelGGL((apply_inverse_kernel<T, 1, 4>), grid, block, 0, st, Gi, Gi32, M, Mp, r, c1, tasks, stat,
-                         prec);
+      hipLaunchKernelGGL((apply_inverse_kernel<T, 1, 4>), grid, block, 0, st, Gi32, M, Mp, r, c1, tasks, stat, prec);
     else
-      hipLaunchKernelGGL((apply_inverse_kernel<T, 1>), grid, block, 0, st, Gi, Gi32, M, Mp, r, c1, tasks, stat,
-                         prec);
+      hipLaunchKernelGGL((apply_inverse_kernel<T, 1>), grid, block, 0, st, Gi32, M, Mp, r, c1, tasks, stat, prec);
   }
+  // the flagged segments in fp64 (a second launch: its registers do not
+  // lower the fp32 kernel's occupancy)
+  const int64_t t64 = B * tiles * nrb;
+  bf16_t* m16 = nullptr;
+  float* m32 = nullptr;
+  if constexpr (TT<T>::ESZ == 2) m16 = reinterpret_cast<bf16_t*>(Mp);
+  else m32 = reinterpret_cast<float*>(Mp);
+  hipLaunchKernelGGL(apply_inverse_f64_kernel, dim3((unsigned)((t64 + AI_WAVES - 1) / AI_WAVES)), dim3(64 * AI_WAVES),
+                     0, st, Gi, M, m16, m32, r, c1, t64, stat, prec);
 }
 
 // ===========================================================================
@@ -3264,13 +3176,16 @@ typedef GemmCfg<bf16_t, 128, 64, 2, 2> CfgL;   // left ALS step: L_b = X_b Z_b (
 
 // One left ALS half-step on the bf16 workspace: R^T -> R; K_b = R_b R_b^T and
 // Q_b^T = R_b W_res^T (fp32) with (K_b + lambda_b I)^-1 by the sweep; Z_b^T;
-// then L_b = X_b Z_b overwrites L (and L^T) in the workspace.
+// then L_b = X_b Z_b overwrites L (and L^T) in the workspace.  The step does
+// not involve the static branch: only where L sits in the first-stage output
+// depends on the structure (column lcol of rows of pitch ldo: k / k + r
+// low-rank, c / c + r Monarch, nb rb / nb rb + r BLAST).
 void left_step_bf16(const dyra_spec& s, const char* plan, const bf16_t* X, int64_t B, int64_t seg, float eps,
-                    char* ws, hipStream_t st, int half_steps) {
+                    char* ws, hipStream_t st, int half_steps, int lcol, int64_t ldo) {
   const PlanLayout PL = plan_layout(s, DYRA_BF16);
   const WsLayout WL = ws_layout(s, B, seg, DYRA_BF16, half_steps);
   const int64_t n = B * seg, c1 = s.c1, c2 = s.c2;
-  const int k = s.k, r = s.r;
+  const int r = s.r;
   const bf16_t* Rt = reinterpret_cast<const bf16_t*>(ws + WL.Rt);
   bf16_t* R = reinterpret_cast<bf16_t*>(ws + WL.R);
   float* K = reinterpret_cast<float*>(ws + WL.K);
@@ -3294,8 +3209,8 @@ void left_step_bf16(const dyra_spec& s, const char* plan, const bf16_t* X, int64
   // L_b = X_b Z_b into [T | L] and L^T
   const int tiles_n = (int)cdiv(r, CfgL::BN);
   hipLaunchKernelGGL(s1_left_kernel<CfgL>, dim3((unsigned)(cdiv(n, CfgL::BM) * tiles_n)), dim3(CfgL::NT), 0, st, X,
-                     Zt, reinterpret_cast<bf16_t*>(ws + WL.A), reinterpret_cast<bf16_t*>(ws + WL.Lt), n, c1, k, r,
-                     seg, B, lt_pitch(n), tiles_n, (int64_t)(k + r));
+                     Zt, reinterpret_cast<bf16_t*>(ws + WL.A), reinterpret_cast<bf16_t*>(ws + WL.Lt), n, c1, lcol, r,
+                     seg, B, lt_pitch(n), tiles_n, ldo);
 }
 
 template <class C, class C3, class C6>
@@ -3346,7 +3261,9 @@ int forward_lowrank(const dyra_spec& s, const char* plan, const void* X, const v
   // further ALS half-steps: left (L from R), right (R from L), ...
   if constexpr (TT<T>::ESZ == 2) {
     for (int h = 2; h < half_steps; ++h) {
-      if (h % 2 == 0) left_step_bf16(s, plan, reinterpret_cast<const bf16_t*>(X), B, seg, eps, ws, st, half_steps);
+      if (h % 2 == 0)
+        left_step_bf16(s, plan, reinterpret_cast<const bf16_t*>(X), B, seg, eps, ws, st, half_steps, k,
+                       (int64_t)(k + r));
       else forward_residual<C, C3>(s, plan, X, si, eps, solver, ws, st, StageEvents{nullptr, 0});
     }
   }
@@ -3368,37 +3285,23 @@ int forward_lowrank(const dyra_spec& s, const char* plan, const void* X, const v
   return hipGetLastError() == hipSuccess ? DYRA_OK : DYRA_EHIP;
 }
 
-// The one-pass output (V recomputed from X) is the default; the two-pass
-// form (V stored by the first stage) stays for comparison.
-constexpr bool kMonarchOnePass = true;
-
 template <int RB>
 void launch_monarch(const bf16_t* X, const char* plan, const PlanLayout& PL, bf16_t* A, bf16_t* Lt, int64_t n,
                     int r, int64_t ldt, hipStream_t st) {
-  const bf16_t* B1t = reinterpret_cast<const bf16_t*>(plan + PL.B1t);
-  const bf16_t* Pt = reinterpret_cast<const bf16_t*>(plan + PL.Pt);
-  if (kMonarchOnePass)
-    hipLaunchKernelGGL((s1_monarch_kernel<RB, false>), dim3((unsigned)cdiv(n, 32)), dim3(256), 0, st, X, B1t, Pt, A,
-                       Lt, n, r, ldt);
-  else
-    hipLaunchKernelGGL((s1_monarch_kernel<RB, true>), dim3((unsigned)cdiv(n, 32)), dim3(256), 0, st, X, B1t, Pt, A,
-                       Lt, n, r, ldt);
+  hipLaunchKernelGGL((s1_monarch_kernel<RB>), dim3((unsigned)cdiv(n, 32)), dim3(256), 0, st, X,
+                     reinterpret_cast<const bf16_t*>(plan + PL.Pt), A, Lt, n, r, ldt);
 }
 
-template <int RB>
 void launch_monarch6(const bf16_t* X, const bf16_t* A, const char* plan, const PlanLayout& PL, const bf16_t* Rt,
                      const bf16_t* bias, bf16_t* Y, int64_t n, int r, SegMap sg, int64_t B, hipStream_t st) {
-  if (kMonarchOnePass)
-    hipLaunchKernelGGL(s6_monarch_fused_kernel, dim3((unsigned)cdiv(n, 32)), dim3(256), 0, st, X,
-                       reinterpret_cast<const bf16_t*>(plan + PL.B1t), reinterpret_cast<const bf16_t*>(plan + PL.B2t),
-                       A, Rt, bias, Y, n, r, sg, B);
-  else
-    hipLaunchKernelGGL((s6_monarch_kernel<RB>), dim3((unsigned)(cdiv(n, 128) * (MO * MO / 128))), dim3(256), 0, st,
-                       A, reinterpret_cast<const bf16_t*>(plan + PL.B2t), Rt, bias, Y, n, r, sg, B);
+  hipLaunchKernelGGL(s6_monarch_fused_kernel, dim3((unsigned)cdiv(n, 32)), dim3(256), 0, st, X,
+                     reinterpret_cast<const bf16_t*>(plan + PL.B1t), reinterpret_cast<const bf16_t*>(plan + PL.B2t), A,
+                     Rt, bias, Y, n, r, sg, B);
 }
 
 int forward_monarch(const dyra_spec& s, const char* plan, const void* X, const void* bias, void* Y,
-                    const SegInfo& si, float eps, int solver, char* ws, hipStream_t st, const StageEvents& E) {
+                    const SegInfo& si, float eps, int solver, char* ws, hipStream_t st, const StageEvents& E,
+                    int half_steps = 2) {
   const PlanLayout PL = plan_layout(s, DYRA_BF16);
   const WsLayout WL = si.layout(s, DYRA_BF16);
   const int64_t B = si.B, n = si.n;
@@ -3413,19 +3316,22 @@ int forward_monarch(const dyra_spec& s, const char* plan, const void* X, const v
   else launch_monarch<4>(Xb, plan, PL, A, Lt, n, r, ldt, st);
   E.mark(1, st);
   forward_residual<CfgB, CfgB3>(s, plan, X, si, eps, solver, ws, st, E);
+  for (int h = 2; h < half_steps; ++h) {   // further ALS half-steps (L sits after the C = m^2 V columns)
+    if (h % 2 == 0) left_step_bf16(s, plan, Xb, B, si.seg, eps, ws, st, half_steps, MO * MO, MO * MO + r);
+    else forward_residual<CfgB, CfgB3>(s, plan, X, si, eps, solver, ws, st, StageEvents{nullptr, 0});
+  }
   E.mark(4, st);
   const bf16_t* Rt = reinterpret_cast<const bf16_t*>(ws + WL.Rt);
   const bf16_t* bb = reinterpret_cast<const bf16_t*>(bias);
   bf16_t* Yb = reinterpret_cast<bf16_t*>(Y);
-  if (r <= 32) launch_monarch6<1>(Xb, A, plan, PL, Rt, bb, Yb, n, r, si.map(), B, st);
-  else if (r <= 64) launch_monarch6<2>(Xb, A, plan, PL, Rt, bb, Yb, n, r, si.map(), B, st);
-  else launch_monarch6<4>(Xb, A, plan, PL, Rt, bb, Yb, n, r, si.map(), B, st);
+  launch_monarch6(Xb, A, plan, PL, Rt, bb, Yb, n, r, si.map(), B, st);
   E.mark(5, st);
   return hipGetLastError() == hipSuccess ? DYRA_OK : DYRA_EHIP;
 }
 
 int forward_blast(const dyra_spec& s, const char* plan, const void* X, const void* bias, void* Y,
-                  const SegInfo& si, float eps, int solver, char* ws, hipStream_t st, const StageEvents& E) {
+                  const SegInfo& si, float eps, int solver, char* ws, hipStream_t st, const StageEvents& E,
+                  int half_steps = 2) {
   const PlanLayout PL = plan_layout(s, DYRA_BF16);
   const WsLayout WL = si.layout(s, DYRA_BF16);
   const int64_t B = si.B, n = si.n, c1 = s.c1, c2 = s.c2;
@@ -3458,6 +3364,10 @@ int forward_blast(const dyra_spec& s, const char* plan, const void* X, const voi
   }
   E.mark(1, st);
   forward_residual<CfgB, CfgB3>(s, plan, X, si, eps, solver, ws, st, E);
+  for (int h = 2; h < half_steps; ++h) {   // further ALS half-steps (L sits after the nb rb Z columns)
+    if (h % 2 == 0) left_step_bf16(s, plan, Xb, B, si.seg, eps, ws, st, half_steps, (int)NR, ldzl);
+    else forward_residual<CfgB, CfgB3>(s, plan, X, si, eps, solver, ws, st, StageEvents{nullptr, 0});
+  }
   if (s.kind == DYRA_BLAST_DIAG) {
     // coupling W'_j = sum_i Z_i diag(s_ij): elementwise over the block grid
     const int zt = (int)std::max<int64_t>(1, std::min<int64_t>(8, (BDC_LDS / 2) / NR));
@@ -3490,11 +3400,11 @@ int forward_blast(const dyra_spec& s, const char* plan, const void* X, const voi
   return hipGetLastError() == hipSuccess ? DYRA_OK : DYRA_EHIP;
 }
 
-// half_steps: 2 t of the ALS (2: t = 1; 3: t = 1.5; 4: t = 2); beyond 2 only
-// for the low-rank structure in bf16.
+// half_steps: 2 t of the ALS (2: t = 1; 3: t = 1.5; 4: t = 2); beyond 2 in
+// bf16 only (every structure).
 int check_als(const dyra_spec& spec, int32_t dtype, int32_t half_steps) {
+  (void)spec;
   if (half_steps < 2 || half_steps > 4) return DYRA_EINVAL;
-  if (half_steps > 2 && spec.kind != DYRA_LOWRANK) return DYRA_EINVAL;
   if (half_steps > 2 && dtype != DYRA_BF16) return DYRA_EDTYPE;
   return DYRA_OK;
 }
@@ -3555,8 +3465,9 @@ int dispatch(const dyra_spec* spec, const void* plan, const void* X, const void*
   const char* plan_c = reinterpret_cast<const char*>(plan);
   char* ws = reinterpret_cast<char*>(workspace);
   if (spec->kind == DYRA_MONARCH)
-    return forward_monarch(*spec, plan_c, X, bias, Y, si, ridge_eps, solver, ws, st, E);
-  if (is_blast(spec->kind)) return forward_blast(*spec, plan_c, X, bias, Y, si, ridge_eps, solver, ws, st, E);
+    return forward_monarch(*spec, plan_c, X, bias, Y, si, ridge_eps, solver, ws, st, E, half_steps);
+  if (is_blast(spec->kind))
+    return forward_blast(*spec, plan_c, X, bias, Y, si, ridge_eps, solver, ws, st, E, half_steps);
   if (dtype == DYRA_BF16)
     return forward_lowrank<CfgB, CfgB3, CfgB6>(*spec, plan_c, X, bias, Y, si, ridge_eps, solver, ws, st, E,
                                                half_steps);

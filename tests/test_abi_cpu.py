@@ -132,8 +132,8 @@ def test_prepare_rejects_missing_outputs():
 
 def test_als_entry_points_validate_on_host():
     """dyra_workspace_size_als / dyra_forward_als reject what they do not
-    support before any HIP call: half_steps outside 2..4, a structure other
-    than low-rank, fp32."""
+    support before any HIP call: half_steps outside 2..4, fp32 (every
+    structure runs more iterations in bf16)."""
     L = D.lib()
     lowrank = D.make_spec(synth.KIND_LOWRANK, 256, 512, 16, k=32)
     monarch = D.make_spec(synth.KIND_MONARCH, 1024, 1024, 16, mblk=32)
@@ -141,7 +141,12 @@ def test_als_entry_points_validate_on_host():
     for h, rc in ((2, 0), (3, 0), (4, 0), (1, -1), (5, -1)):
         assert L.dyra_workspace_size_als(ctypes.byref(lowrank), 2, 64, synth.DT_BF16, h, ctypes.byref(n)) == rc
     assert L.dyra_workspace_size_als(ctypes.byref(lowrank), 2, 64, synth.DT_F32, 3, ctypes.byref(n)) == -6
-    assert L.dyra_workspace_size_als(ctypes.byref(monarch), 2, 64, synth.DT_BF16, 3, ctypes.byref(n)) == -1
+    assert L.dyra_workspace_size_als(ctypes.byref(monarch), 2, 64, synth.DT_BF16, 3, ctypes.byref(n)) == 0
+    base_m = ctypes.c_size_t()
+    L.dyra_workspace_size(ctypes.byref(monarch), 2, 64, synth.DT_BF16, ctypes.byref(base_m))
+    assert n.value > base_m.value
+    blast = D.make_spec(synth.KIND_BLAST, 256, 512, 16, nb=2, rb=16)
+    assert L.dyra_workspace_size_als(ctypes.byref(blast), 2, 64, synth.DT_BF16, 4, ctypes.byref(n)) == 0
     sizes = []
     for h in (2, 3, 4):
         L.dyra_workspace_size_als(ctypes.byref(lowrank), 2, 64, synth.DT_BF16, h, ctypes.byref(n))

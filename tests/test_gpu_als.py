@@ -39,6 +39,23 @@ def test_als_parity(w, half_steps):
     assert np.all(status == D.SOLVE_OK)
 
 
+# the structured static branches: the left step is the same (it does not
+# involve W_hat); only where L sits in the first-stage output differs
+STRUCTURED = [
+    sc(W["monarch"], name="als_monarch", B=3, s=77),
+    sc(W["lm_blast"], name="als_blast", B=2, s=200, c1=512, c2=1536, nb=4, rb=32, r=32, solver="auto"),
+    sc(W["lm_blast_diag"], name="als_blast_diag", B=2, s=200, c1=512, c2=1536, nb=4, rb=32, r=32,
+       solver="auto"),
+]
+
+
+@pytest.mark.parametrize("half_steps", [3, 4])
+@pytest.mark.parametrize("w", STRUCTURED, ids=lambda w: w.name)
+def test_als_structured(w, half_steps):
+    err, status, _, _ = run_same_factor_case(w, half_steps=half_steps)
+    assert np.all(status == D.SOLVE_OK)
+
+
 @pytest.mark.parametrize("half_steps", [3, 4])
 def test_als_full_size_vitl(half_steps):
     run_same_factor_case(W["vitl_fc1"], half_steps=half_steps)
