@@ -949,26 +949,24 @@ __global__ __launch_bounds__(256, 2) void s1_monarch_kernel(const bf16_t* __rest
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int v = 0; v < 16; ++v) lacc[rb][v] = 0.f;
-  // the 16 X loads first (rows past n read row n - 1, zeroed below): one wait on HBM
-  const int64_t rowc = rok ? row : n - 1;
-  uint4 xr[8][2];
+  // one (block, k step) at a time: at about 130 registers three workgroups
+  // share a CU, which hides the X loads better than issuing the row block's
+  // sixteen loads up front at two (measured 35 against 40-53 us)
 #pragma unroll
-  for (int ai = 0; ai < 8; ++ai)
+  for (int ai = 0; ai < 8; ++ai) {
+    const int a = w * 8 + ai;
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
-      xr[ai][s] = *reinterpret_cast<const uint4*>(X + rowc * C + (w * 8 + ai) * MO + 16 * s + 8 * g);
-  // Pt fragments (L2-resident, fragment order); Pt holds whole 32-row groups
-  // (rows past r zero), so its test is wave-uniform
+    for (int s = 0; s < 2; ++s) {
+      const int kk = a * MO + 16 * s + 8 * g;
+      const uint4 xa = rok ? *reinterpret_cast<const uint4*>(X + row * C + kk) : zero4();
 #pragma unroll
-  for (int q = 0; q < 16; ++q) {
-    const int a = w * 8 + (q >> 1), s = q & 1;
-    const uint4 xa = rok ? xr[q >> 1][s] : zero4();
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-      if (rb * 32 < r) {
-        const uint4 pb = *reinterpret_cast<const uint4*>(Pt + ((int64_t)((rb * MO + a) * 2 + s) * 64 + lane) * 8);
+      for (int rb = 0; rb < RB; ++rb) {
+        const int p = rb * 32 + l;
+        const uint4 pb =
+            p < r ? *reinterpret_cast<const uint4*>(Pt + ((int64_t)((rb * MO + a) * 2 + s) * 64 + lane) * 8) : zero4();
         TT<bf16_t>::mma(lacc[rb], pb, xa);
       }
+    }
   }
   // L partials: waves 1..3 -> LDS, wave 0 adds them in order
   if (w > 0) {
@@ -2844,6 +2842,9 @@ __global__ __launch_bounds__(64 * AI_WAVES) void apply_inverse_kernel(const floa
 // 64-column tile), the same reduction-index permutation as the fp32 kernel,
 // on v_mfma_f64_16x16x4f64 (operands one double per lane, k = lane / 16;
 // accumulator rows interleaved: element v of lane (i, g) is row g + 4 v).
+// With NTC > 0 (r <= 16 NTC) every chunk's loads are issued before the
+// first product, so a wave waits on memory once.
+template <int NTC>
 __global__ __launch_bounds__(64 * AI_WAVES) void apply_inverse_f64_kernel(const double* __restrict__ Ginv,
                                                                           const float* __restrict__ M,
                                                                           bf16_t* __restrict__ Mp16,
@@ -2870,16 +2871,21 @@ __global__ __launch_bounds__(64 * AI_WAVES) void apply_inverse_f64_kernel(const 
   f64x4 acc[4];
 #pragma unroll
   for (int jb = 0; jb < 4; ++jb) acc[jb] = f64x4{0.0, 0.0, 0.0, 0.0};
-  for (int t = 0; t < nt; ++t) {
+  // chunk t: the lane's Ginv run (row `row`, q = 16 t + 4 g .. + 3) and its
+  // four M runs (rows q, columns col .. col + 3); past r or c1 they read as
+  // zeros (loads clamped to valid addresses, values selected afterwards)
+  auto load = [&](int t, double4& a, float4 (&m)[4]) {
     const int q0 = 16 * t + 4 * g;              // r % 4 == 0: all four q or none
-    const bool qok = q0 < r;
-    const double4 a = (row < r && qok) ? *reinterpret_cast<const double4*>(Gb + (int64_t)row * r + q0)
-                                       : make_double4(0.0, 0.0, 0.0, 0.0);
-    float4 m[4];
+    const bool aok = row < r && q0 < r, mok = cok && q0 < r;
+    const double4 av = *reinterpret_cast<const double4*>(Gb + (int64_t)(aok ? row : 0) * r + (aok ? q0 : 0));
+    a = aok ? av : make_double4(0.0, 0.0, 0.0, 0.0);
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      m[e] = (cok && qok) ? *reinterpret_cast<const float4*>(Mb + (int64_t)(q0 + e) * c1 + col)
-                          : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int e = 0; e < 4; ++e) {
+      const float4 mv = *reinterpret_cast<const float4*>(Mb + (int64_t)(mok ? q0 + e : 0) * c1 + (mok ? col : 0));
+      m[e] = mok ? mv : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  auto mul = [&](const double4& a, const float4 (&m)[4]) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const double av = e == 0 ? a.x : e == 1 ? a.y : e == 2 ? a.z : a.w;
@@ -2887,6 +2893,21 @@ __global__ __launch_bounds__(64 * AI_WAVES) void apply_inverse_f64_kernel(const 
       acc[1] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, (double)m[e].y, acc[1], 0, 0, 0);
       acc[2] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, (double)m[e].z, acc[2], 0, 0, 0);
       acc[3] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, (double)m[e].w, acc[3], 0, 0, 0);
+    }
+  };
+  if constexpr (NTC > 0) {
+    double4 a[NTC];
+    float4 m[NTC][4];
+#pragma unroll
+    for (int t = 0; t < NTC; ++t) load(t, a[t], m[t]);
+#pragma unroll
+    for (int t = 0; t < NTC; ++t) mul(a[t], m[t]);
+  } else {
+    for (int t = 0; t < nt; ++t) {
+      double4 a;
+      float4 m[4];
+      load(t, a, m);
+      mul(a, m);
     }
   }
   if (!cok) return;
@@ -2934,8 +2955,13 @@ void launch_apply_inverse(const double* Gi, const float* Gi32, const float* M, T
   float* m32 = nullptr;
   if constexpr (TT<T>::ESZ == 2) m16 = reinterpret_cast<bf16_t*>(Mp);
   else m32 = reinterpret_cast<float*>(Mp);
-  hipLaunchKernelGGL(apply_inverse_f64_kernel, dim3((unsigned)((t64 + AI_WAVES - 1) / AI_WAVES)), dim3(64 * AI_WAVES),
-                     0, st, Gi, M, m16, m32, r, c1, t64, stat, prec);
+  const dim3 g64((unsigned)((t64 + AI_WAVES - 1) / AI_WAVES)), b64(64 * AI_WAVES);
+  if (r <= 32)
+    hipLaunchKernelGGL((apply_inverse_f64_kernel<2>), g64, b64, 0, st, Gi, M, m16, m32, r, c1, t64, stat, prec);
+  else if (r <= 64)
+    hipLaunchKernelGGL((apply_inverse_f64_kernel<4>), g64, b64, 0, st, Gi, M, m16, m32, r, c1, t64, stat, prec);
+  else
+    hipLaunchKernelGGL((apply_inverse_f64_kernel<0>), g64, b64, 0, st, Gi, M, m16, m32, r, c1, t64, stat, prec);
 }
 
 // ===========================================================================
