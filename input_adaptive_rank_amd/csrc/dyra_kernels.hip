@@ -554,9 +554,15 @@ __global__ __launch_bounds__(C::NT, WPE) void s6_lowrank_kernel(const typename C
 // epilogue only converts, stages 32 rows per wave in that wave's part of the
 // consumed slot, and writes whole 128-byte lines non-temporally.
 // ---------------------------------------------------------------------------
+//
+// The first part's A operand is A0 (row pitch lda0 bytes; with acolb > 0 its
+// columns start at (n0 / acolb) k for the tile at output column n0: the
+// BLAST coupled output W'_j of block column j), the residual part's A1
+// (pitch lda1: L).  Low-rank: A0 = [T | L], A1 = its L columns.
 template <class C, int NS, int NL, bool HAS_BIAS>
 __global__ __launch_bounds__(C::NT + NL * 64, 1) void s6_lowrank_ws_kernel(
-    const bf16_t* __restrict__ TL, const bf16_t* __restrict__ Vt, const bf16_t* __restrict__ Rt,
+    const bf16_t* __restrict__ A0, int lda0, int acolb, const bf16_t* __restrict__ A1, int lda1,
+    const bf16_t* __restrict__ Vt, const bf16_t* __restrict__ Rt,
     const bf16_t* __restrict__ bias, bf16_t* __restrict__ Y, int n, int c2, int k, int r, SegMap sg, int B,
     int tiles_n, int tiles) {
   static_assert(NS >= 2 && NS <= 4, "ring depth");
@@ -575,7 +581,7 @@ __global__ __launch_bounds__(C::NT + NL * 64, 1) void s6_lowrank_ws_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = lane & 31, gq = lane >> 5;
-  const int lda = (k + r) * 2, kE = k * 2, rE = r * 2, ldr = B * rE;
+  const int kE = k * 2, rE = r * 2, ldr = B * rE;
   const int nk0 = (kE + 127) >> 7, nkr = (rE + 127) >> 7;
   const int G8 = gridDim.x >> 3, xcd = blockIdx.x & 7, lw = blockIdx.x >> 3;
   const int chunk = (tiles + 7) >> 3;
@@ -628,22 +634,25 @@ __global__ __launch_bounds__(C::NT + NL * 64, 1) void s6_lowrank_ws_kernel(
     // lds_off swizzle), which is the same chunk for every j as NL is even
     const int row0 = q * 8 + (lane >> 3);
     const int ch16 = ((lane & 7) ^ ((row0 >> 1) & 7)) << 4;
-    const int a_v = row0 * lda + ch16, v_v = row0 * kE + ch16, r_v = row0 * ldr + ch16;
+    const int a_v0 = row0 * lda0 + ch16, a_v1 = row0 * lda1 + ch16, v_v = row0 * kE + ch16, r_v = row0 * ldr + ch16;
     // Issue state: the k-tiles of a tile come in parts, [T | V] (nk0
     // k-tiles) and then [L_b | R_b] per segment b the tile meets (nkr each);
     // descriptors, row bounds and fast-path flags are set once per part, so
     // a k-tile costs its DMAs and a k offset.  Block j of this loader sits
     // j NL 8 rows below its block 0, an offset the scalar operand carries.
     Cur ic = cc;
-    const int sA = NL * 8 * lda, sV = NL * 8 * kE, sR = NL * 8 * ldr;
+    const int sA0 = NL * 8 * lda0, sA1 = NL * 8 * lda1, sV = NL * 8 * kE, sR = NL * 8 * ldr;
     const uint32_t lq0 = ring_s + q * 1024;   // this loader's block 0 in slot 0
     int p_kind = 0, p_left = 0, p_kb = 0, p_kbytes = 0, p_alo = 0, p_ahi = 0, p_ib = 0;
     int p_fa = 0, p_fb = 0, p_live = 0;   // ints, not bools: kept in registers
+    int p_av = a_v0, p_sa = sA0;          // the part's A row offset and block step
     i32x4v p_ars, p_brs, p_rsb;
     auto set_tv = [&]() __attribute__((always_inline)) {
       p_live = ic.t < hi_tile ? 1 : 0;
       p_kind = 0; p_left = nk0; p_kb = 0; p_kbytes = kE; p_ib = ic.b0;
-      p_ars = rsrc_words(reinterpret_cast<const char*>(TL) + (int64_t)ic.m0 * lda, 0x7fffffffu);
+      p_av = a_v0; p_sa = sA0;
+      p_ars = rsrc_words(reinterpret_cast<const char*>(A0) + (int64_t)ic.m0 * lda0 +
+                             (acolb ? (int64_t)(ic.n0 / acolb) * kE : 0), 0x7fffffffu);
       p_brs = rsrc_words(reinterpret_cast<const char*>(Vt) + (int64_t)ic.n0 * kE, 0x7fffffffu);
       p_rsb = rsrc_words(bias + ic.n0, HAS_BIAS && p_live ? (uint32_t)(c2 - ic.n0) * 2u : 0u);
       p_alo = -ic.m0; p_ahi = n - ic.m0;
@@ -652,7 +661,8 @@ __global__ __launch_bounds__(C::NT + NL * 64, 1) void s6_lowrank_ws_kernel(
     };
     auto set_lr = [&](int ibx) __attribute__((always_inline)) {
       p_kind = 1; p_left = nkr; p_kb = 0; p_kbytes = rE; p_ib = ibx;
-      p_ars = rsrc_words(reinterpret_cast<const char*>(TL) + (int64_t)ic.m0 * lda + kE, 0x7fffffffu);
+      p_av = a_v1; p_sa = sA1;
+      p_ars = rsrc_words(reinterpret_cast<const char*>(A1) + (int64_t)ic.m0 * lda1, 0x7fffffffu);
       p_brs = rsrc_words(reinterpret_cast<const char*>(Rt) + (int64_t)ibx * rE + (int64_t)ic.n0 * ldr, 0x7fffffffu);
       p_alo = (int)sg.lo(ibx) - ic.m0; p_ahi = (int)sg.hi(ibx) - ic.m0;
       p_fa = p_live && p_alo <= 0 && p_ahi >= C::BM ? 1 : 0;
@@ -669,14 +679,14 @@ __global__ __launch_bounds__(C::NT + NL * 64, 1) void s6_lowrank_ws_kernel(
       if (p_fa && fullk) {
         static_for<0, LA>([&](auto jc) __attribute__((always_inline)) {
           constexpr int j = decltype(jc)::value;
-          dma16k<j * NL * 1024>(p_ars, a_v, p_kb + j * sA, lb);
+          dma16k<j * NL * 1024>(p_ars, p_av, p_kb + j * p_sa, lb);
         });
       } else {
         static_for<0, LA>([&](auto jc) __attribute__((always_inline)) {
           constexpr int j = decltype(jc)::value;
           const int rr = row0 + j * NL * 8;
-          const int v = p_live && kok && rr >= p_alo && rr < p_ahi ? a_v : (int)0x80000000u;
-          dma16k<j * NL * 1024>(p_ars, v, p_kb + j * sA, lb);
+          const int v = p_live && kok && rr >= p_alo && rr < p_ahi ? p_av : (int)0x80000000u;
+          dma16k<j * NL * 1024>(p_ars, v, p_kb + j * p_sa, lb);
         });
       }
       auto bdmas = [&](int vb, int sb) __attribute__((always_inline)) {
@@ -1209,8 +1219,14 @@ __global__ __launch_bounds__(C::NT) void s6_blast_kernel(const bf16_t* Wp, int64
                                                          SegMap sg, int64_t B, int tiles_n) {
   constexpr int E = 2;
   __shared__ __attribute__((aligned(16))) char lds[C::LDS];
+  // column-major tile order, so that the contiguous tile range each XCD
+  // takes is a band of output columns over all rows: its V_j and R^T rows,
+  // and the W'_j and L rows of the few block columns j it meets, fit its L2
+  // (row-major bands made every XCD stream all of V and R^T once per row
+  // block: 9x the algorithmic read bytes at the LM BLAST shape)
   const int t = xcd_tile_id(blockIdx.x, gridDim.x);
-  const int64_t m0 = (int64_t)(t / tiles_n) * C::BM, n0 = (int64_t)(t % tiles_n) * C::BN;
+  const int tiles_m = (int)(gridDim.x / tiles_n);
+  const int64_t m0 = (int64_t)(t % tiles_m) * C::BM, n0 = (int64_t)(t / tiles_m) * C::BN;
   const int64_t j = n0 / b2;
   const int64_t bfirst = sg.of(m0);
   const int64_t blast = imin64(B - 1, sg.of(imin64(m0 + C::BM, n) - 1));
@@ -2093,7 +2109,7 @@ __global__ __launch_bounds__(S3_NT, NRB <= 4 ? 2 : 1) void s3_reduce_solve_kerne
     float* __restrict__ Gi32,
     int32_t* __restrict__ status, int32_t* __restrict__ prec, float eps, int strips, int64_t lt_seg_rows,
     int x_rel,
-    const float* __restrict__ gpart, int gchunks, int64_t gprows) {
+    const float* __restrict__ gpart, int gchunks, int64_t gprows, int msplit, float* __restrict__ Mpart) {
   __shared__ __attribute__((aligned(16))) char lds[S3Lds<NB>::BYTES];
   SweepLds* sl = reinterpret_cast<SweepLds*>(lds + S3Lds<NB>::SW_OFF);
   const int64_t bid = blockIdx.x;
@@ -2111,7 +2127,18 @@ __global__ __launch_bounds__(S3_NT, NRB <= 4 ? 2 : 1) void s3_reduce_solve_kerne
   // strips of a segment share one L2 copy of its L^T rows instead of every
   // XCD fetching every segment's rows from HBM.
   int64_t b, strip;   // strip < 0: solve role
-  if ((B & 7) == 0) {
+  int part = 0;       // token part of the strip (msplit > 1)
+  if (msplit > 1) {
+    if (bid < B) {
+      b = bid;
+      strip = -1;
+    } else {
+      const int64_t u = bid - B;
+      b = u / (strips * msplit);
+      strip = (u / msplit) % strips;
+      part = (int)(u % msplit);
+    }
+  } else if ((B & 7) == 0) {
     const int64_t x = bid & 7, j = bid >> 3, per = B >> 3;
     if (j < per) {
       b = x + 8 * j;
@@ -2211,11 +2238,39 @@ __global__ __launch_bounds__(S3_NT, NRB <= 4 ? 2 : 1) void s3_reduce_solve_kerne
   const bf16_t *Ltb, *Xb;
   int64_t tbase;
   seg_ptrs(b, lo, Ltb, Xb, tbase);
+  // this workgroup's tokens: the whole segment, or part `part` of msplit
+  // (32-token aligned; an empty part writes zeros)
+  int64_t plo = lo, phi = hi;
+  float* Mb = M + b * r * c1;
+  if (msplit > 1) {
+    const int64_t chunk = ((hi - lo + msplit - 1) / msplit + 31) & ~(int64_t)31;
+    plo = imin64(hi, lo + part * chunk);
+    phi = imin64(hi, plo + chunk);
+    Mb = Mpart + ((int64_t)part * B + b) * r * c1;
+  }
   // 32-bit buffer offsets reach every X row of a 32-token step and every
   // L^T row of a step
   const bool b32 = 32 * c1 * 2 < ((int64_t)1 << 31) && ((int64_t)r * ldt + 64) * 2 < ((int64_t)1 << 31);
-  if (b32) s3_m_strip<NRB, true>(Ltb, ldt, Xb, c1, r, lo, hi, c0, M + b * r * c1, lds, tbase);
-  else s3_m_strip<NRB, false>(Ltb, ldt, Xb, c1, r, lo, hi, c0, M + b * r * c1, lds, tbase);
+  if (b32) s3_m_strip<NRB, true>(Ltb, ldt, Xb, c1, r, plo, phi, c0, Mb, lds, tbase);
+  else s3_m_strip<NRB, false>(Ltb, ldt, Xb, c1, r, plo, phi, c0, Mb, lds, tbase);
+}
+
+// M = sum over the msplit token parts of the strips' fp32 partials, in part
+// order (float4 per thread).
+__global__ __launch_bounds__(256) void m_split_reduce_kernel(const float* __restrict__ Mpart, float* __restrict__ M,
+                                                             int64_t count4, int msplit) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= count4) return;
+  const float4* src = reinterpret_cast<const float4*>(Mpart);
+  float4 acc = src[i];
+  for (int p = 1; p < msplit; ++p) {
+    const float4 v = src[(int64_t)p * count4 + i];
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
+  }
+  reinterpret_cast<float4*>(M)[i] = acc;
 }
 
 // Gram partials over token chunks: workgroup (b, c) writes
@@ -3003,8 +3058,8 @@ typedef GemmCfg<bf16_t, 256, 128, 2, 2> CfgB6W;
 constexpr int S6W_NS = 3, S6W_NL = 4;
 
 // Whether the persistent S6 applies: every 32-bit offset it forms stays in range.
-bool s6_ws_fits(int64_t n, int64_t c2, int k, int r, int64_t B) {
-  const int64_t lda = (int64_t)(k + r) * 2, ldr = B * r * 2, ldy = c2 * 2;
+bool s6_ws_fits(int64_t n, int64_t c2, int k, int r, int64_t B, int64_t lda_el = 0) {
+  const int64_t lda = (lda_el ? lda_el : (int64_t)(k + r)) * 2, ldr = B * r * 2, ldy = c2 * 2;
   const int64_t tiles = cdiv(n, CfgB6W::BM) * cdiv(c2, CfgB6W::BN);
   return n < ((int64_t)1 << 30) && lda * CfgB6W::BM < ((int64_t)1 << 30) && ldr * CfgB6W::BN < ((int64_t)1 << 30) &&
          ldy * CfgB6W::BM < ((int64_t)1 << 30) && tiles < ((int64_t)1 << 30);
@@ -3022,9 +3077,17 @@ int device_cus() {
   return cus[dev];
 }
 
-void launch_s6_ws(const bf16_t* TL, const bf16_t* Vt, const bf16_t* Rt, const bf16_t* bias, bf16_t* Y, int64_t n,
-                  int64_t c2, int k, int r, SegMap sg, int64_t B, hipStream_t st) {
+// A0 / lda0_el / acolb and A1 / lda1_el: the two A operands (element
+// pitches; A1 null: the L columns of A0 after its k static columns).
+void launch_s6_ws(const bf16_t* A0, int64_t lda0_el, int64_t acolb, const bf16_t* A1, int64_t lda1_el,
+                  const bf16_t* Vt, const bf16_t* Rt, const bf16_t* bias, bf16_t* Y, int64_t n, int64_t c2, int k,
+                  int r, SegMap sg, int64_t B, hipStream_t st) {
   typedef CfgB6W C;
+  if (!A1) {
+    A1 = A0 + k;
+    lda1_el = lda0_el;
+  }
+  const int lda0 = (int)(lda0_el * 2), lda1 = (int)(lda1_el * 2), ac = (int)acolb;
   const int tiles_n = (int)cdiv(c2, C::BN);
   const int tiles = (int)(cdiv(n, C::BM) * tiles_n);
   const int cus = device_cus();
@@ -3032,10 +3095,10 @@ void launch_s6_ws(const bf16_t* TL, const bf16_t* Vt, const bf16_t* Rt, const bf
   const int grid = cus >= 16 ? (cus / 8) * 8 : 8;
   if (bias)
     hipLaunchKernelGGL((s6_lowrank_ws_kernel<C, S6W_NS, S6W_NL, true>), dim3(grid), dim3(C::NT + S6W_NL * 64), 0, st,
-                       TL, Vt, Rt, bias, Y, (int)n, (int)c2, k, r, sg, (int)B, tiles_n, tiles);
+                       A0, lda0, ac, A1, lda1, Vt, Rt, bias, Y, (int)n, (int)c2, k, r, sg, (int)B, tiles_n, tiles);
   else
     hipLaunchKernelGGL((s6_lowrank_ws_kernel<C, S6W_NS, S6W_NL, false>), dim3(grid), dim3(C::NT + S6W_NL * 64), 0, st,
-                       TL, Vt, Rt, bias, Y, (int)n, (int)c2, k, r, sg, (int)B, tiles_n, tiles);
+                       A0, lda0, ac, A1, lda1, Vt, Rt, bias, Y, (int)n, (int)c2, k, r, sg, (int)B, tiles_n, tiles);
 }
 
 
@@ -3078,19 +3141,25 @@ void launch_s3_bf16(const bf16_t* Lt, int64_t ldt, const bf16_t* X, int64_t c1, 
                     float eps,
                     int solve_mode,
                     hipStream_t st, int64_t lt_seg_rows = 0, bool x_rel = false, float* gpart = nullptr,
-                    int gchunks = 0, int64_t gchunk = 0, int64_t gprows = 0) {
+                    int gchunks = 0, int64_t gchunk = 0, int64_t gprows = 0, int msplit = 1,
+                    float* Mpart = nullptr) {
   const int strips = (int)cdiv(c1, S3_STRIP);
   if (gpart && gprows == 0)   // chunk Gram partials first (absolute L^T addressing only)
     hipLaunchKernelGGL((gram_partial_kernel<NB>), dim3((unsigned)(B * gchunks)), dim3(64), 0, st, Lt, ldt, r,
                        sg, n, gchunks, gchunk, gpart);
   auto go = [&](auto kern) {
-    hipLaunchKernelGGL(kern, dim3((unsigned)(B + B * strips)), dim3(S3_NT), 0, st, Lt, ldt, X, c1, r, sg, n, B, M,
-                       G, Gi, Gi32, stat, prec, eps, strips, lt_seg_rows, x_rel ? 1 : 0, gpart, gchunks,
-                       gprows);
+    hipLaunchKernelGGL(kern, dim3((unsigned)(B + B * strips * msplit)), dim3(S3_NT), 0, st, Lt, ldt, X, c1, r, sg, n,
+                       B, M, G, Gi, Gi32, stat, prec, eps, strips, lt_seg_rows, x_rel ? 1 : 0, gpart, gchunks,
+                       gprows, msplit, Mpart);
   };
   if (solve_mode == 2) go(s3_reduce_solve_kernel<NRB, NB, 2>);
   else if (solve_mode == 1) go(s3_reduce_solve_kernel<NRB, NB, 1>);
   else go(s3_reduce_solve_kernel<NRB, NB, 0>);
+  if (msplit > 1) {
+    const int64_t count4 = B * r * c1 / 4;   // c1 % 8 == 0
+    hipLaunchKernelGGL(m_split_reduce_kernel, dim3((unsigned)cdiv(count4, 256)), dim3(256), 0, st, Mpart, M, count4,
+                       msplit);
+  }
 }
 
 // S3, S4 and S5, shared by every structure: M_b, G_b, Ginv_b, M'_b and
@@ -3127,7 +3196,10 @@ void forward_residual(const dyra_spec& s, const char* plan, const void* X, const
   // stays selectable.
   const bool ns = solver == DYRA_SOLVER_NS;
   // solve inside the token-reduction launch: 1 the sweep, 2 the Cholesky
-  // route, 0 none (Newton-Schulz runs after it)
+  // route, 0 none (Newton-Schulz runs after it).  The sweep stays inside
+  // at r = 128 too: the separate 1024-thread sweep launch took as long
+  // (145 against 141 us for one LM BLAST solve) and lost the overlap with
+  // the strips.
   const int mode = ns ? 0 : (solver == DYRA_SOLVER_CHOL ? 2 : 1);
   // S3: M_b, G_b (bf16: with the sweep solve in the same launch)
   bool solved = false;
@@ -3136,11 +3208,13 @@ void forward_residual(const dyra_spec& s, const char* plan, const void* X, const
     float* Gp = reinterpret_cast<float*>(ws + WL.Gp);
     const int gc = (int)WL.gchunks;
     const int64_t gk = WL.gchunk;
-    if (r <= 16) launch_s3_bf16<1, 1>(Lt, ldt, Xb, c1, r, sg, n, B, M, G, Gi, Gi32, stat, prec, eps, mode, st, 0, false, Gp, gc, gk, gram_rows);
-    else if (r <= 32) launch_s3_bf16<2, 1>(Lt, ldt, Xb, c1, r, sg, n, B, M, G, Gi, Gi32, stat, prec, eps, mode, st, 0, false, Gp, gc, gk, gram_rows);
-    else if (r <= 64) launch_s3_bf16<4, 2>(Lt, ldt, Xb, c1, r, sg, n, B, M, G, Gi, Gi32, stat, prec, eps, mode, st, 0, false, Gp, gc, gk, gram_rows);
-    else launch_s3_bf16<8, 4>(Lt, ldt, Xb, c1, r, sg, n, B, M, G, Gi, Gi32, stat, prec, eps, mode, st, 0, false, Gp, gc, gk, gram_rows);
-    solved = !ns;
+    const int ms = WL.msplit;
+    float* Mpt = reinterpret_cast<float*>(ws + WL.Mpart);
+    if (r <= 16) launch_s3_bf16<1, 1>(Lt, ldt, Xb, c1, r, sg, n, B, M, G, Gi, Gi32, stat, prec, eps, mode, st, 0, false, Gp, gc, gk, gram_rows, ms, Mpt);
+    else if (r <= 32) launch_s3_bf16<2, 1>(Lt, ldt, Xb, c1, r, sg, n, B, M, G, Gi, Gi32, stat, prec, eps, mode, st, 0, false, Gp, gc, gk, gram_rows, ms, Mpt);
+    else if (r <= 64) launch_s3_bf16<4, 2>(Lt, ldt, Xb, c1, r, sg, n, B, M, G, Gi, Gi32, stat, prec, eps, mode, st, 0, false, Gp, gc, gk, gram_rows, ms, Mpt);
+    else launch_s3_bf16<8, 4>(Lt, ldt, Xb, c1, r, sg, n, B, M, G, Gi, Gi32, stat, prec, eps, mode, st, 0, false, Gp, gc, gk, gram_rows, ms, Mpt);
+    solved = mode != 0;
   } else {
     const int tr = (int)cdiv(r, C3::BM), tcm = (int)cdiv(c1, C3::BN), tcg = (int)cdiv(r, C3::BN);
     const int64_t grid = B * tr * (tcm + tcg);
@@ -3191,7 +3265,8 @@ void forward_residual(const dyra_spec& s, const char* plan, const void* X, const
       return;
     }
     if (s6_ws_fits(c2, B * r, (int)c1, 0, 1) && device_cus() >= 8) {
-      launch_s6_ws(Wrt, Mp, nullptr, nullptr, Rt, c2, B * r, (int)c1, 0, SegMap{nullptr, c2, 1, c2}, 1, st);
+      launch_s6_ws(Wrt, c1, 0, nullptr, 0, Mp, nullptr, nullptr, Rt, c2, B * r, (int)c1, 0, SegMap{nullptr, c2, 1, c2},
+                   1, st);
       return;
     }
   }
@@ -3299,9 +3374,9 @@ int forward_lowrank(const dyra_spec& s, const char* plan, const void* X, const v
     const int64_t tiles = cdiv(n, C6::BM) * tiles_n;
     constexpr bool BF = TT<T>::ESZ == 2;
     if (BF && s6_ws_fits(n, c2, k, r, B) && device_cus() >= 8)
-      launch_s6_ws(reinterpret_cast<const bf16_t*>(TL), reinterpret_cast<const bf16_t*>(plan + PL.Vt),
-                   reinterpret_cast<const bf16_t*>(Rt), reinterpret_cast<const bf16_t*>(bias),
-                   reinterpret_cast<bf16_t*>(Y), n, c2, k, r, si.map(), B, st);
+      launch_s6_ws(reinterpret_cast<const bf16_t*>(TL), k + r, 0, nullptr, 0,
+                   reinterpret_cast<const bf16_t*>(plan + PL.Vt), reinterpret_cast<const bf16_t*>(Rt),
+                   reinterpret_cast<const bf16_t*>(bias), reinterpret_cast<bf16_t*>(Y), n, c2, k, r, si.map(), B, st);
     else
       hipLaunchKernelGGL((s6_lowrank_kernel<C6, BF, true, BF ? S6_WPE : 1, BF>), dim3((unsigned)tiles), dim3(C6::NT), 0,
                          st, TL, reinterpret_cast<const T*>(plan + PL.Vt), Rt, reinterpret_cast<const T*>(bias),
@@ -3408,7 +3483,14 @@ int forward_blast(const dyra_spec& s, const char* plan, const void* X, const voi
   {
     typedef CfgB6 C6;
     const bf16_t* Rt = reinterpret_cast<const bf16_t*>(ws + WL.Rt);
-    if (b2 % C6::BN == 0) {
+    // the persistent output kernel: part 0 is W'_j V_j^T (W' columns of the
+    // tile's block column j, V_j rows = the tile's output columns of Vb read
+    // as a [c2 x rb] matrix), part 1 is L R_b
+    if (b2 % CfgB6W::BN == 0 && s6_ws_fits(n, c2, rb, r, B, std::max<int64_t>(NR, ldzl)) && device_cus() >= 8) {
+      launch_s6_ws(Wp, NR, b2, ZL + NR, ldzl, reinterpret_cast<const bf16_t*>(plan + PL.Vb), Rt,
+                   reinterpret_cast<const bf16_t*>(bias), reinterpret_cast<bf16_t*>(Y), n, c2, rb, r, si.map(), B,
+                   st);
+    } else if (b2 % C6::BN == 0) {
       const int tiles_n = (int)(c2 / C6::BN);
       const int64_t tiles = cdiv(n, C6::BM) * tiles_n;
       hipLaunchKernelGGL(s6_blast_kernel<C6>, dim3((unsigned)tiles), dim3(C6::NT), 0, st, Wp, NR, ZL, ldzl, NR,

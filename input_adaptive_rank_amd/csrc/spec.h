@@ -173,6 +173,9 @@ struct WsLayout {
   size_t A = 0, Wp = 0, Lt = 0, G = 0, M = 0, Ginv = 0, Mp = 0, Rt = 0, status = 0, Pk = 0, Xit = 0;
   // per-segment precision of M' = Ginv M (0 fp32, 1 fp64), set by the solve
   size_t prec = 0, kprec = 0, Gi32 = 0, Ki32 = 0;
+  // token-split partials of M [msplit][B x r x c1] fp32 (msplit > 1 only)
+  size_t Mpart = 0;
+  int msplit = 1;
   // Gram partials [B][gchunks][r x r] fp32 over token chunks of gchunk tokens
   size_t Gp = 0;
   int64_t gchunk = 0, gchunks = 0;
@@ -181,6 +184,19 @@ struct WsLayout {
   size_t R = 0, K = 0, Kinv = 0, Qt = 0, Zt = 0, kstatus = 0;
   size_t total = 0;
 };
+
+// Token split of the M_b = L_b^T X_b strips: with few (segment, 128-column
+// strip) pairs the reduction runs on too few workgroups to stream X at the
+// chip's rate, so each strip's tokens are cut into parts whose fp32 partials
+// a second launch adds in a fixed order.  At least 512 tokens per part.
+inline int s3_token_split(int64_t B, int64_t c1, int64_t max_len) {
+  const int64_t pairs = B * ((c1 + 127) / 128);
+  if (pairs >= 128) return 1;
+  int64_t ts = (256 + pairs - 1) / pairs;
+  if (ts > 8) ts = 8;
+  if (ts > max_len / 512) ts = max_len / 512;
+  return ts < 1 ? 1 : (int)ts;
+}
 
 // B segments of n rows in all, the longest max_len rows.
 inline WsLayout ws_layout_n(const dyra_spec& s, int64_t B, int64_t n_rows, int64_t max_len, int dtype,
@@ -212,6 +228,8 @@ inline WsLayout ws_layout_n(const dyra_spec& s, int64_t B, int64_t n_rows, int64
   W.Rt = take(c2 * (size_t)B * r * e);
   W.status = take((size_t)B * 4);
   W.prec = take((size_t)B * 4);
+  W.msplit = s3_token_split(B, s.c1, seg);
+  if (W.msplit > 1) W.Mpart = take((size_t)W.msplit * B * r * c1 * 4);
   W.gchunk = s.r > 64 ? 256 : 128;
   W.gchunks = (seg + W.gchunk - 1) / W.gchunk;
   // token-chunk partials, or two per 160-token first-stage tile

@@ -64,6 +64,9 @@ SMALL = [
     # first-stage Gram partials: 170-token segments, so nearly every 160-row
     # tile meets two segments (both partial slots in use)
     sc(W["vitl_fc1"], name="first_stage_gram_short_segments", B=20, s=170, c1=384, c2=512, k=256, r=64),
+    # few (segment, column strip) pairs: the M strips split their tokens
+    # into parts whose fp32 partials a second launch adds (4 parts here)
+    sc(W["vitl_fc1"], name="token_split_long_segments", B=2, s=2100, c1=512, c2=512, k=64, r=64),
 ]
 
 

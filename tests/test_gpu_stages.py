@@ -29,6 +29,8 @@ CASES = [
     # smallest relative pivot is ~eps and M' is formed in fp64
     sc(W["vitl_fc1"], name="stage_short_fp64", B=3, s=40, c1=256, c2=512, k=64, r=64),
     sc(W["vitl_fc1"], name="stage_short_fp64_chol", B=3, s=40, c1=256, c2=512, k=64, r=64, solver="chol"),
+    # M from token-split strips (2 parts) and their ordered reduction
+    sc(W["vitl_fc1"], name="stage_token_split", B=2, s=1100, c1=256, c2=512, k=64, r=64),
 ]
 
 WIDE_PIVOT = 2.0 ** -5     # relative pivot below which the library applies Ginv in fp64

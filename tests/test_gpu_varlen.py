@@ -42,6 +42,9 @@ CASES = [
     ("lowrank_tile_gram", sc(W["vitl_fc1"], c1=384, c2=512, k=256, r=64), list(_mix(7, 9, 160, 700))),
     ("lowrank_tile_short", sc(W["vitl_fc1"], c1=384, c2=512, k=256, r=64), [5, 400, 33, 250]),
     ("monarch_mixed", sc(W["monarch"], r=32), [11, 300, 1, 200, 97]),
+    # few segments, long ones: the M strips split their tokens (2 parts; the
+    # 37-token segment's second part is partial)
+    ("lowrank_token_split", sc(W["vitl_fc1"], c1=512, c2=512, k=64, r=64), [1500, 37, 1100]),
     ("blast_mixed", sc(W["lm_blast"], c1=512, c2=1536, nb=4, rb=32, r=32, n_out=4, solver="auto"),
      [40, 1, 300, 111]),
     ("blast_diag_mixed", sc(W["lm_blast_diag"], c1=512, c2=1536, nb=4, rb=32, r=32, n_out=4, solver="auto"),
