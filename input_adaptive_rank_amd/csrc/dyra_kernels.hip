@@ -1456,7 +1456,7 @@ __device__ __forceinline__ double recip_pos(double D) {
 // thread).
 template <int NT, int TB>
 __device__ __forceinline__ int sweep_inverse(const float* Gb, double* Ob, float* Ob32, int r, float eps,
-                                             SweepLds& sh, double& rho) {
+                                             SweepLds& sh, bool& wide) {
   static_assert(TB % SW_BK == 0 && TB % 2 == 0, "tile");
   const int tid = threadIdx.x;
   const int tpr = (r + TB - 1) / TB;
@@ -1490,7 +1490,7 @@ __device__ __forceinline__ int sweep_inverse(const float* Gb, double* Ob, float*
           *reinterpret_cast<double2*>(&sh.pv[buf][i - k0][j0 + y]) = make_double2(a[x][y], a[x][y + 1]);
     }
   };
-  rho = 1.0;
+  wide = false;
   if (st == DYRA_SOLVE_OK) {
     const double lam = (double)(eps * tr / (float)r);
 #pragma unroll
@@ -1519,7 +1519,7 @@ __device__ __forceinline__ int sweep_inverse(const float* Gb, double* Ob, float*
         const double D = Q[p][p];
         if (!(D > 0.0) || !isfinite(D)) bad = true;
         if (eps == 0.f && !(D > kSingularPivotRel * sh.diag0[kb + p])) bad = true;
-        rho = fmin(rho, D / (sh.diag0[kb + p] + lam));
+        if (D < kWidePivot * (sh.diag0[kb + p] + lam)) wide = true;   // relative pivot below 2^-5
         const double invD = recip_pos(D);
         double c[SW_BK];
 #pragma unroll
@@ -1624,7 +1624,7 @@ __device__ __forceinline__ int packed_lower(int i, int j) { return ((i * (i + 1)
 // r (r + 1) / 2 doubles.  Returns the status (same in every thread).
 template <int NT, int TB>
 __device__ __forceinline__ int chol_inverse(const float* Gb, double* Ob, float* Ob32, int r, float eps,
-                                            SweepLds& sh, double* Cp, double& rho) {
+                                            SweepLds& sh, double* Cp, bool& wide) {
   constexpr int PB = SW_BK;
   static_assert(TB % PB == 0 && TB % 2 == 0, "tile");
   const int tid = threadIdx.x;
@@ -1657,7 +1657,7 @@ __device__ __forceinline__ int chol_inverse(const float* Gb, double* Ob, float* 
         *reinterpret_cast<double2*>(&sh.pv[buf][i - k0][j0 + y]) = make_double2(t[x][y], t[x][y + 1]);
     }
   };
-  rho = 1.0;
+  wide = false;
   if (st == DYRA_SOLVE_OK) {
     const double lam = (double)(eps * tr / (float)r);
 #pragma unroll
@@ -1679,7 +1679,7 @@ __device__ __forceinline__ int chol_inverse(const float* Gb, double* Ob, float* 
 #pragma unroll
         for (int q = 0; q < p; ++q) d = fma(-Ck[p][q], Ck[p][q], d);
         const bool ok = d > 0.0 && isfinite(d) && (eps > 0.f || d > kSingularPivotRel * sh.diag0[kb + p]);
-        rho = fmin(rho, d / (sh.diag0[kb + p] + lam));
+        if (d < kWidePivot * (sh.diag0[kb + p] + lam)) wide = true;   // relative pivot below 2^-5
         if (!ok) bad = true;
         const double c = sqrt(ok ? d : 1.0);
         ic[p] = recip_pos(c);
@@ -2126,17 +2126,24 @@ __global__ __launch_bounds__(S3_NT, NRB <= 4 ? 2 : 1) void s3_reduce_solve_kerne
   // segment b's solve role and all its strips run on XCD b mod 8, so the
   // strips of a segment share one L2 copy of its L^T rows instead of every
   // XCD fetching every segment's rows from HBM.
+  // r > 64: a strip workgroup takes 64 of the r rows of M_b (the r / 64
+  // row blocks of a strip are consecutive roles): 8 row blocks of
+  // accumulators per wave would not fit the registers
+  constexpr int SNRB = NRB > 4 ? 4 : NRB;
+  constexpr int RH = NRB / SNRB;
   int64_t b, strip;   // strip < 0: solve role
   int part = 0;       // token part of the strip (msplit > 1)
-  if (msplit > 1) {
+  int rh = 0;         // row block of 16 SNRB rows (r > 64)
+  if (msplit > 1 || RH > 1) {
     if (bid < B) {
       b = bid;
       strip = -1;
     } else {
       const int64_t u = bid - B;
-      b = u / (strips * msplit);
-      strip = (u / msplit) % strips;
-      part = (int)(u % msplit);
+      b = u / (strips * msplit * RH);
+      strip = (u / (msplit * RH)) % strips;
+      part = (int)((u / RH) % msplit);
+      rh = (int)(u % RH);
     }
   } else if ((B & 7) == 0) {
     const int64_t x = bid & 7, j = bid >> 3, per = B >> 3;
@@ -2220,15 +2227,15 @@ __global__ __launch_bounds__(S3_NT, NRB <= 4 ? 2 : 1) void s3_reduce_solve_kerne
       constexpr int TB = NB <= 2 ? 4 : 8;
       static_assert(32 * NB * (32 * NB + 1) / 2 * 8 <= S3Lds<NB>::SW_OFF, "packed factor fits");
       int st;
-      double rho;
+      bool wide;
       if constexpr (SOLVE == 2)
         st = chol_inverse<S3_NT, TB>(Gs, Gi + b * r * r, Gi32 + b * r * r, r, eps, *sl,
-                                     reinterpret_cast<double*>(lds), rho);
+                                     reinterpret_cast<double*>(lds), wide);
       else
-        st = sweep_inverse<S3_NT, TB>(Gs, Gi + b * r * r, Gi32 + b * r * r, r, eps, *sl, rho);
+        st = sweep_inverse<S3_NT, TB>(Gs, Gi + b * r * r, Gi32 + b * r * r, r, eps, *sl, wide);
       if (threadIdx.x == 0) {
         status[b] = st;
-        prec[b] = st == DYRA_SOLVE_OK && rho < kWidePivot ? 1 : 0;
+        prec[b] = st == DYRA_SOLVE_OK && wide ? 1 : 0;
       }
     }
     return;
@@ -2248,11 +2255,17 @@ __global__ __launch_bounds__(S3_NT, NRB <= 4 ? 2 : 1) void s3_reduce_solve_kerne
     phi = imin64(hi, plo + chunk);
     Mb = Mpart + ((int64_t)part * B + b) * r * c1;
   }
+  // this role's rows: 16 SNRB rows from row 16 SNRB rh of L^T and M_b
+  const int r0 = rh * 16 * SNRB;
+  const int rr = r - r0 < 16 * SNRB ? r - r0 : 16 * SNRB;
+  if (rr <= 0) return;
+  Ltb += (int64_t)r0 * ldt;
+  Mb += (int64_t)r0 * c1;
   // 32-bit buffer offsets reach every X row of a 32-token step and every
   // L^T row of a step
-  const bool b32 = 32 * c1 * 2 < ((int64_t)1 << 31) && ((int64_t)r * ldt + 64) * 2 < ((int64_t)1 << 31);
-  if (b32) s3_m_strip<NRB, true>(Ltb, ldt, Xb, c1, r, plo, phi, c0, Mb, lds, tbase);
-  else s3_m_strip<NRB, false>(Ltb, ldt, Xb, c1, r, plo, phi, c0, Mb, lds, tbase);
+  const bool b32 = 32 * c1 * 2 < ((int64_t)1 << 31) && ((int64_t)rr * ldt + 64) * 2 < ((int64_t)1 << 31);
+  if (b32) s3_m_strip<SNRB, true>(Ltb, ldt, Xb, c1, rr, plo, phi, c0, Mb, lds, tbase);
+  else s3_m_strip<SNRB, false>(Ltb, ldt, Xb, c1, rr, plo, phi, c0, Mb, lds, tbase);
 }
 
 // M = sum over the msplit token parts of the strips' fp32 partials, in part
@@ -2349,16 +2362,17 @@ __global__ __launch_bounds__(NT) void sweep_inverse_kernel(const float* G, doubl
   // every thread reads the flag before the sweep's first barrier; thread 0
   // rewrites it only after the sweep
   if (only_flagged && status[b] != DYRA_SOLVE_FALLBACK) return;
-  double rho;
-  const int st = sweep_inverse<NT, TB>(G + b * r * r, Ginv + b * r * r, Ginv32 + b * r * r, r, eps, sl, rho);
+  bool wide;
+  const int st = sweep_inverse<NT, TB>(G + b * r * r, Ginv + b * r * r, Ginv32 + b * r * r, r, eps, sl, wide);
   if (threadIdx.x == 0) {
     status[b] = (only_flagged && st == DYRA_SOLVE_OK) ? DYRA_SOLVE_FALLBACK : st;
-    prec[b] = st == DYRA_SOLVE_OK && rho < kWidePivot ? 1 : 0;
+    prec[b] = st == DYRA_SOLVE_OK && wide ? 1 : 0;
   }
 }
 
-// r <= 64: 256 threads of 4 x 4 tiles; r <= 128: 1024 threads of 4 x 4 tiles
-// (four waves per SIMD hide part of the pivot blocks' dependent latency).
+// r <= 64: 256 threads of 4 x 4 tiles; r <= 128: 256 threads of 8 x 8 tiles
+// (one wave per SIMD with the whole register file: 1024 threads of 4 x 4
+// leave 128 registers a lane and the sweep spilled to scratch).
 void launch_sweep(const float* G, double* Ginv, float* Ginv32, int32_t* status, int32_t* prec, int r, float eps,
                   int64_t B, bool only_flagged, hipStream_t st) {
   const int f = only_flagged ? 1 : 0;
@@ -2366,7 +2380,7 @@ void launch_sweep(const float* G, double* Ginv, float* Ginv32, int32_t* status, 
     hipLaunchKernelGGL((sweep_inverse_kernel<256, 4>), dim3((unsigned)B), dim3(256), 0, st, G, Ginv, Ginv32, status, prec,
                        r, eps, f);
   else
-    hipLaunchKernelGGL((sweep_inverse_kernel<1024, 4>), dim3((unsigned)B), dim3(1024), 0, st, G, Ginv, Ginv32, status,
+    hipLaunchKernelGGL((sweep_inverse_kernel<256, 8>), dim3((unsigned)B), dim3(256), 0, st, G, Ginv, Ginv32, status,
                        prec, r, eps, f);
 }
 
@@ -2378,11 +2392,11 @@ __global__ __launch_bounds__(NT) void chol_inverse_kernel(const float* G, double
   __shared__ SweepLds sl;
   __shared__ double cp[RMAX * (RMAX + 1) / 2];
   const int64_t b = blockIdx.x;
-  double rho;
-  const int st = chol_inverse<NT, TB>(G + b * r * r, Ginv + b * r * r, Ginv32 + b * r * r, r, eps, sl, cp, rho);
+  bool wide;
+  const int st = chol_inverse<NT, TB>(G + b * r * r, Ginv + b * r * r, Ginv32 + b * r * r, r, eps, sl, cp, wide);
   if (threadIdx.x == 0) {
     status[b] = st;
-    prec[b] = st == DYRA_SOLVE_OK && rho < kWidePivot ? 1 : 0;
+    prec[b] = st == DYRA_SOLVE_OK && wide ? 1 : 0;
   }
 }
 
@@ -2624,10 +2638,14 @@ __global__ __launch_bounds__(512) void ns_inverse_kernel(const float* G, float* 
 constexpr int NS_N = 128;
 constexpr int NS_P = 129;   // padded LDS pitch (odd: row-strided reads spread over banks)
 
-__global__ __launch_bounds__(1024) void ns_polish_kernel(const float* G, const float* Xit, double* Ginv,
-                                                         float* Ginv32, int32_t* status, int32_t* prec, int r,
-                                                         float eps,
-                                                         int maxit, float tol, float accept) {
+// Eight waves: wave (bi, bh) owns rows 32 bi .. + 31 and the two 32-column
+// blocks 64 bh .. + 63 of each product (A' row fragments in registers, 64
+// floats a lane; with 16 waves of one block each a lane had 128 registers
+// and the kernel spilled to scratch).
+__global__ __launch_bounds__(512) void ns_polish_kernel(const float* G, const float* Xit, double* Ginv,
+                                                        float* Ginv32, int32_t* status, int32_t* prec, int r,
+                                                        float eps, int maxit, float tol, float accept) {
+  constexpr int NTH = 512;
   __shared__ float Xs[NS_N * NS_P];
   __shared__ float Ts[NS_N * NS_P];
   __shared__ float dsc[NS_N];
@@ -2636,14 +2654,14 @@ __global__ __launch_bounds__(1024) void ns_polish_kernel(const float* G, const f
   const float* Gb = G + b * r * r;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l = lane & 31, g = lane >> 5;
-  const int bi = w >> 2, bj = w & 3;
+  const int bi = w >> 1, bh = w & 1;
   // every thread reads the status before the first barrier; thread 0
   // rewrites it only at the end
   if (status[b] != DYRA_SOLVE_OK) return;
 
   // trace, ridge and Jacobi scaling
   const float dv = tid < r ? Gb[tid * r + tid] : 0.f;
-  const float tr = block_sum<1024>(dv, red);
+  const float tr = block_sum<NTH>(dv, red);
   const float lam = eps * tr / (float)r;
   float badf = 0.f;
   if (tid < NS_N) {
@@ -2651,13 +2669,12 @@ __global__ __launch_bounds__(1024) void ns_polish_kernel(const float* G, const f
     dsc[tid] = d > 0.f ? rsqrtf(d) : 0.f;
     if (!(d > 0.f) || !isfinite(d)) badf = 1.f;
   }
-  badf = block_sum<1024>(badf, red);   // barrier: dsc complete afterwards
+  badf = block_sum<NTH>(badf, red);   // barrier: dsc complete afterwards
   int st = DYRA_SOLVE_OK;
   if (tr == 0.f) st = DYRA_SOLVE_ZERO;
   else if (!(tr > 0.f) || !isfinite(tr) || badf > 0.f) st = DYRA_SOLVE_NOT_SPD;
   // A' fragments in registers: Af[s] = A'[bi*32 + l][2s + g]
   float Af[64];
-  float fro2 = 0.f;
 #pragma unroll
   for (int s = 0; s < 64; ++s) {
     const int row = bi * 32 + l, col = 2 * s + g;
@@ -2665,14 +2682,11 @@ __global__ __launch_bounds__(1024) void ns_polish_kernel(const float* G, const f
     if (row < r && col < r) v = (Gb[row * r + col] + (row == col ? lam : 0.f)) * dsc[row] * dsc[col];
     else v = row == col ? 1.f : 0.f;
     Af[s] = v;
-    if (bj == 0) fro2 += v * v;   // waves with bj == 0 cover every row band once
   }
-  fro2 = block_sum<1024>(fro2, red);
-  (void)fro2;
   // X_0: the split-precision iterate (A' space), padded with the identity
-  for (int e = tid; e < NS_N * NS_N; e += 1024) {
-    const int i = e / NS_N, j = e % NS_N;
-    Xs[i * NS_P + j] = i < r && j < r ? Xit[b * r * r + i * r + j] : (i == j ? 1.f : 0.f);
+  for (int e = tid; e < NS_N * NS_N; e += NTH) {
+    const int i = e / NS_N, jj = e % NS_N;
+    Xs[i * NS_P + jj] = i < r && jj < r ? Xit[b * r * r + i * r + jj] : (i == jj ? 1.f : 0.f);
   }
   __syncthreads();
   float prev = 1e30f;
@@ -2680,24 +2694,30 @@ __global__ __launch_bounds__(1024) void ns_polish_kernel(const float* G, const f
   bool ok = st == DYRA_SOLVE_OK;
   bool converged = false;
   while (ok && it < maxit) {
-    // T = A' X  (this wave's block)
-    f32x16 acc;
+    // T = A' X  (this wave's two blocks)
+    f32x16 acc[2];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int s = 0; s < 64; ++s) {
-      const float bx = Xs[(2 * s + g) * NS_P + bj * 32 + l];
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(Af[s], bx, acc, 0, 0, 0);
-    }
+      for (int v = 0; v < 16; ++v) acc[j][v] = 0.f;
+#pragma unroll
+    for (int s = 0; s < 64; ++s)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float bx = Xs[(2 * s + g) * NS_P + bh * 64 + 32 * j + l];
+        acc[j] = __builtin_amdgcn_mfma_f32_32x32x2f32(Af[s], bx, acc[j], 0, 0, 0);
+      }
     float e2 = 0.f;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int rr = bi * 32 + (v >> 2) * 8 + g * 4 + (v & 3), cc = bj * 32 + l;
-      Ts[rr * NS_P + cc] = acc[v];
-      const float d = (rr == cc ? 1.f : 0.f) - acc[v];
-      e2 += d * d;
-    }
-    e2 = block_sum<1024>(e2, red);   // contains barriers: Ts complete afterwards
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int rr = bi * 32 + (v >> 2) * 8 + g * 4 + (v & 3), cc = bh * 64 + 32 * j + l;
+        Ts[rr * NS_P + cc] = acc[j][v];
+        const float d = (rr == cc ? 1.f : 0.f) - acc[j][v];
+        e2 += d * d;
+      }
+    e2 = block_sum<NTH>(e2, red);   // contains barriers: Ts complete afterwards
     const float err = sqrtf(e2);
     if (!isfinite(err)) {
       ok = false;
@@ -2713,27 +2733,29 @@ __global__ __launch_bounds__(1024) void ns_polish_kernel(const float* G, const f
     }
     prev = err;
     // X <- 2 X - X T
-    f32x16 acc2;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) acc2[v] = 0.f;
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[j][v] = 0.f;
 #pragma unroll
     for (int s = 0; s < 64; ++s) {
       const float ax = Xs[(bi * 32 + l) * NS_P + 2 * s + g];
-      const float bt = Ts[(2 * s + g) * NS_P + bj * 32 + l];
-      acc2 = __builtin_amdgcn_mfma_f32_32x32x2f32(ax, bt, acc2, 0, 0, 0);
-    }
-    float xo[16];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int rr = bi * 32 + (v >> 2) * 8 + g * 4 + (v & 3), cc = bj * 32 + l;
-      xo[v] = Xs[rr * NS_P + cc];
+      for (int j = 0; j < 2; ++j) {
+        const float bt = Ts[(2 * s + g) * NS_P + bh * 64 + 32 * j + l];
+        acc[j] = __builtin_amdgcn_mfma_f32_32x32x2f32(ax, bt, acc[j], 0, 0, 0);
+      }
     }
+    // every wave is done reading X; each then rewrites its own blocks (which
+    // no other wave writes, so their old values can be read after the barrier)
     __syncthreads();
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int rr = bi * 32 + (v >> 2) * 8 + g * 4 + (v & 3), cc = bj * 32 + l;
-      Xs[rr * NS_P + cc] = 2.f * xo[v] - acc2[v];
-    }
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int rr = bi * 32 + (v >> 2) * 8 + g * 4 + (v & 3), cc = bh * 64 + 32 * j + l;
+        Xs[rr * NS_P + cc] = 2.f * Xs[rr * NS_P + cc] - acc[j][v];
+      }
     __syncthreads();
     ++it;
   }
@@ -2745,9 +2767,9 @@ __global__ __launch_bounds__(1024) void ns_polish_kernel(const float* G, const f
     return;
   }
   const bool good = st == DYRA_SOLVE_OK;
-  for (int e = tid; e < r * r; e += 1024) {
-    const int i = e / r, j = e % r;
-    const double v = good ? (double)dsc[i] * (double)Xs[i * NS_P + j] * (double)dsc[j] : 0.0;
+  for (int e = tid; e < r * r; e += NTH) {
+    const int i = e / r, jj = e % r;
+    const double v = good ? (double)dsc[i] * (double)Xs[i * NS_P + jj] * (double)dsc[jj] : 0.0;
     Ginv[b * r * r + e] = v;
     Ginv32[b * r * r + e] = (float)v;
   }
@@ -3148,7 +3170,9 @@ void launch_s3_bf16(const bf16_t* Lt, int64_t ldt, const bf16_t* X, int64_t c1, 
     hipLaunchKernelGGL((gram_partial_kernel<NB>), dim3((unsigned)(B * gchunks)), dim3(64), 0, st, Lt, ldt, r,
                        sg, n, gchunks, gchunk, gpart);
   auto go = [&](auto kern) {
-    hipLaunchKernelGGL(kern, dim3((unsigned)(B + B * strips * msplit)), dim3(S3_NT), 0, st, Lt, ldt, X, c1, r, sg, n,
+    constexpr int RH = NRB > 4 ? NRB / 4 : 1;   // row blocks per strip (the kernel's SNRB split)
+    hipLaunchKernelGGL(kern, dim3((unsigned)(B + B * strips * msplit * RH)), dim3(S3_NT), 0, st, Lt, ldt, X, c1, r,
+                       sg, n,
                        B, M, G, Gi, Gi32, stat, prec, eps, strips, lt_seg_rows, x_rel ? 1 : 0, gpart, gchunks,
                        gprows, msplit, Mpart);
   };
@@ -3233,10 +3257,8 @@ void forward_residual(const dyra_spec& s, const char* plan, const void* X, const
       // ill-conditioned G still gives an fp32-accurate inverse)
       const float tol = BF ? 1e-4f : 2e-6f, accept = BF ? 1e-2f : 1e-5f;
       hipLaunchKernelGGL(ns_inverse_kernel, dim3((unsigned)B), dim3(512), 0, st, G, Xit, stat, r, eps, 40, tol);
-      hipLaunchKernelGGL(ns_polish_kernel, dim3((unsigned)B), dim3(1024), 0, st, G, Xit, Gi, Gi32, stat, prec, r, eps,
-                         60,
-                         tol,
-                         accept);
+      hipLaunchKernelGGL(ns_polish_kernel, dim3((unsigned)B), dim3(512), 0, st, G, Xit, Gi, Gi32, stat, prec, r, eps,
+                         60, tol, accept);
       launch_sweep(G, Gi, Gi32, stat, prec, r, eps, B, true, st);
     } else if (solver == DYRA_SOLVER_CHOL) {
       launch_chol(G, Gi, Gi32, stat, prec, r, eps, B, st);
