@@ -82,9 +82,9 @@ def STRUCT_TEXT(w):
 
 OUTPUT_KERNEL = {0: "s6_lowrank_kernel (fused T V + L R_b + bias)",
                  "0bf16": "s6_lowrank_ws_kernel (persistent, wave-specialised T V + L R_b + bias)",
-                 1: "s6_monarch_kernel (stage 2 + L R_b + bias)",
-                 2: "s6_blast_kernel (W'_j V_j^T + L R_b + bias)",
-                 3: "s6_blast_kernel (W'_j V_j^T + L R_b + bias)"}
+                 1: "s6_monarch_fused_kernel (stage 1 recomputed from X, V_j B2_j + L R_b + bias)",
+                 2: "s6_lowrank_ws_kernel (persistent: W'_j V_j^T + L R_b + bias)",
+                 3: "s6_lowrank_ws_kernel (persistent: W'_j V_j^T + L R_b + bias)"}
 
 
 def kernel_source_hash():
