@@ -18,6 +18,7 @@
 
 #include <climits>
 #include <cmath>
+#include <atomic>
 #include <mutex>
 #include <type_traits>
 
@@ -3087,16 +3088,18 @@ bool s6_ws_fits(int64_t n, int64_t c2, int k, int r, int64_t B, int64_t lda_el =
          ldy * CfgB6W::BM < ((int64_t)1 << 30) && tiles < ((int64_t)1 << 30);
 }
 
+// Compute units of the current device, queried once per device (calls from
+// several host threads may query it concurrently; they store the same value).
 int device_cus() {
-  static int cus[64] = {0};
+  static std::atomic<int> cus[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cus[dev] == 0) {
-    int v = 0;
+  int v = cus[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cus[dev] = v;
+    cus[dev].store(v, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return v;
 }
 
 // A0 / lda0_el / acolb and A1 / lda1_el: the two A operands (element
