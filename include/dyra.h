@@ -207,9 +207,9 @@ int dyra_workspace_size(const dyra_spec* spec, int64_t B, int64_t s, int32_t dty
  *   Mp     [B][r][c1]   dtype Ginv_b M_b
  *   Rt     [c2][B r]    dtype R_b^T, R_b = Mp_b W_res
  *   status [B]          int32 solver status words
- *   prec   [B]          int32 1 where Mp_b was formed in fp64 (the solve met
- *                       a relative pivot below 2^-5, or Newton-Schulz
- *                       solved it), 0 where in fp32
+ *   prec   [B]          int32 1 where Mp_b was formed in fp64 (the sweep or
+ *                       Cholesky solve met a relative pivot below 2^-5),
+ *                       0 where in fp32 (Newton-Schulz inverses included)
  * Errors: EINVAL, ESHAPE, EDTYPE.
  */
 typedef struct {

@@ -2536,10 +2536,22 @@ __global__ __launch_bounds__(512) void ns_inverse_kernel(const float* G, float* 
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, al), __builtin_bit_cast(bf16x8_t, bh), acc, 0, 0, 0);
     return acc;
   };
+  auto frag_hi = [&](const char (*S)[NSS_N * 256], int row, int ks) {
+    return *reinterpret_cast<const uint4*>(S[0] + row * 256 + ((((2 * ks + g)) ^ row) & 15) * 16);
+  };
+  auto mm1 = [&](f32x16 acc, uint4 ah, uint4 bh) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ah), __builtin_bit_cast(bf16x8_t, bh),
+                                                   acc, 0, 0, 0);
+  };
   float prev = 1e30f;
   int it = 0;
   bool ok = st == DYRA_SOLVE_OK;
   bool converged = false;
+  // Far from the inverse the iteration corrects its own rounding, so while
+  // ||I - A'X||_F > 1/4 the products take the hi parts only (one MFMA
+  // instead of three); split precision from there on, or as soon as a
+  // coarse step fails to reduce the error.
+  bool coarse = true;
   while (ok && it < maxit) {
     // T = A' X (this wave's two blocks); X column cc is stored as row cc
     f32x16 acc[2];
@@ -2547,14 +2559,21 @@ __global__ __launch_bounds__(512) void ns_inverse_kernel(const float* G, float* 
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[j][v] = 0.f;
+    if (coarse) {
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
+      for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        uint4 bh, bl;
-        frag(XS, bh2 * 64 + 32 * j + l, ks, bh, bl);
-        acc[j] = mm3(acc[j], Ahi[ks], Alo[ks], bh, bl);
-      }
+        for (int j = 0; j < 2; ++j) acc[j] = mm1(acc[j], Ahi[ks], frag_hi(XS, bh2 * 64 + 32 * j + l, ks));
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          uint4 bh, bl;
+          frag(XS, bh2 * 64 + 32 * j + l, ks, bh, bl);
+          acc[j] = mm3(acc[j], Ahi[ks], Alo[ks], bh, bl);
+        }
+    }
     float e2 = 0.f;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -2576,26 +2595,44 @@ __global__ __launch_bounds__(512) void ns_inverse_kernel(const float* G, float* 
       break;
     }
     // hand over to the fp32 polish at the tolerance or as soon as split
-    // precision stops reducing the error
-    if (err <= tol || err >= prev) {
+    // precision stops reducing the error (a coarse step that stops reducing
+    // it switches to split precision instead)
+    if (err <= tol) {
       converged = true;
       break;
     }
+    if (err >= prev) {
+      if (!coarse) {
+        converged = true;
+        break;
+      }
+      coarse = false;
+    }
+    if (err < 0.25f) coarse = false;
     prev = err;
     // X <- 2 X - X T: X row bi 32 + l (X symmetric: its stored row), T column cc
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[j][v] = 0.f;
+    if (coarse) {
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      uint4 ah, al;
-      frag(XS, arow, ks, ah, al);
+      for (int ks = 0; ks < 8; ++ks) {
+        const uint4 ah = frag_hi(XS, arow, ks);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        uint4 bh, bl;
-        frag(TS, bh2 * 64 + 32 * j + l, ks, bh, bl);
-        acc[j] = mm3(acc[j], ah, al, bh, bl);
+        for (int j = 0; j < 2; ++j) acc[j] = mm1(acc[j], ah, frag_hi(TS, bh2 * 64 + 32 * j + l, ks));
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        uint4 ah, al;
+        frag(XS, arow, ks, ah, al);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          uint4 bh, bl;
+          frag(TS, bh2 * 64 + 32 * j + l, ks, bh, bl);
+          acc[j] = mm3(acc[j], ah, al, bh, bl);
+        }
       }
     }
     float xo[2][16];
@@ -2776,7 +2813,9 @@ __global__ __launch_bounds__(512) void ns_polish_kernel(const float* G, const fl
   }
   if (tid == 0) {
     status[b] = st;
-    prec[b] = 1;   // no pivots to judge the conditioning by: the fp64 apply
+    // the fp32 apply: the iteration's own tolerance, not the apply's
+    // rounding, bounds the accuracy of M' for a Newton-Schulz inverse
+    prec[b] = 0;
   }
 }
 
