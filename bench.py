@@ -260,7 +260,7 @@ def main():
     # timed region 2: the same K steps with HIP events recorded between the
     # stages on the launch stream (per-stage times and the roofline kernel time)
     # -- for the t = 1 forward, whose stage boundaries the events mark
-    ms_events, stage_ms = None, None
+    ms_events, stage_ms, step_pct = None, None, None
     if not als:
         start.record(stream)
         for i in range(K):
@@ -270,6 +270,9 @@ def main():
         ms_events = start.elapsed_time(end) / K
         stage_ms = {STAGES[j]: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(K)]))
                     for j in range(5)}
+        # per-step spread of the same pass (first to last stage event)
+        steps = np.array([ev[i][0].elapsed_time(ev[i][5]) for i in range(K)])
+        step_pct = {f"p{q}": round(float(np.percentile(steps, q)), 5) for q in (10, 50, 90)}
     status = layer.status(w.B, w.s)
 
     work = stage_work(w)
@@ -366,6 +369,7 @@ def main():
         "ms_per_step": round(ms, 5),
         "ms_per_step_eager": round(ms_eager, 5),
         "ms_per_step_with_stage_events": None if ms_events is None else round(ms_events, 5),
+        "step_ms_with_stage_events": step_pct,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
