@@ -1455,20 +1455,21 @@ __device__ __forceinline__ double recip_pos(double D) {
 // eps = 1e-6), past what fp32 elimination survives.  Needs r % SW_BK == 0,
 // r <= 128 and ceil(r / TB)^2 <= NT.  Returns the status (same in every
 // thread).
-template <int NT, int TB>
+template <int NT, int TB, int TBJ = TB>
 __device__ __forceinline__ int sweep_inverse(const float* Gb, double* Ob, float* Ob32, int r, float eps,
                                              SweepLds& sh, bool& wide) {
-  static_assert(TB % SW_BK == 0 && TB % 2 == 0, "tile");
+  // thread tiles of TB rows x TBJ columns
+  static_assert(TB % SW_BK == 0 && TB % 2 == 0 && TBJ % SW_BK == 0 && TBJ % 2 == 0, "tile");
   const int tid = threadIdx.x;
-  const int tpr = (r + TB - 1) / TB;
-  const int i0 = (tid / tpr) * TB, j0 = (tid % tpr) * TB;
+  const int tpr = (r + TBJ - 1) / TBJ;
+  const int i0 = (tid / tpr) * TB, j0 = (tid % tpr) * TBJ;
   const bool own = i0 < r;
-  double a[TB][TB];
+  double a[TB][TBJ];
   float trf = 0.f;
 #pragma unroll
   for (int x = 0; x < TB; ++x)
 #pragma unroll
-    for (int y = 0; y < TB; ++y) {
+    for (int y = 0; y < TBJ; ++y) {
       const bool v = own && i0 + x < r && j0 + y < r;
       const float g = v ? Gb[(i0 + x) * r + j0 + y] : 0.f;
       a[x][y] = g;
@@ -1486,7 +1487,7 @@ __device__ __forceinline__ int sweep_inverse(const float* Gb, double* Ob, float*
     const int i = i0 + x;
     if (own && i >= k0 && i < k0 + SW_BK) {
 #pragma unroll
-      for (int y = 0; y < TB; y += 2)
+      for (int y = 0; y < TBJ; y += 2)
         if (j0 + y < r)
           *reinterpret_cast<double2*>(&sh.pv[buf][i - k0][j0 + y]) = make_double2(a[x][y], a[x][y + 1]);
     }
@@ -1497,7 +1498,7 @@ __device__ __forceinline__ int sweep_inverse(const float* Gb, double* Ob, float*
 #pragma unroll
     for (int x = 0; x < TB; ++x)
 #pragma unroll
-      for (int y = 0; y < TB; ++y)
+      for (int y = 0; y < TBJ; ++y)
         if (own && x + i0 == y + j0) a[x][y] += lam;
 #pragma unroll
     for (int x = 0; x < TB; ++x) publish_row(x, 0, 0);
@@ -1540,11 +1541,11 @@ __device__ __forceinline__ int sweep_inverse(const float* Gb, double* Ob, float*
       // (a multiple of SW_BK) when this tile holds them
       const int oi = kb - i0, oj = kb - j0;
       // C_j = pivot rows at this tile's columns
-      double cj[SW_BK][TB];
+      double cj[SW_BK][TBJ];
 #pragma unroll
       for (int p = 0; p < SW_BK; ++p)
 #pragma unroll
-        for (int y = 0; y < TB; y += 2) {
+        for (int y = 0; y < TBJ; y += 2) {
           const double2 v = *reinterpret_cast<const double2*>(&buf[p][j0 + y]);
           cj[p][y] = v.x;
           cj[p][y + 1] = v.y;
@@ -1573,7 +1574,7 @@ __device__ __forceinline__ int sweep_inverse(const float* Gb, double* Ob, float*
             d[p] = iK ? Q[xx & (SW_BK - 1)][p] : -v;
           }
 #pragma unroll
-          for (int y = 0; y < TB; ++y) {
+          for (int y = 0; y < TBJ; ++y) {
             const bool jK = oj == (y & ~(SW_BK - 1));
             double v = iK ? 0.0 : a[xx][y];
 #pragma unroll
@@ -1590,7 +1591,7 @@ __device__ __forceinline__ int sweep_inverse(const float* Gb, double* Ob, float*
 #pragma unroll
   for (int x = 0; x < TB; ++x)
 #pragma unroll
-    for (int y = 0; y < TB; ++y)
+    for (int y = 0; y < TBJ; ++y)
       if (own && i0 + x < r && j0 + y < r) {
         const double v = st == DYRA_SOLVE_OK ? -a[x][y] : 0.0;
         Ob[(i0 + x) * r + j0 + y] = v;
@@ -2354,7 +2355,7 @@ __global__ __launch_bounds__(64) void gram_partial_kernel(const bf16_t* __restri
 // only_flagged, segments whose status is not DYRA_SOLVE_FALLBACK are left
 // alone: the Newton-Schulz kernel flags the segments it could not solve, and
 // those keep the FALLBACK status when the sweep succeeds.
-template <int NT, int TB>
+template <int NT, int TB, int TBJ = TB>
 __global__ __launch_bounds__(NT) void sweep_inverse_kernel(const float* G, double* Ginv, float* Ginv32,
                                                            int32_t* status, int32_t* prec, int r, float eps,
                                                            int only_flagged) {
@@ -2364,7 +2365,7 @@ __global__ __launch_bounds__(NT) void sweep_inverse_kernel(const float* G, doubl
   // rewrites it only after the sweep
   if (only_flagged && status[b] != DYRA_SOLVE_FALLBACK) return;
   bool wide;
-  const int st = sweep_inverse<NT, TB>(G + b * r * r, Ginv + b * r * r, Ginv32 + b * r * r, r, eps, sl, wide);
+  const int st = sweep_inverse<NT, TB, TBJ>(G + b * r * r, Ginv + b * r * r, Ginv32 + b * r * r, r, eps, sl, wide);
   if (threadIdx.x == 0) {
     status[b] = (only_flagged && st == DYRA_SOLVE_OK) ? DYRA_SOLVE_FALLBACK : st;
     prec[b] = st == DYRA_SOLVE_OK && wide ? 1 : 0;
@@ -2381,7 +2382,7 @@ void launch_sweep(const float* G, double* Ginv, float* Ginv32, int32_t* status, 
     hipLaunchKernelGGL((sweep_inverse_kernel<256, 4>), dim3((unsigned)B), dim3(256), 0, st, G, Ginv, Ginv32, status, prec,
                        r, eps, f);
   else
-    hipLaunchKernelGGL((sweep_inverse_kernel<256, 8>), dim3((unsigned)B), dim3(256), 0, st, G, Ginv, Ginv32, status,
+    hipLaunchKernelGGL((sweep_inverse_kernel<512, 4, 8>), dim3((unsigned)B), dim3(512), 0, st, G, Ginv, Ginv32, status,
                        prec, r, eps, f);
 }
 
@@ -3262,10 +3263,10 @@ void forward_residual(const dyra_spec& s, const char* plan, const void* X, const
   // stays selectable.
   const bool ns = solver == DYRA_SOLVER_NS;
   // solve inside the token-reduction launch: 1 the sweep, 2 the Cholesky
-  // route, 0 none (Newton-Schulz runs after it).  The sweep stays inside
-  // at r = 128 too: the separate 1024-thread sweep launch took as long
-  // (145 against 141 us for one LM BLAST solve) and lost the overlap with
-  // the strips.
+  // route, 0 none (Newton-Schulz runs after it).  At r = 128 a separate
+  // 512-thread sweep launch is faster on its own (110 us against the
+  // launch's 256-thread solve role) but the forward is slower, since the
+  // solve role overlaps the strips of the other segments.
   const int mode = ns ? 0 : (solver == DYRA_SOLVER_CHOL ? 2 : 1);
   // S3: M_b, G_b (bf16: with the sweep solve in the same launch)
   bool solved = false;
