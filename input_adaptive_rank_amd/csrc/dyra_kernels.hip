@@ -2372,8 +2372,8 @@ __global__ __launch_bounds__(NT) void sweep_inverse_kernel(const float* G, doubl
   }
 }
 
-// r <= 64: 256 threads of 4 x 4 tiles; r <= 128: 256 threads of 8 x 8 tiles
-// (one wave per SIMD with the whole register file: 1024 threads of 4 x 4
+// r <= 64: 256 threads of 4 x 4 tiles; r <= 128: 512 threads of 4 x 8
+// tiles (two waves per SIMD, 212 registers a lane; 1024 threads of 4 x 4
 // leave 128 registers a lane and the sweep spilled to scratch).
 void launch_sweep(const float* G, double* Ginv, float* Ginv32, int32_t* status, int32_t* prec, int r, float eps,
                   int64_t B, bool only_flagged, hipStream_t st) {
@@ -2413,37 +2413,56 @@ void launch_chol(const float* G, double* Ginv, float* Ginv32, int32_t* status, i
 }
 
 // ===========================================================================
-// S4a': Newton-Schulz inverse (one workgroup of 8 waves per segment; wave
+// S4a': Newton-Schulz inverse, one workgroup of 8 waves per segment; wave
 // (bi, h) owns rows 32 bi .. + 31 and columns 64 h .. + 63 of the 128 x 128
-// iterate).  Jacobi-scaled A' = D^-1/2 (G + lambda I) D^-1/2 (unit
-// diagonal, padded with the identity up to 128); X_0 = I / ||A'||_F;
-// X_{k+1} = X_k (2 I - A' X_k) until ||I - A' X_k||_F <= tol or the error
-// stops decreasing; the fp32 polish below finishes it (Ginv = D^-1/2 X
-// D^-1/2).  The products run on bf16 MFMAs in split
-// precision: each operand is held as hi + lo bf16 (about 16 significant
-// bits) and P Q is formed as Phi Qhi + Phi Qlo + Plo Qhi with fp32
-// accumulation, three bf16 MFMAs where an fp32 MFMA product would cost
-// sixteen at gfx950's rates.  X and T = A' X stay in LDS as hi / lo bf16,
-// stored transposed (row c holds column c) so that every MFMA operand is one
-// 16-byte row read; X_k is a polynomial in A', hence symmetric, so its
-// stored rows also serve as the rows of X in X T.  Split precision leaves a
-// floor near 1e-5 relative (higher for ill-conditioned A'), so this phase
-// hands X over once ||I - A' X||_F reaches the tolerance or stops
-// decreasing, and writes it (A' space) to Ginv for the polish.
+// iterate.  Jacobi-scaled A' = D^-1/2 (G + lambda I) D^-1/2 (unit diagonal,
+// padded with the identity up to 128), X_0 = I / ||A'||_F, and the
+// Newton-Schulz step X <- X (2 I - A' X) = X + X E with E = I - A' X, until
+// ||E||_F <= tol; then Ginv = D^-1/2 X D^-1/2.  Every product runs on bf16
+// MFMAs with fp32 accumulation, in two phases:
+//   * coarse, while far from the inverse (the iteration corrects its own
+//     rounding there): T = A' X and X T from the bf16 parts alone, one MFMA
+//     each, X <- 2 X - X T;
+//   * fine, from the first coarse step that fails to reduce ||E||_F, or
+//     once it is below 1/4: A' and X are held as three bf16 terms each
+//     (hi + mid + lo, about 24 significant bits, as fp32) and A' X is
+//     formed from the six products whose terms reach 2^-24 relative, so the
+//     residual E = I - A' X is as accurate as an fp32 product would make it,
+//     while an fp32 MFMA product would cost sixteen MFMAs at gfx950's rates
+//     against these six.  The correction X E takes X's three terms and E
+//     rounded to bf16: rounding X would add about 2^-9 cond(A') ||E|| to
+//     the next residual (A' amplifies it), rounding E only about 2^-9 ||E||
+//     (A' X is close to I), which slows the quadratic convergence by no more
+//     than that factor per step.
+// X and E (T in the coarse phase) stay in LDS, stored transposed (row c
+// holds column c) so that every MFMA operand is one 16-byte row read; X is
+// a polynomial in A', hence symmetric, so its stored rows also serve as its
+// rows in X E.  The iteration stops at the tolerance, or flags the segment
+// for the sweep when a fine step stops reducing ||E||_F (its rounding floor)
+// above `accept`; from ||E||_F <= accept / 4 one more step leaves about its
+// square and is taken without another residual.
 // ===========================================================================
 
 constexpr int NSS_N = 128;
 __device__ __forceinline__ int nss_off(int row, int k) {   // bf16 element (row, k), 16-byte chunks swizzled
   return row * 256 + ((((k >> 3) ^ row) & 15) << 4) + ((k & 7) << 1);
 }
-__device__ __forceinline__ void split_bf16(float x, uint16_t& h, uint16_t& l) {
+// x = h + m + l (bf16 terms; each difference is exact in fp32)
+__device__ __forceinline__ void split3_bf16(float x, uint16_t& h, uint16_t& m, uint16_t& l) {
   h = f2bf(x);
-  l = f2bf(x - bf2f(h));
+  const float r1 = x - bf2f(h);
+  m = f2bf(r1);
+  l = f2bf(r1 - bf2f(m));
 }
-__global__ __launch_bounds__(512) void ns_inverse_kernel(const float* G, float* Xit, int32_t* status, int r, float eps,
-                                                          int maxit, float tol) {
-  __shared__ __attribute__((aligned(16))) char XS[2][NSS_N * 256];   // X hi / lo, stored transposed
-  __shared__ __attribute__((aligned(16))) char TS[2][NSS_N * 256];   // T hi / lo, stored transposed
+__device__ __forceinline__ uint4 pack8_b16(const uint16_t (&v)[8]) {
+  return make_uint4(v[0] | (uint32_t)v[1] << 16, v[2] | (uint32_t)v[3] << 16, v[4] | (uint32_t)v[5] << 16,
+                    v[6] | (uint32_t)v[7] << 16);
+}
+__global__ __launch_bounds__(512) void ns_inverse_kernel(const float* G, double* Ginv, float* Ginv32, int32_t* status,
+                                                          int32_t* prec, int r, float eps, int maxit, float tol,
+                                                          float accept) {
+  __shared__ __attribute__((aligned(16))) char XS[3][NSS_N * 256];   // X hi / mid / lo, stored transposed
+  __shared__ __attribute__((aligned(16))) char TS[NSS_N * 256];      // T (coarse) or E (fine), bf16, transposed
   __shared__ float dsc[NSS_N];
   __shared__ float red[16];
   const int64_t b = blockIdx.x;
@@ -2464,14 +2483,13 @@ __global__ __launch_bounds__(512) void ns_inverse_kernel(const float* G, float* 
   int st = DYRA_SOLVE_OK;
   if (tr == 0.f) st = DYRA_SOLVE_ZERO;
   else if (!(tr > 0.f) || !isfinite(tr) || badf > 0.f) st = DYRA_SOLVE_NOT_SPD;
-  // A' = D^-1/2 (G + lambda I) D^-1/2, padded with I: fragments of rows
-  // bi 32 + l, k = 16 ks + 8 g .. + 7, split into bf16 hi / lo
-  uint4 Ahi[8], Alo[8];
+  // A' fragments of rows bi 32 + l, k = 16 ks + 8 g .. + 7, as three bf16 terms
+  uint4 Ah[8], Am[8], Al[8];
   float fro2 = 0.f;
   const int arow = bi * 32 + l;
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
-    uint16_t h[8], lo[8];
+    uint16_t h[8], m[8], lo[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int col = 16 * ks + 8 * g + e;
@@ -2479,39 +2497,51 @@ __global__ __launch_bounds__(512) void ns_inverse_kernel(const float* G, float* 
       if (arow < r && col < r) v = (Gb[arow * r + col] + (arow == col ? lam : 0.f)) * dsc[arow] * dsc[col];
       else v = arow == col ? 1.f : 0.f;
       if (bh2 == 0) fro2 += v * v;
-      split_bf16(v, h[e], lo[e]);
+      split3_bf16(v, h[e], m[e], lo[e]);
     }
-    Ahi[ks] = make_uint4(h[0] | (uint32_t)h[1] << 16, h[2] | (uint32_t)h[3] << 16, h[4] | (uint32_t)h[5] << 16, h[6] | (uint32_t)h[7] << 16);
-    Alo[ks] = make_uint4(lo[0] | (uint32_t)lo[1] << 16, lo[2] | (uint32_t)lo[3] << 16, lo[4] | (uint32_t)lo[5] << 16, lo[6] | (uint32_t)lo[7] << 16);
+    Ah[ks] = pack8_b16(h);
+    Am[ks] = pack8_b16(m);
+    Al[ks] = pack8_b16(lo);
   }
   fro2 = block_sum<512>(fro2, red);
   const float x0 = 1.f / sqrtf(fro2);
   // this wave's block: accumulator element v of lane (l, g) is (rr, cc) with
   // rr = bi 32 + 8 (v / 4) + 4 g + v % 4, cc = bj 32 + l; stored at row cc,
   // k = rr (four consecutive v at one 8-byte place)
-  auto store_blk = [&](char (*S)[NSS_N * 256], int cc, const float (&x)[16]) {
+  auto store_x = [&](int cc, const float (&x)[16]) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      uint16_t h[4], lo[4];
+      uint16_t h[4], m[4], lo[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) split_bf16(x[4 * q + e], h[e], lo[e]);
+      for (int e = 0; e < 4; ++e) split3_bf16(x[4 * q + e], h[e], m[e], lo[e]);
       const int off = nss_off(cc, bi * 32 + 8 * q + 4 * g);
-      *reinterpret_cast<uint2*>(S[0] + off) = make_uint2(h[0] | (uint32_t)h[1] << 16, h[2] | (uint32_t)h[3] << 16);
-      *reinterpret_cast<uint2*>(S[1] + off) = make_uint2(lo[0] | (uint32_t)lo[1] << 16, lo[2] | (uint32_t)lo[3] << 16);
+      *reinterpret_cast<uint2*>(XS[0] + off) = make_uint2(h[0] | (uint32_t)h[1] << 16, h[2] | (uint32_t)h[3] << 16);
+      *reinterpret_cast<uint2*>(XS[1] + off) = make_uint2(m[0] | (uint32_t)m[1] << 16, m[2] | (uint32_t)m[3] << 16);
+      *reinterpret_cast<uint2*>(XS[2] + off) = make_uint2(lo[0] | (uint32_t)lo[1] << 16, lo[2] | (uint32_t)lo[3] << 16);
     }
   };
-  auto load_blk = [&](char (*S)[NSS_N * 256], int cc, float (&x)[16]) {
+  auto load_x = [&](int cc, float (&x)[16]) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int off = nss_off(cc, bi * 32 + 8 * q + 4 * g);
-      const uint2 h = *reinterpret_cast<const uint2*>(S[0] + off), lo = *reinterpret_cast<const uint2*>(S[1] + off);
-      const uint32_t hw[2] = {h.x, h.y}, lw[2] = {lo.x, lo.y};
+      const uint2 h = *reinterpret_cast<const uint2*>(XS[0] + off);
+      const uint2 m = *reinterpret_cast<const uint2*>(XS[1] + off);
+      const uint2 lo = *reinterpret_cast<const uint2*>(XS[2] + off);
+      const uint32_t hw[2] = {h.x, h.y}, mw[2] = {m.x, m.y}, lw[2] = {lo.x, lo.y};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const uint32_t hb = (hw[e >> 1] >> (16 * (e & 1))) & 0xffffu, lb = (lw[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-        x[4 * q + e] = __uint_as_float(hb << 16) + __uint_as_float(lb << 16);
+        const int sh = 16 * (e & 1);
+        x[4 * q + e] = bf2f((bf16_t)(hw[e >> 1] >> sh)) + (bf2f((bf16_t)(mw[e >> 1] >> sh)) +
+                                                          bf2f((bf16_t)(lw[e >> 1] >> sh)));
       }
     }
+  };
+  auto store_t = [&](int cc, const float (&t)[16]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<uint2*>(TS + nss_off(cc, bi * 32 + 8 * q + 4 * g)) =
+          make_uint2(f2bf(t[4 * q]) | (uint32_t)f2bf(t[4 * q + 1]) << 16,
+                     f2bf(t[4 * q + 2]) | (uint32_t)f2bf(t[4 * q + 3]) << 16);
   };
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
@@ -2522,37 +2552,21 @@ __global__ __launch_bounds__(512) void ns_inverse_kernel(const float* G, float* 
       const int rr = bi * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
       x[v] = rr == cc ? x0 : 0.f;
     }
-    store_blk(XS, cc, x);
+    store_x(cc, x);
   }
   __syncthreads();
-  // acc = P Q over k: P rows from (regs or LDS rows prow), Q columns = LDS rows qrow
-  auto frag = [&](const char (*S)[NSS_N * 256], int row, int ks, uint4& h, uint4& lo) {
-    const int off = row * 256 + ((((2 * ks + g)) ^ row) & 15) * 16;
-    h = *reinterpret_cast<const uint4*>(S[0] + off);
-    lo = *reinterpret_cast<const uint4*>(S[1] + off);
+  // 16-byte operand row (row, k = 16 ks + 8 g .. + 7) of a transposed tile
+  auto frag = [&](const char* S, int row, int ks) {
+    return *reinterpret_cast<const uint4*>(S + row * 256 + ((((2 * ks + g)) ^ row) & 15) * 16);
   };
-  auto mm3 = [&](f32x16 acc, uint4 ah, uint4 al, uint4 bh, uint4 bl) {
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ah), __builtin_bit_cast(bf16x8_t, bh), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ah), __builtin_bit_cast(bf16x8_t, bl), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, al), __builtin_bit_cast(bf16x8_t, bh), acc, 0, 0, 0);
-    return acc;
-  };
-  auto frag_hi = [&](const char (*S)[NSS_N * 256], int row, int ks) {
-    return *reinterpret_cast<const uint4*>(S[0] + row * 256 + ((((2 * ks + g)) ^ row) & 15) * 16);
-  };
-  auto mm1 = [&](f32x16 acc, uint4 ah, uint4 bh) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ah), __builtin_bit_cast(bf16x8_t, bh),
+  auto mma = [&](f32x16 acc, uint4 a, uint4 bq) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, bq),
                                                    acc, 0, 0, 0);
   };
   float prev = 1e30f;
   int it = 0;
   bool ok = st == DYRA_SOLVE_OK;
-  bool converged = false;
-  // Far from the inverse the iteration corrects its own rounding, so while
-  // ||I - A'X||_F > 1/4 the products take the hi parts only (one MFMA
-  // instead of three); split precision from there on, or as soon as a
-  // coarse step fails to reduce the error.
-  bool coarse = true;
+  bool converged = false, coarse = true;
   while (ok && it < maxit) {
     // T = A' X (this wave's two blocks); X column cc is stored as row cc
     f32x16 acc[2];
@@ -2564,15 +2578,20 @@ __global__ __launch_bounds__(512) void ns_inverse_kernel(const float* G, float* 
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[j] = mm1(acc[j], Ahi[ks], frag_hi(XS, bh2 * 64 + 32 * j + l, ks));
+        for (int j = 0; j < 2; ++j) acc[j] = mma(acc[j], Ah[ks], frag(XS[0], bh2 * 64 + 32 * j + l, ks));
     } else {
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          uint4 bh, bl;
-          frag(XS, bh2 * 64 + 32 * j + l, ks, bh, bl);
-          acc[j] = mm3(acc[j], Ahi[ks], Alo[ks], bh, bl);
+        for (int ks = 0; ks < 8; ++ks) {
+          const int cc = bh2 * 64 + 32 * j + l;
+          const uint4 xh = frag(XS[0], cc, ks), xm = frag(XS[1], cc, ks), xl = frag(XS[2], cc, ks);
+          acc[j] = mma(acc[j], Al[ks], xh);
+          acc[j] = mma(acc[j], Am[ks], xm);
+          acc[j] = mma(acc[j], Ah[ks], xl);
+          acc[j] = mma(acc[j], Am[ks], xh);
+          acc[j] = mma(acc[j], Ah[ks], xm);
+          acc[j] = mma(acc[j], Ah[ks], xh);
         }
     }
     float e2 = 0.f;
@@ -2585,33 +2604,42 @@ __global__ __launch_bounds__(512) void ns_inverse_kernel(const float* G, float* 
         const int rr = bi * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
         const float d = (rr == cc ? 1.f : 0.f) - acc[j][v];
         e2 += d * d;
-        tv[v] = acc[j][v];
+        tv[v] = coarse ? acc[j][v] : d;
       }
-      store_blk(TS, cc, tv);
+      store_t(cc, tv);
     }
-    e2 = block_sum<512>(e2, red);   // barriers: T complete afterwards
+    e2 = block_sum<512>(e2, red);   // barriers: T / E complete afterwards
     const float err = sqrtf(e2);
     if (!isfinite(err)) {
       ok = false;
       break;
     }
-    // hand over to the fp32 polish at the tolerance or as soon as split
-    // precision stops reducing the error (a coarse step that stops reducing
-    // it switches to split precision instead)
     if (err <= tol) {
       converged = true;
       break;
     }
-    if (err >= prev) {
-      if (!coarse) {
-        converged = true;
+    bool last = false;
+    if (coarse) {
+      // a coarse step that stopped reducing the error: redo the residual of
+      // the same X in the fine phase (its first error is not compared with
+      // the coarse ones)
+      if (err >= prev) {
+        coarse = false;
+        prev = 1e30f;
+        continue;
+      }
+    } else {
+      // the fine floor: the error stopped falling, or fell less than 4-fold
+      // where exact arithmetic would square it
+      if (err >= prev || (prev < 0.1f && err > 0.25f * prev)) {
+        converged = err < accept;
         break;
       }
-      coarse = false;
+      last = 4.f * err <= accept;
     }
-    if (err < 0.25f) coarse = false;
     prev = err;
-    // X <- 2 X - X T: X row bi 32 + l (X symmetric: its stored row), T column cc
+    // coarse: X <- 2 X - X T; fine: X <- X + X E.  X row bi 32 + l (X
+    // symmetric: its stored row), T / E column cc
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -2619,196 +2647,60 @@ __global__ __launch_bounds__(512) void ns_inverse_kernel(const float* G, float* 
     if (coarse) {
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        const uint4 ah = frag_hi(XS, arow, ks);
+        const uint4 ah = frag(XS[0], arow, ks);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[j] = mm1(acc[j], ah, frag_hi(TS, bh2 * 64 + 32 * j + l, ks));
+        for (int j = 0; j < 2; ++j) acc[j] = mma(acc[j], ah, frag(TS, bh2 * 64 + 32 * j + l, ks));
       }
     } else {
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        uint4 ah, al;
-        frag(XS, arow, ks, ah, al);
+        const uint4 ah = frag(XS[0], arow, ks), am = frag(XS[1], arow, ks), al = frag(XS[2], arow, ks);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          uint4 bh, bl;
-          frag(TS, bh2 * 64 + 32 * j + l, ks, bh, bl);
-          acc[j] = mm3(acc[j], ah, al, bh, bl);
+          const uint4 ej = frag(TS, bh2 * 64 + 32 * j + l, ks);
+          acc[j] = mma(acc[j], al, ej);
+          acc[j] = mma(acc[j], am, ej);
+          acc[j] = mma(acc[j], ah, ej);
         }
       }
     }
     float xo[2][16];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) load_blk(XS, bh2 * 64 + 32 * j + l, xo[j]);
-    __syncthreads();
+    for (int j = 0; j < 2; ++j) load_x(bh2 * 64 + 32 * j + l, xo[j]);
+    __syncthreads();   // every wave is done reading X
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) xo[j][v] = 2.f * xo[j][v] - acc[j][v];
-      store_blk(XS, bh2 * 64 + 32 * j + l, xo[j]);
+      for (int v = 0; v < 16; ++v) xo[j][v] = coarse ? 2.f * xo[j][v] - acc[j][v] : xo[j][v] + acc[j][v];
+      store_x(bh2 * 64 + 32 * j + l, xo[j]);
     }
     __syncthreads();
     ++it;
-  }
-  (void)converged;
-  if (st == DYRA_SOLVE_OK && !ok) {   // broke down: the sweep re-solves the segment
-    if (tid == 0) status[b] = DYRA_SOLVE_FALLBACK;
-    return;
-  }
-  // the iterate in A' space for the fp32 polish (zeros unless solvable)
-  const bool good = st == DYRA_SOLVE_OK;
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int cc = bh2 * 64 + 32 * j + l;
-    float x[16];
-    load_blk(XS, cc, x);
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int rr = bi * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
-      if (rr < r && cc < r) Xit[b * r * r + rr * r + cc] = good ? x[v] : 0.f;
-    }
-  }
-  if (tid == 0) status[b] = st;
-}
-
-// Newton-Schulz polish in fp32: continues from the split-precision iterate
-// (a few iterations from there reach the fp32 floor) and decides convergence
-// as the fp32 iteration does: a stall at or below `accept` is kept, a stall
-// above it flags the segment for the sweep.
-constexpr int NS_N = 128;
-constexpr int NS_P = 129;   // padded LDS pitch (odd: row-strided reads spread over banks)
-
-// Eight waves: wave (bi, bh) owns rows 32 bi .. + 31 and the two 32-column
-// blocks 64 bh .. + 63 of each product (A' row fragments in registers, 64
-// floats a lane; with 16 waves of one block each a lane had 128 registers
-// and the kernel spilled to scratch).
-__global__ __launch_bounds__(512) void ns_polish_kernel(const float* G, const float* Xit, double* Ginv,
-                                                        float* Ginv32, int32_t* status, int32_t* prec, int r,
-                                                        float eps, int maxit, float tol, float accept) {
-  constexpr int NTH = 512;
-  __shared__ float Xs[NS_N * NS_P];
-  __shared__ float Ts[NS_N * NS_P];
-  __shared__ float dsc[NS_N];
-  __shared__ float red[16];
-  const int64_t b = blockIdx.x;
-  const float* Gb = G + b * r * r;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int l = lane & 31, g = lane >> 5;
-  const int bi = w >> 1, bh = w & 1;
-  // every thread reads the status before the first barrier; thread 0
-  // rewrites it only at the end
-  if (status[b] != DYRA_SOLVE_OK) return;
-
-  // trace, ridge and Jacobi scaling
-  const float dv = tid < r ? Gb[tid * r + tid] : 0.f;
-  const float tr = block_sum<NTH>(dv, red);
-  const float lam = eps * tr / (float)r;
-  float badf = 0.f;
-  if (tid < NS_N) {
-    const float d = tid < r ? dv + lam : 1.f;
-    dsc[tid] = d > 0.f ? rsqrtf(d) : 0.f;
-    if (!(d > 0.f) || !isfinite(d)) badf = 1.f;
-  }
-  badf = block_sum<NTH>(badf, red);   // barrier: dsc complete afterwards
-  int st = DYRA_SOLVE_OK;
-  if (tr == 0.f) st = DYRA_SOLVE_ZERO;
-  else if (!(tr > 0.f) || !isfinite(tr) || badf > 0.f) st = DYRA_SOLVE_NOT_SPD;
-  // A' fragments in registers: Af[s] = A'[bi*32 + l][2s + g]
-  float Af[64];
-#pragma unroll
-  for (int s = 0; s < 64; ++s) {
-    const int row = bi * 32 + l, col = 2 * s + g;
-    float v;
-    if (row < r && col < r) v = (Gb[row * r + col] + (row == col ? lam : 0.f)) * dsc[row] * dsc[col];
-    else v = row == col ? 1.f : 0.f;
-    Af[s] = v;
-  }
-  // X_0: the split-precision iterate (A' space), padded with the identity
-  for (int e = tid; e < NS_N * NS_N; e += NTH) {
-    const int i = e / NS_N, jj = e % NS_N;
-    Xs[i * NS_P + jj] = i < r && jj < r ? Xit[b * r * r + i * r + jj] : (i == jj ? 1.f : 0.f);
-  }
-  __syncthreads();
-  float prev = 1e30f;
-  int it = 0;
-  bool ok = st == DYRA_SOLVE_OK;
-  bool converged = false;
-  while (ok && it < maxit) {
-    // T = A' X  (this wave's two blocks)
-    f32x16 acc[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[j][v] = 0.f;
-#pragma unroll
-    for (int s = 0; s < 64; ++s)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const float bx = Xs[(2 * s + g) * NS_P + bh * 64 + 32 * j + l];
-        acc[j] = __builtin_amdgcn_mfma_f32_32x32x2f32(Af[s], bx, acc[j], 0, 0, 0);
-      }
-    float e2 = 0.f;
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int rr = bi * 32 + (v >> 2) * 8 + g * 4 + (v & 3), cc = bh * 64 + 32 * j + l;
-        Ts[rr * NS_P + cc] = acc[j][v];
-        const float d = (rr == cc ? 1.f : 0.f) - acc[j][v];
-        e2 += d * d;
-      }
-    e2 = block_sum<NTH>(e2, red);   // contains barriers: Ts complete afterwards
-    const float err = sqrtf(e2);
-    if (!isfinite(err)) {
-      ok = false;
-      break;
-    }
-    if (err <= tol) {
+    if (last) {
       converged = true;
       break;
     }
-    if (err > 0.5f * prev && prev < 1e-2f) {   // stalled at the fp32 floor
-      converged = err < accept;
-      break;
+    if (coarse && err < 0.25f) {
+      coarse = false;
+      prev = 1e30f;
     }
-    prev = err;
-    // X <- 2 X - X T
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[j][v] = 0.f;
-#pragma unroll
-    for (int s = 0; s < 64; ++s) {
-      const float ax = Xs[(bi * 32 + l) * NS_P + 2 * s + g];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const float bt = Ts[(2 * s + g) * NS_P + bh * 64 + 32 * j + l];
-        acc[j] = __builtin_amdgcn_mfma_f32_32x32x2f32(ax, bt, acc[j], 0, 0, 0);
-      }
-    }
-    // every wave is done reading X; each then rewrites its own blocks (which
-    // no other wave writes, so their old values can be read after the barrier)
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int rr = bi * 32 + (v >> 2) * 8 + g * 4 + (v & 3), cc = bh * 64 + 32 * j + l;
-        Xs[rr * NS_P + cc] = 2.f * Xs[rr * NS_P + cc] - acc[j][v];
-      }
-    __syncthreads();
-    ++it;
   }
   if (st == DYRA_SOLVE_OK && !(ok && converged)) {
-    // Newton-Schulz stalled above tolerance (fp32 with a very ill-conditioned
-    // G) or broke down: flag the segment; the sweep launched after this
-    // kernel solves it.
+    // broke down, or stalled above `accept` (fp32 storage with a very
+    // ill-conditioned G): flag the segment; the sweep launched after this
+    // kernel solves it
     if (tid == 0) status[b] = DYRA_SOLVE_FALLBACK;
     return;
   }
   const bool good = st == DYRA_SOLVE_OK;
-  for (int e = tid; e < r * r; e += NTH) {
+  for (int e = tid; e < r * r; e += 512) {
     const int i = e / r, jj = e % r;
-    const double v = good ? (double)dsc[i] * (double)Xs[i * NS_P + jj] * (double)dsc[jj] : 0.0;
+    // X (i, jj) is stored at row jj, k = i
+    const int off = nss_off(jj, i);
+    const float x = bf2f(*reinterpret_cast<const bf16_t*>(XS[0] + off)) +
+                    (bf2f(*reinterpret_cast<const bf16_t*>(XS[1] + off)) +
+                     bf2f(*reinterpret_cast<const bf16_t*>(XS[2] + off)));
+    const double v = good ? (double)dsc[i] * (double)x * (double)dsc[jj] : 0.0;
     Ginv[b * r * r + e] = v;
     Ginv32[b * r * r + e] = (float)v;
   }
@@ -3250,7 +3142,6 @@ void forward_residual(const dyra_spec& s, const char* plan, const void* X, const
   float* M = reinterpret_cast<float*>(ws + WL.M);
   double* Gi = reinterpret_cast<double*>(ws + WL.Ginv);
   float* Gi32 = reinterpret_cast<float*>(ws + WL.Gi32);
-  float* Xit = reinterpret_cast<float*>(ws + WL.Xit);
   T* Mp = reinterpret_cast<T*>(ws + WL.Mp);
   T* Rt = reinterpret_cast<T*>(ws + WL.Rt);
   int32_t* stat = reinterpret_cast<int32_t*>(ws + WL.status);
@@ -3292,16 +3183,14 @@ void forward_residual(const dyra_spec& s, const char* plan, const void* X, const
   // S4: Ginv_b (unless solved above), M'_b = Ginv_b M_b
   if (!solved) {
     if (ns) {
-      // split-precision Newton-Schulz to its floor, the fp32 polish from there,
-      // then the sweep for any segment the polish flags
+      // Newton-Schulz, then the sweep for any segment it flags.
       // ||I - A' X||_F bounds the relative error of the inverse: 1e-4 is far
       // below the bf16 rounding of M', fp32 storage asks for the fp32 floor
       // (fp32 storage: a stall above 1e-5 goes to the fp64 sweep, so an
       // ill-conditioned G still gives an fp32-accurate inverse)
       const float tol = BF ? 1e-4f : 2e-6f, accept = BF ? 1e-2f : 1e-5f;
-      hipLaunchKernelGGL(ns_inverse_kernel, dim3((unsigned)B), dim3(512), 0, st, G, Xit, stat, r, eps, 40, tol);
-      hipLaunchKernelGGL(ns_polish_kernel, dim3((unsigned)B), dim3(512), 0, st, G, Xit, Gi, Gi32, stat, prec, r, eps,
-                         60, tol, accept);
+      hipLaunchKernelGGL(ns_inverse_kernel, dim3((unsigned)B), dim3(512), 0, st, G, Gi, Gi32, stat, prec, r, eps, 60,
+                         tol, accept);
       launch_sweep(G, Gi, Gi32, stat, prec, r, eps, B, true, st);
     } else if (solver == DYRA_SOLVER_CHOL) {
       launch_chol(G, Gi, Gi32, stat, prec, r, eps, B, st);

@@ -162,7 +162,6 @@ inline S5Split s5_split(int64_t c2, int64_t nr, int64_t K) {
 //                              cancel in Ginv M; fp32 rounding would not)
 // Gi32 [B x r x r] fp32        the same inverse rounded to fp32 (read by the
 //                              fp32 apply of well-conditioned segments)
-// Xit  [B x r x r] fp32        Newton-Schulz iterate handed to its polish
 // Mp   [B x r x c1] dtype      M'_b = Ginv_b M_b
 // Rt   [c2 x B r] dtype        R_b^T for every segment, R_b = M'_b W_res
 // status [B] int32
@@ -170,7 +169,7 @@ inline S5Split s5_split(int64_t c2, int64_t nr, int64_t K) {
 //      BLAST also [slices x n x r] for L = X P split over K
 struct WsLayout {
   int64_t wa = 0;
-  size_t A = 0, Wp = 0, Lt = 0, G = 0, M = 0, Ginv = 0, Mp = 0, Rt = 0, status = 0, Pk = 0, Xit = 0;
+  size_t A = 0, Wp = 0, Lt = 0, G = 0, M = 0, Ginv = 0, Mp = 0, Rt = 0, status = 0, Pk = 0;
   // per-segment precision of M' = Ginv M (0 fp32, 1 fp64), set by the solve
   size_t prec = 0, kprec = 0, Gi32 = 0, Ki32 = 0;
   // token-split partials of M [msplit][B x r x c1] fp32 (msplit > 1 only)
@@ -223,7 +222,6 @@ inline WsLayout ws_layout_n(const dyra_spec& s, int64_t B, int64_t n_rows, int64
   W.M = take((size_t)B * r * c1 * 4);
   W.Ginv = take((size_t)B * r * r * 8);
   W.Gi32 = take((size_t)B * r * r * 4);
-  W.Xit = take((size_t)B * r * r * 4);
   W.Mp = take((size_t)B * r * c1 * e);
   W.Rt = take(c2 * (size_t)B * r * e);
   W.status = take((size_t)B * 4);
