@@ -1859,6 +1859,330 @@ __device__ __forceinline__ int chol_inverse(const float* Gb, double* Ob, float* 
 }
 
 // ===========================================================================
+// S4a': Newton-Schulz inverse of one segment by one workgroup of 8 waves
+// on the 128 x 128 iterate.  Jacobi-scaled A' = D^-1/2 (G + lambda I) D^-1/2 (unit diagonal,
+// padded with the identity up to 128), X_0 = I / ||A'||_F, and the
+// Newton-Schulz step X <- X (2 I - A' X) = X + X E with E = I - A' X, until
+// ||E||_F <= tol; then Ginv = D^-1/2 X D^-1/2.  Every product runs on bf16
+// MFMAs with fp32 accumulation, in two phases:
+//   * coarse, while far from the inverse (the iteration corrects its own
+//     rounding there): T = A' X and X T from the bf16 parts alone, one MFMA
+//     each, X <- 2 X - X T;
+//   * fine, from the first coarse step that fails to reduce ||E||_F, or
+//     once it is below 1/4: A' and X are held as three bf16 terms each
+//     (hi + mid + lo, about 24 significant bits, as fp32) and A' X is
+//     formed from the six products whose terms reach 2^-24 relative, so the
+//     residual E = I - A' X is as accurate as an fp32 product would make it,
+//     while an fp32 MFMA product would cost sixteen MFMAs at gfx950's rates
+//     against these six.  The correction X E takes X's three terms and E
+//     rounded to bf16: rounding X would add about 2^-9 cond(A') ||E|| to
+//     the next residual (A' amplifies it), rounding E only about 2^-9 ||E||
+//     (A' X is close to I), which slows the quadratic convergence by no more
+//     than that factor per step.
+// X and E (T in the coarse phase) stay in LDS, stored transposed (row c
+// holds column c) so that every MFMA operand is one 16-byte row read; X is
+// a polynomial in A', hence symmetric, so its stored rows also serve as its
+// rows in X E.  The iteration stops at the tolerance, or flags the segment
+// for the sweep when a fine step stops reducing ||E||_F (its rounding floor)
+// above `accept`; from ||E||_F <= accept / 4 one more step leaves about its
+// square and is taken without another residual.
+// ===========================================================================
+
+constexpr int NSS_N = 128;
+__device__ __forceinline__ int nss_off(int row, int k) {   // bf16 element (row, k), 16-byte chunks swizzled
+  return row * 256 + ((((k >> 3) ^ row) & 15) << 4) + ((k & 7) << 1);
+}
+// x = h + m + l (bf16 terms; each difference is exact in fp32)
+__device__ __forceinline__ void split3_bf16(float x, uint16_t& h, uint16_t& m, uint16_t& l) {
+  h = f2bf(x);
+  const float r1 = x - bf2f(h);
+  m = f2bf(r1);
+  l = f2bf(r1 - bf2f(m));
+}
+__device__ __forceinline__ uint4 pack8_b16(const uint16_t (&v)[8]) {
+  return make_uint4(v[0] | (uint32_t)v[1] << 16, v[2] | (uint32_t)v[3] << 16, v[4] | (uint32_t)v[5] << 16,
+                    v[6] | (uint32_t)v[7] << 16);
+}
+// LDS of one Newton-Schulz solve: X (three bf16 planes), T or E, the Jacobi
+// scales and a reduction scratch.
+constexpr int NSL_XS = 0, NSL_TS = 3 * NSS_N * 256, NSL_DSC = 4 * NSS_N * 256, NSL_RED = NSL_DSC + NSS_N * 4;
+constexpr int NS_LDS = NSL_RED + 16 * 4;
+// bf16 storage: ||I - A' X||_F <= 1e-4 is far below the bf16 rounding of
+// M'; a floor above 1e-2 goes to the sweep
+constexpr float kNsTolBf16 = 1e-4f, kNsAcceptBf16 = 1e-2f;
+constexpr int kNsMaxit = 60;
+
+// One segment's inverse by 8 waves: wave (bi, bh) owns rows 32 bi .. + 31
+// and the two 32-column blocks from 64 bh.  Gb: G_b (r x r row-major); sm:
+// NS_LDS bytes of LDS.  Writes Ob / Ob32 (zeros unless the status is OK)
+// when the iteration converges; returns the status, with `conv` false when
+// a positive definite G_b could not be solved (the caller then has it
+// re-solved by the sweep).
+__device__ __forceinline__ int ns_solve(const float* Gb, int r, float eps, int maxit, float tol, float accept, char* sm,
+                                        double* Ob, float* Ob32, bool& conv) {
+  constexpr int NT = 512, WPR = 2, JB = 2;   // threads, waves per row block, column blocks per wave
+  char(*XS)[NSS_N * 256] = reinterpret_cast<char(*)[NSS_N * 256]>(sm + NSL_XS);
+  char* TS = sm + NSL_TS;
+  float* dsc = reinterpret_cast<float*>(sm + NSL_DSC);
+  float* red = reinterpret_cast<float*>(sm + NSL_RED);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l = lane & 31, g = lane >> 5;
+  const int bi = w / WPR, bh = w % WPR;   // rows bi 32 .. + 31, columns bh 32 JB .. + 32 JB - 1
+  auto col_of = [&](int j) { return bh * 32 * JB + 32 * j + l; };
+  float dv = 0.f;
+  for (int i = tid; i < r; i += NT) dv += Gb[i * r + i];
+  const float tr = block_sum<NT>(dv, red);
+  const float lam = eps * tr / (float)r;
+  float badf = 0.f;
+  for (int i = tid; i < NSS_N; i += NT) {
+    const float d = i < r ? Gb[i * r + i] + lam : 1.f;
+    dsc[i] = d > 0.f ? rsqrtf(d) : 0.f;
+    if (!(d > 0.f) || !isfinite(d)) badf = 1.f;
+  }
+  badf = block_sum<NT>(badf, red);   // barriers: dsc complete afterwards
+  int st = DYRA_SOLVE_OK;
+  if (tr == 0.f) st = DYRA_SOLVE_ZERO;
+  else if (!(tr > 0.f) || !isfinite(tr) || badf > 0.f) st = DYRA_SOLVE_NOT_SPD;
+  // A' fragments of rows bi 32 + l, k = 16 ks + 8 g .. + 7, as three bf16 terms
+  uint4 Ah[8], Am[8], Al[8];
+  float fro2 = 0.f;
+  const int arow = bi * 32 + l;
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    uint16_t h[8], m[8], lo[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int col = 16 * ks + 8 * g + e;
+      float v;
+      if (arow < r && col < r) v = (Gb[arow * r + col] + (arow == col ? lam : 0.f)) * dsc[arow] * dsc[col];
+      else v = arow == col ? 1.f : 0.f;
+      if (bh == 0) fro2 += v * v;
+      split3_bf16(v, h[e], m[e], lo[e]);
+    }
+    Ah[ks] = pack8_b16(h);
+    Am[ks] = pack8_b16(m);
+    Al[ks] = pack8_b16(lo);
+  }
+  fro2 = block_sum<NT>(fro2, red);
+  const float x0 = 1.f / sqrtf(fro2);
+  // accumulator element v of lane (l, g) in column block j is (rr, cc) with
+  // rr = bi 32 + 8 (v / 4) + 4 g + v % 4, cc = col_of(j); stored at row cc,
+  // k = rr (four consecutive v at one 8-byte place)
+  auto store_x = [&](int cc, const float (&x)[16]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint16_t h[4], m[4], lo[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) split3_bf16(x[4 * q + e], h[e], m[e], lo[e]);
+      const int off = nss_off(cc, bi * 32 + 8 * q + 4 * g);
+      *reinterpret_cast<uint2*>(XS[0] + off) = make_uint2(h[0] | (uint32_t)h[1] << 16, h[2] | (uint32_t)h[3] << 16);
+      *reinterpret_cast<uint2*>(XS[1] + off) = make_uint2(m[0] | (uint32_t)m[1] << 16, m[2] | (uint32_t)m[3] << 16);
+      *reinterpret_cast<uint2*>(XS[2] + off) = make_uint2(lo[0] | (uint32_t)lo[1] << 16, lo[2] | (uint32_t)lo[3] << 16);
+    }
+  };
+  auto load_x = [&](int cc, float (&x)[16]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int off = nss_off(cc, bi * 32 + 8 * q + 4 * g);
+      const uint2 h = *reinterpret_cast<const uint2*>(XS[0] + off);
+      const uint2 m = *reinterpret_cast<const uint2*>(XS[1] + off);
+      const uint2 lo = *reinterpret_cast<const uint2*>(XS[2] + off);
+      const uint32_t hw[2] = {h.x, h.y}, mw[2] = {m.x, m.y}, lw[2] = {lo.x, lo.y};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int sh = 16 * (e & 1);
+        x[4 * q + e] = bf2f((bf16_t)(hw[e >> 1] >> sh)) + (bf2f((bf16_t)(mw[e >> 1] >> sh)) +
+                                                          bf2f((bf16_t)(lw[e >> 1] >> sh)));
+      }
+    }
+  };
+  auto store_t = [&](int cc, const float (&t)[16]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<uint2*>(TS + nss_off(cc, bi * 32 + 8 * q + 4 * g)) =
+          make_uint2(f2bf(t[4 * q]) | (uint32_t)f2bf(t[4 * q + 1]) << 16,
+                     f2bf(t[4 * q + 2]) | (uint32_t)f2bf(t[4 * q + 3]) << 16);
+  };
+#pragma unroll
+  for (int j = 0; j < JB; ++j) {
+    const int cc = col_of(j);
+    float x[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int rr = bi * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
+      x[v] = rr == cc ? x0 : 0.f;
+    }
+    store_x(cc, x);
+  }
+  __syncthreads();
+  // 16-byte operand row (row, k = 16 ks + 8 g .. + 7) of a transposed tile
+  auto frag = [&](const char* S, int row, int ks) {
+    return *reinterpret_cast<const uint4*>(S + row * 256 + ((((2 * ks + g)) ^ row) & 15) * 16);
+  };
+  auto mma = [&](f32x16 acc, uint4 a, uint4 bq) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, bq),
+                                                   acc, 0, 0, 0);
+  };
+  float prev = 1e30f;
+  int it = 0;
+  bool ok = st == DYRA_SOLVE_OK;
+  bool converged = false, coarse = true;
+  while (ok && it < maxit) {
+    // T = A' X (this wave's column blocks); X column cc is stored as row cc
+    f32x16 acc[JB];
+#pragma unroll
+    for (int j = 0; j < JB; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[j][v] = 0.f;
+    if (coarse) {
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+        for (int j = 0; j < JB; ++j) acc[j] = mma(acc[j], Ah[ks], frag(XS[0], col_of(j), ks));
+    } else {
+#pragma unroll
+      for (int j = 0; j < JB; ++j)
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          const int cc = col_of(j);
+          const uint4 xh = frag(XS[0], cc, ks), xm = frag(XS[1], cc, ks), xl = frag(XS[2], cc, ks);
+          acc[j] = mma(acc[j], Al[ks], xh);
+          acc[j] = mma(acc[j], Am[ks], xm);
+          acc[j] = mma(acc[j], Ah[ks], xl);
+          acc[j] = mma(acc[j], Am[ks], xh);
+          acc[j] = mma(acc[j], Ah[ks], xm);
+          acc[j] = mma(acc[j], Ah[ks], xh);
+        }
+    }
+    float e2 = 0.f;
+#pragma unroll
+    for (int j = 0; j < JB; ++j) {
+      const int cc = col_of(j);
+      float tv[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int rr = bi * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
+        const float d = (rr == cc ? 1.f : 0.f) - acc[j][v];
+        e2 += d * d;
+        tv[v] = coarse ? acc[j][v] : d;
+      }
+      store_t(cc, tv);
+    }
+    e2 = block_sum<NT>(e2, red);   // barriers: T / E complete afterwards
+    const float err = sqrtf(e2);
+    if (!isfinite(err)) {
+      ok = false;
+      break;
+    }
+    if (err <= tol) {
+      converged = true;
+      break;
+    }
+    bool last = false;
+    if (coarse) {
+      // a coarse step that stopped reducing the error: redo the residual of
+      // the same X in the fine phase (its first error is not compared with
+      // the coarse ones)
+      if (err >= prev) {
+        coarse = false;
+        prev = 1e30f;
+        continue;
+      }
+    } else {
+      // the fine floor: the error stopped falling, or fell less than 4-fold
+      // where exact arithmetic would square it
+      if (err >= prev || (prev < 0.1f && err > 0.25f * prev)) {
+        converged = err < accept;
+        break;
+      }
+      last = 4.f * err <= accept;
+    }
+    prev = err;
+    // coarse: X <- 2 X - X T; fine: X <- X + X E.  X row bi 32 + l (X
+    // symmetric: its stored row), T / E column cc
+#pragma unroll
+    for (int j = 0; j < JB; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[j][v] = 0.f;
+    if (coarse) {
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const uint4 ah = frag(XS[0], arow, ks);
+#pragma unroll
+        for (int j = 0; j < JB; ++j) acc[j] = mma(acc[j], ah, frag(TS, col_of(j), ks));
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const uint4 ah = frag(XS[0], arow, ks), am = frag(XS[1], arow, ks), al = frag(XS[2], arow, ks);
+#pragma unroll
+        for (int j = 0; j < JB; ++j) {
+          const uint4 ej = frag(TS, col_of(j), ks);
+          acc[j] = mma(acc[j], al, ej);
+          acc[j] = mma(acc[j], am, ej);
+          acc[j] = mma(acc[j], ah, ej);
+        }
+      }
+    }
+    float xo[JB][16];
+#pragma unroll
+    for (int j = 0; j < JB; ++j) load_x(col_of(j), xo[j]);
+    __syncthreads();   // every wave is done reading X
+#pragma unroll
+    for (int j = 0; j < JB; ++j) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) xo[j][v] = coarse ? 2.f * xo[j][v] - acc[j][v] : xo[j][v] + acc[j][v];
+      store_x(col_of(j), xo[j]);
+    }
+    __syncthreads();
+    ++it;
+    if (last) {
+      converged = true;
+      break;
+    }
+    if (coarse && err < 0.25f) {
+      coarse = false;
+      prev = 1e30f;
+    }
+  }
+  conv = !(st == DYRA_SOLVE_OK && !(ok && converged));
+  if (!conv) return st;   // broke down, or stalled above `accept`
+  const bool good = st == DYRA_SOLVE_OK;
+  for (int e = tid; e < r * r; e += NT) {
+    const int i = e / r, jj = e % r;
+    // X (i, jj) is stored at row jj, k = i
+    const int off = nss_off(jj, i);
+    const float x = bf2f(*reinterpret_cast<const bf16_t*>(XS[0] + off)) +
+                    (bf2f(*reinterpret_cast<const bf16_t*>(XS[1] + off)) +
+                     bf2f(*reinterpret_cast<const bf16_t*>(XS[2] + off)));
+    const double v = good ? (double)dsc[i] * (double)x * (double)dsc[jj] : 0.0;
+    Ob[e] = v;
+    Ob32[e] = (float)v;
+  }
+  return st;
+}
+
+// The standalone launch: one 512-thread workgroup per segment.  A segment
+// the iteration cannot solve keeps DYRA_SOLVE_FALLBACK for the sweep
+// launched after this kernel.
+__global__ __launch_bounds__(512) void ns_inverse_kernel(const float* G, double* Ginv, float* Ginv32, int32_t* status,
+                                                          int32_t* prec, int r, float eps, int maxit, float tol,
+                                                          float accept) {
+  __shared__ __attribute__((aligned(16))) char sm[NS_LDS];
+  const int64_t b = blockIdx.x;
+  bool conv;
+  const int st = ns_solve(G + b * r * r, r, eps, maxit, tol, accept, sm, Ginv + b * r * r, Ginv32 + b * r * r,
+                             conv);
+  if (threadIdx.x == 0) {
+    status[b] = conv ? st : DYRA_SOLVE_FALLBACK;
+    // the fp32 apply: the iteration's own tolerance, not the apply's
+    // rounding, bounds the accuracy of M' for a Newton-Schulz inverse
+    prec[b] = 0;
+  }
+}
+
+
+// ===========================================================================
 // S3 (bf16): token reductions without an LDS transpose.
 // Workgroups [0, B): G_b = L_b^T L_b and its inverse (the r x r solve runs
 // here, concurrently with the M strips).  Workgroups [B, ...): one
@@ -2294,25 +2618,30 @@ __global__ __launch_bounds__(256) void m_split_reduce_kernel(const float* __rest
 // streaming the segment's L^T itself (which put the Gram's load latency on the
 // critical path of that launch).
 template <int NB>
-__global__ __launch_bounds__(64) void gram_partial_kernel(const bf16_t* __restrict__ Lt, int64_t ldt, int r,
-                                                          SegMap sg, int64_t n, int gchunks, int64_t gchunk,
-                                                          float* __restrict__ Gp) {
-  // one wave per chunk: every token step's L^T loads are issued before the
-  // MFMAs, and the 32 x 32 blocks go from the accumulators straight to memory
-  constexpr int MAXST = 16;   // gchunk <= 256 tokens = 16 steps of 16
-  const int lane = threadIdx.x, l = lane & 31, g = lane >> 5;
+__global__ __launch_bounds__(64 * NB) void gram_partial_kernel(const bf16_t* __restrict__ Lt, int64_t ldt, int r,
+                                                               SegMap sg, int64_t n, int gchunks, int64_t gchunk,
+                                                               float* __restrict__ Gp) {
+  // one workgroup of NB waves per chunk: wave a forms block row a (the
+  // 32 x 32 blocks (a, 0 .. NB - 1)); every token step's L^T loads are
+  // issued before the MFMAs, and the blocks go from the accumulators
+  // straight to memory
+  constexpr int MAXST = 32;   // L^T row loads in flight per lane: 32 / NB steps of NB rows
+  const int lane = threadIdx.x & 63, l = lane & 31, g = lane >> 5;
+  const int a = threadIdx.x >> 6;
   const int64_t b = blockIdx.x / gchunks, c = blockIdx.x % gchunks;
   const int64_t lo = sg.lo(b) + c * gchunk;
   const int64_t hi = imin64(lo + gchunk, sg.hi(b));
-  f32x16 acc[NB][NB];
+  f32x16 acc[NB];
 #pragma unroll
-  for (int a = 0; a < NB; ++a)
+  for (int bb = 0; bb < NB; ++bb)
 #pragma unroll
-    for (int bb = 0; bb < NB; ++bb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[a][bb][v] = 0.f;
+    for (int v = 0; v < 16; ++v) acc[bb][v] = 0.f;
   const int64_t a0 = lo & ~(int64_t)7;
   const int nsteps = lo < hi ? (int)((hi - a0 + 15) / 16) : 0;
+  auto load = [&](int row, int64_t t0, bool in) {
+    const uint4 v = (in && row < r && t0 < ldt) ? *reinterpret_cast<const uint4*>(Lt + row * ldt + t0) : zero4();
+    return mask_tokens<bf16_t>(v, t0, lo, hi);
+  };
   for (int st0 = 0; st0 < nsteps; st0 += MAXST / NB) {
     constexpr int PF = MAXST / NB;
     uint4 f[PF][NB];
@@ -2321,34 +2650,33 @@ __global__ __launch_bounds__(64) void gram_partial_kernel(const bf16_t* __restri
       const int64_t t0 = a0 + 16 * (int64_t)(st0 + u) + 8 * g;
       const bool in = st0 + u < nsteps;
 #pragma unroll
-      for (int rb = 0; rb < NB; ++rb) {
-        const int row = rb * 32 + l;
-        const uint4 v = (in && row < r && t0 < ldt) ? *reinterpret_cast<const uint4*>(Lt + row * ldt + t0) : zero4();
-        f[u][rb] = mask_tokens<bf16_t>(v, t0, lo, hi);
-      }
+      for (int rb = 0; rb < NB; ++rb) f[u][rb] = load(rb * 32 + l, t0, in);
     }
 #pragma unroll
-    for (int u = 0; u < PF; ++u)
+    for (int u = 0; u < PF; ++u) {
+      // this wave's block row among the loaded ones (a is wave-uniform)
+      uint4 fa = f[u][0];
 #pragma unroll
-      for (int a = 0; a < NB; ++a)
+      for (int rb = 1; rb < NB; ++rb)
+        if (a == rb) fa = f[u][rb];
+      if (st0 + u < nsteps) {   // uniform: steps past the chunk's end are skipped
 #pragma unroll
         for (int bb = 0; bb < NB; ++bb)
-          acc[a][bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, f[u][a]),
-                                                               __builtin_bit_cast(bf16x8_t, f[u][bb]), acc[a][bb],
-                                                               0, 0, 0);
+          acc[bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fa),
+                                                            __builtin_bit_cast(bf16x8_t, f[u][bb]), acc[bb], 0, 0, 0);
+      }
+    }
   }
   // accumulator element v of lane (l, g) in block (a, bb) is
   // G[a 32 + 8 (v / 4) + 4 g + v % 4][bb 32 + l]
   float* out = Gp + (int64_t)blockIdx.x * r * r;
 #pragma unroll
-  for (int a = 0; a < NB; ++a)
+  for (int bb = 0; bb < NB; ++bb)
 #pragma unroll
-    for (int bb = 0; bb < NB; ++bb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int i = a * 32 + (v >> 2) * 8 + g * 4 + (v & 3), jj = bb * 32 + l;
-        if (i < r && jj < r) out[i * r + jj] = acc[a][bb][v];
-      }
+    for (int v = 0; v < 16; ++v) {
+      const int i = a * 32 + (v >> 2) * 8 + g * 4 + (v & 3), jj = bb * 32 + l;
+      if (i < r && jj < r) out[i * r + jj] = acc[bb][v];
+    }
 }
 
 // S4a as its own launch: one 256-thread workgroup per segment.  With
@@ -2412,305 +2740,6 @@ void launch_chol(const float* G, double* Ginv, float* Ginv32, int32_t* status, i
                        prec, r, eps);
 }
 
-// ===========================================================================
-// S4a': Newton-Schulz inverse, one workgroup of 8 waves per segment; wave
-// (bi, h) owns rows 32 bi .. + 31 and columns 64 h .. + 63 of the 128 x 128
-// iterate.  Jacobi-scaled A' = D^-1/2 (G + lambda I) D^-1/2 (unit diagonal,
-// padded with the identity up to 128), X_0 = I / ||A'||_F, and the
-// Newton-Schulz step X <- X (2 I - A' X) = X + X E with E = I - A' X, until
-// ||E||_F <= tol; then Ginv = D^-1/2 X D^-1/2.  Every product runs on bf16
-// MFMAs with fp32 accumulation, in two phases:
-//   * coarse, while far from the inverse (the iteration corrects its own
-//     rounding there): T = A' X and X T from the bf16 parts alone, one MFMA
-//     each, X <- 2 X - X T;
-//   * fine, from the first coarse step that fails to reduce ||E||_F, or
-//     once it is below 1/4: A' and X are held as three bf16 terms each
-//     (hi + mid + lo, about 24 significant bits, as fp32) and A' X is
-//     formed from the six products whose terms reach 2^-24 relative, so the
-//     residual E = I - A' X is as accurate as an fp32 product would make it,
-//     while an fp32 MFMA product would cost sixteen MFMAs at gfx950's rates
-//     against these six.  The correction X E takes X's three terms and E
-//     rounded to bf16: rounding X would add about 2^-9 cond(A') ||E|| to
-//     the next residual (A' amplifies it), rounding E only about 2^-9 ||E||
-//     (A' X is close to I), which slows the quadratic convergence by no more
-//     than that factor per step.
-// X and E (T in the coarse phase) stay in LDS, stored transposed (row c
-// holds column c) so that every MFMA operand is one 16-byte row read; X is
-// a polynomial in A', hence symmetric, so its stored rows also serve as its
-// rows in X E.  The iteration stops at the tolerance, or flags the segment
-// for the sweep when a fine step stops reducing ||E||_F (its rounding floor)
-// above `accept`; from ||E||_F <= accept / 4 one more step leaves about its
-// square and is taken without another residual.
-// ===========================================================================
-
-constexpr int NSS_N = 128;
-__device__ __forceinline__ int nss_off(int row, int k) {   // bf16 element (row, k), 16-byte chunks swizzled
-  return row * 256 + ((((k >> 3) ^ row) & 15) << 4) + ((k & 7) << 1);
-}
-// x = h + m + l (bf16 terms; each difference is exact in fp32)
-__device__ __forceinline__ void split3_bf16(float x, uint16_t& h, uint16_t& m, uint16_t& l) {
-  h = f2bf(x);
-  const float r1 = x - bf2f(h);
-  m = f2bf(r1);
-  l = f2bf(r1 - bf2f(m));
-}
-__device__ __forceinline__ uint4 pack8_b16(const uint16_t (&v)[8]) {
-  return make_uint4(v[0] | (uint32_t)v[1] << 16, v[2] | (uint32_t)v[3] << 16, v[4] | (uint32_t)v[5] << 16,
-                    v[6] | (uint32_t)v[7] << 16);
-}
-__global__ __launch_bounds__(512) void ns_inverse_kernel(const float* G, double* Ginv, float* Ginv32, int32_t* status,
-                                                          int32_t* prec, int r, float eps, int maxit, float tol,
-                                                          float accept) {
-  __shared__ __attribute__((aligned(16))) char XS[3][NSS_N * 256];   // X hi / mid / lo, stored transposed
-  __shared__ __attribute__((aligned(16))) char TS[NSS_N * 256];      // T (coarse) or E (fine), bf16, transposed
-  __shared__ float dsc[NSS_N];
-  __shared__ float red[16];
-  const int64_t b = blockIdx.x;
-  const float* Gb = G + b * r * r;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int l = lane & 31, g = lane >> 5;
-  const int bi = w >> 1, bh2 = w & 1;   // rows bi 32 .. + 31, columns bh2 64 .. + 63 (two 32 x 32 blocks)
-  const float dv = tid < r ? Gb[tid * r + tid] : 0.f;
-  const float tr = block_sum<512>(dv, red);
-  const float lam = eps * tr / (float)r;
-  float badf = 0.f;
-  if (tid < NSS_N) {
-    const float d = tid < r ? dv + lam : 1.f;
-    dsc[tid] = d > 0.f ? rsqrtf(d) : 0.f;
-    if (!(d > 0.f) || !isfinite(d)) badf = 1.f;
-  }
-  badf = block_sum<512>(badf, red);
-  int st = DYRA_SOLVE_OK;
-  if (tr == 0.f) st = DYRA_SOLVE_ZERO;
-  else if (!(tr > 0.f) || !isfinite(tr) || badf > 0.f) st = DYRA_SOLVE_NOT_SPD;
-  // A' fragments of rows bi 32 + l, k = 16 ks + 8 g .. + 7, as three bf16 terms
-  uint4 Ah[8], Am[8], Al[8];
-  float fro2 = 0.f;
-  const int arow = bi * 32 + l;
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    uint16_t h[8], m[8], lo[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int col = 16 * ks + 8 * g + e;
-      float v;
-      if (arow < r && col < r) v = (Gb[arow * r + col] + (arow == col ? lam : 0.f)) * dsc[arow] * dsc[col];
-      else v = arow == col ? 1.f : 0.f;
-      if (bh2 == 0) fro2 += v * v;
-      split3_bf16(v, h[e], m[e], lo[e]);
-    }
-    Ah[ks] = pack8_b16(h);
-    Am[ks] = pack8_b16(m);
-    Al[ks] = pack8_b16(lo);
-  }
-  fro2 = block_sum<512>(fro2, red);
-  const float x0 = 1.f / sqrtf(fro2);
-  // this wave's block: accumulator element v of lane (l, g) is (rr, cc) with
-  // rr = bi 32 + 8 (v / 4) + 4 g + v % 4, cc = bj 32 + l; stored at row cc,
-  // k = rr (four consecutive v at one 8-byte place)
-  auto store_x = [&](int cc, const float (&x)[16]) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      uint16_t h[4], m[4], lo[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) split3_bf16(x[4 * q + e], h[e], m[e], lo[e]);
-      const int off = nss_off(cc, bi * 32 + 8 * q + 4 * g);
-      *reinterpret_cast<uint2*>(XS[0] + off) = make_uint2(h[0] | (uint32_t)h[1] << 16, h[2] | (uint32_t)h[3] << 16);
-      *reinterpret_cast<uint2*>(XS[1] + off) = make_uint2(m[0] | (uint32_t)m[1] << 16, m[2] | (uint32_t)m[3] << 16);
-      *reinterpret_cast<uint2*>(XS[2] + off) = make_uint2(lo[0] | (uint32_t)lo[1] << 16, lo[2] | (uint32_t)lo[3] << 16);
-    }
-  };
-  auto load_x = [&](int cc, float (&x)[16]) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int off = nss_off(cc, bi * 32 + 8 * q + 4 * g);
-      const uint2 h = *reinterpret_cast<const uint2*>(XS[0] + off);
-      const uint2 m = *reinterpret_cast<const uint2*>(XS[1] + off);
-      const uint2 lo = *reinterpret_cast<const uint2*>(XS[2] + off);
-      const uint32_t hw[2] = {h.x, h.y}, mw[2] = {m.x, m.y}, lw[2] = {lo.x, lo.y};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int sh = 16 * (e & 1);
-        x[4 * q + e] = bf2f((bf16_t)(hw[e >> 1] >> sh)) + (bf2f((bf16_t)(mw[e >> 1] >> sh)) +
-                                                          bf2f((bf16_t)(lw[e >> 1] >> sh)));
-      }
-    }
-  };
-  auto store_t = [&](int cc, const float (&t)[16]) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      *reinterpret_cast<uint2*>(TS + nss_off(cc, bi * 32 + 8 * q + 4 * g)) =
-          make_uint2(f2bf(t[4 * q]) | (uint32_t)f2bf(t[4 * q + 1]) << 16,
-                     f2bf(t[4 * q + 2]) | (uint32_t)f2bf(t[4 * q + 3]) << 16);
-  };
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int cc = bh2 * 64 + 32 * j + l;
-    float x[16];
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int rr = bi * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
-      x[v] = rr == cc ? x0 : 0.f;
-    }
-    store_x(cc, x);
-  }
-  __syncthreads();
-  // 16-byte operand row (row, k = 16 ks + 8 g .. + 7) of a transposed tile
-  auto frag = [&](const char* S, int row, int ks) {
-    return *reinterpret_cast<const uint4*>(S + row * 256 + ((((2 * ks + g)) ^ row) & 15) * 16);
-  };
-  auto mma = [&](f32x16 acc, uint4 a, uint4 bq) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, bq),
-                                                   acc, 0, 0, 0);
-  };
-  float prev = 1e30f;
-  int it = 0;
-  bool ok = st == DYRA_SOLVE_OK;
-  bool converged = false, coarse = true;
-  while (ok && it < maxit) {
-    // T = A' X (this wave's two blocks); X column cc is stored as row cc
-    f32x16 acc[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[j][v] = 0.f;
-    if (coarse) {
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[j] = mma(acc[j], Ah[ks], frag(XS[0], bh2 * 64 + 32 * j + l, ks));
-    } else {
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          const int cc = bh2 * 64 + 32 * j + l;
-          const uint4 xh = frag(XS[0], cc, ks), xm = frag(XS[1], cc, ks), xl = frag(XS[2], cc, ks);
-          acc[j] = mma(acc[j], Al[ks], xh);
-          acc[j] = mma(acc[j], Am[ks], xm);
-          acc[j] = mma(acc[j], Ah[ks], xl);
-          acc[j] = mma(acc[j], Am[ks], xh);
-          acc[j] = mma(acc[j], Ah[ks], xm);
-          acc[j] = mma(acc[j], Ah[ks], xh);
-        }
-    }
-    float e2 = 0.f;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int cc = bh2 * 64 + 32 * j + l;
-      float tv[16];
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int rr = bi * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
-        const float d = (rr == cc ? 1.f : 0.f) - acc[j][v];
-        e2 += d * d;
-        tv[v] = coarse ? acc[j][v] : d;
-      }
-      store_t(cc, tv);
-    }
-    e2 = block_sum<512>(e2, red);   // barriers: T / E complete afterwards
-    const float err = sqrtf(e2);
-    if (!isfinite(err)) {
-      ok = false;
-      break;
-    }
-    if (err <= tol) {
-      converged = true;
-      break;
-    }
-    bool last = false;
-    if (coarse) {
-      // a coarse step that stopped reducing the error: redo the residual of
-      // the same X in the fine phase (its first error is not compared with
-      // the coarse ones)
-      if (err >= prev) {
-        coarse = false;
-        prev = 1e30f;
-        continue;
-      }
-    } else {
-      // the fine floor: the error stopped falling, or fell less than 4-fold
-      // where exact arithmetic would square it
-      if (err >= prev || (prev < 0.1f && err > 0.25f * prev)) {
-        converged = err < accept;
-        break;
-      }
-      last = 4.f * err <= accept;
-    }
-    prev = err;
-    // coarse: X <- 2 X - X T; fine: X <- X + X E.  X row bi 32 + l (X
-    // symmetric: its stored row), T / E column cc
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[j][v] = 0.f;
-    if (coarse) {
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const uint4 ah = frag(XS[0], arow, ks);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[j] = mma(acc[j], ah, frag(TS, bh2 * 64 + 32 * j + l, ks));
-      }
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const uint4 ah = frag(XS[0], arow, ks), am = frag(XS[1], arow, ks), al = frag(XS[2], arow, ks);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const uint4 ej = frag(TS, bh2 * 64 + 32 * j + l, ks);
-          acc[j] = mma(acc[j], al, ej);
-          acc[j] = mma(acc[j], am, ej);
-          acc[j] = mma(acc[j], ah, ej);
-        }
-      }
-    }
-    float xo[2][16];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) load_x(bh2 * 64 + 32 * j + l, xo[j]);
-    __syncthreads();   // every wave is done reading X
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) xo[j][v] = coarse ? 2.f * xo[j][v] - acc[j][v] : xo[j][v] + acc[j][v];
-      store_x(bh2 * 64 + 32 * j + l, xo[j]);
-    }
-    __syncthreads();
-    ++it;
-    if (last) {
-      converged = true;
-      break;
-    }
-    if (coarse && err < 0.25f) {
-      coarse = false;
-      prev = 1e30f;
-    }
-  }
-  if (st == DYRA_SOLVE_OK && !(ok && converged)) {
-    // broke down, or stalled above `accept` (fp32 storage with a very
-    // ill-conditioned G): flag the segment; the sweep launched after this
-    // kernel solves it
-    if (tid == 0) status[b] = DYRA_SOLVE_FALLBACK;
-    return;
-  }
-  const bool good = st == DYRA_SOLVE_OK;
-  for (int e = tid; e < r * r; e += 512) {
-    const int i = e / r, jj = e % r;
-    // X (i, jj) is stored at row jj, k = i
-    const int off = nss_off(jj, i);
-    const float x = bf2f(*reinterpret_cast<const bf16_t*>(XS[0] + off)) +
-                    (bf2f(*reinterpret_cast<const bf16_t*>(XS[1] + off)) +
-                     bf2f(*reinterpret_cast<const bf16_t*>(XS[2] + off)));
-    const double v = good ? (double)dsc[i] * (double)x * (double)dsc[jj] : 0.0;
-    Ginv[b * r * r + e] = v;
-    Ginv32[b * r * r + e] = (float)v;
-  }
-  if (tid == 0) {
-    status[b] = st;
-    // the fp32 apply: the iteration's own tolerance, not the apply's
-    // rounding, bounds the accuracy of M' for a Newton-Schulz inverse
-    prec[b] = 0;
-  }
-}
 
 
 // ===========================================================================
@@ -3102,7 +3131,7 @@ void launch_s3_bf16(const bf16_t* Lt, int64_t ldt, const bf16_t* X, int64_t c1, 
                     float* Mpart = nullptr) {
   const int strips = (int)cdiv(c1, S3_STRIP);
   if (gpart && gprows == 0)   // chunk Gram partials first (absolute L^T addressing only)
-    hipLaunchKernelGGL((gram_partial_kernel<NB>), dim3((unsigned)(B * gchunks)), dim3(64), 0, st, Lt, ldt, r,
+    hipLaunchKernelGGL((gram_partial_kernel<NB>), dim3((unsigned)(B * gchunks)), dim3(64 * NB), 0, st, Lt, ldt, r,
                        sg, n, gchunks, gchunk, gpart);
   auto go = [&](auto kern) {
     constexpr int RH = NRB > 4 ? NRB / 4 : 1;   // row blocks per strip (the kernel's SNRB split)
@@ -3154,10 +3183,12 @@ void forward_residual(const dyra_spec& s, const char* plan, const void* X, const
   // stays selectable.
   const bool ns = solver == DYRA_SOLVER_NS;
   // solve inside the token-reduction launch: 1 the sweep, 2 the Cholesky
-  // route, 0 none (Newton-Schulz runs after it).  At r = 128 a separate
+  // route, 0 none (Newton-Schulz runs after it: as the launch's 4-wave solve
+  // role at r = 128 it took 155 us against 99 us for its own 8-wave launch,
+  // more than the overlap with the strips gained).  At r = 128 a separate
   // 512-thread sweep launch is faster on its own (110 us against the
   // launch's 256-thread solve role) but the forward is slower, since the
-  // solve role overlaps the strips of the other segments.
+  // solve role overlaps the strips.
   const int mode = ns ? 0 : (solver == DYRA_SOLVER_CHOL ? 2 : 1);
   // S3: M_b, G_b (bf16: with the sweep solve in the same launch)
   bool solved = false;
@@ -3188,9 +3219,9 @@ void forward_residual(const dyra_spec& s, const char* plan, const void* X, const
       // below the bf16 rounding of M', fp32 storage asks for the fp32 floor
       // (fp32 storage: a stall above 1e-5 goes to the fp64 sweep, so an
       // ill-conditioned G still gives an fp32-accurate inverse)
-      const float tol = BF ? 1e-4f : 2e-6f, accept = BF ? 1e-2f : 1e-5f;
-      hipLaunchKernelGGL(ns_inverse_kernel, dim3((unsigned)B), dim3(512), 0, st, G, Gi, Gi32, stat, prec, r, eps, 60,
-                         tol, accept);
+      const float tol = BF ? kNsTolBf16 : 2e-6f, accept = BF ? kNsAcceptBf16 : 1e-5f;
+      hipLaunchKernelGGL(ns_inverse_kernel, dim3((unsigned)B), dim3(512), 0, st, G, Gi, Gi32, stat, prec, r, eps,
+                         kNsMaxit, tol, accept);
       launch_sweep(G, Gi, Gi32, stat, prec, r, eps, B, true, st);
     } else if (solver == DYRA_SOLVER_CHOL) {
       launch_chol(G, Gi, Gi32, stat, prec, r, eps, B, st);
