@@ -37,7 +37,7 @@
  *     aligned.  "stream" is a hipStream_t passed as void* (NULL = default).
  *   - dtype: DYRA_F32 (fp32 storage, fp32 arithmetic) or DYRA_BF16 (bf16
  *     storage, fp32 accumulation); the r x r solves run in fp64 (sweep,
- *     Cholesky) or fp32 (Newton-Schulz) for both.
+ *     Cholesky) or at fp32 accuracy (Newton-Schulz) for both.
  *   - Size constraints: c1, c2, k, r multiples of 8; 1 <= r <= min(c1, c2);
  *     r <= 128.  Low-rank: k + r <= min(c1, c2).  Monarch: c1 == c2 ==
  *     mblk^2 with mblk == 32 (bf16 only).  BLAST: nb divides c1 and c2,
@@ -86,7 +86,7 @@ extern "C" {
                                  /* not finite still gives a non-finite row of Y_b)           */
 #define DYRA_SOLVE_NOCONV    2   /* reserved: an iterative solve without a usable result */
 #define DYRA_SOLVE_ZERO      3   /* trace(G_b) == 0 (X_b P == 0): R_b := 0               */
-#define DYRA_SOLVE_FALLBACK  4   /* Newton-Schulz did not reach its tolerance in fp32;    */
+#define DYRA_SOLVE_FALLBACK  4   /* Newton-Schulz did not reach its tolerance;            */
                                  /* R_b solved by the sweep instead (result valid)        */
 
 typedef struct {
