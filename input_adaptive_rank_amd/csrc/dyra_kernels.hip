@@ -2162,9 +2162,10 @@ __device__ __forceinline__ int ns_solve(const float* Gb, int r, float eps, int m
   return st;
 }
 
-// The standalone launch: one 512-thread workgroup per segment.  A segment
-// the iteration cannot solve keeps DYRA_SOLVE_FALLBACK for the sweep
-// launched after this kernel.
+// One 512-thread workgroup per segment.  A segment the iteration cannot
+// solve is re-solved in the same workgroup by the fp64 sweep (its buffers
+// overlay the iteration's) and reports DYRA_SOLVE_FALLBACK.
+static_assert(sizeof(SweepLds) <= NS_LDS, "the sweep's LDS fits in the iteration's");
 __global__ __launch_bounds__(512) void ns_inverse_kernel(const float* G, double* Ginv, float* Ginv32, int32_t* status,
                                                           int32_t* prec, int r, float eps, int maxit, float tol,
                                                           float accept) {
@@ -2172,12 +2173,23 @@ __global__ __launch_bounds__(512) void ns_inverse_kernel(const float* G, double*
   const int64_t b = blockIdx.x;
   bool conv;
   const int st = ns_solve(G + b * r * r, r, eps, maxit, tol, accept, sm, Ginv + b * r * r, Ginv32 + b * r * r,
-                             conv);
+                          conv);
+  if (conv) {
+    if (threadIdx.x == 0) {
+      status[b] = st;
+      // the fp32 apply: the iteration's own tolerance, not the apply's
+      // rounding, bounds the accuracy of M' for a Newton-Schulz inverse
+      prec[b] = 0;
+    }
+    return;
+  }
+  __syncthreads();   // every wave is done with the iteration's buffers
+  bool wide;
+  const int st2 = sweep_inverse<512, 4, 8>(G + b * r * r, Ginv + b * r * r, Ginv32 + b * r * r, r, eps,
+                                           *reinterpret_cast<SweepLds*>(sm), wide);
   if (threadIdx.x == 0) {
-    status[b] = conv ? st : DYRA_SOLVE_FALLBACK;
-    // the fp32 apply: the iteration's own tolerance, not the apply's
-    // rounding, bounds the accuracy of M' for a Newton-Schulz inverse
-    prec[b] = 0;
+    status[b] = st2 == DYRA_SOLVE_OK ? DYRA_SOLVE_FALLBACK : st2;
+    prec[b] = st2 == DYRA_SOLVE_OK && wide ? 1 : 0;
   }
 }
 
@@ -2679,23 +2691,17 @@ __global__ __launch_bounds__(64 * NB) void gram_partial_kernel(const bf16_t* __r
     }
 }
 
-// S4a as its own launch: one 256-thread workgroup per segment.  With
-// only_flagged, segments whose status is not DYRA_SOLVE_FALLBACK are left
-// alone: the Newton-Schulz kernel flags the segments it could not solve, and
-// those keep the FALLBACK status when the sweep succeeds.
+// S4a as its own launch (fp32 storage, whose token reduction has no solve
+// role): one workgroup per segment.
 template <int NT, int TB, int TBJ = TB>
 __global__ __launch_bounds__(NT) void sweep_inverse_kernel(const float* G, double* Ginv, float* Ginv32,
-                                                           int32_t* status, int32_t* prec, int r, float eps,
-                                                           int only_flagged) {
+                                                           int32_t* status, int32_t* prec, int r, float eps) {
   __shared__ SweepLds sl;
   const int64_t b = blockIdx.x;
-  // every thread reads the flag before the sweep's first barrier; thread 0
-  // rewrites it only after the sweep
-  if (only_flagged && status[b] != DYRA_SOLVE_FALLBACK) return;
   bool wide;
   const int st = sweep_inverse<NT, TB, TBJ>(G + b * r * r, Ginv + b * r * r, Ginv32 + b * r * r, r, eps, sl, wide);
   if (threadIdx.x == 0) {
-    status[b] = (only_flagged && st == DYRA_SOLVE_OK) ? DYRA_SOLVE_FALLBACK : st;
+    status[b] = st;
     prec[b] = st == DYRA_SOLVE_OK && wide ? 1 : 0;
   }
 }
@@ -2704,14 +2710,13 @@ __global__ __launch_bounds__(NT) void sweep_inverse_kernel(const float* G, doubl
 // tiles (two waves per SIMD, 212 registers a lane; 1024 threads of 4 x 4
 // leave 128 registers a lane and the sweep spilled to scratch).
 void launch_sweep(const float* G, double* Ginv, float* Ginv32, int32_t* status, int32_t* prec, int r, float eps,
-                  int64_t B, bool only_flagged, hipStream_t st) {
-  const int f = only_flagged ? 1 : 0;
+                  int64_t B, hipStream_t st) {
   if (r <= 64)
     hipLaunchKernelGGL((sweep_inverse_kernel<256, 4>), dim3((unsigned)B), dim3(256), 0, st, G, Ginv, Ginv32, status, prec,
-                       r, eps, f);
+                       r, eps);
   else
     hipLaunchKernelGGL((sweep_inverse_kernel<512, 4, 8>), dim3((unsigned)B), dim3(512), 0, st, G, Ginv, Ginv32, status,
-                       prec, r, eps, f);
+                       prec, r, eps);
 }
 
 // The Cholesky route as its own launch (fp32 storage): one workgroup per
@@ -3214,7 +3219,7 @@ void forward_residual(const dyra_spec& s, const char* plan, const void* X, const
   // S4: Ginv_b (unless solved above), M'_b = Ginv_b M_b
   if (!solved) {
     if (ns) {
-      // Newton-Schulz, then the sweep for any segment it flags.
+      // Newton-Schulz (the sweep for any segment it cannot solve).
       // ||I - A' X||_F bounds the relative error of the inverse: 1e-4 is far
       // below the bf16 rounding of M', fp32 storage asks for the fp32 floor
       // (fp32 storage: a stall above 1e-5 goes to the fp64 sweep, so an
@@ -3222,11 +3227,10 @@ void forward_residual(const dyra_spec& s, const char* plan, const void* X, const
       const float tol = BF ? kNsTolBf16 : 2e-6f, accept = BF ? kNsAcceptBf16 : 1e-5f;
       hipLaunchKernelGGL(ns_inverse_kernel, dim3((unsigned)B), dim3(512), 0, st, G, Gi, Gi32, stat, prec, r, eps,
                          kNsMaxit, tol, accept);
-      launch_sweep(G, Gi, Gi32, stat, prec, r, eps, B, true, st);
     } else if (solver == DYRA_SOLVER_CHOL) {
       launch_chol(G, Gi, Gi32, stat, prec, r, eps, B, st);
     } else {
-      launch_sweep(G, Gi, Gi32, stat, prec, r, eps, B, false, st);
+      launch_sweep(G, Gi, Gi32, stat, prec, r, eps, B, st);
     }
   }
   launch_apply_inverse<T>(Gi, Gi32, M, Mp, B, r, c1, stat, prec, st);
