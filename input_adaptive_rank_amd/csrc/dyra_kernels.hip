@@ -2768,15 +2768,93 @@ void launch_chol(const float* G, double* Ginv, float* Ginv32, int32_t* status, i
 // of Ginv (its rounding and the fp32 sums stay far below the storage
 // rounding of M'); a segment whose solve met a relative pivot below 2^-5
 // (near-singular: fewer tokens than r, or nearly collinear columns of L_b)
-// is left to apply_inverse_f64_kernel, since there Ginv has entries of
-// order 1 / lambda_b that cancel in Ginv M.  The RB row blocks share the
+// takes the same task in fp64 (apply_rows_f64 on the fp64 inverse), since
+// there Ginv has entries of order 1 / lambda_b that cancel in Ginv M; the
+// choice is per wave (a task lies in one segment), in one launch.  The RB
+// row blocks share the
 // wave's M loads (accumulator of lane (i, g): rows 4 g .. + 3).  With
 // NTC > 0 (r <= 16 NTC) every chunk is loaded before the first product, so
 // a wave waits on memory once; otherwise the next chunk is loaded before
 // the current one is multiplied.
+// Rows 16 rb .. 16 rb + 15 of M'_b = Ginv_b M_b at 64-column tile ct in
+// fp64, for a segment the solve flagged (prec[b] = 1): the same
+// reduction-index permutation as the fp32 path, on v_mfma_f64_16x16x4f64 (operands one double per lane, k = lane / 16;
+// accumulator rows interleaved: element v of lane (i, g) is row g + 4 v).
+// With NTC > 0 (r <= 16 NTC) every chunk's loads are issued before the
+// first product, so a wave waits on memory once.
+template <typename T, int NTC>
+__device__ __forceinline__ void apply_rows_f64(const double* __restrict__ Gb, const float* __restrict__ Mb,
+                                               T* __restrict__ Mp, int r, int64_t c1, int64_t b, int rb,
+                                               int64_t ct, int lane) {
+  const int i = lane & 15, g = lane >> 4;
+  const int64_t col = ct * 64 + 4 * i;          // c1 % 8 == 0: all four columns or none
+  const bool cok = col < c1;
+  const int row = rb * 16 + i;
+  const int nt = (r + 15) >> 4;
+  f64x4 acc[4];
+#pragma unroll
+  for (int jb = 0; jb < 4; ++jb) acc[jb] = f64x4{0.0, 0.0, 0.0, 0.0};
+  // chunk t: the lane's Ginv run (row `row`, q = 16 t + 4 g .. + 3) and its
+  // four M runs (rows q, columns col .. col + 3); past r or c1 they read as
+  // zeros (loads clamped to valid addresses, values selected afterwards)
+  auto load = [&](int t, double4& a, float4 (&m)[4]) {
+    const int q0 = 16 * t + 4 * g;              // r % 4 == 0: all four q or none
+    const bool aok = row < r && q0 < r, mok = cok && q0 < r;
+    const double4 av = *reinterpret_cast<const double4*>(Gb + (int64_t)(aok ? row : 0) * r + (aok ? q0 : 0));
+    a = aok ? av : make_double4(0.0, 0.0, 0.0, 0.0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float4 mv = *reinterpret_cast<const float4*>(Mb + (int64_t)(mok ? q0 + e : 0) * c1 + (mok ? col : 0));
+      m[e] = mok ? mv : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  auto mul = [&](const double4& a, const float4 (&m)[4]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const double av = e == 0 ? a.x : e == 1 ? a.y : e == 2 ? a.z : a.w;
+      acc[0] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, (double)m[e].x, acc[0], 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, (double)m[e].y, acc[1], 0, 0, 0);
+      acc[2] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, (double)m[e].z, acc[2], 0, 0, 0);
+      acc[3] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, (double)m[e].w, acc[3], 0, 0, 0);
+    }
+  };
+  if constexpr (NTC > 0) {
+    double4 a[NTC];
+    float4 m[NTC][4];
+#pragma unroll
+    for (int t = 0; t < NTC; ++t) load(t, a[t], m[t]);
+#pragma unroll
+    for (int t = 0; t < NTC; ++t) mul(a[t], m[t]);
+  } else {
+    for (int t = 0; t < nt; ++t) {
+      double4 a;
+      float4 m[4];
+      load(t, a, m);
+      mul(a, m);
+    }
+  }
+  if (!cok) return;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int orow = rb * 16 + g + 4 * v;
+    if (orow >= r) continue;
+    const int64_t o = (b * r + orow) * c1 + col;
+    if constexpr (TT<T>::ESZ == 2) {
+      uint2 pk;
+      pk.x = (uint32_t)f2bf((float)acc[0][v]) | ((uint32_t)f2bf((float)acc[1][v]) << 16);
+      pk.y = (uint32_t)f2bf((float)acc[2][v]) | ((uint32_t)f2bf((float)acc[3][v]) << 16);
+      *reinterpret_cast<uint2*>(Mp + o) = pk;
+    } else {
+      *reinterpret_cast<float4*>(Mp + o) =
+          make_float4((float)acc[0][v], (float)acc[1][v], (float)acc[2][v], (float)acc[3][v]);
+    }
+  }
+}
+
 constexpr int AI_WAVES = 4;
 template <typename T, int RB, int NTC = 0>
-__global__ __launch_bounds__(64 * AI_WAVES) void apply_inverse_kernel(const float* __restrict__ Ginv32,
+__global__ __launch_bounds__(64 * AI_WAVES) void apply_inverse_kernel(const double* __restrict__ Ginv,
+                                                                      const float* __restrict__ Ginv32,
                                                                       const float* __restrict__ M,
                                                                       T* __restrict__ Mp, int r, int64_t c1,
                                                                       int64_t tasks,
@@ -2820,7 +2898,14 @@ __global__ __launch_bounds__(64 * AI_WAVES) void apply_inverse_kernel(const floa
       *reinterpret_cast<float4*>(dst) = make_float4(v0, v1, v2, v3);
     }
   };
-  if (wide) return;                           // apply_inverse_f64_kernel's segment
+  if (wide) {
+    // fp64 for this task's row blocks; the M runs are re-read per block (in
+    // cache), which only flagged segments pay
+#pragma unroll 1
+    for (int j = 0; j < RB; ++j)
+      apply_rows_f64<T, RB == 1 ? NTC : 0>(Ginv + b * r * r, Mb, Mp, r, c1, b, grp * RB + j, ct, lane);
+    return;
+  }
   // ---- fp32 (zeros for an unsolved segment) ----
   auto load = [&](int t, float4 (&a)[RB], float4 (&m)[4]) {
 #pragma unroll
@@ -2881,97 +2966,6 @@ __global__ __launch_bounds__(64 * AI_WAVES) void apply_inverse_kernel(const floa
     }
 }
 
-// M'_b = Ginv_b M_b in fp64 for the segments the solve flagged (prec[b] = 1;
-// every other wave returns at once): one wave per (segment, 16-row block,
-// 64-column tile), the same reduction-index permutation as the fp32 kernel,
-// on v_mfma_f64_16x16x4f64 (operands one double per lane, k = lane / 16;
-// accumulator rows interleaved: element v of lane (i, g) is row g + 4 v).
-// With NTC > 0 (r <= 16 NTC) every chunk's loads are issued before the
-// first product, so a wave waits on memory once.
-template <int NTC>
-__global__ __launch_bounds__(64 * AI_WAVES) void apply_inverse_f64_kernel(const double* __restrict__ Ginv,
-                                                                          const float* __restrict__ M,
-                                                                          bf16_t* __restrict__ Mp16,
-                                                                          float* __restrict__ Mp32, int r,
-                                                                          int64_t c1, int64_t tasks,
-                                                                          const int32_t* __restrict__ status,
-                                                                          const int32_t* __restrict__ prec) {
-  const int lane = threadIdx.x & 63;
-  const int64_t task = (int64_t)blockIdx.x * AI_WAVES + (threadIdx.x >> 6);
-  if (task >= tasks) return;
-  const int nrb = (r + 15) >> 4;
-  const int64_t tiles = (c1 + 63) >> 6;
-  const int rb = (int)(task % nrb);
-  const int64_t ct = (task / nrb) % tiles, b = task / (nrb * tiles);
-  const int sb = status[b];
-  if (!((sb == DYRA_SOLVE_OK || sb == DYRA_SOLVE_FALLBACK) && prec[b] != 0)) return;
-  const int i = lane & 15, g = lane >> 4;
-  const double* Gb = Ginv + b * r * r;
-  const float* Mb = M + b * r * c1;
-  const int64_t col = ct * 64 + 4 * i;          // c1 % 8 == 0: all four columns or none
-  const bool cok = col < c1;
-  const int row = rb * 16 + i;
-  const int nt = (r + 15) >> 4;
-  f64x4 acc[4];
-#pragma unroll
-  for (int jb = 0; jb < 4; ++jb) acc[jb] = f64x4{0.0, 0.0, 0.0, 0.0};
-  // chunk t: the lane's Ginv run (row `row`, q = 16 t + 4 g .. + 3) and its
-  // four M runs (rows q, columns col .. col + 3); past r or c1 they read as
-  // zeros (loads clamped to valid addresses, values selected afterwards)
-  auto load = [&](int t, double4& a, float4 (&m)[4]) {
-    const int q0 = 16 * t + 4 * g;              // r % 4 == 0: all four q or none
-    const bool aok = row < r && q0 < r, mok = cok && q0 < r;
-    const double4 av = *reinterpret_cast<const double4*>(Gb + (int64_t)(aok ? row : 0) * r + (aok ? q0 : 0));
-    a = aok ? av : make_double4(0.0, 0.0, 0.0, 0.0);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float4 mv = *reinterpret_cast<const float4*>(Mb + (int64_t)(mok ? q0 + e : 0) * c1 + (mok ? col : 0));
-      m[e] = mok ? mv : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-  };
-  auto mul = [&](const double4& a, const float4 (&m)[4]) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const double av = e == 0 ? a.x : e == 1 ? a.y : e == 2 ? a.z : a.w;
-      acc[0] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, (double)m[e].x, acc[0], 0, 0, 0);
-      acc[1] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, (double)m[e].y, acc[1], 0, 0, 0);
-      acc[2] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, (double)m[e].z, acc[2], 0, 0, 0);
-      acc[3] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, (double)m[e].w, acc[3], 0, 0, 0);
-    }
-  };
-  if constexpr (NTC > 0) {
-    double4 a[NTC];
-    float4 m[NTC][4];
-#pragma unroll
-    for (int t = 0; t < NTC; ++t) load(t, a[t], m[t]);
-#pragma unroll
-    for (int t = 0; t < NTC; ++t) mul(a[t], m[t]);
-  } else {
-    for (int t = 0; t < nt; ++t) {
-      double4 a;
-      float4 m[4];
-      load(t, a, m);
-      mul(a, m);
-    }
-  }
-  if (!cok) return;
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int orow = rb * 16 + g + 4 * v;
-    if (orow >= r) continue;
-    const int64_t o = (b * r + orow) * c1 + col;
-    if (Mp16) {
-      uint2 pk;
-      pk.x = (uint32_t)f2bf((float)acc[0][v]) | ((uint32_t)f2bf((float)acc[1][v]) << 16);
-      pk.y = (uint32_t)f2bf((float)acc[2][v]) | ((uint32_t)f2bf((float)acc[3][v]) << 16);
-      *reinterpret_cast<uint2*>(Mp16 + o) = pk;
-    } else {
-      *reinterpret_cast<float4*>(Mp32 + o) =
-          make_float4((float)acc[0][v], (float)acc[1][v], (float)acc[2][v], (float)acc[3][v]);
-    }
-  }
-}
-
 // M'_b = Ginv_b M_b for B segments of r x c1: four row blocks per wave when
 // that still leaves at least two waves per SIMD of a 256-CU chip, else one.
 template <typename T>
@@ -2981,31 +2975,17 @@ void launch_apply_inverse(const double* Gi, const float* Gi32, const float* M, T
   const int64_t wide = B * tiles * ((nrb + 3) / 4);
   if (nrb >= 4 && wide >= 2048) {
     hipLaunchKernelGGL((apply_inverse_kernel<T, 4>), dim3((unsigned)((wide + AI_WAVES - 1) / AI_WAVES)),
-                       dim3(64 * AI_WAVES), 0, st, Gi32, M, Mp, r, c1, wide, stat, prec);
+                       dim3(64 * AI_WAVES), 0, st, Gi, Gi32, M, Mp, r, c1, wide, stat, prec);
   } else {
     const int64_t tasks = B * tiles * nrb;
     const dim3 grid((unsigned)((tasks + AI_WAVES - 1) / AI_WAVES)), block(64 * AI_WAVES);
     if (r <= 32)
-      hipLaunchKernelGGL((apply_inverse_kernel<T, 1, 2>), grid, block, 0, st, Gi32, M, Mp, r, c1, tasks, stat, prec);
+      hipLaunchKernelGGL((apply_inverse_kernel<T, 1, 2>), grid, block, 0, st, Gi, Gi32, M, Mp, r, c1, tasks, stat, prec);
     else if (r <= 64)
-      hipLaunchKernelGGL((apply_inverse_kernel<T, 1, 4>), grid, block, 0, st, Gi32, M, Mp, r, c1, tasks, stat, prec);
+      hipLaunchKernelGGL((apply_inverse_kernel<T, 1, 4>), grid, block, 0, st, Gi, Gi32, M, Mp, r, c1, tasks, stat, prec);
     else
-      hipLaunchKernelGGL((apply_inverse_kernel<T, 1>), grid, block, 0, st, Gi32, M, Mp, r, c1, tasks, stat, prec);
+      hipLaunchKernelGGL((apply_inverse_kernel<T, 1>), grid, block, 0, st, Gi, Gi32, M, Mp, r, c1, tasks, stat, prec);
   }
-  // the flagged segments in fp64 (a second launch: its registers do not
-  // lower the fp32 kernel's occupancy)
-  const int64_t t64 = B * tiles * nrb;
-  bf16_t* m16 = nullptr;
-  float* m32 = nullptr;
-  if constexpr (TT<T>::ESZ == 2) m16 = reinterpret_cast<bf16_t*>(Mp);
-  else m32 = reinterpret_cast<float*>(Mp);
-  const dim3 g64((unsigned)((t64 + AI_WAVES - 1) / AI_WAVES)), b64(64 * AI_WAVES);
-  if (r <= 32)
-    hipLaunchKernelGGL((apply_inverse_f64_kernel<2>), g64, b64, 0, st, Gi, M, m16, m32, r, c1, t64, stat, prec);
-  else if (r <= 64)
-    hipLaunchKernelGGL((apply_inverse_f64_kernel<4>), g64, b64, 0, st, Gi, M, m16, m32, r, c1, t64, stat, prec);
-  else
-    hipLaunchKernelGGL((apply_inverse_f64_kernel<0>), g64, b64, 0, st, Gi, M, m16, m32, r, c1, t64, stat, prec);
 }
 
 // ===========================================================================
