@@ -1449,22 +1449,47 @@ __device__ __forceinline__ double recip_pos(double D) {
   return fma(x, e, x);
 }
 
+// 1 / D for D > 0 in fp32: the hardware reciprocal (1 ulp) and one Newton step.
+__device__ __forceinline__ float recip_pos(float D) {
+  const float x = __builtin_amdgcn_rcpf(D);
+  return fmaf(x, fmaf(-D, x, 1.f), x);
+}
+template <typename S> struct SwPair;
+template <> struct SwPair<double> {
+  using T = double2;
+  static __device__ __forceinline__ T make(double a, double b) { return make_double2(a, b); }
+};
+template <> struct SwPair<float> {
+  using T = float2;
+  static __device__ __forceinline__ T make(float a, float b) { return make_float2(a, b); }
+};
+// Returned by the fp32 pass (S = float, PASS32) when the segment needs the
+// fp64 sweep: a relative pivot below kWidePivot, or any pivot failure.
+constexpr int kSweepRedo64 = -1;
+
 // Gb: r x r row-major fp32 (global or LDS); Ob: r x r row-major fp64,
-// receives the inverse (zeros unless the status is OK).  The arithmetic is
-// fp64: the ridge bounds cond(G + lambda I) only by about r / eps (~1e8 for
-// eps = 1e-6), past what fp32 elimination survives.  Needs r % SW_BK == 0,
-// r <= 128 and ceil(r / TB)^2 <= NT.  Returns the status (same in every
-// thread).
-template <int NT, int TB, int TBJ = TB>
+// receives the inverse (zeros unless the status is OK).  S is the
+// arithmetic: fp64, since the ridge bounds cond(G + lambda I) only by about
+// r / eps (~1e8 for eps = 1e-6), past what fp32 elimination survives; or fp32
+// for the first pass of sweep_inverse_mixed (PASS32), which stops at the
+// first relative pivot below kWidePivot (or any pivot failure), writes
+// nothing and returns kSweepRedo64.  Needs r % SW_BK == 0, r <= 128 and
+// ceil(r / TB)^2 <= NT.  Returns the status (same in every thread).
+template <int NT, int TB, int TBJ = TB, typename S = double, bool PASS32 = false>
 __device__ __forceinline__ int sweep_inverse(const float* Gb, double* Ob, float* Ob32, int r, float eps,
                                              SweepLds& sh, bool& wide) {
+  static_assert(!PASS32 || sizeof(S) == 4, "the stopping pass is the fp32 one");
+  using P2 = SwPair<S>;
+  using V2 = typename P2::T;
+  // the pivot-row buffers hold S values (fp32 uses the first half)
+  S(*pvs)[SW_BK][128] = reinterpret_cast<S(*)[SW_BK][128]>(&sh.pv[0][0][0]);
   // thread tiles of TB rows x TBJ columns
   static_assert(TB % SW_BK == 0 && TB % 2 == 0 && TBJ % SW_BK == 0 && TBJ % 2 == 0, "tile");
   const int tid = threadIdx.x;
   const int tpr = (r + TBJ - 1) / TBJ;
   const int i0 = (tid / tpr) * TB, j0 = (tid % tpr) * TBJ;
   const bool own = i0 < r;
-  double a[TB][TBJ];
+  S a[TB][TBJ];
   float trf = 0.f;
 #pragma unroll
   for (int x = 0; x < TB; ++x)
@@ -1489,12 +1514,12 @@ __device__ __forceinline__ int sweep_inverse(const float* Gb, double* Ob, float*
 #pragma unroll
       for (int y = 0; y < TBJ; y += 2)
         if (j0 + y < r)
-          *reinterpret_cast<double2*>(&sh.pv[buf][i - k0][j0 + y]) = make_double2(a[x][y], a[x][y + 1]);
+          *reinterpret_cast<V2*>(&pvs[buf][i - k0][j0 + y]) = P2::make(a[x][y], a[x][y + 1]);
     }
   };
   wide = false;
   if (st == DYRA_SOLVE_OK) {
-    const double lam = (double)(eps * tr / (float)r);
+    const S lam = (S)(eps * tr / (float)r);
 #pragma unroll
     for (int x = 0; x < TB; ++x)
 #pragma unroll
@@ -1504,34 +1529,39 @@ __device__ __forceinline__ int sweep_inverse(const float* Gb, double* Ob, float*
     for (int x = 0; x < TB; ++x) publish_row(x, 0, 0);
     __syncthreads();
     for (int kb = 0, blk = 0; kb < r; kb += SW_BK, ++blk) {
-      const double(*buf)[128] = sh.pv[blk & 1];
+      const S(*buf)[128] = pvs[blk & 1];
       // Q <- -A_KK^-1 by sweeping the pivot block's own pivots
-      double Q[SW_BK][SW_BK];
+      S Q[SW_BK][SW_BK];
 #pragma unroll
       for (int x = 0; x < SW_BK; ++x)
 #pragma unroll
         for (int y = 0; y < SW_BK; y += 2) {
-          const double2 v = *reinterpret_cast<const double2*>(&buf[x][kb + y]);
+          const V2 v = *reinterpret_cast<const V2*>(&buf[x][kb + y]);
           Q[x][y] = v.x;
           Q[x][y + 1] = v.y;
         }
       bool bad = false;
 #pragma unroll
       for (int p = 0; p < SW_BK; ++p) {
-        const double D = Q[p][p];
-        if (!(D > 0.0) || !isfinite(D)) bad = true;
-        if (eps == 0.f && !(D > kSingularPivotRel * sh.diag0[kb + p])) bad = true;
-        if (D < kWidePivot * (sh.diag0[kb + p] + lam)) wide = true;   // relative pivot below 2^-5
-        const double invD = recip_pos(D);
-        double c[SW_BK];
+        const S D = Q[p][p];
+        if (!(D > (S)0) || !isfinite(D)) bad = true;
+        const S dg = (S)sh.diag0[kb + p];
+        if (eps == 0.f && !(D > (S)kSingularPivotRel * dg)) bad = true;
+        if (D < (S)kWidePivot * (dg + lam)) wide = true;   // relative pivot below 2^-5
+        const S invD = recip_pos(D);
+        S c[SW_BK];
 #pragma unroll
-        for (int x = 0; x < SW_BK; ++x) c[x] = x == p ? -1.0 : Q[x][p];
+        for (int x = 0; x < SW_BK; ++x) c[x] = x == p ? (S)-1 : Q[x][p];
 #pragma unroll
         for (int x = 0; x < SW_BK; ++x) {
-          const double f = -c[x] * invD;
+          const S f = -c[x] * invD;
 #pragma unroll
-          for (int y = 0; y < SW_BK; ++y) Q[x][y] = fma(f, c[y], (x == p || y == p) ? 0.0 : Q[x][y]);
+          for (int y = 0; y < SW_BK; ++y) Q[x][y] = fma(f, c[y], (x == p || y == p) ? (S)0 : Q[x][y]);
         }
+      }
+      if (PASS32 && (bad || wide)) {   // uniform: the fp64 sweep takes this segment
+        st = kSweepRedo64;
+        break;
       }
       if (bad) {   // uniform: every thread read the same pivot block
         st = DYRA_SOLVE_NOT_SPD;
@@ -1541,22 +1571,22 @@ __device__ __forceinline__ int sweep_inverse(const float* Gb, double* Ob, float*
       // (a multiple of SW_BK) when this tile holds them
       const int oi = kb - i0, oj = kb - j0;
       // C_j = pivot rows at this tile's columns
-      double cj[SW_BK][TBJ];
+      S cj[SW_BK][TBJ];
 #pragma unroll
       for (int p = 0; p < SW_BK; ++p)
 #pragma unroll
         for (int y = 0; y < TBJ; y += 2) {
-          const double2 v = *reinterpret_cast<const double2*>(&buf[p][j0 + y]);
+          const V2 v = *reinterpret_cast<const V2*>(&buf[p][j0 + y]);
           cj[p][y] = v.x;
           cj[p][y + 1] = v.y;
         }
 #pragma unroll
       for (int x = 0; x < TB; x += 2) {
         // C_i for rows x, x + 1: pivot rows at column i (symmetry)
-        double ci[2][SW_BK];
+        S ci[2][SW_BK];
 #pragma unroll
         for (int q = 0; q < SW_BK; ++q) {
-          const double2 v = own ? *reinterpret_cast<const double2*>(&buf[q][i0 + x]) : make_double2(0.0, 0.0);
+          const V2 v = own ? *reinterpret_cast<const V2*>(&buf[q][i0 + x]) : P2::make(0, 0);
           ci[0][q] = v.x;
           ci[1][q] = v.y;
         }
@@ -1565,10 +1595,10 @@ __device__ __forceinline__ int sweep_inverse(const float* Gb, double* Ob, float*
           const int xx = x + h;
           const bool iK = oi == (xx & ~(SW_BK - 1));
           // d = C_i A_KK^-1 = -C_i Q; a row inside the block has C_i = -e_i
-          double d[SW_BK];
+          S d[SW_BK];
 #pragma unroll
           for (int p = 0; p < SW_BK; ++p) {
-            double v = 0.0;
+            S v = 0;
 #pragma unroll
             for (int q = 0; q < SW_BK; ++q) v = fma(ci[h][q], Q[q][p], v);
             d[p] = iK ? Q[xx & (SW_BK - 1)][p] : -v;
@@ -1576,7 +1606,7 @@ __device__ __forceinline__ int sweep_inverse(const float* Gb, double* Ob, float*
 #pragma unroll
           for (int y = 0; y < TBJ; ++y) {
             const bool jK = oj == (y & ~(SW_BK - 1));
-            double v = iK ? 0.0 : a[xx][y];
+            S v = iK ? (S)0 : a[xx][y];
 #pragma unroll
             for (int p = 0; p < SW_BK; ++p) v = fma(-d[p], cj[p][y], v);
             // a column inside the block has C_j = -e_j: a_ij <- d_j
@@ -1588,16 +1618,32 @@ __device__ __forceinline__ int sweep_inverse(const float* Gb, double* Ob, float*
       __syncthreads();
     }
   }
+  if (PASS32 && st != DYRA_SOLVE_OK) return kSweepRedo64;
 #pragma unroll
   for (int x = 0; x < TB; ++x)
 #pragma unroll
     for (int y = 0; y < TBJ; ++y)
       if (own && i0 + x < r && j0 + y < r) {
-        const double v = st == DYRA_SOLVE_OK ? -a[x][y] : 0.0;
+        const double v = st == DYRA_SOLVE_OK ? -(double)a[x][y] : 0.0;
         Ob[(i0 + x) * r + j0 + y] = v;
         Ob32[(i0 + x) * r + j0 + y] = (float)v;
       }
   return st;
+}
+
+// The sweep in two passes: fp32 first (half the fp64 chain latency and LDS
+// bytes per step); a segment whose fp32 pass meets a relative pivot below
+// kWidePivot, or any pivot failure, is swept again in fp64, which then sets
+// its status and its apply precision.  So every decision near a threshold
+// (singular at eps = 0, fp64 apply) is taken in fp64, and an accepted fp32
+// inverse has all relative pivots at or above 2^-5.
+template <int NT, int TB, int TBJ = TB>
+__device__ __forceinline__ int sweep_inverse_mixed(const float* Gb, double* Ob, float* Ob32, int r, float eps,
+                                                   SweepLds& sh, bool& wide) {
+  const int st = sweep_inverse<NT, TB, TBJ, float, true>(Gb, Ob, Ob32, r, eps, sh, wide);
+  if (st != kSweepRedo64) return st;
+  __syncthreads();   // every thread is past the fp32 pass's reads of the shared buffers
+  return sweep_inverse<NT, TB, TBJ, double>(Gb, Ob, Ob32, r, eps, sh, wide);
 }
 
 // ===========================================================================
@@ -2570,7 +2616,7 @@ __global__ __launch_bounds__(S3_NT, NRB <= 4 ? 2 : 1) void s3_reduce_solve_kerne
         st = chol_inverse<S3_NT, TB>(Gs, Gi + b * r * r, Gi32 + b * r * r, r, eps, *sl,
                                      reinterpret_cast<double*>(lds), wide);
       else
-        st = sweep_inverse<S3_NT, TB>(Gs, Gi + b * r * r, Gi32 + b * r * r, r, eps, *sl, wide);
+        st = sweep_inverse_mixed<S3_NT, TB>(Gs, Gi + b * r * r, Gi32 + b * r * r, r, eps, *sl, wide);
       if (threadIdx.x == 0) {
         status[b] = st;
         prec[b] = st == DYRA_SOLVE_OK && wide ? 1 : 0;
@@ -2699,7 +2745,7 @@ __global__ __launch_bounds__(NT) void sweep_inverse_kernel(const float* G, doubl
   __shared__ SweepLds sl;
   const int64_t b = blockIdx.x;
   bool wide;
-  const int st = sweep_inverse<NT, TB, TBJ>(G + b * r * r, Ginv + b * r * r, Ginv32 + b * r * r, r, eps, sl, wide);
+  const int st = sweep_inverse_mixed<NT, TB, TBJ>(G + b * r * r, Ginv + b * r * r, Ginv32 + b * r * r, r, eps, sl, wide);
   if (threadIdx.x == 0) {
     status[b] = st;
     prec[b] = st == DYRA_SOLVE_OK && wide ? 1 : 0;
@@ -2974,8 +3020,11 @@ void launch_apply_inverse(const double* Gi, const float* Gi32, const float* M, T
   const int64_t tiles = (c1 + 63) / 64, nrb = (r + 15) / 16;
   const int64_t wide = B * tiles * ((nrb + 3) / 4);
   if (nrb >= 4 && wide >= 2048) {
-    hipLaunchKernelGGL((apply_inverse_kernel<T, 4>), dim3((unsigned)((wide + AI_WAVES - 1) / AI_WAVES)),
-                       dim3(64 * AI_WAVES), 0, st, Gi, Gi32, M, Mp, r, c1, wide, stat, prec);
+    const dim3 grid((unsigned)((wide + AI_WAVES - 1) / AI_WAVES)), block(64 * AI_WAVES);
+    if (r <= 64)
+      hipLaunchKernelGGL((apply_inverse_kernel<T, 4, 4>), grid, block, 0, st, Gi, Gi32, M, Mp, r, c1, wide, stat, prec);
+    else
+      hipLaunchKernelGGL((apply_inverse_kernel<T, 4>), grid, block, 0, st, Gi, Gi32, M, Mp, r, c1, wide, stat, prec);
   } else {
     const int64_t tasks = B * tiles * nrb;
     const dim3 grid((unsigned)((tasks + AI_WAVES - 1) / AI_WAVES)), block(64 * AI_WAVES);
