@@ -668,7 +668,13 @@ __global__ __launch_bounds__(C::NT + NL * 64, 1) void s6_lowrank_ws_kernel(
       p_alo = (int)sg.lo(ibx) - ic.m0; p_ahi = (int)sg.hi(ibx) - ic.m0;
       p_fa = p_live && p_alo <= 0 && p_ahi >= C::BM ? 1 : 0;
     };
-    set_tv();
+    // a tile's first part: [T | V], or with no static part (k = 0) its
+    // first segment's [L_b | R_b] (the bias descriptor comes from set_tv)
+    auto begin_tile = [&]() __attribute__((always_inline)) {
+      set_tv();
+      if (nk0 == 0) set_lr(ic.b0);
+    };
+    begin_tile();
     // one k-tile into the slot at byte offset `slot`; past the last tile
     // every lane reads out of range, so the DMA count (and with it every
     // wait) stays the same at each step
@@ -711,11 +717,13 @@ __global__ __launch_bounds__(C::NT + NL * 64, 1) void s6_lowrank_ws_kernel(
       if (p_live) {
         p_kb += 128;
         if (--p_left == 0) {
-          if (p_kind == 0) set_lr(ic.b0);
-          else if (p_ib < ic.bl) set_lr(p_ib + 1);
+          if (p_kind == 0 && nkr > 0) set_lr(ic.b0);
+          else if (p_kind == 1 && p_ib < ic.bl) set_lr(p_ib + 1);
           else {
+            // the tile's last part (with no residual part, r = 0: its
+            // [T | V] part), so the next part is the next tile's first
             advance(ic);
-            set_tv();
+            begin_tile();
           }
         }
       }

@@ -64,6 +64,11 @@ SMALL = [
     # first-stage Gram partials: 170-token segments, so nearly every 160-row
     # tile meets two segments (both partial slots in use)
     sc(W["vitl_fc1"], name="first_stage_gram_short_segments", B=20, s=170, c1=384, c2=512, k=256, r=64),
+    # the right factor R^T (4096 x 40 * 64) has 320 tiles of 256 x 128, more
+    # than one per persistent workgroup of its no-residual-part GEMM: each
+    # workgroup's later tiles must get their own operands (they came out of
+    # zero-filled loads when the loaders did not leave an empty L R part)
+    sc(W["vitl_fc1"], name="right_factor_several_tiles", B=40, s=160, c1=256, c2=4096, k=64, r=64),
     # few (segment, column strip) pairs: the M strips split their tokens
     # into parts whose fp32 partials a second launch adds (4 parts here)
     sc(W["vitl_fc1"], name="token_split_long_segments", B=2, s=2100, c1=512, c2=512, k=64, r=64),
