@@ -100,6 +100,16 @@ def test_full_size(name):
     assert np.all(status == D.SOLVE_OK)
 
 
+def test_full_size_larger_batch():
+    """ViT-L fc1 at 40 images (41160 tokens): more first-stage tiles than
+    CUs (a second round), 40 segments in the XCD-grouped token reduction,
+    and a right factor R^T with 320 tiles of 256 x 128, more than one per
+    persistent workgroup."""
+    w = sc(W["vitl_fc1"], name="vitl_fc1_b40", B=40)
+    err, status, _, _ = run_same_factor_case(w)
+    assert np.all(status == D.SOLVE_OK)
+
+
 def test_zero_residual_gives_static_output_and_zero_status():
     """W of exact rank k: P = W_res = 0, so G_b = 0, status ZERO and
     Y = X W_hat + bias."""
