@@ -1912,6 +1912,57 @@ __device__ __forceinline__ int chol_inverse(const float* Gb, double* Ob, float* 
   return st;
 }
 
+// G_b = the sum of segment b's Gram partials, in order, into `out` (r x r
+// fp32, LDS or global; float4 columns, up to 8 partials' loads in flight per
+// thread): gchunks token chunks of the segment, or (gprows > 0) the first
+// stage's per-tile partials of the tiles of gprows tokens that the segment
+// meets, in slot 1 of its first tile when that tile starts in the previous
+// segment, else in slot 0.  The caller synchronises before reading `out`.
+template <int NT>
+__device__ __forceinline__ void gram_sum(const float* __restrict__ gpart, int gchunks, int64_t gprows, int64_t b,
+                                         int64_t lo, int64_t hi, int r, float* out) {
+  const int nq = r * r / 4;   // r % 8 == 0
+  const int64_t rb_lo = gprows > 0 ? lo / gprows : 0;
+  const int nparts = gprows > 0 ? (int)((hi - 1) / gprows - rb_lo + 1) : gchunks;
+  auto part_ptr = [&](int p) -> const float4* {
+    int64_t idx;
+    if (gprows > 0) {
+      const int64_t rb = rb_lo + p;
+      idx = rb * 2 + ((p == 0 && lo > rb * gprows) ? 1 : 0);
+    } else {
+      idx = b * gchunks + p;
+    }
+    return reinterpret_cast<const float4*>(gpart + idx * r * r);
+  };
+  for (int e0 = threadIdx.x; e0 < nq; e0 += 4 * NT) {
+    float4 acc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int c0 = 0; c0 < nparts; c0 += 8) {
+      float4 v[8][4];
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int e = e0 + i * NT;
+          v[c][i] = (c0 + c < nparts && e < nq) ? part_ptr(c0 + c)[e] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[i].x += v[c][i].x;
+          acc[i].y += v[c][i].y;
+          acc[i].z += v[c][i].z;
+          acc[i].w += v[c][i].w;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (e0 + i * NT < nq) reinterpret_cast<float4*>(out)[e0 + i * NT] = acc[i];
+  }
+}
+
 // ===========================================================================
 // S4a': Newton-Schulz inverse of one segment by one workgroup of 8 waves
 // on the 128 x 128 iterate.  Jacobi-scaled A' = D^-1/2 (G + lambda I) D^-1/2 (unit diagonal,
@@ -2220,11 +2271,20 @@ __device__ __forceinline__ int ns_solve(const float* Gb, int r, float eps, int m
 // solve is re-solved in the same workgroup by the fp64 sweep (its buffers
 // overlay the iteration's) and reports DYRA_SOLVE_FALLBACK.
 static_assert(sizeof(SweepLds) <= NS_LDS, "the sweep's LDS fits in the iteration's");
-__global__ __launch_bounds__(512) void ns_inverse_kernel(const float* G, double* Ginv, float* Ginv32, int32_t* status,
+// With gpart, the workgroup first sums segment b's Gram partials into G_b
+// (gram_sum), so the launch needs only the partials and can run beside the
+// M strips.
+__global__ __launch_bounds__(512) void ns_inverse_kernel(float* G, double* Ginv, float* Ginv32, int32_t* status,
                                                           int32_t* prec, int r, float eps, int maxit, float tol,
-                                                          float accept) {
+                                                          float accept, const float* __restrict__ gpart,
+                                                          int gchunks, int64_t gprows, SegMap sg) {
   __shared__ __attribute__((aligned(16))) char sm[NS_LDS];
   const int64_t b = blockIdx.x;
+  if (gpart) {
+    gram_sum<512>(gpart, gchunks, gprows, b, sg.lo(b), sg.hi(b), r, G + b * r * r);
+    __threadfence_block();
+    __syncthreads();   // G_b complete (the workgroup's own global writes)
+  }
   bool conv;
   const int st = ns_solve(G + b * r * r, r, eps, maxit, tol, accept, sm, Ginv + b * r * r, Ginv32 + b * r * r,
                           conv);
@@ -2501,7 +2561,8 @@ __global__ __launch_bounds__(S3_NT, NRB <= 4 ? 2 : 1) void s3_reduce_solve_kerne
     float* __restrict__ Gi32,
     int32_t* __restrict__ status, int32_t* __restrict__ prec, float eps, int strips, int64_t lt_seg_rows,
     int x_rel,
-    const float* __restrict__ gpart, int gchunks, int64_t gprows, int msplit, float* __restrict__ Mpart) {
+    const float* __restrict__ gpart, int gchunks, int64_t gprows, int msplit, float* __restrict__ Mpart,
+    int64_t nsr) {
   __shared__ __attribute__((aligned(16))) char lds[S3Lds<NB>::BYTES];
   SweepLds* sl = reinterpret_cast<SweepLds*>(lds + S3Lds<NB>::SW_OFF);
   const int64_t bid = blockIdx.x;
@@ -2513,7 +2574,8 @@ __global__ __launch_bounds__(S3_NT, NRB <= 4 ? 2 : 1) void s3_reduce_solve_kerne
     Xb = x_rel ? X - lo * c1 : X;
     tbase = lt_seg_rows ? lo : 0;
   };
-  // Roles: B solve workgroups, then B * strips strip workgroups.  Workgroups
+  // Roles: nsr solve workgroups (B, or 0 when the solve runs in a launch of
+  // its own), then B * strips strip workgroups.  Workgroups
   // go to the 8 XCDs in turn (block id mod 8); when B is a multiple of 8,
   // segment b's solve role and all its strips run on XCD b mod 8, so the
   // strips of a segment share one L2 copy of its L^T rows instead of every
@@ -2527,18 +2589,18 @@ __global__ __launch_bounds__(S3_NT, NRB <= 4 ? 2 : 1) void s3_reduce_solve_kerne
   int part = 0;       // token part of the strip (msplit > 1)
   int rh = 0;         // row block of 16 SNRB rows (r > 64)
   if (msplit > 1 || RH > 1) {
-    if (bid < B) {
+    if (bid < nsr) {
       b = bid;
       strip = -1;
     } else {
-      const int64_t u = bid - B;
+      const int64_t u = bid - nsr;
       b = u / (strips * msplit * RH);
       strip = (u / (msplit * RH)) % strips;
       part = (int)((u / RH) % msplit);
       rh = (int)(u % RH);
     }
   } else if ((B & 7) == 0) {
-    const int64_t x = bid & 7, j = bid >> 3, per = B >> 3;
+    const int64_t x = bid & 7, j = bid >> 3, per = nsr >> 3;
     if (j < per) {
       b = x + 8 * j;
       strip = -1;
@@ -2547,12 +2609,12 @@ __global__ __launch_bounds__(S3_NT, NRB <= 4 ? 2 : 1) void s3_reduce_solve_kerne
       b = x + 8 * (u / strips);
       strip = u % strips;
     }
-  } else if (bid < B) {
+  } else if (bid < nsr) {
     b = bid;
     strip = -1;
   } else {
-    b = (bid - B) / strips;
-    strip = (bid - B) % strips;
+    b = (bid - nsr) / strips;
+    strip = (bid - nsr) % strips;
   }
   if (strip < 0) {
     const int64_t lo = sg.lo(b), hi = sg.hi(b);
@@ -2561,51 +2623,7 @@ __global__ __launch_bounds__(S3_NT, NRB <= 4 ? 2 : 1) void s3_reduce_solve_kerne
     seg_ptrs(b, lo, Ltb, Xb, tbase);
     float* Gs = reinterpret_cast<float*>(lds + S3Lds<NB>::G_OFF);
     if (gpart) {
-      // G_b = sum of the segment's partials, in order (float4 columns; up to
-      // 8 partials' loads in flight per thread): gchunks token chunks of the
-      // segment, or (gprows > 0) the first stage's per-tile partials of the
-      // tiles of gprows tokens that the segment meets, in slot 1 of its first
-      // tile when that tile starts in the previous segment, else in slot 0
-      const int nq = r * r / 4;   // r % 8 == 0
-      const int64_t rb_lo = gprows > 0 ? lo / gprows : 0;
-      const int nparts = gprows > 0 ? (int)((hi - 1) / gprows - rb_lo + 1) : gchunks;
-      auto part_ptr = [&](int p) -> const float4* {
-        int64_t idx;
-        if (gprows > 0) {
-          const int64_t rb = rb_lo + p;
-          idx = rb * 2 + ((p == 0 && lo > rb * gprows) ? 1 : 0);
-        } else {
-          idx = b * gchunks + p;
-        }
-        return reinterpret_cast<const float4*>(gpart + idx * r * r);
-      };
-      for (int e0 = threadIdx.x; e0 < nq; e0 += 4 * S3_NT) {
-        float4 acc[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int c0 = 0; c0 < nparts; c0 += 8) {
-          float4 v[8][4];
-#pragma unroll
-          for (int c = 0; c < 8; ++c)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int e = e0 + i * S3_NT;
-              v[c][i] = (c0 + c < nparts && e < nq) ? part_ptr(c0 + c)[e] : make_float4(0.f, 0.f, 0.f, 0.f);
-            }
-#pragma unroll
-          for (int c = 0; c < 8; ++c)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              acc[i].x += v[c][i].x;
-              acc[i].y += v[c][i].y;
-              acc[i].z += v[c][i].z;
-              acc[i].w += v[c][i].w;
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (e0 + i * S3_NT < nq) reinterpret_cast<float4*>(Gs)[e0 + i * S3_NT] = acc[i];
-      }
+      gram_sum<S3_NT>(gpart, gchunks, gprows, b, lo, hi, r, Gs);
       __syncthreads();
     } else {
       s3_gram<NB>(Ltb, ldt, r, lo, hi, Gs, lds, tbase);
@@ -3158,6 +3176,9 @@ inline int64_t lt_pitch(int64_t n) { return cdiv(n, 256) * 256; }
 struct StageEvents {
   void* const* ev;
   int n;
+  // the solve may run on the library's side stream (off for the
+  // allocation-free entry point, which creates nothing)
+  bool fork = true;
   void mark(int i, hipStream_t st) const {
     if (ev && i < n && ev[i]) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(ev[i]), st);
   }
@@ -3170,17 +3191,19 @@ void launch_s3_bf16(const bf16_t* Lt, int64_t ldt, const bf16_t* X, int64_t c1, 
                     int solve_mode,
                     hipStream_t st, int64_t lt_seg_rows = 0, bool x_rel = false, float* gpart = nullptr,
                     int gchunks = 0, int64_t gchunk = 0, int64_t gprows = 0, int msplit = 1,
-                    float* Mpart = nullptr) {
+                    float* Mpart = nullptr, bool solve_roles = true, bool partials_done = false) {
   const int strips = (int)cdiv(c1, S3_STRIP);
-  if (gpart && gprows == 0)   // chunk Gram partials first (absolute L^T addressing only)
+  // without solve roles the launch has the M strips only (and writes no G)
+  const int64_t nsr = solve_roles ? B : 0;
+  if (gpart && gprows == 0 && !partials_done)   // chunk Gram partials first (absolute L^T addressing only)
     hipLaunchKernelGGL((gram_partial_kernel<NB>), dim3((unsigned)(B * gchunks)), dim3(64 * NB), 0, st, Lt, ldt, r,
                        sg, n, gchunks, gchunk, gpart);
   auto go = [&](auto kern) {
     constexpr int RH = NRB > 4 ? NRB / 4 : 1;   // row blocks per strip (the kernel's SNRB split)
-    hipLaunchKernelGGL(kern, dim3((unsigned)(B + B * strips * msplit * RH)), dim3(S3_NT), 0, st, Lt, ldt, X, c1, r,
-                       sg, n,
+    hipLaunchKernelGGL(kern, dim3((unsigned)(nsr + B * strips * msplit * RH)), dim3(S3_NT), 0, st, Lt, ldt, X, c1,
+                       r, sg, n,
                        B, M, G, Gi, Gi32, stat, prec, eps, strips, lt_seg_rows, x_rel ? 1 : 0, gpart, gchunks,
-                       gprows, msplit, Mpart);
+                       gprows, msplit, Mpart, nsr);
   };
   if (solve_mode == 2) go(s3_reduce_solve_kernel<NRB, NB, 2>);
   else if (solve_mode == 1) go(s3_reduce_solve_kernel<NRB, NB, 1>);
@@ -3190,6 +3213,46 @@ void launch_s3_bf16(const bf16_t* Lt, int64_t ldt, const bf16_t* X, int64_t c1, 
     hipLaunchKernelGGL(m_split_reduce_kernel, dim3((unsigned)cdiv(count4, 256)), dim3(256), 0, st, Mpart, M, count4,
                        msplit);
   }
+}
+
+// The library's side stream per device, with a fork and a join event, so a
+// solve that needs only the Gram partials runs beside the M strips: the
+// caller's stream records `fork`, the side stream waits for it and runs the
+// solve, records `join`, and the caller's stream waits for `join` before the
+// apply.  Created on a device's first such forward (never while the caller's
+// stream is being captured: that forward then runs the solve after the
+// strips); default priority; kept until the process ends.  The lock spans
+// each forward's record / wait sequence, so concurrent forwards on one
+// device (from several host threads) each wait on their own records.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kSideDevices = 64;
+std::mutex g_side_mu;
+SideStream g_side[kSideDevices];
+
+// Under g_side_mu: the current device's side stream, created if absent and
+// the caller's stream is not capturing; false if unavailable.
+bool side_stream_locked(hipStream_t caller, SideStream& out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kSideDevices) return false;
+  SideStream& ss = g_side[dev];
+  if (!ss.s) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(caller, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return false;
+    SideStream n;
+    if (hipStreamCreateWithFlags(&n.s, hipStreamNonBlocking) != hipSuccess) return false;
+    if (hipEventCreateWithFlags(&n.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&n.join, hipEventDisableTiming) != hipSuccess) {
+      if (n.fork) (void)hipEventDestroy(n.fork);
+      (void)hipStreamDestroy(n.s);
+      return false;
+    }
+    ss = n;
+  }
+  out = ss;
+  return true;
 }
 
 // S3, S4 and S5, shared by every structure: M_b, G_b, Ginv_b, M'_b and
@@ -3241,11 +3304,49 @@ void forward_residual(const dyra_spec& s, const char* plan, const void* X, const
     const int64_t gk = WL.gchunk;
     const int ms = WL.msplit;
     float* Mpt = reinterpret_cast<float*>(ws + WL.Mpart);
-    if (r <= 16) launch_s3_bf16<1, 1>(Lt, ldt, Xb, c1, r, sg, n, B, M, G, Gi, Gi32, stat, prec, eps, mode, st, 0, false, Gp, gc, gk, gram_rows, ms, Mpt);
-    else if (r <= 32) launch_s3_bf16<2, 1>(Lt, ldt, Xb, c1, r, sg, n, B, M, G, Gi, Gi32, stat, prec, eps, mode, st, 0, false, Gp, gc, gk, gram_rows, ms, Mpt);
-    else if (r <= 64) launch_s3_bf16<4, 2>(Lt, ldt, Xb, c1, r, sg, n, B, M, G, Gi, Gi32, stat, prec, eps, mode, st, 0, false, Gp, gc, gk, gram_rows, ms, Mpt);
-    else launch_s3_bf16<8, 4>(Lt, ldt, Xb, c1, r, sg, n, B, M, G, Gi, Gi32, stat, prec, eps, mode, st, 0, false, Gp, gc, gk, gram_rows, ms, Mpt);
-    solved = mode != 0;
+    auto s3 = [&](bool roles, bool parts_done) {
+      if (r <= 16) launch_s3_bf16<1, 1>(Lt, ldt, Xb, c1, r, sg, n, B, M, G, Gi, Gi32, stat, prec, eps, mode, st, 0, false, Gp, gc, gk, gram_rows, ms, Mpt, roles, parts_done);
+      else if (r <= 32) launch_s3_bf16<2, 1>(Lt, ldt, Xb, c1, r, sg, n, B, M, G, Gi, Gi32, stat, prec, eps, mode, st, 0, false, Gp, gc, gk, gram_rows, ms, Mpt, roles, parts_done);
+      else if (r <= 64) launch_s3_bf16<4, 2>(Lt, ldt, Xb, c1, r, sg, n, B, M, G, Gi, Gi32, stat, prec, eps, mode, st, 0, false, Gp, gc, gk, gram_rows, ms, Mpt, roles, parts_done);
+      else launch_s3_bf16<8, 4>(Lt, ldt, Xb, c1, r, sg, n, B, M, G, Gi, Gi32, stat, prec, eps, mode, st, 0, false, Gp, gc, gk, gram_rows, ms, Mpt, roles, parts_done);
+    };
+    // Newton-Schulz needs only the Gram partials: on the side stream it runs
+    // beside the M strips (a launch with no solve roles) instead of after
+    // them; its workgroup sums G_b from the partials itself
+    std::unique_lock<std::mutex> side_lock;
+    SideStream side;
+    bool fork = false;
+    if (ns && E.fork && (gram_rows > 0 || gc > 0)) {
+      side_lock = std::unique_lock<std::mutex>(g_side_mu);
+      fork = side_stream_locked(st, side);
+      if (!fork) side_lock.unlock();
+    }
+    if (fork) {
+      if (gram_rows == 0) {   // chunk Gram partials first, on the caller's stream
+        if (r <= 32)
+          hipLaunchKernelGGL((gram_partial_kernel<1>), dim3((unsigned)(B * gc)), dim3(64), 0, st, Lt, ldt, r, sg, n,
+                             gc, gk, Gp);
+        else if (r <= 64)
+          hipLaunchKernelGGL((gram_partial_kernel<2>), dim3((unsigned)(B * gc)), dim3(128), 0, st, Lt, ldt, r, sg, n,
+                             gc, gk, Gp);
+        else
+          hipLaunchKernelGGL((gram_partial_kernel<4>), dim3((unsigned)(B * gc)), dim3(256), 0, st, Lt, ldt, r, sg, n,
+                             gc, gk, Gp);
+      }
+      const float tol = kNsTolBf16, accept = kNsAcceptBf16;
+      (void)hipEventRecord(side.fork, st);
+      (void)hipStreamWaitEvent(side.s, side.fork, 0);
+      hipLaunchKernelGGL(ns_inverse_kernel, dim3((unsigned)B), dim3(512), 0, side.s, G, Gi, Gi32, stat, prec, r, eps,
+                         kNsMaxit, tol, accept, Gp, gc, gram_rows, sg);
+      (void)hipEventRecord(side.join, side.s);
+      s3(false, true);
+      (void)hipStreamWaitEvent(st, side.join, 0);
+      side_lock.unlock();
+      solved = true;
+    } else {
+      s3(true, false);
+      solved = mode != 0;
+    }
   } else {
     const int tr = (int)cdiv(r, C3::BM), tcm = (int)cdiv(c1, C3::BN), tcg = (int)cdiv(r, C3::BN);
     const int64_t grid = B * tr * (tcm + tcg);
@@ -3263,7 +3364,7 @@ void forward_residual(const dyra_spec& s, const char* plan, const void* X, const
       // ill-conditioned G still gives an fp32-accurate inverse)
       const float tol = BF ? kNsTolBf16 : 2e-6f, accept = BF ? kNsAcceptBf16 : 1e-5f;
       hipLaunchKernelGGL(ns_inverse_kernel, dim3((unsigned)B), dim3(512), 0, st, G, Gi, Gi32, stat, prec, r, eps,
-                         kNsMaxit, tol, accept);
+                         kNsMaxit, tol, accept, nullptr, 0, (int64_t)0, sg);
     } else if (solver == DYRA_SOLVER_CHOL) {
       launch_chol(G, Gi, Gi32, stat, prec, r, eps, B, st);
     } else {
@@ -3748,7 +3849,7 @@ extern "C" int dyra_forward_noalloc(const dyra_spec* spec, const void* plan, con
   rc = scratch_address(&ws);
   if (rc) return rc;
   rc = forward_impl(spec, plan, X, bias, Y, B, s, dtype, ridge_eps, solver, ws, (size_t)DYRA_NOALLOC_MAX_WORKSPACE,
-                    stream, StageEvents{nullptr, 0});
+                    stream, StageEvents{nullptr, 0, false});
   if (rc || !status_out) return rc;
   const WsLayout WL = ws_layout(*spec, B, s, dtype);
   if (hipMemcpyAsync(status_out, reinterpret_cast<const char*>(ws) + WL.status, (size_t)B * 4,
