@@ -28,16 +28,21 @@
  *   - Arguments are validated on the host before any HIP call; an invalid
  *     call touches no device state.
  *   - The caller owns every buffer (host and device).  The library allocates
- *     no device memory.  Its only process-wide state is read-only after first
- *     use: the compute-unit count of each device (queried once, to size the
- *     persistent kernels' grids) and, for dyra_forward_noalloc only, that
- *     entry point's static device workspace.  Calls on distinct streams with
- *     distinct workspaces are independent.
+ *     no device memory.  Its only process-wide state, created on first use and
+ *     kept until the process ends: the compute-unit count of each device
+ *     (queried once, to size the persistent kernels' grids); per device, one
+ *     side stream with two events, on which a bf16 Newton-Schulz solve runs
+ *     beside the token reduction (the caller's stream waits for it before
+ *     the forward goes on; not created while the caller's stream is being
+ *     captured, nor by dyra_forward_noalloc); and, for dyra_forward_noalloc
+ *     only, that entry point's static device workspace.  Calls on distinct
+ *     streams with distinct workspaces are independent.
  *   - Matrices are row-major and contiguous.  Device pointers must be 16-byte
  *     aligned.  "stream" is a hipStream_t passed as void* (NULL = default).
  *   - dtype: DYRA_F32 (fp32 storage, fp32 arithmetic) or DYRA_BF16 (bf16
- *     storage, fp32 accumulation); the r x r solves run in fp64 (sweep,
- *     Cholesky) or at fp32 accuracy (Newton-Schulz) for both.
+ *     storage, fp32 accumulation); the r x r solves run in fp64 (Cholesky),
+ *     fp32 with an fp64 pass where a pivot needs it (sweep), or at fp32
+ *     accuracy (Newton-Schulz) for both.
  *   - Size constraints: c1, c2, k, r multiples of 8; 1 <= r <= min(c1, c2);
  *     r <= 128.  Low-rank: k + r <= min(c1, c2).  Monarch: c1 == c2 ==
  *     mblk^2 with mblk == 32 (bf16 only).  BLAST: nb divides c1 and c2,
