@@ -255,8 +255,9 @@ int dyra_forward(const dyra_spec* spec, const void* plan, const void* X, const v
  * t = 1.5 (then L again, L_b = X_b (W_res R_b^T)(R_b R_b^T + lambda I)^-1,
  * lambda = ridge_eps * trace(R_b R_b^T) / r, solved by the sweep); 4 is
  * t = 2 (then R again from the new L).  Y uses the last L and R.  Every
- * structure (the left step does not involve the static branch), bf16 only,
- * uniform segments: EINVAL for half_steps outside 2..4, EDTYPE for fp32.
+ * structure (the left step does not involve the static branch) in every
+ * storage type it takes, uniform segments: EINVAL for half_steps outside
+ * 2..4.
  * The workspace must hold
  * dyra_workspace_size_als bytes for the same half_steps; otherwise the
  * arguments, ownership and errors are those of dyra_forward.

@@ -891,6 +891,27 @@ __global__ __launch_bounds__(256) void transpose_b16_kernel(const bf16_t* __rest
   }
 }
 
+// out (cols x rows, row pitch ldo) = in (rows x cols, row pitch ldi)^T for
+// 32-bit elements, 64 x 64 tiles through LDS (the padded pitch keeps the
+// column reads off one bank).
+__global__ __launch_bounds__(256) void transpose_b32_kernel(const float* __restrict__ in, int64_t ldi,
+                                                            float* __restrict__ out, int64_t ldo, int64_t rows,
+                                                            int64_t cols) {
+  __shared__ float tile[64][65];
+  const int64_t tiles_c = (cols + 63) / 64;
+  const int64_t r0 = (int64_t)(blockIdx.x / tiles_c) * 64, c0 = (int64_t)(blockIdx.x % tiles_c) * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int y = ty; y < 64; y += 4) {
+    const int64_t rr = r0 + y, cc = c0 + tx;
+    tile[y][tx] = (rr < rows && cc < cols) ? in[rr * ldi + cc] : 0.f;
+  }
+  __syncthreads();
+  for (int y = ty; y < 64; y += 4) {
+    const int64_t oc = c0 + y, orr = r0 + tx;   // out row oc, column orr
+    if (oc < cols && orr < rows) out[oc * ldo + orr] = tile[tx][y];
+  }
+}
+
 // L_b = X_b Z_b for every segment: out [n x r] at TL columns k .. k + r - 1
 // (pitch ldo) and L^T.  Zt: [B r x c1] (Z_b^T, row-major).  A tile whose rows
 // span several segments accumulates one k-loop per segment with the rows of
@@ -3441,6 +3462,49 @@ void left_step_bf16(const dyra_spec& s, const char* plan, const bf16_t* X, int64
                      seg, B, lt_pitch(n), tiles_n, ldo);
 }
 
+// One left ALS half-step on the fp32 workspace (low-rank; fp32 storage
+// exists for no other structure): R = (R^T)^T; K_b = R_b R_b^T and
+// Q_b^T = R_b W_res^T by the fp32 token reduction with c2 as its token axis
+// (one launch per segment: that kernel addresses tokens absolutely); the
+// sweep's (K_b + lambda_b I)^-1; Z_b^T = (K_b + lambda_b I)^-1 Q_b^T; then
+// L_b = X_b Z_b by the batched engine GEMM into the L columns of [T | L],
+// and L^T again for the next right step.
+void left_step_f32(const dyra_spec& s, const char* plan, const float* X, int64_t B, int64_t seg, float eps,
+                   char* ws, hipStream_t st, int half_steps) {
+  const PlanLayout PL = plan_layout(s, DYRA_F32);
+  const WsLayout WL = ws_layout(s, B, seg, DYRA_F32, half_steps);
+  const int64_t n = B * seg, c1 = s.c1, c2 = s.c2;
+  const int r = s.r, k = s.k;
+  const float* Rt = reinterpret_cast<const float*>(ws + WL.Rt);
+  float* R = reinterpret_cast<float*>(ws + WL.R);
+  float* K = reinterpret_cast<float*>(ws + WL.K);
+  double* Kinv = reinterpret_cast<double*>(ws + WL.Kinv);
+  float* Ki32 = reinterpret_cast<float*>(ws + WL.Ki32);
+  float* Qt = reinterpret_cast<float*>(ws + WL.Qt);
+  float* Zt = reinterpret_cast<float*>(ws + WL.Zt);
+  int32_t* kst = reinterpret_cast<int32_t*>(ws + WL.kstatus);
+  int32_t* kpr = reinterpret_cast<int32_t*>(ws + WL.kprec);
+  const float* Wrt = reinterpret_cast<const float*>(plan + PL.Wrt);
+  float* TL = reinterpret_cast<float*>(ws + WL.A);
+  float* Lt = reinterpret_cast<float*>(ws + WL.Lt);
+  // R [B r x c2] = (R^T [c2 x B r])^T
+  hipLaunchKernelGGL(transpose_b32_kernel, dim3((unsigned)(cdiv(c2, 64) * cdiv(B * r, 64))), dim3(256), 0, st, Rt,
+                     B * r, R, c2, c2, B * r);
+  const int tr = (int)cdiv(r, CfgF3::BM), tcm = (int)cdiv(c1, CfgF3::BN), tcg = (int)cdiv(r, CfgF3::BN);
+  for (int64_t b = 0; b < B; ++b)
+    hipLaunchKernelGGL(s3_gram_kernel<CfgF3>, dim3((unsigned)(tr * (tcm + tcg))), dim3(CfgF3::NT), 0, st,
+                       R + b * r * c2, c2, Wrt, c1, r, SegMap{nullptr, c2, 1, c2}, c2, Qt + b * r * c1, K + b * r * r,
+                       tr, tcm, tcg);
+  launch_sweep(K, Kinv, Ki32, kst, kpr, r, eps, B, st);
+  launch_apply_inverse<float>(Kinv, Ki32, Qt, Zt, B, r, c1, kst, kpr, st);
+  // L_b [seg x r] = X_b [seg x c1] . (Z_b^T [r x c1])^T at column k of [T | L]
+  launch_gemm_tn<CfgF>(X, c1, Zt, c1, TL + k, k + r, seg, r, c1, nullptr, st, (int)B, seg * c1, (int64_t)r * c1,
+                       seg * (k + r));
+  // L^T [r x ldt] = (L [n x r], pitch k + r)^T
+  hipLaunchKernelGGL(transpose_b32_kernel, dim3((unsigned)(cdiv(n, 64) * cdiv(r, 64))), dim3(256), 0, st, TL + k,
+                     (int64_t)(k + r), Lt, lt_pitch(n), n, (int64_t)r);
+}
+
 template <class C, class C3, class C6>
 int forward_lowrank(const dyra_spec& s, const char* plan, const void* X, const void* bias, void* Y,
                     const SegInfo& si, float eps, int solver, char* ws, hipStream_t st,
@@ -3487,12 +3551,15 @@ int forward_lowrank(const dyra_spec& s, const char* plan, const void* X, const v
   E.mark(1, st);
   forward_residual<C, C3>(s, plan, X, si, eps, solver, ws, st, E, gram_rows);
   // further ALS half-steps: left (L from R), right (R from L), ...
-  if constexpr (TT<T>::ESZ == 2) {
-    for (int h = 2; h < half_steps; ++h) {
-      if (h % 2 == 0)
+  for (int h = 2; h < half_steps; ++h) {
+    if (h % 2 == 0) {
+      if constexpr (TT<T>::ESZ == 2)
         left_step_bf16(s, plan, reinterpret_cast<const bf16_t*>(X), B, seg, eps, ws, st, half_steps, k,
                        (int64_t)(k + r));
-      else forward_residual<C, C3>(s, plan, X, si, eps, solver, ws, st, StageEvents{nullptr, 0});
+      else
+        left_step_f32(s, plan, reinterpret_cast<const float*>(X), B, seg, eps, ws, st, half_steps);
+    } else {
+      forward_residual<C, C3>(s, plan, X, si, eps, solver, ws, st, StageEvents{nullptr, 0});
     }
   }
   E.mark(4, st);
@@ -3635,12 +3702,12 @@ int forward_blast(const dyra_spec& s, const char* plan, const void* X, const voi
   return hipGetLastError() == hipSuccess ? DYRA_OK : DYRA_EHIP;
 }
 
-// half_steps: 2 t of the ALS (2: t = 1; 3: t = 1.5; 4: t = 2); beyond 2 in
-// bf16 only (every structure).
+// half_steps: 2 t of the ALS (2: t = 1; 3: t = 1.5; 4: t = 2), for every
+// structure and storage type the forward takes.
 int check_als(const dyra_spec& spec, int32_t dtype, int32_t half_steps) {
   (void)spec;
+  (void)dtype;
   if (half_steps < 2 || half_steps > 4) return DYRA_EINVAL;
-  if (half_steps > 2 && dtype != DYRA_BF16) return DYRA_EDTYPE;
   return DYRA_OK;
 }
 
@@ -3706,7 +3773,8 @@ int dispatch(const dyra_spec* spec, const void* plan, const void* X, const void*
   if (dtype == DYRA_BF16)
     return forward_lowrank<CfgB, CfgB3, CfgB6>(*spec, plan_c, X, bias, Y, si, ridge_eps, solver, ws, st, E,
                                                half_steps);
-  return forward_lowrank<CfgF, CfgF3, CfgF>(*spec, plan_c, X, bias, Y, si, ridge_eps, solver, ws, st, E);
+  return forward_lowrank<CfgF, CfgF3, CfgF>(*spec, plan_c, X, bias, Y, si, ridge_eps, solver, ws, st, E,
+                                            half_steps);
 }
 
 int forward_impl(const dyra_spec* spec, const void* plan, const void* X, const void* bias, void* Y, int64_t B,

@@ -132,15 +132,19 @@ def test_prepare_rejects_missing_outputs():
 
 def test_als_entry_points_validate_on_host():
     """dyra_workspace_size_als / dyra_forward_als reject what they do not
-    support before any HIP call: half_steps outside 2..4, fp32 (every
-    structure runs more iterations in bf16)."""
+    support before any HIP call: half_steps outside 2..4 or a workspace
+    smaller than the ALS layout (bf16 and, for the low-rank structure, fp32)."""
     L = D.lib()
     lowrank = D.make_spec(synth.KIND_LOWRANK, 256, 512, 16, k=32)
     monarch = D.make_spec(synth.KIND_MONARCH, 1024, 1024, 16, mblk=32)
     n = ctypes.c_size_t()
     for h, rc in ((2, 0), (3, 0), (4, 0), (1, -1), (5, -1)):
         assert L.dyra_workspace_size_als(ctypes.byref(lowrank), 2, 64, synth.DT_BF16, h, ctypes.byref(n)) == rc
-    assert L.dyra_workspace_size_als(ctypes.byref(lowrank), 2, 64, synth.DT_F32, 3, ctypes.byref(n)) == -6
+    assert L.dyra_workspace_size_als(ctypes.byref(lowrank), 2, 64, synth.DT_F32, 3, ctypes.byref(n)) == 0
+    n32 = n.value
+    base32 = ctypes.c_size_t()
+    L.dyra_workspace_size(ctypes.byref(lowrank), 2, 64, synth.DT_F32, ctypes.byref(base32))
+    assert n32 > base32.value
     assert L.dyra_workspace_size_als(ctypes.byref(monarch), 2, 64, synth.DT_BF16, 3, ctypes.byref(n)) == 0
     base_m = ctypes.c_size_t()
     L.dyra_workspace_size(ctypes.byref(monarch), 2, 64, synth.DT_BF16, ctypes.byref(base_m))
@@ -158,7 +162,7 @@ def test_als_entry_points_validate_on_host():
     assert L.dyra_forward_als(ctypes.byref(lowrank), 16, 16, None, 16, 2, 64, synth.DT_BF16, 1e-6, 0, 7, 16,
                               1 << 30, None) == -1
     assert L.dyra_forward_als(ctypes.byref(lowrank), 16, 16, None, 16, 2, 64, synth.DT_F32, 1e-6, 0, 3, 16,
-                              1 << 30, None) == -6
+                              base32.value, None) == -3
     assert L.dyra_forward_als(ctypes.byref(lowrank), 16, 16, None, 16, 2, 64, synth.DT_BF16, 1e-6, 0, 3, 16,
                               sizes[0], None) == -3
 

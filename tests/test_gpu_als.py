@@ -32,8 +32,17 @@ CASES = [
 ]
 
 
+# fp32 storage (low-rank, the one structure with fp32): the left step on
+# the fp32 token reduction, the sweep and the engine GEMM; the fp32 bar
+CASES_F32 = [
+    W["tiny_fp32"],
+    sc(W["vitb_fc1"], name="als_ragged_fp32", B=3, s=77, c1=192, c2=200, k=24, r=16, dtype=synth.DT_F32),
+    sc(W["vitl_fc1"], name="als_r64_fp32", B=4, s=257, c1=256, c2=512, k=64, r=64, dtype=synth.DT_F32),
+]
+
+
 @pytest.mark.parametrize("half_steps", [3, 4])
-@pytest.mark.parametrize("w", CASES, ids=lambda w: w.name)
+@pytest.mark.parametrize("w", CASES + CASES_F32, ids=lambda w: w.name)
 def test_als_parity(w, half_steps):
     err, status, _, _ = run_same_factor_case(w, half_steps=half_steps)
     assert np.all(status == D.SOLVE_OK)
