@@ -164,8 +164,8 @@ def main():
                     help="also run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
-              "the DyRA forward shards by segments with no communication, see the design notes.",
+        print(f"bench.py: the benchmark runs on one GPU only (--gpus {args.gpus} requested); "
+              "the DyRA forward would shard by segments, with no communication between GPUs.",
               file=sys.stderr)
         sys.exit(2)
 
