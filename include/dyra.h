@@ -12,7 +12,7 @@
  *   R = (L^T L + lambda I)^-1 (L^T X) W_res
  *   Y = X W_hat + L R + bias    (the n x c2 product X W_res is never formed)
  *
- * Sources (page title + section; see the design notes for the full list):
+ * Sources (page title + section):
  *   nanless.github.io DyRA digest post: the split equations W = W_hat + W_res
  *   and XW = X W_hat + X W_res; the residual-product objective
  *   min ||X W_res - L R||_F^2 and the cheap ALS ordering; the one-iteration

@@ -20,8 +20,7 @@ DNNs"):
         differ", "offline preparation and online computation without
         training", "first reproduction step" (small ridge).
 
-Readings taken where the pages leave a step open (each is listed in the
-design notes as well):
+Readings taken where the pages leave a step open:
   * one input = one segment of s consecutive rows; B segments are solved
     independently.
   * R0 = top-r right singular vectors of W_res (orthonormal rows), so the

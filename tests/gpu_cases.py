@@ -31,7 +31,12 @@ TOL = {synth.DT_F32: 1e-4, synth.DT_BF16: 2e-2}
 # u cond(L_b) of the correction: such a segment is held to
 # ||dY_b|| <= ALPHA u ||Y_b|| + BETA (1 + u cond(L_b)) ||(L R)_b|| instead of
 # TOL, and a_b gains cond(L_b).  Dropping its correction still fails.
-# The derivation of ALPHA, BETA and C_ELEM is in the design notes (tolerances).
+# ALPHA covers the output and first-stage (T) roundings, which measure about
+# 0.45 u ||Y_b|| on the full-size cases (a 3x margin); BETA the correction's
+# own roundings (L, M', R, each at most u relative) and the solve's, so a
+# segment without its correction misses by ||(L R)_b||, ten times the
+# allowance; C_ELEM bounds each element by four units of the magnitudes the
+# device rounds.
 UNIT = {synth.DT_F32: 2.0 ** -16, synth.DT_BF16: 2.0 ** -8}
 ALPHA, BETA, C_ELEM = 1.5, 0.1, 4.0
 
