@@ -256,8 +256,8 @@ int dyra_forward(const dyra_spec* spec, const void* plan, const void* X, const v
  * lambda = ridge_eps * trace(R_b R_b^T) / r, solved by the sweep); 4 is
  * t = 2 (then R again from the new L).  Y uses the last L and R.  Every
  * structure (the left step does not involve the static branch) in every
- * storage type it takes, uniform segments: EINVAL for half_steps outside
- * 2..4.
+ * storage type it takes, uniform segments (ragged ones:
+ * dyra_forward_varlen_als): EINVAL for half_steps outside 2..4.
  * The workspace must hold
  * dyra_workspace_size_als bytes for the same half_steps; otherwise the
  * arguments, ownership and errors are those of dyra_forward.
@@ -338,6 +338,23 @@ int dyra_forward_varlen(const dyra_spec* spec, const void* plan, const void* X, 
                         void* Y, int64_t B, const int64_t* offsets, const int32_t* offsets_dev,
                         int32_t dtype, float ridge_eps, int32_t solver, int32_t* status_out,
                         void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Ragged segments with more ALS iterations: dyra_forward_varlen with
+ * half_steps = 2 t as for dyra_forward_als (2: t = 1, exactly
+ * dyra_forward_varlen; 3: t = 1.5; 4: t = 2), each segment's left and right
+ * steps on its own rows.  The workspace must hold
+ * dyra_workspace_size_varlen_als bytes for the same offsets and half_steps.
+ * Errors as for dyra_forward_varlen, and EINVAL for half_steps outside 2..4.
+ * Source: nanless.github.io DyRA digest, "what the low-rank objective of the
+ * residual product is" (the alternating solves); paperlayer.ai 2.2, E.3.
+ */
+int dyra_workspace_size_varlen_als(const dyra_spec* spec, int64_t B, const int64_t* offsets,
+                                   int32_t dtype, int32_t half_steps, size_t* bytes);
+int dyra_forward_varlen_als(const dyra_spec* spec, const void* plan, const void* X, const void* bias,
+                            void* Y, int64_t B, const int64_t* offsets, const int32_t* offsets_dev,
+                            int32_t dtype, float ridge_eps, int32_t solver, int32_t half_steps,
+                            int32_t* status_out, void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * Copies the B per-segment solver status words of the last dyra_forward on

@@ -914,24 +914,24 @@ __global__ __launch_bounds__(256) void transpose_b32_kernel(const float* __restr
 
 // L_b = X_b Z_b for every segment: out [n x r] at TL columns k .. k + r - 1
 // (pitch ldo) and L^T.  Zt: [B r x c1] (Z_b^T, row-major).  A tile whose rows
-// span several segments accumulates one k-loop per segment with the rows of
-// the others masked off.
+// span several segments (uniform or ragged, sg) accumulates one k-loop per
+// segment with the rows of the others masked off.
 template <class C>
 __global__ __launch_bounds__(C::NT) void s1_left_kernel(const bf16_t* X, const bf16_t* Zt, bf16_t* TL, bf16_t* Lt,
-                                                        int64_t n, int64_t c1, int k, int r, int64_t seg, int64_t B,
+                                                        int64_t n, int64_t c1, int k, int r, SegMap sg,
                                                         int64_t ldt, int tiles_n, int64_t ldo) {
   constexpr int E = 2, KPC = 8;
   __shared__ __attribute__((aligned(16))) char lds[C::LDS];
   const int t = xcd_tile_id(blockIdx.x, gridDim.x);
   const int64_t m0 = (int64_t)(t / tiles_n) * C::BM, n0 = (int64_t)(t % tiles_n) * C::BN;
-  const int64_t bfirst = m0 / seg;
-  const int64_t blast = imin64(B - 1, (imin64(m0 + C::BM, n) - 1) / seg);
+  const int64_t bfirst = sg.of(m0);
+  const int64_t blast = sg.of(imin64(m0 + C::BM, n) - 1);
   const int nkc = ktiles(c1 * E);
   const int total = (int)(blast - bfirst + 1) * nkc;
   auto src = [=](int tt, Phase& ph, int& kt) {
     const int64_t b = bfirst + tt / nkc;
     kt = tt % nkc;
-    ph.a = OpK{reinterpret_cast<const char*>(X), c1 * E, m0, b * seg, imin64((b + 1) * seg, n), c1 * E};
+    ph.a = OpK{reinterpret_cast<const char*>(X), c1 * E, m0, sg.lo(b), sg.hi(b), c1 * E};
     ph.b = OpK{reinterpret_cast<const char*>(Zt + b * r * c1), c1 * E, n0, 0, r, c1 * E};
   };
   f32x16 acc[C::FM][C::FN];
@@ -3105,6 +3105,7 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 struct SegInfo {
   int64_t B = 0, n = 0, seg = 0, max_len = 0, min_len = 0;
   const int32_t* off_dev = nullptr;
+  const int64_t* off_host = nullptr;   // the caller's host offsets (ragged), valid during the call
   SegMap map() const { return SegMap{off_dev, seg, B, n}; }
   WsLayout layout(const dyra_spec& s, int dtype, int half_steps = 2) const {
     return ws_layout_n(s, B, n, max_len, dtype, half_steps);
@@ -3429,11 +3430,11 @@ typedef GemmCfg<bf16_t, 128, 64, 2, 2> CfgL;   // left ALS step: L_b = X_b Z_b (
 // not involve the static branch: only where L sits in the first-stage output
 // depends on the structure (column lcol of rows of pitch ldo: k / k + r
 // low-rank, c / c + r Monarch, nb rb / nb rb + r BLAST).
-void left_step_bf16(const dyra_spec& s, const char* plan, const bf16_t* X, int64_t B, int64_t seg, float eps,
+void left_step_bf16(const dyra_spec& s, const char* plan, const bf16_t* X, const SegInfo& si, float eps,
                     char* ws, hipStream_t st, int half_steps, int lcol, int64_t ldo) {
   const PlanLayout PL = plan_layout(s, DYRA_BF16);
-  const WsLayout WL = ws_layout(s, B, seg, DYRA_BF16, half_steps);
-  const int64_t n = B * seg, c1 = s.c1, c2 = s.c2;
+  const WsLayout WL = si.layout(s, DYRA_BF16, half_steps);
+  const int64_t B = si.B, n = si.n, c1 = s.c1, c2 = s.c2;
   const int r = s.r;
   const bf16_t* Rt = reinterpret_cast<const bf16_t*>(ws + WL.Rt);
   bf16_t* R = reinterpret_cast<bf16_t*>(ws + WL.R);
@@ -3459,7 +3460,7 @@ void left_step_bf16(const dyra_spec& s, const char* plan, const bf16_t* X, int64
   const int tiles_n = (int)cdiv(r, CfgL::BN);
   hipLaunchKernelGGL(s1_left_kernel<CfgL>, dim3((unsigned)(cdiv(n, CfgL::BM) * tiles_n)), dim3(CfgL::NT), 0, st, X,
                      Zt, reinterpret_cast<bf16_t*>(ws + WL.A), reinterpret_cast<bf16_t*>(ws + WL.Lt), n, c1, lcol, r,
-                     seg, B, lt_pitch(n), tiles_n, ldo);
+                     si.map(), lt_pitch(n), tiles_n, ldo);
 }
 
 // One left ALS half-step on the fp32 workspace (low-rank; fp32 storage
@@ -3469,11 +3470,11 @@ void left_step_bf16(const dyra_spec& s, const char* plan, const bf16_t* X, int64
 // sweep's (K_b + lambda_b I)^-1; Z_b^T = (K_b + lambda_b I)^-1 Q_b^T; then
 // L_b = X_b Z_b by the batched engine GEMM into the L columns of [T | L],
 // and L^T again for the next right step.
-void left_step_f32(const dyra_spec& s, const char* plan, const float* X, int64_t B, int64_t seg, float eps,
+void left_step_f32(const dyra_spec& s, const char* plan, const float* X, const SegInfo& si, float eps,
                    char* ws, hipStream_t st, int half_steps) {
   const PlanLayout PL = plan_layout(s, DYRA_F32);
-  const WsLayout WL = ws_layout(s, B, seg, DYRA_F32, half_steps);
-  const int64_t n = B * seg, c1 = s.c1, c2 = s.c2;
+  const WsLayout WL = si.layout(s, DYRA_F32, half_steps);
+  const int64_t B = si.B, n = si.n, seg = si.seg, c1 = s.c1, c2 = s.c2;
   const int r = s.r, k = s.k;
   const float* Rt = reinterpret_cast<const float*>(ws + WL.Rt);
   float* R = reinterpret_cast<float*>(ws + WL.R);
@@ -3497,9 +3498,18 @@ void left_step_f32(const dyra_spec& s, const char* plan, const float* X, int64_t
                        tr, tcm, tcg);
   launch_sweep(K, Kinv, Ki32, kst, kpr, r, eps, B, st);
   launch_apply_inverse<float>(Kinv, Ki32, Qt, Zt, B, r, c1, kst, kpr, st);
-  // L_b [seg x r] = X_b [seg x c1] . (Z_b^T [r x c1])^T at column k of [T | L]
-  launch_gemm_tn<CfgF>(X, c1, Zt, c1, TL + k, k + r, seg, r, c1, nullptr, st, (int)B, seg * c1, (int64_t)r * c1,
-                       seg * (k + r));
+  // L_b [s_b x r] = X_b [s_b x c1] . (Z_b^T [r x c1])^T at column k of [T | L]
+  // (one batched launch for uniform segments, one launch per ragged one)
+  if (!si.off_host) {
+    launch_gemm_tn<CfgF>(X, c1, Zt, c1, TL + k, k + r, seg, r, c1, nullptr, st, (int)B, seg * c1, (int64_t)r * c1,
+                         seg * (k + r));
+  } else {
+    for (int64_t b = 0; b < B; ++b) {
+      const int64_t lo = si.off_host[b], len = si.off_host[b + 1] - lo;
+      launch_gemm_tn<CfgF>(X + lo * c1, c1, Zt + b * r * c1, c1, TL + lo * (k + r) + k, k + r, len, r, c1, nullptr,
+                           st);
+    }
+  }
   // L^T [r x ldt] = (L [n x r], pitch k + r)^T
   hipLaunchKernelGGL(transpose_b32_kernel, dim3((unsigned)(cdiv(n, 64) * cdiv(r, 64))), dim3(256), 0, st, TL + k,
                      (int64_t)(k + r), Lt, lt_pitch(n), n, (int64_t)r);
@@ -3513,7 +3523,7 @@ int forward_lowrank(const dyra_spec& s, const char* plan, const void* X, const v
   const int dtype = TT<T>::ESZ == 2 ? DYRA_BF16 : DYRA_F32;
   const PlanLayout PL = plan_layout(s, dtype);
   const WsLayout WL = si.layout(s, dtype);
-  const int64_t B = si.B, seg = si.seg, n = si.n, c1 = s.c1, c2 = s.c2;
+  const int64_t B = si.B, n = si.n, c1 = s.c1, c2 = s.c2;
   const int k = s.k, r = s.r;
   T* TL = reinterpret_cast<T*>(ws + WL.A);
   T* Lt = reinterpret_cast<T*>(ws + WL.Lt);
@@ -3554,10 +3564,10 @@ int forward_lowrank(const dyra_spec& s, const char* plan, const void* X, const v
   for (int h = 2; h < half_steps; ++h) {
     if (h % 2 == 0) {
       if constexpr (TT<T>::ESZ == 2)
-        left_step_bf16(s, plan, reinterpret_cast<const bf16_t*>(X), B, seg, eps, ws, st, half_steps, k,
+        left_step_bf16(s, plan, reinterpret_cast<const bf16_t*>(X), si, eps, ws, st, half_steps, k,
                        (int64_t)(k + r));
       else
-        left_step_f32(s, plan, reinterpret_cast<const float*>(X), B, seg, eps, ws, st, half_steps);
+        left_step_f32(s, plan, reinterpret_cast<const float*>(X), si, eps, ws, st, half_steps);
     } else {
       forward_residual<C, C3>(s, plan, X, si, eps, solver, ws, st, StageEvents{nullptr, 0});
     }
@@ -3612,7 +3622,7 @@ int forward_monarch(const dyra_spec& s, const char* plan, const void* X, const v
   E.mark(1, st);
   forward_residual<CfgB, CfgB3>(s, plan, X, si, eps, solver, ws, st, E);
   for (int h = 2; h < half_steps; ++h) {   // further ALS half-steps (L sits after the C = m^2 V columns)
-    if (h % 2 == 0) left_step_bf16(s, plan, Xb, B, si.seg, eps, ws, st, half_steps, MO * MO, MO * MO + r);
+    if (h % 2 == 0) left_step_bf16(s, plan, Xb, si, eps, ws, st, half_steps, MO * MO, MO * MO + r);
     else forward_residual<CfgB, CfgB3>(s, plan, X, si, eps, solver, ws, st, StageEvents{nullptr, 0});
   }
   E.mark(4, st);
@@ -3660,7 +3670,7 @@ int forward_blast(const dyra_spec& s, const char* plan, const void* X, const voi
   E.mark(1, st);
   forward_residual<CfgB, CfgB3>(s, plan, X, si, eps, solver, ws, st, E);
   for (int h = 2; h < half_steps; ++h) {   // further ALS half-steps (L sits after the nb rb Z columns)
-    if (h % 2 == 0) left_step_bf16(s, plan, Xb, B, si.seg, eps, ws, st, half_steps, (int)NR, ldzl);
+    if (h % 2 == 0) left_step_bf16(s, plan, Xb, si, eps, ws, st, half_steps, (int)NR, ldzl);
     else forward_residual<CfgB, CfgB3>(s, plan, X, si, eps, solver, ws, st, StageEvents{nullptr, 0});
   }
   if (s.kind == DYRA_BLAST_DIAG) {
@@ -3810,21 +3820,53 @@ int varlen_info(int64_t B, const int64_t* off, const int32_t* off_dev, SegInfo& 
   si.max_len = mx;
   si.min_len = mn;
   si.off_dev = off_dev;
+  si.off_host = off;
   return DYRA_OK;
 }
 }  // namespace
 
-extern "C" int dyra_workspace_size_varlen(const dyra_spec* spec, int64_t B, const int64_t* offsets, int32_t dtype,
-                                          size_t* bytes) {
+extern "C" int dyra_workspace_size_varlen_als(const dyra_spec* spec, int64_t B, const int64_t* offsets,
+                                              int32_t dtype, int32_t half_steps, size_t* bytes) {
   if (!spec || !bytes) return DYRA_EINVAL;
   int rc = validate_spec(spec);
   if (rc) return rc;
   rc = validate_dtype(*spec, dtype);
   if (rc) return rc;
+  rc = check_als(*spec, dtype, half_steps);
+  if (rc) return rc;
   SegInfo si;
   rc = varlen_info(B, offsets, nullptr, si);
   if (rc) return rc;
-  *bytes = si.layout(*spec, dtype).total;
+  *bytes = si.layout(*spec, dtype, half_steps).total;
+  return DYRA_OK;
+}
+
+extern "C" int dyra_workspace_size_varlen(const dyra_spec* spec, int64_t B, const int64_t* offsets, int32_t dtype,
+                                          size_t* bytes) {
+  return dyra_workspace_size_varlen_als(spec, B, offsets, dtype, 2, bytes);
+}
+
+extern "C" int dyra_forward_varlen_als(const dyra_spec* spec, const void* plan, const void* X, const void* bias,
+                                       void* Y, int64_t B, const int64_t* offsets, const int32_t* offsets_dev,
+                                       int32_t dtype, float ridge_eps, int32_t solver, int32_t half_steps,
+                                       int32_t* status_out, void* workspace, size_t ws_bytes, void* stream) {
+  if (!offsets_dev) return DYRA_EINVAL;
+  SegInfo si;
+  int rc = varlen_info(B, offsets, offsets_dev, si);
+  if (rc) return rc;
+  // the uniform checks with one segment of all n rows, then the ragged size
+  rc = check_forward_args(spec, plan, X, Y, 1, si.n, dtype, ridge_eps, solver, workspace, (size_t)-1, half_steps);
+  if (rc) return rc;
+  if (bias && (reinterpret_cast<uintptr_t>(bias) & 15)) return DYRA_EINVAL;
+  if (status_out && (reinterpret_cast<uintptr_t>(status_out) & 3)) return DYRA_EINVAL;
+  const WsLayout WL = si.layout(*spec, dtype, half_steps);
+  if (ws_bytes < WL.total) return DYRA_EWORKSPACE;
+  rc = dispatch(spec, plan, X, bias, Y, si, dtype, ridge_eps, solver, workspace, stream, StageEvents{nullptr, 0},
+                half_steps);
+  if (rc || !status_out) return rc;
+  if (hipMemcpyAsync(status_out, reinterpret_cast<const char*>(workspace) + WL.status, (size_t)B * 4,
+                     hipMemcpyDeviceToDevice, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return DYRA_EHIP;
   return DYRA_OK;
 }
 
@@ -3832,23 +3874,8 @@ extern "C" int dyra_forward_varlen(const dyra_spec* spec, const void* plan, cons
                                    void* Y, int64_t B, const int64_t* offsets, const int32_t* offsets_dev,
                                    int32_t dtype, float ridge_eps, int32_t solver, int32_t* status_out,
                                    void* workspace, size_t ws_bytes, void* stream) {
-  if (!offsets_dev) return DYRA_EINVAL;
-  SegInfo si;
-  int rc = varlen_info(B, offsets, offsets_dev, si);
-  if (rc) return rc;
-  // the uniform checks with one segment of all n rows, then the ragged size
-  rc = check_forward_args(spec, plan, X, Y, 1, si.n, dtype, ridge_eps, solver, workspace, (size_t)-1);
-  if (rc) return rc;
-  if (bias && (reinterpret_cast<uintptr_t>(bias) & 15)) return DYRA_EINVAL;
-  if (status_out && (reinterpret_cast<uintptr_t>(status_out) & 3)) return DYRA_EINVAL;
-  const WsLayout WL = si.layout(*spec, dtype);
-  if (ws_bytes < WL.total) return DYRA_EWORKSPACE;
-  rc = dispatch(spec, plan, X, bias, Y, si, dtype, ridge_eps, solver, workspace, stream, StageEvents{nullptr, 0}, 2);
-  if (rc || !status_out) return rc;
-  if (hipMemcpyAsync(status_out, reinterpret_cast<const char*>(workspace) + WL.status, (size_t)B * 4,
-                     hipMemcpyDeviceToDevice, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
-    return DYRA_EHIP;
-  return DYRA_OK;
+  return dyra_forward_varlen_als(spec, plan, X, bias, Y, B, offsets, offsets_dev, dtype, ridge_eps, solver, 2,
+                                 status_out, workspace, ws_bytes, stream);
 }
 
 extern "C" int dyra_forward(const dyra_spec* spec, const void* plan, const void* X, const void* bias, void* Y,

@@ -102,6 +102,9 @@ def lib():
             "dyra_workspace_size_varlen": [SP, I64, ctypes.POINTER(I64), I32, ctypes.POINTER(SZ)],
             "dyra_forward_varlen": [SP, P, P, P, P, I64, ctypes.POINTER(I64), P, I32, ctypes.c_float, I32, P, P,
                                     SZ, P],
+            "dyra_workspace_size_varlen_als": [SP, I64, ctypes.POINTER(I64), I32, I32, ctypes.POINTER(SZ)],
+            "dyra_forward_varlen_als": [SP, P, P, P, P, I64, ctypes.POINTER(I64), P, I32, ctypes.c_float, I32, I32,
+                                        P, P, SZ, P],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -350,29 +353,30 @@ def _offsets(offsets) -> np.ndarray:
     return off
 
 
-def workspace_size_varlen(spec: Spec, offsets, dtype: int) -> int:
+def workspace_size_varlen(spec: Spec, offsets, dtype: int, half_steps: int = 2) -> int:
     off = _offsets(offsets)
     nb = ctypes.c_size_t()
-    _check("dyra_workspace_size_varlen",
-           lib().dyra_workspace_size_varlen(ctypes.byref(spec), off.size - 1,
-                                            off.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), dtype,
-                                            ctypes.byref(nb)))
+    _check("dyra_workspace_size_varlen_als",
+           lib().dyra_workspace_size_varlen_als(ctypes.byref(spec), off.size - 1,
+                                                off.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), dtype,
+                                                half_steps, ctypes.byref(nb)))
     return nb.value
 
 
 def forward_varlen(spec: Spec, plan, X, bias, Y, offsets, dtype: int, eps: float = 1e-6, solver: int = SOLVER_AUTO,
-                   workspace=None, offsets_dev=None, status=None, stream=None):
+                   workspace=None, offsets_dev=None, status=None, stream=None, half_steps: int = 2):
     """The forward over ragged segments: segment b is rows offsets[b] ..
-    offsets[b + 1] - 1 of X (asynchronous).  offsets_dev: a device int32
-    copy of the offsets (made here when not given); status: optional device
-    int32 [B] for the per-segment solver status words."""
+    offsets[b + 1] - 1 of X (asynchronous), with 2 t = half_steps ALS
+    half-steps.  offsets_dev: a device int32 copy of the offsets (made here
+    when not given); status: optional device int32 [B] for the per-segment
+    solver status words."""
     torch = _torch()
     off = _offsets(offsets)
     B, n = off.size - 1, int(off[-1])
     if np.any(np.diff(off) < 1) or off[0] != 0:
         raise ValueError("offsets must start at 0 and grow by at least one row per segment")
     _check_forward_tensors(spec, plan, X, bias, Y, 1, n, dtype, workspace,
-                           lambda: workspace_size_varlen(spec, off, dtype))
+                           lambda: workspace_size_varlen(spec, off, dtype, half_steps))
     if offsets_dev is None:
         offsets_dev = torch.from_numpy(off.astype(np.int32)).to(X.device)
     _expect_shape(offsets_dev, "offsets_dev", (B + 1,), torch.int32)
@@ -380,12 +384,12 @@ def forward_varlen(spec: Spec, plan, X, bias, Y, offsets, dtype: int, eps: float
     if status is not None:
         _expect_shape(status, "status", (B,), torch.int32)
         _expect_device([("status", status)], X.device)
-    rc = lib().dyra_forward_varlen(ctypes.byref(spec), _dev(plan, "plan"), _dev(X, "X"), _dev(bias, "bias"),
-                                   _dev(Y, "Y"), B, off.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
-                                   _dev(offsets_dev, "offsets_dev"), dtype, eps, solver, _dev(status, "status"),
-                                   _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
-                                   _stream(stream))
-    _check("dyra_forward_varlen", rc)
+    rc = lib().dyra_forward_varlen_als(ctypes.byref(spec), _dev(plan, "plan"), _dev(X, "X"), _dev(bias, "bias"),
+                                       _dev(Y, "Y"), B, off.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                       _dev(offsets_dev, "offsets_dev"), dtype, eps, solver, half_steps,
+                                       _dev(status, "status"), _dev(workspace, "workspace"),
+                                       workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("dyra_forward_varlen_als", rc)
 
 
 NOALLOC_MAX_WORKSPACE = 64 << 20   # DYRA_NOALLOC_MAX_WORKSPACE
@@ -498,18 +502,19 @@ class DyraLayer:
         return Y
 
     def forward_varlen(self, X, offsets, out=None, stream=None):
-        """Ragged segments (t = 1): returns (Y, status) with status a host
-        int32 array of the per-segment solver status words."""
+        """Ragged segments (the layer's ALS iterations): returns (Y, status)
+        with status a device int32 array of the per-segment solver status
+        words."""
         torch = _torch()
         off = _offsets(offsets)
         if X.dtype != torch_dtype(self.dtype) or X.device != self.device:
             raise ValueError("X dtype / device does not match the layer")
         Y = out if out is not None else torch.empty((int(off[-1]), self.spec.c2), dtype=X.dtype, device=X.device)
-        n = workspace_size_varlen(self.spec, off, self.dtype)
+        n = workspace_size_varlen(self.spec, off, self.dtype, self.half_steps)
         ws = torch.empty(n, dtype=torch.uint8, device=self.device)
         st = torch.empty(off.size - 1, dtype=torch.int32, device=self.device)
         forward_varlen(self.spec, self.plan, X, self.bias, Y, off, self.dtype, self.eps, self.solver, ws,
-                       status=st, stream=stream)
+                       status=st, stream=stream, half_steps=self.half_steps)
         return Y, st
 
     def forward_events(self, X, B: int, s: int, out, events, stream=None):

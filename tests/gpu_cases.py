@@ -159,10 +159,11 @@ def parity_report(w, Yg, terms, tol=None, alpha=ALPHA, beta=BETA, c_elem=C_ELEM,
     return m, fails
 
 
-def gpu_forward_varlen(w, factors, X, bias, offsets, eps=1e-6, solver="auto"):
-    """The forward over ragged segments (row offsets) through dyra_forward_varlen."""
+def gpu_forward_varlen(w, factors, X, bias, offsets, eps=1e-6, solver="auto", half_steps=2):
+    """The forward over ragged segments (row offsets) through dyra_forward_varlen_als."""
     import torch
-    layer = D.DyraLayer(D.spec_of(w), factors, w.dtype, bias=bias, eps=eps, solver=D.SOLVERS[solver])
+    layer = D.DyraLayer(D.spec_of(w), factors, w.dtype, bias=bias, eps=eps, solver=D.SOLVERS[solver],
+                        half_steps=half_steps)
     Y, st = layer.forward_varlen(D.to_device(X, w.dtype), offsets)
     torch.cuda.synchronize()
     return Y.float().cpu().numpy().astype(np.float64), st.cpu().numpy()
@@ -185,7 +186,7 @@ def run_same_factor_case(w, eps=1e-6, solver="auto", tol=None, inputs=None, prep
                                     half_steps=half_steps)
     else:
         Yg, status = gpu_forward_varlen(w, host_factors_from_oracle(prep), inp.X, inp.bias, offsets, eps=eps,
-                                        solver=solver)
+                                        solver=solver, half_steps=half_steps)
     m, fails = parity_report(w, Yg, terms, tol=tol, alpha=alpha, beta=beta, c_elem=c_elem, offsets=offsets)
     log(f"  case {w.name} B={w.B} s={w.s} c1={w.c1} c2={w.c2} r={w.r} k={w.k} dtype={w.dtype} "
         f"solver={solver} t={half_steps / 2}: rel_fro={m['rel_fro']:.3e} seg_max={m['seg_rel_max']:.3e} "

@@ -276,3 +276,27 @@ def test_varlen_workspace_matches_uniform_and_forward_rejects_before_hip():
     need = D.workspace_size_varlen(spec, a, synth.DT_BF16)
     assert L.dyra_forward_varlen(ctypes.byref(spec), 1 << 12, 1 << 13, None, 1 << 14, 2, a.ctypes.data_as(P),
                                  1 << 16, synth.DT_BF16, 1e-6, 0, None, 1 << 15, need - 1, None) == -3
+
+
+def test_varlen_als_validates_on_host():
+    """dyra_workspace_size_varlen_als / dyra_forward_varlen_als: half_steps
+    outside 2..4 is EINVAL; half_steps = 2 sizes the plain ragged forward;
+    more half-steps need the ALS buffers; a workspace one byte short is
+    rejected before any HIP call."""
+    spec = _lowrank()
+    a = np.array([0, 50, 77, 140], dtype=np.int64)
+    P = ctypes.POINTER(ctypes.c_int64)
+    L = D.lib()
+    n = ctypes.c_size_t()
+    for h, rc in ((1, -1), (5, -1), (2, 0), (3, 0), (4, 0)):
+        assert L.dyra_workspace_size_varlen_als(ctypes.byref(spec), 3, a.ctypes.data_as(P), synth.DT_BF16, h,
+                                                ctypes.byref(n)) == rc
+    assert D.workspace_size_varlen(spec, a, synth.DT_BF16, 2) == D.workspace_size_varlen(spec, a, synth.DT_BF16)
+    s3 = D.workspace_size_varlen(spec, a, synth.DT_BF16, 3)
+    assert s3 > D.workspace_size_varlen(spec, a, synth.DT_BF16) and s3 == D.workspace_size_varlen(spec, a,
+                                                                                                 synth.DT_BF16, 4)
+    assert D.workspace_size_varlen(spec, a, synth.DT_F32, 4) > D.workspace_size_varlen(spec, a, synth.DT_F32)
+    assert L.dyra_forward_varlen_als(ctypes.byref(spec), 1 << 12, 1 << 13, None, 1 << 14, 3, a.ctypes.data_as(P),
+                                     1 << 16, synth.DT_BF16, 1e-6, 0, 7, None, 1 << 15, 1 << 40, None) == -1
+    assert L.dyra_forward_varlen_als(ctypes.byref(spec), 1 << 12, 1 << 13, None, 1 << 14, 3, a.ctypes.data_as(P),
+                                     1 << 16, synth.DT_BF16, 1e-6, 0, 3, None, 1 << 15, s3 - 1, None) == -3

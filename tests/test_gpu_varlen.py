@@ -83,3 +83,23 @@ def test_uniform_offsets_match_dyra_forward_bitwise(name, base, B, s):
     (Y,), st = gpu_forward(w, f, inp.X, inp.bias)
     Yv, stv = gpu_forward_varlen(w, f, inp.X, inp.bias, np.arange(B + 1, dtype=np.int64) * s)
     assert np.array_equal(Y, Yv) and np.array_equal(st, stv)
+
+
+# more ALS iterations on ragged segments: each segment's left step uses its
+# own rows of X (the left-step GEMM reads the offsets)
+ALS_CASES = [
+    ("als_lowrank_mixed", sc(W["vitb_fc1"], c1=256, c2=264, k=32, r=16), [41, 300, 77, 129, 36, 450]),
+    ("als_lowrank_fp32", sc(W["vitb_fc1"], c1=192, c2=200, k=24, r=16, dtype=synth.DT_F32), [150, 64, 31, 90]),
+    ("als_tile_gram", sc(W["vitl_fc1"], c1=384, c2=512, k=256, r=64), [700, 160, 333, 900]),
+    ("als_monarch", sc(W["monarch"], r=32), [300, 97, 200]),
+    ("als_blast", sc(W["lm_blast"], c1=512, c2=1536, nb=4, rb=32, r=32, n_out=4, solver="auto"), [200, 113, 90]),
+]
+
+
+@pytest.mark.parametrize("half_steps", [3, 4])
+@pytest.mark.parametrize("name,base,lengths", ALS_CASES, ids=[c[0] for c in ALS_CASES])
+def test_ragged_segments_als(name, base, lengths, half_steps):
+    off = _offsets(lengths)
+    w = sc(base, name=name, B=1, s=int(off[-1]))
+    err, status, _, _ = run_same_factor_case(w, solver=w.solver, offsets=off, half_steps=half_steps)
+    assert np.all(status == D.SOLVE_OK)
