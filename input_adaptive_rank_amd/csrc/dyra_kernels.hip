@@ -7,8 +7,9 @@
 // XW ~ X W_hat + L1 R1; paperlayer.ai 2.2 and 2.4):
 //   S1  [T | L] = X [U | P]           one MFMA pass over X (T = X U_f, L = X P)
 //   S3  M_b = L_b^T X_b, G_b = L_b^T L_b   split-N MFMA reductions over tokens
-//   S4  Ginv_b = (G_b + lambda_b I)^-1     symmetric sweep (r < 128) or
-//                                          Newton-Schulz (r >= 128)
+//   S4  Ginv_b = (G_b + lambda_b I)^-1     symmetric sweep (AUTO, every r; fp32,
+//                                          fp64 where a pivot needs it), or the
+//                                          Cholesky route / Newton-Schulz
 //       M'_b = Ginv_b M_b
 //   S5  R_b = M'_b W_res               one GEMM over all segments (R^T stored)
 //   S6  Y_b = T_b V + L_b R_b + bias    one fused GEMM, K = k + r, with a
@@ -3303,11 +3304,11 @@ void forward_residual(const dyra_spec& s, const char* plan, const void* X, const
   int32_t* stat = reinterpret_cast<int32_t*>(ws + WL.status);
   int32_t* prec = reinterpret_cast<int32_t*>(ws + WL.prec);
   const int64_t ldt = lt_pitch(n);
-  // AUTO takes the sweep at every supported r: on MI355X the fp64 sweep on one
-  // workgroup beats Newton-Schulz (split-precision phase plus fp32 polish),
-  // whose one solve per CU the per-CU MFMA rate bounds, at r = 64 and r = 128
-  // alike (one r = 128 solve: about 100 us against 140 us); Newton-Schulz
-  // stays selectable.
+  // AUTO takes the sweep at every supported r: on MI355X the sweep on one
+  // workgroup, overlapping the strips inside the token-reduction launch,
+  // beats Newton-Schulz at r = 64 (32 solves: about 23 against 120 us) and
+  // matches it at r = 128, where Newton-Schulz runs beside the strips on the
+  // side stream; Newton-Schulz and the Cholesky route stay selectable.
   const bool ns = solver == DYRA_SOLVER_NS;
   // solve inside the token-reduction launch: 1 the sweep, 2 the Cholesky
   // route, 0 none (Newton-Schulz runs after it: as the launch's 4-wave solve
