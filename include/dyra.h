@@ -38,7 +38,9 @@
  *     only, that entry point's static device workspace.  Calls on distinct
  *     streams with distinct workspaces are independent.
  *   - Matrices are row-major and contiguous.  Device pointers must be 16-byte
- *     aligned.  "stream" is a hipStream_t passed as void* (NULL = default).
+ *     aligned.  "stream" is a hipStream_t passed as void* (NULL = default);
+ *     it must belong to the current device (grid sizes and the side stream
+ *     are taken from that device).
  *   - dtype: DYRA_F32 (fp32 storage, fp32 arithmetic) or DYRA_BF16 (bf16
  *     storage, fp32 accumulation); the r x r solves run in fp64 (Cholesky),
  *     fp32 with an fp64 pass where a pivot needs it (sweep), or at fp32
