@@ -587,6 +587,21 @@ def test_ragged_segments_are_independent_forwards():
                                   O.forward(X, prep, bias, 3, 20))
 
 
+def test_ragged_segments_are_independent_at_more_iterations():
+    """The same at t = 1.5 and t = 2: every ALS half-step of a segment uses
+    that segment's rows only, so moving a boundary changes only the two
+    segments it separates."""
+    rng, _, prep, X, bias = _setup()
+    off = [0, 9, 23, 60]
+    for t in (1.5, 2.0):
+        Y = O.forward(X, prep, bias, 0, 0, t=t, offsets=off)
+        for lo, hi in zip(off[:-1], off[1:]):
+            np.testing.assert_array_equal(Y[lo:hi], O.forward(X[lo:hi], prep, bias, 1, hi - lo, t=t))
+        Y2 = O.forward(X, prep, bias, 0, 0, t=t, offsets=[0, 9, 30, 60])
+        np.testing.assert_array_equal(Y2[:9], Y[:9])
+        assert not np.allclose(Y2[9:23], Y[9:23])
+
+
 def test_rotation_of_initial_right_factor_changes_nothing():
     rng, _, prep, X, bias = _setup()
     Q = synth.haar_columns(rng.standard_normal((5, 5)))
